@@ -1,0 +1,393 @@
+"""Plain, slow CPU oracle of the single-GPU MoE expert-layer path.
+
+TEST INFRASTRUCTURE. Only the tests, the smoke check and the benchmark's CPU
+baseline may import this module. The product path (the HIP library and its
+Python binding) never imports, calls or links it, and this module imports
+nothing from the product.
+
+Sources (cited by page and section):
+
+* "Expert Parallelism (EP)" (llm-infra-atlas), section 1 "MoE layer 的 forward
+  通路": the layer is router gating (logits = x·Wg^T over [T,E]), routing
+  (top-k plus a score function giving probs and a routing map), metadata
+  (tokens per expert), a permute that makes each local expert's tokens
+  contiguous, a grouped fc1 -> activation -> fc2, and an unpermute that reduces
+  back to token order weighted by the top-k weights, plus shared experts.
+* same page, section 2 "三层抽象与三个代码库的分工": the dispatch output must be
+  expert-contiguous with every segment aligned to the GEMM M tile (the layout
+  contract the grouped GEMM consumes).
+* same page, section 5 "forward / backward 的对称性": permute is an index_select
+  and unpermute a scatter_add; combine is the transpose of dispatch.
+* "Expert Tensor Parallel" design note (HyperParallel issue 104), section 4.3:
+  expert weights w1, w3 of shape [E, H, D] and w2 of shape [E, D, H], SwiGLU
+  with w1/w3 on the input side and w2 on the output side (H there is this
+  module's F).
+
+Readings taken where the pages are silent (each is also listed in the design doc):
+
+1. Score function: softmax over all E logits; the top-k weights are those
+   probabilities at the selected experts, not renormalised (``renorm`` is an
+   option, off by default).
+2. Selection compares the float32 logits with key (-logit, expert index): the
+   lower index wins a tie, results come out best first. -0 and +0 tie.
+3. The float32 logits follow one fixed operation order (``router_logits``),
+   because the top-k decision must be taken identically on both sides.
+4. A router bias is added to the logits, so it moves both the choice and the
+   weights.
+5. Activation: h = silu(x·w1^T) * (x·w3^T), silu(a) = a / (1 + exp(-a)).
+6. Pad rows of every segment are zero, so their h and Y rows are exactly zero.
+   Segments of experts with no token are empty (no rows, no tiles).
+7. Inside a segment rows follow the flattened (token, slot) order t*k + j.
+8. Slots holding -1 (a share that lives on another rank) are skipped by the
+   counts, the permute and the combine.
+9. Storage points: x, weights, h, Y, the shared-expert output and the layer
+   output are stored in the layer dtype (float32 or bf16, round to nearest
+   even); all other arithmetic here is float64.
+
+Float arrays may be passed as float32/float64 values or, for bf16, as uint16
+bit patterns; this module widens them itself.
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict, Optional
+
+import numpy as np
+
+__all__ = [
+    "capacity", "values64", "values32", "round_storage", "round_bf16",
+    "router_logits", "softmax", "select_topk", "route",
+    "dispatch_layout", "permute", "silu", "expert_swiglu", "grouped_swiglu",
+    "shared_experts", "combine", "forward", "token_outputs",
+]
+
+_LANES = 64  # width of one reduction group in the fixed logit order
+
+
+# ----------------------------------------------------------------------------
+# storage types
+# ----------------------------------------------------------------------------
+
+def values64(a: np.ndarray) -> np.ndarray:
+    """Values of a stored array as float64. uint16 arrays are bf16 bit patterns."""
+    a = np.asarray(a)
+    if a.dtype == np.uint16:
+        return (a.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    return a.astype(np.float64)
+
+
+def values32(a: np.ndarray) -> np.ndarray:
+    """Values of a float32 or bf16 (uint16 bits) array as float32 (exact)."""
+    a = np.asarray(a)
+    if a.dtype == np.uint16:
+        return (a.astype(np.uint32) << np.uint32(16)).view(np.float32)
+    if a.dtype != np.float32:
+        raise TypeError("router inputs must be float32 values or bf16 bit patterns")
+    return a
+
+
+def round_bf16(a: np.ndarray) -> np.ndarray:
+    """Round float64 values to the nearest bf16 value (ties to even), returned as float64.
+
+    bf16 keeps 8 significant bits and float32's exponent range; below the
+    smallest normal (2^-126) the spacing stays 2^-133. Inputs are finite."""
+    a = np.asarray(a, dtype=np.float64)
+    _, e = np.frexp(a)                       # |a| in [2^(e-1), 2^e)
+    e = np.maximum(e, -125)
+    quantum = np.ldexp(1.0, e - 8)
+    return np.rint(a / quantum) * quantum    # np.rint rounds half to even
+
+
+def round_storage(a: np.ndarray, dtype: str) -> np.ndarray:
+    """Value after storing float64 ``a`` in the layer dtype, as float64."""
+    if dtype == "f32":
+        return np.asarray(a, dtype=np.float64).astype(np.float32).astype(np.float64)
+    if dtype == "bf16":
+        return round_bf16(a)
+    raise ValueError(dtype)
+
+
+def capacity(T: int, k: int, E: int, m_tile: int) -> int:
+    """Rows the permuted buffer needs in the worst case.
+
+    With N = T*k slots and c_e rows per expert, the padded total is
+    sum_e ceil(c_e / Mt) * Mt <= N + min(E, N) * (Mt - 1), and it is a multiple of
+    Mt, so the largest multiple of Mt not above that bound always suffices."""
+    N = T * k
+    return ((N + min(E, N) * (m_tile - 1)) // m_tile) * m_tile
+
+
+# ----------------------------------------------------------------------------
+# routing ("Expert Parallelism (EP)", section 1: router.gating and routing)
+# ----------------------------------------------------------------------------
+
+def router_logits(x: np.ndarray, wg: np.ndarray, dtype: str,
+                  bias: Optional[np.ndarray] = None) -> np.ndarray:
+    """logits[t, e] = sum_d x[t, d] * Wg[e, d] (+ bias[e]) in float32, fixed order.
+
+    The order (a reading; the pages fix none): elements are taken in chunks of
+    V = 16 bytes (V = 4 float32 or 8 bf16 values). Chunk c covers d in
+    [c*V, c*V + V) and belongs to lane c mod 64. Each lane starts at +0 and adds
+    the rounded products of its chunks in increasing d, one float32 multiply and
+    one float32 add per element (no fused multiply-add). The 64 lane sums are
+    then combined by a butterfly: for m = 32, 16, 8, 4, 2, 1 every lane adds the
+    value of lane (l xor m); all lanes end with the same value. A bias is added
+    last in float32.
+    """
+    x32, w32 = values32(x), values32(wg)
+    T, D = x32.shape
+    E = w32.shape[0]
+    V = 4 if dtype == "f32" else 8
+    if D % V:
+        raise ValueError("D must be a multiple of the 16-byte chunk")
+    chunks = D // V
+    Q = -(-chunks // _LANES)
+    pad = Q * _LANES * V - D
+    wp = np.concatenate([w32, np.zeros((E, pad), np.float32)], axis=1).reshape(E, Q, _LANES, V)
+    out = np.empty((T, E), dtype=np.float32)
+    partner = {m: np.arange(_LANES) ^ m for m in (32, 16, 8, 4, 2, 1)}
+    step = 512
+    for t0 in range(0, T, step):
+        xb = x32[t0:t0 + step]
+        tb = xb.shape[0]
+        xp = np.concatenate([xb, np.zeros((tb, pad), np.float32)], axis=1).reshape(tb, Q, _LANES, V)
+        acc = np.zeros((tb, E, _LANES), dtype=np.float32)
+        for q in range(Q):
+            for i in range(V):
+                prod = xp[:, None, q, :, i] * wp[None, :, q, :, i]   # rounded float32 product
+                acc = acc + prod                                     # rounded float32 sum
+        for m in (32, 16, 8, 4, 2, 1):
+            acc = acc + acc[:, :, partner[m]]
+        out[t0:t0 + tb] = acc[:, :, 0]
+    if bias is not None:
+        out = out + np.asarray(bias, dtype=np.float32)[None, :]
+    return out
+
+
+def softmax(logits: np.ndarray) -> np.ndarray:
+    """p_e = exp(l_e - max l) / sum_e' exp(l_e' - max l), in float64."""
+    l64 = np.asarray(logits, dtype=np.float64)
+    z = np.exp(l64 - l64.max(axis=1, keepdims=True))
+    return z / z.sum(axis=1, keepdims=True)
+
+
+def select_topk(logits: np.ndarray, k: int) -> np.ndarray:
+    """Indices of the k largest logits per row, best first; ties go to the lower index."""
+    l = np.asarray(logits)
+    if not np.all(np.isfinite(l)):
+        raise ValueError("router logits must be finite")
+    order = np.argsort(-l, axis=1, kind="stable")   # stable: equal keys keep index order
+    return np.ascontiguousarray(order[:, :k].astype(np.int32))
+
+
+def route(x, wg, k: int, dtype: str, bias=None, renorm: bool = False):
+    """Softmax-then-top-k routing. Returns (topk_idx [T,k] int32, topk_w [T,k] float64,
+    logits [T,E] float32)."""
+    logits = router_logits(x, wg, dtype, bias)
+    idx = select_topk(logits, k)
+    p = softmax(logits)
+    w = np.take_along_axis(p, idx.astype(np.int64), axis=1)
+    if renorm:
+        w = w / w.sum(axis=1, keepdims=True)
+    return idx, w, logits
+
+
+# ----------------------------------------------------------------------------
+# dispatch metadata and permute ("Expert Parallelism (EP)", sections 1, 2, 5)
+# ----------------------------------------------------------------------------
+
+def dispatch_layout(topk_idx: np.ndarray, E: int, m_tile: int,
+                    m_cap: Optional[int] = None) -> Dict[str, np.ndarray]:
+    """Tokens-per-expert metadata and the stable, tile-aligned permutation maps.
+
+    counts[e]     number of slots (t, j) with topk_idx[t, j] == e (-1 slots skipped)
+    offsets       exclusive prefix sum of ceil(counts / Mt) * Mt, length E + 1
+    dst_row[t,j]  offsets[e] + rank of flat index t*k+j among e's slots (-1 if skipped)
+    src_row[r]    t*k + j of the slot placed in row r, -1 for pad and unused rows
+    tile_expert   expert owning each Mt-row tile, -1 for tiles past offsets[E]
+    """
+    idx = np.asarray(topk_idx)
+    T, k = idx.shape
+    flat = idx.reshape(-1).astype(np.int64)
+    if np.any(flat >= E) or np.any(flat < -1):
+        raise ValueError("topk_idx values must lie in [-1, E)")
+    if m_cap is None:
+        m_cap = capacity(T, k, E, m_tile)
+    valid = flat >= 0
+    counts = np.bincount(flat[valid], minlength=E).astype(np.int64)
+    padded = -(-counts // m_tile) * m_tile
+    offsets = np.concatenate([[0], np.cumsum(padded)]).astype(np.int64)
+    if offsets[-1] > m_cap:
+        raise ValueError("m_cap too small")
+    # stable counting sort of the flat slot order by expert
+    key = np.where(valid, flat, E)
+    order = np.argsort(key, kind="stable")[: int(valid.sum())]
+    sorted_e = flat[order]
+    first = np.concatenate([[0], np.cumsum(counts)])[:-1]
+    rank = np.arange(order.size) - first[sorted_e]
+    dst = np.full(T * k, -1, dtype=np.int64)
+    dst[order] = offsets[sorted_e] + rank
+    src = np.full(m_cap, -1, dtype=np.int64)
+    src[dst[order]] = order
+    tile_expert = np.full(m_cap // m_tile, -1, dtype=np.int64)
+    for e in range(E):
+        tile_expert[offsets[e] // m_tile: offsets[e + 1] // m_tile] = e
+    return {
+        "counts": counts.astype(np.int32),
+        "offsets": offsets.astype(np.int32),
+        "dst_row": dst.reshape(T, k).astype(np.int32),
+        "src_row": src.astype(np.int32),
+        "tile_expert": tile_expert.astype(np.int32),
+        "m_cap": int(m_cap),
+    }
+
+
+def permute(x: np.ndarray, layout: Dict[str, np.ndarray]) -> np.ndarray:
+    """X_perm[r] = x[src_row[r] // k] for rows holding a slot, zero elsewhere.
+
+    Copies stored values unchanged (same dtype as ``x``), so it is exact."""
+    x = np.asarray(x)
+    T, k = layout["dst_row"].shape
+    src = layout["src_row"].astype(np.int64)
+    out = np.zeros((layout["m_cap"], x.shape[1]), dtype=x.dtype)
+    rows = np.nonzero(src >= 0)[0]
+    out[rows] = x[src[rows] // k]
+    return out
+
+
+# ----------------------------------------------------------------------------
+# experts (section 1 "routed_experts_compute: fc1 -> act -> fc2"; ETP note 4.3)
+# ----------------------------------------------------------------------------
+
+def silu(a: np.ndarray) -> np.ndarray:
+    """silu(a) = a * sigmoid(a) = a / (1 + exp(-a)), float64."""
+    a = np.asarray(a, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return a / (1.0 + np.exp(-a))
+
+
+def expert_swiglu(A, w1e, w3e, w2e, dtype: str):
+    """One expert on rows A [M, D]: h = silu(A w1e^T) * (A w3e^T) stored, then
+    Y = h w2e^T stored. Returns (h, Y) as float64 values of the stored results."""
+    A64 = values64(A)
+    a = A64 @ values64(w1e).T
+    b = A64 @ values64(w3e).T
+    h = round_storage(silu(a) * b, dtype)
+    y = round_storage(h @ values64(w2e).T, dtype)
+    return h, y
+
+
+def grouped_swiglu(x_perm, offsets, w1, w3, w2, dtype: str):
+    """m-grouped fc1 -> silu(a)*b -> fc2 over the expert-contiguous buffer.
+
+    Segment e is rows [offsets[e], offsets[e+1]) and uses w1[e], w3[e], w2[e].
+    Returns (h [m_cap, F], Y [m_cap, D]) as float64 values; rows past offsets[E]
+    are zero."""
+    M = x_perm.shape[0]
+    E, F, D = w1.shape
+    h = np.zeros((M, F), dtype=np.float64)
+    y = np.zeros((M, D), dtype=np.float64)
+    for e in range(E):
+        r0, r1 = int(offsets[e]), int(offsets[e + 1])
+        if r1 > r0:
+            h[r0:r1], y[r0:r1] = expert_swiglu(x_perm[r0:r1], w1[e], w3[e], w2[e], dtype)
+    return h, y
+
+
+def shared_experts(x, ws1, ws3, ws2, dtype: str):
+    """Always-active shared experts on every token, summed unweighted and stored once.
+
+    Each shared expert's h is a stored intermediate; the sum of their fc2 outputs is
+    rounded once (the shared experts behave as one expert whose F is the
+    concatenation of theirs)."""
+    x64 = values64(x)
+    total = np.zeros((x64.shape[0], ws2.shape[1]), dtype=np.float64)
+    for s in range(ws1.shape[0]):
+        a = x64 @ values64(ws1[s]).T
+        b = x64 @ values64(ws3[s]).T
+        h = round_storage(silu(a) * b, dtype)
+        total += h @ values64(ws2[s]).T
+    return round_storage(total, dtype)
+
+
+# ----------------------------------------------------------------------------
+# combine (section 1 "combine_postprocess: unpermute-1, weighted reduce")
+# ----------------------------------------------------------------------------
+
+def combine(y_perm, dst_row, topk_w, dtype: str, shared=None):
+    """out[t] = sum_j w[t,j] * Y[dst_row[t,j]] over slots j in order (skipping -1),
+    plus shared[t]; float64, stored once in the layer dtype."""
+    Y = values64(y_perm)
+    dst = np.asarray(dst_row, dtype=np.int64)
+    w = np.asarray(topk_w, dtype=np.float64)
+    T, k = dst.shape
+    out = np.zeros((T, Y.shape[1]), dtype=np.float64)
+    for j in range(k):
+        ok = dst[:, j] >= 0
+        out[ok] += w[ok, j:j + 1] * Y[dst[ok, j]]
+    if shared is not None:
+        out += values64(shared)
+    return round_storage(out, dtype)
+
+
+# ----------------------------------------------------------------------------
+# whole layer
+# ----------------------------------------------------------------------------
+
+def forward(inputs: dict, k: int, m_tile: int, dtype: str, renorm: bool = False,
+            m_cap: Optional[int] = None) -> dict:
+    """Every intermediate of the layer on ``inputs`` (keys as produced by the input
+    generator: x, wg or topk_idx/topk_w, w1, w3, w2, optional bias, ws1/ws3/ws2)."""
+    x = inputs["x"]
+    E = inputs["w1"].shape[0]
+    res: dict = {}
+    if "topk_idx" in inputs:
+        idx = np.asarray(inputs["topk_idx"], dtype=np.int32)
+        w = np.asarray(inputs["topk_w"], dtype=np.float64)
+    else:
+        idx, w, logits = route(x, inputs["wg"], k, dtype, inputs.get("bias"), renorm)
+        res["logits"] = logits
+    res["topk_idx"], res["topk_w"] = idx, w
+    lay = dispatch_layout(idx, E, m_tile, m_cap)
+    res.update(lay)
+    xp = permute(x, lay)
+    res["x_perm"] = xp
+    h, y = grouped_swiglu(xp, lay["offsets"], inputs["w1"], inputs["w3"], inputs["w2"], dtype)
+    res["h"], res["y_perm"] = h, y
+    shared = None
+    if "ws1" in inputs:
+        shared = shared_experts(x, inputs["ws1"], inputs["ws3"], inputs["ws2"], dtype)
+        res["shared"] = shared
+    res["out"] = combine(y, lay["dst_row"], w, dtype, shared)
+    return res
+
+
+def token_outputs(tokens, x, topk_idx, topk_w, w1, w3, w2, dtype: str, shared_w=None):
+    """Layer output of selected tokens only, without building the permuted buffer.
+
+    A row's expert output depends on that row alone, so out[t] is
+    sum_j w[t,j] * FFN_{idx[t,j]}(x[t]) (+ the shared experts on x[t]); the stored
+    rounding points are the same as in ``forward``. Returns (out [n,D],
+    h {(t,j): [F]}, y {(t,j): [D]})."""
+    tokens = np.asarray(tokens, dtype=np.int64)
+    idx = np.asarray(topk_idx, dtype=np.int64)
+    w = np.asarray(topk_w, dtype=np.float64)
+    D = x.shape[1]
+    out = np.zeros((tokens.size, D), dtype=np.float64)
+    hs, ys = {}, {}
+    for e in np.unique(idx[tokens]):
+        if e < 0:
+            continue
+        rows = [(i, j) for i, t in enumerate(tokens) for j in range(idx.shape[1]) if idx[t, j] == e]
+        A = np.stack([x[tokens[i]] for i, _ in rows])
+        h, y = expert_swiglu(A, w1[e], w3[e], w2[e], dtype)
+        for r, (i, j) in enumerate(rows):
+            hs[(int(tokens[i]), j)] = h[r]
+            ys[(int(tokens[i]), j)] = y[r]
+    for i, t in enumerate(tokens):
+        for j in range(idx.shape[1]):
+            if idx[t, j] >= 0:
+                out[i] += w[t, j] * ys[(int(t), j)]
+    if shared_w is not None:
+        out += shared_experts(x[tokens], *shared_w, dtype)
+    return round_storage(out, dtype), hs, ys

@@ -1,0 +1,106 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check that a pin catches each.
+
+Every mutation is applied with monkeypatch to the oracle module only; the pins are the
+checks in test_oracle_pins.py.
+"""
+import numpy as np
+import pytest
+
+from oracle import moe_oracle as orc
+from tests import test_oracle_pins as pins
+
+
+def _swapped_gate_up(A, w1e, w3e, w2e, dtype):
+    A64 = orc.values64(A)
+    a = A64 @ orc.values64(w1e).T
+    b = A64 @ orc.values64(w3e).T
+    h = orc.round_storage(orc.silu(b) * a, dtype)             # w1 and w3 roles swapped
+    return h, orc.round_storage(h @ orc.values64(w2e).T, dtype)
+
+
+def _no_silu(A, w1e, w3e, w2e, dtype):
+    A64 = orc.values64(A)
+    h = (A64 @ orc.values64(w1e).T) * (A64 @ orc.values64(w3e).T)   # activation dropped
+    return h, h @ orc.values64(w2e).T
+
+
+def _ties_high(logits, k):
+    l = np.asarray(logits)
+    order = np.argsort(-l[:, ::-1], axis=1, kind="stable")
+    return (l.shape[1] - 1 - order[:, :k]).astype(np.int32)    # ties to the higher index
+
+
+def _ascending(logits, k):
+    return np.argsort(logits, axis=1, kind="stable")[:, :k].astype(np.int32)  # sign flipped
+
+
+def _unweighted_combine(y_perm, dst_row, topk_w, dtype, shared=None):
+    return orc.__dict__["_orig_combine"](y_perm, dst_row, np.ones_like(topk_w), dtype, shared)
+
+
+def _softmax_over_selected_only(x, wg, k, dtype, bias=None, renorm=False):
+    idx, _, logits = orc.__dict__["_orig_route"](x, wg, k, dtype, bias, renorm)
+    sel = np.take_along_axis(logits.astype(np.float64), idx.astype(np.int64), axis=1)
+    z = np.exp(sel - sel.max(1, keepdims=True))
+    return idx, z / z.sum(1, keepdims=True), logits
+
+
+def _bias_dropped(x, wg, dtype, bias=None):
+    return orc.__dict__["_orig_router_logits"](x, wg, dtype, None)
+
+
+def _unstable_layout(topk_idx, E, m_tile, m_cap=None):
+    lay = orc.__dict__["_orig_dispatch_layout"](topk_idx, E, m_tile, m_cap)
+    # reverse the order of slots inside every segment (an unstable sort)
+    src, dst = lay["src_row"].copy(), lay["dst_row"].copy()
+    off, c = lay["offsets"], lay["counts"]
+    k = dst.shape[1]
+    for e in range(E):
+        seg = src[off[e]:off[e] + c[e]][::-1].copy()
+        src[off[e]:off[e] + c[e]] = seg
+        for r, f in enumerate(seg):
+            dst[f // k, f % k] = off[e] + r
+    lay["src_row"], lay["dst_row"] = src, dst
+    return lay
+
+
+def _first_expert_only_counts(topk_idx, E, m_tile, m_cap=None):
+    return orc.__dict__["_orig_dispatch_layout"](np.asarray(topk_idx)[:, :1], E, m_tile, m_cap)
+
+
+MUTATIONS = {
+    "swapped_gate_up": ("expert_swiglu", _swapped_gate_up, "brute"),
+    "no_silu": ("expert_swiglu", _no_silu, "brute"),
+    "ties_high": ("select_topk", _ties_high, "ties"),
+    "ascending": ("select_topk", _ascending, "brute"),
+    "unweighted_combine": ("combine", _unweighted_combine, "brute"),
+    "softmax_over_selected": ("route", _softmax_over_selected_only, "brute"),
+    "bias_dropped": ("router_logits", _bias_dropped, "brute_bias"),
+    "unstable_layout": ("dispatch_layout", _unstable_layout, "layout"),
+    "first_slot_only": ("dispatch_layout", _first_expert_only_counts, "layout"),
+}
+
+
+def _run_pin(kind):
+    if kind == "brute":
+        pins._check_layer_against_brute(orc, 0, k=2)
+    elif kind == "brute_bias":
+        pins._check_layer_against_brute(orc, 5, k=3, bias=True, shared=True)
+    elif kind == "ties":
+        pins.test_topk_matches_python_sorted_with_ties()
+    elif kind == "layout":
+        pins.test_layout_matches_loop_counting_sort(50, 3, 7, 4, False)
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_planted_mistake_is_caught(name, monkeypatch):
+    attr, fn, kind = MUTATIONS[name]
+    monkeypatch.setitem(orc.__dict__, "_orig_" + attr, getattr(orc, attr))
+    monkeypatch.setattr(orc, attr, fn)
+    with pytest.raises((AssertionError, ValueError, IndexError)):
+        _run_pin(kind)
+
+
+def test_unmutated_pins_pass():
+    for kind in ("brute", "brute_bias", "ties", "layout"):
+        _run_pin(kind)
