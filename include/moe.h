@@ -1,0 +1,158 @@
+/*
+ * moe.h - C ABI of the single-GPU MoE expert-layer path on AMD MI355X (gfx950).
+ *
+ * The layer (page "Expert Parallelism (EP)", llm-infra-atlas, section 1
+ * "MoE layer 的 forward 通路") runs four calls in order:
+ *
+ *   moe_route           router gating and softmax-then-top-k routing
+ *   moe_permute         tokens-per-expert metadata and the expert-contiguous,
+ *                       M-tile-aligned permuted activations
+ *   moe_grouped_swiglu  m-grouped fc1 (w1, w3) -> silu(a)*b -> fc2 (w2)
+ *   moe_combine         unpermute and top-k-weighted reduce back to token order
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Pointers named as device buffers are HIP device memory, 16-byte aligned.
+ *   The caller allocates and owns every buffer (outputs and scratch included).
+ *   The library never allocates or frees memory and keeps no state between
+ *   calls except a per-device cache of the compute-unit count.
+ * - `stream` is a hipStream_t (NULL = the legacy default stream). A call only
+ *   enqueues kernels on it; it never synchronises. Calls are re-entrant.
+ * - Dense arrays are row-major and contiguous. All float buffers of one call
+ *   share `dt`; topk_w, logits and bias are always float32; indices int32.
+ *   bf16 is stored as its 16-bit pattern.
+ * - Arguments are validated on the host before any HIP call, so a bad call
+ *   returns an error without touching the GPU. Device data that is wrong
+ *   (an expert index outside [-1, E)) never causes an out-of-bounds access:
+ *   the slot is skipped and moe_permute reports it through *dev_err.
+ * - Sizes: T >= 1; D, F multiples of 64; E in [1, 64] for moe_route and
+ *   [1, 1024] elsewhere; k in [1, min(E, 32)]; m_tile in {16,32,64,128,256}.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_EINVAL = 1,       /* null or misaligned pointer, unknown dtype/flag           */
+  MOE_ESHAPE = 2,       /* a size outside the ranges above                          */
+  MOE_ECAPACITY = 3,    /* m_cap < moe_capacity(...) or m_cap % m_tile != 0         */
+  MOE_EWORKSPACE = 4,   /* workspace smaller than moe_permute_workspace_bytes(...)  */
+  MOE_EHIP = 5,         /* the HIP runtime reported an error while launching        */
+  MOE_EUNSUPPORTED = 6  /* valid request with no kernel in this build (see below)   */
+} moe_status_t;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype_t;
+
+/*
+ * moe_route - router gating and routing ("Expert Parallelism (EP)", section 1:
+ * "router.gating: logits = x @ W_g^T" then "routing: top-k + score_func ->
+ * probs, routing_map").
+ *
+ *   x [T,D] (dt), wg [E,D] (dt), bias [E] float32 or NULL
+ *   -> topk_idx [T,k] int32, topk_w [T,k] float32, logits [T,E] float32 or NULL
+ *
+ * logits[t,e] = sum_d x[t,d]*wg[e,d] (+ bias[e]) in float32 with a fixed order
+ * so that the selection is reproducible bit for bit: elements are taken in
+ * 16-byte chunks (4 float32 or 8 bf16 values); chunk c belongs to lane c % 64;
+ * each lane accumulates its chunks' products in increasing d, starting from
+ * +0 (float32: a rounded multiply then a rounded add; bf16: a fused
+ * multiply-add, identical because a bf16*bf16 product is exact in float32
+ * unless it underflows below 2^-126); the 64 lane sums are then combined by a
+ * butterfly over lane distances 32,16,8,4,2,1; the bias is added last.
+ * Score: softmax over all E logits. Selection: the k largest logits, best
+ * first, ties to the lower expert index. topk_w[t,j] = softmax probability of
+ * topk_idx[t,j] (renorm = 1 divides the k weights by their sum).
+ * Errors: MOE_EINVAL, MOE_ESHAPE (E > 64 or k > E), MOE_EHIP.
+ */
+moe_status_t moe_route(moe_dtype_t dt, const void* x, const void* wg, const float* bias,
+                       int T, int D, int E, int k, int renorm,
+                       int32_t* topk_idx, float* topk_w, float* logits, void* stream);
+
+/*
+ * moe_permute - dispatch metadata and permute ("Expert Parallelism (EP)",
+ * section 1 "preprocess: tokens_per_expert" and "permute ... each local
+ * expert's tokens contiguous"; section 2: the layout contract, every expert
+ * segment aligned to the GEMM M tile; section 5: permute is an index_select).
+ *
+ *   x [T,D] (dt), topk_idx [T,k] int32 (-1 = slot not handled here)
+ *   -> counts [E]        rows of each expert
+ *      offsets [E+1]     exclusive prefix sum of ceil(counts/m_tile)*m_tile
+ *      dst_row [T,k]     row of slot (t,j) in x_perm, -1 for skipped slots
+ *      src_row [m_cap]   t*k+j of the slot held by each row, -1 for pad/unused
+ *      tile_expert [m_cap/m_tile]  expert of each m_tile-row tile, -1 past offsets[E]
+ *      x_perm [m_cap,D]  x_perm[dst_row[t,j]] = x[t]; pad rows inside a segment
+ *                        are zero; rows >= offsets[E] are not written
+ *      *dev_err          1 if some topk_idx value lies outside [-1, E), else 0
+ * Rows of one expert follow the flat slot order t*k+j (a stable sort).
+ * workspace: device scratch of at least moe_permute_workspace_bytes(T,k,E).
+ * Errors: MOE_EINVAL, MOE_ESHAPE, MOE_ECAPACITY, MOE_EWORKSPACE, MOE_EHIP.
+ */
+moe_status_t moe_permute(moe_dtype_t dt, const void* x, const int32_t* topk_idx,
+                         int T, int D, int E, int k, int m_tile, int64_t m_cap,
+                         void* x_perm, int32_t* counts, int32_t* offsets,
+                         int32_t* dst_row, int32_t* src_row, int32_t* tile_expert,
+                         void* workspace, size_t ws_bytes, int32_t* dev_err, void* stream);
+
+/*
+ * moe_grouped_swiglu - the m-grouped expert GEMMs ("Expert Parallelism (EP)",
+ * section 1 "routed_experts_compute: fc1 -> act -> fc2, grouped GEMM
+ * (m-grouped)" and section 2: one kernel over same-shape expert GEMMs whose
+ * row counts differ, scheduled across groups; weight layout from the
+ * "Expert Tensor Parallel" design note, section 4.3: w1, w3 [E,F,D], w2 [E,D,F]).
+ *
+ *   x_perm [m_cap,D], offsets [E+1], tile_expert [m_cap/m_tile] (from moe_permute)
+ *   w1, w3 [E,F,D], w2 [E,D,F]
+ *   -> h [m_cap,F]       h = silu(x_perm w1[e]^T) * (x_perm w3[e]^T), stored in dt
+ *      y_perm [m_cap,D]  y = h w2[e]^T, stored in dt
+ * for the rows [offsets[e], offsets[e+1]) of every expert e; float32
+ * accumulation; rows >= offsets[E] are neither read nor written. Pad rows
+ * (zero in x_perm) give exact zeros. offsets[e] for e < E must be multiples of
+ * m_tile; offsets[E] may be any value <= m_cap (so a dense FFN over T tokens is
+ * the call with E = 1, offsets = {0, T}, tile_expert all 0).
+ * bf16 needs m_tile in {128, 256}; float32 accepts every m_tile.
+ * Errors: MOE_EINVAL, MOE_ESHAPE, MOE_ECAPACITY (m_cap % m_tile),
+ * MOE_EUNSUPPORTED, MOE_EHIP.
+ */
+moe_status_t moe_grouped_swiglu(moe_dtype_t dt, const void* x_perm, const int32_t* offsets,
+                                const int32_t* tile_expert, int E, int D, int F, int m_tile,
+                                int64_t m_cap, const void* w1, const void* w3, const void* w2,
+                                void* h, void* y_perm, void* stream);
+
+/*
+ * moe_combine - unpermute and weighted reduce ("Expert Parallelism (EP)",
+ * section 1 "combine_postprocess: unpermute-1, weighted by the top-k weights,
+ * reduce back to the original order" plus the shared experts; section 5:
+ * unpermute is a scatter_add, the transpose of the permute).
+ *
+ *   y_perm [m_cap,D], dst_row [T,k], topk_w [T,k] float32, shared [T,D] or NULL
+ *   -> out [T,D]: out[t] = sum_j topk_w[t,j] * y_perm[dst_row[t,j]] (+ shared[t]),
+ *      slots in order j, float32 accumulation, one rounding to dt.
+ * Slots whose dst_row is outside [0, m_cap) are skipped.
+ * Errors: MOE_EINVAL, MOE_ESHAPE, MOE_EHIP.
+ */
+moe_status_t moe_combine(moe_dtype_t dt, const void* y_perm, const int32_t* dst_row,
+                         const float* topk_w, const void* shared, int T, int D, int k,
+                         int64_t m_cap, void* out, void* stream);
+
+/* Worst-case rows of the permuted buffer: with N = T*k slots,
+ * m_tile * floor((N + min(E, N) * (m_tile - 1)) / m_tile). Returns -1 on bad sizes. */
+int64_t moe_capacity(int T, int k, int E, int m_tile);
+
+/* Device scratch bytes moe_permute needs for (T, k, E). Returns 0 on bad sizes. */
+size_t moe_permute_workspace_bytes(int T, int k, int E);
+
+/* Static text of a status code. */
+const char* moe_status_str(moe_status_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

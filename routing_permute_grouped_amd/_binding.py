@@ -1,0 +1,176 @@
+"""ctypes binding of libmoe_mi355x.so: argument marshalling only.
+
+Every step of the layer runs in the library's HIP kernels; PyTorch supplies device
+memory and the current HIP stream. Output buffers not passed in are allocated with
+torch on the input's device. There is no fallback: if the library is missing the
+import fails.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoe_mi355x.so")
+
+MOE_F32, MOE_BF16 = 0, 1
+_STATUS = {0: "MOE_OK", 1: "MOE_EINVAL", 2: "MOE_ESHAPE", 3: "MOE_ECAPACITY",
+           4: "MOE_EWORKSPACE", 5: "MOE_EHIP", 6: "MOE_EUNSUPPORTED"}
+
+# (name, restype, argtypes) of every symbol include/moe.h declares
+_P, _I, _I64, _SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+SIGNATURES = [
+    ("moe_route", _I, [_I, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P]),
+    ("moe_permute", _I, [_I, _P, _P, _I, _I, _I, _I, _I, _I64, _P, _P, _P, _P, _P, _P, _P, _SZ,
+                         _P, _P]),
+    ("moe_grouped_swiglu", _I, [_I, _P, _P, _P, _I, _I, _I, _I, _I64, _P, _P, _P, _P, _P, _P]),
+    ("moe_combine", _I, [_I, _P, _P, _P, _P, _I, _I, _I, _I64, _P, _P]),
+    ("moe_capacity", _I64, [_I, _I, _I, _I]),
+    ("moe_permute_workspace_bytes", _SZ, [_I, _I, _I]),
+    ("moe_status_str", ctypes.c_char_p, [_I]),
+]
+
+
+class MoEError(RuntimeError):
+    def __init__(self, fn: str, status: int, text: str):
+        super().__init__(f"{fn}: {_STATUS.get(status, status)} ({text})")
+        self.status = status
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m routing_permute_grouped_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, res, args in SIGNATURES:
+        fn = getattr(lib, name)
+        fn.restype, fn.argtypes = res, args
+    return lib
+
+
+lib = _load()
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise MoEError(fn, status, lib.moe_status_str(status).decode())
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return MOE_F32
+    if t.dtype == torch.bfloat16:
+        return MOE_BF16
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensor must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def moe_capacity(T: int, k: int, E: int, m_tile: int) -> int:
+    return int(lib.moe_capacity(T, k, E, m_tile))
+
+
+def moe_permute_workspace_bytes(T: int, k: int, E: int) -> int:
+    return int(lib.moe_permute_workspace_bytes(T, k, E))
+
+
+def moe_status_str(status: int) -> str:
+    return lib.moe_status_str(status).decode()
+
+
+def moe_route(x: torch.Tensor, wg: torch.Tensor, k: int, bias: Optional[torch.Tensor] = None,
+              renorm: bool = False, want_logits: bool = False, topk_idx=None, topk_w=None,
+              logits=None, stream=None) -> Tuple[torch.Tensor, torch.Tensor, Optional[torch.Tensor]]:
+    T, D = x.shape
+    E = wg.shape[0]
+    dev = x.device
+    if topk_idx is None:
+        topk_idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    if topk_w is None:
+        topk_w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    if logits is None and want_logits:
+        logits = torch.empty((T, E), dtype=torch.float32, device=dev)
+    if wg.dtype != x.dtype:
+        raise TypeError("x and wg must share a dtype")
+    _check("moe_route", lib.moe_route(_dt(x), _ptr(x), _ptr(wg), _ptr(bias), T, D, E, k,
+                                      int(renorm), _ptr(topk_idx), _ptr(topk_w), _ptr(logits),
+                                      _stream(stream)))
+    return topk_idx, topk_w, logits
+
+
+def moe_permute(x: torch.Tensor, topk_idx: torch.Tensor, E: int, m_tile: int,
+                m_cap: Optional[int] = None, out: Optional[dict] = None, stream=None) -> dict:
+    """Returns dict with x_perm, counts, offsets, dst_row, src_row, tile_expert, dev_err,
+    workspace and m_cap. Buffers given in ``out`` are reused."""
+    T, D = x.shape
+    k = topk_idx.shape[1]
+    dev = x.device
+    if m_cap is None:
+        m_cap = moe_capacity(T, k, E, m_tile)
+    o = dict(out or {})
+    i32 = dict(dtype=torch.int32, device=dev)
+    o.setdefault("x_perm", torch.empty((m_cap, D), dtype=x.dtype, device=dev))
+    o.setdefault("counts", torch.empty(E, **i32))
+    o.setdefault("offsets", torch.empty(E + 1, **i32))
+    o.setdefault("dst_row", torch.empty((T, k), **i32))
+    o.setdefault("src_row", torch.empty(m_cap, **i32))
+    o.setdefault("tile_expert", torch.empty(m_cap // m_tile, **i32))
+    o.setdefault("dev_err", torch.empty(1, **i32))
+    ws = max(4, moe_permute_workspace_bytes(T, k, E))
+    o.setdefault("workspace", torch.empty(ws, dtype=torch.uint8, device=dev))
+    _check("moe_permute", lib.moe_permute(
+        _dt(x), _ptr(x), _ptr(topk_idx), T, D, E, k, m_tile, m_cap, _ptr(o["x_perm"]),
+        _ptr(o["counts"]), _ptr(o["offsets"]), _ptr(o["dst_row"]), _ptr(o["src_row"]),
+        _ptr(o["tile_expert"]), _ptr(o["workspace"]), o["workspace"].numel(), _ptr(o["dev_err"]),
+        _stream(stream)))
+    o["m_cap"] = m_cap
+    return o
+
+
+def moe_grouped_swiglu(x_perm: torch.Tensor, offsets: torch.Tensor, tile_expert: torch.Tensor,
+                       w1: torch.Tensor, w3: torch.Tensor, w2: torch.Tensor, m_tile: int,
+                       m_cap: Optional[int] = None, h: Optional[torch.Tensor] = None,
+                       y_perm: Optional[torch.Tensor] = None, stream=None):
+    E, F, D = w1.shape
+    if m_cap is None:
+        m_cap = x_perm.shape[0]
+    dev = x_perm.device
+    if h is None:
+        h = torch.empty((m_cap, F), dtype=x_perm.dtype, device=dev)
+    if y_perm is None:
+        y_perm = torch.empty((m_cap, D), dtype=x_perm.dtype, device=dev)
+    _check("moe_grouped_swiglu", lib.moe_grouped_swiglu(
+        _dt(x_perm), _ptr(x_perm), _ptr(offsets), _ptr(tile_expert), E, D, F, m_tile, m_cap,
+        _ptr(w1), _ptr(w3), _ptr(w2), _ptr(h), _ptr(y_perm), _stream(stream)))
+    return h, y_perm
+
+
+def moe_combine(y_perm: torch.Tensor, dst_row: torch.Tensor, topk_w: torch.Tensor,
+                shared: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                m_cap: Optional[int] = None, stream=None) -> torch.Tensor:
+    T, k = dst_row.shape
+    D = y_perm.shape[1]
+    if m_cap is None:
+        m_cap = y_perm.shape[0]
+    if out is None:
+        out = torch.empty((T, D), dtype=y_perm.dtype, device=y_perm.device)
+    _check("moe_combine", lib.moe_combine(
+        _dt(y_perm), _ptr(y_perm), _ptr(dst_row), _ptr(topk_w), _ptr(shared), T, D, k, m_cap,
+        _ptr(out), _stream(stream)))
+    return out

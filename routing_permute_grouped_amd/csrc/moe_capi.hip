@@ -1,0 +1,134 @@
+// C ABI entry points: host-side validation, then the kernel launchers.
+// Every check runs before any HIP call, so a rejected call never touches the GPU.
+#include <hip/hip_runtime.h>
+
+#include <mutex>
+
+#include "moe.h"
+#include "kernels.hpp"
+
+namespace moe {
+
+int cu_count() {
+  static std::mutex mu;
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  std::lock_guard<std::mutex> lock(mu);
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+}  // namespace moe
+
+namespace {
+
+constexpr int kMaxExpertsRoute = 64;
+constexpr int kMaxExperts = 1024;
+constexpr int kMaxK = 32;
+constexpr int kMaxDim = 1 << 16;
+
+bool aligned16(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+bool dim_ok(int d) { return d >= 64 && d <= kMaxDim && d % 64 == 0; }
+bool mtile_ok(int mt) { return mt == 16 || mt == 32 || mt == 64 || mt == 128 || mt == 256; }
+bool dtype_ok(int dt) { return dt == MOE_F32 || dt == MOE_BF16; }
+bool tk_ok(int T, int k) { return T >= 1 && (int64_t)T * k <= (1 << 30); }
+
+moe_status_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
+
+}  // namespace
+
+extern "C" {
+
+int64_t moe_capacity(int T, int k, int E, int m_tile) {
+  if (T < 1 || k < 1 || E < 1 || !mtile_ok(m_tile) || !tk_ok(T, k)) return -1;
+  const int64_t N = (int64_t)T * k;
+  const int64_t ne = E < N ? E : N;
+  return (N + ne * (m_tile - 1)) / m_tile * m_tile;
+}
+
+size_t moe_permute_workspace_bytes(int T, int k, int E) {
+  if (T < 1 || k < 1 || E < 1 || E > kMaxExperts || !tk_ok(T, k)) return 0;
+  return moe::permute_workspace_bytes(T, k, E);
+}
+
+const char* moe_status_str(moe_status_t s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_EINVAL: return "invalid argument (null or misaligned pointer, unknown dtype or flag)";
+    case MOE_ESHAPE: return "size outside the supported range";
+    case MOE_ECAPACITY: return "m_cap below the worst-case capacity or not a multiple of m_tile";
+    case MOE_EWORKSPACE: return "workspace smaller than moe_permute_workspace_bytes";
+    case MOE_EHIP: return "HIP runtime error while launching";
+    case MOE_EUNSUPPORTED: return "no kernel for this combination in this build";
+  }
+  return "unknown status";
+}
+
+moe_status_t moe_route(moe_dtype_t dt, const void* x, const void* wg, const float* bias, int T,
+                       int D, int E, int k, int renorm, int32_t* topk_idx, float* topk_w,
+                       float* logits, void* stream) {
+  if (!dtype_ok(dt) || !aligned16(x) || !aligned16(wg) || !aligned4(topk_idx) || !aligned4(topk_w))
+    return MOE_EINVAL;
+  if ((bias && !aligned4(bias)) || (logits && !aligned4(logits))) return MOE_EINVAL;
+  if (renorm != 0 && renorm != 1) return MOE_EINVAL;
+  if (!tk_ok(T, k) || !dim_ok(D) || E < 1 || E > kMaxExpertsRoute || k < 1 || k > E || k > kMaxK)
+    return MOE_ESHAPE;
+  return hip_status(moe::launch_route(dt, x, wg, bias, T, D, E, k, renorm, topk_idx, topk_w,
+                                      logits, static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_permute(moe_dtype_t dt, const void* x, const int32_t* topk_idx, int T, int D,
+                         int E, int k, int m_tile, int64_t m_cap, void* x_perm, int32_t* counts,
+                         int32_t* offsets, int32_t* dst_row, int32_t* src_row,
+                         int32_t* tile_expert, void* workspace, size_t ws_bytes, int32_t* dev_err,
+                         void* stream) {
+  if (!dtype_ok(dt) || !aligned16(x) || !aligned16(x_perm) || !aligned4(topk_idx) ||
+      !aligned4(counts) || !aligned4(offsets) || !aligned4(dst_row) || !aligned4(src_row) ||
+      !aligned4(tile_expert) || !aligned4(workspace) || !aligned4(dev_err))
+    return MOE_EINVAL;
+  if (!tk_ok(T, k) || !dim_ok(D) || E < 1 || E > kMaxExperts || k < 1 || k > E || k > kMaxK ||
+      !mtile_ok(m_tile))
+    return MOE_ESHAPE;
+  const int64_t need = moe_capacity(T, k, E, m_tile);
+  if (m_cap < need || m_cap % m_tile != 0 || m_cap > INT32_MAX) return MOE_ECAPACITY;
+  if (ws_bytes < moe::permute_workspace_bytes(T, k, E)) return MOE_EWORKSPACE;
+  return hip_status(moe::launch_permute(dt, x, topk_idx, T, D, E, k, m_tile, m_cap, x_perm,
+                                        counts, offsets, dst_row, src_row, tile_expert, workspace,
+                                        dev_err, static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_grouped_swiglu(moe_dtype_t dt, const void* x_perm, const int32_t* offsets,
+                                const int32_t* tile_expert, int E, int D, int F, int m_tile,
+                                int64_t m_cap, const void* w1, const void* w3, const void* w2,
+                                void* h, void* y_perm, void* stream) {
+  if (!dtype_ok(dt) || !aligned16(x_perm) || !aligned4(offsets) || !aligned4(tile_expert) ||
+      !aligned16(w1) || !aligned16(w3) || !aligned16(w2) || !aligned16(h) || !aligned16(y_perm))
+    return MOE_EINVAL;
+  if (E < 1 || E > kMaxExperts || !dim_ok(D) || !dim_ok(F) || !mtile_ok(m_tile)) return MOE_ESHAPE;
+  if (m_cap < 1 || m_cap % m_tile != 0 || m_cap > INT32_MAX) return MOE_ECAPACITY;
+  if (dt == MOE_BF16 && m_tile != 128 && m_tile != 256) return MOE_EUNSUPPORTED;
+  return hip_status(moe::launch_grouped_swiglu(dt, x_perm, offsets, tile_expert, E, D, F, m_tile,
+                                               m_cap, w1, w3, w2, h, y_perm,
+                                               static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_combine(moe_dtype_t dt, const void* y_perm, const int32_t* dst_row,
+                         const float* topk_w, const void* shared, int T, int D, int k,
+                         int64_t m_cap, void* out, void* stream) {
+  if (!dtype_ok(dt) || !aligned16(y_perm) || !aligned4(dst_row) || !aligned4(topk_w) ||
+      !aligned16(out) || (shared && !aligned16(shared)))
+    return MOE_EINVAL;
+  if (!tk_ok(T, k) || !dim_ok(D) || k < 1 || k > kMaxK || m_cap < 1 || m_cap > INT32_MAX)
+    return MOE_ESHAPE;
+  return hip_status(moe::launch_combine(dt, y_perm, dst_row, topk_w, shared, T, D, k, m_cap, out,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

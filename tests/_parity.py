@@ -1,0 +1,113 @@
+"""Helpers of the GPU parity tests: upload seeded inputs, run the four library calls,
+download the results and compare them with the oracle."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import routing_permute_grouped_amd as rpg
+from oracle import moe_oracle as orc
+
+TOL = {"f32": 1e-5, "bf16": 2e-2}   # max|gpu - ref| / max|ref| (fp32 / bf16 with fp32 accumulate)
+W_RTOL = 1e-6                        # top-k weights: float32 softmax against float64
+
+
+def log(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(a: np.ndarray) -> torch.Tensor:
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(a).cuda()
+
+
+def to_host(t: torch.Tensor) -> np.ndarray:
+    if t.dtype == torch.bfloat16:
+        return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.contiguous().cpu().numpy()
+
+
+def rel_err(got, ref) -> float:
+    g, r = orc.values64(got), np.asarray(ref, dtype=np.float64)
+    den = np.abs(r).max()
+    return float(np.abs(g - r).max() / (den if den > 0 else 1.0))
+
+
+def poison(t: torch.Tensor) -> torch.Tensor:
+    return t.fill_(float("nan"))
+
+
+def run_gpu(inp: dict, k: int, m_tile: int, renorm: bool = False, want_logits: bool = True) -> dict:
+    """Run route (unless routing is given), permute, grouped SwiGLU (routed and shared)
+    and combine; every float output buffer is NaN-poisoned first."""
+    d = {n: to_dev(a) for n, a in inp.items() if isinstance(a, np.ndarray)}
+    E = inp["w1"].shape[0]
+    T = inp["x"].shape[0]
+    out: dict = {}
+    if "topk_idx" in inp:
+        idx, w = d["topk_idx"], d["topk_w"]
+    else:
+        idx, w, logits = rpg.moe_route(d["x"], d["wg"], k, bias=d.get("bias"), renorm=renorm,
+                                       want_logits=want_logits)
+        out["logits"] = logits
+    out["topk_idx"], out["topk_w"] = idx, w
+    m_cap = rpg.moe_capacity(T, k, E, m_tile)
+    xp = poison(torch.empty((m_cap, inp["x"].shape[1]), dtype=d["x"].dtype, device="cuda"))
+    p = rpg.moe_permute(d["x"], idx, E, m_tile, m_cap=m_cap, out={"x_perm": xp})
+    out.update(p)
+    F = inp["w1"].shape[1]
+    h = poison(torch.empty((m_cap, F), dtype=d["x"].dtype, device="cuda"))
+    y = poison(torch.empty((m_cap, inp["x"].shape[1]), dtype=d["x"].dtype, device="cuda"))
+    rpg.moe_grouped_swiglu(p["x_perm"], p["offsets"], p["tile_expert"], d["w1"], d["w3"], d["w2"],
+                           m_tile, m_cap=m_cap, h=h, y_perm=y)
+    out["h"], out["y_perm"] = h, y
+    shared = None
+    if "ws1" in d:
+        sw = rpg.SharedExperts.from_stacked(d["ws1"], d["ws3"], d["ws2"])
+        rows = rpg.DenseRows(T, m_tile, "cuda")
+        hs = poison(torch.empty((rows.m_cap, sw.w1.shape[1]), dtype=d["x"].dtype, device="cuda"))
+        ys = poison(torch.empty((rows.m_cap, inp["x"].shape[1]), dtype=d["x"].dtype, device="cuda"))
+        rpg.moe_grouped_swiglu(d["x"], rows.offsets, rows.tile_expert, sw.w1, sw.w3, sw.w2, m_tile,
+                               m_cap=rows.m_cap, h=hs, y_perm=ys)
+        shared = ys[:T]
+        out["shared"] = shared
+    o = poison(torch.empty_like(d["x"]))
+    out["out"] = rpg.moe_combine(y, p["dst_row"], w, shared=shared, out=o, m_cap=m_cap)
+    torch.cuda.synchronize()
+    return {kk: (to_host(v) if isinstance(v, torch.Tensor) else v) for kk, v in out.items()}
+
+
+def check_layer(inp: dict, k: int, m_tile: int, dtype: str, renorm: bool = False,
+                expect_dev_err: int = 0) -> dict:
+    """Full element-by-element parity of every output of the layer against the oracle."""
+    ref = orc.forward(inp, k=k, m_tile=m_tile, dtype=dtype, renorm=renorm)
+    g = run_gpu(inp, k, m_tile, renorm)
+    tol = TOL[dtype]
+    if "logits" in ref:
+        np.testing.assert_array_equal(g["logits"].view(np.uint32), ref["logits"].view(np.uint32))
+        np.testing.assert_array_equal(g["topk_idx"], ref["topk_idx"])
+        np.testing.assert_allclose(g["topk_w"], ref["topk_w"], rtol=W_RTOL, atol=0)
+    for key in ("counts", "offsets", "dst_row", "src_row", "tile_expert"):
+        np.testing.assert_array_equal(g[key], ref[key], err_msg=key)
+    assert int(g["dev_err"][0]) == expect_dev_err
+    used = int(ref["offsets"][-1])
+    np.testing.assert_array_equal(g["x_perm"][:used], ref["x_perm"][:used])
+    for key in ("h", "y_perm"):
+        vals = orc.values64(g[key][:used])
+        assert np.all(np.isfinite(vals)), f"{key}: unwritten rows"
+        pad = ref["src_row"][:used] < 0
+        assert np.all(vals[pad] == 0), f"{key}: pad rows not zero"
+        e = rel_err(g[key][:used], ref[key][:used])
+        assert e <= tol, f"{key}: rel err {e:.3e} > {tol}"
+    if "shared" in ref:
+        e = rel_err(g["shared"], ref["shared"])
+        assert e <= tol, f"shared: rel err {e:.3e}"
+    assert np.all(np.isfinite(orc.values64(g["out"])))
+    e = rel_err(g["out"], ref["out"])
+    assert e <= tol, f"out: rel err {e:.3e} > {tol}"
+    return g

@@ -1,0 +1,126 @@
+"""Host-side checks of the C ABI: the library loads, exports every declared symbol, and
+rejects bad arguments before touching the GPU. No call here reaches a kernel launch:
+every argument set below is invalid, and validation runs before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import routing_permute_grouped_amd as rpg
+from oracle import moe_oracle as orc
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "moe.h")
+
+MOE_OK, MOE_EINVAL, MOE_ESHAPE, MOE_ECAPACITY, MOE_EWORKSPACE, MOE_EUNSUPPORTED = 0, 1, 2, 3, 4, 6
+FAKE = 0x10000   # aligned, non-null; never dereferenced because every call is rejected
+lib = rpg.lib
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^(?![\s/*#])[^\n(]*?\b(moe_[a-z_]+)\(", text, re.M)))
+
+
+def test_header_declares_the_four_calls_and_helpers():
+    assert declared_symbols() == sorted(["moe_route", "moe_permute", "moe_grouped_swiglu",
+                                         "moe_combine", "moe_capacity",
+                                         "moe_permute_workspace_bytes", "moe_status_str"])
+
+
+def test_library_exports_every_declared_symbol():
+    raw = ctypes.CDLL(rpg.LIB_PATH)
+    for name in declared_symbols():
+        assert hasattr(raw, name), name
+    assert sorted(n for n, _, _ in rpg.SIGNATURES) == declared_symbols()
+
+
+@pytest.mark.parametrize("T,k,E,mt", [(256, 2, 8, 16), (4096, 2, 8, 128), (8192, 6, 64, 128),
+                                      (16384, 4, 32, 128), (2049, 8, 32, 128), (1, 1, 1, 16),
+                                      (3, 2, 64, 256), (100, 4, 1024, 32)])
+def test_capacity_matches_oracle(T, k, E, mt):
+    assert rpg.moe_capacity(T, k, E, mt) == orc.capacity(T, k, E, mt)
+
+
+def test_capacity_and_workspace_reject_bad_sizes():
+    assert rpg.moe_capacity(0, 2, 8, 128) == -1
+    assert rpg.moe_capacity(8, 2, 8, 100) == -1
+    assert rpg.moe_permute_workspace_bytes(8, 2, 0) == 0
+    assert rpg.moe_permute_workspace_bytes(8, 2, 2000) == 0
+    assert rpg.moe_permute_workspace_bytes(1000, 2, 8) == 4 * (8 + 1) * 4
+
+
+def test_status_strings():
+    for s in range(7):
+        assert len(rpg.moe_status_str(s)) > 0
+    assert rpg.moe_status_str(99) == "unknown status"
+
+
+def route(dt=0, x=FAKE, wg=FAKE, bias=None, T=16, D=128, E=8, k=2, renorm=0, idx=FAKE, w=FAKE,
+          logits=None):
+    return lib.moe_route(dt, x, wg, bias, T, D, E, k, renorm, idx, w, logits, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=2), MOE_EINVAL), (dict(x=None), MOE_EINVAL), (dict(x=FAKE + 8), MOE_EINVAL),
+    (dict(idx=None), MOE_EINVAL), (dict(bias=FAKE + 2), MOE_EINVAL), (dict(renorm=2), MOE_EINVAL),
+    (dict(T=0), MOE_ESHAPE), (dict(D=100), MOE_ESHAPE), (dict(D=0), MOE_ESHAPE),
+    (dict(E=65), MOE_ESHAPE), (dict(E=0), MOE_ESHAPE), (dict(k=0), MOE_ESHAPE),
+    (dict(k=9), MOE_ESHAPE), (dict(E=64, k=33), MOE_ESHAPE),
+])
+def test_route_validation(kw, code):
+    assert route(**kw) == code
+
+
+def permute(dt=1, x=FAKE, idx=FAKE, T=64, D=128, E=8, k=2, mt=16, m_cap=None, xp=FAKE,
+            ws=FAKE, ws_bytes=1 << 20, err=FAKE, counts=FAKE):
+    if m_cap is None:
+        m_cap = orc.capacity(T, k, E, mt)
+    return lib.moe_permute(dt, x, idx, T, D, E, k, mt, m_cap, xp, counts, FAKE, FAKE, FAKE, FAKE,
+                           ws, ws_bytes, err, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=-1), MOE_EINVAL), (dict(x=None), MOE_EINVAL), (dict(xp=FAKE + 4), MOE_EINVAL),
+    (dict(err=None), MOE_EINVAL), (dict(counts=FAKE + 1), MOE_EINVAL),
+    (dict(T=-5), MOE_ESHAPE), (dict(D=96), MOE_ESHAPE), (dict(E=1025), MOE_ESHAPE),
+    (dict(k=3, E=2), MOE_ESHAPE), (dict(mt=48), MOE_ESHAPE),
+    (dict(m_cap=16), MOE_ECAPACITY), (dict(m_cap=orc.capacity(64, 2, 8, 16) + 8), MOE_ECAPACITY),
+    (dict(ws_bytes=3), MOE_EWORKSPACE),
+])
+def test_permute_validation(kw, code):
+    assert permute(**kw) == code
+
+
+def grouped(dt=1, xp=FAKE, E=8, D=128, F=256, mt=128, m_cap=1024, w1=FAKE, h=FAKE):
+    return lib.moe_grouped_swiglu(dt, xp, FAKE, FAKE, E, D, F, mt, m_cap, w1, FAKE, FAKE, h, FAKE,
+                                  None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=5), MOE_EINVAL), (dict(w1=None), MOE_EINVAL), (dict(h=FAKE + 8), MOE_EINVAL),
+    (dict(E=0), MOE_ESHAPE), (dict(F=100), MOE_ESHAPE), (dict(D=32), MOE_ESHAPE),
+    (dict(mt=7), MOE_ESHAPE), (dict(m_cap=0), MOE_ECAPACITY), (dict(m_cap=1000), MOE_ECAPACITY),
+    (dict(mt=64, m_cap=1024), MOE_EUNSUPPORTED), (dict(mt=16, m_cap=1024), MOE_EUNSUPPORTED),
+])
+def test_grouped_validation(kw, code):
+    assert grouped(**kw) == code
+
+
+def combine(dt=1, y=FAKE, dst=FAKE, w=FAKE, shared=None, T=64, D=128, k=2, m_cap=640, out=FAKE):
+    return lib.moe_combine(dt, y, dst, w, shared, T, D, k, m_cap, out, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=3), MOE_EINVAL), (dict(y=None), MOE_EINVAL), (dict(shared=FAKE + 4), MOE_EINVAL),
+    (dict(out=FAKE + 2), MOE_EINVAL), (dict(T=0), MOE_ESHAPE), (dict(k=0), MOE_ESHAPE),
+    (dict(k=33), MOE_ESHAPE), (dict(D=65), MOE_ESHAPE), (dict(m_cap=0), MOE_ESHAPE),
+])
+def test_combine_validation(kw, code):
+    assert combine(**kw) == code
+
+
+def test_binding_raises_on_rejected_call():
+    with pytest.raises(rpg.MoEError) as ei:
+        rpg._binding._check("moe_route", MOE_ESHAPE)
+    assert ei.value.status == MOE_ESHAPE
