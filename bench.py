@@ -1,0 +1,214 @@
+#!/usr/bin/env python3
+"""Throughput of the single-GPU MoE expert layer on MI355X.
+
+One step = route -> permute -> grouped fc1+SwiGLU -> grouped fc2 [-> shared experts]
+-> combine over one batch of seeded synthetic tokens, all inputs resident in HBM.
+Prints one JSON line: MoE-layer tokens/s, the grouped GEMM's TFLOP/s and fraction
+of the bf16 MFMA peak, the permute and combine GB/s and fraction of HBM bandwidth,
+the roofline of the dominant kernel (grouped fc1) measured with HIP events on the
+stream the kernels run on, and the CPU oracle timed on a bounded sample.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+
+PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA (AMD spec)
+PEAK_F32_TFLOPS = 157.3       # MI355X fp32 vector
+PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
+METRIC = "MoE-layer tokens/sec; grouped-GEMM TFLOP/s (% bf16 MFMA peak); permute GB/s"
+
+# rocprofv3 HBM traffic of the dominant kernel, measured for the current kernel source
+# with FETCH_SIZE / WRITE_SIZE and scaled by the same counters on a copy of known size.
+# None when the kernel has changed since the counters were taken.
+TRAFFIC_BYTES_PER_LAUNCH = None
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="dense8_bf16")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=4096)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def cpu_baseline(inp: dict, cfg, tokens: int) -> dict:
+    """The oracle as it stands, on the first ``tokens`` tokens of the same workload."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import moe_oracle as orc
+    sub = dict(inp)
+    sub["x"] = inp["x"][:tokens]
+    if "topk_idx" in inp:
+        sub["topk_idx"], sub["topk_w"] = inp["topk_idx"][:tokens], inp["topk_w"][:tokens]
+    sub.pop("cfg", None)
+    t0 = time.perf_counter()
+    orc.forward(sub, k=cfg.k, m_tile=cfg.m_tile, dtype=cfg.dtype)
+    dt = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {tokens} tokens of {cfg.name} with every expert's weights; one "
+                      f"oracle forward (routing, layout, permute, float64 experts, combine) "
+                      f"took {dt:.2f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus})", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import routing_permute_grouped_amd as rpg
+    import workloads as W
+
+    cfg = W.preset(args.workload)
+    inp = W.generate(cfg, seed=0)
+    cfg = inp["cfg"]
+    T, D, F, E, k, mt = cfg.T, cfg.D, cfg.F, cfg.E, cfg.k, cfg.m_tile
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+
+    def up(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    d = {n: up(a) for n, a in inp.items() if isinstance(a, np.ndarray)}
+    tdt = d["x"].dtype
+    m_cap = rpg.moe_capacity(T, k, E, mt)
+    i32 = dict(dtype=torch.int32, device=dev)
+    buf = {
+        "idx": d.get("topk_idx", torch.empty((T, k), **i32)),
+        "w": d.get("topk_w", torch.empty((T, k), dtype=torch.float32, device=dev)),
+        "x_perm": torch.empty((m_cap, D), dtype=tdt, device=dev),
+        "counts": torch.empty(E, **i32), "offsets": torch.empty(E + 1, **i32),
+        "dst_row": torch.empty((T, k), **i32), "src_row": torch.empty(m_cap, **i32),
+        "tile_expert": torch.empty(m_cap // mt, **i32), "dev_err": torch.empty(1, **i32),
+        "workspace": torch.empty(max(4, rpg.moe_permute_workspace_bytes(T, k, E)),
+                                 dtype=torch.uint8, device=dev),
+        "h": torch.empty((m_cap, F), dtype=tdt, device=dev),
+        "y": torch.empty((m_cap, D), dtype=tdt, device=dev),
+        "out": torch.empty((T, D), dtype=tdt, device=dev),
+    }
+    shared = None
+    if cfg.n_shared:
+        shared = rpg.SharedExperts.from_stacked(d["ws1"], d["ws3"], d["ws2"])
+        rows = rpg.DenseRows(T, mt, dev)
+        buf["hs"] = torch.empty((rows.m_cap, shared.w1.shape[1]), dtype=tdt, device=dev)
+        buf["ys"] = torch.empty((rows.m_cap, D), dtype=tdt, device=dev)
+    routed = "wg" in d
+    stream = torch.cuda.current_stream()
+    marks = ["route", "permute", "fc1", "fc2", "shared", "combine"]
+
+    def step(ev=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record(stream)
+        mark(0)
+        if routed:
+            rpg.moe_route(d["x"], d["wg"], k, bias=d.get("bias"), topk_idx=buf["idx"],
+                          topk_w=buf["w"], stream=stream)
+        mark(1)
+        rpg.moe_permute(d["x"], buf["idx"], E, mt, m_cap=m_cap, out=buf, stream=stream)
+        mark(2)
+        rpg.moe_grouped_fc1_swiglu(buf["x_perm"], buf["offsets"], buf["tile_expert"], d["w1"],
+                                   d["w3"], mt, m_cap, buf["h"], stream=stream)
+        mark(3)
+        rpg.moe_grouped_fc2(buf["h"], buf["offsets"], buf["tile_expert"], d["w2"], mt, m_cap,
+                            buf["y"], stream=stream)
+        mark(4)
+        sh = None
+        if shared is not None:
+            rpg.moe_grouped_swiglu(d["x"], rows.offsets, rows.tile_expert, shared.w1, shared.w3,
+                                   shared.w2, mt, m_cap=rows.m_cap, h=buf["hs"],
+                                   y_perm=buf["ys"], stream=stream)
+            sh = buf["ys"][:T]
+        mark(5)
+        rpg.moe_combine(buf["y"], buf["dst_row"], buf["w"], shared=sh, out=buf["out"],
+                        m_cap=m_cap, stream=stream)
+        mark(6)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    if int(buf["dev_err"].item()) != 0:
+        raise RuntimeError("permute reported expert indices outside [-1, E)")
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(marks) + 1)]
+              for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(events[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    per = {m: [events[s][i].elapsed_time(events[s][i + 1]) * 1e3 for s in range(args.steps)]
+           for i, m in enumerate(marks)}
+    med = {m: statistics.median(v) for m, v in per.items()}
+    avg = {m: statistics.fmean(v) for m, v in per.items()}
+
+    counts = buf["counts"].cpu().numpy().astype(np.int64)
+    n_valid = int(counts.sum())
+    s_el = cfg.elem_bytes
+    fc1_flop = 4.0 * n_valid * D * F
+    fc2_flop = 2.0 * n_valid * D * F
+    gemm_tflops = (fc1_flop + fc2_flop) / ((avg["fc1"] + avg["fc2"]) * 1e-6) / 1e12
+    perm_bytes = (T + n_valid) * D * s_el
+    comb_bytes = (n_valid + T + (T if shared is not None else 0)) * D * s_el
+    perm_gbps = perm_bytes / (avg["permute"] * 1e-6) / 1e9
+    comb_gbps = comb_bytes / (avg["combine"] * 1e-6) / 1e9
+    peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
+    fc1_tflops = fc1_flop / (avg["fc1"] * 1e-6) / 1e12
+    ms_per_step = wall * 1e3 / args.steps
+    rec = {
+        "metric": METRIC,
+        "value": T * args.steps / wall,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded numpy PCG64 draws; Gaussian inputs and weights)",
+        "config": {"workload": cfg.name, "T": T, "D": D, "F": F, "E": E, "k": k, "m_tile": mt,
+                   "n_shared": cfg.n_shared, "F_shared": cfg.F_shared,
+                   "routing": cfg.routing},
+        "roofline": {"kernel": "grouped fc1 + silu(a)*b (gg_bf16_kernel<true>)", "bound": "mfma",
+                     "achieved": fc1_tflops, "peak": peak, "unit": "TFLOP/s",
+                     "frac": fc1_tflops / peak, "traffic": TRAFFIC_BYTES_PER_LAUNCH,
+                     "algorithmic_flop_per_launch": fc1_flop, "avg_launch_us": avg["fc1"]},
+        "grouped_gemm_tflops": gemm_tflops,
+        "grouped_gemm_frac_bf16_peak": gemm_tflops / peak,
+        "permute_GBps": perm_gbps, "permute_frac_hbm": perm_gbps / PEAK_HBM_GBPS,
+        "combine_GBps": comb_gbps, "combine_frac_hbm": comb_gbps / PEAK_HBM_GBPS,
+        "stage_us_median": med, "stage_us_mean": avg,
+        "assignments": n_valid, "padded_rows": int(buf["offsets"][-1].item()),
+        "expert_rows_min_max": [int(counts.min()), int(counts.max())],
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(inp, cfg, min(args.cpu_sample_tokens, T))
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -126,6 +126,21 @@ moe_status_t moe_grouped_swiglu(moe_dtype_t dt, const void* x_perm, const int32_
                                 void* h, void* y_perm, void* stream);
 
 /*
+ * moe_grouped_fc1_swiglu / moe_grouped_fc2 - the two halves of moe_grouped_swiglu
+ * as separate calls (same arguments, same results, same kernels): fc1 writes
+ * h = silu(x_perm w1[e]^T) * (x_perm w3[e]^T), fc2 writes y_perm = h w2[e]^T.
+ * They exist so a caller can time or overlap the two grouped GEMMs on their own.
+ * Errors: as moe_grouped_swiglu.
+ */
+moe_status_t moe_grouped_fc1_swiglu(moe_dtype_t dt, const void* x_perm, const int32_t* offsets,
+                                    const int32_t* tile_expert, int E, int D, int F, int m_tile,
+                                    int64_t m_cap, const void* w1, const void* w3, void* h,
+                                    void* stream);
+moe_status_t moe_grouped_fc2(moe_dtype_t dt, const void* h, const int32_t* offsets,
+                             const int32_t* tile_expert, int E, int D, int F, int m_tile,
+                             int64_t m_cap, const void* w2, void* y_perm, void* stream);
+
+/*
  * moe_combine - unpermute and weighted reduce ("Expert Parallelism (EP)",
  * section 1 "combine_postprocess: unpermute-1, weighted by the top-k weights,
  * reduce back to the original order" plus the shared experts; section 5:

@@ -27,6 +27,8 @@ SIGNATURES = [
     ("moe_permute", _I, [_I, _P, _P, _I, _I, _I, _I, _I, _I64, _P, _P, _P, _P, _P, _P, _P, _SZ,
                          _P, _P]),
     ("moe_grouped_swiglu", _I, [_I, _P, _P, _P, _I, _I, _I, _I, _I64, _P, _P, _P, _P, _P, _P]),
+    ("moe_grouped_fc1_swiglu", _I, [_I, _P, _P, _P, _I, _I, _I, _I, _I64, _P, _P, _P, _P]),
+    ("moe_grouped_fc2", _I, [_I, _P, _P, _P, _I, _I, _I, _I, _I64, _P, _P, _P]),
     ("moe_combine", _I, [_I, _P, _P, _P, _P, _I, _I, _I, _I64, _P, _P]),
     ("moe_capacity", _I64, [_I, _I, _I, _I]),
     ("moe_permute_workspace_bytes", _SZ, [_I, _I, _I]),
@@ -159,6 +161,26 @@ def moe_grouped_swiglu(x_perm: torch.Tensor, offsets: torch.Tensor, tile_expert:
         _dt(x_perm), _ptr(x_perm), _ptr(offsets), _ptr(tile_expert), E, D, F, m_tile, m_cap,
         _ptr(w1), _ptr(w3), _ptr(w2), _ptr(h), _ptr(y_perm), _stream(stream)))
     return h, y_perm
+
+
+def moe_grouped_fc1_swiglu(x_perm: torch.Tensor, offsets: torch.Tensor, tile_expert: torch.Tensor,
+                           w1: torch.Tensor, w3: torch.Tensor, m_tile: int, m_cap: int,
+                           h: torch.Tensor, stream=None) -> torch.Tensor:
+    E, F, D = w1.shape
+    _check("moe_grouped_fc1_swiglu", lib.moe_grouped_fc1_swiglu(
+        _dt(x_perm), _ptr(x_perm), _ptr(offsets), _ptr(tile_expert), E, D, F, m_tile, m_cap,
+        _ptr(w1), _ptr(w3), _ptr(h), _stream(stream)))
+    return h
+
+
+def moe_grouped_fc2(h: torch.Tensor, offsets: torch.Tensor, tile_expert: torch.Tensor,
+                    w2: torch.Tensor, m_tile: int, m_cap: int, y_perm: torch.Tensor,
+                    stream=None) -> torch.Tensor:
+    E, D, F = w2.shape
+    _check("moe_grouped_fc2", lib.moe_grouped_fc2(
+        _dt(h), _ptr(h), _ptr(offsets), _ptr(tile_expert), E, D, F, m_tile, m_cap, _ptr(w2),
+        _ptr(y_perm), _stream(stream)))
+    return y_perm
 
 
 def moe_combine(y_perm: torch.Tensor, dst_row: torch.Tensor, topk_w: torch.Tensor,

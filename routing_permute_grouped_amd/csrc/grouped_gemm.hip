@@ -270,30 +270,36 @@ __global__ __launch_bounds__(256) void gg_f32_kernel(const float* __restrict__ A
 
 }  // namespace
 
-hipError_t launch_grouped_swiglu(int dt, const void* x_perm, const int32_t* offsets,
+hipError_t launch_grouped_swiglu(int dt, int phases, const void* x_perm, const int32_t* offsets,
                                  const int32_t* tile_expert, int E, int D, int F, int m_tile,
                                  int64_t m_cap, const void* w1, const void* w3, const void* w2,
                                  void* h, void* y_perm, hipStream_t s) {
   if (dt == kF32) {
     const dim3 block(256);
     const int mtiles = (int)((m_cap + FM - 1) / FM);
-    hipLaunchKernelGGL(gg_f32_kernel<true>, dim3(mtiles, (F + FN - 1) / FN), block, 0, s,
-                       static_cast<const float*>(x_perm), offsets, tile_expert, E, D, F, m_tile,
-                       (int)m_cap, static_cast<const float*>(w1), static_cast<const float*>(w3),
-                       static_cast<float*>(h));
-    hipLaunchKernelGGL(gg_f32_kernel<false>, dim3(mtiles, (D + FN - 1) / FN), block, 0, s,
-                       static_cast<const float*>(h), offsets, tile_expert, E, F, D, m_tile,
-                       (int)m_cap, static_cast<const float*>(w2), static_cast<const float*>(w2),
-                       static_cast<float*>(y_perm));
+    if (phases & 1)
+      hipLaunchKernelGGL(gg_f32_kernel<true>, dim3(mtiles, (F + FN - 1) / FN), block, 0, s,
+                         static_cast<const float*>(x_perm), offsets, tile_expert, E, D, F, m_tile,
+                         (int)m_cap, static_cast<const float*>(w1), static_cast<const float*>(w3),
+                         static_cast<float*>(h));
+    if (phases & 2)
+      hipLaunchKernelGGL(gg_f32_kernel<false>, dim3(mtiles, (D + FN - 1) / FN), block, 0, s,
+                         static_cast<const float*>(h), offsets, tile_expert, E, F, D, m_tile,
+                         (int)m_cap, static_cast<const float*>(w2), static_cast<const float*>(w2),
+                         static_cast<float*>(y_perm));
     return hipGetLastError();
   }
   const dim3 grid(cu_count()), block(NTHR);
-  hipLaunchKernelGGL(gg_bf16_kernel<true>, grid, block, 0, s, static_cast<const bf16_t*>(x_perm),
-                     offsets, tile_expert, E, D, F, m_tile, (int)m_cap, static_cast<const bf16_t*>(w1),
-                     static_cast<const bf16_t*>(w3), static_cast<bf16_t*>(h));
-  hipLaunchKernelGGL(gg_bf16_kernel<false>, grid, block, 0, s, static_cast<const bf16_t*>(h),
-                     offsets, tile_expert, E, F, D, m_tile, (int)m_cap, static_cast<const bf16_t*>(w2),
-                     static_cast<const bf16_t*>(w2), static_cast<bf16_t*>(y_perm));
+  if (phases & 1)
+    hipLaunchKernelGGL(gg_bf16_kernel<true>, grid, block, 0, s, static_cast<const bf16_t*>(x_perm),
+                       offsets, tile_expert, E, D, F, m_tile, (int)m_cap,
+                       static_cast<const bf16_t*>(w1), static_cast<const bf16_t*>(w3),
+                       static_cast<bf16_t*>(h));
+  if (phases & 2)
+    hipLaunchKernelGGL(gg_bf16_kernel<false>, grid, block, 0, s, static_cast<const bf16_t*>(h),
+                       offsets, tile_expert, E, F, D, m_tile, (int)m_cap,
+                       static_cast<const bf16_t*>(w2), static_cast<const bf16_t*>(w2),
+                       static_cast<bf16_t*>(y_perm));
   return hipGetLastError();
 }
 

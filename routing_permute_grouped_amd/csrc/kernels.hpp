@@ -27,7 +27,8 @@ hipError_t launch_permute(int dt, const void* x, const int32_t* topk_idx, int T,
                           int32_t* offsets, int32_t* dst_row, int32_t* src_row,
                           int32_t* tile_expert, void* workspace, int32_t* dev_err, hipStream_t s);
 
-hipError_t launch_grouped_swiglu(int dt, const void* x_perm, const int32_t* offsets,
+// phase bit 1: fc1 (x_perm, w1, w3 -> h); bit 2: fc2 (h, w2 -> y_perm)
+hipError_t launch_grouped_swiglu(int dt, int phases, const void* x_perm, const int32_t* offsets,
                                  const int32_t* tile_expert, int E, int D, int F, int m_tile,
                                  int64_t m_cap, const void* w1, const void* w3, const void* w2,
                                  void* h, void* y_perm, hipStream_t s);

@@ -104,19 +104,43 @@ moe_status_t moe_permute(moe_dtype_t dt, const void* x, const int32_t* topk_idx,
                                         dev_err, static_cast<hipStream_t>(stream)));
 }
 
+static moe_status_t grouped(int phases, moe_dtype_t dt, const void* x_perm,
+                            const int32_t* offsets, const int32_t* tile_expert, int E, int D, int F,
+                            int m_tile, int64_t m_cap, const void* w1, const void* w3,
+                            const void* w2, void* h, void* y_perm, void* stream) {
+  if (!dtype_ok(dt) || !aligned4(offsets) || !aligned4(tile_expert) || !aligned16(h))
+    return MOE_EINVAL;
+  if ((phases & 1) && (!aligned16(x_perm) || !aligned16(w1) || !aligned16(w3))) return MOE_EINVAL;
+  if ((phases & 2) && (!aligned16(w2) || !aligned16(y_perm))) return MOE_EINVAL;
+  if (E < 1 || E > kMaxExperts || !dim_ok(D) || !dim_ok(F) || !mtile_ok(m_tile)) return MOE_ESHAPE;
+  if (m_cap < 1 || m_cap % m_tile != 0 || m_cap > INT32_MAX) return MOE_ECAPACITY;
+  if (dt == MOE_BF16 && m_tile != 128 && m_tile != 256) return MOE_EUNSUPPORTED;
+  return hip_status(moe::launch_grouped_swiglu(dt, phases, x_perm, offsets, tile_expert, E, D, F,
+                                               m_tile, m_cap, w1, w3, w2, h, y_perm,
+                                               static_cast<hipStream_t>(stream)));
+}
+
 moe_status_t moe_grouped_swiglu(moe_dtype_t dt, const void* x_perm, const int32_t* offsets,
                                 const int32_t* tile_expert, int E, int D, int F, int m_tile,
                                 int64_t m_cap, const void* w1, const void* w3, const void* w2,
                                 void* h, void* y_perm, void* stream) {
-  if (!dtype_ok(dt) || !aligned16(x_perm) || !aligned4(offsets) || !aligned4(tile_expert) ||
-      !aligned16(w1) || !aligned16(w3) || !aligned16(w2) || !aligned16(h) || !aligned16(y_perm))
-    return MOE_EINVAL;
-  if (E < 1 || E > kMaxExperts || !dim_ok(D) || !dim_ok(F) || !mtile_ok(m_tile)) return MOE_ESHAPE;
-  if (m_cap < 1 || m_cap % m_tile != 0 || m_cap > INT32_MAX) return MOE_ECAPACITY;
-  if (dt == MOE_BF16 && m_tile != 128 && m_tile != 256) return MOE_EUNSUPPORTED;
-  return hip_status(moe::launch_grouped_swiglu(dt, x_perm, offsets, tile_expert, E, D, F, m_tile,
-                                               m_cap, w1, w3, w2, h, y_perm,
-                                               static_cast<hipStream_t>(stream)));
+  return grouped(3, dt, x_perm, offsets, tile_expert, E, D, F, m_tile, m_cap, w1, w3, w2, h,
+                 y_perm, stream);
+}
+
+moe_status_t moe_grouped_fc1_swiglu(moe_dtype_t dt, const void* x_perm, const int32_t* offsets,
+                                    const int32_t* tile_expert, int E, int D, int F, int m_tile,
+                                    int64_t m_cap, const void* w1, const void* w3, void* h,
+                                    void* stream) {
+  return grouped(1, dt, x_perm, offsets, tile_expert, E, D, F, m_tile, m_cap, w1, w3, nullptr, h,
+                 nullptr, stream);
+}
+
+moe_status_t moe_grouped_fc2(moe_dtype_t dt, const void* h, const int32_t* offsets,
+                             const int32_t* tile_expert, int E, int D, int F, int m_tile,
+                             int64_t m_cap, const void* w2, void* y_perm, void* stream) {
+  return grouped(2, dt, nullptr, offsets, tile_expert, E, D, F, m_tile, m_cap, nullptr, nullptr,
+                 w2, const_cast<void*>(h), y_perm, stream);
 }
 
 moe_status_t moe_combine(moe_dtype_t dt, const void* y_perm, const int32_t* dst_row,

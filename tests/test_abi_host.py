@@ -19,11 +19,12 @@ lib = rpg.lib
 
 def declared_symbols():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^(?![\s/*#])[^\n(]*?\b(moe_[a-z_]+)\(", text, re.M)))
+    return sorted(set(re.findall(r"^(?![\s/*#])[^\n(]*?\b(moe_[a-z_0-9]+)\(", text, re.M)))
 
 
 def test_header_declares_the_four_calls_and_helpers():
     assert declared_symbols() == sorted(["moe_route", "moe_permute", "moe_grouped_swiglu",
+                                         "moe_grouped_fc1_swiglu", "moe_grouped_fc2",
                                          "moe_combine", "moe_capacity",
                                          "moe_permute_workspace_bytes", "moe_status_str"])
 
@@ -105,6 +106,17 @@ def grouped(dt=1, xp=FAKE, E=8, D=128, F=256, mt=128, m_cap=1024, w1=FAKE, h=FAK
 ])
 def test_grouped_validation(kw, code):
     assert grouped(**kw) == code
+
+
+def test_split_grouped_calls_validate():
+    assert lib.moe_grouped_fc1_swiglu(1, FAKE, FAKE, FAKE, 8, 128, 256, 128, 1024, None, FAKE,
+                                      FAKE, None) == MOE_EINVAL
+    assert lib.moe_grouped_fc1_swiglu(1, FAKE, FAKE, FAKE, 8, 128, 250, 128, 1024, FAKE, FAKE,
+                                      FAKE, None) == MOE_ESHAPE
+    assert lib.moe_grouped_fc2(1, FAKE, FAKE, FAKE, 8, 128, 256, 128, 1000, FAKE, FAKE,
+                               None) == MOE_ECAPACITY
+    assert lib.moe_grouped_fc2(1, FAKE, FAKE, FAKE, 8, 128, 256, 64, 1024, FAKE, FAKE,
+                               None) == MOE_EUNSUPPORTED
 
 
 def combine(dt=1, y=FAKE, dst=FAKE, w=FAKE, shared=None, T=64, D=128, k=2, m_cap=640, out=FAKE):
