@@ -116,7 +116,7 @@ moe_status_t moe_permute(moe_dtype_t dt, const void* x, const int32_t* topk_idx,
  * (zero in x_perm) give exact zeros. offsets[e] for e < E must be multiples of
  * m_tile; offsets[E] may be any value <= m_cap (so a dense FFN over T tokens is
  * the call with E = 1, offsets = {0, T}, tile_expert all 0).
- * bf16 needs m_tile in {128, 256}; float32 accepts every m_tile.
+ * bf16 needs m_tile in {128, 256}; float32 accepts every m_tile. D*F < 2^31.
  * Errors: MOE_EINVAL, MOE_ESHAPE, MOE_ECAPACITY (m_cap % m_tile),
  * MOE_EUNSUPPORTED, MOE_EHIP.
  */

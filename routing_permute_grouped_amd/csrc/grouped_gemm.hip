@@ -5,20 +5,26 @@
 // groups, rows laid out expert-contiguous and tile aligned). Weight layout from the
 // "Expert Tensor Parallel" design note, section 4.3: w1, w3 [E,F,D], w2 [E,D,F].
 //
-// bf16 kernel (float32 accumulation on MFMA v_mfma_f32_32x32x16_bf16):
-//   * output tile 128 rows x (128 h columns from w1 and w3 | 256 y columns); both
-//     operands are K-contiguous, so each tile stages A [128 x 64] and a 256-row
-//     weight panel [256 x 64] of bf16 per k-step in LDS, double buffered (96 KiB)
-//   * LDS rows are 128 bytes; the 16-byte chunk index is XOR-swizzled with the row
-//     so both the global->LDS stores and the MFMA fragment reads are conflict free
-//   * weights are the MFMA A operand and activations the B operand, so every lane
-//     ends with 4 consecutive output columns of one row (8-byte stores)
-//   * fc1 interleaves w1 and w3 rows in the panel so the same wave holds a and b of
-//     the same (row, column) and applies silu(a)*b before rounding to bf16
-//   * persistent grid (one workgroup per CU); the number of row tiles is read on the
-//     device from offsets[E]; tiles are walked in groups of 8 row tiles per column
-//     sweep, and the workgroup id is remapped so that each XCD's L2 sees a
-//     contiguous run of tiles; the expert of a row tile comes from tile_expert.
+// bf16 kernel (float32 accumulation on v_mfma_f32_32x32x16_bf16):
+//   * a tile is up to 256 rows of one expert's segment x a 256-row weight panel
+//     (fc1: 128 h columns, taken from w1 and w3 in alternating 32-row blocks; fc2:
+//     256 y columns). Both operands are K-contiguous; per 64-wide k step the tile
+//     stages A [256 x 64] and the panel [256 x 64] in LDS (64 KiB), double
+//     buffered through registers (128 KiB).
+//   * four waves; on a full tile each wave owns 128 rows x 128 panel rows (16
+//     MFMA blocks, 256 accumulators in AGPRs). A half tile (the last 128 rows of a
+//     segment whose length is an odd number of 128-row tiles) is split 128 rows x
+//     64 panel rows per wave, so all four SIMDs stay busy.
+//   * LDS rows are 128 bytes; the 16-byte chunk index is XOR-swizzled with the
+//     row, so the global->LDS stores and the MFMA fragment reads are conflict free.
+//   * weights are the MFMA A operand and activations the B operand: each lane ends
+//     with 4 consecutive output columns of one row (8-byte stores); for fc1 the w1
+//     and w3 blocks of the same columns land in the same wave, which applies
+//     silu(a)*b before rounding to bf16.
+//   * persistent grid (one workgroup per CU). Each workgroup builds the list of
+//     256-row blocks per expert from offsets[] on the device (no host sync), walks
+//     the (block, column) tiles in groups of 4 blocks per column sweep, and the
+//     workgroup id is remapped so each XCD's L2 sees a contiguous run of tiles.
 // float32 kernel: a plain LDS-tiled VALU GEMM (the tiny float32 layer only).
 #include <math.h>
 
@@ -31,14 +37,15 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int BM = 128;        // rows per tile
+constexpr int BM = 256;        // rows per full tile
+constexpr int BP = 256;        // weight-panel rows per tile
 constexpr int BK = 64;         // k per stage
-constexpr int PANEL = 256;     // weight rows per stage
-constexpr int NTHR = 256;      // 4 waves: 2 (rows) x 2 (weight rows)
-constexpr int GROUP_M = 8;     // row tiles per column sweep
+constexpr int NTHR = 256;      // 4 waves
+constexpr int GROUP_M = 4;     // 256-row blocks per column sweep
 constexpr int XCDS = 8;
+constexpr int MAXE = 1024;
 constexpr int A_BYTES = BM * BK * 2;
-constexpr int B_BYTES = PANEL * BK * 2;
+constexpr int B_BYTES = BP * BK * 2;
 constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
 
 __device__ __forceinline__ float silu_mul(float a, float b) {
@@ -48,166 +55,240 @@ __device__ __forceinline__ float silu_mul(float a, float b) {
 // byte offset of chunk `ch` (16 bytes) of row `r` in a 128-byte-row LDS tile
 __device__ __forceinline__ int swz(int r, int ch) { return r * 128 + ((ch ^ (r & 7)) << 4); }
 
-template <bool FC1>
-__global__ __launch_bounds__(NTHR, 1) void gg_bf16_kernel(
-    const bf16_t* __restrict__ A, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ tile_expert, int E, int K, int N, int m_tile, int m_cap,
-    const bf16_t* __restrict__ W1, const bf16_t* __restrict__ W3, bf16_t* __restrict__ C) {
-  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE_BYTES];
+__device__ __forceinline__ void store4(bf16_t* p, float a, float b, float c, float d) {
+  uint2 pk;
+  pk.x = pack_bf16x2(a, b);
+  pk.y = pack_bf16x2(c, d);
+  *reinterpret_cast<uint2*>(p) = pk;
+}
 
+// Exclusive prefix sum over the 256 threads of the block.
+__device__ __forceinline__ int block_scan_excl(int v, int* wtot) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  int inc = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(inc, d);
+    if (lane >= d) inc += o;
+  }
+  if (lane == 63) wtot[wid] = inc;
+  __syncthreads();
+  int before = 0;
+  for (int w = 0; w < wid; ++w) before += wtot[w];
+  return before + inc - v;
+}
+
+struct Tile {
+  int e, m0, rows, n0;
+};
+
+// LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) char*)p);
+}
+
+// 16 bytes per lane from global memory straight into LDS: the 64 lanes of the wave
+// fill 1 KiB at LDS address `lds` (made wave-uniform), lane l at lds + 16*l.
+// Issued as inline assembly so the compiler adds no waits of its own for it; the
+// pipeline below waits with an explicit s_waitcnt vmcnt(0) and a barrier before
+// any wave reads the stage the loads fill.
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(g), "s"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory", "m0");
+}
+
+// One tile: rows [m0, m0 + rows) of expert e against the weight panel from n0.
+// HALF: rows <= 128; the four waves split the panel instead of the rows.
+//
+// Pipeline: two LDS stages filled by direct global->LDS loads. Iteration kt waits
+// for its own loads of stage kt, meets the other waves at a barrier (after which
+// every wave has finished reading stage kt-1 and all of stage kt has landed),
+// issues the loads of k-step kt+1 into the free stage, then runs the MFMAs of kt.
+template <bool FC1, bool HALF>
+__device__ __forceinline__ void run_tile(char* smem, const Tile& t, const bf16_t* __restrict__ A,
+                                         const bf16_t* __restrict__ W1,
+                                         const bf16_t* __restrict__ W3, bf16_t* __restrict__ C,
+                                         int K, int N) {
+  constexpr int NA = HALF ? 4 : 8;   // 1 KiB (8-row) pieces of A per wave per stage
+  constexpr int NB = 8;              // pieces of the panel per wave per stage
+  constexpr int WN = HALF ? 2 : 4;   // 32-row panel blocks per wave
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave & 1;   // 64-row half of the tile
-  const int wn = wave >> 1;  // 128-row half of the weight panel
-
-  const int mend = min(offsets[E], m_cap);
-  const int n_mt = (mend + BM - 1) / BM;
-  const int cols_per_tile = FC1 ? 128 : PANEL;
-  const int n_nt = (N + cols_per_tile - 1) / cols_per_tile;
-  const int total = n_mt * n_nt;
+  const int wm = HALF ? 0 : (wave & 1);
+  const int pr0 = HALF ? wave * 64 : (wave >> 1) * 128;   // first panel row of this wave
   const int nk = K / BK;
 
+  // Piece j of wave w holds rows 32*j + 8*w .. +7; lane l fills row + l/8, 16-byte
+  // slot l%8, which holds logical chunk (l%8) ^ (row & 7) = (l%8) ^ (l/8).
+  const int lrow = 8 * wave + (lane >> 3);
+  const int lchunk = (lane & 7) ^ (lane >> 3);
+  uint32_t aoff[NA];
+#pragma unroll
+  for (int j = 0; j < NA; ++j) aoff[j] = (uint32_t)(min(32 * j + lrow, t.rows - 1) * K + lchunk * 8);
+  const bf16_t* abase = A + (size_t)t.m0 * K;
+  uint32_t boff[NB];
+  const bf16_t* bbase[NB];
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+    const int pr = 32 * j + lrow;
+    int gr;
+    if (FC1) {  // 32-row blocks alternate w1, w3 over the same 32 columns
+      bbase[j] = ((j & 1) ? W3 : W1) + (size_t)t.e * N * K;
+      gr = t.n0 + (pr >> 6) * 32 + (pr & 31);
+    } else {
+      bbase[j] = W1 + (size_t)t.e * N * K;
+      gr = t.n0 + pr;
+    }
+    boff[j] = (uint32_t)(min(gr, N - 1) * K + lchunk * 8);
+  }
+  const int piece = wave * 1024;  // byte offset of this wave's piece inside a 32-row slab
+
+  const uint32_t lds0 = lds_addr(smem) + piece;
+  auto issue = [&](int kt, int stage) {
+    const uint32_t la = lds0 + stage * STAGE_BYTES;
+    const uint32_t lb = la + A_BYTES;
+    const int ko = kt * BK;
+#pragma unroll
+    for (int j = 0; j < NA; ++j) dma16(abase + aoff[j] + ko, la + j * 4096);
+#pragma unroll
+    for (int j = 0; j < NB; ++j) dma16(bbase[j] + boff[j] + ko, lb + j * 4096);
+  };
+
+  f32x16 acc[4][WN];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < WN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+  issue(0, 0);
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (kt + 1 < nk) issue(kt + 1, cur ^ 1);
+    const char* sa = smem + cur * STAGE_BYTES;
+    const char* sb = sa + A_BYTES;
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      const int chk = ks * 2 + (lane >> 5);
+      bf16x8 wf[WN], af[4];
+#pragma unroll
+      for (int nb = 0; nb < WN; ++nb)
+        wf[nb] = *reinterpret_cast<const bf16x8*>(sb + swz(pr0 + nb * 32 + (lane & 31), chk));
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+        af[mb] = *reinterpret_cast<const bf16x8*>(sa + swz(wm * 128 + mb * 32 + (lane & 31), chk));
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < WN; ++nb)
+          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[nb], af[mb], acc[mb][nb], 0, 0, 0);
+    }
+  }
+  // every wave is done with both stages before the next tile refills them
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+
+  // Lane holds column m = lane & 31 of every 32x32 block and panel rows
+  // 8*g + 4*(lane >> 5) + i (i = 0..3) for g = 0..3.
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) {
+    const int r = wm * 128 + mb * 32 + (lane & 31);
+    if (r >= t.rows) continue;
+    bf16_t* crow = C + (size_t)(t.m0 + r) * N;
+    if (FC1) {
+#pragma unroll
+      for (int p = 0; p < WN / 2; ++p) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int n = t.n0 + pr0 / 2 + p * 32 + g * 8 + (lane >> 5) * 4;
+          if (n >= N) continue;
+          const f32x16& a = acc[mb][2 * p];
+          const f32x16& b = acc[mb][2 * p + 1];
+          store4(crow + n, silu_mul(a[4 * g], b[4 * g]), silu_mul(a[4 * g + 1], b[4 * g + 1]),
+                 silu_mul(a[4 * g + 2], b[4 * g + 2]), silu_mul(a[4 * g + 3], b[4 * g + 3]));
+        }
+      }
+    } else {
+#pragma unroll
+      for (int nb = 0; nb < WN; ++nb) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int n = t.n0 + pr0 + nb * 32 + g * 8 + (lane >> 5) * 4;
+          if (n >= N) continue;
+          const f32x16& a = acc[mb][nb];
+          store4(crow + n, a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]);
+        }
+      }
+    }
+  }
+}
+
+template <bool FC1>
+__global__ __launch_bounds__(NTHR, 1) void gg_bf16_kernel(
+    const bf16_t* __restrict__ A, const int32_t* __restrict__ offsets, int E, int K, int N,
+    int m_cap, const bf16_t* __restrict__ W1, const bf16_t* __restrict__ W3,
+    bf16_t* __restrict__ C) {
+  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE_BYTES];
+  __shared__ int segoff[MAXE + 1];   // segment starts (clamped to the rows in use)
+  __shared__ int tstart[MAXE + 1];   // first 256-row block of each expert
+  __shared__ int wtot[4];
+
+  const int tid = threadIdx.x;
+  const int mend = min(offsets[E], m_cap);
+  for (int e = tid; e <= E; e += NTHR) segoff[e] = min(offsets[e], mend);
+  __syncthreads();
+  int cnt[4], local = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = tid * 4 + i;
+    cnt[i] = e < E ? (max(segoff[e + 1] - segoff[e], 0) + BM - 1) / BM : 0;
+    local += cnt[i];
+  }
+  int run = block_scan_excl(local, wtot);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = tid * 4 + i;
+    if (e < E) tstart[e] = run;
+    run += cnt[i];
+  }
+  if (tid == NTHR - 1) tstart[E] = run;
+  __syncthreads();
+
+  const int n_mb = tstart[E];
+  const int cols = FC1 ? BP / 2 : BP;
+  const int n_nt = (N + cols - 1) / cols;
+  const int total = n_mb * n_nt;
   int vb = blockIdx.x;
   if (gridDim.x % XCDS == 0) vb = (blockIdx.x % XCDS) * (gridDim.x / XCDS) + blockIdx.x / XCDS;
-
-  // this thread's chunk column and first row of the global->LDS copies
-  const int ch = tid & 7;
-  const int row0 = tid >> 3;  // rows row0 + 32*j
 
   for (int w = vb; w < total; w += gridDim.x) {
     const int grp = w / (GROUP_M * n_nt);
     const int first = grp * GROUP_M;
-    const int gm = min(GROUP_M, n_mt - first);
+    const int gm = min(GROUP_M, n_mb - first);
     const int within = w - grp * GROUP_M * n_nt;
-    const int mt = first + within % gm;
+    const int mb = first + within % gm;
     const int nt = within / gm;
-    const int m0 = mt * BM;
-    const int e = tile_expert[m0 / m_tile];
-    if (e < 0 || e >= E) continue;
-    const int n0 = nt * cols_per_tile;
-
-    // global sources of this thread's copies
-    const bf16_t* asrc[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int r = min(m0 + row0 + 32 * j, mend - 1);
-      asrc[j] = A + (size_t)r * K + ch * 8;
+    int lo = 0, hi = E;  // largest expert whose first block is <= mb
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (tstart[mid] <= mb) lo = mid; else hi = mid;
     }
-    const bf16_t* bsrc[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int r = row0 + 32 * j;  // panel row
-      int gr;
-      const bf16_t* W;
-      if (FC1) {
-        W = ((r >> 6) & 1) ? W3 : W1;
-        gr = n0 + (r >> 7) * 64 + (r & 63);
-      } else {
-        W = W1;
-        gr = n0 + r;
-      }
-      gr = min(gr, N - 1);
-      bsrc[j] = W + ((size_t)e * N + gr) * K + ch * 8;
-    }
-
-    u32x4 ra[4], rb[8];
-    auto gload = [&](int kt) {
-      const size_t ko = (size_t)kt * BK;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) ra[j] = ld16(asrc[j] + ko);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) rb[j] = ld16(bsrc[j] + ko);
-    };
-    auto lstore = [&](int stage) {
-      char* sa = smem + stage * STAGE_BYTES;
-      char* sb = sa + A_BYTES;
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        *reinterpret_cast<u32x4*>(sa + swz(row0 + 32 * j, ch)) = ra[j];
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        *reinterpret_cast<u32x4*>(sb + swz(row0 + 32 * j, ch)) = rb[j];
-    };
-
-    f32x16 acc[4][2];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
-
-    gload(0);
-    lstore(0);
-    __syncthreads();
-
-    for (int kt = 0; kt < nk; ++kt) {
-      const int cur = kt & 1;
-      if (kt + 1 < nk) gload(kt + 1);
-      const char* sa = smem + cur * STAGE_BYTES;
-      const char* sb = sa + A_BYTES;
-#pragma unroll
-      for (int ks = 0; ks < BK / 16; ++ks) {
-        const int chk = ks * 2 + (lane >> 5);
-        bf16x8 wf[4], af[2];
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-          const int r = wn * 128 + nb * 32 + (lane & 31);
-          wf[nb] = *reinterpret_cast<const bf16x8*>(sb + swz(r, chk));
-        }
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
-          const int r = wm * 64 + mb * 32 + (lane & 31);
-          af[mb] = *reinterpret_cast<const bf16x8*>(sa + swz(r, chk));
-        }
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-          for (int mb = 0; mb < 2; ++mb)
-            acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[nb], af[mb], acc[nb][mb], 0, 0, 0);
-      }
-      if (kt + 1 < nk) lstore(cur ^ 1);
-      __syncthreads();
-    }
-
-    // epilogue: lane holds column m = lane & 31 of each 32x32 block and rows
-    // n = 8*g + 4*(lane >> 5) + i (i = 0..3) for g = 0..3
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      const int m = m0 + wm * 64 + mb * 32 + (lane & 31);
-      if (m >= mend) continue;
-      if (FC1) {
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int n = n0 + wn * 64 + nb * 32 + g * 8 + (lane >> 5) * 4;
-            if (n >= N) continue;
-            float hv[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) hv[i] = silu_mul(acc[nb][mb][g * 4 + i], acc[nb + 2][mb][g * 4 + i]);
-            uint2 pk;
-            pk.x = pack_bf16x2(hv[0], hv[1]);
-            pk.y = pack_bf16x2(hv[2], hv[3]);
-            *reinterpret_cast<uint2*>(C + (size_t)m * N + n) = pk;
-          }
-        }
-      } else {
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int n = n0 + wn * 128 + nb * 32 + g * 8 + (lane >> 5) * 4;
-            if (n >= N) continue;
-            uint2 pk;
-            pk.x = pack_bf16x2(acc[nb][mb][g * 4 + 0], acc[nb][mb][g * 4 + 1]);
-            pk.y = pack_bf16x2(acc[nb][mb][g * 4 + 2], acc[nb][mb][g * 4 + 3]);
-            *reinterpret_cast<uint2*>(C + (size_t)m * N + n) = pk;
-          }
-        }
-      }
-    }
+    Tile t;
+    t.e = lo;
+    t.m0 = segoff[lo] + (mb - tstart[lo]) * BM;
+    t.rows = min(BM, segoff[lo + 1] - t.m0);
+    t.n0 = nt * cols;
+    if (t.rows > BM / 2)
+      run_tile<FC1, false>(smem, t, A, W1, W3, C, K, N);
+    else
+      run_tile<FC1, true>(smem, t, A, W1, W3, C, K, N);
   }
 }
 
@@ -292,12 +373,12 @@ hipError_t launch_grouped_swiglu(int dt, int phases, const void* x_perm, const i
   const dim3 grid(cu_count()), block(NTHR);
   if (phases & 1)
     hipLaunchKernelGGL(gg_bf16_kernel<true>, grid, block, 0, s, static_cast<const bf16_t*>(x_perm),
-                       offsets, tile_expert, E, D, F, m_tile, (int)m_cap,
+                       offsets, E, D, F, (int)m_cap,
                        static_cast<const bf16_t*>(w1), static_cast<const bf16_t*>(w3),
                        static_cast<bf16_t*>(h));
   if (phases & 2)
     hipLaunchKernelGGL(gg_bf16_kernel<false>, grid, block, 0, s, static_cast<const bf16_t*>(h),
-                       offsets, tile_expert, E, F, D, m_tile, (int)m_cap,
+                       offsets, E, F, D, (int)m_cap,
                        static_cast<const bf16_t*>(w2), static_cast<const bf16_t*>(w2),
                        static_cast<bf16_t*>(y_perm));
   return hipGetLastError();

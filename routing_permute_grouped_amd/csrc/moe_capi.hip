@@ -113,6 +113,7 @@ static moe_status_t grouped(int phases, moe_dtype_t dt, const void* x_perm,
   if ((phases & 1) && (!aligned16(x_perm) || !aligned16(w1) || !aligned16(w3))) return MOE_EINVAL;
   if ((phases & 2) && (!aligned16(w2) || !aligned16(y_perm))) return MOE_EINVAL;
   if (E < 1 || E > kMaxExperts || !dim_ok(D) || !dim_ok(F) || !mtile_ok(m_tile)) return MOE_ESHAPE;
+  if ((int64_t)D * F >= ((int64_t)1 << 31)) return MOE_ESHAPE;  // one expert's matrix is int32-indexed
   if (m_cap < 1 || m_cap % m_tile != 0 || m_cap > INT32_MAX) return MOE_ECAPACITY;
   if (dt == MOE_BF16 && m_tile != 128 && m_tile != 256) return MOE_EUNSUPPORTED;
   return hip_status(moe::launch_grouped_swiglu(dt, phases, x_perm, offsets, tile_expert, E, D, F,

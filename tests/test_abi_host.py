@@ -102,7 +102,7 @@ def grouped(dt=1, xp=FAKE, E=8, D=128, F=256, mt=128, m_cap=1024, w1=FAKE, h=FAK
     (dict(dt=5), MOE_EINVAL), (dict(w1=None), MOE_EINVAL), (dict(h=FAKE + 8), MOE_EINVAL),
     (dict(E=0), MOE_ESHAPE), (dict(F=100), MOE_ESHAPE), (dict(D=32), MOE_ESHAPE),
     (dict(mt=7), MOE_ESHAPE), (dict(m_cap=0), MOE_ECAPACITY), (dict(m_cap=1000), MOE_ECAPACITY),
-    (dict(mt=64, m_cap=1024), MOE_EUNSUPPORTED), (dict(mt=16, m_cap=1024), MOE_EUNSUPPORTED),
+    (dict(mt=64, m_cap=1024), MOE_EUNSUPPORTED), (dict(D=65536, F=32768), MOE_ESHAPE), (dict(mt=16, m_cap=1024), MOE_EUNSUPPORTED),
 ])
 def test_grouped_validation(kw, code):
     assert grouped(**kw) == code
