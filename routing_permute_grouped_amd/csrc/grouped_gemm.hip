@@ -15,16 +15,16 @@
 //     MFMA blocks, 256 accumulators in AGPRs). A half tile (the last 128 rows of a
 //     segment whose length is an odd number of 128-row tiles) is split 128 rows x
 //     64 panel rows per wave, so all four SIMDs stay busy.
-//   * LDS rows are 128 bytes; the 16-byte chunk index is XOR-swizzled with the
-//     row, so the global->LDS stores and the MFMA fragment reads are conflict free.
+//   * LDS rows are 128 bytes; the 16-byte chunk index is XOR-swizzled with half the
+//     row index, so the MFMA fragment reads are conflict free.
 //   * weights are the MFMA A operand and activations the B operand: each lane ends
 //     with 4 consecutive output columns of one row (8-byte stores); for fc1 the w1
 //     and w3 blocks of the same columns land in the same wave, which applies
 //     silu(a)*b before rounding to bf16.
 //   * persistent grid (one workgroup per CU). Each workgroup builds the list of
 //     256-row blocks per expert from offsets[] on the device (no host sync), walks
-//     the (block, column) tiles in groups of 4 blocks per column sweep, and the
-//     workgroup id is remapped so each XCD's L2 sees a contiguous run of tiles.
+//     each expert's (block, column) tiles with up to 16 blocks per column sweep, and
+//     the workgroup id is remapped so each XCD's L2 sees a contiguous run of tiles.
 // float32 kernel: a plain LDS-tiled VALU GEMM (the tiny float32 layer only).
 #include <math.h>
 
@@ -40,8 +40,8 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr int BM = 256;        // rows per full tile
 constexpr int BP = 256;        // weight-panel rows per tile
 constexpr int BK = 64;         // k per stage
-constexpr int NTHR = 256;      // 4 waves
-constexpr int GROUP_M = 4;     // 256-row blocks per column sweep
+constexpr int NTHR = 512;      // 8 waves, two per SIMD
+constexpr int GROUP_M = 16;    // at most this many 256-row blocks per column sweep
 constexpr int XCDS = 8;
 constexpr int MAXE = 1024;
 constexpr int A_BYTES = BM * BK * 2;
@@ -52,8 +52,11 @@ __device__ __forceinline__ float silu_mul(float a, float b) {
   return a / (1.0f + __expf(-a)) * b;
 }
 
-// byte offset of chunk `ch` (16 bytes) of row `r` in a 128-byte-row LDS tile
-__device__ __forceinline__ int swz(int r, int ch) { return r * 128 + ((ch ^ (r & 7)) << 4); }
+// Byte offset of 16-byte chunk `ch` of row `r` in a 128-byte-row LDS tile. The chunk
+// is XOR-swizzled with (r / 2) % 8: the 16 rows that 16 consecutive lanes read at one
+// logical chunk then cover all sixteen 16-byte bank groups of a 256-byte bank row
+// (conflict free for ds_read_b128, which serves 16 lanes per cycle).
+__device__ __forceinline__ int swz(int r, int ch) { return r * 128 + ((ch ^ ((r >> 1) & 7)) << 4); }
 
 __device__ __forceinline__ void store4(bf16_t* p, float a, float b, float c, float d) {
   uint2 pk;
@@ -62,7 +65,7 @@ __device__ __forceinline__ void store4(bf16_t* p, float a, float b, float c, flo
   *reinterpret_cast<uint2*>(p) = pk;
 }
 
-// Exclusive prefix sum over the 256 threads of the block.
+// Exclusive prefix sum over the threads of the block (up to 16 waves).
 __device__ __forceinline__ int block_scan_excl(int v, int* wtot) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   int inc = v;
@@ -100,43 +103,51 @@ __device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
 }
 
 // One tile: rows [m0, m0 + rows) of expert e against the weight panel from n0.
-// HALF: rows <= 128; the four waves split the panel instead of the rows.
+//
+// Eight waves, two per SIMD. Full tile: wave w owns rows 128*(w%2) .. +127 and panel
+// rows 64*(w/2) .. +63 (4 x 2 MFMA blocks of 32x32, 128 accumulators). Half tile
+// (rows <= 128): rows 64*(w%2) .. +63 and the same panel rows (2 x 2 blocks).
+// For fc1 the 64 panel rows of a wave are one w1 block and one w3 block covering the
+// same 32 h columns, so silu(a)*b is formed in registers.
 //
 // Pipeline: two LDS stages filled by direct global->LDS loads. Iteration kt waits
 // for its own loads of stage kt, meets the other waves at a barrier (after which
 // every wave has finished reading stage kt-1 and all of stage kt has landed),
-// issues the loads of k-step kt+1 into the free stage, then runs the MFMAs of kt.
+// issues the loads of k-step kt+1 into the free stage, then runs the MFMAs of kt
+// with the fragments of the next 16-wide k slice loaded while the current slice's
+// MFMAs run.
 template <bool FC1, bool HALF>
 __device__ __forceinline__ void run_tile(char* smem, const Tile& t, const bf16_t* __restrict__ A,
                                          const bf16_t* __restrict__ W1,
                                          const bf16_t* __restrict__ W3, bf16_t* __restrict__ C,
                                          int K, int N) {
-  constexpr int NA = HALF ? 4 : 8;   // 1 KiB (8-row) pieces of A per wave per stage
-  constexpr int NB = 8;              // pieces of the panel per wave per stage
-  constexpr int WN = HALF ? 2 : 4;   // 32-row panel blocks per wave
+  constexpr int NA = HALF ? 2 : 4;   // 1 KiB (8-row) pieces of A per wave per stage
+  constexpr int NB = 4;              // pieces of the panel per wave per stage
+  constexpr int WM = HALF ? 2 : 4;   // 32-row blocks of A per wave
+  constexpr int WN = 2;              // 32-row panel blocks per wave
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = HALF ? 0 : (wave & 1);
-  const int pr0 = HALF ? wave * 64 : (wave >> 1) * 128;   // first panel row of this wave
+  const int arow0 = (wave & 1) * (HALF ? 64 : 128);   // first A row of this wave
+  const int prow0 = (wave >> 1) * 64;                 // first panel row of this wave
   const int nk = K / BK;
 
-  // Piece j of wave w holds rows 32*j + 8*w .. +7; lane l fills row + l/8, 16-byte
-  // slot l%8, which holds logical chunk (l%8) ^ (row & 7) = (l%8) ^ (l/8).
+  // Piece j of wave w holds rows 64*j + 8*w .. +7; lane l fills row 64*j + lrow with
+  // lrow = 8*w + l/8, 16-byte slot l%8, which holds logical chunk (l%8) ^ ((row/2)%8).
   const int lrow = 8 * wave + (lane >> 3);
-  const int lchunk = (lane & 7) ^ (lane >> 3);
+  const int lchunk = (lane & 7) ^ ((lrow >> 1) & 7);
   uint32_t aoff[NA];
 #pragma unroll
-  for (int j = 0; j < NA; ++j) aoff[j] = (uint32_t)(min(32 * j + lrow, t.rows - 1) * K + lchunk * 8);
+  for (int j = 0; j < NA; ++j) aoff[j] = (uint32_t)(min(64 * j + lrow, t.rows - 1) * K + lchunk * 8);
   const bf16_t* abase = A + (size_t)t.m0 * K;
   uint32_t boff[NB];
   const bf16_t* bbase[NB];
 #pragma unroll
   for (int j = 0; j < NB; ++j) {
-    const int pr = 32 * j + lrow;
+    const int pr = 64 * j + lrow;
     int gr;
     if (FC1) {  // 32-row blocks alternate w1, w3 over the same 32 columns
-      bbase[j] = ((j & 1) ? W3 : W1) + (size_t)t.e * N * K;
+      bbase[j] = (((pr >> 5) & 1) ? W3 : W1) + (size_t)t.e * N * K;
       gr = t.n0 + (pr >> 6) * 32 + (pr & 31);
     } else {
       bbase[j] = W1 + (size_t)t.e * N * K;
@@ -144,27 +155,27 @@ __device__ __forceinline__ void run_tile(char* smem, const Tile& t, const bf16_t
     }
     boff[j] = (uint32_t)(min(gr, N - 1) * K + lchunk * 8);
   }
-  const int piece = wave * 1024;  // byte offset of this wave's piece inside a 32-row slab
 
-  const uint32_t lds0 = lds_addr(smem) + piece;
+  const uint32_t lds0 = lds_addr(smem) + wave * 1024;
   auto issue = [&](int kt, int stage) {
     const uint32_t la = lds0 + stage * STAGE_BYTES;
     const uint32_t lb = la + A_BYTES;
     const int ko = kt * BK;
 #pragma unroll
-    for (int j = 0; j < NA; ++j) dma16(abase + aoff[j] + ko, la + j * 4096);
+    for (int j = 0; j < NA; ++j) dma16(abase + aoff[j] + ko, la + j * 8192);
 #pragma unroll
-    for (int j = 0; j < NB; ++j) dma16(bbase[j] + boff[j] + ko, lb + j * 4096);
+    for (int j = 0; j < NB; ++j) dma16(bbase[j] + boff[j] + ko, lb + j * 8192);
   };
 
-  f32x16 acc[4][WN];
+  f32x16 acc[WM][WN];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < WM; ++i)
 #pragma unroll
     for (int j = 0; j < WN; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
+  const int fr = lane & 31;
   issue(0, 0);
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
@@ -174,21 +185,26 @@ __device__ __forceinline__ void run_tile(char* smem, const Tile& t, const bf16_t
     if (kt + 1 < nk) issue(kt + 1, cur ^ 1);
     const char* sa = smem + cur * STAGE_BYTES;
     const char* sb = sa + A_BYTES;
-#pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
+    bf16x8 wf[2][WN], af[2][WM];
+    auto frag = [&](int ks, int buf) {
       const int chk = ks * 2 + (lane >> 5);
-      bf16x8 wf[WN], af[4];
 #pragma unroll
       for (int nb = 0; nb < WN; ++nb)
-        wf[nb] = *reinterpret_cast<const bf16x8*>(sb + swz(pr0 + nb * 32 + (lane & 31), chk));
+        wf[buf][nb] = *reinterpret_cast<const bf16x8*>(sb + swz(prow0 + nb * 32 + fr, chk));
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-        af[mb] = *reinterpret_cast<const bf16x8*>(sa + swz(wm * 128 + mb * 32 + (lane & 31), chk));
+      for (int mb = 0; mb < WM; ++mb)
+        af[buf][mb] = *reinterpret_cast<const bf16x8*>(sa + swz(arow0 + mb * 32 + fr, chk));
+    };
+    frag(0, 0);
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      if (ks + 1 < BK / 16) frag(ks + 1, (ks + 1) & 1);
+#pragma unroll
+      for (int mb = 0; mb < WM; ++mb)
 #pragma unroll
         for (int nb = 0; nb < WN; ++nb)
-          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[nb], af[mb], acc[mb][nb], 0, 0, 0);
+          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[ks & 1][nb], af[ks & 1][mb],
+                                                                acc[mb][nb], 0, 0, 0);
     }
   }
   // every wave is done with both stages before the next tile refills them
@@ -198,29 +214,26 @@ __device__ __forceinline__ void run_tile(char* smem, const Tile& t, const bf16_t
   // Lane holds column m = lane & 31 of every 32x32 block and panel rows
   // 8*g + 4*(lane >> 5) + i (i = 0..3) for g = 0..3.
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb) {
-    const int r = wm * 128 + mb * 32 + (lane & 31);
+  for (int mb = 0; mb < WM; ++mb) {
+    const int r = arow0 + mb * 32 + fr;
     if (r >= t.rows) continue;
     bf16_t* crow = C + (size_t)(t.m0 + r) * N;
     if (FC1) {
 #pragma unroll
-      for (int p = 0; p < WN / 2; ++p) {
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int n = t.n0 + pr0 / 2 + p * 32 + g * 8 + (lane >> 5) * 4;
-          if (n >= N) continue;
-          const f32x16& a = acc[mb][2 * p];
-          const f32x16& b = acc[mb][2 * p + 1];
-          store4(crow + n, silu_mul(a[4 * g], b[4 * g]), silu_mul(a[4 * g + 1], b[4 * g + 1]),
-                 silu_mul(a[4 * g + 2], b[4 * g + 2]), silu_mul(a[4 * g + 3], b[4 * g + 3]));
-        }
+      for (int g = 0; g < 4; ++g) {
+        const int n = t.n0 + prow0 / 2 + g * 8 + (lane >> 5) * 4;
+        if (n >= N) continue;
+        const f32x16& a = acc[mb][0];
+        const f32x16& b = acc[mb][1];
+        store4(crow + n, silu_mul(a[4 * g], b[4 * g]), silu_mul(a[4 * g + 1], b[4 * g + 1]),
+               silu_mul(a[4 * g + 2], b[4 * g + 2]), silu_mul(a[4 * g + 3], b[4 * g + 3]));
       }
     } else {
 #pragma unroll
       for (int nb = 0; nb < WN; ++nb) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const int n = t.n0 + pr0 + nb * 32 + g * 8 + (lane >> 5) * 4;
+          const int n = t.n0 + prow0 + nb * 32 + g * 8 + (lane >> 5) * 4;
           if (n >= N) continue;
           const f32x16& a = acc[mb][nb];
           store4(crow + n, a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]);
@@ -238,7 +251,7 @@ __global__ __launch_bounds__(NTHR, 1) void gg_bf16_kernel(
   __shared__ __attribute__((aligned(16))) char smem[2 * STAGE_BYTES];
   __shared__ int segoff[MAXE + 1];   // segment starts (clamped to the rows in use)
   __shared__ int tstart[MAXE + 1];   // first 256-row block of each expert
-  __shared__ int wtot[4];
+  __shared__ int wtot[NTHR / 64];
 
   const int tid = threadIdx.x;
   const int mend = min(offsets[E], m_cap);
@@ -261,25 +274,32 @@ __global__ __launch_bounds__(NTHR, 1) void gg_bf16_kernel(
   if (tid == NTHR - 1) tstart[E] = run;
   __syncthreads();
 
-  const int n_mb = tstart[E];
+  // Tiles are numbered expert by expert: expert e owns items [istart[e], istart[e+1]),
+  // nb_e row blocks x n_nt column tiles, walked in groups of up to GROUP_M row blocks
+  // per column sweep so every weight panel is used by all (or GROUP_M) row blocks of
+  // its expert back to back, on one XCD.
   const int cols = FC1 ? BP / 2 : BP;
   const int n_nt = (N + cols - 1) / cols;
-  const int total = n_mb * n_nt;
+  const int total = tstart[E] * n_nt;   // istart[e] = tstart[e] * n_nt
   int vb = blockIdx.x;
   if (gridDim.x % XCDS == 0) vb = (blockIdx.x % XCDS) * (gridDim.x / XCDS) + blockIdx.x / XCDS;
 
   for (int w = vb; w < total; w += gridDim.x) {
-    const int grp = w / (GROUP_M * n_nt);
-    const int first = grp * GROUP_M;
-    const int gm = min(GROUP_M, n_mb - first);
-    const int within = w - grp * GROUP_M * n_nt;
-    const int mb = first + within % gm;
-    const int nt = within / gm;
-    int lo = 0, hi = E;  // largest expert whose first block is <= mb
+    const int blk = w / n_nt;     // any item of expert e lies in [tstart[e], tstart[e+1]) * n_nt
+    int lo = 0, hi = E;           // largest expert whose first block is <= blk
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
-      if (tstart[mid] <= mb) lo = mid; else hi = mid;
+      if (tstart[mid] <= blk) lo = mid; else hi = mid;
     }
+    const int nb_e = tstart[lo + 1] - tstart[lo];
+    const int local = w - tstart[lo] * n_nt;
+    const int gsz = min(GROUP_M, nb_e);
+    const int grp = local / (gsz * n_nt);
+    const int first = grp * gsz;
+    const int gm = min(gsz, nb_e - first);
+    const int within = local - grp * gsz * n_nt;
+    const int mb = tstart[lo] + first + within % gm;
+    const int nt = within / gm;
     Tile t;
     t.e = lo;
     t.m0 = segoff[lo] + (mb - tstart[lo]) * BM;
