@@ -4,14 +4,20 @@
 // layout must be expert-contiguous with every segment aligned to the GEMM M tile).
 //
 // Three launches:
-//   1. hist_kernel     per 256-token block, slots of each expert (LDS atomics: the
-//                      counts do not depend on their order)
-//   2. scan_kernel     one workgroup: per-expert exclusive scan over the blocks,
-//                      counts, padded offsets, tile -> expert map, error flag
-//   3. scatter_kernel  per 16-token block: stable ranks of its slots (ballot match
-//                      inside a wave, blocks in order), dst_row/src_row, then each
-//                      token row is read once and written to its k rows; extra
-//                      blocks zero the pad rows of every segment and mark unused rows
+//   1. hist_kernel   per 256-token block, the slots of each expert (LDS atomics:
+//                    counts do not depend on their order) and the bad-index count.
+//   2. rank_kernel   every workgroup reads the small histogram table and derives
+//                    the counts, padded offsets and its own starting rank per expert
+//                    (earlier histogram blocks + earlier tokens of its own block),
+//                    so no single-workgroup scan is needed. Token workgroups (16
+//                    tokens each) rank their slots stably (ballot match inside a
+//                    wave) and write dst_row / src_row; the last workgroup writes
+//                    counts, offsets, tile_expert, the unused rows and the error flag.
+//   3. copy_kernel   streams the rows: each token row is read once (16-byte chunks,
+//                    four in flight per thread) and written to its k rows; the pad
+//                    rows of every segment are zeroed by the same grid.
+#include <algorithm>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -20,9 +26,10 @@ namespace {
 
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxK = 32;
-constexpr int kCopyTokens = 16;
+constexpr int kPlaceTokens = 16;
 constexpr int kThreads = 256;
-static_assert(kHistTokens % kCopyTokens == 0, "copy blocks nest in histogram blocks");
+constexpr int kUnroll = 4;   // 16-byte chunks per thread in flight during the copy
+static_assert(kHistTokens % kPlaceTokens == 0, "place blocks nest in histogram blocks");
 
 __global__ __launch_bounds__(kThreads) void hist_kernel(const int32_t* __restrict__ idx, int T,
                                                         int k, int E, int32_t* __restrict__ hist,
@@ -46,7 +53,7 @@ __global__ __launch_bounds__(kThreads) void hist_kernel(const int32_t* __restric
   if (threadIdx.x == 0) bad[blockIdx.x] = nbad;
 }
 
-// Exclusive scan over the 1024 threads of the block.
+// Exclusive prefix sum over the 256 threads of the block.
 __device__ __forceinline__ int block_exclusive_scan(int v, int* wsum) {
   const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
   int inc = v;
@@ -57,109 +64,100 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* wsum) {
   }
   if (lane == kWave - 1) wsum[wid] = inc;
   __syncthreads();
-  if (wid == 0) {
-    int s = lane < 16 ? wsum[lane] : 0;
-#pragma unroll
-    for (int d = 1; d < 16; d <<= 1) {
-      const int o = __shfl_up(s, d);
-      if (lane >= d) s += o;
-    }
-    if (lane < 16) wsum[lane] = s;  // inclusive totals of waves 0..lane
-  }
-  __syncthreads();
-  return inc - v + (wid ? wsum[wid - 1] : 0);
+  int before = 0;
+  for (int w = 0; w < wid; ++w) before += wsum[w];
+  return before + inc - v;
 }
 
-__global__ __launch_bounds__(1024) void scan_kernel(int32_t* __restrict__ hist,
-                                                    const int32_t* __restrict__ bad, int nbh, int E,
-                                                    int m_tile, int64_t m_cap,
-                                                    int32_t* __restrict__ counts,
-                                                    int32_t* __restrict__ offsets,
-                                                    int32_t* __restrict__ tile_expert,
-                                                    int32_t* __restrict__ dev_err) {
-  __shared__ int off[kMaxExperts + 1];
-  __shared__ int wsum[16];
-  __shared__ int anybad;
+__global__ __launch_bounds__(kThreads) void rank_kernel(
+    const int32_t* __restrict__ idx, int T, int k, int E, int m_tile, int64_t m_cap, int nbh,
+    const int32_t* __restrict__ hist, const int32_t* __restrict__ bad,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ tile_expert, int32_t* __restrict__ dev_err,
+    int32_t* __restrict__ dst_row, int32_t* __restrict__ src_row) {
+  __shared__ int off[kMaxExperts + 1];   // padded segment starts
+  __shared__ int cnt[kMaxExperts];       // rows per expert
+  __shared__ int base[kMaxExperts];      // next free row per expert for this block
+  __shared__ int wsum[kThreads / kWave];
   const int tid = threadIdx.x;
-  if (tid == 0) anybad = 0;
-  int padded = 0;
-  if (tid < E) {
-    int run = 0;
-    for (int b = 0; b < nbh; ++b) {
-      const int c = hist[(size_t)b * E + tid];
-      hist[(size_t)b * E + tid] = run;
-      run += c;
-    }
-    counts[tid] = run;
-    padded = (run + m_tile - 1) / m_tile * m_tile;
-  }
-  const int ex = block_exclusive_scan(padded, wsum);
-  if (tid < E) off[tid] = ex;
-  if (tid == E - 1) off[E] = ex + padded;
-  for (int b = tid; b < nbh; b += 1024)
-    if (bad[b]) anybad = 1;
-  __syncthreads();
-  if (tid == 0) *dev_err = anybad;
-  for (int e = tid; e <= E; e += 1024) offsets[e] = off[e];
-  const int total = off[E];
-  const int64_t ntiles = m_cap / m_tile;
-  for (int64_t q = tid; q < ntiles; q += 1024) {
-    const int64_t r = q * m_tile;
-    int owner = -1;
-    if (r < total) {
-      int lo = 0, hi = E;  // largest e with off[e] <= r
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (off[mid] <= r) lo = mid; else hi = mid;
-      }
-      owner = lo;
-    }
-    tile_expert[q] = owner;
-  }
-}
-
-template <typename TIn>
-__global__ __launch_bounds__(kThreads) void scatter_kernel(
-    const TIn* __restrict__ x, const int32_t* __restrict__ idx, int T, int D, int k, int E,
-    int64_t m_cap, const int32_t* __restrict__ hist_base, const int32_t* __restrict__ counts,
-    const int32_t* __restrict__ offsets, int32_t* __restrict__ dst_row,
-    int32_t* __restrict__ src_row, TIn* __restrict__ x_perm) {
-  constexpr int V = Chunk<TIn>::V;
-  const int nck = D / V;
-  const int nbc = (T + kCopyTokens - 1) / kCopyTokens;
+  const int nbp = (T + kPlaceTokens - 1) / kPlaceTokens;
   const int b = blockIdx.x;
-  const int tid = threadIdx.x;
+  const bool token_block = b < nbp;
+  const int t_begin = b * kPlaceTokens;
+  const int hb = token_block ? t_begin / kHistTokens : nbh;
 
-  if (b >= nbc) {
-    if (b < nbc + E) {  // zero the pad rows of segment e and mark them unused
-      const int e = b - nbc;
-      const int r0 = offsets[e] + counts[e], r1 = offsets[e + 1];
-      const u32x4 z = {0u, 0u, 0u, 0u};
-      for (int64_t i = tid; i < (int64_t)(r1 - r0) * nck; i += kThreads) {
-        const int64_t r = r0 + i / nck, c = i % nck;
-        st16(x_perm + r * D + c * V, z);
+  // per-expert totals and this block's starting rank (earlier histogram blocks);
+  // integer LDS atomics, so the sums do not depend on their order
+  for (int e = tid; e < E; e += kThreads) {
+    cnt[e] = 0;
+    base[e] = 0;
+  }
+  __syncthreads();
+  for (int i = tid; i < nbh * E; i += kThreads) {
+    const int h = i / E, e = i - h * E;
+    const int c = hist[i];
+    if (c) {
+      atomicAdd(&cnt[e], c);
+      if (h < hb) atomicAdd(&base[e], c);
+    }
+  }
+  __syncthreads();
+  int padded[4] = {0, 0, 0, 0};
+  int local = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = tid * 4 + i;
+    if (e < E) padded[i] = (cnt[e] + m_tile - 1) / m_tile * m_tile;
+    local += padded[i];
+  }
+  int run = block_exclusive_scan(local, wsum);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = tid * 4 + i;
+    if (e < E) off[e] = run;
+    run += padded[i];
+  }
+  if (tid == kThreads - 1) off[E] = run;
+  __syncthreads();
+
+  if (!token_block) {   // metadata, unused rows, error flag
+    {
+      for (int i = tid; i < E; i += kThreads) counts[i] = cnt[i];
+      for (int i = tid; i <= E; i += kThreads) offsets[i] = off[i];
+      const int total = off[E];
+      const int64_t ntiles = m_cap / m_tile;
+      for (int64_t q = tid; q < ntiles; q += kThreads) {
+        const int64_t r = q * m_tile;
+        int owner = -1;
+        if (r < total) {
+          int lo = 0, hi = E;  // largest e with off[e] <= r
+          while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (off[mid] <= r) lo = mid; else hi = mid;
+          }
+          owner = lo;
+        }
+        tile_expert[q] = owner;
       }
-      for (int r = r0 + tid; r < r1; r += kThreads) src_row[r] = -1;
-    } else {  // rows past the last segment hold no slot
-      for (int64_t r = offsets[E] + tid; r < m_cap; r += kThreads) src_row[r] = -1;
+      for (int e = 0; e < E; ++e)   // pad rows of every segment
+        for (int r = off[e] + cnt[e] + tid; r < off[e + 1]; r += kThreads) src_row[r] = -1;
+      for (int64_t r = total + tid; r < m_cap; r += kThreads) src_row[r] = -1;
+      int anybad = 0;
+      for (int h = tid; h < nbh; h += kThreads) anybad |= bad[h] != 0;
+      anybad = __syncthreads_or(anybad);
+      if (tid == 0) *dev_err = anybad;
     }
     return;
   }
 
-  __shared__ int base[kMaxExperts];
-  __shared__ int dsts[kCopyTokens * kMaxK];
-  const int t_begin = b * kCopyTokens;
-  const int t_end = min(T, t_begin + kCopyTokens);
-  const int hb = t_begin / kHistTokens;
-  for (int e = tid; e < E; e += kThreads) base[e] = offsets[e] + hist_base[(size_t)hb * E + e];
-  __syncthreads();
-  // slots of this histogram block that precede this copy block
+  // slots of this histogram block that precede this workgroup's tokens
   for (int64_t a = (int64_t)hb * kHistTokens * k + tid; a < (int64_t)t_begin * k; a += kThreads) {
     const int e = idx[a];
     if (e >= 0 && e < E) atomicAdd(&base[e], 1);
   }
   __syncthreads();
 
+  const int t_end = min(T, t_begin + kPlaceTokens);
   const int n = (t_end - t_begin) * k;
   const int64_t a0 = (int64_t)t_begin * k;
   if (tid < kWave) {
@@ -172,33 +170,60 @@ __global__ __launch_bounds__(kThreads) void scatter_kernel(
       const bool valid = a < n && e >= 0 && e < E;
       uint64_t same = __ballot(valid);
       for (int bit = 0; bit < nbits; ++bit) {
-        const bool on = valid && ((e >> bit) & 1);
-        const uint64_t bal = __ballot(on);
+        const uint64_t bal = __ballot(valid && ((e >> bit) & 1));
         same &= ((e >> bit) & 1) ? bal : ~bal;
       }
       int pos = -1;
-      if (valid) pos = base[e] + __popcll(same & lt);
+      if (valid) pos = off[e] + base[e] + __popcll(same & lt);
       if (pos >= m_cap) pos = -1;  // cannot happen with consistent counts; never write past m_cap
       __builtin_amdgcn_wave_barrier();
       if (valid && (same >> lane) == 1ull) base[e] = base[e] + __popcll(same);
       __builtin_amdgcn_wave_barrier();
       if (a < n) {
-        dsts[a] = pos;
         dst_row[a0 + a] = pos;
         if (pos >= 0) src_row[pos] = (int32_t)(a0 + a);
       }
     }
   }
-  __syncthreads();
+}
 
-  const int ntok = t_end - t_begin;
-  for (int i = tid; i < ntok * nck; i += kThreads) {
-    const int tl = i / nck, c = i - tl * nck;
-    const u32x4 v = ld16(x + (size_t)(t_begin + tl) * D + (size_t)c * V);
-    for (int j = 0; j < k; ++j) {
-      const int d = dsts[tl * k + j];
-      if (d >= 0) st16(x_perm + (size_t)d * D + (size_t)c * V, v);
+// Row copy: grid-stride over the T x (D/V) chunks of x (each read once) followed by
+// the pad rows of every segment (zeroed). dst_row, offsets and counts come from
+// rank_kernel.
+template <typename TIn>
+__global__ __launch_bounds__(kThreads) void copy_kernel(
+    const TIn* __restrict__ x, int T, int D, int k, int E, const int32_t* __restrict__ dst_row,
+    const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
+    TIn* __restrict__ x_perm) {
+  constexpr int V = Chunk<TIn>::V;
+  const int nck = D / V;
+  const int64_t ncopy = (int64_t)T * nck;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t g0 = (int64_t)blockIdx.x * kThreads + threadIdx.x; g0 < ncopy; g0 += stride * kUnroll) {
+    u32x4 v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t g = min(g0 + u * stride, ncopy - 1);
+      v[u] = ld16_nt(x + (g / nck) * D + (g % nck) * V);
     }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t g = g0 + u * stride;
+      if (g >= ncopy) continue;
+      const int64_t t = g / nck, c = g % nck;
+      for (int j = 0; j < k; ++j) {
+        const int d = dst_row[t * k + j];
+        if (d >= 0) st16(x_perm + (int64_t)d * D + c * V, v[u]);
+      }
+    }
+  }
+  // pad rows: [offsets[e] + counts[e], offsets[e+1]) for every expert
+  const u32x4 z = {0u, 0u, 0u, 0u};
+  for (int e = 0; e < E; ++e) {
+    const int r0 = offsets[e] + counts[e], r1 = offsets[e + 1];
+    const int64_t n = (int64_t)(r1 - r0) * nck;
+    for (int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x; g < n; g += stride)
+      st16(x_perm + (r0 + g / nck) * D + (g % nck) * V, z);
   }
 }
 
@@ -218,18 +243,21 @@ hipError_t launch_permute(int dt, const void* x, const int32_t* topk_idx, int T,
   int32_t* hist = static_cast<int32_t*>(workspace);
   int32_t* bad = hist + (size_t)nbh * E;
   hipLaunchKernelGGL(hist_kernel, dim3(nbh), dim3(kThreads), 0, s, topk_idx, T, k, E, hist, bad);
-  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, s, hist, bad, nbh, E, m_tile, m_cap,
-                     counts, offsets, tile_expert, dev_err);
-  const int nbc = (T + kCopyTokens - 1) / kCopyTokens;
-  const dim3 grid(nbc + E + 1);
+  const int nbp = (T + kPlaceTokens - 1) / kPlaceTokens;
+  hipLaunchKernelGGL(rank_kernel, dim3(nbp + 1), dim3(kThreads), 0, s, topk_idx, T, k, E, m_tile,
+                     m_cap, nbh, hist, bad, counts, offsets, tile_expert, dev_err, dst_row,
+                     src_row);
+  const int V = dt == kF32 ? 4 : 8;
+  const int64_t chunks = (int64_t)T * (D / V);
+  const int grid = (int)std::min<int64_t>(8 * cu_count(), (chunks + kThreads * kUnroll - 1) / (kThreads * kUnroll));
   if (dt == kF32)
-    hipLaunchKernelGGL(scatter_kernel<float>, grid, dim3(kThreads), 0, s,
-                       static_cast<const float*>(x), topk_idx, T, D, k, E, m_cap, hist, counts,
-                       offsets, dst_row, src_row, static_cast<float*>(x_perm));
+    hipLaunchKernelGGL(copy_kernel<float>, dim3(grid), dim3(kThreads), 0, s,
+                       static_cast<const float*>(x), T, D, k, E, dst_row, counts, offsets,
+                       static_cast<float*>(x_perm));
   else
-    hipLaunchKernelGGL(scatter_kernel<bf16_t>, grid, dim3(kThreads), 0, s,
-                       static_cast<const bf16_t*>(x), topk_idx, T, D, k, E, m_cap, hist, counts,
-                       offsets, dst_row, src_row, static_cast<bf16_t*>(x_perm));
+    hipLaunchKernelGGL(copy_kernel<bf16_t>, dim3(grid), dim3(kThreads), 0, s,
+                       static_cast<const bf16_t*>(x), T, D, k, E, dst_row, counts, offsets,
+                       static_cast<bf16_t*>(x_perm));
   return hipGetLastError();
 }
 

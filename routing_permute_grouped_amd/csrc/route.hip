@@ -2,13 +2,14 @@
 // llm-infra-atlas, section 1: router.gating logits = x @ W_g^T over [T, E], then
 // routing = top-k + score function -> probs and routing map).
 //
-// One wave handles 8 tokens. For each pass over 8 experts, lane l accumulates the
-// 16-byte chunks c = l, l+64, ... of x[t] . wg[e] for the 8x8 (token, expert)
-// pairs, in increasing d. The 64 lane partials of all 64 pairs are then combined
-// with a recursive-halving exchange whose additions are exactly those of a
-// butterfly over lane distances 32, 16, 8, 4, 2, 1 (each pair's partials meet in
-// the same tree), ending with pair p's logit in lane p. This fixed float32 order
-// is what makes the top-k choice reproducible bit for bit.
+// One wave handles TW tokens; per pass over EC experts lane l accumulates the
+// 16-byte chunks c = l, l+64, ... of x[t] . wg[e] for the TW*EC (token, expert)
+// pairs, in increasing d. With few experts a wave takes 2 tokens (many waves); with
+// more, 8 tokens share every gate-weight read (the gate matrix is re-read per wave). The 64 lane partials of every pair are then
+// combined over lane distances 32, 16, 8, 4, 2, 1: recursive halving while a lane
+// holds more than one pair, then plain butterfly steps. Each pair's partials meet in
+// exactly the butterfly's order, so every logit is the same float32 value the fixed
+// order defines, and the top-k choice is reproducible bit for bit.
 #include <math.h>
 
 #include "common.hpp"
@@ -17,9 +18,7 @@
 namespace moe {
 namespace {
 
-constexpr int kTokPerWave = 8;
-constexpr int kExpPerPass = 8;
-static_assert(kTokPerWave * kExpPerPass == kWave, "one (token, expert) pair per lane");
+constexpr int kWavesPerBlock = 4;
 
 // float32: a rounded multiply followed by a rounded add (no contraction).
 __device__ __forceinline__ void dot_step(float& acc, float a, float b, float) {
@@ -33,80 +32,82 @@ __device__ __forceinline__ void dot_step(float& acc, float a, float b, bf16_t) {
   acc = __builtin_fmaf(a, b, acc);
 }
 
-// One recursive-halving step: lanes keep the half of the pairs whose bit log2(M)
-// matches their own and add the partner's partial of the same pairs.
-template <int M>
-__device__ __forceinline__ void halve(float (&v)[kWave], bool upper) {
+// C partial sums per lane, next lane distance M: halve while C > 1 (keep the half of
+// the pairs whose next index bit matches this lane's bit M, add the partner's partial
+// of the same pairs), then add across the remaining distances. Lane l ends with the
+// full sum of pair l >> (6 - log2(C0)).
+template <int C, int M>
+__device__ __forceinline__ float reduce_pairs(float* v, int lane) {
+  if constexpr (C > 1) {
+    const bool upper = (lane & M) != 0;
 #pragma unroll
-  for (int i = 0; i < M; ++i) {
-    const float send = upper ? v[i] : v[i + M];
-    const float keep = upper ? v[i + M] : v[i];
-    v[i] = keep + __shfl_xor(send, M);
+    for (int i = 0; i < C / 2; ++i) {
+      const float send = upper ? v[i] : v[i + C / 2];
+      const float keep = upper ? v[i + C / 2] : v[i];
+      v[i] = keep + __shfl_xor(send, M);
+    }
+    return reduce_pairs<C / 2, M / 2>(v, lane);
+  } else if constexpr (M >= 1) {
+    v[0] = v[0] + __shfl_xor(v[0], M);
+    return reduce_pairs<1, M / 2>(v, lane);
+  } else {
+    return v[0];
   }
 }
 
-// Recursive halving over distances 32..1: lane l ends with pair l's full sum.
-__device__ __forceinline__ float reduce_pairs(float (&v)[kWave], int lane) {
-  halve<32>(v, lane & 32);
-  halve<16>(v, lane & 16);
-  halve<8>(v, lane & 8);
-  halve<4>(v, lane & 4);
-  halve<2>(v, lane & 2);
-  halve<1>(v, lane & 1);
-  return v[0];
-}
-
-template <typename TIn>
-__global__ __launch_bounds__(kWave) void route_kernel(const TIn* __restrict__ x,
-                                                      const TIn* __restrict__ wg,
-                                                      const float* __restrict__ bias, int T, int D,
-                                                      int E, int k, int renorm,
-                                                      int32_t* __restrict__ topk_idx,
-                                                      float* __restrict__ topk_w,
-                                                      float* __restrict__ logits_out) {
+template <typename TIn, int TW, int EC>
+__global__ __launch_bounds__(kWave * kWavesPerBlock) void route_kernel(
+    const TIn* __restrict__ x, const TIn* __restrict__ wg, const float* __restrict__ bias, int T,
+    int D, int E, int k, int renorm, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
+    float* __restrict__ logits_out) {
   constexpr int V = Chunk<TIn>::V;
-  __shared__ float lg[kTokPerWave][kWave];
-  const int lane = threadIdx.x;
-  const int t0 = blockIdx.x * kTokPerWave;
+  constexpr int P = TW * EC;                     // (token, expert) pairs per pass
+  constexpr int LOGP = P == 16 ? 4 : (P == 32 ? 5 : 6);
+  static_assert(P == 16 || P == 32 || P == 64, "pairs per pass");
+  __shared__ float lg[kWavesPerBlock][TW][kWave];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int t0 = (blockIdx.x * kWavesPerBlock + wave) * TW;
   const int nchunk = D / V;
 
-  for (int e0 = 0; e0 < E; e0 += kExpPerPass) {
-    float acc[kWave];
+  for (int e0 = 0; e0 < E; e0 += EC) {
+    float acc[P];
 #pragma unroll
-    for (int p = 0; p < kWave; ++p) acc[p] = 0.0f;
+    for (int p = 0; p < P; ++p) acc[p] = 0.0f;
     for (int c = lane; c < nchunk; c += kWave) {
-      float xv[kTokPerWave][V];
+      float xv[TW][V];
 #pragma unroll
-      for (int t = 0; t < kTokPerWave; ++t) {
+      for (int t = 0; t < TW; ++t) {
         const int tok = min(t0 + t, T - 1);
         Chunk<TIn>::widen(ld16(x + (size_t)tok * D + (size_t)c * V), xv[t]);
       }
 #pragma unroll
-      for (int e = 0; e < kExpPerPass; ++e) {
+      for (int e = 0; e < EC; ++e) {
         const int ee = min(e0 + e, E - 1);
         float wv[V];
         Chunk<TIn>::widen(ld16(wg + (size_t)ee * D + (size_t)c * V), wv);
 #pragma unroll
-        for (int t = 0; t < kTokPerWave; ++t)
+        for (int t = 0; t < TW; ++t)
 #pragma unroll
-          for (int i = 0; i < V; ++i) dot_step(acc[t * kExpPerPass + e], xv[t][i], wv[i], TIn());
+          for (int i = 0; i < V; ++i) dot_step(acc[t * EC + e], xv[t][i], wv[i], TIn());
       }
     }
-    float logit = reduce_pairs(acc, lane);
-    const int t = lane / kExpPerPass;
-    const int e = e0 + lane % kExpPerPass;
-    if (e < E) {
+    float logit = reduce_pairs<P, kWave / 2>(acc, lane);
+    const int p = lane >> (6 - LOGP);
+    const int t = p / EC;
+    const int e = e0 + p % EC;
+    if (e < E && (lane & ((1 << (6 - LOGP)) - 1)) == 0) {
       if (bias) logit = logit + bias[e];
-      lg[t][e] = logit;
+      lg[wave][t][e] = logit;
     }
   }
   __syncthreads();
 
-  for (int t = 0; t < kTokPerWave; ++t) {
+  for (int t = 0; t < TW; ++t) {
     const int tok = t0 + t;
     if (tok >= T) break;
     const bool have = lane < E;
-    const float l = have ? lg[t][lane] : -INFINITY;
+    const float l = have ? lg[wave][t][lane] : -INFINITY;
     if (logits_out && have) logits_out[(size_t)tok * E + lane] = l;
     float mx = l;
 #pragma unroll
@@ -146,20 +147,34 @@ __global__ __launch_bounds__(kWave) void route_kernel(const TIn* __restrict__ x,
   }
 }
 
+template <typename TIn>
+void launch_typed(const TIn* x, const TIn* wg, const float* bias, int T, int D, int E, int k,
+                  int renorm, int32_t* topk_idx, float* topk_w, float* logits, hipStream_t s) {
+  const dim3 block(kWave * kWavesPerBlock);
+  if (E <= 8) {
+    constexpr int TW = 2;
+    const dim3 grid((T + TW * kWavesPerBlock - 1) / (TW * kWavesPerBlock));
+    hipLaunchKernelGGL((route_kernel<TIn, TW, 8>), grid, block, 0, s, x, wg, bias, T, D, E, k,
+                       renorm, topk_idx, topk_w, logits);
+  } else {
+    constexpr int TW = 8;
+    const dim3 grid((T + TW * kWavesPerBlock - 1) / (TW * kWavesPerBlock));
+    hipLaunchKernelGGL((route_kernel<TIn, TW, 8>), grid, block, 0, s, x, wg, bias, T, D, E, k,
+                       renorm, topk_idx, topk_w, logits);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_route(int dt, const void* x, const void* wg, const float* bias, int T, int D,
                         int E, int k, int renorm, int32_t* topk_idx, float* topk_w, float* logits,
                         hipStream_t s) {
-  const dim3 grid((T + kTokPerWave - 1) / kTokPerWave), block(kWave);
   if (dt == kF32)
-    hipLaunchKernelGGL(route_kernel<float>, grid, block, 0, s, static_cast<const float*>(x),
-                       static_cast<const float*>(wg), bias, T, D, E, k, renorm, topk_idx, topk_w,
-                       logits);
+    launch_typed(static_cast<const float*>(x), static_cast<const float*>(wg), bias, T, D, E, k,
+                 renorm, topk_idx, topk_w, logits, s);
   else
-    hipLaunchKernelGGL(route_kernel<bf16_t>, grid, block, 0, s, static_cast<const bf16_t*>(x),
-                       static_cast<const bf16_t*>(wg), bias, T, D, E, k, renorm, topk_idx, topk_w,
-                       logits);
+    launch_typed(static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(wg), bias, T, D, E, k,
+                 renorm, topk_idx, topk_w, logits, s);
   return hipGetLastError();
 }
 
