@@ -45,7 +45,7 @@ typedef enum {
   MOE_ECAPACITY = 3,    /* m_cap < moe_capacity(...) or m_cap % m_tile != 0         */
   MOE_EWORKSPACE = 4,   /* workspace smaller than moe_permute_workspace_bytes(...)  */
   MOE_EHIP = 5,         /* the HIP runtime reported an error while launching        */
-  MOE_EUNSUPPORTED = 6  /* valid request with no kernel in this build (see below)   */
+  MOE_EUNSUPPORTED = 6  /* valid request with no kernel for it (see below)          */
 } moe_status_t;
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype_t;

@@ -66,7 +66,7 @@ const char* moe_status_str(moe_status_t s) {
     case MOE_ECAPACITY: return "m_cap below the worst-case capacity or not a multiple of m_tile";
     case MOE_EWORKSPACE: return "workspace smaller than moe_permute_workspace_bytes";
     case MOE_EHIP: return "HIP runtime error while launching";
-    case MOE_EUNSUPPORTED: return "no kernel for this combination in this build";
+    case MOE_EUNSUPPORTED: return "no kernel for this combination of dtype and m_tile";
   }
   return "unknown status";
 }
