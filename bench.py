@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--workload", default="dense8_bf16")
     ap.add_argument("--cpu-sample-tokens", type=int, default=4096)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-split-k", action="store_true",
+                    help="give the grouped GEMMs no workspace (every tile whole)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only copy MIB MiB device-to-device 10 times (a kernel of known "
                          "traffic for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE), then exit")
@@ -130,6 +132,7 @@ def main():
         "y": torch.empty((m_cap, D), dtype=tdt, device=dev),
         "out": torch.empty((T, D), dtype=tdt, device=dev),
     }
+    gws = None if args.no_split_k else rpg.grouped_workspace(dev)
     shared = None
     if cfg.n_shared:
         shared = rpg.SharedExperts.from_stacked(d["ws1"], d["ws3"], d["ws2"])
@@ -152,16 +155,16 @@ def main():
         rpg.moe_permute(d["x"], buf["idx"], E, mt, m_cap=m_cap, out=buf, stream=stream)
         mark(2)
         rpg.moe_grouped_fc1_swiglu(buf["x_perm"], buf["offsets"], buf["tile_expert"], d["w1"],
-                                   d["w3"], mt, m_cap, buf["h"], stream=stream)
+                                   d["w3"], mt, m_cap, buf["h"], workspace=gws, stream=stream)
         mark(3)
         rpg.moe_grouped_fc2(buf["h"], buf["offsets"], buf["tile_expert"], d["w2"], mt, m_cap,
-                            buf["y"], stream=stream)
+                            buf["y"], workspace=gws, stream=stream)
         mark(4)
         sh = None
         if shared is not None:
             rpg.moe_grouped_swiglu(d["x"], rows.offsets, rows.tile_expert, shared.w1, shared.w3,
                                    shared.w2, mt, m_cap=rows.m_cap, h=buf["hs"],
-                                   y_perm=buf["ys"], stream=stream)
+                                   y_perm=buf["ys"], workspace=gws, stream=stream)
             sh = buf["ys"][:T]
         mark(5)
         rpg.moe_combine(buf["y"], buf["dst_row"], buf["w"], shared=sh, out=buf["out"],
@@ -216,7 +219,7 @@ def main():
         "data": "synthetic (seeded numpy PCG64 draws; Gaussian inputs and weights)",
         "config": {"workload": cfg.name, "T": T, "D": D, "F": F, "E": E, "k": k, "m_tile": mt,
                    "n_shared": cfg.n_shared, "F_shared": cfg.F_shared,
-                   "routing": cfg.routing},
+                   "routing": cfg.routing, "split_k_tail": gws is not None},
         "roofline": {"kernel": "grouped fc1 + silu(a)*b (gg_bf16_kernel<true>)", "bound": "mfma",
                      "achieved": fc1_tflops, "peak": peak, "unit": "TFLOP/s",
                      "frac": fc1_tflops / peak, "traffic": TRAFFIC_BYTES_PER_LAUNCH.get(cfg.name),

@@ -117,13 +117,25 @@ moe_status_t moe_permute(moe_dtype_t dt, const void* x, const int32_t* topk_idx,
  * m_tile; offsets[E] may be any value <= m_cap (so a dense FFN over T tokens is
  * the call with E = 1, offsets = {0, T}, tile_expert all 0).
  * bf16 needs m_tile in {128, 256}; float32 accepts every m_tile. D*F < 2^31.
+ *
+ * workspace: optional device scratch (16-byte aligned; NULL or ws_bytes 0 for
+ * none), owned by the caller and clobbered by the call. With it the bf16 kernels
+ * split the output tiles of their last, partly filled round over k across the
+ * otherwise idle compute units: each share's float32 sums go to a 256 KiB slot of
+ * the workspace and a second kernel adds the shares in a fixed order and applies
+ * the epilogue. moe_grouped_workspace_bytes() gives the size that lets every
+ * such round split; a smaller one splits less or not at all. The split changes
+ * only the float32 summation order of those tiles; results are deterministic for
+ * a given device and ws_bytes. Calls that share a workspace must not overlap.
+ * float32 ignores the workspace.
  * Errors: MOE_EINVAL, MOE_ESHAPE, MOE_ECAPACITY (m_cap % m_tile),
  * MOE_EUNSUPPORTED, MOE_EHIP.
  */
 moe_status_t moe_grouped_swiglu(moe_dtype_t dt, const void* x_perm, const int32_t* offsets,
                                 const int32_t* tile_expert, int E, int D, int F, int m_tile,
                                 int64_t m_cap, const void* w1, const void* w3, const void* w2,
-                                void* h, void* y_perm, void* stream);
+                                void* h, void* y_perm, void* workspace, size_t ws_bytes,
+                                void* stream);
 
 /*
  * moe_grouped_fc1_swiglu / moe_grouped_fc2 - the two halves of moe_grouped_swiglu
@@ -135,10 +147,11 @@ moe_status_t moe_grouped_swiglu(moe_dtype_t dt, const void* x_perm, const int32_
 moe_status_t moe_grouped_fc1_swiglu(moe_dtype_t dt, const void* x_perm, const int32_t* offsets,
                                     const int32_t* tile_expert, int E, int D, int F, int m_tile,
                                     int64_t m_cap, const void* w1, const void* w3, void* h,
-                                    void* stream);
+                                    void* workspace, size_t ws_bytes, void* stream);
 moe_status_t moe_grouped_fc2(moe_dtype_t dt, const void* h, const int32_t* offsets,
                              const int32_t* tile_expert, int E, int D, int F, int m_tile,
-                             int64_t m_cap, const void* w2, void* y_perm, void* stream);
+                             int64_t m_cap, const void* w2, void* y_perm, void* workspace,
+                             size_t ws_bytes, void* stream);
 
 /*
  * moe_combine - unpermute and weighted reduce ("Expert Parallelism (EP)",
@@ -159,6 +172,10 @@ moe_status_t moe_combine(moe_dtype_t dt, const void* y_perm, const int32_t* dst_
 /* Worst-case rows of the permuted buffer: with N = T*k slots,
  * m_tile * floor((N + min(E, N) * (m_tile - 1)) / m_tile). Returns -1 on bad sizes. */
 int64_t moe_capacity(int T, int k, int E, int m_tile);
+
+/* Workspace bytes with which the grouped GEMM calls on the current device can
+ * split every partly filled last round of tiles over k (256 KiB per compute unit). */
+size_t moe_grouped_workspace_bytes(void);
 
 /* Device scratch bytes moe_permute needs for (T, k, E). Returns 0 on bad sizes. */
 size_t moe_permute_workspace_bytes(int T, int k, int E);

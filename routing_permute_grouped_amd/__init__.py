@@ -3,13 +3,16 @@
 The compute runs in hand-written HIP kernels (libmoe_mi355x.so, C ABI in
 include/moe.h); this package only marshals torch tensors into those calls.
 """
-from ._binding import (LIB_PATH, MOE_BF16, MOE_F32, SIGNATURES, MoEError, lib, moe_capacity,
-                       moe_combine, moe_grouped_fc1_swiglu, moe_grouped_fc2, moe_grouped_swiglu, moe_permute, moe_permute_workspace_bytes,
-                       moe_route, moe_status_str)
+from ._binding import (LIB_PATH, MOE_BF16, MOE_F32, SIGNATURES, MoEError, grouped_workspace,
+                       lib, moe_capacity, moe_combine, moe_grouped_fc1_swiglu, moe_grouped_fc2,
+                       moe_grouped_swiglu, moe_grouped_workspace_bytes, moe_permute,
+                       moe_permute_workspace_bytes, moe_route, moe_status_str)
 from .layer import DenseRows, SharedExperts, moe_layer
 
 __all__ = [
-    "LIB_PATH", "MOE_BF16", "MOE_F32", "SIGNATURES", "MoEError", "lib", "moe_capacity",
-    "moe_combine", "moe_grouped_fc1_swiglu", "moe_grouped_fc2", "moe_grouped_swiglu", "moe_permute", "moe_permute_workspace_bytes",
-    "moe_route", "moe_status_str", "DenseRows", "SharedExperts", "moe_layer",
+    "LIB_PATH", "MOE_BF16", "MOE_F32", "SIGNATURES", "MoEError", "grouped_workspace", "lib",
+    "moe_capacity", "moe_combine", "moe_grouped_fc1_swiglu", "moe_grouped_fc2",
+    "moe_grouped_swiglu", "moe_grouped_workspace_bytes", "moe_permute",
+    "moe_permute_workspace_bytes", "moe_route", "moe_status_str", "DenseRows", "SharedExperts",
+    "moe_layer",
 ]

@@ -26,11 +26,14 @@ SIGNATURES = [
     ("moe_route", _I, [_I, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P]),
     ("moe_permute", _I, [_I, _P, _P, _I, _I, _I, _I, _I, _I64, _P, _P, _P, _P, _P, _P, _P, _SZ,
                          _P, _P]),
-    ("moe_grouped_swiglu", _I, [_I, _P, _P, _P, _I, _I, _I, _I, _I64, _P, _P, _P, _P, _P, _P]),
-    ("moe_grouped_fc1_swiglu", _I, [_I, _P, _P, _P, _I, _I, _I, _I, _I64, _P, _P, _P, _P]),
-    ("moe_grouped_fc2", _I, [_I, _P, _P, _P, _I, _I, _I, _I, _I64, _P, _P, _P]),
+    ("moe_grouped_swiglu", _I, [_I, _P, _P, _P, _I, _I, _I, _I, _I64, _P, _P, _P, _P, _P, _P,
+                                _SZ, _P]),
+    ("moe_grouped_fc1_swiglu", _I, [_I, _P, _P, _P, _I, _I, _I, _I, _I64, _P, _P, _P, _P, _SZ,
+                                    _P]),
+    ("moe_grouped_fc2", _I, [_I, _P, _P, _P, _I, _I, _I, _I, _I64, _P, _P, _P, _SZ, _P]),
     ("moe_combine", _I, [_I, _P, _P, _P, _P, _I, _I, _I, _I64, _P, _P]),
     ("moe_capacity", _I64, [_I, _I, _I, _I]),
+    ("moe_grouped_workspace_bytes", _SZ, []),
     ("moe_permute_workspace_bytes", _SZ, [_I, _I, _I]),
     ("moe_status_str", ctypes.c_char_p, [_I]),
 ]
@@ -44,7 +47,7 @@ class MoEError(RuntimeError):
 
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run `python -m routing_permute_grouped_amd.build`")
+        raise ImportError(f"{LIB_PATH} is not built; run `python routing_permute_grouped_amd/build.py`")
     lib = ctypes.CDLL(LIB_PATH)
     for name, res, args in SIGNATURES:
         fn = getattr(lib, name)
@@ -90,6 +93,19 @@ def moe_capacity(T: int, k: int, E: int, m_tile: int) -> int:
 
 def moe_permute_workspace_bytes(T: int, k: int, E: int) -> int:
     return int(lib.moe_permute_workspace_bytes(T, k, E))
+
+
+def moe_grouped_workspace_bytes() -> int:
+    return int(lib.moe_grouped_workspace_bytes())
+
+
+def grouped_workspace(device) -> torch.Tensor:
+    """A workspace of moe_grouped_workspace_bytes() bytes for the grouped GEMM calls."""
+    return torch.empty(moe_grouped_workspace_bytes(), dtype=torch.uint8, device=device)
+
+
+def _ws(ws: Optional[torch.Tensor]):
+    return (None, 0) if ws is None else (_ptr(ws), ws.numel() * ws.element_size())
 
 
 def moe_status_str(status: int) -> str:
@@ -148,7 +164,8 @@ def moe_permute(x: torch.Tensor, topk_idx: torch.Tensor, E: int, m_tile: int,
 def moe_grouped_swiglu(x_perm: torch.Tensor, offsets: torch.Tensor, tile_expert: torch.Tensor,
                        w1: torch.Tensor, w3: torch.Tensor, w2: torch.Tensor, m_tile: int,
                        m_cap: Optional[int] = None, h: Optional[torch.Tensor] = None,
-                       y_perm: Optional[torch.Tensor] = None, stream=None):
+                       y_perm: Optional[torch.Tensor] = None,
+                       workspace: Optional[torch.Tensor] = None, stream=None):
     E, F, D = w1.shape
     if m_cap is None:
         m_cap = x_perm.shape[0]
@@ -159,27 +176,28 @@ def moe_grouped_swiglu(x_perm: torch.Tensor, offsets: torch.Tensor, tile_expert:
         y_perm = torch.empty((m_cap, D), dtype=x_perm.dtype, device=dev)
     _check("moe_grouped_swiglu", lib.moe_grouped_swiglu(
         _dt(x_perm), _ptr(x_perm), _ptr(offsets), _ptr(tile_expert), E, D, F, m_tile, m_cap,
-        _ptr(w1), _ptr(w3), _ptr(w2), _ptr(h), _ptr(y_perm), _stream(stream)))
+        _ptr(w1), _ptr(w3), _ptr(w2), _ptr(h), _ptr(y_perm), *_ws(workspace), _stream(stream)))
     return h, y_perm
 
 
 def moe_grouped_fc1_swiglu(x_perm: torch.Tensor, offsets: torch.Tensor, tile_expert: torch.Tensor,
                            w1: torch.Tensor, w3: torch.Tensor, m_tile: int, m_cap: int,
-                           h: torch.Tensor, stream=None) -> torch.Tensor:
+                           h: torch.Tensor, workspace: Optional[torch.Tensor] = None,
+                           stream=None) -> torch.Tensor:
     E, F, D = w1.shape
     _check("moe_grouped_fc1_swiglu", lib.moe_grouped_fc1_swiglu(
         _dt(x_perm), _ptr(x_perm), _ptr(offsets), _ptr(tile_expert), E, D, F, m_tile, m_cap,
-        _ptr(w1), _ptr(w3), _ptr(h), _stream(stream)))
+        _ptr(w1), _ptr(w3), _ptr(h), *_ws(workspace), _stream(stream)))
     return h
 
 
 def moe_grouped_fc2(h: torch.Tensor, offsets: torch.Tensor, tile_expert: torch.Tensor,
                     w2: torch.Tensor, m_tile: int, m_cap: int, y_perm: torch.Tensor,
-                    stream=None) -> torch.Tensor:
+                    workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     E, D, F = w2.shape
     _check("moe_grouped_fc2", lib.moe_grouped_fc2(
         _dt(h), _ptr(h), _ptr(offsets), _ptr(tile_expert), E, D, F, m_tile, m_cap, _ptr(w2),
-        _ptr(y_perm), _stream(stream)))
+        _ptr(y_perm), *_ws(workspace), _stream(stream)))
     return y_perm
 
 

@@ -28,6 +28,8 @@
 // float32 kernel: a plain LDS-tiled VALU GEMM (the tiny float32 layer only).
 #include <math.h>
 
+#include <algorithm>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -120,7 +122,7 @@ template <bool FC1, bool HALF>
 __device__ __forceinline__ void run_tile(char* smem, const Tile& t, const bf16_t* __restrict__ A,
                                          const bf16_t* __restrict__ W1,
                                          const bf16_t* __restrict__ W3, bf16_t* __restrict__ C,
-                                         int K, int N) {
+                                         int K, int N, int kb, int ke, float* __restrict__ part) {
   constexpr int NA = HALF ? 2 : 4;   // 1 KiB (8-row) pieces of A per wave per stage
   constexpr int NB = 4;              // pieces of the panel per wave per stage
   constexpr int WM = HALF ? 2 : 4;   // 32-row blocks of A per wave
@@ -130,8 +132,6 @@ __device__ __forceinline__ void run_tile(char* smem, const Tile& t, const bf16_t
   const int wave = tid >> 6;
   const int arow0 = (wave & 1) * (HALF ? 64 : 128);   // first A row of this wave
   const int prow0 = (wave >> 1) * 64;                 // first panel row of this wave
-  const int nk = K / BK;
-
   // Piece j of wave w holds rows 64*j + 8*w .. +7; lane l fills row 64*j + lrow with
   // lrow = 8*w + l/8, 16-byte slot l%8, which holds logical chunk (l%8) ^ ((row/2)%8).
   const int lrow = 8 * wave + (lane >> 3);
@@ -176,13 +176,13 @@ __device__ __forceinline__ void run_tile(char* smem, const Tile& t, const bf16_t
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
   const int fr = lane & 31;
-  issue(0, 0);
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
+  issue(kb, 0);
+  for (int kt = kb; kt < ke; ++kt) {
+    const int cur = (kt - kb) & 1;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    if (kt + 1 < nk) issue(kt + 1, cur ^ 1);
+    if (kt + 1 < ke) issue(kt + 1, cur ^ 1);
     const char* sa = smem + cur * STAGE_BYTES;
     const char* sb = sa + A_BYTES;
     bf16x8 wf[2][WN], af[2][WM];
@@ -213,6 +213,22 @@ __device__ __forceinline__ void run_tile(char* smem, const Tile& t, const bf16_t
 
   // Lane holds column m = lane & 31 of every 32x32 block and panel rows
   // 8*g + 4*(lane >> 5) + i (i = 0..3) for g = 0..3.
+  if (part) {   // split-K share: raw float32 sums, row-major [BM][BP]
+#pragma unroll
+    for (int mb = 0; mb < WM; ++mb) {
+      const int r = arow0 + mb * 32 + fr;
+#pragma unroll
+      for (int nb = 0; nb < WN; ++nb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int pr = prow0 + nb * 32 + g * 8 + (lane >> 5) * 4;
+          const f32x16& a = acc[mb][nb];
+          float4 v = {a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]};
+          *reinterpret_cast<float4*>(part + r * BP + pr) = v;
+        }
+    }
+    return;
+  }
 #pragma unroll
   for (int mb = 0; mb < WM; ++mb) {
     const int r = arow0 + mb * 32 + fr;
@@ -243,72 +259,182 @@ __device__ __forceinline__ void run_tile(char* smem, const Tile& t, const bf16_t
   }
 }
 
+// Per-workgroup schedule tables in LDS: segment starts and the first 256-row block
+// of each expert, built from offsets[] on the device.
+struct Sched {
+  int segoff[MAXE + 1];   // segment starts (clamped to the rows in use)
+  int tstart[MAXE + 1];   // first 256-row block of each expert
+  int wtot[16];
+};
+
+__device__ void build_sched(Sched& sc, const int32_t* __restrict__ offsets, int E, int m_cap) {
+  const int tid = threadIdx.x;
+  const int mend = min(offsets[E], m_cap);
+  for (int e = tid; e <= E; e += blockDim.x) sc.segoff[e] = min(offsets[e], mend);
+  __syncthreads();
+  const int per = (MAXE + blockDim.x - 1) / blockDim.x;   // experts per thread (<= 4)
+  int cnt[4], local = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = tid * per + i;
+    cnt[i] = (i < per && e < E) ? (max(sc.segoff[e + 1] - sc.segoff[e], 0) + BM - 1) / BM : 0;
+    local += cnt[i];
+  }
+  int run = block_scan_excl(local, sc.wtot);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = tid * per + i;
+    if (i < per && e < E) sc.tstart[e] = run;
+    run += cnt[i];
+  }
+  if (tid == (int)blockDim.x - 1) sc.tstart[E] = run;
+  __syncthreads();
+}
+
+// Tiles are numbered expert by expert: expert e owns items [tstart[e], tstart[e+1]) * n_nt,
+// nb_e row blocks x n_nt column tiles, walked in groups of up to GROUP_M row blocks per
+// column sweep so every weight panel is used by all (or GROUP_M) row blocks of its
+// expert back to back.
+__device__ Tile decode_item(const Sched& sc, int E, int n_nt, int cols, int w) {
+  const int blk = w / n_nt;
+  int lo = 0, hi = E;   // largest expert whose first block is <= blk
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (sc.tstart[mid] <= blk) lo = mid; else hi = mid;
+  }
+  const int nb_e = sc.tstart[lo + 1] - sc.tstart[lo];
+  const int local = w - sc.tstart[lo] * n_nt;
+  const int gsz = min(GROUP_M, nb_e);
+  const int grp = local / (gsz * n_nt);
+  const int first = grp * gsz;
+  const int gm = min(gsz, nb_e - first);
+  const int within = local - grp * gsz * n_nt;
+  const int mb = sc.tstart[lo] + first + within % gm;
+  Tile t;
+  t.e = lo;
+  t.m0 = sc.segoff[lo] + (mb - sc.tstart[lo]) * BM;
+  t.rows = min(BM, sc.segoff[lo + 1] - t.m0);
+  t.n0 = (within / gm) * cols;
+  return t;
+}
+
+// Split-K tail: when the last round of tiles would leave at least half of the G
+// workgroups idle, each of its `tail` tiles is cut into S k-ranges (S * tail <= G and
+// <= the workspace slots). Share sh of tail tile i is item full + sh*tail + i and writes
+// its float32 sums to workspace slot sh*tail + i; gg_tail_reduce adds the shares in
+// order sh = 0..S-1. Items [0, full) are whole tiles.
+struct Split {
+  int full, tail, S, nks;
+};
+
+__device__ Split split_plan(int total, int G, int slots, int nk) {
+  Split p;
+  const int rounds = (total + G - 1) / G;
+  p.full = total;
+  p.tail = 0;
+  p.S = 1;
+  p.nks = nk;
+  if (total == 0 || rounds == 0) return p;
+  const int tail = total - (rounds - 1) * G;
+  if (tail > 0 && 2 * tail <= G && slots >= 2 * tail && nk >= 2) {
+    int S = min(min(8, G / tail), min(slots / tail, nk));
+    const int nks = (nk + S - 1) / S;
+    S = (nk + nks - 1) / nks;   // no empty share
+    if (S >= 2) {
+      p.full = (rounds - 1) * G;
+      p.tail = tail;
+      p.S = S;
+      p.nks = nks;
+    }
+  }
+  return p;
+}
+
 template <bool FC1>
 __global__ __launch_bounds__(NTHR, 1) void gg_bf16_kernel(
     const bf16_t* __restrict__ A, const int32_t* __restrict__ offsets, int E, int K, int N,
     int m_cap, const bf16_t* __restrict__ W1, const bf16_t* __restrict__ W3,
-    bf16_t* __restrict__ C) {
+    bf16_t* __restrict__ C, float* __restrict__ ws, int slots) {
   __shared__ __attribute__((aligned(16))) char smem[2 * STAGE_BYTES];
-  __shared__ int segoff[MAXE + 1];   // segment starts (clamped to the rows in use)
-  __shared__ int tstart[MAXE + 1];   // first 256-row block of each expert
-  __shared__ int wtot[NTHR / 64];
+  __shared__ Sched sc;
+  build_sched(sc, offsets, E, m_cap);
 
-  const int tid = threadIdx.x;
-  const int mend = min(offsets[E], m_cap);
-  for (int e = tid; e <= E; e += NTHR) segoff[e] = min(offsets[e], mend);
-  __syncthreads();
-  int cnt[4], local = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int e = tid * 4 + i;
-    cnt[i] = e < E ? (max(segoff[e + 1] - segoff[e], 0) + BM - 1) / BM : 0;
-    local += cnt[i];
-  }
-  int run = block_scan_excl(local, wtot);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int e = tid * 4 + i;
-    if (e < E) tstart[e] = run;
-    run += cnt[i];
-  }
-  if (tid == NTHR - 1) tstart[E] = run;
-  __syncthreads();
-
-  // Tiles are numbered expert by expert: expert e owns items [istart[e], istart[e+1]),
-  // nb_e row blocks x n_nt column tiles, walked in groups of up to GROUP_M row blocks
-  // per column sweep so every weight panel is used by all (or GROUP_M) row blocks of
-  // its expert back to back, on one XCD.
   const int cols = FC1 ? BP / 2 : BP;
   const int n_nt = (N + cols - 1) / cols;
-  const int total = tstart[E] * n_nt;   // istart[e] = tstart[e] * n_nt
+  const int total = sc.tstart[E] * n_nt;
+  const int nk = K / BK;
+  const Split sp = split_plan(total, gridDim.x, ws ? slots : 0, nk);
+  const int items = sp.full + sp.tail * sp.S;
   int vb = blockIdx.x;
   if (gridDim.x % XCDS == 0) vb = (blockIdx.x % XCDS) * (gridDim.x / XCDS) + blockIdx.x / XCDS;
 
-  for (int w = vb; w < total; w += gridDim.x) {
-    const int blk = w / n_nt;     // any item of expert e lies in [tstart[e], tstart[e+1]) * n_nt
-    int lo = 0, hi = E;           // largest expert whose first block is <= blk
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (tstart[mid] <= blk) lo = mid; else hi = mid;
+  for (int w = vb; w < items; w += gridDim.x) {
+    int kb = 0, ke = nk, tile = w;
+    float* part = nullptr;
+    if (w >= sp.full) {   // share sh of tail tile i; shares of one k-range are adjacent
+      const int j = w - sp.full, sh = j / sp.tail, i = j - sh * sp.tail;
+      tile = sp.full + i;
+      kb = sh * sp.nks;
+      ke = min(nk, kb + sp.nks);
+      part = ws + (size_t)j * (BM * BP);
     }
-    const int nb_e = tstart[lo + 1] - tstart[lo];
-    const int local = w - tstart[lo] * n_nt;
-    const int gsz = min(GROUP_M, nb_e);
-    const int grp = local / (gsz * n_nt);
-    const int first = grp * gsz;
-    const int gm = min(gsz, nb_e - first);
-    const int within = local - grp * gsz * n_nt;
-    const int mb = tstart[lo] + first + within % gm;
-    const int nt = within / gm;
-    Tile t;
-    t.e = lo;
-    t.m0 = segoff[lo] + (mb - tstart[lo]) * BM;
-    t.rows = min(BM, segoff[lo + 1] - t.m0);
-    t.n0 = nt * cols;
+    const Tile t = decode_item(sc, E, n_nt, cols, tile);
     if (t.rows > BM / 2)
-      run_tile<FC1, false>(smem, t, A, W1, W3, C, K, N);
+      run_tile<FC1, false>(smem, t, A, W1, W3, C, K, N, kb, ke, part);
     else
-      run_tile<FC1, true>(smem, t, A, W1, W3, C, K, N);
+      run_tile<FC1, true>(smem, t, A, W1, W3, C, K, N, kb, ke, part);
+  }
+}
+
+// Sums the split-K shares of the tail tiles in split order and applies the epilogue
+// (fc1: silu(a)*b; fc2: the sum), rounding once to bf16. G must be the grid size the
+// GEMM ran with.
+template <bool FC1>
+__global__ __launch_bounds__(256) void gg_tail_reduce(const int32_t* __restrict__ offsets, int E,
+                                                      int K, int N, int m_cap, int G, int slots,
+                                                      const float* __restrict__ ws,
+                                                      bf16_t* __restrict__ C) {
+  __shared__ Sched sc;
+  build_sched(sc, offsets, E, m_cap);
+  const int cols = FC1 ? BP / 2 : BP;
+  const int n_nt = (N + cols - 1) / cols;
+  const Split sp = split_plan(sc.tstart[E] * n_nt, G, slots, K / BK);
+  if (sp.tail == 0) return;
+  constexpr int Q = (FC1 ? BP / 2 : BP) / 4;   // 4-column groups per row
+  const int64_t units = (int64_t)sp.tail * BM * Q;
+  for (int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; u < units;
+       u += (int64_t)gridDim.x * blockDim.x) {
+    const int i = (int)(u / (BM * Q));
+    const int rem = (int)(u - (int64_t)i * BM * Q);
+    const int r = rem / Q, q = rem - r * Q;
+    const Tile t = decode_item(sc, E, n_nt, cols, sp.full + i);
+    if (r >= t.rows) continue;
+    const float* base = ws + (size_t)i * (BM * BP) + r * BP;
+    const size_t stride = (size_t)sp.tail * (BM * BP);   // next share of the same tile
+    if (FC1) {
+      const int fl = 4 * q;                              // h column inside the tile
+      const int pa = (fl >> 5) * 64 + (fl & 31);         // its w1 panel row; w3 is 32 later
+      float4 a = {0, 0, 0, 0}, b = {0, 0, 0, 0};
+      for (int sh = 0; sh < sp.S; ++sh) {
+        const float4 va = *reinterpret_cast<const float4*>(base + sh * stride + pa);
+        const float4 vb = *reinterpret_cast<const float4*>(base + sh * stride + pa + 32);
+        a.x += va.x; a.y += va.y; a.z += va.z; a.w += va.w;
+        b.x += vb.x; b.y += vb.y; b.z += vb.z; b.w += vb.w;
+      }
+      const int n = t.n0 + fl;
+      if (n < N)
+        store4(C + (size_t)(t.m0 + r) * N + n, silu_mul(a.x, b.x), silu_mul(a.y, b.y),
+               silu_mul(a.z, b.z), silu_mul(a.w, b.w));
+    } else {
+      const int nl = 4 * q;
+      float4 a = {0, 0, 0, 0};
+      for (int sh = 0; sh < sp.S; ++sh) {
+        const float4 v = *reinterpret_cast<const float4*>(base + sh * stride + nl);
+        a.x += v.x; a.y += v.y; a.z += v.z; a.w += v.w;
+      }
+      const int n = t.n0 + nl;
+      if (n < N) store4(C + (size_t)(t.m0 + r) * N + n, a.x, a.y, a.z, a.w);
+    }
   }
 }
 
@@ -371,10 +497,13 @@ __global__ __launch_bounds__(256) void gg_f32_kernel(const float* __restrict__ A
 
 }  // namespace
 
+size_t grouped_workspace_bytes() { return (size_t)cu_count() * BM * BP * sizeof(float); }
+
 hipError_t launch_grouped_swiglu(int dt, int phases, const void* x_perm, const int32_t* offsets,
                                  const int32_t* tile_expert, int E, int D, int F, int m_tile,
                                  int64_t m_cap, const void* w1, const void* w3, const void* w2,
-                                 void* h, void* y_perm, hipStream_t s) {
+                                 void* h, void* y_perm, void* workspace, size_t ws_bytes,
+                                 hipStream_t s) {
   if (dt == kF32) {
     const dim3 block(256);
     const int mtiles = (int)((m_cap + FM - 1) / FM);
@@ -390,17 +519,27 @@ hipError_t launch_grouped_swiglu(int dt, int phases, const void* x_perm, const i
                          static_cast<float*>(y_perm));
     return hipGetLastError();
   }
-  const dim3 grid(cu_count()), block(NTHR);
-  if (phases & 1)
+  const int G = cu_count();
+  const dim3 grid(G), block(NTHR);
+  float* ws = static_cast<float*>(workspace);
+  const int slots = ws ? (int)std::min<size_t>(ws_bytes / (BM * BP * sizeof(float)), 1 << 20) : 0;
+  const dim3 rgrid(4 * G), rblock(256);
+  if (phases & 1) {
     hipLaunchKernelGGL(gg_bf16_kernel<true>, grid, block, 0, s, static_cast<const bf16_t*>(x_perm),
-                       offsets, E, D, F, (int)m_cap,
-                       static_cast<const bf16_t*>(w1), static_cast<const bf16_t*>(w3),
-                       static_cast<bf16_t*>(h));
-  if (phases & 2)
+                       offsets, E, D, F, (int)m_cap, static_cast<const bf16_t*>(w1),
+                       static_cast<const bf16_t*>(w3), static_cast<bf16_t*>(h), ws, slots);
+    if (slots)
+      hipLaunchKernelGGL(gg_tail_reduce<true>, rgrid, rblock, 0, s, offsets, E, D, F, (int)m_cap,
+                         G, slots, ws, static_cast<bf16_t*>(h));
+  }
+  if (phases & 2) {
     hipLaunchKernelGGL(gg_bf16_kernel<false>, grid, block, 0, s, static_cast<const bf16_t*>(h),
-                       offsets, E, F, D, (int)m_cap,
-                       static_cast<const bf16_t*>(w2), static_cast<const bf16_t*>(w2),
-                       static_cast<bf16_t*>(y_perm));
+                       offsets, E, F, D, (int)m_cap, static_cast<const bf16_t*>(w2),
+                       static_cast<const bf16_t*>(w2), static_cast<bf16_t*>(y_perm), ws, slots);
+    if (slots)
+      hipLaunchKernelGGL(gg_tail_reduce<false>, rgrid, rblock, 0, s, offsets, E, F, D, (int)m_cap,
+                         G, slots, ws, static_cast<bf16_t*>(y_perm));
+  }
   return hipGetLastError();
 }
 

@@ -53,6 +53,8 @@ int64_t moe_capacity(int T, int k, int E, int m_tile) {
   return (N + ne * (m_tile - 1)) / m_tile * m_tile;
 }
 
+size_t moe_grouped_workspace_bytes(void) { return moe::grouped_workspace_bytes(); }
+
 size_t moe_permute_workspace_bytes(int T, int k, int E) {
   if (T < 1 || k < 1 || E < 1 || E > kMaxExperts || !tk_ok(T, k)) return 0;
   return moe::permute_workspace_bytes(T, k, E);
@@ -107,9 +109,12 @@ moe_status_t moe_permute(moe_dtype_t dt, const void* x, const int32_t* topk_idx,
 static moe_status_t grouped(int phases, moe_dtype_t dt, const void* x_perm,
                             const int32_t* offsets, const int32_t* tile_expert, int E, int D, int F,
                             int m_tile, int64_t m_cap, const void* w1, const void* w3,
-                            const void* w2, void* h, void* y_perm, void* stream) {
+                            const void* w2, void* h, void* y_perm, void* workspace,
+                            size_t ws_bytes, void* stream) {
   if (!dtype_ok(dt) || !aligned4(offsets) || !aligned4(tile_expert) || !aligned16(h))
     return MOE_EINVAL;
+  if (workspace && !aligned16(workspace)) return MOE_EINVAL;
+  if (!workspace) ws_bytes = 0;
   if ((phases & 1) && (!aligned16(x_perm) || !aligned16(w1) || !aligned16(w3))) return MOE_EINVAL;
   if ((phases & 2) && (!aligned16(w2) || !aligned16(y_perm))) return MOE_EINVAL;
   if (E < 1 || E > kMaxExperts || !dim_ok(D) || !dim_ok(F) || !mtile_ok(m_tile)) return MOE_ESHAPE;
@@ -118,30 +123,33 @@ static moe_status_t grouped(int phases, moe_dtype_t dt, const void* x_perm,
   if (dt == MOE_BF16 && m_tile != 128 && m_tile != 256) return MOE_EUNSUPPORTED;
   return hip_status(moe::launch_grouped_swiglu(dt, phases, x_perm, offsets, tile_expert, E, D, F,
                                                m_tile, m_cap, w1, w3, w2, h, y_perm,
+                                               ws_bytes ? workspace : nullptr, ws_bytes,
                                                static_cast<hipStream_t>(stream)));
 }
 
 moe_status_t moe_grouped_swiglu(moe_dtype_t dt, const void* x_perm, const int32_t* offsets,
                                 const int32_t* tile_expert, int E, int D, int F, int m_tile,
                                 int64_t m_cap, const void* w1, const void* w3, const void* w2,
-                                void* h, void* y_perm, void* stream) {
+                                void* h, void* y_perm, void* workspace, size_t ws_bytes,
+                                void* stream) {
   return grouped(3, dt, x_perm, offsets, tile_expert, E, D, F, m_tile, m_cap, w1, w3, w2, h,
-                 y_perm, stream);
+                 y_perm, workspace, ws_bytes, stream);
 }
 
 moe_status_t moe_grouped_fc1_swiglu(moe_dtype_t dt, const void* x_perm, const int32_t* offsets,
                                     const int32_t* tile_expert, int E, int D, int F, int m_tile,
                                     int64_t m_cap, const void* w1, const void* w3, void* h,
-                                    void* stream) {
+                                    void* workspace, size_t ws_bytes, void* stream) {
   return grouped(1, dt, x_perm, offsets, tile_expert, E, D, F, m_tile, m_cap, w1, w3, nullptr, h,
-                 nullptr, stream);
+                 nullptr, workspace, ws_bytes, stream);
 }
 
 moe_status_t moe_grouped_fc2(moe_dtype_t dt, const void* h, const int32_t* offsets,
                              const int32_t* tile_expert, int E, int D, int F, int m_tile,
-                             int64_t m_cap, const void* w2, void* y_perm, void* stream) {
+                             int64_t m_cap, const void* w2, void* y_perm, void* workspace,
+                             size_t ws_bytes, void* stream) {
   return grouped(2, dt, nullptr, offsets, tile_expert, E, D, F, m_tile, m_cap, nullptr, nullptr,
-                 w2, const_cast<void*>(h), y_perm, stream);
+                 w2, const_cast<void*>(h), y_perm, workspace, ws_bytes, stream);
 }
 
 moe_status_t moe_combine(moe_dtype_t dt, const void* y_perm, const int32_t* dst_row,

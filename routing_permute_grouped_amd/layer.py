@@ -44,10 +44,11 @@ def moe_layer(x: torch.Tensor, w1: torch.Tensor, w3: torch.Tensor, w2: torch.Ten
               m_tile: int, wg: Optional[torch.Tensor] = None, bias: Optional[torch.Tensor] = None,
               topk_idx: Optional[torch.Tensor] = None, topk_w: Optional[torch.Tensor] = None,
               shared: Optional[SharedExperts] = None, renorm: bool = False,
-              check: bool = False) -> dict:
+              check: bool = False, split_k: bool = True) -> dict:
     """Run the layer; returns every intermediate (dict). With routing given
     (``topk_idx``/``topk_w``) the route step is skipped. ``check`` synchronises and
-    raises if the permute saw an expert index outside [-1, E)."""
+    raises if the permute saw an expert index outside [-1, E). ``split_k`` gives the
+    grouped GEMMs a workspace so they can split a partly filled last round of tiles."""
     E = w1.shape[0]
     res = {}
     if topk_idx is None:
@@ -55,14 +56,15 @@ def moe_layer(x: torch.Tensor, w1: torch.Tensor, w3: torch.Tensor, w2: torch.Ten
     res["topk_idx"], res["topk_w"] = topk_idx, topk_w
     p = B.moe_permute(x, topk_idx, E, m_tile)
     res.update(p)
+    ws = B.grouped_workspace(x.device) if split_k else None
     h, y = B.moe_grouped_swiglu(p["x_perm"], p["offsets"], p["tile_expert"], w1, w3, w2, m_tile,
-                                m_cap=p["m_cap"])
+                                m_cap=p["m_cap"], workspace=ws)
     res["h"], res["y_perm"] = h, y
     sh = None
     if shared is not None:
         rows = DenseRows(x.shape[0], m_tile, x.device)
         _, ys = B.moe_grouped_swiglu(x, rows.offsets, rows.tile_expert, shared.w1, shared.w3,
-                                     shared.w2, m_tile, m_cap=rows.m_cap)
+                                     shared.w2, m_tile, m_cap=rows.m_cap, workspace=ws)
         sh = ys[: x.shape[0]]
         res["shared"] = sh
     res["out"] = B.moe_combine(y, p["dst_row"], topk_w, shared=sh, m_cap=p["m_cap"])

@@ -42,9 +42,12 @@ def poison(t: torch.Tensor) -> torch.Tensor:
     return t.fill_(float("nan"))
 
 
-def run_gpu(inp: dict, k: int, m_tile: int, renorm: bool = False, want_logits: bool = True) -> dict:
+def run_gpu(inp: dict, k: int, m_tile: int, renorm: bool = False, want_logits: bool = True,
+            ws_bytes: int | None = None) -> dict:
     """Run route (unless routing is given), permute, grouped SwiGLU (routed and shared)
-    and combine; every float output buffer is NaN-poisoned first."""
+    and combine; every float output buffer is NaN-poisoned first. The grouped calls get
+    a NaN-poisoned workspace of ``ws_bytes`` (default moe_grouped_workspace_bytes(); 0 =
+    none, so no split-K tail)."""
     d = {n: to_dev(a) for n, a in inp.items() if isinstance(a, np.ndarray)}
     E = inp["w1"].shape[0]
     T = inp["x"].shape[0]
@@ -61,10 +64,15 @@ def run_gpu(inp: dict, k: int, m_tile: int, renorm: bool = False, want_logits: b
     p = rpg.moe_permute(d["x"], idx, E, m_tile, m_cap=m_cap, out={"x_perm": xp})
     out.update(p)
     F = inp["w1"].shape[1]
+    if ws_bytes is None:
+        ws_bytes = rpg.moe_grouped_workspace_bytes()
+    ws = None
+    if ws_bytes:
+        ws = poison(torch.empty(ws_bytes // 4, dtype=torch.float32, device="cuda"))
     h = poison(torch.empty((m_cap, F), dtype=d["x"].dtype, device="cuda"))
     y = poison(torch.empty((m_cap, inp["x"].shape[1]), dtype=d["x"].dtype, device="cuda"))
     rpg.moe_grouped_swiglu(p["x_perm"], p["offsets"], p["tile_expert"], d["w1"], d["w3"], d["w2"],
-                           m_tile, m_cap=m_cap, h=h, y_perm=y)
+                           m_tile, m_cap=m_cap, h=h, y_perm=y, workspace=ws)
     out["h"], out["y_perm"] = h, y
     shared = None
     if "ws1" in d:
@@ -73,7 +81,7 @@ def run_gpu(inp: dict, k: int, m_tile: int, renorm: bool = False, want_logits: b
         hs = poison(torch.empty((rows.m_cap, sw.w1.shape[1]), dtype=d["x"].dtype, device="cuda"))
         ys = poison(torch.empty((rows.m_cap, inp["x"].shape[1]), dtype=d["x"].dtype, device="cuda"))
         rpg.moe_grouped_swiglu(d["x"], rows.offsets, rows.tile_expert, sw.w1, sw.w3, sw.w2, m_tile,
-                               m_cap=rows.m_cap, h=hs, y_perm=ys)
+                               m_cap=rows.m_cap, h=hs, y_perm=ys, workspace=ws)
         shared = ys[:T]
         out["shared"] = shared
     o = poison(torch.empty_like(d["x"]))
@@ -83,10 +91,10 @@ def run_gpu(inp: dict, k: int, m_tile: int, renorm: bool = False, want_logits: b
 
 
 def check_layer(inp: dict, k: int, m_tile: int, dtype: str, renorm: bool = False,
-                expect_dev_err: int = 0) -> dict:
+                expect_dev_err: int = 0, ws_bytes: int | None = None) -> dict:
     """Full element-by-element parity of every output of the layer against the oracle."""
     ref = orc.forward(inp, k=k, m_tile=m_tile, dtype=dtype, renorm=renorm)
-    g = run_gpu(inp, k, m_tile, renorm)
+    g = run_gpu(inp, k, m_tile, renorm, ws_bytes=ws_bytes)
     tol = TOL[dtype]
     if "logits" in ref:
         np.testing.assert_array_equal(g["logits"].view(np.uint32), ref["logits"].view(np.uint32))

@@ -26,6 +26,7 @@ def test_header_declares_the_four_calls_and_helpers():
     assert declared_symbols() == sorted(["moe_route", "moe_permute", "moe_grouped_swiglu",
                                          "moe_grouped_fc1_swiglu", "moe_grouped_fc2",
                                          "moe_combine", "moe_capacity",
+                                         "moe_grouped_workspace_bytes",
                                          "moe_permute_workspace_bytes", "moe_status_str"])
 
 
@@ -93,16 +94,19 @@ def test_permute_validation(kw, code):
     assert permute(**kw) == code
 
 
-def grouped(dt=1, xp=FAKE, E=8, D=128, F=256, mt=128, m_cap=1024, w1=FAKE, h=FAKE):
+def grouped(dt=1, xp=FAKE, E=8, D=128, F=256, mt=128, m_cap=1024, w1=FAKE, h=FAKE, ws=None,
+            ws_bytes=0):
     return lib.moe_grouped_swiglu(dt, xp, FAKE, FAKE, E, D, F, mt, m_cap, w1, FAKE, FAKE, h, FAKE,
-                                  None)
+                                  ws, ws_bytes, None)
 
 
 @pytest.mark.parametrize("kw,code", [
     (dict(dt=5), MOE_EINVAL), (dict(w1=None), MOE_EINVAL), (dict(h=FAKE + 8), MOE_EINVAL),
     (dict(E=0), MOE_ESHAPE), (dict(F=100), MOE_ESHAPE), (dict(D=32), MOE_ESHAPE),
     (dict(mt=7), MOE_ESHAPE), (dict(m_cap=0), MOE_ECAPACITY), (dict(m_cap=1000), MOE_ECAPACITY),
-    (dict(mt=64, m_cap=1024), MOE_EUNSUPPORTED), (dict(D=65536, F=32768), MOE_ESHAPE), (dict(mt=16, m_cap=1024), MOE_EUNSUPPORTED),
+    (dict(mt=64, m_cap=1024), MOE_EUNSUPPORTED), (dict(D=65536, F=32768), MOE_ESHAPE),
+    (dict(mt=16, m_cap=1024), MOE_EUNSUPPORTED), (dict(ws=FAKE + 8, ws_bytes=1 << 20), MOE_EINVAL),
+    (dict(dt=7, ws=FAKE, ws_bytes=1 << 20), MOE_EINVAL),
 ])
 def test_grouped_validation(kw, code):
     assert grouped(**kw) == code
@@ -110,13 +114,20 @@ def test_grouped_validation(kw, code):
 
 def test_split_grouped_calls_validate():
     assert lib.moe_grouped_fc1_swiglu(1, FAKE, FAKE, FAKE, 8, 128, 256, 128, 1024, None, FAKE,
-                                      FAKE, None) == MOE_EINVAL
+                                      FAKE, None, 0, None) == MOE_EINVAL
     assert lib.moe_grouped_fc1_swiglu(1, FAKE, FAKE, FAKE, 8, 128, 250, 128, 1024, FAKE, FAKE,
-                                      FAKE, None) == MOE_ESHAPE
+                                      FAKE, None, 0, None) == MOE_ESHAPE
+    assert lib.moe_grouped_fc1_swiglu(1, FAKE, FAKE, FAKE, 8, 128, 256, 128, 1024, FAKE, FAKE,
+                                      FAKE, FAKE + 4, 1 << 20, None) == MOE_EINVAL
     assert lib.moe_grouped_fc2(1, FAKE, FAKE, FAKE, 8, 128, 256, 128, 1000, FAKE, FAKE,
-                               None) == MOE_ECAPACITY
+                               None, 0, None) == MOE_ECAPACITY
     assert lib.moe_grouped_fc2(1, FAKE, FAKE, FAKE, 8, 128, 256, 64, 1024, FAKE, FAKE,
-                               None) == MOE_EUNSUPPORTED
+                               FAKE, 1 << 20, None) == MOE_EUNSUPPORTED
+
+
+def test_grouped_workspace_size_is_whole_slots():
+    n = rpg.moe_grouped_workspace_bytes()
+    assert n > 0 and n % (256 * 256 * 4) == 0
 
 
 def combine(dt=1, y=FAKE, dst=FAKE, w=FAKE, shared=None, T=64, D=128, k=2, m_cap=640, out=FAKE):

@@ -94,6 +94,27 @@ def test_out_of_range_expert_ids_are_flagged_and_skipped():
     assert P.rel_err(g["out"], ref["out"]) <= P.TOL["bf16"]
 
 
+@pytest.mark.parametrize("ws_slots", [0, 10])
+def test_grouped_gemm_workspace_sizes(ws_slots):
+    # no workspace: every tile whole; 10 slots of 256x256 float32: fc1's 4 tiles split
+    # in 2 k-ranges and fc2's 2 tiles in 4, unlike the default size (8 and 4)
+    P.log(f"[parity] E=1 k=1 workspace {ws_slots} slots")
+    P.check_layer(_bf16_layer(300, 256, 256, 1, 1), 1, 128, "bf16",
+                  ws_bytes=ws_slots * 256 * 256 * 4)
+
+
+def test_split_k_tail_agrees_with_whole_tiles():
+    P.log("[parity] split-K tail vs whole tiles")
+    inp = W.generate(SMALL["dense8"], seed=5)
+    a = P.run_gpu(inp, 2, 128)
+    b = P.run_gpu(inp, 2, 128, ws_bytes=0)
+    used = int(a["offsets"][-1])
+    # only the float32 summation order of the split tiles differs, so the two bf16
+    # results are at most a rounding step or two apart
+    for key in ("h", "y_perm"):
+        assert P.rel_err(a[key][:used], orc.values64(b[key][:used])) <= 2.0 ** -7, key
+
+
 def test_bitwise_run_to_run_determinism():
     P.log("[parity] determinism")
     inp = W.generate(SMALL["fine64_shared2"], seed=4)
