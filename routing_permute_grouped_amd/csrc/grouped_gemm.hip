@@ -92,15 +92,31 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) char*)p);
 }
 
-// 16 bytes per lane from global memory straight into LDS: the 64 lanes of the wave
-// fill 1 KiB at LDS address `lds` (made wave-uniform), lane l at lds + 16*l.
-// Issued as inline assembly so the compiler adds no waits of its own for it; the
-// pipeline below waits with an explicit s_waitcnt vmcnt(0) and a barrier before
-// any wave reads the stage the loads fill.
-__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+// Raw buffer descriptor over [base, base + bytes): the hardware zero-fills any lane
+// whose offset falls outside the range.
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4 buffer_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((int32_t)(uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int32_t)((uint32_t)(a >> 32) & 0xffffu));
+  r[2] = __builtin_amdgcn_readfirstlane((int32_t)bytes);
+  r[3] = 0x00020000;   // raw (untyped) buffer, 32-bit data format
+  return r;
+}
+
+// 16 bytes per lane from a buffer straight into LDS: lane l reads base + voff_l + soff
+// and the 64 lanes of the wave fill 1 KiB at LDS address `lds` (wave-uniform), lane l
+// at lds + 16*l. Buffer addressing takes a 32-bit offset per lane and the k-step in a
+// scalar offset, which issues faster than 64-bit flat addresses. Issued as inline
+// assembly so the compiler adds no waits of its own for it; the pipeline below waits
+// with an explicit s_waitcnt vmcnt(0) and a barrier before any wave reads the stage
+// the loads fill.
+__device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
                :
-               : "v"(g), "s"(__builtin_amdgcn_readfirstlane(lds))
+               : "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(soff)),
+                 "s"(__builtin_amdgcn_readfirstlane(lds))
                : "memory", "m0");
 }
 
@@ -112,7 +128,7 @@ __device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
 // For fc1 the 64 panel rows of a wave are one w1 block and one w3 block covering the
 // same 32 h columns, so silu(a)*b is formed in registers.
 //
-// Pipeline: two LDS stages filled by direct global->LDS loads. Iteration kt waits
+// Pipeline: two LDS stages filled by direct buffer->LDS loads. Iteration kt waits
 // for its own loads of stage kt, meets the other waves at a barrier (after which
 // every wave has finished reading stage kt-1 and all of stage kt has landed),
 // issues the loads of k-step kt+1 into the free stage, then runs the MFMAs of kt
@@ -136,35 +152,34 @@ __device__ __forceinline__ void run_tile(char* smem, const Tile& t, const bf16_t
   // lrow = 8*w + l/8, 16-byte slot l%8, which holds logical chunk (l%8) ^ ((row/2)%8).
   const int lrow = 8 * wave + (lane >> 3);
   const int lchunk = (lane & 7) ^ ((lrow >> 1) & 7);
+  // Byte offsets (k-step 0) of this lane's rows: A inside the tile's rows, the panel
+  // inside expert e's matrix. Rows past the tile or the matrix are clamped to the last.
   uint32_t aoff[NA];
 #pragma unroll
-  for (int j = 0; j < NA; ++j) aoff[j] = (uint32_t)(min(64 * j + lrow, t.rows - 1) * K + lchunk * 8);
-  const bf16_t* abase = A + (size_t)t.m0 * K;
+  for (int j = 0; j < NA; ++j)
+    aoff[j] = (uint32_t)(min(64 * j + lrow, t.rows - 1) * K + lchunk * 8) * 2u;
+  const i32x4 rsa = buffer_rsrc(A + (size_t)t.m0 * K, (uint32_t)t.rows * K * 2u);
+  // fc1: panel rows alternate 32-row blocks of w1 and w3 over the same 32 columns;
+  // row 64*j + lrow is in a w3 block exactly when lrow >= 32, i.e. for waves 4..7
+  const bf16_t* wsel = (FC1 && wave >= 4) ? W3 : W1;
+  const i32x4 rsb = buffer_rsrc(wsel + (size_t)t.e * N * K, (uint32_t)N * K * 2u);
   uint32_t boff[NB];
-  const bf16_t* bbase[NB];
 #pragma unroll
   for (int j = 0; j < NB; ++j) {
     const int pr = 64 * j + lrow;
-    int gr;
-    if (FC1) {  // 32-row blocks alternate w1, w3 over the same 32 columns
-      bbase[j] = (((pr >> 5) & 1) ? W3 : W1) + (size_t)t.e * N * K;
-      gr = t.n0 + (pr >> 6) * 32 + (pr & 31);
-    } else {
-      bbase[j] = W1 + (size_t)t.e * N * K;
-      gr = t.n0 + pr;
-    }
-    boff[j] = (uint32_t)(min(gr, N - 1) * K + lchunk * 8);
+    const int gr = FC1 ? t.n0 + (pr >> 6) * 32 + (pr & 31) : t.n0 + pr;
+    boff[j] = (uint32_t)(min(gr, N - 1) * K + lchunk * 8) * 2u;
   }
 
   const uint32_t lds0 = lds_addr(smem) + wave * 1024;
   auto issue = [&](int kt, int stage) {
     const uint32_t la = lds0 + stage * STAGE_BYTES;
     const uint32_t lb = la + A_BYTES;
-    const int ko = kt * BK;
+    const uint32_t ko = (uint32_t)kt * BK * 2u;
 #pragma unroll
-    for (int j = 0; j < NA; ++j) dma16(abase + aoff[j] + ko, la + j * 8192);
+    for (int j = 0; j < NA; ++j) dma16(rsa, aoff[j], ko, la + j * 8192);
 #pragma unroll
-    for (int j = 0; j < NB; ++j) dma16(bbase[j] + boff[j] + ko, lb + j * 8192);
+    for (int j = 0; j < NB; ++j) dma16(rsb, boff[j], ko, lb + j * 8192);
   };
 
   f32x16 acc[WM][WN];
