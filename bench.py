@@ -3,10 +3,13 @@
 
 One step = route -> permute -> grouped fc1+SwiGLU -> grouped fc2 [-> shared experts]
 -> combine over one batch of seeded synthetic tokens, all inputs resident in HBM.
+Between timed steps (outside the HIP-event brackets of each step) a 512 MiB buffer is
+written so the 256 MB Infinity Cache holds nothing of the previous step.
 Prints one JSON line: MoE-layer tokens/s, the grouped GEMM's TFLOP/s and fraction
 of the bf16 MFMA peak, the permute and combine GB/s and fraction of HBM bandwidth,
-the roofline of the dominant kernel (grouped fc1) measured with HIP events on the
-stream the kernels run on, and the CPU oracle timed on a bounded sample.
+per-stage median / p10 / p90 / CV, the roofline of the dominant kernel (grouped fc1)
+measured with HIP events on the stream the kernels run on, and the CPU oracle timed
+on a bounded sample.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME]
 """
@@ -30,19 +33,21 @@ METRIC = "MoE-layer tokens/sec; grouped-GEMM TFLOP/s (% bf16 MFMA peak); permute
 # rocprofv3 FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0, the factors measured on a device copy of
 # known size (bench.py --copy-calibration 256). Taken for the current kernel source;
 # a workload without an entry reports null.
-TRAFFIC_BYTES_PER_LAUNCH = {"dense8_bf16": 7.305e9}
+TRAFFIC_BYTES_PER_LAUNCH = {"dense8_bf16": 7.247e9}
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="dense8_bf16")
     ap.add_argument("--cpu-sample-tokens", type=int, default=4096)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-split-k", action="store_true",
                     help="give the grouped GEMMs no workspace (every tile whole)")
+    ap.add_argument("--flush-mib", type=int, default=512,
+                    help="MiB written between timed steps to evict the Infinity Cache (0: none)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only copy MIB MiB device-to-device 10 times (a kernel of known "
                          "traffic for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE), then exit")
@@ -171,6 +176,8 @@ def main():
                         m_cap=m_cap, stream=stream)
         mark(6)
 
+    flush = (torch.empty(args.flush_mib * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
+             if args.flush_mib > 0 else None)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -182,14 +189,24 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
+        if flush is not None:
+            flush.fill_(float(s))          # outside the step's event brackets
         step(events[s])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
     per = {m: [events[s][i].elapsed_time(events[s][i + 1]) * 1e3 for s in range(args.steps)]
            for i, m in enumerate(marks)}
+    per["step"] = [events[s][0].elapsed_time(events[s][-1]) * 1e3 for s in range(args.steps)]
     med = {m: statistics.median(v) for m, v in per.items()}
     avg = {m: statistics.fmean(v) for m, v in per.items()}
+
+    def pct(v, q):
+        return float(np.percentile(np.asarray(v), q))
+
+    spread = {m: {"p10": pct(v, 10), "p90": pct(v, 90),
+                  "cv": statistics.pstdev(v) / statistics.fmean(v) if statistics.fmean(v) else 0.0}
+              for m, v in per.items()}
 
     counts = buf["counts"].cpu().numpy().astype(np.int64)
     n_valid = int(counts.sum())
@@ -203,10 +220,10 @@ def main():
     comb_gbps = comb_bytes / (avg["combine"] * 1e-6) / 1e9
     peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
     fc1_tflops = fc1_flop / (avg["fc1"] * 1e-6) / 1e12
-    ms_per_step = wall * 1e3 / args.steps
+    ms_per_step = avg["step"] * 1e-3
     rec = {
         "metric": METRIC,
-        "value": T * args.steps / wall,
+        "value": T / (avg["step"] * 1e-6),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -229,7 +246,10 @@ def main():
         "grouped_gemm_frac_bf16_peak": gemm_tflops / peak,
         "permute_GBps": perm_gbps, "permute_frac_hbm": perm_gbps / PEAK_HBM_GBPS,
         "combine_GBps": comb_gbps, "combine_frac_hbm": comb_gbps / PEAK_HBM_GBPS,
-        "stage_us_median": med, "stage_us_mean": avg,
+        "stage_us_median": med, "stage_us_mean": avg, "stage_us_spread": spread,
+        "timing": {"value_from": "sum of per-step HIP-event durations on the compute stream",
+                   "cache_flush_MiB_between_steps": args.flush_mib,
+                   "wall_ms_per_step_incl_flush": wall * 1e3 / args.steps},
         "assignments": n_valid, "padded_rows": int(buf["offsets"][-1].item()),
         "expert_rows_min_max": [int(counts.min()), int(counts.max())],
         "cpu_baseline": None,
