@@ -43,7 +43,7 @@ constexpr int BM = 256;        // rows per full tile
 constexpr int BP = 256;        // weight-panel rows per tile
 constexpr int BK = 64;         // k per stage
 constexpr int NTHR = 512;      // 8 waves, two per SIMD
-constexpr int GROUP_M = 16;    // at most this many 256-row blocks per column sweep
+constexpr int GROUP_M = 4;     // at most this many 256-row blocks per column sweep
 constexpr int XCDS = 8;
 constexpr int MAXE = 1024;
 constexpr int A_BYTES = BM * BK * 2;
