@@ -2,14 +2,17 @@
 // llm-infra-atlas, section 1: router.gating logits = x @ W_g^T over [T, E], then
 // routing = top-k + score function -> probs and routing map).
 //
-// One wave handles TW tokens; per pass over EC experts lane l accumulates the
-// 16-byte chunks c = l, l+64, ... of x[t] . wg[e] for the TW*EC (token, expert)
-// pairs, in increasing d. With few experts a wave takes 2 tokens (many waves); with
-// more, 8 tokens share every gate-weight read (the gate matrix is re-read per wave). The 64 lane partials of every pair are then
-// combined over lane distances 32, 16, 8, 4, 2, 1: recursive halving while a lane
-// holds more than one pair, then plain butterfly steps. Each pair's partials meet in
-// exactly the butterfly's order, so every logit is the same float32 value the fixed
-// order defines, and the top-k choice is reproducible bit for bit.
+// A pass covers TW tokens x EC experts: lane l accumulates the 16-byte chunks
+// c = l, l+64, ... of x[t] . wg[e] for the TW*EC (token, expert) pairs, in increasing d.
+// With at most 8 experts every wave takes its own 2 tokens and does the one pass.
+// With more, the 4 waves of a block share 8 tokens (every gate-weight chunk a wave
+// reads serves 8 tokens) and take the passes over the experts in turn, so there are
+// four times as many waves to hide memory latency; the logits meet in LDS and each
+// wave then routes 2 of the tokens. The 64 lane partials of every pair are combined
+// over lane distances 32, 16, 8, 4, 2, 1: recursive halving while a lane holds more
+// than one pair, then plain butterfly steps. Each pair's partials meet in exactly the
+// butterfly's order, so every logit is the same float32 value the fixed order defines,
+// and the top-k choice is reproducible bit for bit.
 #include <math.h>
 
 #include "common.hpp"
@@ -55,7 +58,7 @@ __device__ __forceinline__ float reduce_pairs(float* v, int lane) {
   }
 }
 
-template <typename TIn, int TW, int EC>
+template <typename TIn, int TW, int EC, bool SHARED>
 __global__ __launch_bounds__(kWave * kWavesPerBlock) void route_kernel(
     const TIn* __restrict__ x, const TIn* __restrict__ wg, const float* __restrict__ bias, int T,
     int D, int E, int k, int renorm, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
@@ -64,13 +67,16 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock) void route_kernel(
   constexpr int P = TW * EC;                     // (token, expert) pairs per pass
   constexpr int LOGP = P == 16 ? 4 : (P == 32 ? 5 : 6);
   static_assert(P == 16 || P == 32 || P == 64, "pairs per pass");
-  __shared__ float lg[kWavesPerBlock][TW][kWave];
+  constexpr int NL = SHARED ? 1 : kWavesPerBlock;   // logit tables per block
+  __shared__ float lg[NL][TW][kWave];
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
-  const int t0 = (blockIdx.x * kWavesPerBlock + wave) * TW;
+  // SHARED: the block's waves share tokens t0 .. t0+TW-1 and split the passes
+  const int t0 = SHARED ? blockIdx.x * TW : (blockIdx.x * kWavesPerBlock + wave) * TW;
+  const int tab = SHARED ? 0 : wave;
   const int nchunk = D / V;
 
-  for (int e0 = 0; e0 < E; e0 += EC) {
+  for (int e0 = SHARED ? wave * EC : 0; e0 < E; e0 += SHARED ? kWavesPerBlock * EC : EC) {
     float acc[P];
 #pragma unroll
     for (int p = 0; p < P; ++p) acc[p] = 0.0f;
@@ -98,16 +104,16 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock) void route_kernel(
     const int e = e0 + p % EC;
     if (e < E && (lane & ((1 << (6 - LOGP)) - 1)) == 0) {
       if (bias) logit = logit + bias[e];
-      lg[wave][t][e] = logit;
+      lg[tab][t][e] = logit;
     }
   }
   __syncthreads();
 
-  for (int t = 0; t < TW; ++t) {
+  for (int t = SHARED ? wave : 0; t < TW; t += SHARED ? kWavesPerBlock : 1) {
     const int tok = t0 + t;
     if (tok >= T) break;
     const bool have = lane < E;
-    const float l = have ? lg[wave][t][lane] : -INFINITY;
+    const float l = have ? lg[tab][t][lane] : -INFINITY;
     if (logits_out && have) logits_out[(size_t)tok * E + lane] = l;
     float mx = l;
 #pragma unroll
@@ -154,13 +160,13 @@ void launch_typed(const TIn* x, const TIn* wg, const float* bias, int T, int D, 
   if (E <= 8) {
     constexpr int TW = 2;
     const dim3 grid((T + TW * kWavesPerBlock - 1) / (TW * kWavesPerBlock));
-    hipLaunchKernelGGL((route_kernel<TIn, TW, 8>), grid, block, 0, s, x, wg, bias, T, D, E, k,
-                       renorm, topk_idx, topk_w, logits);
+    hipLaunchKernelGGL((route_kernel<TIn, TW, 8, false>), grid, block, 0, s, x, wg, bias, T, D,
+                       E, k, renorm, topk_idx, topk_w, logits);
   } else {
     constexpr int TW = 8;
-    const dim3 grid((T + TW * kWavesPerBlock - 1) / (TW * kWavesPerBlock));
-    hipLaunchKernelGGL((route_kernel<TIn, TW, 8>), grid, block, 0, s, x, wg, bias, T, D, E, k,
-                       renorm, topk_idx, topk_w, logits);
+    const dim3 grid((T + TW - 1) / TW);
+    hipLaunchKernelGGL((route_kernel<TIn, TW, 8, true>), grid, block, 0, s, x, wg, bias, T, D, E,
+                       k, renorm, topk_idx, topk_w, logits);
   }
 }
 
