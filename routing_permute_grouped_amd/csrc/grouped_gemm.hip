@@ -120,7 +120,61 @@ __device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t voff, uint32_t soff, 
                : "memory", "m0");
 }
 
-// One tile: rows [m0, m0 + rows) of expert e against the weight panel from n0.
+// Load addresses of one tile at k-step 0, per lane: buffer descriptors for its A rows
+// and for expert e's weight matrix, and the byte offsets of the rows this lane fills.
+// Piece j of wave w holds rows 64*j + 8*w .. +7; lane l fills row 64*j + lrow with
+// lrow = 8*w + l/8, 16-byte slot l%8, which holds logical chunk (l%8) ^ ((row/2)%8).
+// Rows past the tile or the matrix are clamped to the last one.
+struct TileLoads {
+  i32x4 rsa, rsb;
+  uint32_t aoff[4], boff[4];
+  int na;   // A pieces per wave: 4 for a full tile, 2 for a half tile
+};
+
+template <bool FC1>
+__device__ __forceinline__ TileLoads tile_loads(const Tile& t, const bf16_t* __restrict__ A,
+                                                const bf16_t* __restrict__ W1,
+                                                const bf16_t* __restrict__ W3, int K, int N) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int lrow = 8 * wave + (lane >> 3);
+  const int lchunk = (lane & 7) ^ ((lrow >> 1) & 7);
+  TileLoads o;
+  o.na = t.rows > BM / 2 ? 4 : 2;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    o.aoff[j] = (uint32_t)(min(64 * j + lrow, t.rows - 1) * K + lchunk * 8) * 2u;
+  o.rsa = buffer_rsrc(A + (size_t)t.m0 * K, (uint32_t)t.rows * K * 2u);
+  // fc1: panel rows alternate 32-row blocks of w1 and w3 over the same 32 columns;
+  // row 64*j + lrow is in a w3 block exactly when lrow >= 32, i.e. for waves 4..7
+  const bf16_t* wsel = (FC1 && wave >= 4) ? W3 : W1;
+  o.rsb = buffer_rsrc(wsel + (size_t)t.e * N * K, (uint32_t)N * K * 2u);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int pr = 64 * j + lrow;
+    const int gr = FC1 ? t.n0 + (pr >> 6) * 32 + (pr & 31) : t.n0 + pr;
+    o.boff[j] = (uint32_t)(min(gr, N - 1) * K + lchunk * 8) * 2u;
+  }
+  return o;
+}
+
+// Loads of k-step kt into the LDS stage at `la` (this wave's first piece): the A pieces
+// (part 0) or the panel pieces (part 1).
+__device__ __forceinline__ void issue_loads(const TileLoads& o, uint32_t la, int kt, int part) {
+  const uint32_t ko = (uint32_t)kt * BK * 2u;
+  if (part == 0) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (j < o.na) dma16(o.rsa, o.aoff[j], ko, la + j * 8192);
+  } else {
+    const uint32_t lb = la + A_BYTES;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dma16(o.rsb, o.boff[j], ko, lb + j * 8192);
+  }
+}
+
+// One tile: rows [m0, m0 + rows) of expert e against the weight panel from n0, k-steps
+// [kb, ke).
 //
 // Eight waves, two per SIMD. Full tile: wave w owns rows 128*(w%2) .. +127 and panel
 // rows 64*(w/2) .. +63 (4 x 2 MFMA blocks of 32x32, 128 accumulators). Half tile
@@ -128,21 +182,22 @@ __device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t voff, uint32_t soff, 
 // For fc1 the 64 panel rows of a wave are one w1 block and one w3 block covering the
 // same 32 h columns, so silu(a)*b is formed in registers.
 //
-// Pipeline: two LDS stages filled by direct buffer->LDS loads. Iteration kt waits
-// for its own loads of stage kt, meets the other waves at a barrier (after which
-// every wave has finished reading stage kt-1 and all of stage kt has landed), then
-// runs the MFMAs of kt with the fragments of the next 16-wide k slice loaded while
-// the current slice's MFMAs run; the loads of k-step kt+1 into the free stage are
-// issued in two halves (A, then the panel) under the first two slices, which keeps
-// the memory system from seeing all of a CU's requests in one burst (5-8% faster
-// than issuing them all right after the barrier).
+// Pipeline: two LDS stages filled by direct buffer->LDS loads; step kb uses stage
+// `stage0`. Iteration kt waits for its own loads of its stage, meets the other waves
+// at a barrier (after which every wave has finished reading the other stage and all
+// of this one has landed), then runs the MFMAs of kt with the fragments of the next
+// 16-wide k slice loaded while the current slice's MFMAs run. The loads of k-step
+// kt+1 into the free stage are issued in two halves (A, then the panel) under the
+// first two slices, which keeps the memory system from seeing all of a CU's requests
+// in one burst (5-8% faster than issuing them right after the barrier). In the last
+// step the free stage instead receives the first step of the next tile (`nxt`, step
+// `nkb`), so its load latency hides under this tile's last MFMAs and its epilogue;
+// `primed` says that this tile's first step was loaded that way.
 template <bool FC1, bool HALF>
-__device__ __forceinline__ void run_tile(char* smem, const Tile& t, const bf16_t* __restrict__ A,
-                                         const bf16_t* __restrict__ W1,
-                                         const bf16_t* __restrict__ W3, bf16_t* __restrict__ C,
-                                         int K, int N, int kb, int ke, float* __restrict__ part) {
-  constexpr int NA = HALF ? 2 : 4;   // 1 KiB (8-row) pieces of A per wave per stage
-  constexpr int NB = 4;              // pieces of the panel per wave per stage
+__device__ __forceinline__ void run_tile(char* smem, const Tile& t, const TileLoads& ld,
+                                         bf16_t* __restrict__ C, int N, int kb, int ke,
+                                         float* __restrict__ part, int stage0, bool primed,
+                                         const TileLoads& nxt, bool has_next, int nkb) {
   constexpr int WM = HALF ? 2 : 4;   // 32-row blocks of A per wave
   constexpr int WN = 2;              // 32-row panel blocks per wave
   const int tid = threadIdx.x;
@@ -150,43 +205,7 @@ __device__ __forceinline__ void run_tile(char* smem, const Tile& t, const bf16_t
   const int wave = tid >> 6;
   const int arow0 = (wave & 1) * (HALF ? 64 : 128);   // first A row of this wave
   const int prow0 = (wave >> 1) * 64;                 // first panel row of this wave
-  // Piece j of wave w holds rows 64*j + 8*w .. +7; lane l fills row 64*j + lrow with
-  // lrow = 8*w + l/8, 16-byte slot l%8, which holds logical chunk (l%8) ^ ((row/2)%8).
-  const int lrow = 8 * wave + (lane >> 3);
-  const int lchunk = (lane & 7) ^ ((lrow >> 1) & 7);
-  // Byte offsets (k-step 0) of this lane's rows: A inside the tile's rows, the panel
-  // inside expert e's matrix. Rows past the tile or the matrix are clamped to the last.
-  uint32_t aoff[NA];
-#pragma unroll
-  for (int j = 0; j < NA; ++j)
-    aoff[j] = (uint32_t)(min(64 * j + lrow, t.rows - 1) * K + lchunk * 8) * 2u;
-  const i32x4 rsa = buffer_rsrc(A + (size_t)t.m0 * K, (uint32_t)t.rows * K * 2u);
-  // fc1: panel rows alternate 32-row blocks of w1 and w3 over the same 32 columns;
-  // row 64*j + lrow is in a w3 block exactly when lrow >= 32, i.e. for waves 4..7
-  const bf16_t* wsel = (FC1 && wave >= 4) ? W3 : W1;
-  const i32x4 rsb = buffer_rsrc(wsel + (size_t)t.e * N * K, (uint32_t)N * K * 2u);
-  uint32_t boff[NB];
-#pragma unroll
-  for (int j = 0; j < NB; ++j) {
-    const int pr = 64 * j + lrow;
-    const int gr = FC1 ? t.n0 + (pr >> 6) * 32 + (pr & 31) : t.n0 + pr;
-    boff[j] = (uint32_t)(min(gr, N - 1) * K + lchunk * 8) * 2u;
-  }
-
   const uint32_t lds0 = lds_addr(smem) + wave * 1024;
-  // Loads of k-step kt into `stage`: the A pieces (part 0), the panel pieces (part 1).
-  auto issue = [&](int kt, int stage, int part) {
-    const uint32_t la = lds0 + stage * STAGE_BYTES;
-    const uint32_t lb = la + A_BYTES;
-    const uint32_t ko = (uint32_t)kt * BK * 2u;
-    if (part == 0) {
-#pragma unroll
-      for (int j = 0; j < NA; ++j) dma16(rsa, aoff[j], ko, la + j * 8192);
-    } else {
-#pragma unroll
-      for (int j = 0; j < NB; ++j) dma16(rsb, boff[j], ko, lb + j * 8192);
-    }
-  };
 
   f32x16 acc[WM][WN];
 #pragma unroll
@@ -197,10 +216,12 @@ __device__ __forceinline__ void run_tile(char* smem, const Tile& t, const bf16_t
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
   const int fr = lane & 31;
-  issue(kb, 0, 0);
-  issue(kb, 0, 1);
+  if (!primed) {
+    issue_loads(ld, lds0 + stage0 * STAGE_BYTES, kb, 0);
+    issue_loads(ld, lds0 + stage0 * STAGE_BYTES, kb, 1);
+  }
   for (int kt = kb; kt < ke; ++kt) {
-    const int cur = (kt - kb) & 1;
+    const int cur = (stage0 + kt - kb) & 1;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
@@ -221,7 +242,10 @@ __device__ __forceinline__ void run_tile(char* smem, const Tile& t, const bf16_t
     for (int ks = 0; ks < BK / 16; ++ks) {
       // the next stage's loads go out in two halves under the first two k slices
       // rather than in one burst after the barrier
-      if (ks < 2 && kt + 1 < ke) issue(kt + 1, cur ^ 1, ks);
+      if (ks < 2) {
+        if (kt + 1 < ke) issue_loads(ld, lds0 + (cur ^ 1) * STAGE_BYTES, kt + 1, ks);
+        else if (has_next) issue_loads(nxt, lds0 + (cur ^ 1) * STAGE_BYTES, nkb, ks);
+      }
       if (ks + 1 < BK / 16) frag(ks + 1, (ks + 1) & 1);
 #pragma unroll
       for (int mb = 0; mb < WM; ++mb)
@@ -231,9 +255,9 @@ __device__ __forceinline__ void run_tile(char* smem, const Tile& t, const bf16_t
                                                                 acc[mb][nb], 0, 0, 0);
     }
   }
-  // every wave is done with both stages before the next tile refills them
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
+  // No barrier here: the next tile's first step went into the stage nobody reads in
+  // this tile's last step, and its second step's loads are issued only after its
+  // first barrier, which every wave reaches after finishing this tile's MFMAs.
 
   // Lane holds column m = lane & 31 of every 32x32 block and panel rows
   // 8*g + 4*(lane >> 5) + i (i = 0..3) for g = 0..3.
@@ -392,21 +416,52 @@ __global__ __launch_bounds__(NTHR, 1) void gg_bf16_kernel(
   int vb = blockIdx.x;
   if (gridDim.x % XCDS == 0) vb = (blockIdx.x % XCDS) * (gridDim.x / XCDS) + blockIdx.x / XCDS;
 
-  for (int w = vb; w < items; w += gridDim.x) {
-    int kb = 0, ke = nk, tile = w;
-    float* part = nullptr;
+  // work item w: tile, k-range and (for a split-K share) its workspace slot
+  struct Work {
+    Tile t;
+    int kb, ke;
+    float* part;
+  };
+  auto work = [&](int w) {
+    Work r;
+    int tile = w;
+    r.kb = 0;
+    r.ke = nk;
+    r.part = nullptr;
     if (w >= sp.full) {   // share sh of tail tile i; shares of one k-range are adjacent
       const int j = w - sp.full, sh = j / sp.tail, i = j - sh * sp.tail;
       tile = sp.full + i;
-      kb = sh * sp.nks;
-      ke = min(nk, kb + sp.nks);
-      part = ws + (size_t)j * (BM * BP);
+      r.kb = sh * sp.nks;
+      r.ke = min(nk, r.kb + sp.nks);
+      r.part = ws + (size_t)j * (BM * BP);
     }
-    const Tile t = decode_item(sc, E, n_nt, cols, tile);
-    if (t.rows > BM / 2)
-      run_tile<FC1, false>(smem, t, A, W1, W3, C, K, N, kb, ke, part);
+    r.t = decode_item(sc, E, n_nt, cols, tile);
+    return r;
+  };
+
+  if (vb >= items) return;
+  Work cur = work(vb);
+  TileLoads ld = tile_loads<FC1>(cur.t, A, W1, W3, K, N);
+  int stage0 = 0;
+  bool primed = false;
+  for (int w = vb; w < items; w += gridDim.x) {
+    const bool has_next = w + (int)gridDim.x < items;
+    Work nw = cur;
+    TileLoads nl = ld;
+    if (has_next) {
+      nw = work(w + gridDim.x);
+      nl = tile_loads<FC1>(nw.t, A, W1, W3, K, N);
+    }
+    if (cur.t.rows > BM / 2)
+      run_tile<FC1, false>(smem, cur.t, ld, C, N, cur.kb, cur.ke, cur.part, stage0, primed, nl,
+                           has_next, nw.kb);
     else
-      run_tile<FC1, true>(smem, t, A, W1, W3, C, K, N, kb, ke, part);
+      run_tile<FC1, true>(smem, cur.t, ld, C, N, cur.kb, cur.ke, cur.part, stage0, primed, nl,
+                          has_next, nw.kb);
+    stage0 = (stage0 + cur.ke - cur.kb) & 1;
+    primed = has_next;
+    cur = nw;
+    ld = nl;
   }
 }
 
