@@ -33,7 +33,7 @@ METRIC = "MoE-layer tokens/sec; grouped-GEMM TFLOP/s (% bf16 MFMA peak); permute
 # rocprofv3 FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0, the factors measured on a device copy of
 # known size (bench.py --copy-calibration 256). Taken for the current kernel source;
 # a workload without an entry reports null.
-TRAFFIC_BYTES_PER_LAUNCH = {"dense8_bf16": 7.247e9}
+TRAFFIC_BYTES_PER_LAUNCH = {"dense8_bf16": 4.361e9}
 
 
 def parse():
