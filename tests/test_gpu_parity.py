@@ -10,6 +10,7 @@ import numpy as np
 import pytest
 import torch
 
+import routing_permute_grouped_amd as rpg
 import workloads as W
 from oracle import moe_oracle as orc
 from tests import _parity as P
@@ -113,6 +114,49 @@ def test_split_k_tail_agrees_with_whole_tiles():
     # results are at most a rounding step or two apart
     for key in ("h", "y_perm"):
         assert P.rel_err(a[key][:used], orc.values64(b[key][:used])) <= 2.0 ** -7, key
+
+
+# More tiles than workgroups: every workgroup runs several tiles back to back (the next
+# tile's first k-step loaded during the current one's last step, stages alternating),
+# half tiles follow full ones, and the last round is split over k.
+MULTI_ROUND = {
+    "dense8_multiround": W.shrink(W.preset("dense8_bf16"), T=4096, D=512, F=2048),
+    "skew32_multiround": W.shrink(W.preset("skew32_zipf_bf16"), T=4096, D=512, F=1024),
+}
+
+
+@pytest.mark.parametrize("name", list(MULTI_ROUND))
+def test_layer_parity_multi_round(name):
+    cfg = MULTI_ROUND[name]
+    P.log(f"[parity] {name}: {cfg}")
+    inp = W.generate(cfg, seed=7)
+    cfg = inp["cfg"]
+    P.check_layer(inp, cfg.k, cfg.m_tile, cfg.dtype)
+
+
+def test_two_call_form_matches_one_call():
+    # moe_grouped_fc1_swiglu then moe_grouped_fc2 run the same kernels as
+    # moe_grouped_swiglu: identical bits
+    P.log("[parity] fc1 + fc2 calls vs one grouped call")
+    inp = W.generate(MULTI_ROUND["dense8_multiround"], seed=8)
+    d = {n: P.to_dev(a) for n, a in inp.items() if isinstance(a, np.ndarray)}
+    T, k, E = inp["x"].shape[0], 2, inp["w1"].shape[0]
+    idx, w, _ = rpg.moe_route(d["x"], d["wg"], k)
+    m_cap = rpg.moe_capacity(T, k, E, 128)
+    p = rpg.moe_permute(d["x"], idx, E, 128, m_cap=m_cap)
+    ws = rpg.grouped_workspace(d["x"].device)
+    h1, y1 = rpg.moe_grouped_swiglu(p["x_perm"], p["offsets"], p["tile_expert"], d["w1"], d["w3"],
+                                    d["w2"], 128, m_cap=m_cap, workspace=ws)
+    F, D = inp["w1"].shape[1], inp["x"].shape[1]
+    h2 = torch.empty((m_cap, F), dtype=d["x"].dtype, device="cuda")
+    y2 = torch.empty((m_cap, D), dtype=d["x"].dtype, device="cuda")
+    rpg.moe_grouped_fc1_swiglu(p["x_perm"], p["offsets"], p["tile_expert"], d["w1"], d["w3"], 128,
+                               m_cap, h2, workspace=ws)
+    rpg.moe_grouped_fc2(h2, p["offsets"], p["tile_expert"], d["w2"], 128, m_cap, y2, workspace=ws)
+    torch.cuda.synchronize()
+    used = int(p["offsets"][-1].item())
+    assert torch.equal(h1[:used].view(torch.int16), h2[:used].view(torch.int16))
+    assert torch.equal(y1[:used].view(torch.int16), y2[:used].view(torch.int16))
 
 
 def test_bitwise_run_to_run_determinism():
