@@ -134,6 +134,15 @@ def test_layer_parity_multi_round(name):
     P.check_layer(inp, cfg.k, cfg.m_tile, cfg.dtype)
 
 
+def test_max_experts_given_routing():
+    # E = 1024 (the largest the library takes): the grouped GEMM's per-expert schedule
+    # tables are full; ~1000 one-half-tile segments, F = 192 ragged against 128 columns
+    cfg = W.shrink(W.preset("etp_shard32_bf16"), E=1024, k=8, D=128, F=192, poisson_mean=6.0)
+    P.log(f"[parity] E=1024 given routing: {cfg}")
+    inp = W.generate(cfg, seed=11)
+    P.check_layer(inp, 8, 128, "bf16")
+
+
 def test_two_call_form_matches_one_call():
     # moe_grouped_fc1_swiglu then moe_grouped_fc2 run the same kernels as
     # moe_grouped_swiglu: identical bits
