@@ -46,6 +46,11 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-split-k", action="store_true",
                     help="give the grouped GEMMs no workspace (every tile whole)")
+    ap.add_argument("--shared-overlap", choices=["none", "start", "after-route"],
+                    default="none",
+                    help="run the shared experts' GEMM on a second stream (with its own "
+                         "split-K workspace), from the step's start or after the router; the "
+                         "per-stage times of route / permute then include waiting for CUs")
     ap.add_argument("--flush-mib", type=int, default=512,
                     help="MiB written between timed steps to evict the Infinity Cache (0: none)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -147,15 +152,35 @@ def main():
     routed = "wg" in d
     stream = torch.cuda.current_stream()
     marks = ["route", "permute", "fc1", "fc2", "shared", "combine"]
+    overlap = shared is not None and args.shared_overlap != "none"
+    if overlap:
+        side = torch.cuda.Stream(device=dev)          # default priority
+        gws_side = None if args.no_split_k else rpg.grouped_workspace(dev)
+        ev_go, ev_sh = torch.cuda.Event(), torch.cuda.Event()
+
+    def shared_gemm(on, ws):
+        rpg.moe_grouped_swiglu(d["x"], rows.offsets, rows.tile_expert, shared.w1, shared.w3,
+                               shared.w2, mt, m_cap=rows.m_cap, h=buf["hs"], y_perm=buf["ys"],
+                               workspace=ws, stream=on)
+
+    def launch_side():
+        ev_go.record(stream)
+        side.wait_event(ev_go)
+        shared_gemm(side, gws_side)
+        ev_sh.record(side)
 
     def step(ev=None):
         def mark(i):
             if ev is not None:
                 ev[i].record(stream)
         mark(0)
+        if overlap and args.shared_overlap == "start":
+            launch_side()
         if routed:
             rpg.moe_route(d["x"], d["wg"], k, bias=d.get("bias"), topk_idx=buf["idx"],
                           topk_w=buf["w"], stream=stream)
+        if overlap and args.shared_overlap == "after-route":
+            launch_side()
         mark(1)
         rpg.moe_permute(d["x"], buf["idx"], E, mt, m_cap=m_cap, out=buf, stream=stream)
         mark(2)
@@ -167,9 +192,10 @@ def main():
         mark(4)
         sh = None
         if shared is not None:
-            rpg.moe_grouped_swiglu(d["x"], rows.offsets, rows.tile_expert, shared.w1, shared.w3,
-                                   shared.w2, mt, m_cap=rows.m_cap, h=buf["hs"],
-                                   y_perm=buf["ys"], workspace=gws, stream=stream)
+            if overlap:
+                stream.wait_event(ev_sh)
+            else:
+                shared_gemm(stream, gws)
             sh = buf["ys"][:T]
         mark(5)
         rpg.moe_combine(buf["y"], buf["dst_row"], buf["w"], shared=sh, out=buf["out"],
@@ -236,7 +262,8 @@ def main():
         "data": "synthetic (seeded numpy PCG64 draws; Gaussian inputs and weights)",
         "config": {"workload": cfg.name, "T": T, "D": D, "F": F, "E": E, "k": k, "m_tile": mt,
                    "n_shared": cfg.n_shared, "F_shared": cfg.F_shared,
-                   "routing": cfg.routing, "split_k_tail": gws is not None},
+                   "routing": cfg.routing, "split_k_tail": gws is not None,
+                   "shared_overlap": args.shared_overlap if shared is not None else None},
         "roofline": {"kernel": "grouped fc1 + silu(a)*b (gg_bf16_kernel<true>)", "bound": "mfma",
                      "achieved": fc1_tflops, "peak": peak, "unit": "TFLOP/s",
                      "frac": fc1_tflops / peak, "traffic": TRAFFIC_BYTES_PER_LAUNCH.get(cfg.name),
