@@ -75,26 +75,50 @@ def copy_calibration(mib: int) -> None:
 
 def cpu_baseline(inp: dict, cfg, tokens: int, min_seconds: float = 10.0) -> dict:
     """The oracle as it stands, on the first ``tokens`` tokens of the same workload,
-    repeated (at most 8 passes) until about ``min_seconds`` of CPU work is timed."""
+    repeated (at most 8 passes) until about ``min_seconds`` of CPU work is timed. Each
+    pass calls the oracle's stage functions in the order of ``oracle.forward`` and times
+    each stage with time.perf_counter."""
     from threadpoolctl import threadpool_info
 
     from oracle import moe_oracle as orc
-    sub = dict(inp)
-    sub["x"] = inp["x"][:tokens]
-    if "topk_idx" in inp:
-        sub["topk_idx"], sub["topk_w"] = inp["topk_idx"][:tokens], inp["topk_w"][:tokens]
-    sub.pop("cfg", None)
-    passes, dt = 0, 0.0
-    while passes == 0 or (dt < min_seconds and passes < 8):
-        t0 = time.perf_counter()
-        orc.forward(sub, k=cfg.k, m_tile=cfg.m_tile, dtype=cfg.dtype)
-        dt += time.perf_counter() - t0
+    x = inp["x"][:tokens]
+    E = inp["w1"].shape[0]
+    stages = {"route": 0.0, "layout": 0.0, "permute": 0.0, "experts": 0.0, "shared": 0.0,
+              "combine": 0.0}
+    passes = 0
+    while passes == 0 or (sum(stages.values()) < min_seconds and passes < 8):
+        t = time.perf_counter()
+        if "topk_idx" in inp:
+            idx, w = inp["topk_idx"][:tokens], inp["topk_w"][:tokens].astype(np.float64)
+        else:
+            idx, w, _ = orc.route(x, inp["wg"], cfg.k, cfg.dtype, inp.get("bias"), False)
+        t1 = time.perf_counter()
+        lay = orc.dispatch_layout(idx, E, cfg.m_tile)
+        t2 = time.perf_counter()
+        xp = orc.permute(x, lay)
+        t3 = time.perf_counter()
+        _, y = orc.grouped_swiglu(xp, lay["offsets"], inp["w1"], inp["w3"], inp["w2"], cfg.dtype)
+        t4 = time.perf_counter()
+        sh = None
+        if "ws1" in inp:
+            sh = orc.shared_experts(x, inp["ws1"], inp["ws3"], inp["ws2"], cfg.dtype)
+        t5 = time.perf_counter()
+        orc.combine(y, lay["dst_row"], w, cfg.dtype, sh)
+        t6 = time.perf_counter()
+        for name, dt in zip(stages, (t1 - t, t2 - t1, t3 - t2, t4 - t3, t5 - t4, t6 - t5)):
+            stages[name] += dt
         passes += 1
-    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    return {"value": passes * tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+    total = sum(stages.values())
+    pools = threadpool_info()
+    threads = max([p.get("num_threads", 1) for p in pools] + [1])
+    blas = sorted({f"{p.get('internal_api')} {p.get('version')}" for p in pools
+                   if p.get("user_api") == "blas"})
+    return {"value": passes * tokens / total, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "affinity_cores": len(os.sched_getaffinity(0)), "blas": blas,
+            "stage_s_per_pass": {n: v / passes for n, v in stages.items()},
             "sample": f"first {tokens} tokens of {cfg.name} with every expert's weights; "
-                      f"{passes} oracle forward pass(es) (routing, layout, permute, float64 "
-                      f"experts, combine) took {dt:.2f} s"}
+                      f"{passes} oracle pass(es) (routing, layout, permute, float64 "
+                      f"experts, combine) took {total:.2f} s"}
 
 
 def main():
@@ -236,6 +260,7 @@ def main():
 
     counts = buf["counts"].cpu().numpy().astype(np.int64)
     n_valid = int(counts.sum())
+    n_padded = int(buf["offsets"][-1].item())      # rows the GEMMs compute, pad rows included
     s_el = cfg.elem_bytes
     fc1_flop = 4.0 * n_valid * D * F
     fc2_flop = 2.0 * n_valid * D * F
@@ -271,13 +296,16 @@ def main():
                      "algorithmic_flop_per_launch": fc1_flop, "avg_launch_us": avg["fc1"]},
         "grouped_gemm_tflops": gemm_tflops,
         "grouped_gemm_frac_bf16_peak": gemm_tflops / peak,
+        "padded": {"rows": n_padded, "fc1_tflops": fc1_tflops * n_padded / max(n_valid, 1),
+                   "grouped_gemm_tflops": gemm_tflops * n_padded / max(n_valid, 1),
+                   "note": "the same times with pad rows counted as work"},
         "permute_GBps": perm_gbps, "permute_frac_hbm": perm_gbps / PEAK_HBM_GBPS,
         "combine_GBps": comb_gbps, "combine_frac_hbm": comb_gbps / PEAK_HBM_GBPS,
         "stage_us_median": med, "stage_us_mean": avg, "stage_us_spread": spread,
         "timing": {"value_from": "sum of per-step HIP-event durations on the compute stream",
                    "cache_flush_MiB_between_steps": args.flush_mib,
                    "wall_ms_per_step_incl_flush": wall * 1e3 / args.steps},
-        "assignments": n_valid, "padded_rows": int(buf["offsets"][-1].item()),
+        "assignments": n_valid,
         "expert_rows_min_max": [int(counts.min()), int(counts.max())],
         "cpu_baseline": None,
     }
