@@ -80,22 +80,57 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock) void route_kernel(
     float acc[P];
 #pragma unroll
     for (int p = 0; p < P; ++p) acc[p] = 0.0f;
-    for (int c = lane; c < nchunk; c += kWave) {
-      float xv[TW][V];
-#pragma unroll
-      for (int t = 0; t < TW; ++t) {
-        const int tok = min(t0 + t, T - 1);
-        Chunk<TIn>::widen(ld16(x + (size_t)tok * D + (size_t)c * V), xv[t]);
-      }
-#pragma unroll
-      for (int e = 0; e < EC; ++e) {
-        const int ee = min(e0 + e, E - 1);
-        float wv[V];
-        Chunk<TIn>::widen(ld16(wg + (size_t)ee * D + (size_t)c * V), wv);
+    if constexpr (!SHARED) {
+      // few experts: the raw chunks of step c + 64 are loaded while step c is summed
+      // (the summation order is unchanged)
+      u32x4 xr[2][TW], wr[2][EC];
+      auto load = [&](int c, int b) {
 #pragma unroll
         for (int t = 0; t < TW; ++t)
+          xr[b][t] = ld16(x + (size_t)min(t0 + t, T - 1) * D + (size_t)c * V);
 #pragma unroll
-          for (int i = 0; i < V; ++i) dot_step(acc[t * EC + e], xv[t][i], wv[i], TIn());
+        for (int e = 0; e < EC; ++e) wr[b][e] = ld16(wg + (size_t)min(e0 + e, E - 1) * D + (size_t)c * V);
+      };
+      auto sum = [&](int b) {
+        float xv[TW][V];
+#pragma unroll
+        for (int t = 0; t < TW; ++t) Chunk<TIn>::widen(xr[b][t], xv[t]);
+#pragma unroll
+        for (int e = 0; e < EC; ++e) {
+          float wv[V];
+          Chunk<TIn>::widen(wr[b][e], wv);
+#pragma unroll
+          for (int t = 0; t < TW; ++t)
+#pragma unroll
+            for (int i = 0; i < V; ++i) dot_step(acc[t * EC + e], xv[t][i], wv[i], TIn());
+        }
+      };
+      if (lane < nchunk) load(lane, 0);
+      for (int c = lane; c < nchunk; c += 2 * kWave) {   // buffers 0 / 1 hold c / c + 64
+        if (c + kWave < nchunk) load(c + kWave, 1);
+        sum(0);
+        if (c + kWave >= nchunk) break;
+        if (c + 2 * kWave < nchunk) load(c + 2 * kWave, 0);
+        sum(1);
+      }
+    } else {
+      for (int c = lane; c < nchunk; c += kWave) {
+        float xv[TW][V];
+#pragma unroll
+        for (int t = 0; t < TW; ++t) {
+          const int tok = min(t0 + t, T - 1);
+          Chunk<TIn>::widen(ld16(x + (size_t)tok * D + (size_t)c * V), xv[t]);
+        }
+#pragma unroll
+        for (int e = 0; e < EC; ++e) {
+          const int ee = min(e0 + e, E - 1);
+          float wv[V];
+          Chunk<TIn>::widen(ld16(wg + (size_t)ee * D + (size_t)c * V), wv);
+#pragma unroll
+          for (int t = 0; t < TW; ++t)
+#pragma unroll
+            for (int i = 0; i < V; ++i) dot_step(acc[t * EC + e], xv[t][i], wv[i], TIn());
+        }
       }
     }
     float logit = reduce_pairs<P, kWave / 2>(acc, lane);
