@@ -25,7 +25,6 @@ namespace moe {
 namespace {
 
 constexpr int kMaxExperts = 1024;
-constexpr int kMaxK = 32;
 constexpr int kPlaceTokens = 16;
 constexpr int kThreads = 256;
 constexpr int kUnroll = 4;   // 16-byte chunks per thread in flight during the copy
