@@ -117,6 +117,8 @@ moe_status_t moe_permute(moe_dtype_t dt, const void* x, const int32_t* topk_idx,
  * m_tile; offsets[E] may be any value <= m_cap (so a dense FFN over T tokens is
  * the call with E = 1, offsets = {0, T}, tile_expert all 0).
  * bf16 needs m_tile in {128, 256}; float32 accepts every m_tile. D*F < 2^31.
+ * offsets that break this contract (negative, decreasing, past m_cap) give
+ * unspecified values in h and y_perm but no access outside rows [0, m_cap).
  *
  * workspace: optional device scratch (16-byte aligned; NULL or ws_bytes 0 for
  * none), owned by the caller and clobbered by the call. With it the bf16 kernels

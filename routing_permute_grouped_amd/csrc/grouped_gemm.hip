@@ -317,8 +317,10 @@ struct Sched {
 
 __device__ void build_sched(Sched& sc, const int32_t* __restrict__ offsets, int E, int m_cap) {
   const int tid = threadIdx.x;
-  const int mend = min(offsets[E], m_cap);
-  for (int e = tid; e <= E; e += blockDim.x) sc.segoff[e] = min(offsets[e], mend);
+  // clamped into [0, min(offsets[E], m_cap)], so offsets that break the contract
+  // (negative, decreasing, past m_cap) can only shrink the work, never move it outside
+  const int mend = max(0, min(offsets[E], m_cap));
+  for (int e = tid; e <= E; e += blockDim.x) sc.segoff[e] = max(0, min(offsets[e], mend));
   __syncthreads();
   const int per = (MAXE + blockDim.x - 1) / blockDim.x;   // experts per thread (<= 4)
   int cnt[4], local = 0;

@@ -143,6 +143,28 @@ def test_max_experts_given_routing():
     P.check_layer(inp, 8, 128, "bf16")
 
 
+def test_grouped_gemm_stays_inside_m_cap_with_bad_offsets():
+    # offsets that break the contract (decreasing, negative, past m_cap) only shrink the
+    # work: nothing is written at or beyond m_cap rows
+    P.log("[parity] grouped GEMM with out-of-contract offsets")
+    E, D, F, m_cap, guard = 4, 256, 256, 1024, 256
+    g = torch.Generator(device="cuda").manual_seed(3)
+    xp = torch.randn(m_cap + guard, D, device="cuda", generator=g).to(torch.bfloat16)
+    w1 = (torch.randn(E, F, D, device="cuda", generator=g) * 0.05).to(torch.bfloat16)
+    w3 = (torch.randn(E, F, D, device="cuda", generator=g) * 0.05).to(torch.bfloat16)
+    w2 = (torch.randn(E, D, F, device="cuda", generator=g) * 0.05).to(torch.bfloat16)
+    te = torch.zeros(m_cap // 128, dtype=torch.int32, device="cuda")
+    ws = rpg.grouped_workspace(xp.device)
+    for offs in ([0, 640, 256, 768, 5000], [-384, 128, -7, 896, 1024], [0, 384, 384, 2048, 900]):
+        h = torch.full((m_cap + guard, F), float("nan"), dtype=torch.bfloat16, device="cuda")
+        y = torch.full((m_cap + guard, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+        off = torch.tensor(offs, dtype=torch.int32, device="cuda")
+        rpg.moe_grouped_swiglu(xp, off, te, w1, w3, w2, 128, m_cap=m_cap, h=h, y_perm=y,
+                               workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.isnan(h[m_cap:].float()).all() and torch.isnan(y[m_cap:].float()).all(), offs
+
+
 def test_two_call_form_matches_one_call():
     # moe_grouped_fc1_swiglu then moe_grouped_fc2 run the same kernels as
     # moe_grouped_swiglu: identical bits
