@@ -44,6 +44,22 @@ Readings taken where the pages are silent:
    output are stored in the layer dtype (float32 or bf16, round to nearest
    even); all other arithmetic here is float64.
 
+Backward (same page, section 5: every forward operator has a mirror; permute's is an
+unpermute (scatter_add), combine's is a dispatch, an m-grouped fc's is an m-grouped
+dgrad plus a k-grouped wgrad). Readings:
+
+10. The forward stores the fc1 pre-activations a = X w1^T and b = X w3^T in the
+    layer dtype; the backward uses those stored values.
+11. Given dout [T, D] (stored), combine's mirror sends w[t,j] * dout[t] to row
+    dst[t,j] (stored; pad rows zero) and gives dw[t,j] = <dout[t], Y[dst[t,j]]>.
+12. dh = dY w2[e], da = dh * b * silu'(a), db = dh * silu(a), dX = da w1[e] + db w3[e]
+    (each stored once); dW2[e] = dY^T h, dW1[e] = da^T X, dW3[e] = db^T X over the
+    expert's rows (weight gradients kept in float32 on the device, float64 here).
+13. dx[t] = sum_j dX[dst[t,j]] (slots in order j, skipping -1) plus the shared
+    experts' input gradient, stored once: permute's mirror is combine with unit
+    weights. The shared experts' output gradient is dout itself.
+14. The router's own backward (through softmax and top-k) is not part of this path.
+
 Float arrays may be passed as float32/float64 values or, for bf16, as uint16
 bit patterns; this module widens them itself.
 """
@@ -59,6 +75,9 @@ __all__ = [
     "router_logits", "softmax", "select_topk", "route",
     "dispatch_layout", "permute", "silu", "expert_swiglu", "grouped_swiglu",
     "shared_experts", "combine", "forward", "token_outputs",
+    "silu_grad", "preactivations", "combine_backward", "swiglu_backward",
+    "expert_backward", "grouped_backward", "permute_backward", "shared_backward",
+    "backward",
 ]
 
 _LANES = 64  # width of one reduction group in the fixed logit order
@@ -99,7 +118,10 @@ def round_bf16(a: np.ndarray) -> np.ndarray:
 
 
 def round_storage(a: np.ndarray, dtype: str) -> np.ndarray:
-    """Value after storing float64 ``a`` in the layer dtype, as float64."""
+    """Value after storing float64 ``a`` in the layer dtype, as float64. ``"f64"`` keeps
+    the value (no rounding): the pins use it to compare derivatives exactly."""
+    if dtype == "f64":
+        return np.asarray(a, dtype=np.float64)
     if dtype == "f32":
         return np.asarray(a, dtype=np.float64).astype(np.float32).astype(np.float64)
     if dtype == "bf16":
@@ -391,3 +413,137 @@ def token_outputs(tokens, x, topk_idx, topk_w, w1, w3, w2, dtype: str, shared_w=
     if shared_w is not None:
         out += shared_experts(x[tokens], *shared_w, dtype)
     return round_storage(out, dtype), hs, ys
+
+
+# ----------------------------------------------------------------------------
+# backward (section 5: each forward operator and its mirror)
+# ----------------------------------------------------------------------------
+
+def silu_grad(a: np.ndarray) -> np.ndarray:
+    """d silu(a) / da = s + a s (1 - s) with s = 1 / (1 + exp(-a)), float64."""
+    a = np.asarray(a, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        s_ = 1.0 / (1.0 + np.exp(-a))
+    return s_ * (1.0 + a * (1.0 - s_))
+
+
+def preactivations(x_perm, offsets, w1, w3, dtype: str):
+    """The stored fc1 pre-activations ab = [x w1[e]^T | x w3[e]^T] per segment row
+    [m_cap, 2F] (rows past offsets[E] zero), as the forward keeps them for the backward."""
+    E, F, _ = w1.shape
+    xp = values64(x_perm)
+    ab = np.zeros((xp.shape[0], 2 * F), dtype=np.float64)
+    for e in range(E):
+        r0, r1 = int(offsets[e]), int(offsets[e + 1])
+        if r1 > r0:
+            ab[r0:r1, :F] = xp[r0:r1] @ values64(w1[e]).T
+            ab[r0:r1, F:] = xp[r0:r1] @ values64(w3[e]).T
+    return round_storage(ab, dtype)
+
+
+def combine_backward(dout, y_perm, dst_row, topk_w, rows_used: int, dtype: str):
+    """Mirror of ``combine``: dY[dst[t,j]] = w[t,j] * dout[t] (stored), zero on every other
+    row below ``rows_used``; dw[t,j] = <dout[t], Y[dst[t,j]]> (0 for skipped slots)."""
+    G = values64(dout)
+    Y = values64(y_perm)
+    dst = np.asarray(dst_row, dtype=np.int64)
+    w = np.asarray(topk_w, dtype=np.float64)
+    T, k = dst.shape
+    dY = np.zeros((Y.shape[0], G.shape[1]), dtype=np.float64)
+    dw = np.zeros((T, k), dtype=np.float64)
+    for j in range(k):
+        ok = dst[:, j] >= 0
+        dY[dst[ok, j]] = w[ok, j:j + 1] * G[ok]
+        dw[ok, j] = np.einsum("td,td->t", G[ok], Y[dst[ok, j]])
+    dY[rows_used:] = 0.0
+    return round_storage(dY, dtype), dw
+
+
+def swiglu_backward(dh, a, b, dtype: str):
+    """da = dh * b * silu'(a), db = dh * silu(a), each stored (a, b, dh stored values)."""
+    dh, a, b = values64(dh), values64(a), values64(b)
+    return round_storage(dh * b * silu_grad(a), dtype), round_storage(dh * silu(a), dtype)
+
+
+def expert_backward(A, a, b, h, dY, w1e, w3e, w2e, dtype: str):
+    """One expert's mirror on its rows: returns (dh, da, db, dA, dW1, dW3, dW2); the
+    activation gradients are stored values, the weight gradients float64."""
+    A64, h64, dY64 = values64(A), values64(h), values64(dY)
+    dh = round_storage(dY64 @ values64(w2e), dtype)
+    da, db = swiglu_backward(dh, a, b, dtype)
+    dA = round_storage(da @ values64(w1e) + db @ values64(w3e), dtype)
+    return dh, da, db, dA, da.T @ A64, db.T @ A64, dY64.T @ h64
+
+
+def grouped_backward(x_perm, ab, h, dY, offsets, w1, w3, w2, dtype: str):
+    """``expert_backward`` over every segment [offsets[e], offsets[e+1]) of the
+    expert-contiguous buffers; ab = [a | b] per row. Returns dh [m_cap,F],
+    dab [m_cap,2F], dX [m_cap,D] (rows past offsets[E] zero) and dW1, dW3 [E,F,D],
+    dW2 [E,D,F] (an expert without rows gets zero weight gradients)."""
+    E, F, D = w1.shape
+    M = np.asarray(x_perm).shape[0]
+    ab64 = values64(ab)
+    dh = np.zeros((M, F))
+    dab = np.zeros((M, 2 * F))
+    dX = np.zeros((M, D))
+    dW1, dW3, dW2 = np.zeros((E, F, D)), np.zeros((E, F, D)), np.zeros((E, D, F))
+    for e in range(E):
+        r0, r1 = int(offsets[e]), int(offsets[e + 1])
+        if r1 <= r0:
+            continue
+        out = expert_backward(x_perm[r0:r1], ab64[r0:r1, :F], ab64[r0:r1, F:], h[r0:r1],
+                              dY[r0:r1], w1[e], w3[e], w2[e], dtype)
+        dh[r0:r1], dab[r0:r1, :F], dab[r0:r1, F:], dX[r0:r1] = out[:4]
+        dW1[e], dW3[e], dW2[e] = out[4:]
+    return dh, dab, dX, dW1, dW3, dW2
+
+
+def permute_backward(dX, dst_row, dtype: str, shared=None):
+    """Mirror of ``permute`` (an unpermute / scatter_add): dx[t] = sum_j dX[dst[t,j]] over
+    slots in order, skipping -1, plus ``shared``, stored once."""
+    dst = np.asarray(dst_row)
+    return combine(dX, dst, np.ones(dst.shape), dtype, shared)
+
+
+def shared_backward(x, ws1, ws3, ws2, dout, dtype: str):
+    """Mirror of ``shared_experts`` (the shared experts are summed, so each one's output
+    gradient is dout). Returns (dx_shared stored once over all shared experts,
+    dws1, dws3, dws2 float64)."""
+    x64, G = values64(x), values64(dout)
+    S = ws1.shape[0]
+    dx = np.zeros_like(x64)
+    dws1, dws3, dws2 = np.zeros(ws1.shape), np.zeros(ws3.shape), np.zeros(ws2.shape)
+    for s_ in range(S):
+        a = x64 @ values64(ws1[s_]).T
+        b = x64 @ values64(ws3[s_]).T
+        h = round_storage(silu(a) * b, dtype)
+        a, b = round_storage(a, dtype), round_storage(b, dtype)
+        dh = round_storage(G @ values64(ws2[s_]), dtype)
+        da, db = swiglu_backward(dh, a, b, dtype)
+        dx += da @ values64(ws1[s_]) + db @ values64(ws3[s_])
+        dws1[s_], dws3[s_], dws2[s_] = da.T @ x64, db.T @ x64, G.T @ h
+    return round_storage(dx, dtype), dws1, dws3, dws2
+
+
+def backward(inputs: dict, dout, k: int, m_tile: int, dtype: str, renorm: bool = False,
+             m_cap: Optional[int] = None) -> dict:
+    """Forward (with the saved pre-activations) and the mirror of every step for the
+    output gradient ``dout`` [T, D]. The routing is taken as given (the router's own
+    backward is not part of the path): topk_w gets its gradient dtopk_w."""
+    fwd = forward(inputs, k, m_tile, dtype, renorm, m_cap)
+    x = inputs["x"]
+    xp, offs, h, Y = fwd["x_perm"], fwd["offsets"], fwd["h"], fwd["y_perm"]
+    ab = preactivations(xp, offs, inputs["w1"], inputs["w3"], dtype)
+    res = {"fwd": fwd, "ab": ab}
+    dY, dw = combine_backward(dout, Y, fwd["dst_row"], fwd["topk_w"], int(offs[-1]), dtype)
+    res["dy_perm"], res["dtopk_w"] = dY, dw
+    dh, dab, dX, dW1, dW3, dW2 = grouped_backward(xp, ab, h, dY, offs, inputs["w1"],
+                                                 inputs["w3"], inputs["w2"], dtype)
+    res.update(dh=dh, dab=dab, dx_perm=dX, dw1=dW1, dw3=dW3, dw2=dW2)
+    dxs = None
+    if "ws1" in inputs:
+        dxs, res["dws1"], res["dws3"], res["dws2"] = shared_backward(
+            x, inputs["ws1"], inputs["ws3"], inputs["ws2"], dout, dtype)
+        res["dx_shared"] = dxs
+    res["dx"] = permute_backward(dX, fwd["dst_row"], dtype, dxs)
+    return res

@@ -7,6 +7,7 @@ import numpy as np
 import pytest
 
 from oracle import moe_oracle as orc
+from tests import test_oracle_backward_pins as bpins
 from tests import test_oracle_pins as pins
 
 
@@ -68,7 +69,44 @@ def _first_expert_only_counts(topk_idx, E, m_tile, m_cap=None):
     return orc.__dict__["_orig_dispatch_layout"](np.asarray(topk_idx)[:, :1], E, m_tile, m_cap)
 
 
+def _silu_grad_dropped_term(a):
+    s = 1.0 / (1.0 + np.exp(-np.asarray(a, dtype=np.float64)))
+    return s                                                      # the a*s*(1-s) term dropped
+
+
+def _swiglu_grads_swapped(dh, a, b, dtype):
+    da, db = orc.__dict__["_orig_swiglu_backward"](dh, a, b, dtype)
+    return db, da                                                 # gate and up gradients swapped
+
+
+def _dgrad_without_up(A, a, b, h, dY, w1e, w3e, w2e, dtype):
+    out = list(orc.__dict__["_orig_expert_backward"](A, a, b, h, dY, w1e, w3e, w2e, dtype))
+    out[3] = orc.round_storage(out[1] @ orc.values64(w1e), dtype)  # db w3 term dropped
+    return tuple(out)
+
+
+def _dispatch_unweighted(dout, y_perm, dst_row, topk_w, rows_used, dtype):
+    return orc.__dict__["_orig_combine_backward"](dout, y_perm, dst_row, np.ones_like(topk_w),
+                                                  rows_used, dtype)
+
+
+def _unpermute_without_shared(dX, dst_row, dtype, shared=None):
+    return orc.__dict__["_orig_permute_backward"](dX, dst_row, dtype, None)
+
+
+def _wgrad_up_from_gate(A, a, b, h, dY, w1e, w3e, w2e, dtype):
+    out = list(orc.__dict__["_orig_expert_backward"](A, a, b, h, dY, w1e, w3e, w2e, dtype))
+    out[5] = out[4]                                               # dW3 taken from da
+    return tuple(out)
+
+
 MUTATIONS = {
+    "bwd_silu_grad_term": ("silu_grad", _silu_grad_dropped_term, "autograd"),
+    "bwd_swiglu_swapped": ("swiglu_backward", _swiglu_grads_swapped, "autograd"),
+    "bwd_dgrad_no_up": ("expert_backward", _dgrad_without_up, "autograd"),
+    "bwd_dispatch_unweighted": ("combine_backward", _dispatch_unweighted, "autograd"),
+    "bwd_unpermute_no_shared": ("permute_backward", _unpermute_without_shared, "autograd"),
+    "bwd_wgrad_up_from_gate": ("expert_backward", _wgrad_up_from_gate, "autograd"),
     "swapped_gate_up": ("expert_swiglu", _swapped_gate_up, "brute"),
     "no_silu": ("expert_swiglu", _no_silu, "brute"),
     "ties_high": ("select_topk", _ties_high, "ties"),
@@ -90,6 +128,8 @@ def _run_pin(kind):
         pins.test_topk_matches_python_sorted_with_ties()
     elif kind == "layout":
         pins.test_layout_matches_loop_counting_sort(50, 3, 7, 4, False)
+    elif kind == "autograd":
+        bpins._check_backward_against_autograd(orc, 0)
 
 
 @pytest.mark.parametrize("name", sorted(MUTATIONS))
@@ -102,5 +142,5 @@ def test_planted_mistake_is_caught(name, monkeypatch):
 
 
 def test_unmutated_pins_pass():
-    for kind in ("brute", "brute_bias", "ties", "layout"):
+    for kind in ("brute", "brute_bias", "ties", "layout", "autograd"):
         _run_pin(kind)
