@@ -28,10 +28,15 @@ SIGNATURES = [
                          _P, _P]),
     ("moe_grouped_swiglu", _I, [_I, _P, _P, _P, _I, _I, _I, _I, _I64, _P, _P, _P, _P, _P, _P,
                                 _SZ, _P]),
-    ("moe_grouped_fc1_swiglu", _I, [_I, _P, _P, _P, _I, _I, _I, _I, _I64, _P, _P, _P, _P, _SZ,
-                                    _P]),
+    ("moe_grouped_fc1_swiglu", _I, [_I, _P, _P, _P, _I, _I, _I, _I, _I64, _P, _P, _P, _P, _P,
+                                    _SZ, _P]),
     ("moe_grouped_fc2", _I, [_I, _P, _P, _P, _I, _I, _I, _I, _I64, _P, _P, _P, _SZ, _P]),
     ("moe_combine", _I, [_I, _P, _P, _P, _P, _I, _I, _I, _I64, _P, _P]),
+    ("moe_combine_backward", _I, [_I, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I64, _P, _P, _P]),
+    ("moe_grouped_dgrad_swiglu", _I, [_I, _P, _P, _P, _I, _I, _I, _I, _I64, _P, _P, _P, _P, _P,
+                                      _SZ, _P]),
+    ("moe_grouped_wgrad", _I, [_I, _P, _P, _I64, _P, _I, _I, _I, _I, _I, _I64, _P, _P, _P]),
+    ("moe_transpose", _I, [_I, _P, _I, _I, _I, _I, _P, _P, _I64, _I64, _P]),
     ("moe_capacity", _I64, [_I, _I, _I, _I]),
     ("moe_grouped_workspace_bytes", _SZ, []),
     ("moe_permute_workspace_bytes", _SZ, [_I, _I, _I]),
@@ -182,12 +187,14 @@ def moe_grouped_swiglu(x_perm: torch.Tensor, offsets: torch.Tensor, tile_expert:
 
 def moe_grouped_fc1_swiglu(x_perm: torch.Tensor, offsets: torch.Tensor, tile_expert: torch.Tensor,
                            w1: torch.Tensor, w3: torch.Tensor, m_tile: int, m_cap: int,
-                           h: torch.Tensor, workspace: Optional[torch.Tensor] = None,
-                           stream=None) -> torch.Tensor:
+                           h: torch.Tensor, ab: Optional[torch.Tensor] = None,
+                           workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """h = silu(x_perm w1[e]^T) * (x_perm w3[e]^T); with ``ab`` [m_cap, 2F] also the
+    pre-activations [a | b] that the backward reads."""
     E, F, D = w1.shape
     _check("moe_grouped_fc1_swiglu", lib.moe_grouped_fc1_swiglu(
         _dt(x_perm), _ptr(x_perm), _ptr(offsets), _ptr(tile_expert), E, D, F, m_tile, m_cap,
-        _ptr(w1), _ptr(w3), _ptr(h), *_ws(workspace), _stream(stream)))
+        _ptr(w1), _ptr(w3), _ptr(h), _ptr(ab), *_ws(workspace), _stream(stream)))
     return h
 
 
@@ -201,9 +208,11 @@ def moe_grouped_fc2(h: torch.Tensor, offsets: torch.Tensor, tile_expert: torch.T
     return y_perm
 
 
-def moe_combine(y_perm: torch.Tensor, dst_row: torch.Tensor, topk_w: torch.Tensor,
+def moe_combine(y_perm: torch.Tensor, dst_row: torch.Tensor, topk_w: Optional[torch.Tensor],
                 shared: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
                 m_cap: Optional[int] = None, stream=None) -> torch.Tensor:
+    """out[t] = sum_j topk_w[t,j] y_perm[dst_row[t,j]] (+ shared[t]); ``topk_w`` None means
+    unit weights (the unpermute-and-sum that is the permute's backward)."""
     T, k = dst_row.shape
     D = y_perm.shape[1]
     if m_cap is None:
@@ -214,3 +223,91 @@ def moe_combine(y_perm: torch.Tensor, dst_row: torch.Tensor, topk_w: torch.Tenso
         _dt(y_perm), _ptr(y_perm), _ptr(dst_row), _ptr(topk_w), _ptr(shared), T, D, k, m_cap,
         _ptr(out), _stream(stream)))
     return out
+
+
+def moe_combine_backward(dout: torch.Tensor, y_perm: torch.Tensor, src_row: torch.Tensor,
+                         offsets: torch.Tensor, dst_row: torch.Tensor, topk_w: torch.Tensor,
+                         m_cap: Optional[int] = None, dy_perm: Optional[torch.Tensor] = None,
+                         dtopk_w: Optional[torch.Tensor] = None, stream=None):
+    """Returns (dy_perm [m_cap, D], dtopk_w [T, k] float32)."""
+    T, k = dst_row.shape
+    D = dout.shape[1]
+    E = offsets.shape[0] - 1
+    if m_cap is None:
+        m_cap = y_perm.shape[0]
+    if dy_perm is None:
+        dy_perm = torch.empty((m_cap, D), dtype=dout.dtype, device=dout.device)
+    if dtopk_w is None:
+        dtopk_w = torch.empty((T, k), dtype=torch.float32, device=dout.device)
+    if y_perm.dtype != dout.dtype:
+        raise TypeError("dout and y_perm must share a dtype")
+    _check("moe_combine_backward", lib.moe_combine_backward(
+        _dt(dout), _ptr(dout), _ptr(y_perm), _ptr(src_row), _ptr(offsets), _ptr(dst_row),
+        _ptr(topk_w), T, D, E, k, m_cap, _ptr(dy_perm), _ptr(dtopk_w), _stream(stream)))
+    return dy_perm, dtopk_w
+
+
+def moe_grouped_dgrad_swiglu(dy_perm: torch.Tensor, offsets: torch.Tensor,
+                             tile_expert: torch.Tensor, w2t: torch.Tensor, ab: torch.Tensor,
+                             m_tile: int, m_cap: Optional[int] = None,
+                             dab: Optional[torch.Tensor] = None, dh: Optional[torch.Tensor] = None,
+                             workspace: Optional[torch.Tensor] = None, stream=None):
+    """dab [m_cap, 2F] = [dh*b*silu'(a) | dh*silu(a)] with dh = dy_perm w2[e] (w2t [E,F,D]);
+    ``dh`` [m_cap, F], when given, receives dh."""
+    E, F, D = w2t.shape
+    if m_cap is None:
+        m_cap = dy_perm.shape[0]
+    if dab is None:
+        dab = torch.empty((m_cap, 2 * F), dtype=dy_perm.dtype, device=dy_perm.device)
+    _check("moe_grouped_dgrad_swiglu", lib.moe_grouped_dgrad_swiglu(
+        _dt(dy_perm), _ptr(dy_perm), _ptr(offsets), _ptr(tile_expert), E, D, F, m_tile, m_cap,
+        _ptr(w2t), _ptr(ab), _ptr(dab), _ptr(dh), *_ws(workspace), _stream(stream)))
+    return dab
+
+
+def moe_grouped_wgrad(pT: torch.Tensor, qT: torch.Tensor, offsets: torch.Tensor, m_tile: int,
+                      m_cap: int, NS: Optional[int] = None, out_lo: Optional[torch.Tensor] = None,
+                      out_hi: Optional[torch.Tensor] = None, stream=None):
+    """out[e] = pT[:, seg e] qT[:, seg e]^T in float32, rows < NS in out_lo [E, NS, N2] and
+    the rest in out_hi [E, N1-NS, N2]. Returns (out_lo, out_hi)."""
+    N1, ld = pT.shape
+    N2 = qT.shape[0]
+    E = offsets.shape[0] - 1
+    if qT.shape[1] != ld:
+        raise ValueError("pT and qT must have the same row length")
+    NS = N1 if NS is None else NS
+    f32 = dict(dtype=torch.float32, device=pT.device)
+    if out_lo is None and NS > 0:
+        out_lo = torch.empty((E, NS, N2), **f32)
+    if out_hi is None and NS < N1:
+        out_hi = torch.empty((E, N1 - NS, N2), **f32)
+    _check("moe_grouped_wgrad", lib.moe_grouped_wgrad(
+        _dt(pT), _ptr(pT), _ptr(qT), ld, _ptr(offsets), E, N1, N2, NS, m_tile, m_cap,
+        _ptr(out_lo), _ptr(out_hi), _stream(stream)))
+    return out_lo, out_hi
+
+
+def moe_transpose(src: torch.Tensor, rows: Optional[int] = None,
+                  nrows_dev: Optional[torch.Tensor] = None, dst: Optional[torch.Tensor] = None,
+                  ld: Optional[int] = None, col0: int = 0, R: Optional[int] = None,
+                  stream=None) -> torch.Tensor:
+    """src [R, C] or [B, R, C] -> dst [(B,) C, ld] with dst[..., c, col0 + r] = src[..., r, c]
+    for r < rows (and < *nrows_dev), zeros up to the next multiple of 64. ``R`` (a multiple
+    of 64, default src's row count) may exceed src's rows when batch is 1."""
+    batched = src.dim() == 3
+    B = src.shape[0] if batched else 1
+    Rs, C = src.shape[-2:]
+    R = Rs if R is None else R
+    rows = Rs if rows is None else rows
+    if batched and R != Rs:
+        raise ValueError("a batched transpose takes R equal to the source rows")
+    if rows > Rs:
+        raise ValueError("rows exceeds the source")
+    ld = R if ld is None else ld
+    if dst is None:
+        shape = (B, C, ld) if batched else (C, ld)
+        dst = torch.empty(shape, dtype=src.dtype, device=src.device)
+    _check("moe_transpose", lib.moe_transpose(
+        _dt(src), _ptr(src), B, R, C, rows, _ptr(nrows_dev), _ptr(dst), ld, col0,
+        _stream(stream)))
+    return dst

@@ -6,7 +6,17 @@
 //
 // Each token's k expert rows are gathered by 16-byte chunks and reduced in float32
 // in slot order; the shared row is added last and the sum is rounded once. Every
-// thread keeps four chunks' row reads in flight per slot.
+// thread keeps four chunks' row reads in flight per slot. Without weights the same
+// kernel is the plain unpermute-and-sum, which is also the backward of the permute
+// (section 5: the permute's mirror is a scatter_add).
+//
+// The backward of the combine (section 5: the mirror of unpermute-and-reduce is a
+// dispatch) runs over the rows of the permuted buffer: the row holding slot
+// s = t*k + j gets dy = topk_w[s] * dout[t], rounded once, and the slot's weight
+// gradient <dout[t], y_perm[row]> is reduced by the row's wave in a fixed order; pad
+// rows get zeros, so the grouped GEMMs of the backward see exact zeros there.
+#include <algorithm>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -31,7 +41,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(
   for (int i = threadIdx.x; i < ntok * k; i += kThreads) {
     const int d = dst_row[(size_t)t_begin * k + i];
     ds[i] = (d >= 0 && d < m_cap) ? d : -1;
-    ws[i] = w[(size_t)t_begin * k + i];
+    ws[i] = w ? w[(size_t)t_begin * k + i] : 1.0f;   // no weights: the plain unpermute
   }
   __syncthreads();
   const int nck = D / V;
@@ -81,7 +91,93 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(
   }
 }
 
+// One wave per row of the permuted buffer, rows [0, min(offsets[E], m_cap)); each lane
+// takes 16-byte chunks lane, lane+64, ... in increasing order, kU of them in flight.
+// The dot product is summed per lane in chunk order, then over lanes by an xor
+// butterfly (every lane ends with the same value, lane 0 stores it).
+template <typename TIn>
+__global__ __launch_bounds__(kThreads) void combine_bwd_kernel(
+    const TIn* __restrict__ dout, const TIn* __restrict__ y, const int32_t* __restrict__ src_row,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ dst_row,
+    const float* __restrict__ w, int T, int D, int E, int k, int64_t m_cap, TIn* __restrict__ dy,
+    float* __restrict__ dw) {
+  constexpr int V = Chunk<TIn>::V;
+  const int lane = threadIdx.x & 63;
+  const int64_t mend = max((int64_t)0, min((int64_t)offsets[E], m_cap));
+  const int64_t nslots = (int64_t)T * k;
+  const int nck = D / V;
+  const int64_t waves = (int64_t)gridDim.x * (kThreads / 64);
+  for (int64_t r = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6); r < mend;
+       r += waves) {
+    const int s = src_row[r];
+    TIn* drow = dy + r * D;
+    if (s < 0 || s >= nslots) {   // pad row
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      for (int c = lane; c < nck; c += 64) st16(drow + (size_t)c * V, z);
+      continue;
+    }
+    const TIn* g = dout + (size_t)(s / k) * D;
+    const TIn* yr = y + r * D;
+    const float wj = w[s];
+    float acc = 0.0f;
+    for (int c0 = lane; c0 < nck; c0 += 64 * kU) {
+      u32x4 gv[kU], yv[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int c = c0 + 64 * u;
+        if (c < nck) {
+          gv[u] = ld16(g + (size_t)c * V);
+          yv[u] = ld16_nt(yr + (size_t)c * V);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int c = c0 + 64 * u;
+        if (c >= nck) continue;
+        float gf[V], yf[V], o[V];
+        Chunk<TIn>::widen(gv[u], gf);
+        Chunk<TIn>::widen(yv[u], yf);
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+          acc = __builtin_fmaf(gf[v], yf[v], acc);
+          o[v] = wj * gf[v];
+        }
+        st16(drow + (size_t)c * V, Chunk<TIn>::narrow(o));
+      }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
+    if (lane == 0) dw[s] = acc;
+  }
+  // slots that no row holds (skipped, or outside the rows in use) have zero gradient
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < nslots;
+       i += (int64_t)gridDim.x * kThreads) {
+    const int d = dst_row[i];
+    if (d < 0 || d >= mend) dw[i] = 0.0f;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_combine_backward(int dt, const void* dout, const void* y_perm,
+                                   const int32_t* src_row, const int32_t* offsets,
+                                   const int32_t* dst_row, const float* topk_w, int T, int D, int E,
+                                   int k, int64_t m_cap, void* dy_perm, float* dtopk_w,
+                                   hipStream_t s) {
+  const int64_t want = (m_cap + 3) / 4;
+  const dim3 grid((unsigned)std::min<int64_t>(want, 16 * cu_count())), block(kThreads);
+  if (dt == kF32)
+    hipLaunchKernelGGL(combine_bwd_kernel<float>, grid, block, 0, s,
+                       static_cast<const float*>(dout), static_cast<const float*>(y_perm), src_row,
+                       offsets, dst_row, topk_w, T, D, E, k, m_cap, static_cast<float*>(dy_perm),
+                       dtopk_w);
+  else
+    hipLaunchKernelGGL(combine_bwd_kernel<bf16_t>, grid, block, 0, s,
+                       static_cast<const bf16_t*>(dout), static_cast<const bf16_t*>(y_perm),
+                       src_row, offsets, dst_row, topk_w, T, D, E, k, m_cap,
+                       static_cast<bf16_t*>(dy_perm), dtopk_w);
+  return hipGetLastError();
+}
 
 hipError_t launch_combine(int dt, const void* y_perm, const int32_t* dst_row, const float* topk_w,
                           const void* shared, int T, int D, int k, int64_t m_cap, void* out,

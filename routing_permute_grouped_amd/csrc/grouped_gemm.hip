@@ -67,6 +67,65 @@ __device__ __forceinline__ void store4(bf16_t* p, float a, float b, float c, flo
   *reinterpret_cast<uint2*>(p) = pk;
 }
 
+__device__ __forceinline__ void load4(const bf16_t* p, float* v) {
+  const uint2 pk = *reinterpret_cast<const uint2*>(p);
+  v[0] = bf16_lo(pk.x);
+  v[1] = bf16_hi(pk.x);
+  v[2] = bf16_lo(pk.y);
+  v[3] = bf16_hi(pk.y);
+}
+
+// What the m-grouped kernel does with its float32 sums (C = A W^T per segment row):
+//   kFc1   the panel interleaves w1 and w3 rows: h = silu(a)*b -> C [m][N]; when `ab` is
+//          set, the pre-activations a and b are stored too, as ab [m][2N] = [a | b]
+//   kFc2   y -> C [m][N]
+//   kDgrad the sums are dh (dY w2[e]); dh is rounded to bf16, then with (a, b) read from
+//          ab [m][2N]: da = dh*b*silu'(a), db = dh*silu(a) -> C [m][2N] = [da | db];
+//          dh itself -> `dh` [m][N] when set
+// (the backward of the activation, "Expert Parallelism (EP)", section 5: the fc of the
+// forward mirrors into an m-grouped dgrad).
+enum Mode { kFc1 = 0, kFc2 = 1, kDgrad = 2 };
+
+struct Epi {
+  bf16_t* C;
+  bf16_t* ab;
+  bf16_t* dh;
+  int N;   // output columns (fc1, dgrad: F; fc2: D)
+};
+
+// Four consecutive output columns n..n+3 of row m; u holds the w3 sums for kFc1.
+template <int MODE>
+__device__ __forceinline__ void emit4(const Epi& ep, int m, int n, const float* v, const float* u) {
+  const size_t row = (size_t)m * ep.N;
+  if (MODE == kFc1) {
+    store4(ep.C + row + n, silu_mul(v[0], u[0]), silu_mul(v[1], u[1]), silu_mul(v[2], u[2]),
+           silu_mul(v[3], u[3]));
+    if (ep.ab) {
+      bf16_t* p = ep.ab + 2 * row + n;
+      store4(p, v[0], v[1], v[2], v[3]);
+      store4(p + ep.N, u[0], u[1], u[2], u[3]);
+    }
+  } else if (MODE == kFc2) {
+    store4(ep.C + row + n, v[0], v[1], v[2], v[3]);
+  } else {
+    float d[4], a[4], b[4], da[4], db[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) d[i] = bf16_to_f32(f32_to_bf16(v[i]));
+    load4(ep.ab + 2 * row + n, a);
+    load4(ep.ab + 2 * row + ep.N + n, b);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float s = 1.0f / (1.0f + __expf(-a[i]));   // sigmoid; silu = a*s
+      db[i] = d[i] * (a[i] * s);
+      da[i] = d[i] * b[i] * (s * (1.0f + a[i] * (1.0f - s)));
+    }
+    bf16_t* p = ep.C + 2 * row + n;
+    store4(p, da[0], da[1], da[2], da[3]);
+    store4(p + ep.N, db[0], db[1], db[2], db[3]);
+    if (ep.dh) store4(ep.dh + row + n, d[0], d[1], d[2], d[3]);
+  }
+}
+
 // Exclusive prefix sum over the threads of the block (up to 16 waves).
 __device__ __forceinline__ int block_scan_excl(int v, int* wtot) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
@@ -193,11 +252,10 @@ __device__ __forceinline__ void issue_loads(const TileLoads& o, uint32_t la, int
 // step the free stage instead receives the first step of the next tile (`nxt`, step
 // `nkb`), so its load latency hides under this tile's last MFMAs and its epilogue;
 // `primed` says that this tile's first step was loaded that way.
-template <bool FC1, bool HALF>
-__device__ __forceinline__ void run_tile(char* smem, const Tile& t, const TileLoads& ld,
-                                         bf16_t* __restrict__ C, int N, int kb, int ke,
-                                         float* __restrict__ part, int stage0, bool primed,
-                                         const TileLoads& nxt, bool has_next, int nkb) {
+template <bool HALF>
+__device__ __forceinline__ void mainloop(char* smem, const TileLoads& ld, int kb, int ke,
+                                         int stage0, bool primed, const TileLoads& nxt,
+                                         bool has_next, int nkb, f32x16 (&acc)[HALF ? 2 : 4][2]) {
   constexpr int WM = HALF ? 2 : 4;   // 32-row blocks of A per wave
   constexpr int WN = 2;              // 32-row panel blocks per wave
   const int tid = threadIdx.x;
@@ -207,7 +265,6 @@ __device__ __forceinline__ void run_tile(char* smem, const Tile& t, const TileLo
   const int prow0 = (wave >> 1) * 64;                 // first panel row of this wave
   const uint32_t lds0 = lds_addr(smem) + wave * 1024;
 
-  f32x16 acc[WM][WN];
 #pragma unroll
   for (int i = 0; i < WM; ++i)
 #pragma unroll
@@ -258,10 +315,28 @@ __device__ __forceinline__ void run_tile(char* smem, const Tile& t, const TileLo
   // No barrier here: the next tile's first step went into the stage nobody reads in
   // this tile's last step, and its second step's loads are issued only after its
   // first barrier, which every wave reaches after finishing this tile's MFMAs.
+}
 
-  // Lane holds column m = lane & 31 of every 32x32 block and panel rows
-  // 8*g + 4*(lane >> 5) + i (i = 0..3) for g = 0..3.
-  if (part) {   // split-K share: raw float32 sums, row-major [BM][BP]
+// One tile of the m-grouped kernel: the main loop, then either the raw float32 sums of
+// a split-K share (`part`, row-major [BM][BP]) or the MODE epilogue.
+// After the main loop lane l holds column m = l % 32 of every 32x32 block and panel rows
+// 8*g + 4*(l / 32) + i (i = 0..3) for g = 0..3.
+template <int MODE, bool HALF>
+__device__ __forceinline__ void run_tile(char* smem, const Tile& t, const TileLoads& ld,
+                                         const Epi& ep, int kb, int ke,
+                                         float* __restrict__ part, int stage0, bool primed,
+                                         const TileLoads& nxt, bool has_next, int nkb) {
+  constexpr int WM = HALF ? 2 : 4;
+  constexpr int WN = 2;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int arow0 = (wave & 1) * (HALF ? 64 : 128);
+  const int prow0 = (wave >> 1) * 64;
+  const int fr = lane & 31;
+  f32x16 acc[WM][WN];
+  mainloop<HALF>(smem, ld, kb, ke, stage0, primed, nxt, has_next, nkb, acc);
+
+  if (part) {
 #pragma unroll
     for (int mb = 0; mb < WM; ++mb) {
       const int r = arow0 + mb * 32 + fr;
@@ -281,16 +356,18 @@ __device__ __forceinline__ void run_tile(char* smem, const Tile& t, const TileLo
   for (int mb = 0; mb < WM; ++mb) {
     const int r = arow0 + mb * 32 + fr;
     if (r >= t.rows) continue;
-    bf16_t* crow = C + (size_t)(t.m0 + r) * N;
-    if (FC1) {
+    const int m = t.m0 + r;
+    if (MODE == kFc1) {
+      // the wave's two panel blocks are the w1 and w3 rows of the same 32 h columns
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int n = t.n0 + prow0 / 2 + g * 8 + (lane >> 5) * 4;
-        if (n >= N) continue;
+        if (n >= ep.N) continue;
         const f32x16& a = acc[mb][0];
         const f32x16& b = acc[mb][1];
-        store4(crow + n, silu_mul(a[4 * g], b[4 * g]), silu_mul(a[4 * g + 1], b[4 * g + 1]),
-               silu_mul(a[4 * g + 2], b[4 * g + 2]), silu_mul(a[4 * g + 3], b[4 * g + 3]));
+        const float v[4] = {a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]};
+        const float u[4] = {b[4 * g], b[4 * g + 1], b[4 * g + 2], b[4 * g + 3]};
+        emit4<MODE>(ep, m, n, v, u);
       }
     } else {
 #pragma unroll
@@ -298,9 +375,10 @@ __device__ __forceinline__ void run_tile(char* smem, const Tile& t, const TileLo
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int n = t.n0 + prow0 + nb * 32 + g * 8 + (lane >> 5) * 4;
-          if (n >= N) continue;
+          if (n >= ep.N) continue;
           const f32x16& a = acc[mb][nb];
-          store4(crow + n, a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]);
+          const float v[4] = {a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]};
+          emit4<MODE>(ep, m, n, v, v);
         }
       }
     }
@@ -400,11 +478,12 @@ __device__ Split split_plan(int total, int G, int slots, int nk) {
   return p;
 }
 
-template <bool FC1>
+template <int MODE>
 __global__ __launch_bounds__(NTHR, 1) void gg_bf16_kernel(
     const bf16_t* __restrict__ A, const int32_t* __restrict__ offsets, int E, int K, int N,
     int m_cap, const bf16_t* __restrict__ W1, const bf16_t* __restrict__ W3,
-    bf16_t* __restrict__ C, float* __restrict__ ws, int slots) {
+    Epi ep, float* __restrict__ ws, int slots) {
+  constexpr bool FC1 = MODE == kFc1;
   __shared__ __attribute__((aligned(16))) char smem[2 * STAGE_BYTES];
   __shared__ Sched sc;
   build_sched(sc, offsets, E, m_cap);
@@ -455,10 +534,10 @@ __global__ __launch_bounds__(NTHR, 1) void gg_bf16_kernel(
       nl = tile_loads<FC1>(nw.t, A, W1, W3, K, N);
     }
     if (cur.t.rows > BM / 2)
-      run_tile<FC1, false>(smem, cur.t, ld, C, N, cur.kb, cur.ke, cur.part, stage0, primed, nl,
+      run_tile<MODE, false>(smem, cur.t, ld, ep, cur.kb, cur.ke, cur.part, stage0, primed, nl,
                            has_next, nw.kb);
     else
-      run_tile<FC1, true>(smem, cur.t, ld, C, N, cur.kb, cur.ke, cur.part, stage0, primed, nl,
+      run_tile<MODE, true>(smem, cur.t, ld, ep, cur.kb, cur.ke, cur.part, stage0, primed, nl,
                           has_next, nw.kb);
     stage0 = (stage0 + cur.ke - cur.kb) & 1;
     primed = has_next;
@@ -467,16 +546,16 @@ __global__ __launch_bounds__(NTHR, 1) void gg_bf16_kernel(
   }
 }
 
-// Sums the split-K shares of the tail tiles in split order and applies the epilogue
-// (fc1: silu(a)*b; fc2: the sum), rounding once to bf16. G must be the grid size the
-// GEMM ran with.
-template <bool FC1>
+// Sums the split-K shares of the tail tiles in split order and applies the MODE
+// epilogue, rounding once to bf16. G must be the grid size the GEMM ran with.
+template <int MODE>
 __global__ __launch_bounds__(256) void gg_tail_reduce(const int32_t* __restrict__ offsets, int E,
-                                                      int K, int N, int m_cap, int G, int slots,
-                                                      const float* __restrict__ ws,
-                                                      bf16_t* __restrict__ C) {
+                                                      int K, int m_cap, int G, int slots,
+                                                      const float* __restrict__ ws, Epi ep) {
+  constexpr bool FC1 = MODE == kFc1;
   __shared__ Sched sc;
   build_sched(sc, offsets, E, m_cap);
+  const int N = ep.N;
   const int cols = FC1 ? BP / 2 : BP;
   const int n_nt = (N + cols - 1) / cols;
   const Split sp = split_plan(sc.tstart[E] * n_nt, G, slots, K / BK);
@@ -492,46 +571,219 @@ __global__ __launch_bounds__(256) void gg_tail_reduce(const int32_t* __restrict_
     if (r >= t.rows) continue;
     const float* base = ws + (size_t)i * (BM * BP) + r * BP;
     const size_t stride = (size_t)sp.tail * (BM * BP);   // next share of the same tile
-    if (FC1) {
-      const int fl = 4 * q;                              // h column inside the tile
-      const int pa = (fl >> 5) * 64 + (fl & 31);         // its w1 panel row; w3 is 32 later
-      float4 a = {0, 0, 0, 0}, b = {0, 0, 0, 0};
-      for (int sh = 0; sh < sp.S; ++sh) {
-        const float4 va = *reinterpret_cast<const float4*>(base + sh * stride + pa);
+    const int fl = 4 * q;                                // output column inside the tile
+    // fc1: column fl's w1 panel row; its w3 row is 32 later
+    const int pa = FC1 ? (fl >> 5) * 64 + (fl & 31) : fl;
+    float a[4] = {0, 0, 0, 0}, b[4] = {0, 0, 0, 0};
+    for (int sh = 0; sh < sp.S; ++sh) {
+      const float4 va = *reinterpret_cast<const float4*>(base + sh * stride + pa);
+      a[0] += va.x; a[1] += va.y; a[2] += va.z; a[3] += va.w;
+      if (FC1) {
         const float4 vb = *reinterpret_cast<const float4*>(base + sh * stride + pa + 32);
-        a.x += va.x; a.y += va.y; a.z += va.z; a.w += va.w;
-        b.x += vb.x; b.y += vb.y; b.z += vb.z; b.w += vb.w;
+        b[0] += vb.x; b[1] += vb.y; b[2] += vb.z; b[3] += vb.w;
       }
-      const int n = t.n0 + fl;
-      if (n < N)
-        store4(C + (size_t)(t.m0 + r) * N + n, silu_mul(a.x, b.x), silu_mul(a.y, b.y),
-               silu_mul(a.z, b.z), silu_mul(a.w, b.w));
-    } else {
-      const int nl = 4 * q;
-      float4 a = {0, 0, 0, 0};
-      for (int sh = 0; sh < sp.S; ++sh) {
-        const float4 v = *reinterpret_cast<const float4*>(base + sh * stride + nl);
-        a.x += v.x; a.y += v.y; a.z += v.z; a.w += v.w;
-      }
-      const int n = t.n0 + nl;
-      if (n < N) store4(C + (size_t)(t.m0 + r) * N + n, a.x, a.y, a.z, a.w);
     }
+    const int n = t.n0 + fl;
+    if (n < N) emit4<MODE>(ep, t.m0 + r, n, a, b);
   }
 }
 
 // ---------------------------------------------------------------------------
-// float32: 16 rows x 64 columns per workgroup, k-steps of 32 staged in LDS
+// k-grouped weight gradient ("Expert Parallelism (EP)", section 5: the backward of an
+// m-grouped fc is an m-grouped dgrad plus a k-grouped wgrad). For every expert e with
+// segment rows [s_e, s_e+1) (offsets, clamped to the rows in use):
+//   out[e][i][j] = sum over r in the segment of P[r][i] * Q[r][j]     (i < N1, j < N2)
+// with both operands given K-contiguous, i.e. transposed: pT [N1][ld], qT [N2][ld]. Rows
+// i < NS of the result go to out_lo [E][NS][N2], the others to out_hi [E][N1-NS][N2]
+// (float32), so [dW1 | dW3] from [da | db] lands in two separate arrays. Experts without
+// rows get zeros. Tiles are 256 rows of pT x 256 rows of qT with the m-grouped kernel's
+// pipeline (k-steps of 64 over the segment); every expert has the same tile grid, walked
+// in groups of up to GROUP_M pT blocks per qT sweep.
+// ---------------------------------------------------------------------------
+struct WSched {
+  int seg[MAXE + 1];   // segment bounds (starts rounded down to 8 elements)
+  int elist[MAXE];     // experts with rows, in order
+  int nne;
+  int wtot[16];
+};
+
+__device__ void build_wsched(WSched& sc, const int32_t* __restrict__ offsets, int E, int m_cap) {
+  const int tid = threadIdx.x;
+  const int mend = max(0, min(offsets[E], m_cap));
+  // a start that is not a multiple of 8 elements (outside the contract) is rounded down so
+  // every 16-byte load stays aligned
+  for (int e = tid; e <= E; e += blockDim.x)
+    sc.seg[e] = e < E ? (max(0, min(offsets[e], mend)) & ~7) : mend;
+  __syncthreads();
+  const int per = (MAXE + blockDim.x - 1) / blockDim.x;   // experts per thread (<= 4)
+  bool has[4];
+  int local = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = tid * per + i;
+    has[i] = i < per && e < E && sc.seg[e + 1] > sc.seg[e];
+    local += has[i];
+  }
+  int run = block_scan_excl(local, sc.wtot);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (has[i]) sc.elist[run++] = tid * per + i;
+  if (tid == (int)blockDim.x - 1) sc.nne = run;
+  __syncthreads();
+}
+
+struct WTile {
+  Tile t;       // e, first pT row (m0), pT rows, first qT row (n0)
+  int kseg0;    // first column of the segment
+  int nk;       // k-steps
+};
+
+__device__ __forceinline__ WTile wg_decode(const WSched& sc, int N1, int N2, int w) {
+  const int n_t1 = (N1 + BM - 1) / BM, n_t2 = (N2 + BP - 1) / BP;
+  const int per = n_t1 * n_t2;
+  const int ei = w / per;
+  const int local = w - ei * per;
+  const int gsz = min(GROUP_M, n_t1);
+  const int grp = local / (gsz * n_t2);
+  const int first = grp * gsz;
+  const int gm = min(gsz, n_t1 - first);
+  const int within = local - grp * gsz * n_t2;
+  WTile r;
+  r.t.e = sc.elist[ei];
+  r.t.m0 = (first + within % gm) * BM;
+  r.t.rows = min(BM, N1 - r.t.m0);
+  r.t.n0 = (within / gm) * BP;
+  r.kseg0 = sc.seg[r.t.e];
+  r.nk = (sc.seg[r.t.e + 1] - r.kseg0 + BK - 1) / BK;
+  return r;
+}
+
+// Same lane-to-row assignment as tile_loads; both descriptors start at the segment's
+// first column and end at the last row's end of ld, so nothing past the operand is read.
+__device__ __forceinline__ TileLoads wg_loads(const WTile& w, const bf16_t* __restrict__ pT,
+                                              const bf16_t* __restrict__ qT, int ld, int N2) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int lrow = 8 * wave + (lane >> 3);
+  const int lchunk = (lane & 7) ^ ((lrow >> 1) & 7);
+  const int prows = min(BP, N2 - w.t.n0);
+  TileLoads o;
+  o.na = w.t.rows > BM / 2 ? 4 : 2;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    o.aoff[j] = (uint32_t)(min(64 * j + lrow, w.t.rows - 1) * ld + lchunk * 8) * 2u;
+    o.boff[j] = (uint32_t)(min(64 * j + lrow, prows - 1) * ld + lchunk * 8) * 2u;
+  }
+  o.rsa = buffer_rsrc(pT + (size_t)w.t.m0 * ld + w.kseg0,
+                      (uint32_t)(w.t.rows * ld - w.kseg0) * 2u);
+  o.rsb = buffer_rsrc(qT + (size_t)w.t.n0 * ld + w.kseg0, (uint32_t)(prows * ld - w.kseg0) * 2u);
+  return o;
+}
+
+template <bool HALF>
+__device__ __forceinline__ void wg_tile(char* smem, const WTile& w, const TileLoads& ld, int N1,
+                                        int N2, int NS, float* __restrict__ out_lo,
+                                        float* __restrict__ out_hi, int stage0, bool primed,
+                                        const TileLoads& nxt, bool has_next) {
+  constexpr int WM = HALF ? 2 : 4;
+  constexpr int WN = 2;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int arow0 = (wave & 1) * (HALF ? 64 : 128);
+  const int prow0 = (wave >> 1) * 64;
+  const int fr = lane & 31;
+  f32x16 acc[WM][WN];
+  mainloop<HALF>(smem, ld, 0, w.nk, stage0, primed, nxt, has_next, 0, acc);
+#pragma unroll
+  for (int mb = 0; mb < WM; ++mb) {
+    const int r = arow0 + mb * 32 + fr;
+    if (r >= w.t.rows) continue;
+    const int i = w.t.m0 + r;
+    float* orow = i < NS ? out_lo + ((size_t)w.t.e * NS + i) * N2
+                         : out_hi + ((size_t)w.t.e * (N1 - NS) + (i - NS)) * N2;
+#pragma unroll
+    for (int nb = 0; nb < WN; ++nb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int j = w.t.n0 + prow0 + nb * 32 + g * 8 + (lane >> 5) * 4;
+        if (j >= N2) continue;
+        const f32x16& a = acc[mb][nb];
+        *reinterpret_cast<float4*>(orow + j) =
+            float4{a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]};
+      }
+  }
+}
+
+__global__ __launch_bounds__(NTHR, 1) void wg_bf16_kernel(
+    const bf16_t* __restrict__ pT, const bf16_t* __restrict__ qT, int ld,
+    const int32_t* __restrict__ offsets, int E, int N1, int N2, int NS, int m_cap,
+    float* __restrict__ out_lo, float* __restrict__ out_hi) {
+  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE_BYTES];
+  __shared__ WSched sc;
+  build_wsched(sc, offsets, E, m_cap);
+  int vb = blockIdx.x;
+  if (gridDim.x % XCDS == 0) vb = (blockIdx.x % XCDS) * (gridDim.x / XCDS) + blockIdx.x / XCDS;
+
+  // experts without rows: zero gradient
+  const int q2 = N2 / 4;
+  const int64_t per_e = (int64_t)N1 * q2;
+  for (int e = 0; e < E; ++e) {
+    if (sc.seg[e + 1] > sc.seg[e]) continue;
+    for (int64_t u = (int64_t)vb * NTHR + threadIdx.x; u < per_e; u += (int64_t)gridDim.x * NTHR) {
+      const int i = (int)(u / q2), j = (int)(u - (int64_t)i * q2) * 4;
+      float* orow = i < NS ? out_lo + ((size_t)e * NS + i) * N2
+                           : out_hi + ((size_t)e * (N1 - NS) + (i - NS)) * N2;
+      *reinterpret_cast<float4*>(orow + j) = float4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+  }
+
+  const int items = sc.nne * ((N1 + BM - 1) / BM) * ((N2 + BP - 1) / BP);
+  if (vb >= items) return;
+  WTile cur = wg_decode(sc, N1, N2, vb);
+  TileLoads ld_ = wg_loads(cur, pT, qT, ld, N2);
+  int stage0 = 0;
+  bool primed = false;
+  for (int w = vb; w < items; w += gridDim.x) {
+    const bool has_next = w + (int)gridDim.x < items;
+    WTile nw = cur;
+    TileLoads nl = ld_;
+    if (has_next) {
+      nw = wg_decode(sc, N1, N2, w + gridDim.x);
+      nl = wg_loads(nw, pT, qT, ld, N2);
+    }
+    if (cur.t.rows > BM / 2)
+      wg_tile<false>(smem, cur, ld_, N1, N2, NS, out_lo, out_hi, stage0, primed, nl, has_next);
+    else
+      wg_tile<true>(smem, cur, ld_, N1, N2, NS, out_lo, out_hi, stage0, primed, nl, has_next);
+    stage0 = (stage0 + cur.nk) & 1;
+    primed = has_next;
+    cur = nw;
+    ld_ = nl;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// float32: 16 rows x 64 columns per workgroup, k-steps of 32 staged in LDS (the tiny
+// float32 layer only); the same modes as the bf16 kernel, without rounding.
 // ---------------------------------------------------------------------------
 constexpr int FM = 16, FN = 64, FK = 32;
 
-template <bool FC1>
+struct Epi32 {
+  float* C;
+  float* ab;
+  float* dh;
+  int N;
+};
+
+template <int MODE>
 __global__ __launch_bounds__(256) void gg_f32_kernel(const float* __restrict__ A,
                                                      const int32_t* __restrict__ offsets,
                                                      const int32_t* __restrict__ tile_expert, int E,
-                                                     int K, int N, int m_tile, int m_cap,
+                                                     int K, int m_tile, int m_cap,
                                                      const float* __restrict__ W1,
-                                                     const float* __restrict__ W3,
-                                                     float* __restrict__ C) {
+                                                     const float* __restrict__ W3, Epi32 ep) {
+  constexpr bool FC1 = MODE == kFc1;
+  const int N = ep.N;
   __shared__ float As[FM][FK + 1];
   __shared__ float B1[FN][FK + 1];
   __shared__ float B3[FC1 ? FN : 1][FK + 1];
@@ -572,7 +824,75 @@ __global__ __launch_bounds__(256) void gg_f32_kernel(const float* __restrict__ A
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int n = n0 + tc + 16 * j;
-    if (n < N) C[(size_t)m * N + n] = FC1 ? a1[j] / (1.0f + expf(-a1[j])) * a3[j] : a1[j];
+    if (n >= N) continue;
+    const size_t row = (size_t)m * N;
+    if (MODE == kFc1) {
+      ep.C[row + n] = a1[j] / (1.0f + expf(-a1[j])) * a3[j];
+      if (ep.ab) {
+        ep.ab[2 * row + n] = a1[j];
+        ep.ab[2 * row + N + n] = a3[j];
+      }
+    } else if (MODE == kFc2) {
+      ep.C[row + n] = a1[j];
+    } else {
+      const float d = a1[j];
+      const float a = ep.ab[2 * row + n], b = ep.ab[2 * row + N + n];
+      const float s = 1.0f / (1.0f + expf(-a));
+      ep.C[2 * row + n] = d * b * (s * (1.0f + a * (1.0f - s)));
+      ep.C[2 * row + N + n] = d * (a * s);
+      if (ep.dh) ep.dh[row + n] = d;
+    }
+  }
+}
+
+// float32 k-grouped weight gradient: a 64 x 64 block of out[e] per workgroup, k-steps of
+// 16 segment rows staged in LDS; columns past the segment's end are masked, so segments
+// of any length work.
+constexpr int WT = 64, WK = 16;
+
+__global__ __launch_bounds__(256) void wg_f32_kernel(const float* __restrict__ pT,
+                                                     const float* __restrict__ qT, int ld,
+                                                     const int32_t* __restrict__ offsets, int E,
+                                                     int N1, int N2, int NS, int m_cap,
+                                                     float* __restrict__ out_lo,
+                                                     float* __restrict__ out_hi) {
+  __shared__ float Ps[WT][WK + 1];
+  __shared__ float Qs[WT][WK + 1];
+  const int e = blockIdx.y;
+  const int nt2 = (N2 + WT - 1) / WT;
+  const int i0 = (blockIdx.x / nt2) * WT, j0 = (blockIdx.x % nt2) * WT;
+  const int mend = max(0, min(offsets[E], m_cap));
+  const int s0 = max(0, min(offsets[e], mend));
+  const int s1 = max(s0, min(offsets[e + 1], mend));
+  const int tid = threadIdx.x;
+  const int ti = tid / 16, tj = tid % 16;
+  float acc[4][4] = {};
+  for (int k0 = s0; k0 < s1; k0 += WK) {
+    for (int x = tid; x < WT * WK; x += 256) {
+      const int r = x / WK, c = x % WK, k = k0 + c;
+      Ps[r][c] = (i0 + r < N1 && k < s1) ? pT[(size_t)(i0 + r) * ld + k] : 0.0f;
+      Qs[r][c] = (j0 + r < N2 && k < s1) ? qT[(size_t)(j0 + r) * ld + k] : 0.0f;
+    }
+    __syncthreads();
+    for (int c = 0; c < WK; ++c)
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+          acc[a][b] = fmaf(Ps[ti + 16 * a][c], Qs[tj + 16 * b][c], acc[a][b]);
+    __syncthreads();
+  }
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    const int i = i0 + ti + 16 * a;
+    if (i >= N1) continue;
+    float* orow = i < NS ? out_lo + ((size_t)e * NS + i) * N2
+                         : out_hi + ((size_t)e * (N1 - NS) + (i - NS)) * N2;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int j = j0 + tj + 16 * b;
+      if (j < N2) orow[j] = acc[a][b];
+    }
   }
 }
 
@@ -580,24 +900,29 @@ __global__ __launch_bounds__(256) void gg_f32_kernel(const float* __restrict__ A
 
 size_t grouped_workspace_bytes() { return (size_t)cu_count() * BM * BP * sizeof(float); }
 
-hipError_t launch_grouped_swiglu(int dt, int phases, const void* x_perm, const int32_t* offsets,
-                                 const int32_t* tile_expert, int E, int D, int F, int m_tile,
-                                 int64_t m_cap, const void* w1, const void* w3, const void* w2,
-                                 void* h, void* y_perm, void* workspace, size_t ws_bytes,
-                                 hipStream_t s) {
+// One m-grouped GEMM (C = A W^T per segment) with the MODE epilogue. K: reduction width,
+// ep.N: output columns.
+static hipError_t launch_mgrouped(int dt, int mode, const void* A, const int32_t* offsets,
+                                  const int32_t* tile_expert, int E, int K, int m_tile,
+                                  int64_t m_cap, const void* W1, const void* W3, void* C, void* ab,
+                                  void* dh, int N, void* workspace, size_t ws_bytes,
+                                  hipStream_t s) {
   if (dt == kF32) {
     const dim3 block(256);
-    const int mtiles = (int)((m_cap + FM - 1) / FM);
-    if (phases & 1)
-      hipLaunchKernelGGL(gg_f32_kernel<true>, dim3(mtiles, (F + FN - 1) / FN), block, 0, s,
-                         static_cast<const float*>(x_perm), offsets, tile_expert, E, D, F, m_tile,
-                         (int)m_cap, static_cast<const float*>(w1), static_cast<const float*>(w3),
-                         static_cast<float*>(h));
-    if (phases & 2)
-      hipLaunchKernelGGL(gg_f32_kernel<false>, dim3(mtiles, (D + FN - 1) / FN), block, 0, s,
-                         static_cast<const float*>(h), offsets, tile_expert, E, F, D, m_tile,
-                         (int)m_cap, static_cast<const float*>(w2), static_cast<const float*>(w2),
-                         static_cast<float*>(y_perm));
+    const dim3 grid((unsigned)((m_cap + FM - 1) / FM), (N + FN - 1) / FN);
+    const Epi32 ep{static_cast<float*>(C), static_cast<float*>(ab), static_cast<float*>(dh), N};
+    const float* a = static_cast<const float*>(A);
+    const float* w1 = static_cast<const float*>(W1);
+    const float* w3 = static_cast<const float*>(W3);
+    if (mode == kFc1)
+      hipLaunchKernelGGL(gg_f32_kernel<kFc1>, grid, block, 0, s, a, offsets, tile_expert, E, K,
+                         m_tile, (int)m_cap, w1, w3, ep);
+    else if (mode == kFc2)
+      hipLaunchKernelGGL(gg_f32_kernel<kFc2>, grid, block, 0, s, a, offsets, tile_expert, E, K,
+                         m_tile, (int)m_cap, w1, w1, ep);
+    else
+      hipLaunchKernelGGL(gg_f32_kernel<kDgrad>, grid, block, 0, s, a, offsets, tile_expert, E, K,
+                         m_tile, (int)m_cap, w1, w1, ep);
     return hipGetLastError();
   }
   const int G = cu_count();
@@ -605,22 +930,70 @@ hipError_t launch_grouped_swiglu(int dt, int phases, const void* x_perm, const i
   float* ws = static_cast<float*>(workspace);
   const int slots = ws ? (int)std::min<size_t>(ws_bytes / (BM * BP * sizeof(float)), 1 << 20) : 0;
   const dim3 rgrid(4 * G), rblock(256);
+  const Epi ep{static_cast<bf16_t*>(C), static_cast<bf16_t*>(ab), static_cast<bf16_t*>(dh), N};
+  const bf16_t* a = static_cast<const bf16_t*>(A);
+  const bf16_t* w1 = static_cast<const bf16_t*>(W1);
+  const bf16_t* w3 = static_cast<const bf16_t*>(W3);
+  if (mode == kFc1) {
+    hipLaunchKernelGGL(gg_bf16_kernel<kFc1>, grid, block, 0, s, a, offsets, E, K, N, (int)m_cap,
+                       w1, w3, ep, ws, slots);
+    if (slots)
+      hipLaunchKernelGGL(gg_tail_reduce<kFc1>, rgrid, rblock, 0, s, offsets, E, K, (int)m_cap, G,
+                         slots, ws, ep);
+  } else if (mode == kFc2) {
+    hipLaunchKernelGGL(gg_bf16_kernel<kFc2>, grid, block, 0, s, a, offsets, E, K, N, (int)m_cap,
+                       w1, w1, ep, ws, slots);
+    if (slots)
+      hipLaunchKernelGGL(gg_tail_reduce<kFc2>, rgrid, rblock, 0, s, offsets, E, K, (int)m_cap, G,
+                         slots, ws, ep);
+  } else {
+    hipLaunchKernelGGL(gg_bf16_kernel<kDgrad>, grid, block, 0, s, a, offsets, E, K, N, (int)m_cap,
+                       w1, w1, ep, ws, slots);
+    if (slots)
+      hipLaunchKernelGGL(gg_tail_reduce<kDgrad>, rgrid, rblock, 0, s, offsets, E, K, (int)m_cap, G,
+                         slots, ws, ep);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_grouped_swiglu(int dt, int phases, const void* x_perm, const int32_t* offsets,
+                                 const int32_t* tile_expert, int E, int D, int F, int m_tile,
+                                 int64_t m_cap, const void* w1, const void* w3, const void* w2,
+                                 void* h, void* ab, void* y_perm, void* workspace, size_t ws_bytes,
+                                 hipStream_t s) {
   if (phases & 1) {
-    hipLaunchKernelGGL(gg_bf16_kernel<true>, grid, block, 0, s, static_cast<const bf16_t*>(x_perm),
-                       offsets, E, D, F, (int)m_cap, static_cast<const bf16_t*>(w1),
-                       static_cast<const bf16_t*>(w3), static_cast<bf16_t*>(h), ws, slots);
-    if (slots)
-      hipLaunchKernelGGL(gg_tail_reduce<true>, rgrid, rblock, 0, s, offsets, E, D, F, (int)m_cap,
-                         G, slots, ws, static_cast<bf16_t*>(h));
+    const hipError_t e = launch_mgrouped(dt, kFc1, x_perm, offsets, tile_expert, E, D, m_tile,
+                                         m_cap, w1, w3, h, ab, nullptr, F, workspace, ws_bytes, s);
+    if (e != hipSuccess) return e;
   }
-  if (phases & 2) {
-    hipLaunchKernelGGL(gg_bf16_kernel<false>, grid, block, 0, s, static_cast<const bf16_t*>(h),
-                       offsets, E, F, D, (int)m_cap, static_cast<const bf16_t*>(w2),
-                       static_cast<const bf16_t*>(w2), static_cast<bf16_t*>(y_perm), ws, slots);
-    if (slots)
-      hipLaunchKernelGGL(gg_tail_reduce<false>, rgrid, rblock, 0, s, offsets, E, F, D, (int)m_cap,
-                         G, slots, ws, static_cast<bf16_t*>(y_perm));
+  if (phases & 2)
+    return launch_mgrouped(dt, kFc2, h, offsets, tile_expert, E, F, m_tile, m_cap, w2, w2, y_perm,
+                           nullptr, nullptr, D, workspace, ws_bytes, s);
+  return hipSuccess;
+}
+
+hipError_t launch_grouped_dgrad_swiglu(int dt, const void* dy_perm, const int32_t* offsets,
+                                       const int32_t* tile_expert, int E, int D, int F,
+                                       int m_tile, int64_t m_cap, const void* w2t, const void* ab,
+                                       void* dab, void* dh, void* workspace, size_t ws_bytes,
+                                       hipStream_t s) {
+  return launch_mgrouped(dt, kDgrad, dy_perm, offsets, tile_expert, E, D, m_tile, m_cap, w2t, w2t,
+                         dab, const_cast<void*>(ab), dh, F, workspace, ws_bytes, s);
+}
+
+hipError_t launch_grouped_wgrad(int dt, const void* pT, const void* qT, int64_t ld,
+                                const int32_t* offsets, int E, int N1, int N2, int NS,
+                                int64_t m_cap, float* out_lo, float* out_hi, hipStream_t s) {
+  if (dt == kF32) {
+    const dim3 grid(((N1 + WT - 1) / WT) * ((N2 + WT - 1) / WT), E), block(256);
+    hipLaunchKernelGGL(wg_f32_kernel, grid, block, 0, s, static_cast<const float*>(pT),
+                       static_cast<const float*>(qT), (int)ld, offsets, E, N1, N2, NS, (int)m_cap,
+                       out_lo, out_hi);
+    return hipGetLastError();
   }
+  hipLaunchKernelGGL(wg_bf16_kernel, dim3(cu_count()), dim3(NTHR), 0, s,
+                     static_cast<const bf16_t*>(pT), static_cast<const bf16_t*>(qT), (int)ld,
+                     offsets, E, N1, N2, NS, (int)m_cap, out_lo, out_hi);
   return hipGetLastError();
 }
 

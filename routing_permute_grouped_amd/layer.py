@@ -44,32 +44,126 @@ def moe_layer(x: torch.Tensor, w1: torch.Tensor, w3: torch.Tensor, w2: torch.Ten
               m_tile: int, wg: Optional[torch.Tensor] = None, bias: Optional[torch.Tensor] = None,
               topk_idx: Optional[torch.Tensor] = None, topk_w: Optional[torch.Tensor] = None,
               shared: Optional[SharedExperts] = None, renorm: bool = False,
-              check: bool = False, split_k: bool = True) -> dict:
+              check: bool = False, split_k: bool = True, save_for_backward: bool = False) -> dict:
     """Run the layer; returns every intermediate (dict). With routing given
     (``topk_idx``/``topk_w``) the route step is skipped. ``check`` synchronises and
     raises if the permute saw an expert index outside [-1, E). ``split_k`` gives the
-    grouped GEMMs a workspace so they can split a partly filled last round of tiles."""
-    E = w1.shape[0]
+    grouped GEMMs a workspace so they can split a partly filled last round of tiles.
+    ``save_for_backward`` also keeps fc1's pre-activations (``ab``, and ``shared_ab`` /
+    ``shared_h`` for the shared experts), which ``moe_layer_backward`` reads."""
+    E, F, D = w1.shape
     res = {}
     if topk_idx is None:
         topk_idx, topk_w, _ = B.moe_route(x, wg, k, bias=bias, renorm=renorm)
     res["topk_idx"], res["topk_w"] = topk_idx, topk_w
     p = B.moe_permute(x, topk_idx, E, m_tile)
     res.update(p)
+    m_cap = p["m_cap"]
     ws = B.grouped_workspace(x.device) if split_k else None
-    h, y = B.moe_grouped_swiglu(p["x_perm"], p["offsets"], p["tile_expert"], w1, w3, w2, m_tile,
-                                m_cap=p["m_cap"], workspace=ws)
+    if save_for_backward:
+        h = torch.empty((m_cap, F), dtype=x.dtype, device=x.device)
+        ab = torch.empty((m_cap, 2 * F), dtype=x.dtype, device=x.device)
+        y = torch.empty((m_cap, D), dtype=x.dtype, device=x.device)
+        B.moe_grouped_fc1_swiglu(p["x_perm"], p["offsets"], p["tile_expert"], w1, w3, m_tile,
+                                 m_cap, h, ab=ab, workspace=ws)
+        B.moe_grouped_fc2(h, p["offsets"], p["tile_expert"], w2, m_tile, m_cap, y, workspace=ws)
+        res["ab"] = ab
+    else:
+        h, y = B.moe_grouped_swiglu(p["x_perm"], p["offsets"], p["tile_expert"], w1, w3, w2,
+                                    m_tile, m_cap=m_cap, workspace=ws)
     res["h"], res["y_perm"] = h, y
     sh = None
     if shared is not None:
         rows = DenseRows(x.shape[0], m_tile, x.device)
-        _, ys = B.moe_grouped_swiglu(x, rows.offsets, rows.tile_expert, shared.w1, shared.w3,
-                                     shared.w2, m_tile, m_cap=rows.m_cap, workspace=ws)
+        if save_for_backward:
+            SF = shared.w1.shape[1]
+            hs = torch.empty((rows.m_cap, SF), dtype=x.dtype, device=x.device)
+            abs_ = torch.empty((rows.m_cap, 2 * SF), dtype=x.dtype, device=x.device)
+            ys = torch.empty((rows.m_cap, D), dtype=x.dtype, device=x.device)
+            B.moe_grouped_fc1_swiglu(x, rows.offsets, rows.tile_expert, shared.w1, shared.w3,
+                                     m_tile, rows.m_cap, hs, ab=abs_, workspace=ws)
+            B.moe_grouped_fc2(hs, rows.offsets, rows.tile_expert, shared.w2, m_tile, rows.m_cap,
+                              ys, workspace=ws)
+            res["shared_h"], res["shared_ab"] = hs, abs_
+        else:
+            _, ys = B.moe_grouped_swiglu(x, rows.offsets, rows.tile_expert, shared.w1, shared.w3,
+                                         shared.w2, m_tile, m_cap=rows.m_cap, workspace=ws)
         sh = ys[: x.shape[0]]
         res["shared"] = sh
-    res["out"] = B.moe_combine(y, p["dst_row"], topk_w, shared=sh, m_cap=p["m_cap"])
+    res["out"] = B.moe_combine(y, p["dst_row"], topk_w, shared=sh, m_cap=m_cap)
     if check:
         torch.cuda.current_stream().synchronize()
         if int(p["dev_err"].item()) != 0:
             raise ValueError("topk_idx holds expert indices outside [-1, E)")
+    return res
+
+
+def _round64(n: int) -> int:
+    return -(-n // 64) * 64
+
+
+def transposed_weights(w1: torch.Tensor, w3: torch.Tensor, w2: torch.Tensor):
+    """The weights as the backward GEMMs read them: w2t [E,F,D] (w2[e]^T) and
+    w13t [E,D,2F] = [w1[e]^T | w3[e]^T]."""
+    E, F, D = w1.shape
+    w2t = B.moe_transpose(w2)
+    w13t = torch.empty((E, D, 2 * F), dtype=w1.dtype, device=w1.device)
+    B.moe_transpose(w1, dst=w13t, ld=2 * F, col0=0)
+    B.moe_transpose(w3, dst=w13t, ld=2 * F, col0=F)
+    return w2t, w13t
+
+
+def _experts_backward(dy, x_rows, ab, h, offsets, tile_expert, w1, w3, w2, m_tile, m_cap,
+                      rows_valid, nrows_dev, ws):
+    """dgrad and wgrad of one grouped SwiGLU FFN over rows [0, m_cap) (section 5 of
+    "Expert Parallelism (EP)": the m-grouped fc mirrors into an m-grouped dgrad and a
+    k-grouped wgrad). Returns (dab, dX, dw1, dw3, dw2)."""
+    E, F, D = w1.shape
+    w2t, w13t = transposed_weights(w1, w3, w2)
+    dab = B.moe_grouped_dgrad_swiglu(dy, offsets, tile_expert, w2t, ab, m_tile, m_cap,
+                                     workspace=ws)
+    dX = torch.empty((m_cap, D), dtype=dy.dtype, device=dy.device)
+    B.moe_grouped_fc2(dab, offsets, tile_expert, w13t, m_tile, m_cap, dX, workspace=ws)
+    ld = _round64(m_cap)
+    T = dict(rows=rows_valid, nrows_dev=nrows_dev, R=ld)
+    dabT = B.moe_transpose(dab, **T)
+    xT = B.moe_transpose(x_rows, **T)
+    dyT = B.moe_transpose(dy, **T)
+    hT = B.moe_transpose(h, **T)
+    dw1, dw3 = B.moe_grouped_wgrad(dabT, xT, offsets, m_tile, m_cap, NS=F)
+    dw2, _ = B.moe_grouped_wgrad(dyT, hT, offsets, m_tile, m_cap, NS=D)
+    return dab, dX, dw1, dw3, dw2
+
+
+def moe_layer_backward(fwd: dict, dout: torch.Tensor, x: torch.Tensor, w1: torch.Tensor,
+                       w3: torch.Tensor, w2: torch.Tensor, m_tile: int,
+                       shared: Optional[SharedExperts] = None, split_k: bool = True) -> dict:
+    """Backward of ``moe_layer(..., save_for_backward=True)`` for the output gradient
+    ``dout`` [T, D], as the mirror of each forward step ("Expert Parallelism (EP)",
+    section 5): combine -> dispatch (moe_combine_backward), grouped SwiGLU -> dgrad +
+    wgrad, permute -> unpermute (moe_combine without weights). Routing is taken as
+    given; its weights get their gradient ``dtopk_w``. Weight gradients are float32
+    (``dw1``, ``dw3`` [E,F,D], ``dw2`` [E,D,F]; for the shared experts ``dws1``, ``dws3``
+    [1,S*Fs,D] and ``dws2`` [1,D,S*Fs], the concatenated layout of SharedExperts)."""
+    m_cap = fwd["m_cap"]
+    offs, te = fwd["offsets"], fwd["tile_expert"]
+    E = w1.shape[0]
+    ws = B.grouped_workspace(x.device) if split_k else None
+    res = {}
+    dy, dtw = B.moe_combine_backward(dout, fwd["y_perm"], fwd["src_row"], offs, fwd["dst_row"],
+                                     fwd["topk_w"], m_cap=m_cap)
+    res["dy_perm"], res["dtopk_w"] = dy, dtw
+    dab, dX, dw1, dw3, dw2 = _experts_backward(dy, fwd["x_perm"], fwd["ab"], fwd["h"], offs, te,
+                                               w1, w3, w2, m_tile, m_cap, m_cap, offs[E:], ws)
+    res.update(dab=dab, dx_perm=dX, dw1=dw1, dw3=dw3, dw2=dw2)
+    dxs = None
+    if shared is not None:
+        T = x.shape[0]
+        rows = DenseRows(T, m_tile, x.device)
+        _, dXs, dws1, dws3, dws2 = _experts_backward(
+            dout, x, fwd["shared_ab"], fwd["shared_h"], rows.offsets, rows.tile_expert,
+            shared.w1, shared.w3, shared.w2, m_tile, rows.m_cap, T, None, ws)
+        dxs = dXs[:T]
+        res.update(dx_shared=dxs, dws1=dws1, dws3=dws3, dws2=dws2)
+    res["dx"] = B.moe_combine(dX, fwd["dst_row"], None, shared=dxs, m_cap=m_cap)
     return res

@@ -22,10 +22,12 @@ def declared_symbols():
     return sorted(set(re.findall(r"^(?![\s/*#])[^\n(]*?\b(moe_[a-z_0-9]+)\(", text, re.M)))
 
 
-def test_header_declares_the_four_calls_and_helpers():
+def test_header_declares_the_calls_and_helpers():
     assert declared_symbols() == sorted(["moe_route", "moe_permute", "moe_grouped_swiglu",
                                          "moe_grouped_fc1_swiglu", "moe_grouped_fc2",
-                                         "moe_combine", "moe_capacity",
+                                         "moe_combine", "moe_combine_backward",
+                                         "moe_grouped_dgrad_swiglu", "moe_grouped_wgrad",
+                                         "moe_transpose", "moe_capacity",
                                          "moe_grouped_workspace_bytes",
                                          "moe_permute_workspace_bytes", "moe_status_str"])
 
@@ -114,11 +116,13 @@ def test_grouped_validation(kw, code):
 
 def test_split_grouped_calls_validate():
     assert lib.moe_grouped_fc1_swiglu(1, FAKE, FAKE, FAKE, 8, 128, 256, 128, 1024, None, FAKE,
-                                      FAKE, None, 0, None) == MOE_EINVAL
+                                      FAKE, None, None, 0, None) == MOE_EINVAL
     assert lib.moe_grouped_fc1_swiglu(1, FAKE, FAKE, FAKE, 8, 128, 250, 128, 1024, FAKE, FAKE,
-                                      FAKE, None, 0, None) == MOE_ESHAPE
+                                      FAKE, None, None, 0, None) == MOE_ESHAPE
     assert lib.moe_grouped_fc1_swiglu(1, FAKE, FAKE, FAKE, 8, 128, 256, 128, 1024, FAKE, FAKE,
-                                      FAKE, FAKE + 4, 1 << 20, None) == MOE_EINVAL
+                                      FAKE, None, FAKE + 4, 1 << 20, None) == MOE_EINVAL
+    assert lib.moe_grouped_fc1_swiglu(1, FAKE, FAKE, FAKE, 8, 128, 256, 128, 1024, FAKE, FAKE,
+                                      FAKE, FAKE + 2, None, 0, None) == MOE_EINVAL
     assert lib.moe_grouped_fc2(1, FAKE, FAKE, FAKE, 8, 128, 256, 128, 1000, FAKE, FAKE,
                                None, 0, None) == MOE_ECAPACITY
     assert lib.moe_grouped_fc2(1, FAKE, FAKE, FAKE, 8, 128, 256, 64, 1024, FAKE, FAKE,
@@ -141,6 +145,86 @@ def combine(dt=1, y=FAKE, dst=FAKE, w=FAKE, shared=None, T=64, D=128, k=2, m_cap
 ])
 def test_combine_validation(kw, code):
     assert combine(**kw) == code
+
+
+def test_combine_accepts_missing_weights_only_as_null():
+    # NULL weights are the unit-weight unpermute; a misaligned pointer is still rejected
+    assert combine(w=FAKE + 2) == MOE_EINVAL
+    assert combine(w=None, T=0) == MOE_ESHAPE
+
+
+def combine_bwd(dt=1, dout=FAKE, y=FAKE, src=FAKE, off=FAKE, dst=FAKE, w=FAKE, T=64, D=128, E=8,
+                k=2, m_cap=640, dy=FAKE, dw=FAKE):
+    return lib.moe_combine_backward(dt, dout, y, src, off, dst, w, T, D, E, k, m_cap, dy, dw, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=2), MOE_EINVAL), (dict(dout=None), MOE_EINVAL), (dict(y=FAKE + 4), MOE_EINVAL),
+    (dict(src=None), MOE_EINVAL), (dict(off=FAKE + 1), MOE_EINVAL), (dict(w=None), MOE_EINVAL),
+    (dict(dy=FAKE + 8), MOE_EINVAL), (dict(dw=None), MOE_EINVAL), (dict(T=0), MOE_ESHAPE),
+    (dict(D=96), MOE_ESHAPE), (dict(E=0), MOE_ESHAPE), (dict(E=1025), MOE_ESHAPE),
+    (dict(k=0), MOE_ESHAPE), (dict(k=33), MOE_ESHAPE), (dict(m_cap=0), MOE_ESHAPE),
+])
+def test_combine_backward_validation(kw, code):
+    assert combine_bwd(**kw) == code
+
+
+def dgrad(dt=1, dy=FAKE, E=8, D=128, F=256, mt=128, m_cap=1024, w2t=FAKE, ab=FAKE, dab=FAKE,
+          dh=None, ws=None, ws_bytes=0):
+    return lib.moe_grouped_dgrad_swiglu(dt, dy, FAKE, FAKE, E, D, F, mt, m_cap, w2t, ab, dab, dh,
+                                        ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=9), MOE_EINVAL), (dict(dy=None), MOE_EINVAL), (dict(w2t=FAKE + 2), MOE_EINVAL),
+    (dict(ab=None), MOE_EINVAL), (dict(dab=None), MOE_EINVAL), (dict(dh=FAKE + 8), MOE_EINVAL),
+    (dict(ws=FAKE + 4, ws_bytes=1 << 20), MOE_EINVAL), (dict(E=0), MOE_ESHAPE),
+    (dict(F=200), MOE_ESHAPE), (dict(D=65536, F=32768), MOE_ESHAPE), (dict(m_cap=1000),
+                                                                        MOE_ECAPACITY),
+    (dict(mt=64), MOE_EUNSUPPORTED),
+])
+def test_dgrad_validation(kw, code):
+    assert dgrad(**kw) == code
+
+
+def wgrad(dt=1, pT=FAKE, qT=FAKE, ld=1024, off=FAKE, E=8, N1=512, N2=128, NS=256, mt=128,
+          m_cap=1024, lo=FAKE, hi=FAKE):
+    return lib.moe_grouped_wgrad(dt, pT, qT, ld, off, E, N1, N2, NS, mt, m_cap, lo, hi, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=4), MOE_EINVAL), (dict(pT=None), MOE_EINVAL), (dict(qT=FAKE + 2), MOE_EINVAL),
+    (dict(off=None), MOE_EINVAL), (dict(lo=None), MOE_EINVAL), (dict(hi=FAKE + 4), MOE_EINVAL),
+    (dict(NS=-1), MOE_ESHAPE), (dict(NS=513), MOE_ESHAPE), (dict(N1=500), MOE_ESHAPE),
+    (dict(N2=0), MOE_ESHAPE), (dict(E=0), MOE_ESHAPE), (dict(mt=48), MOE_ESHAPE),
+    (dict(m_cap=1000), MOE_ECAPACITY), (dict(ld=1020), MOE_ESHAPE), (dict(ld=1000), MOE_ESHAPE),
+    (dict(ld=(1 << 22) + 8, m_cap=1024), MOE_ESHAPE), (dict(mt=32, m_cap=1024), MOE_EUNSUPPORTED),
+])
+def test_wgrad_validation(kw, code):
+    assert wgrad(**kw) == code
+
+
+def test_wgrad_needs_only_the_output_halves_it_writes():
+    # NS = N1: every row goes to out_lo, so out_hi may be NULL (and the reverse); these
+    # calls are made invalid by an unrelated size so nothing launches
+    assert wgrad(NS=512, hi=None, N2=100) == MOE_ESHAPE
+    assert wgrad(NS=0, lo=None, N2=100) == MOE_ESHAPE
+    assert wgrad(NS=256, hi=None) == MOE_EINVAL
+
+
+def transpose(dt=1, src=FAKE, B=1, R=256, C=128, rows=256, nrows=None, dst=FAKE, ld=256, col0=0):
+    return lib.moe_transpose(dt, src, B, R, C, rows, nrows, dst, ld, col0, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=3), MOE_EINVAL), (dict(src=None), MOE_EINVAL), (dict(dst=FAKE + 4), MOE_EINVAL),
+    (dict(nrows=FAKE + 2), MOE_EINVAL), (dict(B=0), MOE_ESHAPE), (dict(R=200), MOE_ESHAPE),
+    (dict(R=0, rows=0), MOE_ESHAPE), (dict(C=100), MOE_ESHAPE), (dict(rows=257), MOE_ESHAPE),
+    (dict(rows=-1), MOE_ESHAPE), (dict(col0=4, ld=512), MOE_ESHAPE), (dict(ld=252), MOE_ESHAPE),
+    (dict(col0=8, ld=256), MOE_ESHAPE), (dict(ld=260), MOE_ESHAPE),
+])
+def test_transpose_validation(kw, code):
+    assert transpose(**kw) == code
 
 
 def test_binding_raises_on_rejected_call():

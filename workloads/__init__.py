@@ -20,7 +20,9 @@ Generator recipe (numpy PCG64, ``default_rng(seed)``):
   w1, w3 and fan_in = F for w2 (std = 1/sqrt(fan_in));
 * draws are float32, and bf16 presets round them to bf16 with
   round-to-nearest-even, stored as uint16 bit patterns;
-* large weights are drawn expert by expert so host memory stays bounded.
+* large weights are drawn expert by expert so host memory stays bounded;
+* the output gradient of the backward, dout [T, D] ~ N(0, 1), has a stream of its
+  own (a unit-variance upstream gradient, stored in the preset's dtype).
 """
 from __future__ import annotations
 
@@ -33,7 +35,7 @@ from typing import Dict, Optional
 import numpy as np
 
 __all__ = [
-    "MoEConfig", "PRESETS", "preset", "shrink", "generate",
+    "MoEConfig", "PRESETS", "preset", "shrink", "generate", "output_grad",
     "f32_to_bf16_bits", "bf16_bits_to_f32", "as_f32",
 ]
 
@@ -110,7 +112,7 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
 # stream keyed by (seed, tag, block), so slabs can be drawn in parallel threads and a
 # slab's values do not depend on which other arrays were drawn.
 _TAGS = {"routing": 10, "x": 1, "wg": 2, "w1": 3, "w3": 4, "w2": 5,
-         "ws1": 6, "ws3": 7, "ws2": 8, "bias": 9}
+         "ws1": 6, "ws3": 7, "ws2": 8, "bias": 9, "dout": 11}
 _X_ROWS_PER_BLOCK = 1024
 _POOL_THREADS = max(1, min(16, len(os.sched_getaffinity(0))))
 
@@ -198,6 +200,18 @@ def generate(cfg: MoEConfig, seed: int = 0) -> dict:
         rank = _rng(seed, "bias").permutation(E).astype(np.float64) + 1.0
         out["bias"] = (-cfg.zipf_s * cfg.zipf_beta * np.log(rank)).astype(np.float32)
     out["cfg"] = cfg
+    return out
+
+
+def output_grad(cfg: MoEConfig, seed: int = 0) -> np.ndarray:
+    """dout [T, D] ~ N(0, 1) in cfg's dtype (``cfg`` with T filled in, as ``generate``
+    returns it), drawn in 1024-row blocks like x."""
+    T, D, dt = cfg.T, cfg.D, cfg.dtype
+    out = np.empty((T, D), dtype=np.float32 if dt == "f32" else np.uint16)
+    for b in range(-(-T // _X_ROWS_PER_BLOCK)):
+        r0 = b * _X_ROWS_PER_BLOCK
+        r1 = min(T, r0 + _X_ROWS_PER_BLOCK)
+        out[r0:r1] = _slab(seed, "dout", b, (r1 - r0, D), 1.0, dt)
     return out
 
 
