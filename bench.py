@@ -44,6 +44,8 @@ def parse():
     ap.add_argument("--workload", default="dense8_bf16")
     ap.add_argument("--cpu-sample-tokens", type=int, default=4096)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the timed backward pass (reported under \"backward\")")
     ap.add_argument("--no-split-k", action="store_true",
                     help="give the grouped GEMMs no workspace (every tile whole)")
     ap.add_argument("--shared-overlap", choices=["none", "start", "after-route"],
@@ -309,9 +311,136 @@ def main():
         "expert_rows_min_max": [int(counts.min()), int(counts.max())],
         "cpu_baseline": None,
     }
+    if not args.no_backward:
+        rec["backward"] = bench_backward(args, cfg, d, buf, shared, gws, flush, n_valid)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(inp, cfg, min(args.cpu_sample_tokens, T))
     print(json.dumps(rec), flush=True)
+
+
+def bench_backward(args, cfg, d, buf, shared, gws, flush, n_valid) -> dict:
+    """Time the layer's backward for a seeded output gradient, every buffer allocated
+    beforehand: combine backward -> dgrad (dh -> [da | db], then dX) -> wgrad ([dW1 | dW3],
+    dW2) [-> the shared experts' backward] -> unpermute. The forward is run once before
+    (untimed) with fc1 keeping [a | b]."""
+    import torch
+
+    import routing_permute_grouped_amd as rpg
+    import workloads as W
+
+    T, D, F, E, k, mt = cfg.T, cfg.D, cfg.F, cfg.E, cfg.k, cfg.m_tile
+    dev = d["x"].device
+    tdt = d["x"].dtype
+    stream = torch.cuda.current_stream()
+    m_cap = buf["x_perm"].shape[0]
+
+    def em(*shape, dtype=tdt):
+        return torch.empty(shape, dtype=dtype, device=dev)
+
+    dout_np = W.output_grad(cfg, seed=1)
+    dout = (torch.from_numpy(dout_np.view(np.int16)).to(dev).view(torch.bfloat16)
+            if dout_np.dtype == np.uint16 else torch.from_numpy(dout_np).to(dev))
+    f32 = torch.float32
+    b = {"ab": em(m_cap, 2 * F), "dy": em(m_cap, D), "dtw": em(T, k, dtype=f32),
+         "dab": em(m_cap, 2 * F), "dX": em(m_cap, D), "dw1": em(E, F, D, dtype=f32),
+         "dw3": em(E, F, D, dtype=f32), "dw2": em(E, D, F, dtype=f32), "dx": em(T, D)}
+    offs, te = buf["offsets"], buf["tile_expert"]
+    # forward once more, keeping fc1's pre-activations (routing/permute as in the timed run)
+    rpg.moe_grouped_fc1_swiglu(buf["x_perm"], offs, te, d["w1"], d["w3"], mt, m_cap, buf["h"],
+                               ab=b["ab"], workspace=gws)
+    rpg.moe_grouped_fc2(buf["h"], offs, te, d["w2"], mt, m_cap, buf["y"], workspace=gws)
+    if shared is not None:
+        rows = rpg.DenseRows(T, mt, dev)
+        SF = shared.w1.shape[1]
+        b.update(s_h=em(rows.m_cap, SF), s_ab=em(rows.m_cap, 2 * SF),
+                 s_dab=em(rows.m_cap, 2 * SF), s_dX=em(rows.m_cap, D),
+                 s_dw1=em(1, SF, D, dtype=f32), s_dw3=em(1, SF, D, dtype=f32),
+                 s_dw2=em(1, D, SF, dtype=f32))
+        rpg.moe_grouped_fc1_swiglu(d["x"], rows.offsets, rows.tile_expert, shared.w1, shared.w3,
+                                   mt, rows.m_cap, b["s_h"], ab=b["s_ab"], workspace=gws)
+
+    def experts_bwd(dy, xr, ab, h, o, tt, w1, w3, w2, mcap, pre):
+        Fx = w1.shape[1]
+        rpg.moe_grouped_dgrad_swiglu(dy, o, tt, w2, ab, mt, mcap, dab=b[pre + "dab"],
+                                     workspace=gws, stream=stream)
+        mark()
+        rpg.moe_grouped_dgrad_fc1(b[pre + "dab"], o, tt, w1, w3, mt, mcap, dx_perm=b[pre + "dX"],
+                                  workspace=gws, stream=stream)
+        mark()
+        rpg.moe_grouped_wgrad(b[pre + "dab"], xr, o, mt, mcap, NS=Fx, out_lo=b[pre + "dw1"],
+                              out_hi=b[pre + "dw3"], stream=stream)
+        mark()
+        rpg.moe_grouped_wgrad(dy, h, o, mt, mcap, NS=D, out_lo=b[pre + "dw2"], stream=stream)
+        mark()
+
+    marks = ["combine_bwd", "dgrad_fc2", "dgrad_fc1", "wgrad_fc1", "wgrad_fc2"]
+    if shared is not None:
+        marks += ["s_dgrad_fc2", "s_dgrad_fc1", "s_wgrad_fc1", "s_wgrad_fc2"]
+    marks += ["unpermute"]
+    cur = {"ev": None, "i": 0}
+
+    def mark():
+        if cur["ev"] is not None:
+            cur["ev"][cur["i"]].record(stream)
+        cur["i"] += 1
+
+    def step(ev=None):
+        cur["ev"], cur["i"] = ev, 0
+        mark()
+        rpg.moe_combine_backward(dout, buf["y"], buf["src_row"], offs, buf["dst_row"], buf["w"],
+                                 m_cap=m_cap, dy_perm=b["dy"], dtopk_w=b["dtw"], stream=stream)
+        mark()
+        experts_bwd(b["dy"], buf["x_perm"], b["ab"], buf["h"], offs, te, d["w1"], d["w3"],
+                    d["w2"], m_cap, "")
+        sh = None
+        if shared is not None:
+            experts_bwd(dout, d["x"], b["s_ab"], b["s_h"], rows.offsets, rows.tile_expert,
+                        shared.w1, shared.w3, shared.w2, rows.m_cap, "s_")
+            sh = b["s_dX"][:T]
+        rpg.moe_combine(b["dX"], buf["dst_row"], None, shared=sh, out=b["dx"], m_cap=m_cap,
+                        stream=stream)
+        mark()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(marks) + 1)]
+              for _ in range(args.steps)]
+    for s_ in range(args.steps):
+        if flush is not None:
+            flush.fill_(float(s_))
+        step(events[s_])
+    torch.cuda.synchronize()
+    per = {m: [events[s_][i].elapsed_time(events[s_][i + 1]) * 1e3 for s_ in range(args.steps)]
+           for i, m in enumerate(marks)}
+    per["step"] = [events[s_][0].elapsed_time(events[s_][-1]) * 1e3 for s_ in range(args.steps)]
+    avg = {m: statistics.fmean(v) for m, v in per.items()}
+    med = {m: statistics.median(v) for m, v in per.items()}
+    ndf = float(n_valid) * D * F
+    peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
+
+    def tf(flop, *stages):
+        t = sum(avg[m] for m in stages)
+        return flop / (t * 1e-6) / 1e12
+
+    gemm_stages = ["dgrad_fc2", "dgrad_fc1", "wgrad_fc1", "wgrad_fc2"]
+    routed_flop = 12.0 * ndf
+    out = {
+        "tokens_per_s": T / (avg["step"] * 1e-6),
+        "ms_per_step": avg["step"] * 1e-3,
+        "algorithmic_flop": {"routed": routed_flop,
+                             "shared": 12.0 * T * D * cfg.n_shared * cfg.F_shared},
+        "kernels_tflops": {"dgrad_fc2 (dh -> [da|db])": tf(2 * ndf, "dgrad_fc2"),
+                           "dgrad_fc1 (dX)": tf(4 * ndf, "dgrad_fc1"),
+                           "wgrad_fc1 ([dW1|dW3])": tf(4 * ndf, "wgrad_fc1"),
+                           "wgrad_fc2 (dW2)": tf(2 * ndf, "wgrad_fc2")},
+        "grouped_gemm_tflops": tf(routed_flop, *gemm_stages),
+        "grouped_gemm_frac_bf16_peak": tf(routed_flop, *gemm_stages) / peak,
+        "stage_us_mean": avg, "stage_us_median": med,
+        "note": "algorithmic FLOP: 12 D F per routed assignment (dgrad 6 + wgrad 6); "
+                "weight gradients are float32",
+    }
+    return out
 
 
 if __name__ == "__main__":

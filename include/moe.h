@@ -17,13 +17,12 @@
  *   moe_combine_backward      dispatch of the output gradient to the permuted rows
  *                             and the gradient of the top-k weights
  *   moe_grouped_dgrad_swiglu  dh = dY w2[e], then the SwiGLU backward -> [da | db]
- *   moe_grouped_fc2           (again) dX = [da | db] [w1[e] | w3[e]]^T, given
- *                             transposed weights
+ *   moe_grouped_dgrad_fc1     dX = da w1[e] + db w3[e]
  *   moe_grouped_wgrad         k-grouped dW2 = dY^T h, [dW1 | dW3] = [da | db]^T X
  *   moe_combine (no weights)  unpermute-and-sum: dx from dX (+ the shared experts' dx)
  *
- * with moe_transpose bringing weights and activations into the K-contiguous form
- * the GEMMs read.
+ * The backward GEMMs read the weights and activations in the layouts the forward
+ * uses; nothing is transposed in memory.
  *
  * Conventions shared by every call
  * --------------------------------
@@ -162,9 +161,6 @@ moe_status_t moe_grouped_swiglu(moe_dtype_t dt, const void* x_perm, const int32_
  * fc1 also stores the pre-activations for the backward when `ab` is non-NULL:
  * ab [m_cap, 2F] = [x_perm w1[e]^T | x_perm w3[e]^T] rounded to dt (h is formed
  * from the unrounded float32 sums); NULL skips it.
- * moe_grouped_fc2 is a plain m-grouped C = A B[e]^T: the backward calls it with
- * A = [da | db] [m_cap, 2F], B = [w1[e] | w3[e]]^T as [E, D, 2F] and F := 2F to
- * get dX, the input gradient of the routed experts.
  * Errors: as moe_grouped_swiglu.
  */
 moe_status_t moe_grouped_fc1_swiglu(moe_dtype_t dt, const void* x_perm, const int32_t* offsets,
@@ -222,8 +218,7 @@ moe_status_t moe_combine_backward(moe_dtype_t dt, const void* dout, const void* 
  * into an m-grouped dgrad).
  *
  *   dy_perm [m_cap,D], offsets, tile_expert (as moe_grouped_swiglu),
- *   w2t [E,F,D] (w2t[e] = w2[e]^T, see moe_transpose), ab [m_cap,2F] (from
- *   moe_grouped_fc1_swiglu)
+ *   w2 [E,D,F] (the forward's), ab [m_cap,2F] (from moe_grouped_fc1_swiglu)
  *   -> dh = dy_perm w2[e] per segment row, rounded to dt, then
  *      dab [m_cap,2F] = [dh*b*silu'(a) | dh*silu(a)] rounded to dt, with
  *      silu'(a) = s*(1 + a*(1 - s)), s = 1/(1 + exp(-a));
@@ -234,53 +229,46 @@ moe_status_t moe_combine_backward(moe_dtype_t dt, const void* dout, const void* 
  */
 moe_status_t moe_grouped_dgrad_swiglu(moe_dtype_t dt, const void* dy_perm, const int32_t* offsets,
                                       const int32_t* tile_expert, int E, int D, int F, int m_tile,
-                                      int64_t m_cap, const void* w2t, const void* ab, void* dab,
+                                      int64_t m_cap, const void* w2, const void* ab, void* dab,
                                       void* dh, void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * moe_grouped_dgrad_fc1 - the m-grouped dgrad of fc1 (same passage): the input
+ * gradient of the routed experts.
+ *
+ *   dab [m_cap,2F] = [da | db] (from moe_grouped_dgrad_swiglu), offsets,
+ *   tile_expert, w1, w3 [E,F,D] (the forward's)
+ *   -> dx_perm [m_cap,D] = da w1[e] + db w3[e] per segment row (one float32 sum
+ *      over the 2F terms, rounded once to dt).
+ * Rows >= offsets[E] are neither read nor written. Sizes, m_tile, workspace and
+ * errors as moe_grouped_swiglu.
+ */
+moe_status_t moe_grouped_dgrad_fc1(moe_dtype_t dt, const void* dab, const int32_t* offsets,
+                                   const int32_t* tile_expert, int E, int D, int F, int m_tile,
+                                   int64_t m_cap, const void* w1, const void* w3, void* dx_perm,
+                                   void* workspace, size_t ws_bytes, void* stream);
 
 /*
  * moe_grouped_wgrad - k-grouped GEMM for the weight gradients ("Expert
  * Parallelism (EP)", section 5: the backward of an m-grouped fc holds a
  * k-grouped GEMM, whose reduction runs over each expert's rows).
  *
- *   pT [N1, ld], qT [N2, ld] (dt): the two operands transposed, pT[i][r] = P[r][i]
- *   offsets [E+1] (segment rows, as moe_permute gives them)
- *   -> out[e][i][j] = sum_{offsets[e] <= r < offsets[e+1]} pT[i][r] * qT[j][r]
+ *   P [m_cap, N1], Q [m_cap, N2] (dt, row-major), offsets [E+1] (segment rows)
+ *   -> out[e][i][j] = sum_{offsets[e] <= r < offsets[e+1]} P[r][i] * Q[r][j]
  *      in float32, i < N1, j < N2; rows i < NS go to out_lo [E,NS,N2], rows
- *      i >= NS to out_hi [E,N1-NS,N2] (NULL when NS = N1 or NS = 0 respectively).
+ *      i >= NS to out_hi [E,N1-NS,N2] (either may be NULL when it gets no rows).
  *      Experts without rows get zeros.
- * Uses: [dW1 | dW3] = [da | db]^T x_perm (pT = dab transposed, N1 = 2F, NS = F,
- * qT = x_perm transposed, N2 = D); dW2 = dY^T h (pT = dy_perm transposed, N1 = D,
- * NS = D, qT = h transposed, N2 = F).
- * Segments are clamped to [0, min(offsets[E], m_cap)]. bf16 reads each segment in
- * steps of 64 columns: segment starts must be multiples of 64 (m_tile % 64 == 0),
- * and the columns from offsets[E] up to the next multiple of 64 must hold zeros
- * (moe_transpose writes them). float32 takes any segments.
- * N1, N2 multiples of 64 (<= 65536); ld a multiple of 8, at least m_cap rounded up
- * to 64, at most 2^22. The float32 sums of one output element run in a fixed order.
- * Errors: MOE_EINVAL, MOE_ESHAPE, MOE_ECAPACITY, MOE_EUNSUPPORTED (bf16 with
- * m_tile % 64 != 0), MOE_EHIP.
+ * Uses: [dW1 | dW3] = [da | db]^T x_perm (P = dab, N1 = 2F, NS = F, Q = x_perm,
+ * N2 = D); dW2 = dY^T h (P = dy_perm, N1 = NS = D, Q = h, N2 = F).
+ * Segments are clamped to [0, min(offsets[E], m_cap)] and may have any length
+ * and start (a dense FFN over T rows is E = 1, offsets = {0, T}); rows outside
+ * the segments are not read. The float32 sums of one element run in a fixed
+ * order. N1, N2 multiples of 64 (<= 65536); (m_cap + 64) * max(N1, N2) < 2^31.
+ * Errors: MOE_EINVAL, MOE_ESHAPE, MOE_ECAPACITY, MOE_EHIP.
  */
-moe_status_t moe_grouped_wgrad(moe_dtype_t dt, const void* pT, const void* qT, int64_t ld,
+moe_status_t moe_grouped_wgrad(moe_dtype_t dt, const void* P, const void* Q,
                                const int32_t* offsets, int E, int N1, int N2, int NS, int m_tile,
                                int64_t m_cap, float* out_lo, float* out_hi, void* stream);
-
-/*
- * moe_transpose - batched transpose into K-contiguous operands for the backward
- * GEMMs (weights: w2 [E,D,F] -> w2t [E,F,D]; w1, w3 [E,F,D] -> the halves
- * [:, :, 0:F] and [:, :, F:2F] of [E,D,2F]; activations [rows, N] -> [N, ld]).
- *
- *   src [batch][R][C] (dt; only rows r < rows are read)
- *   -> dst[b][c][col0 + r] = src[b][r][c] for r < rows', and 0 for
- *      rows' <= r < min(R, rows' rounded up to 64), where rows' = rows, or
- *      min(rows, *nrows_dev) when nrows_dev (a device int, e.g. offsets + E) is set.
- *      dst[b] is [C][ld_dst]; other columns are not written.
- * R, C multiples of 64 (R <= 2^22, C <= 65536); 0 <= rows <= R; col0 and ld_dst
- * multiples of 8 with ld_dst >= col0 + R; batch <= 65535.
- * Errors: MOE_EINVAL, MOE_ESHAPE, MOE_EHIP.
- */
-moe_status_t moe_transpose(moe_dtype_t dt, const void* src, int batch, int R, int C, int rows,
-                           const int32_t* nrows_dev, void* dst, int64_t ld_dst, int64_t col0,
-                           void* stream);
 
 /* Worst-case rows of the permuted buffer: with N = T*k slots,
  * m_tile * floor((N + min(E, N) * (m_tile - 1)) / m_tile). Returns -1 on bad sizes. */

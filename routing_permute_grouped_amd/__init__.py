@@ -5,18 +5,17 @@ include/moe.h); this package only marshals torch tensors into those calls.
 """
 from ._binding import (LIB_PATH, MOE_BF16, MOE_F32, SIGNATURES, MoEError, grouped_workspace,
                        lib, moe_capacity, moe_combine, moe_combine_backward,
-                       moe_grouped_dgrad_swiglu, moe_grouped_fc1_swiglu, moe_grouped_fc2,
-                       moe_grouped_swiglu, moe_grouped_wgrad, moe_grouped_workspace_bytes,
-                       moe_permute, moe_permute_workspace_bytes, moe_route, moe_status_str,
-                       moe_transpose)
-from .layer import (DenseRows, SharedExperts, moe_layer, moe_layer_backward,
-                    transposed_weights)
+                       moe_grouped_dgrad_fc1, moe_grouped_dgrad_swiglu, moe_grouped_fc1_swiglu,
+                       moe_grouped_fc2, moe_grouped_swiglu, moe_grouped_wgrad,
+                       moe_grouped_workspace_bytes, moe_permute, moe_permute_workspace_bytes,
+                       moe_route, moe_status_str)
+from .layer import DenseRows, SharedExperts, moe_layer, moe_layer_backward
 
 __all__ = [
     "LIB_PATH", "MOE_BF16", "MOE_F32", "SIGNATURES", "MoEError", "grouped_workspace", "lib",
-    "moe_capacity", "moe_combine", "moe_combine_backward", "moe_grouped_dgrad_swiglu",
-    "moe_grouped_fc1_swiglu", "moe_grouped_fc2", "moe_grouped_swiglu", "moe_grouped_wgrad",
-    "moe_grouped_workspace_bytes", "moe_permute", "moe_permute_workspace_bytes", "moe_route",
-    "moe_status_str", "moe_transpose", "DenseRows", "SharedExperts", "moe_layer",
-    "moe_layer_backward", "transposed_weights",
+    "moe_capacity", "moe_combine", "moe_combine_backward", "moe_grouped_dgrad_fc1",
+    "moe_grouped_dgrad_swiglu", "moe_grouped_fc1_swiglu", "moe_grouped_fc2", "moe_grouped_swiglu",
+    "moe_grouped_wgrad", "moe_grouped_workspace_bytes", "moe_permute",
+    "moe_permute_workspace_bytes", "moe_route", "moe_status_str", "DenseRows", "SharedExperts",
+    "moe_layer", "moe_layer_backward",
 ]

@@ -35,8 +35,9 @@ SIGNATURES = [
     ("moe_combine_backward", _I, [_I, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I64, _P, _P, _P]),
     ("moe_grouped_dgrad_swiglu", _I, [_I, _P, _P, _P, _I, _I, _I, _I, _I64, _P, _P, _P, _P, _P,
                                       _SZ, _P]),
-    ("moe_grouped_wgrad", _I, [_I, _P, _P, _I64, _P, _I, _I, _I, _I, _I, _I64, _P, _P, _P]),
-    ("moe_transpose", _I, [_I, _P, _I, _I, _I, _I, _P, _P, _I64, _I64, _P]),
+    ("moe_grouped_dgrad_fc1", _I, [_I, _P, _P, _P, _I, _I, _I, _I, _I64, _P, _P, _P, _P, _SZ,
+                                   _P]),
+    ("moe_grouped_wgrad", _I, [_I, _P, _P, _P, _I, _I, _I, _I, _I, _I64, _P, _P, _P]),
     ("moe_capacity", _I64, [_I, _I, _I, _I]),
     ("moe_grouped_workspace_bytes", _SZ, []),
     ("moe_permute_workspace_bytes", _SZ, [_I, _I, _I]),
@@ -248,66 +249,58 @@ def moe_combine_backward(dout: torch.Tensor, y_perm: torch.Tensor, src_row: torc
 
 
 def moe_grouped_dgrad_swiglu(dy_perm: torch.Tensor, offsets: torch.Tensor,
-                             tile_expert: torch.Tensor, w2t: torch.Tensor, ab: torch.Tensor,
+                             tile_expert: torch.Tensor, w2: torch.Tensor, ab: torch.Tensor,
                              m_tile: int, m_cap: Optional[int] = None,
                              dab: Optional[torch.Tensor] = None, dh: Optional[torch.Tensor] = None,
                              workspace: Optional[torch.Tensor] = None, stream=None):
-    """dab [m_cap, 2F] = [dh*b*silu'(a) | dh*silu(a)] with dh = dy_perm w2[e] (w2t [E,F,D]);
+    """dab [m_cap, 2F] = [dh*b*silu'(a) | dh*silu(a)] with dh = dy_perm w2[e] (w2 [E,D,F]);
     ``dh`` [m_cap, F], when given, receives dh."""
-    E, F, D = w2t.shape
+    E, D, F = w2.shape
     if m_cap is None:
         m_cap = dy_perm.shape[0]
     if dab is None:
         dab = torch.empty((m_cap, 2 * F), dtype=dy_perm.dtype, device=dy_perm.device)
     _check("moe_grouped_dgrad_swiglu", lib.moe_grouped_dgrad_swiglu(
         _dt(dy_perm), _ptr(dy_perm), _ptr(offsets), _ptr(tile_expert), E, D, F, m_tile, m_cap,
-        _ptr(w2t), _ptr(ab), _ptr(dab), _ptr(dh), *_ws(workspace), _stream(stream)))
+        _ptr(w2), _ptr(ab), _ptr(dab), _ptr(dh), *_ws(workspace), _stream(stream)))
     return dab
 
 
-def moe_grouped_wgrad(pT: torch.Tensor, qT: torch.Tensor, offsets: torch.Tensor, m_tile: int,
-                      m_cap: int, NS: Optional[int] = None, out_lo: Optional[torch.Tensor] = None,
-                      out_hi: Optional[torch.Tensor] = None, stream=None):
-    """out[e] = pT[:, seg e] qT[:, seg e]^T in float32, rows < NS in out_lo [E, NS, N2] and
-    the rest in out_hi [E, N1-NS, N2]. Returns (out_lo, out_hi)."""
-    N1, ld = pT.shape
-    N2 = qT.shape[0]
+def moe_grouped_dgrad_fc1(dab: torch.Tensor, offsets: torch.Tensor, tile_expert: torch.Tensor,
+                          w1: torch.Tensor, w3: torch.Tensor, m_tile: int,
+                          m_cap: Optional[int] = None, dx_perm: Optional[torch.Tensor] = None,
+                          workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """dx_perm [m_cap, D] = da w1[e] + db w3[e] for dab = [da | db] (w1, w3 [E,F,D])."""
+    E, F, D = w1.shape
+    if m_cap is None:
+        m_cap = dab.shape[0]
+    if dx_perm is None:
+        dx_perm = torch.empty((m_cap, D), dtype=dab.dtype, device=dab.device)
+    _check("moe_grouped_dgrad_fc1", lib.moe_grouped_dgrad_fc1(
+        _dt(dab), _ptr(dab), _ptr(offsets), _ptr(tile_expert), E, D, F, m_tile, m_cap, _ptr(w1),
+        _ptr(w3), _ptr(dx_perm), *_ws(workspace), _stream(stream)))
+    return dx_perm
+
+
+def moe_grouped_wgrad(P: torch.Tensor, Q: torch.Tensor, offsets: torch.Tensor, m_tile: int,
+                      m_cap: Optional[int] = None, NS: Optional[int] = None,
+                      out_lo: Optional[torch.Tensor] = None, out_hi: Optional[torch.Tensor] = None,
+                      stream=None):
+    """out[e] = P[seg e]^T Q[seg e] in float32 (P [m_cap, N1], Q [m_cap, N2]), rows < NS in
+    out_lo [E, NS, N2] and the rest in out_hi [E, N1-NS, N2]. Returns (out_lo, out_hi)."""
+    N1, N2 = P.shape[1], Q.shape[1]
     E = offsets.shape[0] - 1
-    if qT.shape[1] != ld:
-        raise ValueError("pT and qT must have the same row length")
+    if m_cap is None:
+        m_cap = P.shape[0]
     NS = N1 if NS is None else NS
-    f32 = dict(dtype=torch.float32, device=pT.device)
+    f32 = dict(dtype=torch.float32, device=P.device)
     if out_lo is None and NS > 0:
         out_lo = torch.empty((E, NS, N2), **f32)
     if out_hi is None and NS < N1:
         out_hi = torch.empty((E, N1 - NS, N2), **f32)
+    if P.dtype != Q.dtype:
+        raise TypeError("P and Q must share a dtype")
     _check("moe_grouped_wgrad", lib.moe_grouped_wgrad(
-        _dt(pT), _ptr(pT), _ptr(qT), ld, _ptr(offsets), E, N1, N2, NS, m_tile, m_cap,
-        _ptr(out_lo), _ptr(out_hi), _stream(stream)))
+        _dt(P), _ptr(P), _ptr(Q), _ptr(offsets), E, N1, N2, NS, m_tile, m_cap, _ptr(out_lo),
+        _ptr(out_hi), _stream(stream)))
     return out_lo, out_hi
-
-
-def moe_transpose(src: torch.Tensor, rows: Optional[int] = None,
-                  nrows_dev: Optional[torch.Tensor] = None, dst: Optional[torch.Tensor] = None,
-                  ld: Optional[int] = None, col0: int = 0, R: Optional[int] = None,
-                  stream=None) -> torch.Tensor:
-    """src [R, C] or [B, R, C] -> dst [(B,) C, ld] with dst[..., c, col0 + r] = src[..., r, c]
-    for r < rows (and < *nrows_dev), zeros up to the next multiple of 64. ``R`` (a multiple
-    of 64, default src's row count) may exceed src's rows when batch is 1."""
-    batched = src.dim() == 3
-    B = src.shape[0] if batched else 1
-    Rs, C = src.shape[-2:]
-    R = Rs if R is None else R
-    rows = Rs if rows is None else rows
-    if batched and R != Rs:
-        raise ValueError("a batched transpose takes R equal to the source rows")
-    if rows > Rs:
-        raise ValueError("rows exceeds the source")
-    ld = R if ld is None else ld
-    if dst is None:
-        shape = (B, C, ld) if batched else (C, ld)
-        dst = torch.empty(shape, dtype=src.dtype, device=src.device)
-    _check("moe_transpose", lib.moe_transpose(
-        _dt(src), _ptr(src), B, R, C, rows, _ptr(nrows_dev), _ptr(dst), ld, col0,
-        _stream(stream)))
-    return dst

@@ -67,14 +67,6 @@ __device__ __forceinline__ void store4(bf16_t* p, float a, float b, float c, flo
   *reinterpret_cast<uint2*>(p) = pk;
 }
 
-__device__ __forceinline__ void load4(const bf16_t* p, float* v) {
-  const uint2 pk = *reinterpret_cast<const uint2*>(p);
-  v[0] = bf16_lo(pk.x);
-  v[1] = bf16_hi(pk.x);
-  v[2] = bf16_lo(pk.y);
-  v[3] = bf16_hi(pk.y);
-}
-
 // What the m-grouped kernel does with its float32 sums (C = A W^T per segment row):
 //   kFc1   the panel interleaves w1 and w3 rows: h = silu(a)*b -> C [m][N]; when `ab` is
 //          set, the pre-activations a and b are stored too, as ab [m][2N] = [a | b]
@@ -93,6 +85,26 @@ struct Epi {
   int N;   // output columns (fc1, dgrad: F; fc2: D)
 };
 
+// kDgrad for columns n..n+3 of the row starting at element `row` (m * N): v holds the dh
+// sums, pa and pb the packed bf16 a and b of those columns.
+__device__ __forceinline__ void dgrad4(const Epi& ep, size_t row, int n, const float* v, uint2 pa,
+                                       uint2 pb) {
+  const float a[4] = {bf16_lo(pa.x), bf16_hi(pa.x), bf16_lo(pa.y), bf16_hi(pa.y)};
+  const float b[4] = {bf16_lo(pb.x), bf16_hi(pb.x), bf16_lo(pb.y), bf16_hi(pb.y)};
+  float d[4], da[4], db[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    d[i] = bf16_to_f32(f32_to_bf16(v[i]));              // dh as stored
+    const float s = 1.0f / (1.0f + __expf(-a[i]));      // sigmoid; silu = a*s
+    db[i] = d[i] * (a[i] * s);
+    da[i] = d[i] * b[i] * (s * (1.0f + a[i] * (1.0f - s)));
+  }
+  bf16_t* p = ep.C + 2 * row + n;
+  store4(p, da[0], da[1], da[2], da[3]);
+  store4(p + ep.N, db[0], db[1], db[2], db[3]);
+  if (ep.dh) store4(ep.dh + row + n, d[0], d[1], d[2], d[3]);
+}
+
 // Four consecutive output columns n..n+3 of row m; u holds the w3 sums for kFc1.
 template <int MODE>
 __device__ __forceinline__ void emit4(const Epi& ep, int m, int n, const float* v, const float* u) {
@@ -108,21 +120,8 @@ __device__ __forceinline__ void emit4(const Epi& ep, int m, int n, const float* 
   } else if (MODE == kFc2) {
     store4(ep.C + row + n, v[0], v[1], v[2], v[3]);
   } else {
-    float d[4], a[4], b[4], da[4], db[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) d[i] = bf16_to_f32(f32_to_bf16(v[i]));
-    load4(ep.ab + 2 * row + n, a);
-    load4(ep.ab + 2 * row + ep.N + n, b);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float s = 1.0f / (1.0f + __expf(-a[i]));   // sigmoid; silu = a*s
-      db[i] = d[i] * (a[i] * s);
-      da[i] = d[i] * b[i] * (s * (1.0f + a[i] * (1.0f - s)));
-    }
-    bf16_t* p = ep.C + 2 * row + n;
-    store4(p, da[0], da[1], da[2], da[3]);
-    store4(p + ep.N, db[0], db[1], db[2], db[3]);
-    if (ep.dh) store4(ep.dh + row + n, d[0], d[1], d[2], d[3]);
+    dgrad4(ep, row, n, v, *reinterpret_cast<const uint2*>(ep.ab + 2 * row + n),
+           *reinterpret_cast<const uint2*>(ep.ab + 2 * row + ep.N + n));
   }
 }
 
@@ -179,21 +178,44 @@ __device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t voff, uint32_t soff, 
                : "memory", "m0");
 }
 
-// Load addresses of one tile at k-step 0, per lane: buffer descriptors for its A rows
-// and for expert e's weight matrix, and the byte offsets of the rows this lane fills.
-// Piece j of wave w holds rows 64*j + 8*w .. +7; lane l fills row 64*j + lrow with
-// lrow = 8*w + l/8, 16-byte slot l%8, which holds logical chunk (l%8) ^ ((row/2)%8).
-// Rows past the tile or the matrix are clamped to the last one.
+// Each operand of a tile is staged per k-step as 256 "rows" (A rows or panel rows,
+// the MFMA's M or N index) x 64 k values, in one of two LDS layouts:
+//  * K-contiguous (the operand's rows hold k contiguous in memory): 256 LDS rows of
+//    128 bytes. Piece j of wave w holds rows 64*j + 8*w .. +7; lane l fills row
+//    64*j + lrow with lrow = 8*w + l/8, 16-byte slot l%8, which holds logical chunk
+//    (l%8) ^ ((row/2)%8). Rows past the tile or the matrix are clamped to the last one.
+//  * MN-major (the operand is stored [k][n], n contiguous, e.g. w2 [E,D,F] read as the
+//    dgrad's [F x D] panel, or activations [rows, N] read over their rows in the wgrad):
+//    64 LDS rows (one per k) of 512 bytes. Piece j of wave w holds k rows
+//    2*(8*j + w) and +1 (l / 32); lane l fills 16-byte slot l%32 of its row with the 8
+//    columns of logical slot (l%32) ^ (4*(k%4)). Fragments are read back with the
+//    gfx950 transposing LDS load (see frag_mn).
+// Both layouts fill 1 KiB per wave and piece, at the same LDS offsets.
 struct TileLoads {
-  i32x4 rsa, rsb;
+  i32x4 rsa, rsb, rsb2;
   uint32_t aoff[4], boff[4];
-  int na;   // A pieces per wave: 4 for a full tile, 2 for a half tile
+  uint32_t astep, bstep;   // bytes between k-steps (K-contiguous: 128; MN-major: 64 rows)
+  int bsplit;              // k-steps read from rsb; the following ones from rsb2, from its start
+  int na;                  // A pieces per wave: 4 for a full tile, 2 for a half K-contiguous one
 };
 
-template <bool FC1>
+// Byte offset of lane's 16 bytes of piece j in an MN-major operand with row pitch ld.
+__device__ __forceinline__ uint32_t mn_off(int j, int ld) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = 2 * (8 * j + wave) + (lane >> 5);
+  return (uint32_t)(r * ld + 8 * ((lane & 31) ^ (4 * (r & 3)))) * 2u;
+}
+
+// Loads of an m-grouped tile: A = rows [m0, m0 + rows) of a K-contiguous [m][K] buffer;
+// the panel = expert e's weights from panel row n0:
+//   P_MN false: W1 [E][N][K] (fc1 interleaves W1 and W3 rows in 32-row blocks);
+//   P_MN true:  [E][K][N] read MN-major, the first `ksplit` k from W1 [E][ksplit][N] and
+//               the rest from W3 [E][K - ksplit][N] (ksplit = K: W1 only).
+template <bool FC1, bool P_MN>
 __device__ __forceinline__ TileLoads tile_loads(const Tile& t, const bf16_t* __restrict__ A,
                                                 const bf16_t* __restrict__ W1,
-                                                const bf16_t* __restrict__ W3, int K, int N) {
+                                                const bf16_t* __restrict__ W3, int K, int N,
+                                                int ksplit) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int lrow = 8 * wave + (lane >> 3);
@@ -204,15 +226,32 @@ __device__ __forceinline__ TileLoads tile_loads(const Tile& t, const bf16_t* __r
   for (int j = 0; j < 4; ++j)
     o.aoff[j] = (uint32_t)(min(64 * j + lrow, t.rows - 1) * K + lchunk * 8) * 2u;
   o.rsa = buffer_rsrc(A + (size_t)t.m0 * K, (uint32_t)t.rows * K * 2u);
-  // fc1: panel rows alternate 32-row blocks of w1 and w3 over the same 32 columns;
-  // row 64*j + lrow is in a w3 block exactly when lrow >= 32, i.e. for waves 4..7
-  const bf16_t* wsel = (FC1 && wave >= 4) ? W3 : W1;
-  o.rsb = buffer_rsrc(wsel + (size_t)t.e * N * K, (uint32_t)N * K * 2u);
+  o.astep = BK * 2;
+  if (P_MN) {
+    // columns past N read into the next row (or past the end, zero-filled): such panel
+    // rows only feed output columns that are not stored
+    o.rsb = buffer_rsrc(W1 + (size_t)t.e * ksplit * N + t.n0, (uint32_t)(ksplit * N - t.n0) * 2u);
+    o.rsb2 = ksplit < K ? buffer_rsrc(W3 + (size_t)t.e * (K - ksplit) * N + t.n0,
+                                      (uint32_t)((K - ksplit) * N - t.n0) * 2u)
+                        : o.rsb;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int pr = 64 * j + lrow;
-    const int gr = FC1 ? t.n0 + (pr >> 6) * 32 + (pr & 31) : t.n0 + pr;
-    o.boff[j] = (uint32_t)(min(gr, N - 1) * K + lchunk * 8) * 2u;
+    for (int j = 0; j < 4; ++j) o.boff[j] = mn_off(j, N);
+    o.bstep = (uint32_t)BK * N * 2u;
+    o.bsplit = ksplit / BK;
+  } else {
+    // fc1: panel rows alternate 32-row blocks of w1 and w3 over the same 32 columns;
+    // row 64*j + lrow is in a w3 block exactly when lrow >= 32, i.e. for waves 4..7
+    const bf16_t* wsel = (FC1 && wave >= 4) ? W3 : W1;
+    o.rsb = buffer_rsrc(wsel + (size_t)t.e * N * K, (uint32_t)N * K * 2u);
+    o.rsb2 = o.rsb;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int pr = 64 * j + lrow;
+      const int gr = FC1 ? t.n0 + (pr >> 6) * 32 + (pr & 31) : t.n0 + pr;
+      o.boff[j] = (uint32_t)(min(gr, N - 1) * K + lchunk * 8) * 2u;
+    }
+    o.bstep = BK * 2;
+    o.bsplit = 1 << 30;
   }
   return o;
 }
@@ -220,16 +259,42 @@ __device__ __forceinline__ TileLoads tile_loads(const Tile& t, const bf16_t* __r
 // Loads of k-step kt into the LDS stage at `la` (this wave's first piece): the A pieces
 // (part 0) or the panel pieces (part 1).
 __device__ __forceinline__ void issue_loads(const TileLoads& o, uint32_t la, int kt, int part) {
-  const uint32_t ko = (uint32_t)kt * BK * 2u;
   if (part == 0) {
+    const uint32_t ko = (uint32_t)kt * o.astep;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       if (j < o.na) dma16(o.rsa, o.aoff[j], ko, la + j * 8192);
   } else {
     const uint32_t lb = la + A_BYTES;
+    const bool second = kt >= o.bsplit;
+    const i32x4 rs = second ? o.rsb2 : o.rsb;
+    const uint32_t ko = (uint32_t)(second ? kt - o.bsplit : kt) * o.bstep;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) dma16(o.rsb, o.boff[j], ko, lb + j * 8192);
+    for (int j = 0; j < 4; ++j) dma16(rs, o.boff[j], ko, lb + j * 8192);
   }
+}
+
+// MFMA fragment of 32 rows (MFMA index nbase .. +31) for k slice ks from an MN-major
+// stage: lane l gets index nbase + l%32 and k = 16*ks + 8*(l/32) .. +7, as two
+// transposing 8-byte LDS loads. Within each 16-lane group, lane j of the load names row
+// k0 + j/4 and the 4 columns starting at 4*(j%4) of the group's 16, and the hardware hands
+// lane i column i of that 16 x 4 block, i.e. 4 consecutive k of one column. Row k's
+// 8-byte units are XOR-swizzled by 8*(k%4) (matching the loads), so the 16 lanes of a
+// group and the two groups of a half-wave hit distinct banks.
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ bf16x8 frag_mn(const char* stage, int nbase, int ks) {
+  const int lane = threadIdx.x & 63;
+  const int q = (lane >> 2) & 3;
+  const int k = ks * 16 + (lane >> 5) * 8 + q;
+  const int u = (nbase >> 2) + ((lane >> 4) & 1) * 4 + (lane & 3);
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  const __attribute__((address_space(3))) char* p =
+      (const __attribute__((address_space(3))) char*)stage + k * 512 + ((u ^ (8 * q)) << 3);
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 4 * 512));
+  const i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, v);
 }
 
 // One tile: rows [m0, m0 + rows) of expert e against the weight panel from n0, k-steps
@@ -252,7 +317,7 @@ __device__ __forceinline__ void issue_loads(const TileLoads& o, uint32_t la, int
 // step the free stage instead receives the first step of the next tile (`nxt`, step
 // `nkb`), so its load latency hides under this tile's last MFMAs and its epilogue;
 // `primed` says that this tile's first step was loaded that way.
-template <bool HALF>
+template <bool HALF, bool A_MN, bool P_MN>
 __device__ __forceinline__ void mainloop(char* smem, const TileLoads& ld, int kb, int ke,
                                          int stage0, bool primed, const TileLoads& nxt,
                                          bool has_next, int nkb, f32x16 (&acc)[HALF ? 2 : 4][2]) {
@@ -289,10 +354,12 @@ __device__ __forceinline__ void mainloop(char* smem, const TileLoads& ld, int kb
       const int chk = ks * 2 + (lane >> 5);
 #pragma unroll
       for (int nb = 0; nb < WN; ++nb)
-        wf[buf][nb] = *reinterpret_cast<const bf16x8*>(sb + swz(prow0 + nb * 32 + fr, chk));
+        wf[buf][nb] = P_MN ? frag_mn(sb, prow0 + nb * 32, ks)
+                           : *reinterpret_cast<const bf16x8*>(sb + swz(prow0 + nb * 32 + fr, chk));
 #pragma unroll
       for (int mb = 0; mb < WM; ++mb)
-        af[buf][mb] = *reinterpret_cast<const bf16x8*>(sa + swz(arow0 + mb * 32 + fr, chk));
+        af[buf][mb] = A_MN ? frag_mn(sa, arow0 + mb * 32, ks)
+                           : *reinterpret_cast<const bf16x8*>(sa + swz(arow0 + mb * 32 + fr, chk));
     };
     frag(0, 0);
 #pragma unroll
@@ -321,7 +388,7 @@ __device__ __forceinline__ void mainloop(char* smem, const TileLoads& ld, int kb
 // a split-K share (`part`, row-major [BM][BP]) or the MODE epilogue.
 // After the main loop lane l holds column m = l % 32 of every 32x32 block and panel rows
 // 8*g + 4*(l / 32) + i (i = 0..3) for g = 0..3.
-template <int MODE, bool HALF>
+template <int MODE, bool HALF, bool P_MN>
 __device__ __forceinline__ void run_tile(char* smem, const Tile& t, const TileLoads& ld,
                                          const Epi& ep, int kb, int ke,
                                          float* __restrict__ part, int stage0, bool primed,
@@ -334,7 +401,7 @@ __device__ __forceinline__ void run_tile(char* smem, const Tile& t, const TileLo
   const int prow0 = (wave >> 1) * 64;
   const int fr = lane & 31;
   f32x16 acc[WM][WN];
-  mainloop<HALF>(smem, ld, kb, ke, stage0, primed, nxt, has_next, nkb, acc);
+  mainloop<HALF, false, P_MN>(smem, ld, kb, ke, stage0, primed, nxt, has_next, nkb, acc);
 
   if (part) {
 #pragma unroll
@@ -369,6 +436,30 @@ __device__ __forceinline__ void run_tile(char* smem, const Tile& t, const TileLo
         const float u[4] = {b[4 * g], b[4 * g + 1], b[4 * g + 2], b[4 * g + 3]};
         emit4<MODE>(ep, m, n, v, u);
       }
+    } else if (MODE == kDgrad) {
+      // all of the row's (a, b) loads first, so they are in flight together rather than
+      // one round trip per group of four columns
+      const size_t row = (size_t)m * ep.N;
+      uint2 pa[WN][4], pb[WN][4];
+#pragma unroll
+      for (int nb = 0; nb < WN; ++nb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int n = t.n0 + prow0 + nb * 32 + g * 8 + (lane >> 5) * 4;
+          if (n >= ep.N) continue;
+          pa[nb][g] = *reinterpret_cast<const uint2*>(ep.ab + 2 * row + n);
+          pb[nb][g] = *reinterpret_cast<const uint2*>(ep.ab + 2 * row + ep.N + n);
+        }
+#pragma unroll
+      for (int nb = 0; nb < WN; ++nb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int n = t.n0 + prow0 + nb * 32 + g * 8 + (lane >> 5) * 4;
+          if (n >= ep.N) continue;
+          const f32x16& a = acc[mb][nb];
+          const float v[4] = {a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]};
+          dgrad4(ep, row, n, v, pa[nb][g], pb[nb][g]);
+        }
     } else {
 #pragma unroll
       for (int nb = 0; nb < WN; ++nb) {
@@ -478,10 +569,11 @@ __device__ Split split_plan(int total, int G, int slots, int nk) {
   return p;
 }
 
-template <int MODE>
+// P_MN: the weights are read MN-major (see tile_loads); ksplit as there.
+template <int MODE, bool P_MN>
 __global__ __launch_bounds__(NTHR, 1) void gg_bf16_kernel(
     const bf16_t* __restrict__ A, const int32_t* __restrict__ offsets, int E, int K, int N,
-    int m_cap, const bf16_t* __restrict__ W1, const bf16_t* __restrict__ W3,
+    int m_cap, const bf16_t* __restrict__ W1, const bf16_t* __restrict__ W3, int ksplit,
     Epi ep, float* __restrict__ ws, int slots) {
   constexpr bool FC1 = MODE == kFc1;
   __shared__ __attribute__((aligned(16))) char smem[2 * STAGE_BYTES];
@@ -522,7 +614,7 @@ __global__ __launch_bounds__(NTHR, 1) void gg_bf16_kernel(
 
   if (vb >= items) return;
   Work cur = work(vb);
-  TileLoads ld = tile_loads<FC1>(cur.t, A, W1, W3, K, N);
+  TileLoads ld = tile_loads<FC1, P_MN>(cur.t, A, W1, W3, K, N, ksplit);
   int stage0 = 0;
   bool primed = false;
   for (int w = vb; w < items; w += gridDim.x) {
@@ -531,14 +623,14 @@ __global__ __launch_bounds__(NTHR, 1) void gg_bf16_kernel(
     TileLoads nl = ld;
     if (has_next) {
       nw = work(w + gridDim.x);
-      nl = tile_loads<FC1>(nw.t, A, W1, W3, K, N);
+      nl = tile_loads<FC1, P_MN>(nw.t, A, W1, W3, K, N, ksplit);
     }
     if (cur.t.rows > BM / 2)
-      run_tile<MODE, false>(smem, cur.t, ld, ep, cur.kb, cur.ke, cur.part, stage0, primed, nl,
-                           has_next, nw.kb);
+      run_tile<MODE, false, P_MN>(smem, cur.t, ld, ep, cur.kb, cur.ke, cur.part, stage0, primed,
+                                  nl, has_next, nw.kb);
     else
-      run_tile<MODE, true>(smem, cur.t, ld, ep, cur.kb, cur.ke, cur.part, stage0, primed, nl,
-                          has_next, nw.kb);
+      run_tile<MODE, true, P_MN>(smem, cur.t, ld, ep, cur.kb, cur.ke, cur.part, stage0, primed,
+                                 nl, has_next, nw.kb);
     stage0 = (stage0 + cur.ke - cur.kb) & 1;
     primed = has_next;
     cur = nw;
@@ -593,15 +685,17 @@ __global__ __launch_bounds__(256) void gg_tail_reduce(const int32_t* __restrict_
 // m-grouped fc is an m-grouped dgrad plus a k-grouped wgrad). For every expert e with
 // segment rows [s_e, s_e+1) (offsets, clamped to the rows in use):
 //   out[e][i][j] = sum over r in the segment of P[r][i] * Q[r][j]     (i < N1, j < N2)
-// with both operands given K-contiguous, i.e. transposed: pT [N1][ld], qT [N2][ld]. Rows
+// with P [rows][N1] and Q [rows][N2] the activations as the forward and the dgrad leave
+// them (row-major): both operands are read MN-major, a k-step being 64 segment rows. Rows
 // i < NS of the result go to out_lo [E][NS][N2], the others to out_hi [E][N1-NS][N2]
 // (float32), so [dW1 | dW3] from [da | db] lands in two separate arrays. Experts without
-// rows get zeros. Tiles are 256 rows of pT x 256 rows of qT with the m-grouped kernel's
-// pipeline (k-steps of 64 over the segment); every expert has the same tile grid, walked
-// in groups of up to GROUP_M pT blocks per qT sweep.
+// rows get zeros. Tiles are 256 columns of P x 256 columns of Q with the m-grouped
+// kernel's pipeline; every expert has the same tile grid, walked in groups of up to
+// GROUP_M P blocks per Q sweep. The buffer descriptors of a tile end at its segment's
+// last row, so the rows of the last, partial k-step past the segment read as zeros.
 // ---------------------------------------------------------------------------
 struct WSched {
-  int seg[MAXE + 1];   // segment bounds (starts rounded down to 8 elements)
+  int seg[MAXE + 1];   // segment bounds
   int elist[MAXE];     // experts with rows, in order
   int nne;
   int wtot[16];
@@ -610,10 +704,7 @@ struct WSched {
 __device__ void build_wsched(WSched& sc, const int32_t* __restrict__ offsets, int E, int m_cap) {
   const int tid = threadIdx.x;
   const int mend = max(0, min(offsets[E], m_cap));
-  // a start that is not a multiple of 8 elements (outside the contract) is rounded down so
-  // every 16-byte load stays aligned
-  for (int e = tid; e <= E; e += blockDim.x)
-    sc.seg[e] = e < E ? (max(0, min(offsets[e], mend)) & ~7) : mend;
+  for (int e = tid; e <= E; e += blockDim.x) sc.seg[e] = max(0, min(offsets[e], mend));
   __syncthreads();
   const int per = (MAXE + blockDim.x - 1) / blockDim.x;   // experts per thread (<= 4)
   bool has[4];
@@ -633,8 +724,9 @@ __device__ void build_wsched(WSched& sc, const int32_t* __restrict__ offsets, in
 }
 
 struct WTile {
-  Tile t;       // e, first pT row (m0), pT rows, first qT row (n0)
-  int kseg0;    // first column of the segment
+  Tile t;       // e, first P column (m0), P columns (rows), first Q column (n0)
+  int kseg0;    // first row of the segment
+  int klen;     // rows of the segment
   int nk;       // k-steps
 };
 
@@ -654,29 +746,28 @@ __device__ __forceinline__ WTile wg_decode(const WSched& sc, int N1, int N2, int
   r.t.rows = min(BM, N1 - r.t.m0);
   r.t.n0 = (within / gm) * BP;
   r.kseg0 = sc.seg[r.t.e];
-  r.nk = (sc.seg[r.t.e + 1] - r.kseg0 + BK - 1) / BK;
+  r.klen = sc.seg[r.t.e + 1] - r.kseg0;
+  r.nk = (r.klen + BK - 1) / BK;
   return r;
 }
 
-// Same lane-to-row assignment as tile_loads; both descriptors start at the segment's
-// first column and end at the last row's end of ld, so nothing past the operand is read.
-__device__ __forceinline__ TileLoads wg_loads(const WTile& w, const bf16_t* __restrict__ pT,
-                                              const bf16_t* __restrict__ qT, int ld, int N2) {
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int lrow = 8 * wave + (lane >> 3);
-  const int lchunk = (lane & 7) ^ ((lrow >> 1) & 7);
-  const int prows = min(BP, N2 - w.t.n0);
+// Both operands MN-major (mn_off); each descriptor starts at the segment's first row and
+// the tile's first column and ends at the segment's last row.
+__device__ __forceinline__ TileLoads wg_loads(const WTile& w, const bf16_t* __restrict__ P,
+                                              const bf16_t* __restrict__ Q, int N1, int N2) {
   TileLoads o;
-  o.na = w.t.rows > BM / 2 ? 4 : 2;
+  o.na = 4;
+  o.rsa = buffer_rsrc(P + (size_t)w.kseg0 * N1 + w.t.m0, (uint32_t)(w.klen * N1 - w.t.m0) * 2u);
+  o.rsb = buffer_rsrc(Q + (size_t)w.kseg0 * N2 + w.t.n0, (uint32_t)(w.klen * N2 - w.t.n0) * 2u);
+  o.rsb2 = o.rsb;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    o.aoff[j] = (uint32_t)(min(64 * j + lrow, w.t.rows - 1) * ld + lchunk * 8) * 2u;
-    o.boff[j] = (uint32_t)(min(64 * j + lrow, prows - 1) * ld + lchunk * 8) * 2u;
+    o.aoff[j] = mn_off(j, N1);
+    o.boff[j] = mn_off(j, N2);
   }
-  o.rsa = buffer_rsrc(pT + (size_t)w.t.m0 * ld + w.kseg0,
-                      (uint32_t)(w.t.rows * ld - w.kseg0) * 2u);
-  o.rsb = buffer_rsrc(qT + (size_t)w.t.n0 * ld + w.kseg0, (uint32_t)(prows * ld - w.kseg0) * 2u);
+  o.astep = (uint32_t)BK * N1 * 2u;
+  o.bstep = (uint32_t)BK * N2 * 2u;
+  o.bsplit = 1 << 30;
   return o;
 }
 
@@ -693,7 +784,7 @@ __device__ __forceinline__ void wg_tile(char* smem, const WTile& w, const TileLo
   const int prow0 = (wave >> 1) * 64;
   const int fr = lane & 31;
   f32x16 acc[WM][WN];
-  mainloop<HALF>(smem, ld, 0, w.nk, stage0, primed, nxt, has_next, 0, acc);
+  mainloop<HALF, true, true>(smem, ld, 0, w.nk, stage0, primed, nxt, has_next, 0, acc);
 #pragma unroll
   for (int mb = 0; mb < WM; ++mb) {
     const int r = arow0 + mb * 32 + fr;
@@ -715,7 +806,7 @@ __device__ __forceinline__ void wg_tile(char* smem, const WTile& w, const TileLo
 }
 
 __global__ __launch_bounds__(NTHR, 1) void wg_bf16_kernel(
-    const bf16_t* __restrict__ pT, const bf16_t* __restrict__ qT, int ld,
+    const bf16_t* __restrict__ P, const bf16_t* __restrict__ Q,
     const int32_t* __restrict__ offsets, int E, int N1, int N2, int NS, int m_cap,
     float* __restrict__ out_lo, float* __restrict__ out_hi) {
   __shared__ __attribute__((aligned(16))) char smem[2 * STAGE_BYTES];
@@ -740,7 +831,7 @@ __global__ __launch_bounds__(NTHR, 1) void wg_bf16_kernel(
   const int items = sc.nne * ((N1 + BM - 1) / BM) * ((N2 + BP - 1) / BP);
   if (vb >= items) return;
   WTile cur = wg_decode(sc, N1, N2, vb);
-  TileLoads ld_ = wg_loads(cur, pT, qT, ld, N2);
+  TileLoads ld_ = wg_loads(cur, P, Q, N1, N2);
   int stage0 = 0;
   bool primed = false;
   for (int w = vb; w < items; w += gridDim.x) {
@@ -749,7 +840,7 @@ __global__ __launch_bounds__(NTHR, 1) void wg_bf16_kernel(
     TileLoads nl = ld_;
     if (has_next) {
       nw = wg_decode(sc, N1, N2, w + gridDim.x);
-      nl = wg_loads(nw, pT, qT, ld, N2);
+      nl = wg_loads(nw, P, Q, N1, N2);
     }
     if (cur.t.rows > BM / 2)
       wg_tile<false>(smem, cur, ld_, N1, N2, NS, out_lo, out_hi, stage0, primed, nl, has_next);
@@ -775,13 +866,14 @@ struct Epi32 {
   int N;
 };
 
-template <int MODE>
+template <int MODE, bool P_MN>
 __global__ __launch_bounds__(256) void gg_f32_kernel(const float* __restrict__ A,
                                                      const int32_t* __restrict__ offsets,
                                                      const int32_t* __restrict__ tile_expert, int E,
                                                      int K, int m_tile, int m_cap,
                                                      const float* __restrict__ W1,
-                                                     const float* __restrict__ W3, Epi32 ep) {
+                                                     const float* __restrict__ W3, int ksplit,
+                                                     Epi32 ep) {
   constexpr bool FC1 = MODE == kFc1;
   const int N = ep.N;
   __shared__ float As[FM][FK + 1];
@@ -802,11 +894,20 @@ __global__ __launch_bounds__(256) void gg_f32_kernel(const float* __restrict__ A
       const int gm = min(m0 + r, mend - 1);
       As[r][c] = A[(size_t)gm * K + k0 + c];
     }
-    for (int i = tid; i < FN * FK; i += 256) {
-      const int r = i / FK, c = i % FK;
-      const int gn = min(n0 + r, N - 1);
-      B1[r][c] = W1[((size_t)e * N + gn) * K + k0 + c];
-      if (FC1) B3[r][c] = W3[((size_t)e * N + gn) * K + k0 + c];
+    if (P_MN) {   // W1 [E][ksplit][N] then W3 [E][K - ksplit][N], read along N
+      for (int i = tid; i < FN * FK; i += 256) {
+        const int c = i / FN, r = i % FN, k = k0 + c;
+        const int gn = min(n0 + r, N - 1);
+        B1[r][c] = k < ksplit ? W1[((size_t)e * ksplit + k) * N + gn]
+                              : W3[((size_t)e * (K - ksplit) + (k - ksplit)) * N + gn];
+      }
+    } else {
+      for (int i = tid; i < FN * FK; i += 256) {
+        const int r = i / FK, c = i % FK;
+        const int gn = min(n0 + r, N - 1);
+        B1[r][c] = W1[((size_t)e * N + gn) * K + k0 + c];
+        if (FC1) B3[r][c] = W3[((size_t)e * N + gn) * K + k0 + c];
+      }
     }
     __syncthreads();
     for (int kk = 0; kk < FK; ++kk) {
@@ -846,12 +947,11 @@ __global__ __launch_bounds__(256) void gg_f32_kernel(const float* __restrict__ A
 }
 
 // float32 k-grouped weight gradient: a 64 x 64 block of out[e] per workgroup, k-steps of
-// 16 segment rows staged in LDS; columns past the segment's end are masked, so segments
-// of any length work.
+// 16 segment rows staged in LDS; rows past the segment's end are masked.
 constexpr int WT = 64, WK = 16;
 
-__global__ __launch_bounds__(256) void wg_f32_kernel(const float* __restrict__ pT,
-                                                     const float* __restrict__ qT, int ld,
+__global__ __launch_bounds__(256) void wg_f32_kernel(const float* __restrict__ P,
+                                                     const float* __restrict__ Q,
                                                      const int32_t* __restrict__ offsets, int E,
                                                      int N1, int N2, int NS, int m_cap,
                                                      float* __restrict__ out_lo,
@@ -869,9 +969,9 @@ __global__ __launch_bounds__(256) void wg_f32_kernel(const float* __restrict__ p
   float acc[4][4] = {};
   for (int k0 = s0; k0 < s1; k0 += WK) {
     for (int x = tid; x < WT * WK; x += 256) {
-      const int r = x / WK, c = x % WK, k = k0 + c;
-      Ps[r][c] = (i0 + r < N1 && k < s1) ? pT[(size_t)(i0 + r) * ld + k] : 0.0f;
-      Qs[r][c] = (j0 + r < N2 && k < s1) ? qT[(size_t)(j0 + r) * ld + k] : 0.0f;
+      const int c = x / WT, r = x % WT, k = k0 + c;
+      Ps[r][c] = (i0 + r < N1 && k < s1) ? P[(size_t)k * N1 + i0 + r] : 0.0f;
+      Qs[r][c] = (j0 + r < N2 && k < s1) ? Q[(size_t)k * N2 + j0 + r] : 0.0f;
     }
     __syncthreads();
     for (int c = 0; c < WK; ++c)
@@ -900,13 +1000,14 @@ __global__ __launch_bounds__(256) void wg_f32_kernel(const float* __restrict__ p
 
 size_t grouped_workspace_bytes() { return (size_t)cu_count() * BM * BP * sizeof(float); }
 
-// One m-grouped GEMM (C = A W^T per segment) with the MODE epilogue. K: reduction width,
-// ep.N: output columns.
-static hipError_t launch_mgrouped(int dt, int mode, const void* A, const int32_t* offsets,
-                                  const int32_t* tile_expert, int E, int K, int m_tile,
-                                  int64_t m_cap, const void* W1, const void* W3, void* C, void* ab,
-                                  void* dh, int N, void* workspace, size_t ws_bytes,
-                                  hipStream_t s) {
+// One m-grouped GEMM per segment with the MODE epilogue: C = A W^T, W [E][N][K]
+// (p_mn false), or C = A W with W [E][K][N] split at ksplit between W1 and W3 (p_mn
+// true). K: reduction width, ep.N: output columns.
+static hipError_t launch_mgrouped(int dt, int mode, bool p_mn, const void* A,
+                                  const int32_t* offsets, const int32_t* tile_expert, int E, int K,
+                                  int m_tile, int64_t m_cap, const void* W1, const void* W3,
+                                  int ksplit, void* C, void* ab, void* dh, int N, void* workspace,
+                                  size_t ws_bytes, hipStream_t s) {
   if (dt == kF32) {
     const dim3 block(256);
     const dim3 grid((unsigned)((m_cap + FM - 1) / FM), (N + FN - 1) / FN);
@@ -914,15 +1015,19 @@ static hipError_t launch_mgrouped(int dt, int mode, const void* A, const int32_t
     const float* a = static_cast<const float*>(A);
     const float* w1 = static_cast<const float*>(W1);
     const float* w3 = static_cast<const float*>(W3);
+    const int mc = (int)m_cap;
     if (mode == kFc1)
-      hipLaunchKernelGGL(gg_f32_kernel<kFc1>, grid, block, 0, s, a, offsets, tile_expert, E, K,
-                         m_tile, (int)m_cap, w1, w3, ep);
+      hipLaunchKernelGGL((gg_f32_kernel<kFc1, false>), grid, block, 0, s, a, offsets, tile_expert,
+                         E, K, m_tile, mc, w1, w3, K, ep);
+    else if (mode == kFc2 && !p_mn)
+      hipLaunchKernelGGL((gg_f32_kernel<kFc2, false>), grid, block, 0, s, a, offsets, tile_expert,
+                         E, K, m_tile, mc, w1, w1, K, ep);
     else if (mode == kFc2)
-      hipLaunchKernelGGL(gg_f32_kernel<kFc2>, grid, block, 0, s, a, offsets, tile_expert, E, K,
-                         m_tile, (int)m_cap, w1, w1, ep);
+      hipLaunchKernelGGL((gg_f32_kernel<kFc2, true>), grid, block, 0, s, a, offsets, tile_expert,
+                         E, K, m_tile, mc, w1, w3, ksplit, ep);
     else
-      hipLaunchKernelGGL(gg_f32_kernel<kDgrad>, grid, block, 0, s, a, offsets, tile_expert, E, K,
-                         m_tile, (int)m_cap, w1, w1, ep);
+      hipLaunchKernelGGL((gg_f32_kernel<kDgrad, true>), grid, block, 0, s, a, offsets,
+                         tile_expert, E, K, m_tile, mc, w1, w1, ksplit, ep);
     return hipGetLastError();
   }
   const int G = cu_count();
@@ -934,24 +1039,29 @@ static hipError_t launch_mgrouped(int dt, int mode, const void* A, const int32_t
   const bf16_t* a = static_cast<const bf16_t*>(A);
   const bf16_t* w1 = static_cast<const bf16_t*>(W1);
   const bf16_t* w3 = static_cast<const bf16_t*>(W3);
+  const int mc = (int)m_cap;
   if (mode == kFc1) {
-    hipLaunchKernelGGL(gg_bf16_kernel<kFc1>, grid, block, 0, s, a, offsets, E, K, N, (int)m_cap,
-                       w1, w3, ep, ws, slots);
+    hipLaunchKernelGGL((gg_bf16_kernel<kFc1, false>), grid, block, 0, s, a, offsets, E, K, N, mc,
+                       w1, w3, K, ep, ws, slots);
     if (slots)
-      hipLaunchKernelGGL(gg_tail_reduce<kFc1>, rgrid, rblock, 0, s, offsets, E, K, (int)m_cap, G,
-                         slots, ws, ep);
+      hipLaunchKernelGGL(gg_tail_reduce<kFc1>, rgrid, rblock, 0, s, offsets, E, K, mc, G, slots,
+                         ws, ep);
   } else if (mode == kFc2) {
-    hipLaunchKernelGGL(gg_bf16_kernel<kFc2>, grid, block, 0, s, a, offsets, E, K, N, (int)m_cap,
-                       w1, w1, ep, ws, slots);
+    if (p_mn)
+      hipLaunchKernelGGL((gg_bf16_kernel<kFc2, true>), grid, block, 0, s, a, offsets, E, K, N, mc,
+                         w1, w3, ksplit, ep, ws, slots);
+    else
+      hipLaunchKernelGGL((gg_bf16_kernel<kFc2, false>), grid, block, 0, s, a, offsets, E, K, N,
+                         mc, w1, w1, K, ep, ws, slots);
     if (slots)
-      hipLaunchKernelGGL(gg_tail_reduce<kFc2>, rgrid, rblock, 0, s, offsets, E, K, (int)m_cap, G,
-                         slots, ws, ep);
+      hipLaunchKernelGGL(gg_tail_reduce<kFc2>, rgrid, rblock, 0, s, offsets, E, K, mc, G, slots,
+                         ws, ep);
   } else {
-    hipLaunchKernelGGL(gg_bf16_kernel<kDgrad>, grid, block, 0, s, a, offsets, E, K, N, (int)m_cap,
-                       w1, w1, ep, ws, slots);
+    hipLaunchKernelGGL((gg_bf16_kernel<kDgrad, true>), grid, block, 0, s, a, offsets, E, K, N, mc,
+                       w1, w1, K, ep, ws, slots);
     if (slots)
-      hipLaunchKernelGGL(gg_tail_reduce<kDgrad>, rgrid, rblock, 0, s, offsets, E, K, (int)m_cap, G,
-                         slots, ws, ep);
+      hipLaunchKernelGGL(gg_tail_reduce<kDgrad>, rgrid, rblock, 0, s, offsets, E, K, mc, G, slots,
+                         ws, ep);
   }
   return hipGetLastError();
 }
@@ -962,38 +1072,49 @@ hipError_t launch_grouped_swiglu(int dt, int phases, const void* x_perm, const i
                                  void* h, void* ab, void* y_perm, void* workspace, size_t ws_bytes,
                                  hipStream_t s) {
   if (phases & 1) {
-    const hipError_t e = launch_mgrouped(dt, kFc1, x_perm, offsets, tile_expert, E, D, m_tile,
-                                         m_cap, w1, w3, h, ab, nullptr, F, workspace, ws_bytes, s);
+    const hipError_t e = launch_mgrouped(dt, kFc1, false, x_perm, offsets, tile_expert, E, D,
+                                         m_tile, m_cap, w1, w3, D, h, ab, nullptr, F, workspace,
+                                         ws_bytes, s);
     if (e != hipSuccess) return e;
   }
   if (phases & 2)
-    return launch_mgrouped(dt, kFc2, h, offsets, tile_expert, E, F, m_tile, m_cap, w2, w2, y_perm,
-                           nullptr, nullptr, D, workspace, ws_bytes, s);
+    return launch_mgrouped(dt, kFc2, false, h, offsets, tile_expert, E, F, m_tile, m_cap, w2, w2, F,
+                           y_perm, nullptr, nullptr, D, workspace, ws_bytes, s);
   return hipSuccess;
 }
 
 hipError_t launch_grouped_dgrad_swiglu(int dt, const void* dy_perm, const int32_t* offsets,
                                        const int32_t* tile_expert, int E, int D, int F,
-                                       int m_tile, int64_t m_cap, const void* w2t, const void* ab,
+                                       int m_tile, int64_t m_cap, const void* w2, const void* ab,
                                        void* dab, void* dh, void* workspace, size_t ws_bytes,
                                        hipStream_t s) {
-  return launch_mgrouped(dt, kDgrad, dy_perm, offsets, tile_expert, E, D, m_tile, m_cap, w2t, w2t,
-                         dab, const_cast<void*>(ab), dh, F, workspace, ws_bytes, s);
+  // dh = dY w2[e]: w2 [E][D][F] is the [K = D][N = F] operand, read MN-major
+  return launch_mgrouped(dt, kDgrad, true, dy_perm, offsets, tile_expert, E, D, m_tile, m_cap, w2,
+                         w2, D, dab, const_cast<void*>(ab), dh, F, workspace, ws_bytes, s);
 }
 
-hipError_t launch_grouped_wgrad(int dt, const void* pT, const void* qT, int64_t ld,
-                                const int32_t* offsets, int E, int N1, int N2, int NS,
-                                int64_t m_cap, float* out_lo, float* out_hi, hipStream_t s) {
+hipError_t launch_grouped_dgrad_fc1(int dt, const void* dab, const int32_t* offsets,
+                                    const int32_t* tile_expert, int E, int D, int F, int m_tile,
+                                    int64_t m_cap, const void* w1, const void* w3, void* dx_perm,
+                                    void* workspace, size_t ws_bytes, hipStream_t s) {
+  // dX = [da | db] [w1[e] ; w3[e]]: K = 2F, k < F from w1 [E][F][D], the rest from w3
+  return launch_mgrouped(dt, kFc2, true, dab, offsets, tile_expert, E, 2 * F, m_tile, m_cap, w1,
+                         w3, F, dx_perm, nullptr, nullptr, D, workspace, ws_bytes, s);
+}
+
+hipError_t launch_grouped_wgrad(int dt, const void* P, const void* Q, const int32_t* offsets,
+                                int E, int N1, int N2, int NS, int64_t m_cap, float* out_lo,
+                                float* out_hi, hipStream_t s) {
   if (dt == kF32) {
     const dim3 grid(((N1 + WT - 1) / WT) * ((N2 + WT - 1) / WT), E), block(256);
-    hipLaunchKernelGGL(wg_f32_kernel, grid, block, 0, s, static_cast<const float*>(pT),
-                       static_cast<const float*>(qT), (int)ld, offsets, E, N1, N2, NS, (int)m_cap,
-                       out_lo, out_hi);
+    hipLaunchKernelGGL(wg_f32_kernel, grid, block, 0, s, static_cast<const float*>(P),
+                       static_cast<const float*>(Q), offsets, E, N1, N2, NS, (int)m_cap, out_lo,
+                       out_hi);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(wg_bf16_kernel, dim3(cu_count()), dim3(NTHR), 0, s,
-                     static_cast<const bf16_t*>(pT), static_cast<const bf16_t*>(qT), (int)ld,
-                     offsets, E, N1, N2, NS, (int)m_cap, out_lo, out_hi);
+                     static_cast<const bf16_t*>(P), static_cast<const bf16_t*>(Q), offsets, E, N1,
+                     N2, NS, (int)m_cap, out_lo, out_hi);
   return hipGetLastError();
 }
 

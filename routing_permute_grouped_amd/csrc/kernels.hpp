@@ -38,17 +38,24 @@ hipError_t launch_grouped_swiglu(int dt, int phases, const void* x_perm, const i
                                  void* h, void* ab, void* y_perm, void* workspace, size_t ws_bytes,
                                  hipStream_t s);
 
-// dh = dy_perm w2t[e]^T (w2t [E,F,D]), then [da | db] from ab -> dab; dh stored if non-null
+// dh = dy_perm w2[e] (w2 [E,D,F]), then [da | db] from ab -> dab; dh stored if non-null
 hipError_t launch_grouped_dgrad_swiglu(int dt, const void* dy_perm, const int32_t* offsets,
                                        const int32_t* tile_expert, int E, int D, int F,
-                                       int m_tile, int64_t m_cap, const void* w2t, const void* ab,
+                                       int m_tile, int64_t m_cap, const void* w2, const void* ab,
                                        void* dab, void* dh, void* workspace, size_t ws_bytes,
                                        hipStream_t s);
 
-// out[e] = pT[:, seg e] qT[:, seg e]^T, rows < NS to out_lo, the rest to out_hi (float32)
-hipError_t launch_grouped_wgrad(int dt, const void* pT, const void* qT, int64_t ld,
-                                const int32_t* offsets, int E, int N1, int N2, int NS,
-                                int64_t m_cap, float* out_lo, float* out_hi, hipStream_t s);
+// dx_perm = da w1[e] + db w3[e] with dab = [da | db] [m_cap, 2F], w1, w3 [E,F,D]
+hipError_t launch_grouped_dgrad_fc1(int dt, const void* dab, const int32_t* offsets,
+                                    const int32_t* tile_expert, int E, int D, int F, int m_tile,
+                                    int64_t m_cap, const void* w1, const void* w3, void* dx_perm,
+                                    void* workspace, size_t ws_bytes, hipStream_t s);
+
+// out[e] = P[seg e]^T Q[seg e] (P [rows, N1], Q [rows, N2]), rows < NS of it to out_lo,
+// the rest to out_hi (float32)
+hipError_t launch_grouped_wgrad(int dt, const void* P, const void* Q, const int32_t* offsets,
+                                int E, int N1, int N2, int NS, int64_t m_cap, float* out_lo,
+                                float* out_hi, hipStream_t s);
 
 // dy_perm rows [0, min(offsets[E], m_cap)): topk_w[s] * dout[s / k] for the row of slot s,
 // zero for pad rows; dtopk_w[s] = <dout[t], y_perm[row of s]>, 0 for slots without a row
@@ -57,12 +64,6 @@ hipError_t launch_combine_backward(int dt, const void* dout, const void* y_perm,
                                    const int32_t* dst_row, const float* topk_w, int T, int D, int E,
                                    int k, int64_t m_cap, void* dy_perm, float* dtopk_w,
                                    hipStream_t s);
-
-// dst[b][c][col0 + r] = src[b][r][c] for r < rows, 0 for rows <= r < roundup(rows, 64)
-// (capped at R); rows = min(rows_src, *nrows_dev) when nrows_dev is set
-hipError_t launch_transpose(int dt, const void* src, int batch, int R, int C, int rows_src,
-                            const int32_t* nrows_dev, void* dst, int64_t ld_dst, int64_t col0,
-                            hipStream_t s);
 
 hipError_t launch_combine(int dt, const void* y_perm, const int32_t* dst_row, const float* topk_w,
                           const void* shared, int T, int D, int k, int64_t m_cap, void* out,

@@ -32,7 +32,6 @@ constexpr int kMaxExpertsRoute = 64;
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxK = 32;
 constexpr int kMaxDim = 1 << 16;
-constexpr int64_t kMaxLd = 1 << 22;   // rows of the transposed operands of the backward
 
 bool aligned16(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
@@ -154,53 +153,63 @@ moe_status_t moe_grouped_fc2(moe_dtype_t dt, const void* h, const int32_t* offse
                  w2, const_cast<void*>(h), nullptr, y_perm, workspace, ws_bytes, stream);
 }
 
-moe_status_t moe_grouped_dgrad_swiglu(moe_dtype_t dt, const void* dy_perm, const int32_t* offsets,
-                                      const int32_t* tile_expert, int E, int D, int F, int m_tile,
-                                      int64_t m_cap, const void* w2t, const void* ab, void* dab,
-                                      void* dh, void* workspace, size_t ws_bytes, void* stream) {
-  if (!dtype_ok(dt) || !aligned4(offsets) || !aligned4(tile_expert) || !aligned16(dy_perm) ||
-      !aligned16(w2t) || !aligned16(ab) || !aligned16(dab) || (dh && !aligned16(dh)))
+static moe_status_t dgrad_common(moe_dtype_t dt, const void* a, const int32_t* offsets,
+                                 const int32_t* tile_expert, int E, int D, int F, int m_tile,
+                                 int64_t m_cap, void* workspace) {
+  if (!dtype_ok(dt) || !aligned4(offsets) || !aligned4(tile_expert) || !aligned16(a))
     return MOE_EINVAL;
   if (workspace && !aligned16(workspace)) return MOE_EINVAL;
-  if (!workspace) ws_bytes = 0;
   if (E < 1 || E > kMaxExperts || !dim_ok(D) || !dim_ok(F) || !mtile_ok(m_tile)) return MOE_ESHAPE;
   if ((int64_t)D * F >= ((int64_t)1 << 31)) return MOE_ESHAPE;
   if (m_cap < 1 || m_cap % m_tile != 0 || m_cap > INT32_MAX) return MOE_ECAPACITY;
   if (dt == MOE_BF16 && m_tile != 128 && m_tile != 256) return MOE_EUNSUPPORTED;
+  return MOE_OK;
+}
+
+moe_status_t moe_grouped_dgrad_swiglu(moe_dtype_t dt, const void* dy_perm, const int32_t* offsets,
+                                      const int32_t* tile_expert, int E, int D, int F, int m_tile,
+                                      int64_t m_cap, const void* w2, const void* ab, void* dab,
+                                      void* dh, void* workspace, size_t ws_bytes, void* stream) {
+  if (!aligned16(w2) || !aligned16(ab) || !aligned16(dab) || (dh && !aligned16(dh)))
+    return MOE_EINVAL;
+  const moe_status_t st = dgrad_common(dt, dy_perm, offsets, tile_expert, E, D, F, m_tile, m_cap,
+                                       workspace);
+  if (st != MOE_OK) return st;
+  if (!workspace) ws_bytes = 0;
   return hip_status(moe::launch_grouped_dgrad_swiglu(dt, dy_perm, offsets, tile_expert, E, D, F,
-                                                     m_tile, m_cap, w2t, ab, dab, dh,
+                                                     m_tile, m_cap, w2, ab, dab, dh,
                                                      ws_bytes ? workspace : nullptr, ws_bytes,
                                                      static_cast<hipStream_t>(stream)));
 }
 
-moe_status_t moe_grouped_wgrad(moe_dtype_t dt, const void* pT, const void* qT, int64_t ld,
+moe_status_t moe_grouped_dgrad_fc1(moe_dtype_t dt, const void* dab, const int32_t* offsets,
+                                   const int32_t* tile_expert, int E, int D, int F, int m_tile,
+                                   int64_t m_cap, const void* w1, const void* w3, void* dx_perm,
+                                   void* workspace, size_t ws_bytes, void* stream) {
+  if (!aligned16(w1) || !aligned16(w3) || !aligned16(dx_perm)) return MOE_EINVAL;
+  const moe_status_t st = dgrad_common(dt, dab, offsets, tile_expert, E, D, F, m_tile, m_cap,
+                                       workspace);
+  if (st != MOE_OK) return st;
+  if (!workspace) ws_bytes = 0;
+  return hip_status(moe::launch_grouped_dgrad_fc1(dt, dab, offsets, tile_expert, E, D, F, m_tile,
+                                                  m_cap, w1, w3, dx_perm,
+                                                  ws_bytes ? workspace : nullptr, ws_bytes,
+                                                  static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_grouped_wgrad(moe_dtype_t dt, const void* P, const void* Q,
                                const int32_t* offsets, int E, int N1, int N2, int NS, int m_tile,
                                int64_t m_cap, float* out_lo, float* out_hi, void* stream) {
-  if (!dtype_ok(dt) || !aligned16(pT) || !aligned16(qT) || !aligned4(offsets)) return MOE_EINVAL;
+  if (!dtype_ok(dt) || !aligned16(P) || !aligned16(Q) || !aligned4(offsets)) return MOE_EINVAL;
   if (NS < 0 || NS > N1) return MOE_ESHAPE;
   if ((NS > 0 && !aligned16(out_lo)) || (NS < N1 && !aligned16(out_hi))) return MOE_EINVAL;
   if (E < 1 || E > kMaxExperts || !dim_ok(N1) || !dim_ok(N2) || !mtile_ok(m_tile))
     return MOE_ESHAPE;
-  if (m_cap < 1 || m_cap % m_tile != 0) return MOE_ECAPACITY;
-  // every k-step of 64 columns stays inside a row of ld columns; 256 rows of ld bf16 values
-  // stay under 2^32 bytes
-  if (ld % 8 != 0 || ld < (m_cap + 63) / 64 * 64 || ld > kMaxLd) return MOE_ESHAPE;
-  if (dt == MOE_BF16 && m_tile % 64 != 0) return MOE_EUNSUPPORTED;
-  return hip_status(moe::launch_grouped_wgrad(dt, pT, qT, ld, offsets, E, N1, N2, NS, m_cap,
-                                              out_lo, out_hi, static_cast<hipStream_t>(stream)));
-}
-
-moe_status_t moe_transpose(moe_dtype_t dt, const void* src, int batch, int R, int C, int rows,
-                           const int32_t* nrows_dev, void* dst, int64_t ld_dst, int64_t col0,
-                           void* stream) {
-  if (!dtype_ok(dt) || !aligned16(src) || !aligned16(dst) || (nrows_dev && !aligned4(nrows_dev)))
-    return MOE_EINVAL;
-  if (batch < 1 || batch > 65535 || R < 64 || R % 64 != 0 || R > kMaxLd || !dim_ok(C) ||
-      rows < 0 || rows > R)
-    return MOE_ESHAPE;
-  if (col0 < 0 || col0 % 8 != 0 || ld_dst % 8 != 0 || ld_dst < col0 + R) return MOE_ESHAPE;
-  return hip_status(moe::launch_transpose(dt, src, batch, R, C, rows, nrows_dev, dst, ld_dst, col0,
-                                          static_cast<hipStream_t>(stream)));
+  if (m_cap < 1 || m_cap % m_tile != 0 || m_cap > INT32_MAX) return MOE_ECAPACITY;
+  // a segment's rows of one operand are addressed with 32-bit byte offsets
+  if ((m_cap + 64) * (int64_t)(N1 > N2 ? N1 : N2) >= ((int64_t)1 << 31)) return MOE_ESHAPE;
+  return hip_status(moe::launch_grouped_wgrad(dt, P, Q, offsets, E, N1, N2, NS, m_cap, out_lo,
+                                              out_hi, static_cast<hipStream_t>(stream)));
 }
 
 moe_status_t moe_combine(moe_dtype_t dt, const void* y_perm, const int32_t* dst_row,

@@ -98,40 +98,16 @@ def moe_layer(x: torch.Tensor, w1: torch.Tensor, w3: torch.Tensor, w2: torch.Ten
     return res
 
 
-def _round64(n: int) -> int:
-    return -(-n // 64) * 64
-
-
-def transposed_weights(w1: torch.Tensor, w3: torch.Tensor, w2: torch.Tensor):
-    """The weights as the backward GEMMs read them: w2t [E,F,D] (w2[e]^T) and
-    w13t [E,D,2F] = [w1[e]^T | w3[e]^T]."""
-    E, F, D = w1.shape
-    w2t = B.moe_transpose(w2)
-    w13t = torch.empty((E, D, 2 * F), dtype=w1.dtype, device=w1.device)
-    B.moe_transpose(w1, dst=w13t, ld=2 * F, col0=0)
-    B.moe_transpose(w3, dst=w13t, ld=2 * F, col0=F)
-    return w2t, w13t
-
-
-def _experts_backward(dy, x_rows, ab, h, offsets, tile_expert, w1, w3, w2, m_tile, m_cap,
-                      rows_valid, nrows_dev, ws):
+def _experts_backward(dy, x_rows, ab, h, offsets, tile_expert, w1, w3, w2, m_tile, m_cap, ws):
     """dgrad and wgrad of one grouped SwiGLU FFN over rows [0, m_cap) (section 5 of
     "Expert Parallelism (EP)": the m-grouped fc mirrors into an m-grouped dgrad and a
     k-grouped wgrad). Returns (dab, dX, dw1, dw3, dw2)."""
-    E, F, D = w1.shape
-    w2t, w13t = transposed_weights(w1, w3, w2)
-    dab = B.moe_grouped_dgrad_swiglu(dy, offsets, tile_expert, w2t, ab, m_tile, m_cap,
+    F, D = w1.shape[1], w1.shape[2]
+    dab = B.moe_grouped_dgrad_swiglu(dy, offsets, tile_expert, w2, ab, m_tile, m_cap,
                                      workspace=ws)
-    dX = torch.empty((m_cap, D), dtype=dy.dtype, device=dy.device)
-    B.moe_grouped_fc2(dab, offsets, tile_expert, w13t, m_tile, m_cap, dX, workspace=ws)
-    ld = _round64(m_cap)
-    T = dict(rows=rows_valid, nrows_dev=nrows_dev, R=ld)
-    dabT = B.moe_transpose(dab, **T)
-    xT = B.moe_transpose(x_rows, **T)
-    dyT = B.moe_transpose(dy, **T)
-    hT = B.moe_transpose(h, **T)
-    dw1, dw3 = B.moe_grouped_wgrad(dabT, xT, offsets, m_tile, m_cap, NS=F)
-    dw2, _ = B.moe_grouped_wgrad(dyT, hT, offsets, m_tile, m_cap, NS=D)
+    dX = B.moe_grouped_dgrad_fc1(dab, offsets, tile_expert, w1, w3, m_tile, m_cap, workspace=ws)
+    dw1, dw3 = B.moe_grouped_wgrad(dab, x_rows, offsets, m_tile, m_cap, NS=F)
+    dw2, _ = B.moe_grouped_wgrad(dy, h, offsets, m_tile, m_cap, NS=D)
     return dab, dX, dw1, dw3, dw2
 
 
@@ -147,14 +123,13 @@ def moe_layer_backward(fwd: dict, dout: torch.Tensor, x: torch.Tensor, w1: torch
     [1,S*Fs,D] and ``dws2`` [1,D,S*Fs], the concatenated layout of SharedExperts)."""
     m_cap = fwd["m_cap"]
     offs, te = fwd["offsets"], fwd["tile_expert"]
-    E = w1.shape[0]
     ws = B.grouped_workspace(x.device) if split_k else None
     res = {}
     dy, dtw = B.moe_combine_backward(dout, fwd["y_perm"], fwd["src_row"], offs, fwd["dst_row"],
                                      fwd["topk_w"], m_cap=m_cap)
     res["dy_perm"], res["dtopk_w"] = dy, dtw
     dab, dX, dw1, dw3, dw2 = _experts_backward(dy, fwd["x_perm"], fwd["ab"], fwd["h"], offs, te,
-                                               w1, w3, w2, m_tile, m_cap, m_cap, offs[E:], ws)
+                                               w1, w3, w2, m_tile, m_cap, ws)
     res.update(dab=dab, dx_perm=dX, dw1=dw1, dw3=dw3, dw2=dw2)
     dxs = None
     if shared is not None:
@@ -162,7 +137,7 @@ def moe_layer_backward(fwd: dict, dout: torch.Tensor, x: torch.Tensor, w1: torch
         rows = DenseRows(T, m_tile, x.device)
         _, dXs, dws1, dws3, dws2 = _experts_backward(
             dout, x, fwd["shared_ab"], fwd["shared_h"], rows.offsets, rows.tile_expert,
-            shared.w1, shared.w3, shared.w2, m_tile, rows.m_cap, T, None, ws)
+            shared.w1, shared.w3, shared.w2, m_tile, rows.m_cap, ws)
         dxs = dXs[:T]
         res.update(dx_shared=dxs, dws1=dws1, dws3=dws3, dws2=dws2)
     res["dx"] = B.moe_combine(dX, fwd["dst_row"], None, shared=dxs, m_cap=m_cap)

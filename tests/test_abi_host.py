@@ -26,8 +26,8 @@ def test_header_declares_the_calls_and_helpers():
     assert declared_symbols() == sorted(["moe_route", "moe_permute", "moe_grouped_swiglu",
                                          "moe_grouped_fc1_swiglu", "moe_grouped_fc2",
                                          "moe_combine", "moe_combine_backward",
-                                         "moe_grouped_dgrad_swiglu", "moe_grouped_wgrad",
-                                         "moe_transpose", "moe_capacity",
+                                         "moe_grouped_dgrad_swiglu", "moe_grouped_dgrad_fc1",
+                                         "moe_grouped_wgrad", "moe_capacity",
                                          "moe_grouped_workspace_bytes",
                                          "moe_permute_workspace_bytes", "moe_status_str"])
 
@@ -169,36 +169,52 @@ def test_combine_backward_validation(kw, code):
     assert combine_bwd(**kw) == code
 
 
-def dgrad(dt=1, dy=FAKE, E=8, D=128, F=256, mt=128, m_cap=1024, w2t=FAKE, ab=FAKE, dab=FAKE,
+def dgrad(dt=1, dy=FAKE, E=8, D=128, F=256, mt=128, m_cap=1024, w2=FAKE, ab=FAKE, dab=FAKE,
           dh=None, ws=None, ws_bytes=0):
-    return lib.moe_grouped_dgrad_swiglu(dt, dy, FAKE, FAKE, E, D, F, mt, m_cap, w2t, ab, dab, dh,
+    return lib.moe_grouped_dgrad_swiglu(dt, dy, FAKE, FAKE, E, D, F, mt, m_cap, w2, ab, dab, dh,
                                         ws, ws_bytes, None)
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(dt=9), MOE_EINVAL), (dict(dy=None), MOE_EINVAL), (dict(w2t=FAKE + 2), MOE_EINVAL),
+    (dict(dt=9), MOE_EINVAL), (dict(dy=None), MOE_EINVAL), (dict(w2=FAKE + 2), MOE_EINVAL),
     (dict(ab=None), MOE_EINVAL), (dict(dab=None), MOE_EINVAL), (dict(dh=FAKE + 8), MOE_EINVAL),
     (dict(ws=FAKE + 4, ws_bytes=1 << 20), MOE_EINVAL), (dict(E=0), MOE_ESHAPE),
-    (dict(F=200), MOE_ESHAPE), (dict(D=65536, F=32768), MOE_ESHAPE), (dict(m_cap=1000),
-                                                                        MOE_ECAPACITY),
-    (dict(mt=64), MOE_EUNSUPPORTED),
+    (dict(F=200), MOE_ESHAPE), (dict(D=65536, F=32768), MOE_ESHAPE),
+    (dict(m_cap=1000), MOE_ECAPACITY), (dict(mt=64), MOE_EUNSUPPORTED),
 ])
 def test_dgrad_validation(kw, code):
     assert dgrad(**kw) == code
 
 
-def wgrad(dt=1, pT=FAKE, qT=FAKE, ld=1024, off=FAKE, E=8, N1=512, N2=128, NS=256, mt=128,
-          m_cap=1024, lo=FAKE, hi=FAKE):
-    return lib.moe_grouped_wgrad(dt, pT, qT, ld, off, E, N1, N2, NS, mt, m_cap, lo, hi, None)
+def dgrad_fc1(dt=1, dab=FAKE, E=8, D=128, F=256, mt=128, m_cap=1024, w1=FAKE, w3=FAKE, dx=FAKE,
+              ws=None, ws_bytes=0):
+    return lib.moe_grouped_dgrad_fc1(dt, dab, FAKE, FAKE, E, D, F, mt, m_cap, w1, w3, dx, ws,
+                                     ws_bytes, None)
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(dt=4), MOE_EINVAL), (dict(pT=None), MOE_EINVAL), (dict(qT=FAKE + 2), MOE_EINVAL),
+    (dict(dt=2), MOE_EINVAL), (dict(dab=None), MOE_EINVAL), (dict(w1=None), MOE_EINVAL),
+    (dict(w3=FAKE + 2), MOE_EINVAL), (dict(dx=FAKE + 4), MOE_EINVAL),
+    (dict(ws=FAKE + 8, ws_bytes=1 << 20), MOE_EINVAL), (dict(E=1025), MOE_ESHAPE),
+    (dict(D=100), MOE_ESHAPE), (dict(mt=100), MOE_ESHAPE), (dict(m_cap=0), MOE_ECAPACITY),
+    (dict(mt=32, m_cap=1024), MOE_EUNSUPPORTED),
+])
+def test_dgrad_fc1_validation(kw, code):
+    assert dgrad_fc1(**kw) == code
+
+
+def wgrad(dt=1, P=FAKE, Q=FAKE, off=FAKE, E=8, N1=512, N2=128, NS=256, mt=128, m_cap=1024,
+          lo=FAKE, hi=FAKE):
+    return lib.moe_grouped_wgrad(dt, P, Q, off, E, N1, N2, NS, mt, m_cap, lo, hi, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=4), MOE_EINVAL), (dict(P=None), MOE_EINVAL), (dict(Q=FAKE + 2), MOE_EINVAL),
     (dict(off=None), MOE_EINVAL), (dict(lo=None), MOE_EINVAL), (dict(hi=FAKE + 4), MOE_EINVAL),
     (dict(NS=-1), MOE_ESHAPE), (dict(NS=513), MOE_ESHAPE), (dict(N1=500), MOE_ESHAPE),
     (dict(N2=0), MOE_ESHAPE), (dict(E=0), MOE_ESHAPE), (dict(mt=48), MOE_ESHAPE),
-    (dict(m_cap=1000), MOE_ECAPACITY), (dict(ld=1020), MOE_ESHAPE), (dict(ld=1000), MOE_ESHAPE),
-    (dict(ld=(1 << 22) + 8, m_cap=1024), MOE_ESHAPE), (dict(mt=32, m_cap=1024), MOE_EUNSUPPORTED),
+    (dict(m_cap=1000), MOE_ECAPACITY), (dict(m_cap=0), MOE_ECAPACITY),
+    (dict(N1=65536, NS=0, m_cap=1 << 15), MOE_ESHAPE),
 ])
 def test_wgrad_validation(kw, code):
     assert wgrad(**kw) == code
@@ -210,21 +226,6 @@ def test_wgrad_needs_only_the_output_halves_it_writes():
     assert wgrad(NS=512, hi=None, N2=100) == MOE_ESHAPE
     assert wgrad(NS=0, lo=None, N2=100) == MOE_ESHAPE
     assert wgrad(NS=256, hi=None) == MOE_EINVAL
-
-
-def transpose(dt=1, src=FAKE, B=1, R=256, C=128, rows=256, nrows=None, dst=FAKE, ld=256, col0=0):
-    return lib.moe_transpose(dt, src, B, R, C, rows, nrows, dst, ld, col0, None)
-
-
-@pytest.mark.parametrize("kw,code", [
-    (dict(dt=3), MOE_EINVAL), (dict(src=None), MOE_EINVAL), (dict(dst=FAKE + 4), MOE_EINVAL),
-    (dict(nrows=FAKE + 2), MOE_EINVAL), (dict(B=0), MOE_ESHAPE), (dict(R=200), MOE_ESHAPE),
-    (dict(R=0, rows=0), MOE_ESHAPE), (dict(C=100), MOE_ESHAPE), (dict(rows=257), MOE_ESHAPE),
-    (dict(rows=-1), MOE_ESHAPE), (dict(col0=4, ld=512), MOE_ESHAPE), (dict(ld=252), MOE_ESHAPE),
-    (dict(col0=8, ld=256), MOE_ESHAPE), (dict(ld=260), MOE_ESHAPE),
-])
-def test_transpose_validation(kw, code):
-    assert transpose(**kw) == code
 
 
 def test_binding_raises_on_rejected_call():

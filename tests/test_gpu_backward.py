@@ -5,7 +5,7 @@ kernel leaves unwritten fails the test), then the whole chain, moe_layer(...,
 save_for_backward=True) followed by moe_layer_backward, against oracle.backward on the
 same seeded inputs and output gradient.
 
-Bar: data movement (transposes) bit-exact; dy_perm, dab, dx_perm, dx, dx_shared, the
+Bar: dy_perm, dab, dx_perm, dx, dx_shared, the
 top-k weight gradients and the float32 weight gradients within max|gpu - ref| / max|ref|
 <= 1e-5 (float32 layers) or 2e-2 (bf16 layers, float32 accumulation); pad rows of
 dy_perm, dab and dx_perm exactly zero; experts without rows get exactly zero weight
@@ -21,51 +21,6 @@ from oracle import moe_oracle as orc
 from tests import _parity as P
 
 pytestmark = pytest.mark.gpu
-
-
-def _bits_equal(a: torch.Tensor, b: np.ndarray) -> bool:
-    return np.array_equal(P.to_host(a).view(np.uint8), np.ascontiguousarray(b).view(np.uint8))
-
-
-# ---------------------------------------------------------------------------
-# moe_transpose
-# ---------------------------------------------------------------------------
-
-@pytest.mark.parametrize("dt", ["bf16", "f32"])
-def test_transpose_batched_with_offset_columns(dt):
-    P.log(f"[bwd] transpose batched {dt}")
-    rng = np.random.default_rng(5)
-    src = rng.standard_normal((3, 128, 192)).astype(np.float32)
-    if dt == "bf16":
-        src = W.f32_to_bf16_bits(src)
-    s = P.to_dev(src)
-    dst = P.poison(torch.empty((3, 192, 2 * 128 + 16), dtype=s.dtype, device="cuda"))
-    rpg.moe_transpose(s, dst=dst, ld=2 * 128 + 16, col0=136)
-    torch.cuda.synchronize()
-    got = P.to_host(dst)
-    assert np.array_equal(got[:, :, 136:264].view(np.uint8),
-                          np.ascontiguousarray(src.transpose(0, 2, 1)).view(np.uint8))
-    assert np.all(np.isnan(W.as_f32(got[:, :, :136], dt)))   # other columns untouched
-    assert np.all(np.isnan(W.as_f32(got[:, :, 264:], dt)))
-
-
-@pytest.mark.parametrize("rows,nrows", [(300, None), (300, 130), (300, 0), (256, 4000)])
-def test_transpose_rows_and_zero_tail(rows, nrows):
-    P.log(f"[bwd] transpose rows={rows} nrows={nrows}")
-    rng = np.random.default_rng(6)
-    src = W.f32_to_bf16_bits(rng.standard_normal((rows, 128)).astype(np.float32))
-    s = P.to_dev(src)
-    R = 384
-    nd = None if nrows is None else torch.tensor([nrows], dtype=torch.int32, device="cuda")
-    dst = P.poison(torch.empty((128, R), dtype=s.dtype, device="cuda"))
-    rpg.moe_transpose(s, rows=rows, nrows_dev=nd, R=R, dst=dst, ld=R)
-    torch.cuda.synchronize()
-    got = P.to_host(dst)
-    n = rows if nrows is None else min(rows, nrows)
-    z = min(R, -(-n // 64) * 64)
-    assert np.array_equal(got[:, :n], src[:n].T)
-    assert np.all(got[:, n:z] == 0)
-    assert np.all(np.isnan(W.as_f32(got[:, z:], "bf16")))
 
 
 # ---------------------------------------------------------------------------
@@ -122,7 +77,6 @@ def test_dgrad_swiglu_against_oracle(dt, split):
     f = ref["fwd"]
     store = (lambda a: a.astype(np.float32)) if dt == "f32" else \
         (lambda a: W.f32_to_bf16_bits(a.astype(np.float32)))
-    w2t = np.ascontiguousarray(inp["w2"].transpose(0, 2, 1))
     M, F = f["m_cap"], cfg.F
     tdt = torch.float32 if dt == "f32" else torch.bfloat16
     dab = P.poison(torch.empty((M, 2 * F), dtype=tdt, device="cuda"))
@@ -131,7 +85,7 @@ def test_dgrad_swiglu_against_oracle(dt, split):
                               device="cuda")) if split else None
     rpg.moe_grouped_dgrad_swiglu(P.to_dev(store(ref["dy_perm"])),
                                  P.to_dev(f["offsets"].astype(np.int32)),
-                                 P.to_dev(f["tile_expert"].astype(np.int32)), P.to_dev(w2t),
+                                 P.to_dev(f["tile_expert"].astype(np.int32)), P.to_dev(inp["w2"]),
                                  P.to_dev(store(ref["ab"])), cfg.m_tile, M, dab=dab, dh=dh,
                                  workspace=ws)
     torch.cuda.synchronize()
@@ -145,35 +99,67 @@ def test_dgrad_swiglu_against_oracle(dt, split):
 
 
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
-def test_wgrad_is_the_per_expert_contraction(dt):
-    """k-grouped GEMM against its definition on the oracle's layout, with an empty expert,
-    a split row NS inside a 256-row tile and N1, N2 not multiples of 256."""
-    P.log(f"[bwd] wgrad {dt}")
+@pytest.mark.parametrize("split", [True, False])
+def test_dgrad_fc1_against_oracle(dt, split):
+    P.log(f"[bwd] dgrad_fc1 {dt} split={split}")
+    cfg, inp, dout = _small(dt)
+    ref = orc.backward(inp, dout, cfg.k, cfg.m_tile, dt)
+    f = ref["fwd"]
+    store = (lambda a: a.astype(np.float32)) if dt == "f32" else \
+        (lambda a: W.f32_to_bf16_bits(a.astype(np.float32)))
+    M = f["m_cap"]
+    tdt = torch.float32 if dt == "f32" else torch.bfloat16
+    dx = P.poison(torch.empty((M, cfg.D), dtype=tdt, device="cuda"))
+    ws = P.poison(torch.empty(rpg.moe_grouped_workspace_bytes() // 4, dtype=torch.float32,
+                              device="cuda")) if split else None
+    rpg.moe_grouped_dgrad_fc1(P.to_dev(store(ref["dab"])), P.to_dev(f["offsets"].astype(np.int32)),
+                              P.to_dev(f["tile_expert"].astype(np.int32)), P.to_dev(inp["w1"]),
+                              P.to_dev(inp["w3"]), cfg.m_tile, M, dx_perm=dx, workspace=ws)
+    torch.cuda.synchronize()
+    used = int(f["offsets"][-1])
+    g = P.to_host(dx)[:used]
+    assert np.all(np.isfinite(orc.values64(g)))
+    e = P.rel_err(g, ref["dx_perm"][:used])
+    assert e <= P.TOL[dt], e
+    assert np.all(orc.values64(g)[f["src_row"][:used] < 0] == 0)
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("mt,ragged", [(128, False), (16, False), (128, True)])
+def test_wgrad_is_the_per_expert_contraction(dt, mt, ragged):
+    """k-grouped GEMM against its definition: an empty expert, a split row NS inside a
+    256-row tile, N1 and N2 not multiples of 256, segments of m_tile multiples (and with
+    ``ragged`` a last segment ending mid k-step, with NaN rows behind it that must not be
+    read)."""
+    P.log(f"[bwd] wgrad {dt} mt={mt} ragged={ragged}")
     rng = np.random.default_rng(9)
-    E, mt = 5, 128 if dt == "bf16" else 16
+    E = 5
     idx = rng.integers(0, E - 1, size=(300, 2)).astype(np.int32)   # expert E-1 gets no rows
     lay = orc.dispatch_layout(idx, E, mt)
     M = lay["m_cap"]
-    ld = -(-M // 64) * 64
+    offs = lay["offsets"].copy()
+    if ragged:
+        offs[E - 1] -= 37     # the last non-empty segment ends 37 rows early
+        offs[E] = offs[E - 1]
     N1, N2, NS = 320, 192, 192
-    P_ = rng.standard_normal((N1, ld)).astype(np.float32)
-    Q_ = rng.standard_normal((N2, ld)).astype(np.float32)
-    used = int(lay["offsets"][-1])
-    P_[:, used:] = 0.0
-    Q_[:, used:] = 0.0
+    P_ = rng.standard_normal((M, N1)).astype(np.float32)
+    Q_ = rng.standard_normal((M, N2)).astype(np.float32)
+    used = int(offs[E])
+    P_[used:] = np.nan
+    Q_[used:] = np.nan
     if dt == "bf16":
         P_, Q_ = W.f32_to_bf16_bits(P_), W.f32_to_bf16_bits(Q_)
     lo = P.poison(torch.empty((E, NS, N2), dtype=torch.float32, device="cuda"))
     hi = P.poison(torch.empty((E, N1 - NS, N2), dtype=torch.float32, device="cuda"))
-    rpg.moe_grouped_wgrad(P.to_dev(P_), P.to_dev(Q_), P.to_dev(lay["offsets"]), mt, M, NS=NS,
-                          out_lo=lo, out_hi=hi)
+    rpg.moe_grouped_wgrad(P.to_dev(P_), P.to_dev(Q_), P.to_dev(offs), mt, M, NS=NS, out_lo=lo,
+                          out_hi=hi)
     torch.cuda.synchronize()
     got = np.concatenate([P.to_host(lo), P.to_host(hi)], axis=1)
     p64, q64 = orc.values64(P_), orc.values64(Q_)
     ref = np.zeros((E, N1, N2))
     for e in range(E):
-        r0, r1 = int(lay["offsets"][e]), int(lay["offsets"][e + 1])
-        ref[e] = p64[:, r0:r1] @ q64[:, r0:r1].T
+        r0, r1 = int(offs[e]), int(offs[e + 1])
+        ref[e] = p64[r0:r1].T @ q64[r0:r1]
     assert np.all(np.isfinite(got))
     assert np.all(got[E - 1] == 0)
     e = P.rel_err(got, ref)
