@@ -29,11 +29,13 @@ PEAK_F32_TFLOPS = 157.3       # MI355X fp32 vector
 PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
 METRIC = "MoE-layer tokens/sec; grouped-GEMM TFLOP/s (% bf16 MFMA peak); permute GB/s"
 
-# HBM-side traffic of the dominant kernel (grouped fc1) per launch, per workload:
-# rocprofv3 FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0, the factors measured on a device copy of
-# known size (bench.py --copy-calibration 256). Taken for the current kernel source;
-# a workload without an entry reports null.
-TRAFFIC_BYTES_PER_LAUNCH = {"dense8_bf16": 4.361e9}
+# HBM-side traffic of the dominant kernels per launch, per workload: rocprofv3
+# FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0, the factors measured on a device copy of known
+# size (bench.py --copy-calibration 256). Taken for the current kernel source; a
+# workload without an entry reports null. Forward: grouped fc1; backward: the wgrad of
+# fc1 ([dW1 | dW3]).
+TRAFFIC_BYTES_PER_LAUNCH = {}
+BWD_TRAFFIC_BYTES_PER_LAUNCH = {}
 
 
 def parse():
@@ -291,7 +293,7 @@ def main():
                    "n_shared": cfg.n_shared, "F_shared": cfg.F_shared,
                    "routing": cfg.routing, "split_k_tail": gws is not None,
                    "shared_overlap": args.shared_overlap if shared is not None else None},
-        "roofline": {"kernel": "grouped fc1 + silu(a)*b (gg_bf16_kernel<true>)", "bound": "mfma",
+        "roofline": {"kernel": "grouped fc1 + silu(a)*b (gg_bf16_kernel<kFc1>)", "bound": "mfma",
                      "achieved": fc1_tflops, "peak": peak, "unit": "TFLOP/s",
                      "frac": fc1_tflops / peak, "traffic": TRAFFIC_BYTES_PER_LAUNCH.get(cfg.name),
                      "traffic_unit": "bytes per launch",
@@ -425,6 +427,7 @@ def bench_backward(args, cfg, d, buf, shared, gws, flush, n_valid) -> dict:
 
     gemm_stages = ["dgrad_fc2", "dgrad_fc1", "wgrad_fc1", "wgrad_fc2"]
     routed_flop = 12.0 * ndf
+    wg1 = tf(4 * ndf, "wgrad_fc1")
     out = {
         "tokens_per_s": T / (avg["step"] * 1e-6),
         "ms_per_step": avg["step"] * 1e-3,
@@ -434,6 +437,11 @@ def bench_backward(args, cfg, d, buf, shared, gws, flush, n_valid) -> dict:
                            "dgrad_fc1 (dX)": tf(4 * ndf, "dgrad_fc1"),
                            "wgrad_fc1 ([dW1|dW3])": tf(4 * ndf, "wgrad_fc1"),
                            "wgrad_fc2 (dW2)": tf(2 * ndf, "wgrad_fc2")},
+        "roofline": {"kernel": "k-grouped wgrad of fc1, [dW1 | dW3] (wg_bf16_kernel)",
+                     "bound": "mfma", "achieved": wg1, "peak": peak, "unit": "TFLOP/s",
+                     "frac": wg1 / peak, "traffic": BWD_TRAFFIC_BYTES_PER_LAUNCH.get(cfg.name),
+                     "traffic_unit": "bytes per launch",
+                     "algorithmic_flop_per_launch": 4 * ndf, "avg_launch_us": avg["wgrad_fc1"]},
         "grouped_gemm_tflops": tf(routed_flop, *gemm_stages),
         "grouped_gemm_frac_bf16_peak": tf(routed_flop, *gemm_stages) / peak,
         "stage_us_mean": avg, "stage_us_median": med,

@@ -77,7 +77,7 @@ __all__ = [
     "shared_experts", "combine", "forward", "token_outputs",
     "silu_grad", "preactivations", "combine_backward", "swiglu_backward",
     "expert_backward", "grouped_backward", "permute_backward", "shared_backward",
-    "backward",
+    "backward", "token_backward", "expert_weight_grad_slices",
 ]
 
 _LANES = 64  # width of one reduction group in the fixed logit order
@@ -547,3 +547,65 @@ def backward(inputs: dict, dout, k: int, m_tile: int, dtype: str, renorm: bool =
         res["dx_shared"] = dxs
     res["dx"] = permute_backward(dX, fwd["dst_row"], dtype, dxs)
     return res
+
+
+def token_backward(tokens, x, topk_idx, topk_w, w1, w3, w2, dout, dtype: str, shared_w=None):
+    """Backward of selected tokens only, without the permuted buffer: a slot's rows of
+    dY, dh, [da | db] and dX depend on its own token alone, so each sampled token's slots
+    are run one expert at a time with the rounding points of ``backward``. Returns
+    (dx [n,D], dtopk_w [n,k], slots {(t, j): {"dy", "dab", "dx_perm"}})."""
+    tokens = np.asarray(tokens, dtype=np.int64)
+    idx = np.asarray(topk_idx, dtype=np.int64)
+    w = np.asarray(topk_w, dtype=np.float64)
+    G = values64(dout)
+    F = w1.shape[1]
+    D = G.shape[1]
+    dw = np.zeros((tokens.size, idx.shape[1]))
+    acc = np.zeros((tokens.size, D))
+    slots = {}
+    pos = {int(t): i for i, t in enumerate(tokens)}
+    for e in np.unique(idx[tokens]):
+        if e < 0:
+            continue
+        sel = [(int(t), j) for t in tokens for j in range(idx.shape[1]) if idx[t, j] == e]
+        A = values64(np.stack([x[t] for t, _ in sel]))
+        w1e, w3e, w2e = values64(w1[e]), values64(w3[e]), values64(w2[e])
+        a_ = A @ w1e.T
+        b_ = A @ w3e.T
+        h = round_storage(silu(a_) * b_, dtype)
+        y = round_storage(h @ w2e.T, dtype)
+        a, b = round_storage(a_, dtype), round_storage(b_, dtype)
+        g = np.stack([G[t] for t, _ in sel])
+        wj = np.array([w[t, j] for t, j in sel])[:, None]
+        dY = round_storage(wj * g, dtype)
+        dh = round_storage(dY @ w2e, dtype)
+        da, db = swiglu_backward(dh, a, b, dtype)
+        dX = round_storage(da @ w1e + db @ w3e, dtype)
+        for r, (t, j) in enumerate(sel):
+            dw[pos[t], j] = float(np.dot(g[r], y[r]))
+            acc[pos[t]] += dX[r]
+            slots[(t, j)] = {"dy": dY[r], "dab": np.concatenate([da[r], db[r]]), "dx_perm": dX[r]}
+    dxs = None
+    if shared_w is not None:
+        dxs = shared_backward(x[tokens], *shared_w, G[tokens], dtype)[0]
+        acc += dxs
+    return round_storage(acc, dtype), dw, slots
+
+
+def expert_weight_grad_slices(x_rows, dy_rows, w1e, w3e, w2e, fs, dtype: str):
+    """Rows f in ``fs`` of dW1 and dW3 and columns f of dW2 for one expert from its rows
+    only: x_rows [n, D] are the expert's input rows and dy_rows [n, D] their stored output
+    gradients (pad rows, being zero in both, may be left out). The intermediates at
+    columns fs (a, b, h, dh, da, db) take the rounding points of ``backward``.
+    Returns (dW1[fs, :] [|fs|, D], dW3[fs, :], dW2[:, fs] [D, |fs|]), float64."""
+    fs = np.asarray(fs, dtype=np.int64)
+    X = values64(x_rows)
+    dY = values64(dy_rows)
+    w1f, w3f = values64(w1e[fs]), values64(w3e[fs])
+    a_ = X @ w1f.T
+    b_ = X @ w3f.T
+    h = round_storage(silu(a_) * b_, dtype)
+    a, b = round_storage(a_, dtype), round_storage(b_, dtype)
+    dh = round_storage(dY @ values64(w2e[:, fs]), dtype)
+    da, db = swiglu_backward(dh, a, b, dtype)
+    return da.T @ X, db.T @ X, dY.T @ h

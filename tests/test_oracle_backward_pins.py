@@ -231,3 +231,50 @@ def test_stored_gradients_are_representable_and_near_exact(dtype, rel):
         ref = ex[n]
         err = np.max(np.abs(lo[n] - ref)) / np.max(np.abs(ref))
         assert err < rel, (n, err)
+
+
+# ---------------------------------------------------------------------------
+# the sampled forms used at full size agree with the whole backward
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["bf16", "f64"])
+def test_token_backward_equals_backward_rows(dtype):
+    inp, dout = _case(41, T=12, D=16, F=8, E=4, k=2)
+    for n in ("x", "w1", "w3", "w2", "ws1", "ws3", "ws2"):
+        inp[n] = orc.round_storage(inp[n], dtype)
+    dout = orc.round_storage(dout, dtype)
+    res = orc.backward(inp, dout, 2, 4, dtype)
+    toks = np.array([0, 5, 11])
+    dx, dw, slots = orc.token_backward(toks, inp["x"], inp["topk_idx"], inp["topk_w"], inp["w1"],
+                                       inp["w3"], inp["w2"], dout, dtype,
+                                       (inp["ws1"], inp["ws3"], inp["ws2"]))
+    # the same float64 arithmetic batched differently: equal up to a last-bit rounding flip
+    tol = 1e-12 if dtype == "f64" else 2 ** -7
+    _close(dx, res["dx"][toks], "dx", tol)
+    _close(dw, res["dtopk_w"][toks], "dtopk_w", 1e-12)
+    assert len(slots) == int((inp["topk_idx"][toks] >= 0).sum())
+    for (t, j), v in slots.items():
+        r = res["fwd"]["dst_row"][t, j]
+        _close(v["dy"], res["dy_perm"][r], "dy", tol)
+        _close(v["dab"], res["dab"][r], "dab", tol)
+        _close(v["dx_perm"], res["dx_perm"][r], "dX", tol)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f64"])
+def test_weight_grad_slices_equal_backward(dtype):
+    inp, dout = _case(42, T=20, D=16, F=12, E=3, k=2, shared=False)
+    for n in ("x", "w1", "w3", "w2"):
+        inp[n] = orc.round_storage(inp[n], dtype)
+    dout = orc.round_storage(dout, dtype)
+    res = orc.backward(inp, dout, 2, 4, dtype)
+    off = res["fwd"]["offsets"]
+    fs = [0, 5, 11]
+    for e in range(3):
+        r0, r1 = int(off[e]), int(off[e + 1])
+        d1, d3, d2 = orc.expert_weight_grad_slices(res["fwd"]["x_perm"][r0:r1],
+                                                   res["dy_perm"][r0:r1], inp["w1"][e],
+                                                   inp["w3"][e], inp["w2"][e], fs, dtype)
+        tol = 1e-12 if dtype == "f64" else 1e-2
+        _close(d1, res["dw1"][e][fs], "dW1", tol)
+        _close(d3, res["dw3"][e][fs], "dW3", tol)
+        _close(d2, res["dw2"][e][:, fs], "dW2", tol)
