@@ -4,28 +4,33 @@
 // same-shape expert GEMMs with different row counts, a tile scheduler across the
 // groups, rows laid out expert-contiguous and tile aligned). Weight layout from the
 // "Expert Tensor Parallel" design note, section 4.3: w1, w3 [E,F,D], w2 [E,D,F].
+// The backward's GEMMs (section 5: an m-grouped fc mirrors into an m-grouped dgrad and
+// a k-grouped wgrad) run on the same tile pipeline.
 //
-// bf16 kernel (float32 accumulation on v_mfma_f32_32x32x16_bf16):
+// bf16 kernels (float32 accumulation on v_mfma_f32_32x32x16_bf16):
 //   * a tile is up to 256 rows of one expert's segment x a 256-row weight panel
-//     (fc1: 128 h columns, taken from w1 and w3 in alternating 32-row blocks; fc2:
-//     256 y columns). Both operands are K-contiguous; per 64-wide k step the tile
-//     stages A [256 x 64] and the panel [256 x 64] in LDS (64 KiB), double
-//     buffered through registers (128 KiB).
-//   * four waves; on a full tile each wave owns 128 rows x 128 panel rows (16
-//     MFMA blocks, 256 accumulators in AGPRs). A half tile (the last 128 rows of a
-//     segment whose length is an odd number of 128-row tiles) is split 128 rows x
-//     64 panel rows per wave, so all four SIMDs stay busy.
-//   * LDS rows are 128 bytes; the 16-byte chunk index is XOR-swizzled with half the
-//     row index, so the MFMA fragment reads are conflict free.
+//     (fc1: 128 h columns, taken from w1 and w3 in alternating 32-row blocks; fc2 and
+//     the dgrads: 256 output columns). Per 64-wide k step the tile stages A [256 x 64]
+//     and the panel [256 x 64] in LDS (64 KiB) with direct buffer->LDS loads, two
+//     stages (128 KiB).
+//   * eight waves, two per SIMD; on a full tile each wave owns 128 rows x 64 panel rows
+//     (8 MFMA blocks, 128 accumulators). A half tile (the last 128 rows of a segment
+//     whose length is an odd number of 128-row tiles) is split 64 rows x 64 panel rows
+//     per wave, so all four SIMDs stay busy.
+//   * an operand whose k is contiguous in memory is staged as 128-byte LDS rows with the
+//     16-byte chunk index XOR-swizzled by half the row index; an operand stored [k][n]
+//     (w2 read by the dgrad of fc2, w1/w3 by the dgrad of fc1, the activations by the
+//     wgrad) is staged as 512-byte k rows and read back with the transposing LDS load.
+//     Both layouts are free of bank conflicts for the fragment reads.
 //   * weights are the MFMA A operand and activations the B operand: each lane ends
 //     with 4 consecutive output columns of one row (8-byte stores); for fc1 the w1
 //     and w3 blocks of the same columns land in the same wave, which applies
 //     silu(a)*b before rounding to bf16.
 //   * persistent grid (one workgroup per CU). Each workgroup builds the list of
 //     256-row blocks per expert from offsets[] on the device (no host sync), walks
-//     each expert's (block, column) tiles with up to 16 blocks per column sweep, and
-//     the workgroup id is remapped so each XCD's L2 sees a contiguous run of tiles.
-// float32 kernel: a plain LDS-tiled VALU GEMM (the tiny float32 layer only).
+//     each expert's (block, column) tiles with up to GROUP_M blocks per column sweep,
+//     and the workgroup id is remapped so each XCD's L2 sees a contiguous run of tiles.
+// float32 kernels: plain LDS-tiled VALU GEMMs (the tiny float32 layer only).
 #include <math.h>
 
 #include <algorithm>
