@@ -34,8 +34,8 @@ METRIC = "MoE-layer tokens/sec; grouped-GEMM TFLOP/s (% bf16 MFMA peak); permute
 # size (bench.py --copy-calibration 256). Taken for the current kernel source; a
 # workload without an entry reports null. Forward: grouped fc1; backward: the wgrad of
 # fc1 ([dW1 | dW3]).
-TRAFFIC_BYTES_PER_LAUNCH = {}
-BWD_TRAFFIC_BYTES_PER_LAUNCH = {}
+TRAFFIC_BYTES_PER_LAUNCH = {"dense8_bf16": 4.493e9}
+BWD_TRAFFIC_BYTES_PER_LAUNCH = {"dense8_bf16": 8.600e9}
 
 
 def parse():
