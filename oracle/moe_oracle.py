@@ -60,6 +60,15 @@ dgrad plus a k-grouped wgrad). Readings:
     weights. The shared experts' output gradient is dout itself.
 14. The router's own backward (through softmax and top-k) is not part of this path.
 
+Masked layout for decode (same page: decode uses the masked grouped GEMM because each
+local expert's row count is known only at run time). Readings:
+
+15. Every expert owns a fixed slab of ``cap`` rows; slot (t, j) of expert e goes to row
+    e*cap + rank, rank being its stable rank among e's slots (the contiguous layout's
+    rank). A slot whose rank is cap or more is dropped (no row; combine skips it) and
+    flagged. counts[e] = min(#slots of e, cap) rows are valid; the rest of a slab is
+    neither computed nor read.
+
 Float arrays may be passed as float32/float64 values or, for bf16, as uint16
 bit patterns; this module widens them itself.
 """
@@ -78,6 +87,7 @@ __all__ = [
     "silu_grad", "preactivations", "combine_backward", "swiglu_backward",
     "expert_backward", "grouped_backward", "permute_backward", "shared_backward",
     "backward", "token_backward", "expert_weight_grad_slices",
+    "masked_layout", "masked_swiglu", "forward_masked",
 ]
 
 _LANES = 64  # width of one reduction group in the fixed logit order
@@ -609,3 +619,81 @@ def expert_weight_grad_slices(x_rows, dy_rows, w1e, w3e, w2e, fs, dtype: str):
     dh = round_storage(dY @ values64(w2e[:, fs]), dtype)
     da, db = swiglu_backward(dh, a, b, dtype)
     return da.T @ X, db.T @ X, dY.T @ h
+
+
+# ----------------------------------------------------------------------------
+# masked layout for decode (section 2 "m_grouped_*_masked (decode)"; section 3: the
+# rows each local expert receives are known only at run time)
+# ----------------------------------------------------------------------------
+
+def masked_layout(topk_idx: np.ndarray, E: int, cap: int) -> Dict[str, np.ndarray]:
+    """Fixed slabs of ``cap`` rows per expert.
+
+    counts[e]     valid rows of e's slab: min(#slots of e, cap)
+    dst_row[t,j]  e*cap + rank of t*k+j among e's slots, -1 if skipped or dropped
+    src_row[r]    t*k + j of the slot in row r, -1 for rows past counts
+    dropped       number of slots whose rank reached cap
+    m_cap         E*cap
+    """
+    idx = np.asarray(topk_idx)
+    T, k = idx.shape
+    flat = idx.reshape(-1).astype(np.int64)
+    if np.any(flat >= E) or np.any(flat < -1):
+        raise ValueError("topk_idx values must lie in [-1, E)")
+    dst = np.full(T * k, -1, dtype=np.int64)
+    src = np.full(E * cap, -1, dtype=np.int64)
+    seen = np.zeros(E, dtype=np.int64)
+    dropped = 0
+    for a, e in enumerate(flat):          # flat slot order: the stable rank
+        if e < 0:
+            continue
+        if seen[e] < cap:
+            dst[a] = e * cap + seen[e]
+            src[dst[a]] = a
+        else:
+            dropped += 1
+        seen[e] += 1
+    return {"counts": np.minimum(seen, cap).astype(np.int32),
+            "dst_row": dst.reshape(T, k).astype(np.int32), "src_row": src.astype(np.int32),
+            "dropped": int(dropped), "m_cap": int(E * cap)}
+
+
+def masked_swiglu(x_masked, counts, cap: int, w1, w3, w2, dtype: str):
+    """``expert_swiglu`` on the valid rows [e*cap, e*cap + counts[e]) of every slab.
+    Returns (h [E*cap, F], Y [E*cap, D]); rows past counts are zero here (the GPU leaves
+    them unwritten)."""
+    E, F, D = w1.shape
+    h = np.zeros((E * cap, F))
+    y = np.zeros((E * cap, D))
+    for e in range(E):
+        r0, r1 = e * cap, e * cap + int(counts[e])
+        if r1 > r0:
+            h[r0:r1], y[r0:r1] = expert_swiglu(x_masked[r0:r1], w1[e], w3[e], w2[e], dtype)
+    return h, y
+
+
+def forward_masked(inputs: dict, k: int, cap: int, dtype: str, renorm: bool = False) -> dict:
+    """The layer on the masked layout: route (or the given routing), masked_layout,
+    permute into the slabs, masked_swiglu, shared experts, combine."""
+    x = inputs["x"]
+    E = inputs["w1"].shape[0]
+    res: dict = {}
+    if "topk_idx" in inputs:
+        idx = np.asarray(inputs["topk_idx"], dtype=np.int32)
+        w = np.asarray(inputs["topk_w"], dtype=np.float64)
+    else:
+        idx, w, logits = route(x, inputs["wg"], k, dtype, inputs.get("bias"), renorm)
+        res["logits"] = logits
+    res["topk_idx"], res["topk_w"] = idx, w
+    lay = masked_layout(idx, E, cap)
+    res.update(lay)
+    xm = permute(x, lay)
+    res["x_perm"] = xm
+    h, y = masked_swiglu(xm, lay["counts"], cap, inputs["w1"], inputs["w3"], inputs["w2"], dtype)
+    res["h"], res["y_perm"] = h, y
+    shared = None
+    if "ws1" in inputs:
+        shared = shared_experts(x, inputs["ws1"], inputs["ws3"], inputs["ws2"], dtype)
+        res["shared"] = shared
+    res["out"] = combine(y, lay["dst_row"], w, dtype, shared)
+    return res

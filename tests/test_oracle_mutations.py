@@ -100,7 +100,32 @@ def _wgrad_up_from_gate(A, a, b, h, dY, w1e, w3e, w2e, dtype):
     return tuple(out)
 
 
+def _masked_keeps_the_last(topk_idx, E, cap):
+    # keeps each expert's last cap slots instead of its first
+    idx = np.asarray(topk_idx)
+    rev = orc.__dict__["_orig_masked_layout"](idx[::-1, ::-1].copy(), E, cap)
+    T, k = idx.shape
+    dst = rev["dst_row"][::-1, ::-1].copy()
+    src = np.where(rev["src_row"] >= 0, T * k - 1 - rev["src_row"], -1).astype(np.int32)
+    rev["dst_row"], rev["src_row"] = dst, src
+    return rev
+
+
+def _masked_offsets_by_count(topk_idx, E, cap):
+    # packs the slabs back to back (a contiguous layout) instead of at e*cap
+    lay = orc.__dict__["_orig_masked_layout"](topk_idx, E, cap)
+    start = np.concatenate([[0], np.cumsum(lay["counts"])[:-1]])
+    dst = lay["dst_row"].copy()
+    ok = dst >= 0
+    e = dst[ok] // cap
+    dst[ok] = start[e] + dst[ok] % cap
+    lay["dst_row"] = dst
+    return lay
+
+
 MUTATIONS = {
+    "masked_keeps_last": ("masked_layout", _masked_keeps_the_last, "masked"),
+    "masked_packed": ("masked_layout", _masked_offsets_by_count, "masked"),
     "bwd_silu_grad_term": ("silu_grad", _silu_grad_dropped_term, "autograd"),
     "bwd_swiglu_swapped": ("swiglu_backward", _swiglu_grads_swapped, "autograd"),
     "bwd_dgrad_no_up": ("expert_backward", _dgrad_without_up, "autograd"),
@@ -128,6 +153,8 @@ def _run_pin(kind):
         pins.test_topk_matches_python_sorted_with_ties()
     elif kind == "layout":
         pins.test_layout_matches_loop_counting_sort(50, 3, 7, 4, False)
+    elif kind == "masked":
+        pins.test_masked_layout_matches_loop_and_contiguous_ranks(33, 3, 4, 8)
     elif kind == "autograd":
         bpins._check_backward_against_autograd(orc, 0)
 
@@ -142,5 +169,5 @@ def test_planted_mistake_is_caught(name, monkeypatch):
 
 
 def test_unmutated_pins_pass():
-    for kind in ("brute", "brute_bias", "ties", "layout", "autograd"):
+    for kind in ("brute", "brute_bias", "ties", "layout", "autograd", "masked"):
         _run_pin(kind)

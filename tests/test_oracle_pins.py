@@ -529,3 +529,72 @@ def test_token_outputs_equal_forward_rows():
     np.testing.assert_allclose(out, res["out"][toks], rtol=0, atol=1e-12)
     for (t, j), y in ys.items():
         np.testing.assert_allclose(y, res["y_perm"][res["dst_row"][t, j]], rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# masked layout (decode)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("T,k,E,cap", [(20, 2, 5, 16), (33, 3, 4, 8), (7, 1, 3, 16), (64, 4, 8, 4)])
+def test_masked_layout_matches_loop_and_contiguous_ranks(T, k, E, cap):
+    rng = np.random.default_rng(T * 7 + cap)
+    idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    idx[rng.random((T, k)) < 0.15] = -1
+    lay = orc.masked_layout(idx, E, cap)
+    # plain loops: each expert's slots in flat order t*k+j fill its slab from row e*cap
+    fill = [0] * E
+    dropped = 0
+    for t in range(T):
+        for j in range(k):
+            e = int(idx[t, j])
+            if e < 0:
+                assert lay["dst_row"][t, j] == -1
+                continue
+            if fill[e] < cap:
+                assert lay["dst_row"][t, j] == e * cap + fill[e]
+                assert lay["src_row"][e * cap + fill[e]] == t * k + j
+            else:
+                assert lay["dst_row"][t, j] == -1
+                dropped += 1
+            fill[e] += 1
+    assert lay["dropped"] == dropped
+    assert list(lay["counts"]) == [min(c, cap) for c in fill]
+    for e in range(E):
+        assert np.all(lay["src_row"][e * cap + min(fill[e], cap):(e + 1) * cap] == -1)
+    # same stable ranks as the contiguous layout
+    con = orc.dispatch_layout(idx, E, 16)
+    for t in range(T):
+        for j in range(k):
+            e = idx[t, j]
+            if e >= 0 and lay["dst_row"][t, j] >= 0:
+                assert lay["dst_row"][t, j] - e * cap == con["dst_row"][t, j] - con["offsets"][e]
+
+
+def test_masked_forward_equals_contiguous_forward_when_nothing_drops():
+    inp = _tiny_layer(31, T=15, D=16, F=8, E=4, k=2, shared=True)
+    a = orc.forward(inp, k=2, m_tile=4, dtype="f32")
+    b = orc.forward_masked(inp, k=2, cap=15, dtype="f32")
+    assert b["dropped"] == 0
+    np.testing.assert_array_equal(a["out"], b["out"])
+    for t in range(15):
+        for j in range(2):
+            np.testing.assert_array_equal(a["y_perm"][a["dst_row"][t, j]],
+                                          b["y_perm"][b["dst_row"][t, j]])
+
+
+def test_masked_forward_drops_slots_past_capacity_like_brute_force():
+    inp = _tiny_layer(32, T=12, D=16, F=8, E=3, k=2)
+    cap = 3
+    res = orc.forward_masked(inp, k=2, cap=cap, dtype="f32")
+    assert res["dropped"] > 0
+    idx, w = res["topk_idx"], res["topk_w"]
+    seen = [0, 0, 0]
+    ref = np.zeros((12, 16))
+    for t in range(12):
+        for j in range(2):
+            e = int(idx[t, j])
+            if seen[e] < cap:
+                ref[t] += w[t, j] * np.asarray(
+                    _py_ffn(inp["x"][t], inp["w1"][e], inp["w3"][e], inp["w2"][e]))
+            seen[e] += 1
+    np.testing.assert_allclose(res["out"], ref, rtol=0, atol=1e-5 * np.abs(ref).max())
