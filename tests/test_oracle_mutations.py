@@ -153,8 +153,9 @@ def _run_pin(kind):
         pins.test_topk_matches_python_sorted_with_ties()
     elif kind == "layout":
         pins.test_layout_matches_loop_counting_sort(50, 3, 7, 4, False)
-    elif kind == "masked":
+    elif kind == "masked":   # one case with full slabs and drops, one with partly filled slabs
         pins.test_masked_layout_matches_loop_and_contiguous_ranks(33, 3, 4, 8)
+        pins.test_masked_layout_matches_loop_and_contiguous_ranks(20, 2, 5, 16)
     elif kind == "autograd":
         bpins._check_backward_against_autograd(orc, 0)
 
