@@ -154,6 +154,9 @@ def main():
         return torch.from_numpy(a).to(dev)
 
     d = {n: up(a) for n, a in inp.items() if isinstance(a, np.ndarray)}
+    if cfg.cap:
+        print(json.dumps(bench_masked(args, cfg, d, inp)), flush=True)
+        return
     tdt = d["x"].dtype
     m_cap = rpg.moe_capacity(T, k, E, mt)
     i32 = dict(dtype=torch.int32, device=dev)
@@ -318,6 +321,137 @@ def main():
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(inp, cfg, min(args.cpu_sample_tokens, T))
     print(json.dumps(rec), flush=True)
+
+
+def bench_masked(args, cfg, d, inp) -> dict:
+    """A decode step on the masked layout: route -> masked permute (slabs of cap rows per
+    expert) -> masked grouped SwiGLU [-> shared experts] -> combine, timed like the
+    contiguous step. The grouped GEMM of a decode batch streams every active expert's
+    weights for a few rows, so its roofline is HBM. The same step on the contiguous
+    layout (segments padded to the M tile) is timed next to it."""
+    import torch
+
+    import routing_permute_grouped_amd as rpg
+
+    T, D, F, E, k, cap, mt = cfg.T, cfg.D, cfg.F, cfg.E, cfg.k, cfg.cap, cfg.m_tile
+    dev = d["x"].device
+    tdt = d["x"].dtype
+    i32 = dict(dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+    gws = None if args.no_split_k else rpg.grouped_workspace(dev)
+    buf = {"idx": torch.empty((T, k), **i32), "w": torch.empty((T, k), dtype=torch.float32,
+                                                                device=dev),
+           "x_masked": torch.empty((E * cap, D), dtype=tdt, device=dev),
+           "h": torch.empty((E * cap, F), dtype=tdt, device=dev),
+           "y": torch.empty((E * cap, D), dtype=tdt, device=dev),
+           "out": torch.empty((T, D), dtype=tdt, device=dev)}
+    m_cap = rpg.moe_capacity(T, k, E, mt)
+    cbuf = {"x_perm": torch.empty((m_cap, D), dtype=tdt, device=dev),
+            "h": torch.empty((m_cap, F), dtype=tdt, device=dev),
+            "y": torch.empty((m_cap, D), dtype=tdt, device=dev)}
+    shared = None
+    if cfg.n_shared:
+        shared = rpg.SharedExperts.from_stacked(d["ws1"], d["ws3"], d["ws2"])
+        rows = rpg.DenseRows(T, mt, dev)
+        buf["hs"] = torch.empty((rows.m_cap, shared.w1.shape[1]), dtype=tdt, device=dev)
+        buf["ys"] = torch.empty((rows.m_cap, D), dtype=tdt, device=dev)
+    marks = ["route", "permute", "gemm", "shared", "combine"]
+
+    def step(ev=None, contiguous=False):
+        def mark(i):
+            if ev is not None:
+                ev[i].record(stream)
+        mark(0)
+        rpg.moe_route(d["x"], d["wg"], k, bias=d.get("bias"), topk_idx=buf["idx"],
+                      topk_w=buf["w"], stream=stream)
+        mark(1)
+        if contiguous:
+            p = rpg.moe_permute(d["x"], buf["idx"], E, mt, m_cap=m_cap, out=cbuf, stream=stream)
+            cbuf.update(p)   # reuse the metadata buffers from the first call on
+            mark(2)
+            rpg.moe_grouped_swiglu(p["x_perm"], p["offsets"], p["tile_expert"], d["w1"], d["w3"],
+                                   d["w2"], mt, m_cap=m_cap, h=cbuf["h"], y_perm=cbuf["y"],
+                                   workspace=gws, stream=stream)
+            y, mc = cbuf["y"], m_cap
+        else:
+            p = rpg.moe_permute_masked(d["x"], buf["idx"], E, cap, out=buf, stream=stream)
+            buf.update(p)
+            mark(2)
+            rpg.moe_grouped_swiglu_masked(p["x_masked"], p["counts"], d["w1"], d["w3"], d["w2"],
+                                          cap, h=buf["h"], y=buf["y"], workspace=gws,
+                                          stream=stream)
+            y, mc = buf["y"], E * cap
+        buf["p"] = p
+        mark(3)
+        sh = None
+        if shared is not None:
+            rpg.moe_grouped_swiglu(d["x"], rows.offsets, rows.tile_expert, shared.w1, shared.w3,
+                                   shared.w2, mt, m_cap=rows.m_cap, h=buf["hs"], y_perm=buf["ys"],
+                                   workspace=gws, stream=stream)
+            sh = buf["ys"][:T]
+        mark(4)
+        rpg.moe_combine(y, p["dst_row"], buf["w"], shared=sh, out=buf["out"], m_cap=mc,
+                        stream=stream)
+        mark(5)
+
+    flush = (torch.empty(args.flush_mib * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
+             if args.flush_mib > 0 else None)
+
+    def timed(contiguous):
+        for _ in range(args.warmup):
+            step(contiguous=contiguous)
+        torch.cuda.synchronize()
+        events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(marks) + 1)]
+                  for _ in range(args.steps)]
+        for s_ in range(args.steps):
+            if flush is not None:
+                flush.fill_(float(s_))
+            step(events[s_], contiguous)
+        torch.cuda.synchronize()
+        per = {m: [events[s_][i].elapsed_time(events[s_][i + 1]) * 1e3
+                   for s_ in range(args.steps)] for i, m in enumerate(marks)}
+        per["step"] = [events[s_][0].elapsed_time(events[s_][-1]) * 1e3
+                       for s_ in range(args.steps)]
+        return ({m: statistics.fmean(v) for m, v in per.items()},
+                {m: statistics.median(v) for m, v in per.items()})
+
+    avg, med = timed(False)
+    if int(buf["p"]["dev_err"].item()) != 0:
+        raise RuntimeError("masked permute flagged bad indices or dropped slots")
+    counts = buf["p"]["counts"].cpu().numpy().astype(np.int64)
+    cavg, _ = timed(True)
+    n_valid = int(counts.sum())
+    active = int((counts > 0).sum())
+    s_el = cfg.elem_bytes
+    w_bytes = active * 3.0 * D * F * s_el
+    act_bytes = n_valid * (2.0 * D + 2.0 * F) * s_el
+    gemm_bytes = w_bytes + act_bytes
+    gbps = gemm_bytes / (avg["gemm"] * 1e-6) / 1e9
+    flop = 6.0 * n_valid * D * F
+    return {
+        "metric": METRIC, "value": T / (avg["step"] * 1e-6), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": avg["step"] * 1e-3,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype,
+        "data": "synthetic (seeded numpy PCG64 draws; Gaussian inputs and weights)",
+        "config": {"workload": cfg.name, "T": T, "D": D, "F": F, "E": E, "k": k,
+                   "layout": "masked", "cap": cap, "n_shared": cfg.n_shared,
+                   "F_shared": cfg.F_shared, "split_k_tail": gws is not None},
+        "roofline": {"kernel": "grouped fc1 + fc2 on the masked layout "
+                               "(gg_bf16_kernel<kFc1>, <kFc2>)", "bound": "hbm",
+                     "achieved": gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": gbps / PEAK_HBM_GBPS, "traffic": None,
+                     "traffic_unit": "bytes per launch",
+                     "algorithmic_bytes": gemm_bytes,
+                     "note": "active experts' w1, w3, w2 once plus the valid rows' x, h "
+                             "(written and read) and y"},
+        "grouped_gemm_tflops": flop / (avg["gemm"] * 1e-6) / 1e12,
+        "stage_us_mean": avg, "stage_us_median": med,
+        "contiguous_layout": {"m_tile": mt, "stage_us_mean": cavg,
+                              "ms_per_step": cavg["step"] * 1e-3},
+        "assignments": n_valid, "active_experts": active,
+        "expert_rows_min_max": [int(counts.min()), int(counts.max())],
+        "cpu_baseline": None,
+    }
 
 
 def bench_backward(args, cfg, d, buf, shared, gws, flush, n_valid) -> dict:

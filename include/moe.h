@@ -10,6 +10,9 @@
  *   moe_grouped_swiglu  m-grouped fc1 (w1, w3) -> silu(a)*b -> fc2 (w2)
  *   moe_combine         unpermute and top-k-weighted reduce back to token order
  *
+ * For decode, moe_permute_masked and moe_grouped_swiglu_masked replace the middle
+ * two calls with fixed-capacity per-expert slabs (the masked layout).
+ *
  * and its backward ("Expert Parallelism (EP)", section 5: each forward operator
  * has a mirror; permute <-> unpermute, dispatch <-> combine, an m-grouped fc <->
  * an m-grouped dgrad plus a k-grouped wgrad) as five more:
@@ -113,6 +116,48 @@ moe_status_t moe_permute(moe_dtype_t dt, const void* x, const int32_t* topk_idx,
                          void* x_perm, int32_t* counts, int32_t* offsets,
                          int32_t* dst_row, int32_t* src_row, int32_t* tile_expert,
                          void* workspace, size_t ws_bytes, int32_t* dev_err, void* stream);
+
+/*
+ * moe_permute_masked - the masked (fixed-capacity) layout for decode ("Expert
+ * Parallelism (EP)", section 2: the masked grouped GEMM serves decode; section 3:
+ * the rows each local expert receives are known only at run time).
+ *
+ *   x [T,D] (dt), topk_idx [T,k] int32 (-1 = slot not handled here), cap
+ *   -> x_masked [E*cap,D]  expert e's slab is rows [e*cap, (e+1)*cap); slot (t,j)
+ *                          of e goes to row e*cap + its stable rank among e's slots
+ *                          (the rank moe_permute gives it); rows past counts[e]
+ *                          are not written
+ *      counts [E]          valid rows of each slab: min(#slots of e, cap)
+ *      dst_row [T,k]       row of slot (t,j), -1 if skipped or dropped
+ *      src_row [E*cap]     t*k+j of the slot in each row, -1 for unused rows
+ *      *dev_err            bit 0: some topk_idx value outside [-1, E); bit 1: some
+ *                          expert had more than cap slots (the slots past cap are
+ *                          dropped: no row, and moe_combine skips them)
+ * cap a multiple of 16 (E*cap < 2^31). workspace as moe_permute
+ * (moe_permute_workspace_bytes). moe_combine takes the same dst_row with
+ * m_cap = E*cap.
+ * Errors: MOE_EINVAL, MOE_ESHAPE, MOE_ECAPACITY (cap), MOE_EWORKSPACE, MOE_EHIP.
+ */
+moe_status_t moe_permute_masked(moe_dtype_t dt, const void* x, const int32_t* topk_idx,
+                                int T, int D, int E, int k, int cap, void* x_masked,
+                                int32_t* counts, int32_t* dst_row, int32_t* src_row,
+                                void* workspace, size_t ws_bytes, int32_t* dev_err,
+                                void* stream);
+
+/*
+ * moe_grouped_swiglu_masked - moe_grouped_swiglu on the masked layout (same page and
+ * sections): for every expert e, rows [e*cap, e*cap + min(counts[e], cap)) of
+ * x_masked [E*cap,D] give h [E*cap,F] and y [E*cap,D] with the same arithmetic,
+ * storage and workspace rules as moe_grouped_swiglu; the other rows of h and y are
+ * neither read nor written. counts stays on the device (no host synchronisation).
+ * cap a multiple of 16 (E*cap < 2^31); D*F < 2^31.
+ * Errors: MOE_EINVAL, MOE_ESHAPE, MOE_ECAPACITY (cap), MOE_EHIP.
+ */
+moe_status_t moe_grouped_swiglu_masked(moe_dtype_t dt, const void* x_masked,
+                                       const int32_t* counts, int E, int D, int F, int cap,
+                                       const void* w1, const void* w3, const void* w2,
+                                       void* h, void* y, void* workspace, size_t ws_bytes,
+                                       void* stream);
 
 /*
  * moe_grouped_swiglu - the m-grouped expert GEMMs ("Expert Parallelism (EP)",

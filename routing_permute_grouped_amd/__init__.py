@@ -7,15 +7,16 @@ from ._binding import (LIB_PATH, MOE_BF16, MOE_F32, SIGNATURES, MoEError, groupe
                        lib, moe_capacity, moe_combine, moe_combine_backward,
                        moe_grouped_dgrad_fc1, moe_grouped_dgrad_swiglu, moe_grouped_fc1_swiglu,
                        moe_grouped_fc2, moe_grouped_swiglu, moe_grouped_wgrad,
-                       moe_grouped_workspace_bytes, moe_permute, moe_permute_workspace_bytes,
-                       moe_route, moe_status_str)
-from .layer import DenseRows, SharedExperts, moe_layer, moe_layer_backward
+                       moe_grouped_swiglu_masked, moe_grouped_workspace_bytes, moe_permute,
+                       moe_permute_masked, moe_permute_workspace_bytes, moe_route, moe_status_str)
+from .layer import DenseRows, SharedExperts, moe_layer, moe_layer_backward, moe_layer_masked
 
 __all__ = [
     "LIB_PATH", "MOE_BF16", "MOE_F32", "SIGNATURES", "MoEError", "grouped_workspace", "lib",
     "moe_capacity", "moe_combine", "moe_combine_backward", "moe_grouped_dgrad_fc1",
     "moe_grouped_dgrad_swiglu", "moe_grouped_fc1_swiglu", "moe_grouped_fc2", "moe_grouped_swiglu",
-    "moe_grouped_wgrad", "moe_grouped_workspace_bytes", "moe_permute",
+    "moe_grouped_wgrad", "moe_grouped_swiglu_masked", "moe_grouped_workspace_bytes",
+    "moe_permute", "moe_permute_masked",
     "moe_permute_workspace_bytes", "moe_route", "moe_status_str", "DenseRows", "SharedExperts",
-    "moe_layer", "moe_layer_backward",
+    "moe_layer", "moe_layer_backward", "moe_layer_masked",
 ]

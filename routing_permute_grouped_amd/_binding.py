@@ -32,6 +32,9 @@ SIGNATURES = [
                                     _SZ, _P]),
     ("moe_grouped_fc2", _I, [_I, _P, _P, _P, _I, _I, _I, _I, _I64, _P, _P, _P, _SZ, _P]),
     ("moe_combine", _I, [_I, _P, _P, _P, _P, _I, _I, _I, _I64, _P, _P]),
+    ("moe_permute_masked", _I, [_I, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _SZ, _P, _P]),
+    ("moe_grouped_swiglu_masked", _I, [_I, _P, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _SZ,
+                                       _P]),
     ("moe_combine_backward", _I, [_I, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I64, _P, _P, _P]),
     ("moe_grouped_dgrad_swiglu", _I, [_I, _P, _P, _P, _I, _I, _I, _I, _I64, _P, _P, _P, _P, _P,
                                       _SZ, _P]),
@@ -304,3 +307,44 @@ def moe_grouped_wgrad(P: torch.Tensor, Q: torch.Tensor, offsets: torch.Tensor, m
         _dt(P), _ptr(P), _ptr(Q), _ptr(offsets), E, N1, N2, NS, m_tile, m_cap, _ptr(out_lo),
         _ptr(out_hi), _stream(stream)))
     return out_lo, out_hi
+
+
+def moe_permute_masked(x: torch.Tensor, topk_idx: torch.Tensor, E: int, cap: int,
+                       out: Optional[dict] = None, stream=None) -> dict:
+    """The masked layout: returns dict with x_masked [E*cap, D], counts, dst_row, src_row,
+    dev_err, workspace, cap and m_cap = E*cap. Buffers given in ``out`` are reused."""
+    T, D = x.shape
+    k = topk_idx.shape[1]
+    dev = x.device
+    o = dict(out or {})
+    i32 = dict(dtype=torch.int32, device=dev)
+    o.setdefault("x_masked", torch.empty((E * cap, D), dtype=x.dtype, device=dev))
+    o.setdefault("counts", torch.empty(E, **i32))
+    o.setdefault("dst_row", torch.empty((T, k), **i32))
+    o.setdefault("src_row", torch.empty(E * cap, **i32))
+    o.setdefault("dev_err", torch.empty(1, **i32))
+    ws = max(4, moe_permute_workspace_bytes(T, k, E))
+    o.setdefault("workspace", torch.empty(ws, dtype=torch.uint8, device=dev))
+    _check("moe_permute_masked", lib.moe_permute_masked(
+        _dt(x), _ptr(x), _ptr(topk_idx), T, D, E, k, cap, _ptr(o["x_masked"]), _ptr(o["counts"]),
+        _ptr(o["dst_row"]), _ptr(o["src_row"]), _ptr(o["workspace"]), o["workspace"].numel(),
+        _ptr(o["dev_err"]), _stream(stream)))
+    o["cap"], o["m_cap"] = cap, E * cap
+    return o
+
+
+def moe_grouped_swiglu_masked(x_masked: torch.Tensor, counts: torch.Tensor, w1: torch.Tensor,
+                              w3: torch.Tensor, w2: torch.Tensor, cap: int,
+                              h: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None,
+                              workspace: Optional[torch.Tensor] = None, stream=None):
+    """h, y on the valid rows of every slab of the masked layout."""
+    E, F, D = w1.shape
+    dev = x_masked.device
+    if h is None:
+        h = torch.empty((E * cap, F), dtype=x_masked.dtype, device=dev)
+    if y is None:
+        y = torch.empty((E * cap, D), dtype=x_masked.dtype, device=dev)
+    _check("moe_grouped_swiglu_masked", lib.moe_grouped_swiglu_masked(
+        _dt(x_masked), _ptr(x_masked), _ptr(counts), E, D, F, cap, _ptr(w1), _ptr(w3), _ptr(w2),
+        _ptr(h), _ptr(y), *_ws(workspace), _stream(stream)))
+    return h, y

@@ -481,27 +481,45 @@ __device__ __forceinline__ void run_tile(char* smem, const Tile& t, const TileLo
   }
 }
 
-// Per-workgroup schedule tables in LDS: segment starts and the first 256-row block
-// of each expert, built from offsets[] on the device.
+// The rows of each expert: contiguous segments [offsets[e], offsets[e+1]) (cap = 0), or
+// the masked layout's slabs, rows [e*cap, e*cap + min(counts[e], cap)) (cap > 0).
+struct Segs {
+  const int32_t* offsets;
+  const int32_t* counts;
+  int cap;
+};
+
+// Per-workgroup schedule tables in LDS: segment bounds and the first 256-row block of
+// each expert, built from the offsets or counts on the device.
 struct Sched {
   int segoff[MAXE + 1];   // segment starts (clamped to the rows in use)
+  int segend[MAXE];       // segment ends
   int tstart[MAXE + 1];   // first 256-row block of each expert
   int wtot[16];
 };
 
-__device__ void build_sched(Sched& sc, const int32_t* __restrict__ offsets, int E, int m_cap) {
+__device__ void build_sched(Sched& sc, const Segs& sg, int E, int m_cap) {
   const int tid = threadIdx.x;
-  // clamped into [0, min(offsets[E], m_cap)], so offsets that break the contract
-  // (negative, decreasing, past m_cap) can only shrink the work, never move it outside
-  const int mend = max(0, min(offsets[E], m_cap));
-  for (int e = tid; e <= E; e += blockDim.x) sc.segoff[e] = max(0, min(offsets[e], mend));
+  if (sg.cap > 0) {
+    for (int e = tid; e < E; e += blockDim.x) {
+      sc.segoff[e] = e * sg.cap;
+      sc.segend[e] = e * sg.cap + max(0, min(sg.counts[e], sg.cap));
+    }
+  } else {
+    // clamped into [0, min(offsets[E], m_cap)], so offsets that break the contract
+    // (negative, decreasing, past m_cap) can only shrink the work, never move it outside
+    const int mend = max(0, min(sg.offsets[E], m_cap));
+    for (int e = tid; e <= E; e += blockDim.x) sc.segoff[e] = max(0, min(sg.offsets[e], mend));
+    __syncthreads();
+    for (int e = tid; e < E; e += blockDim.x) sc.segend[e] = sc.segoff[e + 1];
+  }
   __syncthreads();
   const int per = (MAXE + blockDim.x - 1) / blockDim.x;   // experts per thread (<= 4)
   int cnt[4], local = 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int e = tid * per + i;
-    cnt[i] = (i < per && e < E) ? (max(sc.segoff[e + 1] - sc.segoff[e], 0) + BM - 1) / BM : 0;
+    cnt[i] = (i < per && e < E) ? (max(sc.segend[e] - sc.segoff[e], 0) + BM - 1) / BM : 0;
     local += cnt[i];
   }
   int run = block_scan_excl(local, sc.wtot);
@@ -537,7 +555,7 @@ __device__ Tile decode_item(const Sched& sc, int E, int n_nt, int cols, int w) {
   Tile t;
   t.e = lo;
   t.m0 = sc.segoff[lo] + (mb - sc.tstart[lo]) * BM;
-  t.rows = min(BM, sc.segoff[lo + 1] - t.m0);
+  t.rows = min(BM, sc.segend[lo] - t.m0);
   t.n0 = (within / gm) * cols;
   return t;
 }
@@ -577,13 +595,13 @@ __device__ Split split_plan(int total, int G, int slots, int nk) {
 // P_MN: the weights are read MN-major (see tile_loads); ksplit as there.
 template <int MODE, bool P_MN>
 __global__ __launch_bounds__(NTHR, 1) void gg_bf16_kernel(
-    const bf16_t* __restrict__ A, const int32_t* __restrict__ offsets, int E, int K, int N,
+    const bf16_t* __restrict__ A, Segs sg, int E, int K, int N,
     int m_cap, const bf16_t* __restrict__ W1, const bf16_t* __restrict__ W3, int ksplit,
     Epi ep, float* __restrict__ ws, int slots) {
   constexpr bool FC1 = MODE == kFc1;
   __shared__ __attribute__((aligned(16))) char smem[2 * STAGE_BYTES];
   __shared__ Sched sc;
-  build_sched(sc, offsets, E, m_cap);
+  build_sched(sc, sg, E, m_cap);
 
   const int cols = FC1 ? BP / 2 : BP;
   const int n_nt = (N + cols - 1) / cols;
@@ -646,12 +664,12 @@ __global__ __launch_bounds__(NTHR, 1) void gg_bf16_kernel(
 // Sums the split-K shares of the tail tiles in split order and applies the MODE
 // epilogue, rounding once to bf16. G must be the grid size the GEMM ran with.
 template <int MODE>
-__global__ __launch_bounds__(256) void gg_tail_reduce(const int32_t* __restrict__ offsets, int E,
-                                                      int K, int m_cap, int G, int slots,
-                                                      const float* __restrict__ ws, Epi ep) {
+__global__ __launch_bounds__(256) void gg_tail_reduce(Segs sg, int E, int K, int m_cap, int G,
+                                                      int slots, const float* __restrict__ ws,
+                                                      Epi ep) {
   constexpr bool FC1 = MODE == kFc1;
   __shared__ Sched sc;
-  build_sched(sc, offsets, E, m_cap);
+  build_sched(sc, sg, E, m_cap);
   const int N = ep.N;
   const int cols = FC1 ? BP / 2 : BP;
   const int n_nt = (N + cols - 1) / cols;
@@ -872,8 +890,7 @@ struct Epi32 {
 };
 
 template <int MODE, bool P_MN>
-__global__ __launch_bounds__(256) void gg_f32_kernel(const float* __restrict__ A,
-                                                     const int32_t* __restrict__ offsets,
+__global__ __launch_bounds__(256) void gg_f32_kernel(const float* __restrict__ A, Segs sg,
                                                      const int32_t* __restrict__ tile_expert, int E,
                                                      int K, int m_tile, int m_cap,
                                                      const float* __restrict__ W1,
@@ -884,11 +901,18 @@ __global__ __launch_bounds__(256) void gg_f32_kernel(const float* __restrict__ A
   __shared__ float As[FM][FK + 1];
   __shared__ float B1[FN][FK + 1];
   __shared__ float B3[FC1 ? FN : 1][FK + 1];
-  const int mend = min(offsets[E], m_cap);
   const int m0 = blockIdx.x * FM;
-  if (m0 >= mend) return;
-  const int e = tile_expert[m0 / m_tile];
-  if (e < 0 || e >= E) return;
+  int e, mend;
+  if (sg.cap > 0) {   // masked slabs (cap a multiple of FM: a block never straddles two)
+    e = m0 / sg.cap;
+    if (e >= E) return;
+    mend = e * sg.cap + max(0, min(sg.counts[e], sg.cap));
+  } else {
+    mend = min(sg.offsets[E], m_cap);
+    if (m0 >= mend) return;
+    e = tile_expert[m0 / m_tile];
+  }
+  if (m0 >= mend || e < 0 || e >= E) return;
   const int n0 = blockIdx.y * FN;
   const int tid = threadIdx.x;
   const int tr = tid / 16, tc = tid % 16;
@@ -1008,8 +1032,8 @@ size_t grouped_workspace_bytes() { return (size_t)cu_count() * BM * BP * sizeof(
 // One m-grouped GEMM per segment with the MODE epilogue: C = A W^T, W [E][N][K]
 // (p_mn false), or C = A W with W [E][K][N] split at ksplit between W1 and W3 (p_mn
 // true). K: reduction width, ep.N: output columns.
-static hipError_t launch_mgrouped(int dt, int mode, bool p_mn, const void* A,
-                                  const int32_t* offsets, const int32_t* tile_expert, int E, int K,
+static hipError_t launch_mgrouped(int dt, int mode, bool p_mn, const void* A, Segs sg,
+                                  const int32_t* tile_expert, int E, int K,
                                   int m_tile, int64_t m_cap, const void* W1, const void* W3,
                                   int ksplit, void* C, void* ab, void* dh, int N, void* workspace,
                                   size_t ws_bytes, hipStream_t s) {
@@ -1022,16 +1046,16 @@ static hipError_t launch_mgrouped(int dt, int mode, bool p_mn, const void* A,
     const float* w3 = static_cast<const float*>(W3);
     const int mc = (int)m_cap;
     if (mode == kFc1)
-      hipLaunchKernelGGL((gg_f32_kernel<kFc1, false>), grid, block, 0, s, a, offsets, tile_expert,
+      hipLaunchKernelGGL((gg_f32_kernel<kFc1, false>), grid, block, 0, s, a, sg, tile_expert,
                          E, K, m_tile, mc, w1, w3, K, ep);
     else if (mode == kFc2 && !p_mn)
-      hipLaunchKernelGGL((gg_f32_kernel<kFc2, false>), grid, block, 0, s, a, offsets, tile_expert,
+      hipLaunchKernelGGL((gg_f32_kernel<kFc2, false>), grid, block, 0, s, a, sg, tile_expert,
                          E, K, m_tile, mc, w1, w1, K, ep);
     else if (mode == kFc2)
-      hipLaunchKernelGGL((gg_f32_kernel<kFc2, true>), grid, block, 0, s, a, offsets, tile_expert,
+      hipLaunchKernelGGL((gg_f32_kernel<kFc2, true>), grid, block, 0, s, a, sg, tile_expert,
                          E, K, m_tile, mc, w1, w3, ksplit, ep);
     else
-      hipLaunchKernelGGL((gg_f32_kernel<kDgrad, true>), grid, block, 0, s, a, offsets,
+      hipLaunchKernelGGL((gg_f32_kernel<kDgrad, true>), grid, block, 0, s, a, sg,
                          tile_expert, E, K, m_tile, mc, w1, w1, ksplit, ep);
     return hipGetLastError();
   }
@@ -1046,44 +1070,45 @@ static hipError_t launch_mgrouped(int dt, int mode, bool p_mn, const void* A,
   const bf16_t* w3 = static_cast<const bf16_t*>(W3);
   const int mc = (int)m_cap;
   if (mode == kFc1) {
-    hipLaunchKernelGGL((gg_bf16_kernel<kFc1, false>), grid, block, 0, s, a, offsets, E, K, N, mc,
+    hipLaunchKernelGGL((gg_bf16_kernel<kFc1, false>), grid, block, 0, s, a, sg, E, K, N, mc,
                        w1, w3, K, ep, ws, slots);
     if (slots)
-      hipLaunchKernelGGL(gg_tail_reduce<kFc1>, rgrid, rblock, 0, s, offsets, E, K, mc, G, slots,
+      hipLaunchKernelGGL(gg_tail_reduce<kFc1>, rgrid, rblock, 0, s, sg, E, K, mc, G, slots,
                          ws, ep);
   } else if (mode == kFc2) {
     if (p_mn)
-      hipLaunchKernelGGL((gg_bf16_kernel<kFc2, true>), grid, block, 0, s, a, offsets, E, K, N, mc,
+      hipLaunchKernelGGL((gg_bf16_kernel<kFc2, true>), grid, block, 0, s, a, sg, E, K, N, mc,
                          w1, w3, ksplit, ep, ws, slots);
     else
-      hipLaunchKernelGGL((gg_bf16_kernel<kFc2, false>), grid, block, 0, s, a, offsets, E, K, N,
+      hipLaunchKernelGGL((gg_bf16_kernel<kFc2, false>), grid, block, 0, s, a, sg, E, K, N,
                          mc, w1, w1, K, ep, ws, slots);
     if (slots)
-      hipLaunchKernelGGL(gg_tail_reduce<kFc2>, rgrid, rblock, 0, s, offsets, E, K, mc, G, slots,
+      hipLaunchKernelGGL(gg_tail_reduce<kFc2>, rgrid, rblock, 0, s, sg, E, K, mc, G, slots,
                          ws, ep);
   } else {
-    hipLaunchKernelGGL((gg_bf16_kernel<kDgrad, true>), grid, block, 0, s, a, offsets, E, K, N, mc,
+    hipLaunchKernelGGL((gg_bf16_kernel<kDgrad, true>), grid, block, 0, s, a, sg, E, K, N, mc,
                        w1, w1, K, ep, ws, slots);
     if (slots)
-      hipLaunchKernelGGL(gg_tail_reduce<kDgrad>, rgrid, rblock, 0, s, offsets, E, K, mc, G, slots,
+      hipLaunchKernelGGL(gg_tail_reduce<kDgrad>, rgrid, rblock, 0, s, sg, E, K, mc, G, slots,
                          ws, ep);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_grouped_swiglu(int dt, int phases, const void* x_perm, const int32_t* offsets,
-                                 const int32_t* tile_expert, int E, int D, int F, int m_tile,
-                                 int64_t m_cap, const void* w1, const void* w3, const void* w2,
-                                 void* h, void* ab, void* y_perm, void* workspace, size_t ws_bytes,
-                                 hipStream_t s) {
+                                 const int32_t* counts, int cap, const int32_t* tile_expert, int E,
+                                 int D, int F, int m_tile, int64_t m_cap, const void* w1,
+                                 const void* w3, const void* w2, void* h, void* ab, void* y_perm,
+                                 void* workspace, size_t ws_bytes, hipStream_t s) {
+  const Segs sg{offsets, counts, cap};
   if (phases & 1) {
-    const hipError_t e = launch_mgrouped(dt, kFc1, false, x_perm, offsets, tile_expert, E, D,
-                                         m_tile, m_cap, w1, w3, D, h, ab, nullptr, F, workspace,
-                                         ws_bytes, s);
+    const hipError_t e = launch_mgrouped(dt, kFc1, false, x_perm, sg, tile_expert, E, D, m_tile,
+                                         m_cap, w1, w3, D, h, ab, nullptr, F, workspace, ws_bytes,
+                                         s);
     if (e != hipSuccess) return e;
   }
   if (phases & 2)
-    return launch_mgrouped(dt, kFc2, false, h, offsets, tile_expert, E, F, m_tile, m_cap, w2, w2, F,
+    return launch_mgrouped(dt, kFc2, false, h, sg, tile_expert, E, F, m_tile, m_cap, w2, w2, F,
                            y_perm, nullptr, nullptr, D, workspace, ws_bytes, s);
   return hipSuccess;
 }
@@ -1094,7 +1119,8 @@ hipError_t launch_grouped_dgrad_swiglu(int dt, const void* dy_perm, const int32_
                                        void* dab, void* dh, void* workspace, size_t ws_bytes,
                                        hipStream_t s) {
   // dh = dY w2[e]: w2 [E][D][F] is the [K = D][N = F] operand, read MN-major
-  return launch_mgrouped(dt, kDgrad, true, dy_perm, offsets, tile_expert, E, D, m_tile, m_cap, w2,
+  return launch_mgrouped(dt, kDgrad, true, dy_perm, Segs{offsets, nullptr, 0}, tile_expert, E, D,
+                         m_tile, m_cap, w2,
                          w2, D, dab, const_cast<void*>(ab), dh, F, workspace, ws_bytes, s);
 }
 
@@ -1103,7 +1129,8 @@ hipError_t launch_grouped_dgrad_fc1(int dt, const void* dab, const int32_t* offs
                                     int64_t m_cap, const void* w1, const void* w3, void* dx_perm,
                                     void* workspace, size_t ws_bytes, hipStream_t s) {
   // dX = [da | db] [w1[e] ; w3[e]]: K = 2F, k < F from w1 [E][F][D], the rest from w3
-  return launch_mgrouped(dt, kFc2, true, dab, offsets, tile_expert, E, 2 * F, m_tile, m_cap, w1,
+  return launch_mgrouped(dt, kFc2, true, dab, Segs{offsets, nullptr, 0}, tile_expert, E, 2 * F,
+                         m_tile, m_cap, w1,
                          w3, F, dx_perm, nullptr, nullptr, D, workspace, ws_bytes, s);
 }
 

@@ -27,16 +27,25 @@ hipError_t launch_permute(int dt, const void* x, const int32_t* topk_idx, int T,
                           int32_t* offsets, int32_t* dst_row, int32_t* src_row,
                           int32_t* tile_expert, void* workspace, int32_t* dev_err, hipStream_t s);
 
+// The masked layout: slot (t, j) of expert e to row e*cap + rank (rank < cap, else
+// dropped: dst_row -1 and bit 2 of *dev_err); counts[e] = min(#slots, cap); src_row
+// [E*cap]; rows past counts are not written.
+hipError_t launch_permute_masked(int dt, const void* x, const int32_t* topk_idx, int T, int D,
+                                 int E, int k, int cap, void* x_masked, int32_t* counts,
+                                 int32_t* dst_row, int32_t* src_row, void* workspace,
+                                 int32_t* dev_err, hipStream_t s);
+
 // Workspace that lets the grouped GEMM split its last round of tiles over k.
 size_t grouped_workspace_bytes();
 
 // phase bit 1: fc1 (x_perm, w1, w3 -> h, and ab = [a | b] when non-null);
-// bit 2: fc2 (h, w2 -> y_perm)
+// bit 2: fc2 (h, w2 -> y_perm). Rows: the segments [offsets[e], offsets[e+1]) when
+// cap == 0, else the masked slabs [e*cap, e*cap + min(counts[e], cap)).
 hipError_t launch_grouped_swiglu(int dt, int phases, const void* x_perm, const int32_t* offsets,
-                                 const int32_t* tile_expert, int E, int D, int F, int m_tile,
-                                 int64_t m_cap, const void* w1, const void* w3, const void* w2,
-                                 void* h, void* ab, void* y_perm, void* workspace, size_t ws_bytes,
-                                 hipStream_t s);
+                                 const int32_t* counts, int cap, const int32_t* tile_expert, int E,
+                                 int D, int F, int m_tile, int64_t m_cap, const void* w1,
+                                 const void* w3, const void* w2, void* h, void* ab, void* y_perm,
+                                 void* workspace, size_t ws_bytes, hipStream_t s);
 
 // dh = dy_perm w2[e] (w2 [E,D,F]), then [da | db] from ab -> dab; dh stored if non-null
 hipError_t launch_grouped_dgrad_swiglu(int dt, const void* dy_perm, const int32_t* offsets,

@@ -39,6 +39,8 @@ bool dim_ok(int d) { return d >= 64 && d <= kMaxDim && d % 64 == 0; }
 bool mtile_ok(int mt) { return mt == 16 || mt == 32 || mt == 64 || mt == 128 || mt == 256; }
 bool dtype_ok(int dt) { return dt == MOE_F32 || dt == MOE_BF16; }
 bool tk_ok(int T, int k) { return T >= 1 && (int64_t)T * k <= (1 << 30); }
+// masked slabs: a multiple of 16 rows each, E*cap rows addressable with int32
+bool cap_ok(int E, int cap) { return cap >= 16 && cap % 16 == 0 && (int64_t)E * cap <= INT32_MAX; }
 
 moe_status_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
 
@@ -122,10 +124,10 @@ static moe_status_t grouped(int phases, moe_dtype_t dt, const void* x_perm,
   if ((int64_t)D * F >= ((int64_t)1 << 31)) return MOE_ESHAPE;  // one expert's matrix is int32-indexed
   if (m_cap < 1 || m_cap % m_tile != 0 || m_cap > INT32_MAX) return MOE_ECAPACITY;
   if (dt == MOE_BF16 && m_tile != 128 && m_tile != 256) return MOE_EUNSUPPORTED;
-  return hip_status(moe::launch_grouped_swiglu(dt, phases, x_perm, offsets, tile_expert, E, D, F,
-                                               m_tile, m_cap, w1, w3, w2, h, ab, y_perm,
-                                               ws_bytes ? workspace : nullptr, ws_bytes,
-                                               static_cast<hipStream_t>(stream)));
+  return hip_status(moe::launch_grouped_swiglu(dt, phases, x_perm, offsets, nullptr, 0,
+                                               tile_expert, E, D, F, m_tile, m_cap, w1, w3, w2, h,
+                                               ab, y_perm, ws_bytes ? workspace : nullptr,
+                                               ws_bytes, static_cast<hipStream_t>(stream)));
 }
 
 moe_status_t moe_grouped_swiglu(moe_dtype_t dt, const void* x_perm, const int32_t* offsets,
@@ -151,6 +153,41 @@ moe_status_t moe_grouped_fc2(moe_dtype_t dt, const void* h, const int32_t* offse
                              size_t ws_bytes, void* stream) {
   return grouped(2, dt, nullptr, offsets, tile_expert, E, D, F, m_tile, m_cap, nullptr, nullptr,
                  w2, const_cast<void*>(h), nullptr, y_perm, workspace, ws_bytes, stream);
+}
+
+moe_status_t moe_permute_masked(moe_dtype_t dt, const void* x, const int32_t* topk_idx, int T,
+                                int D, int E, int k, int cap, void* x_masked, int32_t* counts,
+                                int32_t* dst_row, int32_t* src_row, void* workspace,
+                                size_t ws_bytes, int32_t* dev_err, void* stream) {
+  if (!dtype_ok(dt) || !aligned16(x) || !aligned16(x_masked) || !aligned4(topk_idx) ||
+      !aligned4(counts) || !aligned4(dst_row) || !aligned4(src_row) || !aligned4(workspace) ||
+      !aligned4(dev_err))
+    return MOE_EINVAL;
+  if (!tk_ok(T, k) || !dim_ok(D) || E < 1 || E > kMaxExperts || k < 1 || k > E || k > kMaxK)
+    return MOE_ESHAPE;
+  if (!cap_ok(E, cap)) return MOE_ECAPACITY;
+  if (ws_bytes < moe::permute_workspace_bytes(T, k, E)) return MOE_EWORKSPACE;
+  return hip_status(moe::launch_permute_masked(dt, x, topk_idx, T, D, E, k, cap, x_masked, counts,
+                                               dst_row, src_row, workspace, dev_err,
+                                               static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_grouped_swiglu_masked(moe_dtype_t dt, const void* x_masked,
+                                       const int32_t* counts, int E, int D, int F, int cap,
+                                       const void* w1, const void* w3, const void* w2, void* h,
+                                       void* y, void* workspace, size_t ws_bytes, void* stream) {
+  if (!dtype_ok(dt) || !aligned4(counts) || !aligned16(x_masked) || !aligned16(w1) ||
+      !aligned16(w3) || !aligned16(w2) || !aligned16(h) || !aligned16(y))
+    return MOE_EINVAL;
+  if (workspace && !aligned16(workspace)) return MOE_EINVAL;
+  if (!workspace) ws_bytes = 0;
+  if (E < 1 || E > kMaxExperts || !dim_ok(D) || !dim_ok(F)) return MOE_ESHAPE;
+  if ((int64_t)D * F >= ((int64_t)1 << 31)) return MOE_ESHAPE;
+  if (!cap_ok(E, cap)) return MOE_ECAPACITY;
+  return hip_status(moe::launch_grouped_swiglu(dt, 3, x_masked, nullptr, counts, cap, nullptr, E,
+                                               D, F, 16, (int64_t)E * cap, w1, w3, w2, h, nullptr,
+                                               y, ws_bytes ? workspace : nullptr, ws_bytes,
+                                               static_cast<hipStream_t>(stream)));
 }
 
 static moe_status_t dgrad_common(moe_dtype_t dt, const void* a, const int32_t* offsets,

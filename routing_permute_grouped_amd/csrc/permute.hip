@@ -68,8 +68,13 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* wsum) {
   return before + inc - v;
 }
 
+// MASKED: the masked layout (fixed slabs of `cap` rows, expert e from row e*cap; m_tile
+// unused, m_cap = E*cap): ranks at or past cap are dropped, counts are capped, offsets
+// and tile_expert are not written.
+template <bool MASKED>
 __global__ __launch_bounds__(kThreads) void rank_kernel(
-    const int32_t* __restrict__ idx, int T, int k, int E, int m_tile, int64_t m_cap, int nbh,
+    const int32_t* __restrict__ idx, int T, int k, int E, int m_tile, int cap, int64_t m_cap,
+    int nbh,
     const int32_t* __restrict__ hist, const int32_t* __restrict__ bad,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
     int32_t* __restrict__ tile_expert, int32_t* __restrict__ dev_err,
@@ -101,24 +106,44 @@ __global__ __launch_bounds__(kThreads) void rank_kernel(
     }
   }
   __syncthreads();
-  int padded[4] = {0, 0, 0, 0};
-  int local = 0;
+  if (MASKED) {
+    for (int e = tid; e <= E; e += kThreads) off[e] = e * cap;
+  } else {
+    int padded[4] = {0, 0, 0, 0};
+    int local = 0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int e = tid * 4 + i;
-    if (e < E) padded[i] = (cnt[e] + m_tile - 1) / m_tile * m_tile;
-    local += padded[i];
-  }
-  int run = block_exclusive_scan(local, wsum);
+    for (int i = 0; i < 4; ++i) {
+      const int e = tid * 4 + i;
+      if (e < E) padded[i] = (cnt[e] + m_tile - 1) / m_tile * m_tile;
+      local += padded[i];
+    }
+    int run = block_exclusive_scan(local, wsum);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int e = tid * 4 + i;
-    if (e < E) off[e] = run;
-    run += padded[i];
+    for (int i = 0; i < 4; ++i) {
+      const int e = tid * 4 + i;
+      if (e < E) off[e] = run;
+      run += padded[i];
+    }
+    if (tid == kThreads - 1) off[E] = run;
   }
-  if (tid == kThreads - 1) off[E] = run;
   __syncthreads();
 
+  if (!token_block && MASKED) {   // capped counts, unused slab rows, error flags
+    int over = 0;
+    for (int e = tid; e < E; e += kThreads) {
+      counts[e] = min(cnt[e], cap);
+      over |= cnt[e] > cap;
+    }
+    for (int e = 0; e < E; ++e)
+      for (int r = e * cap + min(cnt[e], cap) + tid; r < (e + 1) * cap; r += kThreads)
+        src_row[r] = -1;
+    int anybad = 0;
+    for (int h = tid; h < nbh; h += kThreads) anybad |= bad[h] != 0;
+    anybad = __syncthreads_or(anybad);
+    over = __syncthreads_or(over);
+    if (tid == 0) *dev_err = anybad | (over << 1);
+    return;
+  }
   if (!token_block) {   // metadata, unused rows, error flag
     {
       for (int i = tid; i < E; i += kThreads) counts[i] = cnt[i];
@@ -173,7 +198,10 @@ __global__ __launch_bounds__(kThreads) void rank_kernel(
         same &= ((e >> bit) & 1) ? bal : ~bal;
       }
       int pos = -1;
-      if (valid) pos = off[e] + base[e] + __popcll(same & lt);
+      if (valid) {
+        const int rank = base[e] + __popcll(same & lt);
+        pos = (MASKED && rank >= cap) ? -1 : off[e] + rank;   // masked: past the slab is dropped
+      }
       if (pos >= m_cap) pos = -1;  // cannot happen with consistent counts; never write past m_cap
       __builtin_amdgcn_wave_barrier();
       if (valid && (same >> lane) == 1ull) base[e] = base[e] + __popcll(same);
@@ -226,6 +254,23 @@ __global__ __launch_bounds__(kThreads) void copy_kernel(
   }
 }
 
+hipError_t launch_copy(int dt, const void* x, int T, int D, int k, int E,
+                              const int32_t* dst_row, const int32_t* counts,
+                              const int32_t* offsets, void* x_perm, hipStream_t s) {
+  const int V = dt == kF32 ? 4 : 8;
+  const int64_t chunks = (int64_t)T * (D / V);
+  const int grid = (int)std::min<int64_t>(8 * cu_count(), (chunks + kThreads * kUnroll - 1) / (kThreads * kUnroll));
+  if (dt == kF32)
+    hipLaunchKernelGGL(copy_kernel<float>, dim3(grid), dim3(kThreads), 0, s,
+                       static_cast<const float*>(x), T, D, k, E, dst_row, counts, offsets,
+                       static_cast<float*>(x_perm));
+  else
+    hipLaunchKernelGGL(copy_kernel<bf16_t>, dim3(grid), dim3(kThreads), 0, s,
+                       static_cast<const bf16_t*>(x), T, D, k, E, dst_row, counts, offsets,
+                       static_cast<bf16_t*>(x_perm));
+  return hipGetLastError();
+}
+
 }  // namespace
 
 size_t permute_workspace_bytes(int T, int k, int E) {
@@ -243,21 +288,26 @@ hipError_t launch_permute(int dt, const void* x, const int32_t* topk_idx, int T,
   int32_t* bad = hist + (size_t)nbh * E;
   hipLaunchKernelGGL(hist_kernel, dim3(nbh), dim3(kThreads), 0, s, topk_idx, T, k, E, hist, bad);
   const int nbp = (T + kPlaceTokens - 1) / kPlaceTokens;
-  hipLaunchKernelGGL(rank_kernel, dim3(nbp + 1), dim3(kThreads), 0, s, topk_idx, T, k, E, m_tile,
-                     m_cap, nbh, hist, bad, counts, offsets, tile_expert, dev_err, dst_row,
-                     src_row);
-  const int V = dt == kF32 ? 4 : 8;
-  const int64_t chunks = (int64_t)T * (D / V);
-  const int grid = (int)std::min<int64_t>(8 * cu_count(), (chunks + kThreads * kUnroll - 1) / (kThreads * kUnroll));
-  if (dt == kF32)
-    hipLaunchKernelGGL(copy_kernel<float>, dim3(grid), dim3(kThreads), 0, s,
-                       static_cast<const float*>(x), T, D, k, E, dst_row, counts, offsets,
-                       static_cast<float*>(x_perm));
-  else
-    hipLaunchKernelGGL(copy_kernel<bf16_t>, dim3(grid), dim3(kThreads), 0, s,
-                       static_cast<const bf16_t*>(x), T, D, k, E, dst_row, counts, offsets,
-                       static_cast<bf16_t*>(x_perm));
-  return hipGetLastError();
+  hipLaunchKernelGGL(rank_kernel<false>, dim3(nbp + 1), dim3(kThreads), 0, s, topk_idx, T, k, E,
+                     m_tile, 0, m_cap, nbh, hist, bad, counts, offsets, tile_expert, dev_err,
+                     dst_row, src_row);
+  return launch_copy(dt, x, T, D, k, E, dst_row, counts, offsets, x_perm, s);
+}
+
+hipError_t launch_permute_masked(int dt, const void* x, const int32_t* topk_idx, int T, int D,
+                                 int E, int k, int cap, void* x_masked, int32_t* counts,
+                                 int32_t* dst_row, int32_t* src_row, void* workspace,
+                                 int32_t* dev_err, hipStream_t s) {
+  const int nbh = (T + kHistTokens - 1) / kHistTokens;
+  int32_t* hist = static_cast<int32_t*>(workspace);
+  int32_t* bad = hist + (size_t)nbh * E;
+  hipLaunchKernelGGL(hist_kernel, dim3(nbh), dim3(kThreads), 0, s, topk_idx, T, k, E, hist, bad);
+  const int nbp = (T + kPlaceTokens - 1) / kPlaceTokens;
+  hipLaunchKernelGGL(rank_kernel<true>, dim3(nbp + 1), dim3(kThreads), 0, s, topk_idx, T, k, E, 0,
+                     cap, (int64_t)E * cap, nbh, hist, bad, counts, nullptr, nullptr, dev_err,
+                     dst_row, src_row);
+  // no pad rows to zero in the masked layout (E = 0 skips that pass)
+  return launch_copy(dt, x, T, D, k, 0, dst_row, counts, nullptr, x_masked, s);
 }
 
 }  // namespace moe

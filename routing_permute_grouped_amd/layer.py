@@ -98,6 +98,36 @@ def moe_layer(x: torch.Tensor, w1: torch.Tensor, w3: torch.Tensor, w2: torch.Ten
     return res
 
 
+def moe_layer_masked(x: torch.Tensor, w1: torch.Tensor, w3: torch.Tensor, w2: torch.Tensor,
+                     k: int, cap: int, wg: Optional[torch.Tensor] = None,
+                     bias: Optional[torch.Tensor] = None, topk_idx: Optional[torch.Tensor] = None,
+                     topk_w: Optional[torch.Tensor] = None,
+                     shared: Optional[SharedExperts] = None, renorm: bool = False,
+                     split_k: bool = True, shared_m_tile: int = 128) -> dict:
+    """The layer on the masked (fixed-capacity) layout for decode: route -> masked
+    permute (slabs of ``cap`` rows per expert) -> masked grouped SwiGLU [-> shared
+    experts] -> combine. Slots past an expert's cap are dropped (bit 1 of dev_err)."""
+    E = w1.shape[0]
+    res = {}
+    if topk_idx is None:
+        topk_idx, topk_w, _ = B.moe_route(x, wg, k, bias=bias, renorm=renorm)
+    res["topk_idx"], res["topk_w"] = topk_idx, topk_w
+    p = B.moe_permute_masked(x, topk_idx, E, cap)
+    res.update(p)
+    ws = B.grouped_workspace(x.device) if split_k else None
+    h, y = B.moe_grouped_swiglu_masked(p["x_masked"], p["counts"], w1, w3, w2, cap, workspace=ws)
+    res["h"], res["y_perm"] = h, y
+    sh = None
+    if shared is not None:
+        rows = DenseRows(x.shape[0], shared_m_tile, x.device)
+        _, ys = B.moe_grouped_swiglu(x, rows.offsets, rows.tile_expert, shared.w1, shared.w3,
+                                     shared.w2, shared_m_tile, m_cap=rows.m_cap, workspace=ws)
+        sh = ys[: x.shape[0]]
+        res["shared"] = sh
+    res["out"] = B.moe_combine(y, p["dst_row"], topk_w, shared=sh, m_cap=p["m_cap"])
+    return res
+
+
 def _experts_backward(dy, x_rows, ab, h, offsets, tile_expert, w1, w3, w2, m_tile, m_cap, ws):
     """dgrad and wgrad of one grouped SwiGLU FFN over rows [0, m_cap) (section 5 of
     "Expert Parallelism (EP)": the m-grouped fc mirrors into an m-grouped dgrad and a

@@ -27,7 +27,8 @@ def test_header_declares_the_calls_and_helpers():
                                          "moe_grouped_fc1_swiglu", "moe_grouped_fc2",
                                          "moe_combine", "moe_combine_backward",
                                          "moe_grouped_dgrad_swiglu", "moe_grouped_dgrad_fc1",
-                                         "moe_grouped_wgrad", "moe_capacity",
+                                         "moe_grouped_wgrad", "moe_permute_masked",
+                                         "moe_grouped_swiglu_masked", "moe_capacity",
                                          "moe_grouped_workspace_bytes",
                                          "moe_permute_workspace_bytes", "moe_status_str"])
 
@@ -226,6 +227,40 @@ def test_wgrad_needs_only_the_output_halves_it_writes():
     assert wgrad(NS=512, hi=None, N2=100) == MOE_ESHAPE
     assert wgrad(NS=0, lo=None, N2=100) == MOE_ESHAPE
     assert wgrad(NS=256, hi=None) == MOE_EINVAL
+
+
+def permute_masked(dt=1, x=FAKE, idx=FAKE, T=64, D=128, E=8, k=2, cap=16, xm=FAKE, ws=FAKE,
+                   ws_bytes=1 << 20):
+    return lib.moe_permute_masked(dt, x, idx, T, D, E, k, cap, xm, FAKE, FAKE, FAKE, ws, ws_bytes,
+                                  FAKE, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=3), MOE_EINVAL), (dict(x=None), MOE_EINVAL), (dict(xm=FAKE + 4), MOE_EINVAL),
+    (dict(idx=FAKE + 2), MOE_EINVAL), (dict(T=0), MOE_ESHAPE), (dict(D=96), MOE_ESHAPE),
+    (dict(k=9), MOE_ESHAPE), (dict(E=1025), MOE_ESHAPE), (dict(cap=0), MOE_ECAPACITY),
+    (dict(cap=24), MOE_ECAPACITY), (dict(E=1024, k=2, cap=1 << 21), MOE_ECAPACITY),
+    (dict(ws_bytes=0), MOE_EWORKSPACE),
+])
+def test_permute_masked_validation(kw, code):
+    assert permute_masked(**kw) == code
+
+
+def grouped_masked(dt=1, xm=FAKE, counts=FAKE, E=8, D=128, F=256, cap=32, w1=FAKE, h=FAKE,
+                   ws=None, ws_bytes=0):
+    return lib.moe_grouped_swiglu_masked(dt, xm, counts, E, D, F, cap, w1, FAKE, FAKE, h, FAKE,
+                                         ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=2), MOE_EINVAL), (dict(xm=None), MOE_EINVAL), (dict(counts=None), MOE_EINVAL),
+    (dict(w1=FAKE + 8), MOE_EINVAL), (dict(h=None), MOE_EINVAL),
+    (dict(ws=FAKE + 4, ws_bytes=1 << 20), MOE_EINVAL), (dict(E=0), MOE_ESHAPE),
+    (dict(F=100), MOE_ESHAPE), (dict(D=65536, F=32768), MOE_ESHAPE), (dict(cap=8), MOE_ECAPACITY),
+    (dict(cap=40), MOE_ECAPACITY),
+])
+def test_grouped_masked_validation(kw, code):
+    assert grouped_masked(**kw) == code
 
 
 def test_binding_raises_on_rejected_call():

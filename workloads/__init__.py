@@ -7,7 +7,9 @@ the method's arithmetic (routing, permutation, expert FFN, combine) lives here.
 Presets follow the workloads named for the path: a tiny fp32 layer, a dense
 8-expert bf16 layer, a fine-grained 64-expert layer with two shared experts, a
 skewed-routing stress case, and one expert-tensor-parallel rank's local shard
-(32 experts, D=7168, F cut 4-way to 512, routing given as input). Sizes of the
+(32 experts, D=7168, F cut 4-way to 512, routing given as input); and two decode
+steps (64 and 128 tokens through the dense and the fine-grained layer) on the masked
+layout. Sizes of the
 expert weights follow the SwiGLU layout w1/w3 [E,F,D], w2 [E,D,F] (HyperParallel
 issue 104, "Expert Tensor Parallel" design note, section 4.3 weight placement).
 
@@ -56,6 +58,7 @@ class MoEConfig:
     zipf_s: float = 0.0       # >0: router bias b_e = -zipf_s * zipf_beta * ln(rank_e)
     zipf_beta: float = 1.0
     poisson_mean: float = 0.0  # given routing: rows per expert ~ Poisson(mean)
+    cap: int = 0               # >0: the masked (fixed-capacity slab) layout with cap rows per expert
 
     @property
     def elem_bytes(self) -> int:
@@ -78,6 +81,13 @@ PRESETS: Dict[str, MoEConfig] = {
     "etp_shard32_bf16": MoEConfig("etp_shard32_bf16", T=0, D=7168, F=512, E=32, k=8,
                                   m_tile=128, dtype="bf16", routing="given",
                                   poisson_mean=512.0),
+    # decode steps on the masked layout: a small batch of tokens, slabs of cap = T rows
+    # per expert (no slot can be dropped)
+    "decode8_bf16": MoEConfig("decode8_bf16", T=64, D=4096, F=14336, E=8, k=2, m_tile=128,
+                              dtype="bf16", cap=64),
+    "decode64_shared2_bf16": MoEConfig("decode64_shared2_bf16", T=128, D=2048, F=1408, E=64,
+                                       k=6, m_tile=128, dtype="bf16", n_shared=2,
+                                       F_shared=1408, cap=128),
 }
 
 
