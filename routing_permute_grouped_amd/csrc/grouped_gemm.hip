@@ -389,6 +389,114 @@ __device__ __forceinline__ void mainloop(char* smem, const TileLoads& ld, int kb
   // first barrier, which every wave reaches after finishing this tile's MFMAs.
 }
 
+// kDgrad epilogue through LDS. The lane layout of the accumulators (4 consecutive
+// columns of 32 different rows per instruction) would make the ab loads and dab stores
+// touch 32 rows x 8 bytes per wave instruction; instead dh (rounded to bf16, as stored)
+// goes into the LDS stage the tile's last k-step used (free once every wave has passed
+// the barrier below), 128 rows x 256 columns per pass, and is read back by rows, so the
+// ab loads and the dab and dh stores are whole 16-byte chunks of consecutive columns.
+// LDS rows are 512 bytes; the 8-byte unit u of row r is stored at u ^ (r % 32), so the
+// 32 rows a half-wave writes hit 32 distinct bank pairs, and a 16-byte row read lands
+// on chunk c ^ ((r % 32) / 2) with its halves swapped when r is odd.
+// Barrier for LDS traffic only: this wave's LDS accesses are complete, then every wave
+// meets; outstanding global loads (the next tile's first stage) keep flying.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+template <bool HALF>
+__device__ __forceinline__ void dgrad_epilogue(char* stage, const Tile& t, const Epi& ep,
+                                               const f32x16 (&acc)[HALF ? 2 : 4][2]) {
+  constexpr int WM = HALF ? 2 : 4;
+  constexpr int PASSES = HALF ? 1 : 2;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int arow0 = (wave & 1) * (HALF ? 64 : 128);
+  const int prow0 = (wave >> 1) * 64;
+  const int fr = lane & 31;
+  const int N = ep.N;
+  // dh as stored (bf16), packed now: half the registers of the float32 sums
+  uint2 pk[WM][2][4];
+#pragma unroll
+  for (int mb = 0; mb < WM; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x16& a = acc[mb][nb];
+        pk[mb][nb][g] = uint2{pack_bf16x2(a[4 * g], a[4 * g + 1]),
+                              pack_bf16x2(a[4 * g + 2], a[4 * g + 3])};
+      }
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) {
+    lds_barrier();   // the stage is free: MFMA reads (or the previous pass) are done
+    if (HALF || (wave & 1) == p) {
+#pragma unroll
+      for (int mb = 0; mb < WM; ++mb) {
+        const int rl = (HALF ? arow0 : 0) + mb * 32 + fr;   // row within the pass
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int u = (prow0 + nb * 32 + g * 8 + (lane >> 5) * 4) >> 2;
+            *reinterpret_cast<uint2*>(stage + rl * 512 + ((u ^ (rl & 31)) << 3)) = pk[mb][nb][g];
+          }
+      }
+    }
+    lds_barrier();
+    // 128 rows x 32 chunks of 8 columns; 16 rows per round of the 512 threads
+    const int c = threadIdx.x & 31;
+    const int n = t.n0 + 8 * c;
+#pragma unroll
+    for (int it0 = 0; it0 < 8; it0 += 4) {
+      uint4 va[4], vb[4];
+      bool ok[4];
+      size_t row[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int rl = (threadIdx.x >> 5) + 16 * (it0 + i);
+        const int r = p * 128 + rl;
+        ok[i] = r < t.rows && n < N;
+        row[i] = (size_t)(t.m0 + r) * N;
+        if (ok[i]) {
+          va[i] = *reinterpret_cast<const uint4*>(ep.ab + 2 * row[i] + n);
+          vb[i] = *reinterpret_cast<const uint4*>(ep.ab + 2 * row[i] + N + n);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (!ok[i]) continue;
+        const int rl = (threadIdx.x >> 5) + 16 * (it0 + i);
+        const int m = rl & 31;
+        uint4 d = *reinterpret_cast<const uint4*>(stage + rl * 512 + ((c ^ (m >> 1)) << 4));
+        if (m & 1) d = uint4{d.z, d.w, d.x, d.y};
+        const uint32_t dw[4] = {d.x, d.y, d.z, d.w};
+        const uint32_t aw[4] = {va[i].x, va[i].y, va[i].z, va[i].w};
+        const uint32_t bw[4] = {vb[i].x, vb[i].y, vb[i].z, vb[i].w};
+        uint32_t oa[4], ob[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          float da2[2], db2[2];
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const float dh = h ? bf16_hi(dw[q]) : bf16_lo(dw[q]);
+            const float av = h ? bf16_hi(aw[q]) : bf16_lo(aw[q]);
+            const float bv = h ? bf16_hi(bw[q]) : bf16_lo(bw[q]);
+            const float sg = 1.0f / (1.0f + __expf(-av));   // sigmoid; silu = a*s
+            db2[h] = dh * (av * sg);
+            da2[h] = dh * bv * (sg * (1.0f + av * (1.0f - sg)));
+          }
+          oa[q] = pack_bf16x2(da2[0], da2[1]);
+          ob[q] = pack_bf16x2(db2[0], db2[1]);
+        }
+        *reinterpret_cast<uint4*>(ep.C + 2 * row[i] + n) = uint4{oa[0], oa[1], oa[2], oa[3]};
+        *reinterpret_cast<uint4*>(ep.C + 2 * row[i] + N + n) = uint4{ob[0], ob[1], ob[2], ob[3]};
+        if (ep.dh) *reinterpret_cast<uint4*>(ep.dh + row[i] + n) = uint4{d.x, d.y, d.z, d.w};
+      }
+    }
+  }
+}
+
 // One tile of the m-grouped kernel: the main loop, then either the raw float32 sums of
 // a split-K share (`part`, row-major [BM][BP]) or the MODE epilogue.
 // After the main loop lane l holds column m = l % 32 of every 32x32 block and panel rows
@@ -424,6 +532,10 @@ __device__ __forceinline__ void run_tile(char* smem, const Tile& t, const TileLo
     }
     return;
   }
+  if (MODE == kDgrad) {
+    dgrad_epilogue<HALF>(smem + ((stage0 + ke - kb - 1) & 1) * STAGE_BYTES, t, ep, acc);
+    return;
+  }
 #pragma unroll
   for (int mb = 0; mb < WM; ++mb) {
     const int r = arow0 + mb * 32 + fr;
@@ -441,30 +553,6 @@ __device__ __forceinline__ void run_tile(char* smem, const Tile& t, const TileLo
         const float u[4] = {b[4 * g], b[4 * g + 1], b[4 * g + 2], b[4 * g + 3]};
         emit4<MODE>(ep, m, n, v, u);
       }
-    } else if (MODE == kDgrad) {
-      // all of the row's (a, b) loads first, so they are in flight together rather than
-      // one round trip per group of four columns
-      const size_t row = (size_t)m * ep.N;
-      uint2 pa[WN][4], pb[WN][4];
-#pragma unroll
-      for (int nb = 0; nb < WN; ++nb)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int n = t.n0 + prow0 + nb * 32 + g * 8 + (lane >> 5) * 4;
-          if (n >= ep.N) continue;
-          pa[nb][g] = *reinterpret_cast<const uint2*>(ep.ab + 2 * row + n);
-          pb[nb][g] = *reinterpret_cast<const uint2*>(ep.ab + 2 * row + ep.N + n);
-        }
-#pragma unroll
-      for (int nb = 0; nb < WN; ++nb)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int n = t.n0 + prow0 + nb * 32 + g * 8 + (lane >> 5) * 4;
-          if (n >= ep.N) continue;
-          const f32x16& a = acc[mb][nb];
-          const float v[4] = {a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]};
-          dgrad4(ep, row, n, v, pa[nb][g], pb[nb][g]);
-        }
     } else {
 #pragma unroll
       for (int nb = 0; nb < WN; ++nb) {
@@ -794,6 +882,10 @@ __device__ __forceinline__ TileLoads wg_loads(const WTile& w, const bf16_t* __re
   return o;
 }
 
+// One wgrad tile. The float32 result (256 x 256, 256 KiB) leaves through the LDS stage
+// the tile's last k-step used, 64 rows (64 KiB) per pass: the owning waves write their
+// accumulators (16-byte unit u of row r stored at u ^ (r % 16): the 16 rows a quarter-wave
+// writes hit distinct banks), then every wave stores whole 1 KiB rows to the output.
 template <bool HALF>
 __device__ __forceinline__ void wg_tile(char* smem, const WTile& w, const TileLoads& ld, int N1,
                                         int N2, int NS, float* __restrict__ out_lo,
@@ -801,6 +893,7 @@ __device__ __forceinline__ void wg_tile(char* smem, const WTile& w, const TileLo
                                         const TileLoads& nxt, bool has_next) {
   constexpr int WM = HALF ? 2 : 4;
   constexpr int WN = 2;
+  constexpr int PASSES = HALF ? 2 : 4;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int arow0 = (wave & 1) * (HALF ? 64 : 128);
@@ -808,23 +901,39 @@ __device__ __forceinline__ void wg_tile(char* smem, const WTile& w, const TileLo
   const int fr = lane & 31;
   f32x16 acc[WM][WN];
   mainloop<HALF, true, true>(smem, ld, 0, w.nk, stage0, primed, nxt, has_next, 0, acc);
+  char* stage = smem + ((stage0 + w.nk - 1) & 1) * STAGE_BYTES;
 #pragma unroll
-  for (int mb = 0; mb < WM; ++mb) {
-    const int r = arow0 + mb * 32 + fr;
-    if (r >= w.t.rows) continue;
-    const int i = w.t.m0 + r;
-    float* orow = i < NS ? out_lo + ((size_t)w.t.e * NS + i) * N2
-                         : out_hi + ((size_t)w.t.e * (N1 - NS) + (i - NS)) * N2;
+  for (int p = 0; p < PASSES; ++p) {
+    lds_barrier();
 #pragma unroll
-    for (int nb = 0; nb < WN; ++nb)
+    for (int mb = 0; mb < WM; ++mb) {
+      const int r = arow0 + mb * 32 + fr;
+      // rows [64p, 64p + 64): a block of 32 rows lies in one pass
+      if ((arow0 + mb * 32) / 64 != p) continue;
+      const int rl = r - 64 * p;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int j = w.t.n0 + prow0 + nb * 32 + g * 8 + (lane >> 5) * 4;
-        if (j >= N2) continue;
-        const f32x16& a = acc[mb][nb];
-        *reinterpret_cast<float4*>(orow + j) =
-            float4{a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]};
-      }
+      for (int nb = 0; nb < WN; ++nb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int u = (prow0 + nb * 32 + g * 8 + (lane >> 5) * 4) >> 2;
+          const f32x16& a = acc[mb][nb];
+          *reinterpret_cast<float4*>(stage + rl * 1024 + ((u ^ (rl & 15)) << 4)) =
+              float4{a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]};
+        }
+    }
+    lds_barrier();
+    const int j = w.t.n0 + 4 * lane;
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int rl = wave + 8 * it;
+      const int r = 64 * p + rl;
+      if (r >= w.t.rows || j >= N2) continue;
+      const int i = w.t.m0 + r;
+      float* orow = i < NS ? out_lo + ((size_t)w.t.e * NS + i) * N2
+                           : out_hi + ((size_t)w.t.e * (N1 - NS) + (i - NS)) * N2;
+      *reinterpret_cast<float4*>(orow + j) =
+          *reinterpret_cast<const float4*>(stage + rl * 1024 + ((lane ^ (rl & 15)) << 4));
+    }
   }
 }
 
