@@ -69,6 +69,19 @@ local expert's row count is known only at run time). Readings:
     flagged. counts[e] = min(#slots of e, cap) rows are valid; the rest of a slab is
     neither computed nor read.
 
+FP8 payload (section 3 of the same page: dispatch in FP8 e4m3 "plus scales", combine in
+BF16). Readings:
+
+16. The scales are MX block scales: one power-of-two scale 2^X per 32 consecutive values
+    along D (E8M0, stored as X + 127). X is the smallest integer with max|v| <= 448 * 2^X
+    (448 is e4m3's largest value), so no value of the block saturates; X = -127 for an
+    all-zero block. Each value is v / 2^X rounded to the nearest e4m3 value (OCP E4M3:
+    bias 7, no infinities, max 448), ties to even.
+17. x is quantized once per token before the permute (the permute copies its rows); the
+    fc1 weights w1, w3 are quantized the same way along D; fc1 contracts the dequantized
+    values (float64 here, float32 accumulation on the device); h and everything after it
+    stay bf16 (fc2 and the combine are the bf16 path).
+
 Float arrays may be passed as float32/float64 values or, for bf16, as uint16
 bit patterns; this module widens them itself.
 """
@@ -88,6 +101,8 @@ __all__ = [
     "expert_backward", "grouped_backward", "permute_backward", "shared_backward",
     "backward", "token_backward", "expert_weight_grad_slices",
     "masked_layout", "masked_swiglu", "forward_masked",
+    "e4m3_decode", "e4m3_round", "e4m3_encode", "mx_quantize", "mx_dequantize",
+    "expert_fc1_mx", "grouped_fc1_mx", "forward_mxfp8",
 ]
 
 _LANES = 64  # width of one reduction group in the fixed logit order
@@ -696,4 +711,132 @@ def forward_masked(inputs: dict, k: int, cap: int, dtype: str, renorm: bool = Fa
         shared = shared_experts(x, inputs["ws1"], inputs["ws3"], inputs["ws2"], dtype)
         res["shared"] = shared
     res["out"] = combine(y, lay["dst_row"], w, dtype, shared)
+    return res
+
+
+# ----------------------------------------------------------------------------
+# FP8 (e4m3) payload with MX block scales (section 3: dispatch = FP8 e4m3 plus scales,
+# combine = BF16)
+# ----------------------------------------------------------------------------
+
+def e4m3_decode(code) -> np.ndarray:
+    """Value of OCP E4M3 codes (bias 7; exponent field 0 is subnormal, m/8 * 2^-6;
+    0x7f and 0xff are NaN; no infinities), float64."""
+    c = np.asarray(code, dtype=np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 15
+    m = (c & 7).astype(np.float64)
+    v = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * 2.0 ** (e - 7.0))
+    v = np.where((c & 0x7F) == 0x7F, np.nan, v)
+    return sign * v
+
+
+def e4m3_round(v) -> np.ndarray:
+    """Nearest e4m3 value to float64 ``v`` (ties to an even mantissa), saturating at
+    +-448: subnormals are multiples of 2^-9 below 2^-6; a normal binade [2^e, 2^(e+1))
+    has steps of 2^(e-3)."""
+    v = np.asarray(v, dtype=np.float64)
+    a = np.abs(v)
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    step = np.where(a < 2.0 ** -6, 2.0 ** -9, 2.0 ** (np.clip(e, -6, 8) - 3))
+    q = np.rint(a / step) * step          # np.rint rounds halves to even
+    return np.copysign(np.minimum(q, 448.0), v)   # the sign survives rounding to zero
+
+
+_E4M3_VALUES = e4m3_decode(np.arange(0x7F))   # codes 0x00..0x7e, increasing
+
+
+def e4m3_encode(v) -> np.ndarray:
+    """Code (uint8) of e4m3 values (exact members of the format, e.g. e4m3_round's
+    output); -0 encodes as 0x80."""
+    v = np.asarray(v, dtype=np.float64)
+    mag = np.searchsorted(_E4M3_VALUES, np.abs(v))
+    if not np.all(_E4M3_VALUES[np.minimum(mag, 0x7E)] == np.abs(v)):
+        raise ValueError("not an e4m3 value")
+    return (mag | np.where(np.signbit(v), 0x80, 0)).astype(np.uint8)
+
+
+def mx_quantize(x, block: int = 32):
+    """MX quantization of the rows of ``x`` [R, C] (C a multiple of ``block``), with the
+    block scale that lets no value saturate: returns (codes [R, C] uint8 e4m3,
+    scales [R, C/block] uint8 = X + 127)."""
+    v = values64(x)
+    R, C = v.shape
+    b = v.reshape(R, C // block, block)
+    amax = np.abs(b).max(axis=2)
+    # smallest X with amax <= 448 * 2^X: with amax = m * 2^e, 1 <= m < 2, that is e - 8
+    # when m <= 1.75 (448 = 1.75 * 2^8) and e - 7 otherwise
+    safe = np.where(amax > 0, amax, 1.0)
+    e = np.floor(np.log2(safe))
+    m = safe / 2.0 ** e
+    X = np.where(amax > 0, np.where(m <= 1.75, e - 8, e - 7), -127)
+    X = np.clip(X, -127, 127)
+    q = e4m3_round(b / 2.0 ** X[:, :, None])
+    return e4m3_encode(q).reshape(R, C), (X + 127).astype(np.uint8)
+
+
+def mx_dequantize(codes, scales, block: int = 32) -> np.ndarray:
+    """codes [R, C] e4m3, scales [R, C/block] E8M0 -> float64 values."""
+    c = np.asarray(codes)
+    R, C = c.shape
+    X = np.asarray(scales, dtype=np.float64) - 127.0
+    return (e4m3_decode(c).reshape(R, C // block, block) * 2.0 ** X[:, :, None]).reshape(R, C)
+
+
+def expert_fc1_mx(Aq, As, w1q, w1s, w3q, w3s):
+    """h = silu(A w1^T) * (A w3^T) of dequantized MX operands, float64 (rounded by the
+    caller)."""
+    A = mx_dequantize(Aq, As)
+    return silu(A @ mx_dequantize(w1q, w1s).T) * (A @ mx_dequantize(w3q, w3s).T)
+
+
+def grouped_fc1_mx(xq_perm, xs_perm, offsets, w1q, w1s, w3q, w3s):
+    """``expert_fc1_mx`` per segment [offsets[e], offsets[e+1]), stored in bf16; rows past
+    offsets[E] zero."""
+    E = w1q.shape[0]
+    F = w1q.shape[1]
+    h = np.zeros((xq_perm.shape[0], F))
+    for e in range(E):
+        r0, r1 = int(offsets[e]), int(offsets[e + 1])
+        if r1 > r0:
+            h[r0:r1] = round_bf16(expert_fc1_mx(xq_perm[r0:r1], xs_perm[r0:r1], w1q[e], w1s[e],
+                                                w3q[e], w3s[e]))
+    return h
+
+
+def forward_mxfp8(inputs: dict, k: int, m_tile: int, renorm: bool = False) -> dict:
+    """The bf16 layer with an FP8 payload: route on the bf16 x, quantize x per token (MX
+    e4m3), permute codes and scales, fc1 on the dequantized payload and MX-quantized
+    w1, w3, then fc2, shared experts and combine in bf16."""
+    x = inputs["x"]
+    E, F, D = inputs["w1"].shape
+    res: dict = {}
+    if "topk_idx" in inputs:
+        idx = np.asarray(inputs["topk_idx"], dtype=np.int32)
+        w = np.asarray(inputs["topk_w"], dtype=np.float64)
+    else:
+        idx, w, logits = route(x, inputs["wg"], k, "bf16", inputs.get("bias"), renorm)
+        res["logits"] = logits
+    res["topk_idx"], res["topk_w"] = idx, w
+    lay = dispatch_layout(idx, E, m_tile)
+    res.update(lay)
+    xq, xs = mx_quantize(x)
+    res["xq"], res["xs"] = xq, xs
+    res["xq_perm"], res["xs_perm"] = permute(xq, lay), permute(xs, lay)
+    wq = {n: [mx_quantize(inputs[n][e]) for e in range(E)] for n in ("w1", "w3")}
+    w1q = np.stack([q for q, _ in wq["w1"]]); w1s = np.stack([s_ for _, s_ in wq["w1"]])
+    w3q = np.stack([q for q, _ in wq["w3"]]); w3s = np.stack([s_ for _, s_ in wq["w3"]])
+    res.update(w1q=w1q, w1s=w1s, w3q=w3q, w3s=w3s)
+    h = grouped_fc1_mx(res["xq_perm"], res["xs_perm"], lay["offsets"], w1q, w1s, w3q, w3s)
+    y = np.zeros((h.shape[0], D))
+    for e in range(E):
+        r0, r1 = int(lay["offsets"][e]), int(lay["offsets"][e + 1])
+        if r1 > r0:
+            y[r0:r1] = round_bf16(h[r0:r1] @ values64(inputs["w2"][e]).T)
+    res["h"], res["y_perm"] = h, y
+    shared = None
+    if "ws1" in inputs:
+        shared = shared_experts(x, inputs["ws1"], inputs["ws3"], inputs["ws2"], "bf16")
+        res["shared"] = shared
+    res["out"] = combine(y, lay["dst_row"], w, "bf16", shared)
     return res

@@ -123,7 +123,28 @@ def _masked_offsets_by_count(topk_idx, E, cap):
     return lay
 
 
+def _e4m3_truncating(v):
+    v = np.asarray(v, dtype=np.float64)
+    a = np.abs(v)
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    step = np.where(a < 2.0 ** -6, 2.0 ** -9, 2.0 ** (np.clip(e, -6, 8) - 3))
+    return np.copysign(np.minimum(np.floor(a / step) * step, 448.0), v)   # rounds toward zero
+
+
+def _mx_floor_scale(x, block=32):
+    # the scale 2^(floor(log2 amax) - 8): the largest values of a block saturate
+    v = orc.values64(x)
+    R, C = v.shape
+    b = v.reshape(R, C // block, block)
+    amax = np.abs(b).max(axis=2)
+    X = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - 8, -127)
+    q = orc.e4m3_round(np.clip(b / 2.0 ** X[:, :, None], -448, 448))
+    return orc.e4m3_encode(q).reshape(R, C), (X + 127).astype(np.uint8)
+
+
 MUTATIONS = {
+    "e4m3_truncating": ("e4m3_round", _e4m3_truncating, "fp8"),
+    "mx_floor_scale": ("mx_quantize", _mx_floor_scale, "fp8"),
     "masked_keeps_last": ("masked_layout", _masked_keeps_the_last, "masked"),
     "masked_packed": ("masked_layout", _masked_offsets_by_count, "masked"),
     "bwd_silu_grad_term": ("silu_grad", _silu_grad_dropped_term, "autograd"),
@@ -153,6 +174,9 @@ def _run_pin(kind):
         pins.test_topk_matches_python_sorted_with_ties()
     elif kind == "layout":
         pins.test_layout_matches_loop_counting_sort(50, 3, 7, 4, False)
+    elif kind == "fp8":
+        pins.test_e4m3_round_matches_torch_float8_rounding()
+        pins.test_mx_scale_is_the_smallest_power_that_avoids_saturation()
     elif kind == "masked":   # one case with full slabs and drops, one with partly filled slabs
         pins.test_masked_layout_matches_loop_and_contiguous_ranks(33, 3, 4, 8)
         pins.test_masked_layout_matches_loop_and_contiguous_ranks(20, 2, 5, 16)
@@ -170,5 +194,5 @@ def test_planted_mistake_is_caught(name, monkeypatch):
 
 
 def test_unmutated_pins_pass():
-    for kind in ("brute", "brute_bias", "ties", "layout", "autograd", "masked"):
+    for kind in ("brute", "brute_bias", "ties", "layout", "autograd", "masked", "fp8"):
         _run_pin(kind)

@@ -598,3 +598,93 @@ def test_masked_forward_drops_slots_past_capacity_like_brute_force():
                     _py_ffn(inp["x"][t], inp["w1"][e], inp["w3"][e], inp["w2"][e]))
             seen[e] += 1
     np.testing.assert_allclose(res["out"], ref, rtol=0, atol=1e-5 * np.abs(ref).max())
+
+
+# ---------------------------------------------------------------------------
+# FP8 (e4m3) payload with MX block scales
+# ---------------------------------------------------------------------------
+
+def test_e4m3_decode_matches_torch_float8_for_every_code():
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = orc.e4m3_decode(codes)
+    np.testing.assert_array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    np.testing.assert_array_equal(got[ok], ref[ok])
+    np.testing.assert_array_equal(np.signbit(got[ok]), np.signbit(ref[ok]))
+    assert got[0x38] == 1.0 and got[0x7E] == 448.0 and got[0x01] == 2.0 ** -9
+
+
+def test_e4m3_round_matches_torch_float8_rounding():
+    rng = np.random.default_rng(71)
+    v = np.concatenate([rng.standard_normal(20000) * 10.0 ** rng.uniform(-4, 2.3, 20000),
+                        # exact halfway points between neighbouring codes (ties to even)
+                        (orc.e4m3_decode(np.arange(0, 0x7E)) + orc.e4m3_decode(np.arange(1, 0x7F))) / 2,
+                        [0.0, -0.0, 448.0, -448.0, 2.0 ** -10, 2.0 ** -6]])
+    v = v[np.abs(v) <= 448.0]
+    ref = torch.from_numpy(v).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+    np.testing.assert_array_equal(orc.e4m3_round(v), ref)
+    codes = orc.e4m3_encode(orc.e4m3_round(v))
+    np.testing.assert_array_equal(codes, torch.from_numpy(v).to(torch.float8_e4m3fn)
+                                  .view(torch.uint8).numpy())
+
+
+def test_mx_scale_is_the_smallest_power_that_avoids_saturation():
+    rng = np.random.default_rng(72)
+    x = (rng.standard_normal((40, 96)) * 10.0 ** rng.uniform(-6, 6, (40, 1))).astype(np.float32)
+    x[3] = 0.0                                   # an all-zero row: every block zero
+    x[5, :32] = 448.0                            # exactly at the limit: scale 2^0
+    x[6, 32:64] = 449.0                          # just above: scale 2^1
+    q, s = orc.mx_quantize(x)
+    for r in range(40):
+        for b in range(3):
+            blk = x[r, 32 * b:32 * b + 32].astype(np.float64)
+            amax = np.abs(blk).max()
+            if amax == 0:
+                assert s[r, b] == 0 and not np.any(q[r, 32 * b:32 * b + 32] & 0x7F)
+                continue
+            X = -127
+            while amax > 448.0 * 2.0 ** X:        # plain search for the smallest X
+                X += 1
+            assert s[r, b] == X + 127, (r, b)
+            ref = torch.from_numpy(blk / 2.0 ** X).to(torch.float8_e4m3fn).view(torch.uint8)
+            np.testing.assert_array_equal(q[r, 32 * b:32 * b + 32], ref.numpy())
+    assert s[5, 0] == 127 and s[6, 1] == 128
+    d = orc.mx_dequantize(q, s)
+    # relative error of e4m3 rounding: at most 2^-4 where the scaled value is normal
+    scaled = np.abs(x.astype(np.float64)) / 2.0 ** (np.repeat(s, 32, axis=1) - 127.0)
+    normal = scaled >= 2.0 ** -6
+    assert np.all(np.abs(d - x)[normal] <= 2.0 ** -4 * np.abs(x[normal]))
+
+
+def test_mx_fc1_equals_the_swiglu_of_the_dequantized_operands():
+    rng = np.random.default_rng(73)
+    A = rng.standard_normal((9, 64)).astype(np.float32)
+    w1 = (rng.standard_normal((12, 64)) / 8).astype(np.float32)
+    w3 = (rng.standard_normal((12, 64)) / 8).astype(np.float32)
+    (aq, as_), (q1, s1), (q3, s3) = orc.mx_quantize(A), orc.mx_quantize(w1), orc.mx_quantize(w3)
+    got = orc.expert_fc1_mx(aq, as_, q1, s1, q3, s3)
+    Ad = torch.from_numpy(orc.mx_dequantize(aq, as_))
+    ref = (torch.nn.functional.silu(Ad @ torch.from_numpy(orc.mx_dequantize(q1, s1)).T)
+           * (Ad @ torch.from_numpy(orc.mx_dequantize(q3, s3)).T)).numpy()
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_mx_forward_equals_bf16_forward_on_exactly_representable_inputs():
+    # inputs that are e4m3 values times one power of two per 32-block quantize exactly,
+    # so the FP8 path must reproduce the bf16 layer bit for bit
+    rng = np.random.default_rng(74)
+    T, D, F, E, k = 20, 64, 32, 4, 2
+    pick = lambda shape, p: orc.e4m3_decode(rng.integers(0, 0x70, size=shape)) * \
+        np.where(rng.random(shape) < 0.5, -1, 1) * 2.0 ** p
+    inp = {"x": pick((T, D), -4).astype(np.float32),
+           "wg": (rng.standard_normal((E, D)) / 8).astype(np.float32),
+           "w1": pick((E, F, D), -9).astype(np.float32), "w3": pick((E, F, D), -9).astype(np.float32),
+           "w2": (rng.standard_normal((E, D, F)) / 8).astype(np.float32)}
+    for n in inp:   # every value above is also a bf16 value; round the rest to bf16
+        inp[n] = orc.round_bf16(inp[n]).astype(np.float32)
+    a = orc.forward(inp, k=k, m_tile=16, dtype="bf16")
+    b = orc.forward_mxfp8(inp, k=k, m_tile=16)
+    np.testing.assert_array_equal(orc.mx_dequantize(b["xq"], b["xs"]), inp["x"])
+    np.testing.assert_array_equal(a["h"], b["h"])
+    np.testing.assert_array_equal(a["out"], b["out"])
