@@ -46,6 +46,9 @@ def parse():
     ap.add_argument("--workload", default="dense8_bf16")
     ap.add_argument("--cpu-sample-tokens", type=int, default=4096)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--fp8", action="store_true",
+                    help="also time the layer with the FP8 (e4m3, MX-scaled) payload "
+                         "(reported under \"fp8_payload\")")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the timed backward pass (reported under \"backward\")")
     ap.add_argument("--no-split-k", action="store_true",
@@ -318,6 +321,8 @@ def main():
     }
     if not args.no_backward:
         rec["backward"] = bench_backward(args, cfg, d, buf, shared, gws, flush, n_valid)
+    if args.fp8:
+        rec["fp8_payload"] = bench_fp8(args, cfg, d, buf, shared, gws, flush, n_valid)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(inp, cfg, min(args.cpu_sample_tokens, T))
     print(json.dumps(rec), flush=True)
@@ -451,6 +456,96 @@ def bench_masked(args, cfg, d, inp) -> dict:
         "assignments": n_valid, "active_experts": active,
         "expert_rows_min_max": [int(counts.min()), int(counts.max())],
         "cpu_baseline": None,
+    }
+
+
+PEAK_FP8_TFLOPS = 5033.2     # MI355X dense fp8 MFMA (AMD spec)
+
+
+def bench_fp8(args, cfg, d, buf, shared, gws, flush, n_valid) -> dict:
+    """The same step with the FP8 payload: route -> MX-quantize x -> permute codes and
+    scales -> fc1 on the scaled-FP8 MFMA -> fc2 (bf16) [-> shared experts] -> combine.
+    w1 and w3 are quantized once, outside the timed steps. Also reports how far its output
+    lies from the bf16 step's."""
+    import torch
+
+    import routing_permute_grouped_amd as rpg
+
+    T, D, F, E, k, mt = cfg.T, cfg.D, cfg.F, cfg.E, cfg.k, cfg.m_tile
+    dev = d["x"].device
+    stream = torch.cuda.current_stream()
+    m_cap = buf["x_perm"].shape[0]
+    mw = rpg.MxWeights.quantize(d["w1"], d["w3"])
+    u8 = dict(dtype=torch.uint8, device=dev)
+    fb = {"xq": torch.empty((T, D), **u8), "xs": torch.empty((T, D // 32), **u8),
+          "xq_perm": torch.empty((m_cap, D), **u8), "xs_perm": torch.empty((m_cap, D // 32), **u8),
+          "out": torch.empty_like(buf["out"])}
+    for n in ("counts", "offsets", "dst_row", "src_row", "tile_expert", "dev_err", "workspace"):
+        fb[n] = torch.empty_like(buf[n])
+    marks = ["route", "quantize", "permute", "fc1", "fc2", "shared", "combine"]
+    routed = "wg" in d
+
+    def step(ev=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record(stream)
+        mark(0)
+        if routed:
+            rpg.moe_route(d["x"], d["wg"], k, bias=d.get("bias"), topk_idx=buf["idx"],
+                          topk_w=buf["w"], stream=stream)
+        mark(1)
+        rpg.moe_quantize_mxfp8(d["x"], q=fb["xq"], scales=fb["xs"], stream=stream)
+        mark(2)
+        rpg.moe_permute_mxfp8(fb["xq"], fb["xs"], buf["idx"], E, mt, m_cap=m_cap, out=fb,
+                              stream=stream)
+        mark(3)
+        rpg.moe_grouped_fc1_swiglu_mxfp8(fb["xq_perm"], fb["xs_perm"], fb["offsets"],
+                                         fb["tile_expert"], mw.w1q, mw.w1s, mw.w3q, mw.w3s, mt,
+                                         m_cap, h=buf["h"], workspace=gws, stream=stream)
+        mark(4)
+        rpg.moe_grouped_fc2(buf["h"], fb["offsets"], fb["tile_expert"], d["w2"], mt, m_cap,
+                            buf["y"], workspace=gws, stream=stream)
+        mark(5)
+        sh = None
+        if shared is not None:
+            rows = rpg.DenseRows(T, mt, dev)
+            rpg.moe_grouped_swiglu(d["x"], rows.offsets, rows.tile_expert, shared.w1, shared.w3,
+                                   shared.w2, mt, m_cap=rows.m_cap, h=buf["hs"],
+                                   y_perm=buf["ys"], workspace=gws, stream=stream)
+            sh = buf["ys"][:T]
+        mark(6)
+        rpg.moe_combine(buf["y"], fb["dst_row"], buf["w"], shared=sh, out=fb["out"],
+                        m_cap=m_cap, stream=stream)
+        mark(7)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(marks) + 1)]
+              for _ in range(args.steps)]
+    for s_ in range(args.steps):
+        if flush is not None:
+            flush.fill_(float(s_))
+        step(events[s_])
+    torch.cuda.synchronize()
+    per = {m: [events[s_][i].elapsed_time(events[s_][i + 1]) * 1e3 for s_ in range(args.steps)]
+           for i, m in enumerate(marks)}
+    per["step"] = [events[s_][0].elapsed_time(events[s_][-1]) * 1e3 for s_ in range(args.steps)]
+    avg = {m: statistics.fmean(v) for m, v in per.items()}
+    fc1_flop = 4.0 * n_valid * D * F
+    fc1_tf = fc1_flop / (avg["fc1"] * 1e-6) / 1e12
+    ref = buf["out"].float()
+    dev_out = (fb["out"].float() - ref).abs().max().item() / ref.abs().max().item()
+    return {
+        "tokens_per_s": T / (avg["step"] * 1e-6), "ms_per_step": avg["step"] * 1e-3,
+        "fc1": {"kernel": "grouped fc1 + silu(a)*b on MX e4m3 (gg_bf16_kernel<kFc1, MX>)",
+                "achieved_tflops": fc1_tf, "peak_fp8_tflops": PEAK_FP8_TFLOPS,
+                "frac_fp8_peak": fc1_tf / PEAK_FP8_TFLOPS,
+                "frac_bf16_peak": fc1_tf / PEAK_BF16_TFLOPS},
+        "stage_us_mean": avg,
+        "out_rel_diff_vs_bf16_step": dev_out,
+        "note": "x quantized per token (32-value blocks, power-of-two scales, no saturation); "
+                "w1, w3 quantized once; fc2, shared experts and combine in bf16",
     }
 
 

@@ -11,7 +11,9 @@
  *   moe_combine         unpermute and top-k-weighted reduce back to token order
  *
  * For decode, moe_permute_masked and moe_grouped_swiglu_masked replace the middle
- * two calls with fixed-capacity per-expert slabs (the masked layout).
+ * two calls with fixed-capacity per-expert slabs (the masked layout). With an FP8
+ * payload, moe_quantize_mxfp8, moe_permute_mxfp8 and moe_grouped_fc1_swiglu_mxfp8
+ * replace the permute and fc1.
  *
  * and its backward ("Expert Parallelism (EP)", section 5: each forward operator
  * has a mirror; permute <-> unpermute, dispatch <-> combine, an m-grouped fc <->
@@ -216,6 +218,44 @@ moe_status_t moe_grouped_fc2(moe_dtype_t dt, const void* h, const int32_t* offse
                              const int32_t* tile_expert, int E, int D, int F, int m_tile,
                              int64_t m_cap, const void* w2, void* y_perm, void* workspace,
                              size_t ws_bytes, void* stream);
+
+/*
+ * FP8 payload ("Expert Parallelism (EP)", section 3: dispatch in FP8 e4m3 "plus scale",
+ * combine in BF16). The token rows travel through the permute and fc1 as OCP E4M3 codes
+ * (bias 7, no infinities, largest value 448) with MX block scales: one power-of-two
+ * scale 2^X per 32 consecutive values of a row, stored as the byte X + 127 (E8M0). X is
+ * the smallest integer with max|v| <= 448 * 2^X over the block (no value saturates),
+ * -127 for an all-zero block; each code is v / 2^X rounded to the nearest e4m3 value,
+ * ties to even. fc1 multiplies on the scaled-FP8 MFMA with float32 accumulation and
+ * writes h in bf16; fc2 and the combine are the bf16 calls above.
+ *
+ * moe_quantize_mxfp8: x [R,C] (dt) -> q [R,C] uint8 codes, scales [R,C/32] uint8.
+ *   C a multiple of 32 (<= 65536). Used for the token rows before the permute and,
+ *   once, for w1 and w3 ([E*F, D] rows).
+ * moe_permute_mxfp8: moe_permute's metadata (same outputs, same rules) and the rows of
+ *   xq [T,D] and xs [T,D/32] copied to xq_perm [m_cap,D], xs_perm [m_cap,D/32]; pad rows
+ *   get zero bytes (the value 0). D a multiple of 512.
+ * moe_grouped_fc1_swiglu_mxfp8: h [m_cap,F] (bf16) = silu(a)*b with a, b the float32
+ *   products of the dequantized rows and w1q/w1s, w3q/w3s ([E,F,D] codes, [E,F,D/32]
+ *   scales), per segment as moe_grouped_fc1_swiglu (workspace likewise). D a multiple of
+ *   128; m_tile 128 or 256.
+ * Errors: MOE_EINVAL, MOE_ESHAPE, MOE_ECAPACITY, MOE_EWORKSPACE, MOE_EUNSUPPORTED,
+ * MOE_EHIP.
+ */
+moe_status_t moe_quantize_mxfp8(moe_dtype_t dt, const void* x, int64_t R, int C, void* q,
+                                void* scales, void* stream);
+moe_status_t moe_permute_mxfp8(const void* xq, const void* xs, const int32_t* topk_idx,
+                               int T, int D, int E, int k, int m_tile, int64_t m_cap,
+                               void* xq_perm, void* xs_perm, int32_t* counts, int32_t* offsets,
+                               int32_t* dst_row, int32_t* src_row, int32_t* tile_expert,
+                               void* workspace, size_t ws_bytes, int32_t* dev_err,
+                               void* stream);
+moe_status_t moe_grouped_fc1_swiglu_mxfp8(const void* xq_perm, const void* xs_perm,
+                                          const int32_t* offsets, const int32_t* tile_expert,
+                                          int E, int D, int F, int m_tile, int64_t m_cap,
+                                          const void* w1q, const void* w1s, const void* w3q,
+                                          const void* w3s, void* h, void* workspace,
+                                          size_t ws_bytes, void* stream);
 
 /*
  * moe_combine - unpermute and weighted reduce ("Expert Parallelism (EP)",

@@ -102,7 +102,7 @@ __all__ = [
     "backward", "token_backward", "expert_weight_grad_slices",
     "masked_layout", "masked_swiglu", "forward_masked",
     "e4m3_decode", "e4m3_round", "e4m3_encode", "mx_quantize", "mx_dequantize",
-    "expert_fc1_mx", "grouped_fc1_mx", "forward_mxfp8",
+    "expert_fc1_mx", "grouped_fc1_mx", "forward_mxfp8", "token_outputs_mx",
 ]
 
 _LANES = 64  # width of one reduction group in the fixed logit order
@@ -840,3 +840,26 @@ def forward_mxfp8(inputs: dict, k: int, m_tile: int, renorm: bool = False) -> di
         res["shared"] = shared
     res["out"] = combine(y, lay["dst_row"], w, "bf16", shared)
     return res
+
+
+def token_outputs_mx(tokens, x, topk_idx, topk_w, w1, w3, w2, shared_w=None):
+    """Layer output of selected tokens on the FP8 payload, one expert at a time: a row's
+    quantization and fc1 depend on that row alone, and only the experts the tokens use
+    have their w1, w3 quantized. Returns out [n, D] (bf16 values)."""
+    tokens = np.asarray(tokens, dtype=np.int64)
+    idx = np.asarray(topk_idx, dtype=np.int64)
+    w = np.asarray(topk_w, dtype=np.float64)
+    xq, xs = mx_quantize(x[tokens])
+    out = np.zeros((tokens.size, x.shape[1]))
+    for e in np.unique(idx[tokens]):
+        if e < 0:
+            continue
+        sel = [(i, j) for i, t in enumerate(tokens) for j in range(idx.shape[1]) if idx[t, j] == e]
+        rows = [i for i, _ in sel]
+        h = round_bf16(expert_fc1_mx(xq[rows], xs[rows], *mx_quantize(w1[e]), *mx_quantize(w3[e])))
+        y = round_bf16(h @ values64(w2[e]).T)
+        for r, (i, j) in enumerate(sel):
+            out[i] += w[tokens[i], j] * y[r]
+    if shared_w is not None:
+        out += shared_experts(x[tokens], *shared_w, "bf16")
+    return round_bf16(out)

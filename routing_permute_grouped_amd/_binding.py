@@ -32,6 +32,11 @@ SIGNATURES = [
                                     _SZ, _P]),
     ("moe_grouped_fc2", _I, [_I, _P, _P, _P, _I, _I, _I, _I, _I64, _P, _P, _P, _SZ, _P]),
     ("moe_combine", _I, [_I, _P, _P, _P, _P, _I, _I, _I, _I64, _P, _P]),
+    ("moe_quantize_mxfp8", _I, [_I, _P, _I64, _I, _P, _P, _P]),
+    ("moe_permute_mxfp8", _I, [_P, _P, _P, _I, _I, _I, _I, _I, _I64, _P, _P, _P, _P, _P, _P, _P, _P,
+                               _SZ, _P, _P]),
+    ("moe_grouped_fc1_swiglu_mxfp8", _I, [_P, _P, _P, _P, _I, _I, _I, _I, _I64, _P, _P, _P, _P, _P,
+                                          _P, _SZ, _P]),
     ("moe_permute_masked", _I, [_I, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _SZ, _P, _P]),
     ("moe_grouped_swiglu_masked", _I, [_I, _P, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _SZ,
                                        _P]),
@@ -348,3 +353,74 @@ def moe_grouped_swiglu_masked(x_masked: torch.Tensor, counts: torch.Tensor, w1: 
         _dt(x_masked), _ptr(x_masked), _ptr(counts), E, D, F, cap, _ptr(w1), _ptr(w3), _ptr(w2),
         _ptr(h), _ptr(y), *_ws(workspace), _stream(stream)))
     return h, y
+
+
+def _bytes_ptr(t: torch.Tensor) -> int:
+    if t.dtype != torch.uint8:
+        raise TypeError("FP8 codes and scales are uint8 tensors")
+    return _ptr(t)
+
+
+def moe_quantize_mxfp8(x: torch.Tensor, q: Optional[torch.Tensor] = None,
+                       scales: Optional[torch.Tensor] = None, stream=None):
+    """MX e4m3 codes and E8M0 scales of the rows of x [..., C] (C a multiple of 32).
+    Returns (q uint8 [..., C], scales uint8 [..., C/32])."""
+    C = x.shape[-1]
+    R = x.numel() // C
+    if q is None:
+        q = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((*x.shape[:-1], C // 32), dtype=torch.uint8, device=x.device)
+    _check("moe_quantize_mxfp8", lib.moe_quantize_mxfp8(
+        _dt(x), _ptr(x), R, C, _bytes_ptr(q), _bytes_ptr(scales), _stream(stream)))
+    return q, scales
+
+
+def moe_permute_mxfp8(xq: torch.Tensor, xs: torch.Tensor, topk_idx: torch.Tensor, E: int,
+                      m_tile: int, m_cap: Optional[int] = None, out: Optional[dict] = None,
+                      stream=None) -> dict:
+    """moe_permute for the FP8 payload: dict with xq_perm, xs_perm and the metadata."""
+    T, D = xq.shape
+    k = topk_idx.shape[1]
+    dev = xq.device
+    if m_cap is None:
+        m_cap = moe_capacity(T, k, E, m_tile)
+    o = dict(out or {})
+    i32 = dict(dtype=torch.int32, device=dev)
+    o.setdefault("xq_perm", torch.empty((m_cap, D), dtype=torch.uint8, device=dev))
+    o.setdefault("xs_perm", torch.empty((m_cap, D // 32), dtype=torch.uint8, device=dev))
+    o.setdefault("counts", torch.empty(E, **i32))
+    o.setdefault("offsets", torch.empty(E + 1, **i32))
+    o.setdefault("dst_row", torch.empty((T, k), **i32))
+    o.setdefault("src_row", torch.empty(m_cap, **i32))
+    o.setdefault("tile_expert", torch.empty(m_cap // m_tile, **i32))
+    o.setdefault("dev_err", torch.empty(1, **i32))
+    ws = max(4, moe_permute_workspace_bytes(T, k, E))
+    o.setdefault("workspace", torch.empty(ws, dtype=torch.uint8, device=dev))
+    _check("moe_permute_mxfp8", lib.moe_permute_mxfp8(
+        _bytes_ptr(xq), _bytes_ptr(xs), _ptr(topk_idx), T, D, E, k, m_tile, m_cap,
+        _bytes_ptr(o["xq_perm"]), _bytes_ptr(o["xs_perm"]), _ptr(o["counts"]), _ptr(o["offsets"]),
+        _ptr(o["dst_row"]), _ptr(o["src_row"]), _ptr(o["tile_expert"]), _ptr(o["workspace"]),
+        o["workspace"].numel(), _ptr(o["dev_err"]), _stream(stream)))
+    o["m_cap"] = m_cap
+    return o
+
+
+def moe_grouped_fc1_swiglu_mxfp8(xq_perm: torch.Tensor, xs_perm: torch.Tensor,
+                                 offsets: torch.Tensor, tile_expert: torch.Tensor,
+                                 w1q: torch.Tensor, w1s: torch.Tensor, w3q: torch.Tensor,
+                                 w3s: torch.Tensor, m_tile: int, m_cap: Optional[int] = None,
+                                 h: Optional[torch.Tensor] = None,
+                                 workspace: Optional[torch.Tensor] = None,
+                                 stream=None) -> torch.Tensor:
+    """h [m_cap, F] bf16 = silu(a)*b from the FP8 payload and MX-quantized w1, w3."""
+    E, F, D = w1q.shape
+    if m_cap is None:
+        m_cap = xq_perm.shape[0]
+    if h is None:
+        h = torch.empty((m_cap, F), dtype=torch.bfloat16, device=xq_perm.device)
+    _check("moe_grouped_fc1_swiglu_mxfp8", lib.moe_grouped_fc1_swiglu_mxfp8(
+        _bytes_ptr(xq_perm), _bytes_ptr(xs_perm), _ptr(offsets), _ptr(tile_expert), E, D, F,
+        m_tile, m_cap, _bytes_ptr(w1q), _bytes_ptr(w1s), _bytes_ptr(w3q), _bytes_ptr(w3s), _ptr(h),
+        *_ws(workspace), _stream(stream)))
+    return h

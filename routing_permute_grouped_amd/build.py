@@ -16,7 +16,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB_NAME = "libmoe_mi355x.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
-SOURCES = ["moe_capi.hip", "route.hip", "permute.hip", "grouped_gemm.hip", "combine.hip"]
+SOURCES = ["moe_capi.hip", "route.hip", "permute.hip", "grouped_gemm.hip", "combine.hip",
+           "quantize.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -216,7 +216,9 @@ __device__ __forceinline__ uint32_t mn_off(int j, int ld) {
 //   P_MN false: W1 [E][N][K] (fc1 interleaves W1 and W3 rows in 32-row blocks);
 //   P_MN true:  [E][K][N] read MN-major, the first `ksplit` k from W1 [E][ksplit][N] and
 //               the rest from W3 [E][K - ksplit][N] (ksplit = K: W1 only).
-template <bool FC1, bool P_MN>
+// EB: bytes per element (2: bf16; 1: the FP8 payload, whose 64-wide k-steps hold 128
+// k values in the same 128-byte LDS rows).
+template <bool FC1, bool P_MN, int EB = 2>
 __device__ __forceinline__ TileLoads tile_loads(const Tile& t, const bf16_t* __restrict__ A,
                                                 const bf16_t* __restrict__ W1,
                                                 const bf16_t* __restrict__ W3, int K, int N,
@@ -227,10 +229,11 @@ __device__ __forceinline__ TileLoads tile_loads(const Tile& t, const bf16_t* __r
   const int lchunk = (lane & 7) ^ ((lrow >> 1) & 7);
   TileLoads o;
   o.na = t.rows > BM / 2 ? 4 : 2;
+  const char* Ab = reinterpret_cast<const char*>(A);
 #pragma unroll
   for (int j = 0; j < 4; ++j)
-    o.aoff[j] = (uint32_t)(min(64 * j + lrow, t.rows - 1) * K + lchunk * 8) * 2u;
-  o.rsa = buffer_rsrc(A + (size_t)t.m0 * K, (uint32_t)t.rows * K * 2u);
+    o.aoff[j] = (uint32_t)(min(64 * j + lrow, t.rows - 1) * K) * EB + lchunk * 16;
+  o.rsa = buffer_rsrc(Ab + (size_t)t.m0 * K * EB, (uint32_t)t.rows * K * EB);
   o.astep = BK * 2;
   if (P_MN) {
     // columns past N read into the next row (or past the end, zero-filled): such panel
@@ -246,14 +249,14 @@ __device__ __forceinline__ TileLoads tile_loads(const Tile& t, const bf16_t* __r
   } else {
     // fc1: panel rows alternate 32-row blocks of w1 and w3 over the same 32 columns;
     // row 64*j + lrow is in a w3 block exactly when lrow >= 32, i.e. for waves 4..7
-    const bf16_t* wsel = (FC1 && wave >= 4) ? W3 : W1;
-    o.rsb = buffer_rsrc(wsel + (size_t)t.e * N * K, (uint32_t)N * K * 2u);
+    const char* wsel = reinterpret_cast<const char*>((FC1 && wave >= 4) ? W3 : W1);
+    o.rsb = buffer_rsrc(wsel + (size_t)t.e * N * K * EB, (uint32_t)N * K * EB);
     o.rsb2 = o.rsb;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int pr = 64 * j + lrow;
       const int gr = FC1 ? t.n0 + (pr >> 6) * 32 + (pr & 31) : t.n0 + pr;
-      o.boff[j] = (uint32_t)(min(gr, N - 1) * K + lchunk * 8) * 2u;
+      o.boff[j] = (uint32_t)(min(gr, N - 1) * K) * EB + lchunk * 16;
     }
     o.bstep = BK * 2;
     o.bsplit = 1 << 30;
@@ -389,6 +392,12 @@ __device__ __forceinline__ void mainloop(char* smem, const TileLoads& ld, int kb
   // first barrier, which every wave reaches after finishing this tile's MFMAs.
 }
 
+// Barrier for LDS traffic only: this wave's LDS accesses are complete, then every wave
+// meets; outstanding global loads (the next tile's first stage) keep flying.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // kDgrad epilogue through LDS. The lane layout of the accumulators (4 consecutive
 // columns of 32 different rows per instruction) would make the ab loads and dab stores
 // touch 32 rows x 8 bytes per wave instruction; instead dh (rounded to bf16, as stored)
@@ -398,12 +407,6 @@ __device__ __forceinline__ void mainloop(char* smem, const TileLoads& ld, int kb
 // LDS rows are 512 bytes; the 8-byte unit u of row r is stored at u ^ (r % 32), so the
 // 32 rows a half-wave writes hit 32 distinct bank pairs, and a 16-byte row read lands
 // on chunk c ^ ((r % 32) / 2) with its halves swapped when r is odd.
-// Barrier for LDS traffic only: this wave's LDS accesses are complete, then every wave
-// meets; outstanding global loads (the next tile's first stage) keep flying.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
 template <bool HALF>
 __device__ __forceinline__ void dgrad_epilogue(char* stage, const Tile& t, const Epi& ep,
                                                const f32x16 (&acc)[HALF ? 2 : 4][2]) {
@@ -497,15 +500,13 @@ __device__ __forceinline__ void dgrad_epilogue(char* stage, const Tile& t, const
   }
 }
 
-// One tile of the m-grouped kernel: the main loop, then either the raw float32 sums of
-// a split-K share (`part`, row-major [BM][BP]) or the MODE epilogue.
-// After the main loop lane l holds column m = l % 32 of every 32x32 block and panel rows
-// 8*g + 4*(l / 32) + i (i = 0..3) for g = 0..3.
-template <int MODE, bool HALF, bool P_MN>
-__device__ __forceinline__ void run_tile(char* smem, const Tile& t, const TileLoads& ld,
-                                         const Epi& ep, int kb, int ke,
-                                         float* __restrict__ part, int stage0, bool primed,
-                                         const TileLoads& nxt, bool has_next, int nkb) {
+// The end of a tile: the raw float32 sums of a split-K share (`part`, row-major
+// [BM][BP]) or the MODE epilogue. Lane l holds column m = l % 32 of every 32x32 block
+// and panel rows 8*g + 4*(l / 32) + i (i = 0..3) for g = 0..3.
+template <int MODE, bool HALF>
+__device__ __forceinline__ void finish_tile(char* smem, const Tile& t, const Epi& ep, int kb,
+                                            int ke, float* __restrict__ part, int stage0,
+                                            const f32x16 (&acc)[HALF ? 2 : 4][2]) {
   constexpr int WM = HALF ? 2 : 4;
   constexpr int WN = 2;
   const int lane = threadIdx.x & 63;
@@ -513,9 +514,6 @@ __device__ __forceinline__ void run_tile(char* smem, const Tile& t, const TileLo
   const int arow0 = (wave & 1) * (HALF ? 64 : 128);
   const int prow0 = (wave >> 1) * 64;
   const int fr = lane & 31;
-  f32x16 acc[WM][WN];
-  mainloop<HALF, false, P_MN>(smem, ld, kb, ke, stage0, primed, nxt, has_next, nkb, acc);
-
   if (part) {
 #pragma unroll
     for (int mb = 0; mb < WM; ++mb) {
@@ -567,6 +565,149 @@ __device__ __forceinline__ void run_tile(char* smem, const Tile& t, const TileLo
       }
     }
   }
+}
+
+// One tile of the m-grouped kernel: the main loop, then finish_tile.
+template <int MODE, bool HALF, bool P_MN>
+__device__ __forceinline__ void run_tile(char* smem, const Tile& t, const TileLoads& ld,
+                                         const Epi& ep, int kb, int ke,
+                                         float* __restrict__ part, int stage0, bool primed,
+                                         const TileLoads& nxt, bool has_next, int nkb) {
+  f32x16 acc[HALF ? 2 : 4][2];
+  mainloop<HALF, false, P_MN>(smem, ld, kb, ke, stage0, primed, nxt, has_next, nkb, acc);
+  finish_tile<MODE, HALF>(smem, t, ep, kb, ke, part, stage0, acc);
+}
+
+// ---------------------------------------------------------------------------
+// fc1 on the FP8 payload ("Expert Parallelism (EP)", section 3: dispatch in FP8 e4m3
+// with scales): activations and w1, w3 in OCP e4m3 with one E8M0 scale per 32 values
+// along K, on v_mfma_scale_f32_32x32x64_f8f6f4. A k-step holds 128 k (128-byte LDS
+// rows, the bf16 kernel's stage layout); each of its two 64-wide slices is one scaled
+// MFMA per block. In that instruction lane l supplies row (or column) l % 32 and 32 of
+// the slice's 64 k values as two 16-byte halves, and one scale byte: the first halves
+// of lanes l and l + 32 form one 32-value scale block, scaled by lane l's byte, the
+// second halves the other, scaled by lane l + 32's (the pairing of k values between the
+// two operands follows the same placement, so any consistent order contracts right;
+// checked on the device with in-bounds probes before this kernel used them).
+// ---------------------------------------------------------------------------
+typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
+
+struct MxScales {
+  const uint8_t* a;    // [rows][K/32] E8M0 scales of the activation rows
+  const uint8_t* w1;   // [E][N][K/32]
+  const uint8_t* w3;
+};
+
+// This wave's scale dwords for k-step kt (the 4 block scales of a row's 128 k values):
+// its A rows and its two panel blocks (w1 rows, then w3 rows, of the same columns).
+template <bool HALF>
+__device__ __forceinline__ void mx_scale_words(const Tile& t, const MxScales& ms, int K, int N,
+                                               int kt, uint32_t (&sa)[HALF ? 2 : 4],
+                                               uint32_t (&sw)[2]) {
+  constexpr int WM = HALF ? 2 : 4;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int arow0 = (wave & 1) * (HALF ? 64 : 128);
+  const int prow0 = (wave >> 1) * 64;
+  const int fr = lane & 31;
+  const int kb = K / 32;
+#pragma unroll
+  for (int mb = 0; mb < WM; ++mb) {
+    const int r = min(arow0 + mb * 32 + fr, t.rows - 1);
+    sa[mb] = *reinterpret_cast<const uint32_t*>(ms.a + (size_t)(t.m0 + r) * kb + 4 * kt);
+  }
+  const int n = min(t.n0 + prow0 / 2 + fr, N - 1);
+  sw[0] = *reinterpret_cast<const uint32_t*>(ms.w1 + ((size_t)t.e * N + n) * kb + 4 * kt);
+  sw[1] = *reinterpret_cast<const uint32_t*>(ms.w3 + ((size_t)t.e * N + n) * kb + 4 * kt);
+}
+
+// The bf16 main loop's pipeline (same stages, barrier, split issue and cross-tile
+// prefetch) with FP8 fragments and scaled MFMAs.
+template <bool HALF>
+__device__ __forceinline__ void mainloop_mx(char* smem, const TileLoads& ld, int kb, int ke,
+                                            int stage0, bool primed, const TileLoads& nxt,
+                                            bool has_next, int nkb, const Tile& t,
+                                            const MxScales& ms, int K, int N,
+                                            f32x16 (&acc)[HALF ? 2 : 4][2]) {
+  constexpr int WM = HALF ? 2 : 4;
+  constexpr int WN = 2;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int arow0 = (wave & 1) * (HALF ? 64 : 128);
+  const int prow0 = (wave >> 1) * 64;
+  const int fr = lane & 31;
+  const int half = lane >> 5;
+  const uint32_t lds0 = lds_addr(smem) + wave * 1024;
+#pragma unroll
+  for (int i = 0; i < WM; ++i)
+#pragma unroll
+    for (int j = 0; j < WN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+  if (!primed) {
+    issue_loads(ld, lds0 + stage0 * STAGE_BYTES, kb, 0);
+    issue_loads(ld, lds0 + stage0 * STAGE_BYTES, kb, 1);
+  }
+  uint32_t sa[WM], sw[WN];
+  for (int kt = kb; kt < ke; ++kt) {
+    const int cur = (stage0 + kt - kb) & 1;
+    // this step's scales (small, L2-resident): issued before the wait for the stage's
+    // loads, which they join
+    mx_scale_words<HALF>(t, ms, K, N, kt, sa, sw);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    const char* sA = smem + cur * STAGE_BYTES;
+    const char* sB = sA + A_BYTES;
+    // one slice's fragments at a time (8 registers each: double-buffering them would not
+    // fit beside the 128 accumulators); the other wave of the SIMD covers the LDS latency
+    i32x8 wf[WN], af[WM];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      if (kt + 1 < ke) issue_loads(ld, lds0 + (cur ^ 1) * STAGE_BYTES, kt + 1, ks);
+      else if (has_next) issue_loads(nxt, lds0 + (cur ^ 1) * STAGE_BYTES, nkb, ks);
+      // lane half h takes 16-byte chunks 4*ks + h and 4*ks + 2 + h: the first half of
+      // both lanes of a row is the slice's first MX block, the second half the other
+      const int c0 = 4 * ks + half, c1 = c0 + 2;
+#pragma unroll
+      for (int nb = 0; nb < WN; ++nb) {
+        const int r = prow0 + nb * 32 + fr;
+        const uint4 lo = *reinterpret_cast<const uint4*>(sB + swz(r, c0));
+        const uint4 hi = *reinterpret_cast<const uint4*>(sB + swz(r, c1));
+        wf[nb] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                       (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      }
+#pragma unroll
+      for (int mb = 0; mb < WM; ++mb) {
+        const int r = arow0 + mb * 32 + fr;
+        const uint4 lo = *reinterpret_cast<const uint4*>(sA + swz(r, c0));
+        const uint4 hi = *reinterpret_cast<const uint4*>(sA + swz(r, c1));
+        af[mb] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                       (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      }
+      // lane half h supplies the scale of block 2*ks + h of the step, in byte 0 (the
+      // byte the instruction reads with op_sel 0)
+      const int sh = 8 * (2 * ks + half);
+#pragma unroll
+      for (int mb = 0; mb < WM; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < WN; ++nb)
+          acc[mb][nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              wf[nb], af[mb], acc[mb][nb], 0, 0, 0, (int)((sw[nb] >> sh) & 0xFFu), 0,
+              (int)((sa[mb] >> sh) & 0xFFu));
+    }
+  }
+}
+
+template <bool HALF>
+__device__ __forceinline__ void run_tile_mx(char* smem, const Tile& t, const TileLoads& ld,
+                                            const Epi& ep, int kb, int ke,
+                                            float* __restrict__ part, int stage0, bool primed,
+                                            const TileLoads& nxt, bool has_next, int nkb,
+                                            const MxScales& ms, int K, int N) {
+  f32x16 acc[HALF ? 2 : 4][2];
+  mainloop_mx<HALF>(smem, ld, kb, ke, stage0, primed, nxt, has_next, nkb, t, ms, K, N, acc);
+  finish_tile<kFc1, HALF>(smem, t, ep, kb, ke, part, stage0, acc);
 }
 
 // The rows of each expert: contiguous segments [offsets[e], offsets[e+1]) (cap = 0), or
@@ -680,13 +821,15 @@ __device__ Split split_plan(int total, int G, int slots, int nk) {
   return p;
 }
 
-// P_MN: the weights are read MN-major (see tile_loads); ksplit as there.
-template <int MODE, bool P_MN>
+// P_MN: the weights are read MN-major (see tile_loads); ksplit as there. MX: fc1 on the
+// FP8 payload (A, W1, W3 hold e4m3 bytes, ms their scales).
+template <int MODE, bool P_MN, bool MX = false>
 __global__ __launch_bounds__(NTHR, 1) void gg_bf16_kernel(
     const bf16_t* __restrict__ A, Segs sg, int E, int K, int N,
     int m_cap, const bf16_t* __restrict__ W1, const bf16_t* __restrict__ W3, int ksplit,
-    Epi ep, float* __restrict__ ws, int slots) {
+    Epi ep, float* __restrict__ ws, int slots, MxScales ms) {
   constexpr bool FC1 = MODE == kFc1;
+  constexpr int EB = MX ? 1 : 2;
   __shared__ __attribute__((aligned(16))) char smem[2 * STAGE_BYTES];
   __shared__ Sched sc;
   build_sched(sc, sg, E, m_cap);
@@ -694,7 +837,7 @@ __global__ __launch_bounds__(NTHR, 1) void gg_bf16_kernel(
   const int cols = FC1 ? BP / 2 : BP;
   const int n_nt = (N + cols - 1) / cols;
   const int total = sc.tstart[E] * n_nt;
-  const int nk = K / BK;
+  const int nk = K * EB / (BK * 2);   // 128-byte k-steps
   const Split sp = split_plan(total, gridDim.x, ws ? slots : 0, nk);
   const int items = sp.full + sp.tail * sp.S;
   int vb = blockIdx.x;
@@ -725,7 +868,7 @@ __global__ __launch_bounds__(NTHR, 1) void gg_bf16_kernel(
 
   if (vb >= items) return;
   Work cur = work(vb);
-  TileLoads ld = tile_loads<FC1, P_MN>(cur.t, A, W1, W3, K, N, ksplit);
+  TileLoads ld = tile_loads<FC1, P_MN, EB>(cur.t, A, W1, W3, K, N, ksplit);
   int stage0 = 0;
   bool primed = false;
   for (int w = vb; w < items; w += gridDim.x) {
@@ -734,14 +877,22 @@ __global__ __launch_bounds__(NTHR, 1) void gg_bf16_kernel(
     TileLoads nl = ld;
     if (has_next) {
       nw = work(w + gridDim.x);
-      nl = tile_loads<FC1, P_MN>(nw.t, A, W1, W3, K, N, ksplit);
+      nl = tile_loads<FC1, P_MN, EB>(nw.t, A, W1, W3, K, N, ksplit);
     }
-    if (cur.t.rows > BM / 2)
+    if (MX) {
+      if (cur.t.rows > BM / 2)
+        run_tile_mx<false>(smem, cur.t, ld, ep, cur.kb, cur.ke, cur.part, stage0, primed, nl,
+                           has_next, nw.kb, ms, K, N);
+      else
+        run_tile_mx<true>(smem, cur.t, ld, ep, cur.kb, cur.ke, cur.part, stage0, primed, nl,
+                          has_next, nw.kb, ms, K, N);
+    } else if (cur.t.rows > BM / 2) {
       run_tile<MODE, false, P_MN>(smem, cur.t, ld, ep, cur.kb, cur.ke, cur.part, stage0, primed,
                                   nl, has_next, nw.kb);
-    else
+    } else {
       run_tile<MODE, true, P_MN>(smem, cur.t, ld, ep, cur.kb, cur.ke, cur.part, stage0, primed,
                                  nl, has_next, nw.kb);
+    }
     stage0 = (stage0 + cur.ke - cur.kb) & 1;
     primed = has_next;
     cur = nw;
@@ -1180,23 +1331,23 @@ static hipError_t launch_mgrouped(int dt, int mode, bool p_mn, const void* A, Se
   const int mc = (int)m_cap;
   if (mode == kFc1) {
     hipLaunchKernelGGL((gg_bf16_kernel<kFc1, false>), grid, block, 0, s, a, sg, E, K, N, mc,
-                       w1, w3, K, ep, ws, slots);
+                       w1, w3, K, ep, ws, slots, MxScales{});
     if (slots)
       hipLaunchKernelGGL(gg_tail_reduce<kFc1>, rgrid, rblock, 0, s, sg, E, K, mc, G, slots,
                          ws, ep);
   } else if (mode == kFc2) {
     if (p_mn)
       hipLaunchKernelGGL((gg_bf16_kernel<kFc2, true>), grid, block, 0, s, a, sg, E, K, N, mc,
-                         w1, w3, ksplit, ep, ws, slots);
+                         w1, w3, ksplit, ep, ws, slots, MxScales{});
     else
       hipLaunchKernelGGL((gg_bf16_kernel<kFc2, false>), grid, block, 0, s, a, sg, E, K, N,
-                         mc, w1, w1, K, ep, ws, slots);
+                         mc, w1, w1, K, ep, ws, slots, MxScales{});
     if (slots)
       hipLaunchKernelGGL(gg_tail_reduce<kFc2>, rgrid, rblock, 0, s, sg, E, K, mc, G, slots,
                          ws, ep);
   } else {
     hipLaunchKernelGGL((gg_bf16_kernel<kDgrad, true>), grid, block, 0, s, a, sg, E, K, N, mc,
-                       w1, w1, K, ep, ws, slots);
+                       w1, w1, K, ep, ws, slots, MxScales{});
     if (slots)
       hipLaunchKernelGGL(gg_tail_reduce<kDgrad>, rgrid, rblock, 0, s, sg, E, K, mc, G, slots,
                          ws, ep);
@@ -1220,6 +1371,30 @@ hipError_t launch_grouped_swiglu(int dt, int phases, const void* x_perm, const i
     return launch_mgrouped(dt, kFc2, false, h, sg, tile_expert, E, F, m_tile, m_cap, w2, w2, F,
                            y_perm, nullptr, nullptr, D, workspace, ws_bytes, s);
   return hipSuccess;
+}
+
+hipError_t launch_grouped_fc1_mx(const void* xq_perm, const void* xs_perm,
+                                 const int32_t* offsets, int E, int D, int F, int64_t m_cap,
+                                 const void* w1q, const void* w1s, const void* w3q,
+                                 const void* w3s, void* h, void* workspace, size_t ws_bytes,
+                                 hipStream_t s) {
+  const int G = cu_count();
+  float* ws = static_cast<float*>(workspace);
+  const int slots = ws ? (int)std::min<size_t>(ws_bytes / (BM * BP * sizeof(float)), 1 << 20) : 0;
+  const Segs sg{offsets, nullptr, 0};
+  const Epi ep{static_cast<bf16_t*>(h), nullptr, nullptr, F};
+  const MxScales ms{static_cast<const uint8_t*>(xs_perm), static_cast<const uint8_t*>(w1s),
+                    static_cast<const uint8_t*>(w3s)};
+  hipLaunchKernelGGL((gg_bf16_kernel<kFc1, false, true>), dim3(G), dim3(NTHR), 0, s,
+                     static_cast<const bf16_t*>(xq_perm), sg, E, D, F, (int)m_cap,
+                     static_cast<const bf16_t*>(w1q), static_cast<const bf16_t*>(w3q), D, ep, ws,
+                     slots, ms);
+  // the reduction counts k-steps as K / 64 bf16 values: the FP8 kernel's 128-byte steps
+  // are D / 128
+  if (slots)
+    hipLaunchKernelGGL(gg_tail_reduce<kFc1>, dim3(4 * G), dim3(256), 0, s, sg, E, D / 2,
+                       (int)m_cap, G, slots, ws, ep);
+  return hipGetLastError();
 }
 
 hipError_t launch_grouped_dgrad_swiglu(int dt, const void* dy_perm, const int32_t* offsets,

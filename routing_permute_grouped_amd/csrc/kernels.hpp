@@ -47,6 +47,26 @@ hipError_t launch_grouped_swiglu(int dt, int phases, const void* x_perm, const i
                                  const void* w3, const void* w2, void* h, void* ab, void* y_perm,
                                  void* workspace, size_t ws_bytes, hipStream_t s);
 
+// fc1 on the FP8 payload: x (e4m3 [m_cap, D], E8M0 scales [m_cap, D/32]) against w1, w3
+// (e4m3 [E,F,D], scales [E,F,D/32]) -> h = silu(a)*b in bf16
+hipError_t launch_grouped_fc1_mx(const void* xq_perm, const void* xs_perm,
+                                 const int32_t* offsets, int E, int D, int F, int64_t m_cap,
+                                 const void* w1q, const void* w1s, const void* w3q,
+                                 const void* w3s, void* h, void* workspace, size_t ws_bytes,
+                                 hipStream_t s);
+
+// MX quantization of x [R, C] (dt) -> e4m3 codes [R, C] and E8M0 scales [R, C/32]
+hipError_t launch_quantize_mx(int dt, const void* x, int64_t R, int C, void* q, void* scales,
+                              hipStream_t s);
+
+// permute of the FP8 payload: the metadata of launch_permute, then the rows of the codes
+// (D bytes) and of the scales (D/32 bytes)
+hipError_t launch_permute_mx(const void* xq, const void* xs, const int32_t* topk_idx, int T, int D,
+                             int E, int k, int m_tile, int64_t m_cap, void* xq_perm,
+                             void* xs_perm, int32_t* counts, int32_t* offsets, int32_t* dst_row,
+                             int32_t* src_row, int32_t* tile_expert, void* workspace,
+                             int32_t* dev_err, hipStream_t s);
+
 // dh = dy_perm w2[e] (w2 [E,D,F]), then [da | db] from ab -> dab; dh stored if non-null
 hipError_t launch_grouped_dgrad_swiglu(int dt, const void* dy_perm, const int32_t* offsets,
                                        const int32_t* tile_expert, int E, int D, int F,

@@ -190,6 +190,58 @@ moe_status_t moe_grouped_swiglu_masked(moe_dtype_t dt, const void* x_masked,
                                                static_cast<hipStream_t>(stream)));
 }
 
+moe_status_t moe_quantize_mxfp8(moe_dtype_t dt, const void* x, int64_t R, int C, void* q,
+                                void* scales, void* stream) {
+  if (!dtype_ok(dt) || !aligned16(x) || !aligned16(q) || !scales) return MOE_EINVAL;
+  if (R < 1 || C < 32 || C % 32 != 0 || C > kMaxDim || R > ((int64_t)1 << 31)) return MOE_ESHAPE;
+  return hip_status(moe::launch_quantize_mx(dt, x, R, C, q, scales,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_permute_mxfp8(const void* xq, const void* xs, const int32_t* topk_idx, int T,
+                               int D, int E, int k, int m_tile, int64_t m_cap, void* xq_perm,
+                               void* xs_perm, int32_t* counts, int32_t* offsets,
+                               int32_t* dst_row, int32_t* src_row, int32_t* tile_expert,
+                               void* workspace, size_t ws_bytes, int32_t* dev_err,
+                               void* stream) {
+  if (!aligned16(xq) || !aligned16(xs) || !aligned16(xq_perm) || !aligned16(xs_perm) ||
+      !aligned4(topk_idx) || !aligned4(counts) || !aligned4(offsets) || !aligned4(dst_row) ||
+      !aligned4(src_row) || !aligned4(tile_expert) || !aligned4(workspace) || !aligned4(dev_err))
+    return MOE_EINVAL;
+  if (!tk_ok(T, k) || !dim_ok(D) || D % 512 != 0 || E < 1 || E > kMaxExperts || k < 1 || k > E ||
+      k > kMaxK || !mtile_ok(m_tile))
+    return MOE_ESHAPE;
+  const int64_t need = moe_capacity(T, k, E, m_tile);
+  if (m_cap < need || m_cap % m_tile != 0 || m_cap > INT32_MAX) return MOE_ECAPACITY;
+  if (ws_bytes < moe::permute_workspace_bytes(T, k, E)) return MOE_EWORKSPACE;
+  return hip_status(moe::launch_permute_mx(xq, xs, topk_idx, T, D, E, k, m_tile, m_cap, xq_perm,
+                                           xs_perm, counts, offsets, dst_row, src_row,
+                                           tile_expert, workspace, dev_err,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_grouped_fc1_swiglu_mxfp8(const void* xq_perm, const void* xs_perm,
+                                          const int32_t* offsets, const int32_t* tile_expert,
+                                          int E, int D, int F, int m_tile, int64_t m_cap,
+                                          const void* w1q, const void* w1s, const void* w3q,
+                                          const void* w3s, void* h, void* workspace,
+                                          size_t ws_bytes, void* stream) {
+  if (!aligned16(xq_perm) || !aligned4(xs_perm) || !aligned4(offsets) || !aligned4(tile_expert) ||
+      !aligned16(w1q) || !aligned4(w1s) || !aligned16(w3q) || !aligned4(w3s) || !aligned16(h))
+    return MOE_EINVAL;
+  if (workspace && !aligned16(workspace)) return MOE_EINVAL;
+  if (!workspace) ws_bytes = 0;
+  if (E < 1 || E > kMaxExperts || !dim_ok(D) || D % 128 != 0 || !dim_ok(F) || !mtile_ok(m_tile))
+    return MOE_ESHAPE;
+  if ((int64_t)D * F >= ((int64_t)1 << 31)) return MOE_ESHAPE;
+  if (m_cap < 1 || m_cap % m_tile != 0 || m_cap > INT32_MAX) return MOE_ECAPACITY;
+  if (m_tile != 128 && m_tile != 256) return MOE_EUNSUPPORTED;
+  return hip_status(moe::launch_grouped_fc1_mx(xq_perm, xs_perm, offsets, E, D, F, m_cap, w1q,
+                                               w1s, w3q, w3s, h,
+                                               ws_bytes ? workspace : nullptr, ws_bytes,
+                                               static_cast<hipStream_t>(stream)));
+}
+
 static moe_status_t dgrad_common(moe_dtype_t dt, const void* a, const int32_t* offsets,
                                  const int32_t* tile_expert, int E, int D, int F, int m_tile,
                                  int64_t m_cap, void* workspace) {

@@ -310,4 +310,25 @@ hipError_t launch_permute_masked(int dt, const void* x, const int32_t* topk_idx,
   return launch_copy(dt, x, T, D, k, 0, dst_row, counts, nullptr, x_masked, s);
 }
 
+hipError_t launch_permute_mx(const void* xq, const void* xs, const int32_t* topk_idx, int T, int D,
+                             int E, int k, int m_tile, int64_t m_cap, void* xq_perm,
+                             void* xs_perm, int32_t* counts, int32_t* offsets, int32_t* dst_row,
+                             int32_t* src_row, int32_t* tile_expert, void* workspace,
+                             int32_t* dev_err, hipStream_t s) {
+  const int nbh = (T + kHistTokens - 1) / kHistTokens;
+  int32_t* hist = static_cast<int32_t*>(workspace);
+  int32_t* bad = hist + (size_t)nbh * E;
+  hipLaunchKernelGGL(hist_kernel, dim3(nbh), dim3(kThreads), 0, s, topk_idx, T, k, E, hist, bad);
+  const int nbp = (T + kPlaceTokens - 1) / kPlaceTokens;
+  hipLaunchKernelGGL(rank_kernel<false>, dim3(nbp + 1), dim3(kThreads), 0, s, topk_idx, T, k, E,
+                     m_tile, 0, m_cap, nbh, hist, bad, counts, offsets, tile_expert, dev_err,
+                     dst_row, src_row);
+  // the rows are copied as raw bytes: D code bytes = D/2 two-byte units, D/32 scale bytes
+  // = D/64 units (D % 512 == 0 keeps both whole 16-byte chunks); pad rows get zero bytes
+  // (code 0 is +0, scale byte 0 is 2^-127)
+  const hipError_t e = launch_copy(kBF16, xq, T, D / 2, k, E, dst_row, counts, offsets, xq_perm, s);
+  if (e != hipSuccess) return e;
+  return launch_copy(kBF16, xs, T, D / 64, k, E, dst_row, counts, offsets, xs_perm, s);
+}
+
 }  // namespace moe

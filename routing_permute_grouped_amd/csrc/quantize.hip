@@ -1,0 +1,94 @@
+// MX quantization of the FP8 payload ("Expert Parallelism (EP)", llm-infra-atlas,
+// section 3: dispatch in FP8 e4m3 with scales, combine in BF16).
+//
+// Every 32 consecutive values of a row share one power-of-two scale 2^X, stored as the
+// E8M0 byte X + 127: X is the smallest integer with max|v| <= 448 * 2^X (448 is the
+// largest OCP E4M3 value), so no value saturates, and -127 for an all-zero block. Each
+// value becomes the e4m3 code of v / 2^X rounded to nearest, ties to even. One thread
+// per block: the scale comes from frexp of the block's max (exact), the division by 2^X
+// is an exact ldexp, and the rounding to e4m3 is done on the float32 bits.
+#include <math.h>
+
+#include <algorithm>
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+namespace {
+
+constexpr int kThreads = 256;
+
+// e4m3 code of a float32 value with |v| <= 448: subnormal codes below 2^-6 (steps of
+// 2^-9), otherwise the 3-bit mantissa rounded to nearest even (a carry moves to the next
+// exponent, which the code layout absorbs). The sign is kept, -0 included.
+__device__ __forceinline__ uint32_t e4m3_code(float v) {
+  const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
+  const float a = fabsf(v);
+  uint32_t code;
+  if (a < 0.015625f) {                                   // 2^-6
+    code = (uint32_t)rintf(a * 512.0f);                  // 0..8; 8 is 2^-6 itself
+  } else {
+    int e;
+    const float m = frexpf(a, &e);                       // a = m * 2^e, 0.5 <= m < 1
+    const uint32_t q = (uint32_t)rintf((2.0f * m - 1.0f) * 8.0f);   // 0..8
+    code = ((uint32_t)(e - 1 + 7) << 3) + q;
+  }
+  return sign | code;
+}
+
+template <typename TIn>
+__global__ __launch_bounds__(kThreads) void quantize_mx_kernel(const TIn* __restrict__ x,
+                                                              int64_t nblocks, int C,
+                                                              uint8_t* __restrict__ q,
+                                                              uint8_t* __restrict__ scales) {
+  constexpr int V = Chunk<TIn>::V;   // values per 16-byte chunk
+  constexpr int NC = 32 / V;         // chunks per block
+  for (int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x; b < nblocks;
+       b += (int64_t)gridDim.x * kThreads) {
+    const TIn* src = x + b * 32;     // rows are C values long and C % 32 == 0
+    float v[32];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) Chunk<TIn>::widen(ld16(src + c * V), v + c * V);
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    int X = -127;
+    if (amax > 0.0f) {
+      int e;
+      const float m = 2.0f * frexpf(amax, &e);           // amax = m * 2^(e-1), 1 <= m < 2
+      X = (m <= 1.75f) ? (e - 1) - 8 : (e - 1) - 7;
+      X = max(-127, min(127, X));
+    }
+    uint32_t w[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      w[i] = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) w[i] |= e4m3_code(ldexpf(v[4 * i + j], -X)) << (8 * j);
+    }
+    st16(q + b * 32, u32x4{w[0], w[1], w[2], w[3]});
+    st16(q + b * 32 + 16, u32x4{w[4], w[5], w[6], w[7]});
+    scales[b] = (uint8_t)(X + 127);
+  }
+  (void)C;
+}
+
+}  // namespace
+
+hipError_t launch_quantize_mx(int dt, const void* x, int64_t R, int C, void* q, void* scales,
+                              hipStream_t s) {
+  const int64_t nblocks = R * (C / 32);
+  const int grid = (int)std::min<int64_t>(8 * cu_count(), (nblocks + kThreads - 1) / kThreads);
+  if (dt == kF32)
+    hipLaunchKernelGGL(quantize_mx_kernel<float>, dim3(grid), dim3(kThreads), 0, s,
+                       static_cast<const float*>(x), nblocks, C, static_cast<uint8_t*>(q),
+                       static_cast<uint8_t*>(scales));
+  else
+    hipLaunchKernelGGL(quantize_mx_kernel<bf16_t>, dim3(grid), dim3(kThreads), 0, s,
+                       static_cast<const bf16_t*>(x), nblocks, C, static_cast<uint8_t*>(q),
+                       static_cast<uint8_t*>(scales));
+  return hipGetLastError();
+}
+
+}  // namespace moe

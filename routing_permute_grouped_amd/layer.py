@@ -128,6 +128,59 @@ def moe_layer_masked(x: torch.Tensor, w1: torch.Tensor, w3: torch.Tensor, w2: to
     return res
 
 
+@dataclass
+class MxWeights:
+    """fc1's weights quantized once for the FP8 payload: e4m3 codes [E,F,D] and E8M0
+    scales [E,F,D/32] of w1 and w3."""
+    w1q: torch.Tensor
+    w1s: torch.Tensor
+    w3q: torch.Tensor
+    w3s: torch.Tensor
+
+    @staticmethod
+    def quantize(w1: torch.Tensor, w3: torch.Tensor) -> "MxWeights":
+        w1q, w1s = B.moe_quantize_mxfp8(w1)
+        w3q, w3s = B.moe_quantize_mxfp8(w3)
+        return MxWeights(w1q, w1s, w3q, w3s)
+
+
+def moe_layer_mxfp8(x: torch.Tensor, mw: MxWeights, w2: torch.Tensor, k: int, m_tile: int,
+                    wg: Optional[torch.Tensor] = None, bias: Optional[torch.Tensor] = None,
+                    topk_idx: Optional[torch.Tensor] = None,
+                    topk_w: Optional[torch.Tensor] = None,
+                    shared: Optional[SharedExperts] = None, renorm: bool = False,
+                    split_k: bool = True) -> dict:
+    """The layer with an FP8 payload (EP page section 3: dispatch in e4m3 plus scales,
+    combine in bf16): route on the bf16 x -> MX-quantize x -> permute codes and scales ->
+    fc1 on the scaled-FP8 MFMA -> fc2 (bf16) [-> shared experts, bf16] -> combine."""
+    E = mw.w1q.shape[0]
+    res = {}
+    if topk_idx is None:
+        topk_idx, topk_w, _ = B.moe_route(x, wg, k, bias=bias, renorm=renorm)
+    res["topk_idx"], res["topk_w"] = topk_idx, topk_w
+    xq, xs = B.moe_quantize_mxfp8(x)
+    res["xq"], res["xs"] = xq, xs
+    p = B.moe_permute_mxfp8(xq, xs, topk_idx, E, m_tile)
+    res.update(p)
+    m_cap = p["m_cap"]
+    ws = B.grouped_workspace(x.device) if split_k else None
+    h = B.moe_grouped_fc1_swiglu_mxfp8(p["xq_perm"], p["xs_perm"], p["offsets"], p["tile_expert"],
+                                       mw.w1q, mw.w1s, mw.w3q, mw.w3s, m_tile, m_cap,
+                                       workspace=ws)
+    y = torch.empty((m_cap, x.shape[1]), dtype=x.dtype, device=x.device)
+    B.moe_grouped_fc2(h, p["offsets"], p["tile_expert"], w2, m_tile, m_cap, y, workspace=ws)
+    res["h"], res["y_perm"] = h, y
+    sh = None
+    if shared is not None:
+        rows = DenseRows(x.shape[0], m_tile, x.device)
+        _, ys = B.moe_grouped_swiglu(x, rows.offsets, rows.tile_expert, shared.w1, shared.w3,
+                                     shared.w2, m_tile, m_cap=rows.m_cap, workspace=ws)
+        sh = ys[: x.shape[0]]
+        res["shared"] = sh
+    res["out"] = B.moe_combine(y, p["dst_row"], topk_w, shared=sh, m_cap=m_cap)
+    return res
+
+
 def _experts_backward(dy, x_rows, ab, h, offsets, tile_expert, w1, w3, w2, m_tile, m_cap, ws):
     """dgrad and wgrad of one grouped SwiGLU FFN over rows [0, m_cap) (section 5 of
     "Expert Parallelism (EP)": the m-grouped fc mirrors into an m-grouped dgrad and a

@@ -28,7 +28,9 @@ def test_header_declares_the_calls_and_helpers():
                                          "moe_combine", "moe_combine_backward",
                                          "moe_grouped_dgrad_swiglu", "moe_grouped_dgrad_fc1",
                                          "moe_grouped_wgrad", "moe_permute_masked",
-                                         "moe_grouped_swiglu_masked", "moe_capacity",
+                                         "moe_grouped_swiglu_masked", "moe_quantize_mxfp8",
+                                         "moe_permute_mxfp8", "moe_grouped_fc1_swiglu_mxfp8",
+                                         "moe_capacity",
                                          "moe_grouped_workspace_bytes",
                                          "moe_permute_workspace_bytes", "moe_status_str"])
 
@@ -261,6 +263,33 @@ def grouped_masked(dt=1, xm=FAKE, counts=FAKE, E=8, D=128, F=256, cap=32, w1=FAK
 ])
 def test_grouped_masked_validation(kw, code):
     assert grouped_masked(**kw) == code
+
+
+def test_mxfp8_calls_validate():
+    q = lib.moe_quantize_mxfp8
+    assert q(5, FAKE, 16, 64, FAKE, FAKE, None) == MOE_EINVAL
+    assert q(1, FAKE + 2, 16, 64, FAKE, FAKE, None) == MOE_EINVAL
+    assert q(1, FAKE, 16, 64, FAKE, None, None) == MOE_EINVAL
+    assert q(1, FAKE, 0, 64, FAKE, FAKE, None) == MOE_ESHAPE
+    assert q(1, FAKE, 16, 48, FAKE, FAKE, None) == MOE_ESHAPE
+    p = lambda **kw: lib.moe_permute_mxfp8(kw.get("xq", FAKE), FAKE, FAKE, kw.get("T", 64),
+                                           kw.get("D", 512), 8, 2, kw.get("mt", 128),
+                                           kw.get("m_cap", 2048), FAKE, FAKE, FAKE, FAKE, FAKE,
+                                           FAKE, FAKE, FAKE, kw.get("ws", 1 << 20), FAKE, None)
+    assert p(xq=None) == MOE_EINVAL
+    assert p(D=256) == MOE_ESHAPE           # scale rows must be whole 16-byte chunks
+    assert p(m_cap=100) == MOE_ECAPACITY
+    assert p(ws=0) == MOE_EWORKSPACE
+    f = lambda **kw: lib.moe_grouped_fc1_swiglu_mxfp8(
+        kw.get("xq", FAKE), FAKE, FAKE, FAKE, 8, kw.get("D", 512), kw.get("F", 256),
+        kw.get("mt", 128), kw.get("m_cap", 1024), FAKE, FAKE, FAKE, FAKE, kw.get("h", FAKE),
+        None, 0, None)
+    assert f(xq=FAKE + 4) == MOE_EINVAL
+    assert f(h=None) == MOE_EINVAL
+    assert f(D=192) == MOE_ESHAPE
+    assert f(F=100) == MOE_ESHAPE
+    assert f(m_cap=1000) == MOE_ECAPACITY
+    assert f(mt=64, m_cap=1024) == MOE_EUNSUPPORTED
 
 
 def test_binding_raises_on_rejected_call():

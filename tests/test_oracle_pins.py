@@ -688,3 +688,15 @@ def test_mx_forward_equals_bf16_forward_on_exactly_representable_inputs():
     np.testing.assert_array_equal(orc.mx_dequantize(b["xq"], b["xs"]), inp["x"])
     np.testing.assert_array_equal(a["h"], b["h"])
     np.testing.assert_array_equal(a["out"], b["out"])
+
+
+def test_token_outputs_mx_equal_forward_rows():
+    inp = _tiny_layer(33, T=15, D=64, F=16, E=4, k=2, shared=True)
+    for n in inp:
+        inp[n] = orc.round_bf16(inp[n]).astype(np.float32)
+    res = orc.forward_mxfp8(inp, k=2, m_tile=16)
+    toks = np.array([1, 7, 14])
+    out = orc.token_outputs_mx(toks, inp["x"], res["topk_idx"], res["topk_w"], inp["w1"],
+                               inp["w3"], inp["w2"], (inp["ws1"], inp["ws3"], inp["ws2"]))
+    # the same float64 arithmetic batched differently: equal up to a last-bit bf16 flip
+    np.testing.assert_allclose(out, res["out"][toks], rtol=0, atol=2 ** -7 * np.abs(out).max())
