@@ -478,7 +478,7 @@ def bench_fp8(args, cfg, d, buf, shared, gws, flush, n_valid) -> dict:
     mw = rpg.MxWeights.quantize(d["w1"], d["w3"])
     u8 = dict(dtype=torch.uint8, device=dev)
     fb = {"xq": torch.empty((T, D), **u8), "xs": torch.empty((T, D // 32), **u8),
-          "xq_perm": torch.empty((m_cap, D), **u8), "xs_perm": torch.empty((m_cap, D // 32), **u8),
+          "xq_perm": torch.empty((m_cap, D), **u8), "xs_perm": torch.empty((D // 128, m_cap, 4), **u8),
           "out": torch.empty_like(buf["out"])}
     for n in ("counts", "offsets", "dst_row", "src_row", "tile_expert", "dev_err", "workspace"):
         fb[n] = torch.empty_like(buf[n])

@@ -229,21 +229,34 @@ moe_status_t moe_grouped_fc2(moe_dtype_t dt, const void* h, const int32_t* offse
  * ties to even. fc1 multiplies on the scaled-FP8 MFMA with float32 accumulation and
  * writes h in bf16; fc2 and the combine are the bf16 calls above.
  *
- * moe_quantize_mxfp8: x [R,C] (dt) -> q [R,C] uint8 codes, scales [R,C/32] uint8.
- *   C a multiple of 32 (<= 65536). Used for the token rows before the permute and,
- *   once, for w1 and w3 ([E*F, D] rows).
- * moe_permute_mxfp8: moe_permute's metadata (same outputs, same rules) and the rows of
- *   xq [T,D] and xs [T,D/32] copied to xq_perm [m_cap,D], xs_perm [m_cap,D/32]; pad rows
- *   get zero bytes (the value 0). D a multiple of 512.
+ * Scale layouts (moe_mx_layout_t). MOE_MX_ROWS: scales [R, C/32] bytes, row by row (the
+ * plain MX layout). MOE_MX_KSTEPS: the GEMM's operand layout, 32-bit words [C/128][R]:
+ * word (s, r) holds row r's scales of the four blocks of k step s (values
+ * 128*s .. 128*s + 127), block 4*s + j in byte j. One k step of the fc1 GEMM reads one
+ * word per row, so 32 consecutive rows are 128 consecutive bytes (the row layout would
+ * put every row's byte on its own cache line).
+ *
+ * moe_quantize_mxfp8: x [R,C] (dt) -> q [R,C] uint8 codes and scales in `layout`
+ *   (MOE_MX_ROWS: C a multiple of 32; MOE_MX_KSTEPS: C a multiple of 128; C <= 65536).
+ *   Used with MOE_MX_ROWS for the token rows before the permute and, once, with
+ *   MOE_MX_KSTEPS for w1 and w3 (R = E*F rows of D values).
+ * moe_permute_mxfp8: moe_permute's metadata (same outputs, same rules), the code rows of
+ *   xq [T,D] copied to xq_perm [m_cap,D], and the scales xs [T,D/32] (MOE_MX_ROWS)
+ *   gathered into xs_perm in MOE_MX_KSTEPS over m_cap rows ([D/128][m_cap] words);
+ *   pad rows get zero bytes (code 0 is the value 0). Rows at or past offsets[E] are not
+ *   written. D a multiple of 128.
  * moe_grouped_fc1_swiglu_mxfp8: h [m_cap,F] (bf16) = silu(a)*b with a, b the float32
- *   products of the dequantized rows and w1q/w1s, w3q/w3s ([E,F,D] codes, [E,F,D/32]
- *   scales), per segment as moe_grouped_fc1_swiglu (workspace likewise). D a multiple of
- *   128; m_tile 128 or 256.
- * Errors: MOE_EINVAL, MOE_ESHAPE, MOE_ECAPACITY, MOE_EWORKSPACE, MOE_EUNSUPPORTED,
- * MOE_EHIP.
+ *   products of the dequantized rows and w1q/w1s, w3q/w3s ([E,F,D] codes; scales in
+ *   MOE_MX_KSTEPS over the E*F rows, [D/128][E*F] words), per segment as
+ *   moe_grouped_fc1_swiglu (workspace likewise); xs_perm as moe_permute_mxfp8 writes it.
+ *   D a multiple of 128; m_tile 128 or 256.
+ * Errors: MOE_EINVAL (also an unknown layout), MOE_ESHAPE, MOE_ECAPACITY,
+ * MOE_EWORKSPACE, MOE_EUNSUPPORTED, MOE_EHIP.
  */
+typedef enum { MOE_MX_ROWS = 0, MOE_MX_KSTEPS = 1 } moe_mx_layout_t;
+
 moe_status_t moe_quantize_mxfp8(moe_dtype_t dt, const void* x, int64_t R, int C, void* q,
-                                void* scales, void* stream);
+                                void* scales, moe_mx_layout_t layout, void* stream);
 moe_status_t moe_permute_mxfp8(const void* xq, const void* xs, const int32_t* topk_idx,
                                int T, int D, int E, int k, int m_tile, int64_t m_cap,
                                void* xq_perm, void* xs_perm, int32_t* counts, int32_t* offsets,

@@ -3,7 +3,7 @@
 The compute runs in hand-written HIP kernels (libmoe_mi355x.so, C ABI in
 include/moe.h); this package only marshals torch tensors into those calls.
 """
-from ._binding import (LIB_PATH, MOE_BF16, MOE_F32, SIGNATURES, MoEError, grouped_workspace,
+from ._binding import (LIB_PATH, MOE_BF16, MOE_F32, MOE_MX_KSTEPS, MOE_MX_ROWS, SIGNATURES, MoEError, grouped_workspace,
                        lib, moe_capacity, moe_combine, moe_combine_backward,
                        moe_grouped_dgrad_fc1, moe_grouped_dgrad_swiglu, moe_grouped_fc1_swiglu,
                        moe_grouped_fc2, moe_grouped_swiglu, moe_grouped_wgrad,
@@ -15,7 +15,7 @@ from .layer import (DenseRows, MxWeights, SharedExperts, moe_layer, moe_layer_ba
                     moe_layer_masked, moe_layer_mxfp8)
 
 __all__ = [
-    "LIB_PATH", "MOE_BF16", "MOE_F32", "SIGNATURES", "MoEError", "grouped_workspace", "lib",
+    "LIB_PATH", "MOE_BF16", "MOE_F32", "MOE_MX_KSTEPS", "MOE_MX_ROWS", "SIGNATURES", "MoEError", "grouped_workspace", "lib",
     "moe_capacity", "moe_combine", "moe_combine_backward", "moe_grouped_dgrad_fc1",
     "moe_grouped_dgrad_swiglu", "moe_grouped_fc1_swiglu", "moe_grouped_fc2", "moe_grouped_swiglu",
     "moe_grouped_wgrad", "moe_grouped_swiglu_masked", "moe_grouped_workspace_bytes",

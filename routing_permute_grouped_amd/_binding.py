@@ -17,6 +17,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmoe_mi355x.so")
 
 MOE_F32, MOE_BF16 = 0, 1
+MOE_MX_ROWS, MOE_MX_KSTEPS = 0, 1   # moe_mx_layout_t
 _STATUS = {0: "MOE_OK", 1: "MOE_EINVAL", 2: "MOE_ESHAPE", 3: "MOE_ECAPACITY",
            4: "MOE_EWORKSPACE", 5: "MOE_EHIP", 6: "MOE_EUNSUPPORTED"}
 
@@ -32,7 +33,7 @@ SIGNATURES = [
                                     _SZ, _P]),
     ("moe_grouped_fc2", _I, [_I, _P, _P, _P, _I, _I, _I, _I, _I64, _P, _P, _P, _SZ, _P]),
     ("moe_combine", _I, [_I, _P, _P, _P, _P, _I, _I, _I, _I64, _P, _P]),
-    ("moe_quantize_mxfp8", _I, [_I, _P, _I64, _I, _P, _P, _P]),
+    ("moe_quantize_mxfp8", _I, [_I, _P, _I64, _I, _P, _P, _I, _P]),
     ("moe_permute_mxfp8", _I, [_P, _P, _P, _I, _I, _I, _I, _I, _I64, _P, _P, _P, _P, _P, _P, _P, _P,
                                _SZ, _P, _P]),
     ("moe_grouped_fc1_swiglu_mxfp8", _I, [_P, _P, _P, _P, _I, _I, _I, _I, _I64, _P, _P, _P, _P, _P,
@@ -362,24 +363,27 @@ def _bytes_ptr(t: torch.Tensor) -> int:
 
 
 def moe_quantize_mxfp8(x: torch.Tensor, q: Optional[torch.Tensor] = None,
-                       scales: Optional[torch.Tensor] = None, stream=None):
-    """MX e4m3 codes and E8M0 scales of the rows of x [..., C] (C a multiple of 32).
-    Returns (q uint8 [..., C], scales uint8 [..., C/32])."""
+                       scales: Optional[torch.Tensor] = None, layout: int = 0, stream=None):
+    """MX e4m3 codes and E8M0 scales of the rows of x [..., C]. Returns (q uint8 [..., C],
+    scales): layout MOE_MX_ROWS, uint8 [..., C/32] (C a multiple of 32); MOE_MX_KSTEPS,
+    the GEMM's k-step words as uint8 [C/128, R, 4] (R rows, C a multiple of 128)."""
     C = x.shape[-1]
     R = x.numel() // C
     if q is None:
         q = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
     if scales is None:
-        scales = torch.empty((*x.shape[:-1], C // 32), dtype=torch.uint8, device=x.device)
+        shape = (C // 128, R, 4) if layout == MOE_MX_KSTEPS else (*x.shape[:-1], C // 32)
+        scales = torch.empty(shape, dtype=torch.uint8, device=x.device)
     _check("moe_quantize_mxfp8", lib.moe_quantize_mxfp8(
-        _dt(x), _ptr(x), R, C, _bytes_ptr(q), _bytes_ptr(scales), _stream(stream)))
+        _dt(x), _ptr(x), R, C, _bytes_ptr(q), _bytes_ptr(scales), layout, _stream(stream)))
     return q, scales
 
 
 def moe_permute_mxfp8(xq: torch.Tensor, xs: torch.Tensor, topk_idx: torch.Tensor, E: int,
                       m_tile: int, m_cap: Optional[int] = None, out: Optional[dict] = None,
                       stream=None) -> dict:
-    """moe_permute for the FP8 payload: dict with xq_perm, xs_perm and the metadata."""
+    """moe_permute for the FP8 payload: dict with xq_perm [m_cap, D], xs_perm (the scales
+    in k-step words, uint8 [D/128, m_cap, 4]) and the metadata."""
     T, D = xq.shape
     k = topk_idx.shape[1]
     dev = xq.device
@@ -388,7 +392,7 @@ def moe_permute_mxfp8(xq: torch.Tensor, xs: torch.Tensor, topk_idx: torch.Tensor
     o = dict(out or {})
     i32 = dict(dtype=torch.int32, device=dev)
     o.setdefault("xq_perm", torch.empty((m_cap, D), dtype=torch.uint8, device=dev))
-    o.setdefault("xs_perm", torch.empty((m_cap, D // 32), dtype=torch.uint8, device=dev))
+    o.setdefault("xs_perm", torch.empty((D // 128, m_cap, 4), dtype=torch.uint8, device=dev))
     o.setdefault("counts", torch.empty(E, **i32))
     o.setdefault("offsets", torch.empty(E + 1, **i32))
     o.setdefault("dst_row", torch.empty((T, k), **i32))
@@ -413,7 +417,8 @@ def moe_grouped_fc1_swiglu_mxfp8(xq_perm: torch.Tensor, xs_perm: torch.Tensor,
                                  h: Optional[torch.Tensor] = None,
                                  workspace: Optional[torch.Tensor] = None,
                                  stream=None) -> torch.Tensor:
-    """h [m_cap, F] bf16 = silu(a)*b from the FP8 payload and MX-quantized w1, w3."""
+    """h [m_cap, F] bf16 = silu(a)*b from the FP8 payload and MX-quantized w1, w3 (codes
+    [E, F, D], scales in k-step words [D/128, E*F, 4])."""
     E, F, D = w1q.shape
     if m_cap is None:
         m_cap = xq_perm.shape[0]

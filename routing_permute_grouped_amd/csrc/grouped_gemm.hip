@@ -266,12 +266,15 @@ __device__ __forceinline__ TileLoads tile_loads(const Tile& t, const bf16_t* __r
 
 // Loads of k-step kt into the LDS stage at `la` (this wave's first piece): the A pieces
 // (part 0) or the panel pieces (part 1).
+// NA > 0 gives the number of A pieces at compile time (it must equal o.na), which keeps
+// the issue free of branches.
+template <int NA = 0>
 __device__ __forceinline__ void issue_loads(const TileLoads& o, uint32_t la, int kt, int part) {
   if (part == 0) {
     const uint32_t ko = (uint32_t)kt * o.astep;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      if (j < o.na) dma16(o.rsa, o.aoff[j], ko, la + j * 8192);
+      if (NA > 0 ? j < NA : j < o.na) dma16(o.rsa, o.aoff[j], ko, la + j * 8192);
   } else {
     const uint32_t lb = la + A_BYTES;
     const bool second = kt >= o.bsplit;
@@ -592,16 +595,20 @@ __device__ __forceinline__ void run_tile(char* smem, const Tile& t, const TileLo
 // ---------------------------------------------------------------------------
 typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
 
+// The scales in k-step words: word (s, r) at [s * rows + r] holds row r's four E8M0
+// bytes for k step s (128 values), so a wave's 32 rows of one step are 128 consecutive
+// bytes.
 struct MxScales {
-  const uint8_t* a;    // [rows][K/32] E8M0 scales of the activation rows
-  const uint8_t* w1;   // [E][N][K/32]
-  const uint8_t* w3;
+  const uint32_t* a;    // [K/128][ra]: the activation rows
+  const uint32_t* w1;   // [K/128][E*N]: rows e*N + n
+  const uint32_t* w3;
+  int64_t ra;
 };
 
-// This wave's scale dwords for k-step kt (the 4 block scales of a row's 128 k values):
-// its A rows and its two panel blocks (w1 rows, then w3 rows, of the same columns).
+// This wave's scale words for k-step kt: its A rows and its two panel blocks (w1 rows,
+// then w3 rows, of the same columns).
 template <bool HALF>
-__device__ __forceinline__ void mx_scale_words(const Tile& t, const MxScales& ms, int K, int N,
+__device__ __forceinline__ void mx_scale_words(const Tile& t, const MxScales& ms, int E, int N,
                                                int kt, uint32_t (&sa)[HALF ? 2 : 4],
                                                uint32_t (&sw)[2]) {
   constexpr int WM = HALF ? 2 : 4;
@@ -610,25 +617,28 @@ __device__ __forceinline__ void mx_scale_words(const Tile& t, const MxScales& ms
   const int arow0 = (wave & 1) * (HALF ? 64 : 128);
   const int prow0 = (wave >> 1) * 64;
   const int fr = lane & 31;
-  const int kb = K / 32;
+  const uint32_t* a = ms.a + (size_t)kt * ms.ra + t.m0;
 #pragma unroll
-  for (int mb = 0; mb < WM; ++mb) {
-    const int r = min(arow0 + mb * 32 + fr, t.rows - 1);
-    sa[mb] = *reinterpret_cast<const uint32_t*>(ms.a + (size_t)(t.m0 + r) * kb + 4 * kt);
-  }
-  const int n = min(t.n0 + prow0 / 2 + fr, N - 1);
-  sw[0] = *reinterpret_cast<const uint32_t*>(ms.w1 + ((size_t)t.e * N + n) * kb + 4 * kt);
-  sw[1] = *reinterpret_cast<const uint32_t*>(ms.w3 + ((size_t)t.e * N + n) * kb + 4 * kt);
+  for (int mb = 0; mb < WM; ++mb) sa[mb] = a[min(arow0 + mb * 32 + fr, t.rows - 1)];
+  const size_t wrow = (size_t)kt * E * N + (size_t)t.e * N + min(t.n0 + prow0 / 2 + fr, N - 1);
+  sw[0] = ms.w1[wrow];
+  sw[1] = ms.w3[wrow];
 }
 
-// The bf16 main loop's pipeline (same stages, barrier, split issue and cross-tile
-// prefetch) with FP8 fragments and scaled MFMAs.
-template <bool HALF>
-__device__ __forceinline__ void mainloop_mx(char* smem, const TileLoads& ld, int kb, int ke,
-                                            int stage0, bool primed, const TileLoads& nxt,
-                                            bool has_next, int nkb, const Tile& t,
-                                            const MxScales& ms, int K, int N,
-                                            f32x16 (&acc)[HALF ? 2 : 4][2]) {
+// The MFMAs of one k step (two 64-wide slices) from the LDS stage at sA / sB, with the
+// next stage's loads issued by `issue(ks)` at the start of slice ks. Lane half h takes
+// 16-byte chunks 4*ks + h and 4*ks + 2 + h of slice ks: the first half of both lanes of
+// a row is the slice's first MX block, the second half the other. There is one set of
+// fragments (8 registers each; a second set would not fit beside the 128 accumulators),
+// and it rolls: the MFMAs go panel block by panel block, and each fragment of the
+// second slice is read as soon as the first slice's last MFMA on that register has been
+// issued, so every read has several MFMAs to land under. The order is pinned (the
+// compiler would otherwise hoist the reads, which needs a second set of registers).
+template <bool HALF, typename Issue>
+__device__ __forceinline__ void mx_step(const char* sA, const char* sB,
+                                        const uint32_t (&sa)[HALF ? 2 : 4],
+                                        const uint32_t (&sw)[2],
+                                        f32x16 (&acc)[HALF ? 2 : 4][2], Issue issue) {
   constexpr int WM = HALF ? 2 : 4;
   constexpr int WN = 2;
   const int lane = threadIdx.x & 63;
@@ -637,6 +647,54 @@ __device__ __forceinline__ void mainloop_mx(char* smem, const TileLoads& ld, int
   const int prow0 = (wave >> 1) * 64;
   const int fr = lane & 31;
   const int half = lane >> 5;
+  auto frag = [&](const char* base, int r, int ks) {
+    const int c0 = 4 * ks + half;
+    const uint4 lo = *reinterpret_cast<const uint4*>(base + swz(r, c0));
+    const uint4 hi = *reinterpret_cast<const uint4*>(base + swz(r, c0 + 2));
+    return i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                 (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+  };
+  i32x8 wf[WN], af[WM];
+#pragma unroll
+  for (int nb = 0; nb < WN; ++nb) wf[nb] = frag(sB, prow0 + nb * 32 + fr, 0);
+#pragma unroll
+  for (int mb = 0; mb < WM; ++mb) af[mb] = frag(sA, arow0 + mb * 32 + fr, 0);
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    issue(ks);
+    // lane half h supplies the scale of block 2*ks + h of the step, in byte 0 (the byte
+    // the instruction reads with op_sel 0)
+    const int sh = 8 * (2 * ks + half);
+#pragma unroll
+    for (int nb = 0; nb < WN; ++nb) {
+#pragma unroll
+      for (int mb = 0; mb < WM; ++mb) {
+        acc[mb][nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            wf[nb], af[mb], acc[mb][nb], 0, 0, 0, (int)((sw[nb] >> sh) & 0xFFu), 0,
+            (int)((sa[mb] >> sh) & 0xFFu));
+        if (ks == 0 && nb == WN - 1) af[mb] = frag(sA, arow0 + mb * 32 + fr, 1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (ks == 0) wf[nb] = frag(sB, prow0 + nb * 32 + fr, 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
+// The bf16 main loop's pipeline (same stages, barrier, split issue and cross-tile
+// prefetch) with FP8 fragments and scaled MFMAs. The steps before the last issue the
+// next step of this tile with no branch in the loop body, so the compiler keeps the
+// MFMAs between the two halves of the issue; the last step, peeled off, issues the
+// next tile's first.
+template <bool HALF>
+__device__ __forceinline__ void mainloop_mx(char* smem, const TileLoads& ld, int kb, int ke,
+                                            int stage0, bool primed, const TileLoads& nxt,
+                                            bool has_next, int nkb, const Tile& t,
+                                            const MxScales& ms, int E, int N,
+                                            f32x16 (&acc)[HALF ? 2 : 4][2]) {
+  constexpr int WM = HALF ? 2 : 4;
+  constexpr int WN = 2;
+  const int wave = threadIdx.x >> 6;
   const uint32_t lds0 = lds_addr(smem) + wave * 1024;
 #pragma unroll
   for (int i = 0; i < WM; ++i)
@@ -648,55 +706,52 @@ __device__ __forceinline__ void mainloop_mx(char* smem, const TileLoads& ld, int
     issue_loads(ld, lds0 + stage0 * STAGE_BYTES, kb, 0);
     issue_loads(ld, lds0 + stage0 * STAGE_BYTES, kb, 1);
   }
-  uint32_t sa[WM], sw[WN];
-  for (int kt = kb; kt < ke; ++kt) {
-    const int cur = (stage0 + kt - kb) & 1;
-    // this step's scales (small, L2-resident): issued before the wait for the stage's
-    // loads, which they join
-    mx_scale_words<HALF>(t, ms, K, N, kt, sa, sw);
+  // the scale words run one step ahead of the MFMAs, like the stage loads
+  uint32_t na[WM], nw[WN];
+  if (kb >= ke) return;
+  mx_scale_words<HALF>(t, ms, E, N, kb, na, nw);
+  // step kt: wait for its stage, take its scale words, fetch the next step's
+  auto enter = [&](int kt, uint32_t (&sa)[WM], uint32_t (&sw)[WN]) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    const char* sA = smem + cur * STAGE_BYTES;
-    const char* sB = sA + A_BYTES;
-    // one slice's fragments at a time (8 registers each: double-buffering them would not
-    // fit beside the 128 accumulators); the other wave of the SIMD covers the LDS latency
-    i32x8 wf[WN], af[WM];
+    // The compiler counts only its own loads (the scale words), not the stage copies
+    // issued from inline asm, so it would place its wait for these words before their
+    // first MFMA, after the next stage's copies have gone out, and that wait would
+    // drain them too. Using the words here, where every load has already landed, puts
+    // its wait here instead.
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      if (kt + 1 < ke) issue_loads(ld, lds0 + (cur ^ 1) * STAGE_BYTES, kt + 1, ks);
-      else if (has_next) issue_loads(nxt, lds0 + (cur ^ 1) * STAGE_BYTES, nkb, ks);
-      // lane half h takes 16-byte chunks 4*ks + h and 4*ks + 2 + h: the first half of
-      // both lanes of a row is the slice's first MX block, the second half the other
-      const int c0 = 4 * ks + half, c1 = c0 + 2;
-#pragma unroll
-      for (int nb = 0; nb < WN; ++nb) {
-        const int r = prow0 + nb * 32 + fr;
-        const uint4 lo = *reinterpret_cast<const uint4*>(sB + swz(r, c0));
-        const uint4 hi = *reinterpret_cast<const uint4*>(sB + swz(r, c1));
-        wf[nb] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
-                       (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-      }
-#pragma unroll
-      for (int mb = 0; mb < WM; ++mb) {
-        const int r = arow0 + mb * 32 + fr;
-        const uint4 lo = *reinterpret_cast<const uint4*>(sA + swz(r, c0));
-        const uint4 hi = *reinterpret_cast<const uint4*>(sA + swz(r, c1));
-        af[mb] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
-                       (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-      }
-      // lane half h supplies the scale of block 2*ks + h of the step, in byte 0 (the
-      // byte the instruction reads with op_sel 0)
-      const int sh = 8 * (2 * ks + half);
-#pragma unroll
-      for (int mb = 0; mb < WM; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < WN; ++nb)
-          acc[mb][nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-              wf[nb], af[mb], acc[mb][nb], 0, 0, 0, (int)((sw[nb] >> sh) & 0xFFu), 0,
-              (int)((sa[mb] >> sh) & 0xFFu));
+    for (int i = 0; i < WM; ++i) {
+      sa[i] = na[i];
+      asm volatile("" ::"v"(sa[i]));
     }
+#pragma unroll
+    for (int i = 0; i < WN; ++i) {
+      sw[i] = nw[i];
+      asm volatile("" ::"v"(sw[i]));
+    }
+  };
+  int kt = kb;
+  for (; kt + 1 < ke; ++kt) {
+    const int cur = (stage0 + kt - kb) & 1;
+    uint32_t sa[WM], sw[WN];
+    enter(kt, sa, sw);
+    mx_scale_words<HALF>(t, ms, E, N, kt + 1, na, nw);
+    const char* sA = smem + cur * STAGE_BYTES;
+    const uint32_t lnext = lds0 + (cur ^ 1) * STAGE_BYTES;
+    mx_step<HALF>(sA, sA + A_BYTES, sa, sw, acc, [&](int ks) {
+      issue_loads<HALF ? 2 : 4>(ld, lnext, kt + 1, ks);
+    });
   }
+  // the last step: the free stage receives the next tile's first step
+  const int cur = (stage0 + kt - kb) & 1;
+  uint32_t sa[WM], sw[WN];
+  enter(kt, sa, sw);
+  const char* sA = smem + cur * STAGE_BYTES;
+  const uint32_t lnext = lds0 + (cur ^ 1) * STAGE_BYTES;
+  mx_step<HALF>(sA, sA + A_BYTES, sa, sw, acc, [&](int ks) {
+    if (has_next) issue_loads(nxt, lnext, nkb, ks);
+  });
 }
 
 template <bool HALF>
@@ -704,9 +759,9 @@ __device__ __forceinline__ void run_tile_mx(char* smem, const Tile& t, const Til
                                             const Epi& ep, int kb, int ke,
                                             float* __restrict__ part, int stage0, bool primed,
                                             const TileLoads& nxt, bool has_next, int nkb,
-                                            const MxScales& ms, int K, int N) {
+                                            const MxScales& ms, int E, int N) {
   f32x16 acc[HALF ? 2 : 4][2];
-  mainloop_mx<HALF>(smem, ld, kb, ke, stage0, primed, nxt, has_next, nkb, t, ms, K, N, acc);
+  mainloop_mx<HALF>(smem, ld, kb, ke, stage0, primed, nxt, has_next, nkb, t, ms, E, N, acc);
   finish_tile<kFc1, HALF>(smem, t, ep, kb, ke, part, stage0, acc);
 }
 
@@ -882,10 +937,10 @@ __global__ __launch_bounds__(NTHR, 1) void gg_bf16_kernel(
     if (MX) {
       if (cur.t.rows > BM / 2)
         run_tile_mx<false>(smem, cur.t, ld, ep, cur.kb, cur.ke, cur.part, stage0, primed, nl,
-                           has_next, nw.kb, ms, K, N);
+                           has_next, nw.kb, ms, E, N);
       else
         run_tile_mx<true>(smem, cur.t, ld, ep, cur.kb, cur.ke, cur.part, stage0, primed, nl,
-                          has_next, nw.kb, ms, K, N);
+                          has_next, nw.kb, ms, E, N);
     } else if (cur.t.rows > BM / 2) {
       run_tile<MODE, false, P_MN>(smem, cur.t, ld, ep, cur.kb, cur.ke, cur.part, stage0, primed,
                                   nl, has_next, nw.kb);
@@ -1383,8 +1438,8 @@ hipError_t launch_grouped_fc1_mx(const void* xq_perm, const void* xs_perm,
   const int slots = ws ? (int)std::min<size_t>(ws_bytes / (BM * BP * sizeof(float)), 1 << 20) : 0;
   const Segs sg{offsets, nullptr, 0};
   const Epi ep{static_cast<bf16_t*>(h), nullptr, nullptr, F};
-  const MxScales ms{static_cast<const uint8_t*>(xs_perm), static_cast<const uint8_t*>(w1s),
-                    static_cast<const uint8_t*>(w3s)};
+  const MxScales ms{static_cast<const uint32_t*>(xs_perm), static_cast<const uint32_t*>(w1s),
+                    static_cast<const uint32_t*>(w3s), m_cap};
   hipLaunchKernelGGL((gg_bf16_kernel<kFc1, false, true>), dim3(G), dim3(NTHR), 0, s,
                      static_cast<const bf16_t*>(xq_perm), sg, E, D, F, (int)m_cap,
                      static_cast<const bf16_t*>(w1q), static_cast<const bf16_t*>(w3q), D, ep, ws,

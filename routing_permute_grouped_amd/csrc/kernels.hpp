@@ -55,12 +55,13 @@ hipError_t launch_grouped_fc1_mx(const void* xq_perm, const void* xs_perm,
                                  const void* w3s, void* h, void* workspace, size_t ws_bytes,
                                  hipStream_t s);
 
-// MX quantization of x [R, C] (dt) -> e4m3 codes [R, C] and E8M0 scales [R, C/32]
+// MX quantization of x [R, C] (dt) -> e4m3 codes [R, C] and E8M0 scales, [R, C/32]
+// bytes or (ksteps) [C/128][R] words of four bytes
 hipError_t launch_quantize_mx(int dt, const void* x, int64_t R, int C, void* q, void* scales,
-                              hipStream_t s);
+                              bool ksteps, hipStream_t s);
 
 // permute of the FP8 payload: the metadata of launch_permute, then the rows of the codes
-// (D bytes) and of the scales (D/32 bytes)
+// (D bytes) and the scales (rows of D/32 bytes in, [D/128][m_cap] k-step words out)
 hipError_t launch_permute_mx(const void* xq, const void* xs, const int32_t* topk_idx, int T, int D,
                              int E, int k, int m_tile, int64_t m_cap, void* xq_perm,
                              void* xs_perm, int32_t* counts, int32_t* offsets, int32_t* dst_row,

@@ -191,10 +191,12 @@ moe_status_t moe_grouped_swiglu_masked(moe_dtype_t dt, const void* x_masked,
 }
 
 moe_status_t moe_quantize_mxfp8(moe_dtype_t dt, const void* x, int64_t R, int C, void* q,
-                                void* scales, void* stream) {
+                                void* scales, moe_mx_layout_t layout, void* stream) {
   if (!dtype_ok(dt) || !aligned16(x) || !aligned16(q) || !scales) return MOE_EINVAL;
+  if (layout != MOE_MX_ROWS && layout != MOE_MX_KSTEPS) return MOE_EINVAL;
   if (R < 1 || C < 32 || C % 32 != 0 || C > kMaxDim || R > ((int64_t)1 << 31)) return MOE_ESHAPE;
-  return hip_status(moe::launch_quantize_mx(dt, x, R, C, q, scales,
+  if (layout == MOE_MX_KSTEPS && C % 128 != 0) return MOE_ESHAPE;
+  return hip_status(moe::launch_quantize_mx(dt, x, R, C, q, scales, layout == MOE_MX_KSTEPS,
                                             static_cast<hipStream_t>(stream)));
 }
 
@@ -204,11 +206,11 @@ moe_status_t moe_permute_mxfp8(const void* xq, const void* xs, const int32_t* to
                                int32_t* dst_row, int32_t* src_row, int32_t* tile_expert,
                                void* workspace, size_t ws_bytes, int32_t* dev_err,
                                void* stream) {
-  if (!aligned16(xq) || !aligned16(xs) || !aligned16(xq_perm) || !aligned16(xs_perm) ||
+  if (!aligned16(xq) || !aligned4(xs) || !aligned16(xq_perm) || !aligned4(xs_perm) ||
       !aligned4(topk_idx) || !aligned4(counts) || !aligned4(offsets) || !aligned4(dst_row) ||
       !aligned4(src_row) || !aligned4(tile_expert) || !aligned4(workspace) || !aligned4(dev_err))
     return MOE_EINVAL;
-  if (!tk_ok(T, k) || !dim_ok(D) || D % 512 != 0 || E < 1 || E > kMaxExperts || k < 1 || k > E ||
+  if (!tk_ok(T, k) || !dim_ok(D) || D % 128 != 0 || E < 1 || E > kMaxExperts || k < 1 || k > E ||
       k > kMaxK || !mtile_ok(m_tile))
     return MOE_ESHAPE;
   const int64_t need = moe_capacity(T, k, E, m_tile);

@@ -254,6 +254,24 @@ __global__ __launch_bounds__(kThreads) void copy_kernel(
   }
 }
 
+// Scales of the FP8 payload into k-step words: out[s * m_cap + row] is word s of the
+// [T, D/32]-byte scale row of the token that fills permuted row `row` (its src_row
+// assignment / k), 0 for a pad row; rows at or past offsets[E] are not written. Threads
+// run along the rows, so the stores are whole lines; the loads are single words of the
+// scale rows (T * D/32 bytes, small enough to stay in L2).
+__global__ __launch_bounds__(kThreads) void scale_ksteps_kernel(
+    const uint32_t* __restrict__ xs, int nsw, int k, int E, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ src_row, int64_t m_cap, uint32_t* __restrict__ out) {
+  const int64_t used = max<int64_t>(0, min<int64_t>(offsets[E], m_cap));
+  const int64_t n = used * nsw;
+  for (int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x; g < n;
+       g += (int64_t)gridDim.x * kThreads) {
+    const int64_t st = g / used, row = g - st * used;
+    const int a = src_row[row];
+    out[st * m_cap + row] = a >= 0 ? xs[(int64_t)(a / k) * nsw + st] : 0u;
+  }
+}
+
 hipError_t launch_copy(int dt, const void* x, int T, int D, int k, int E,
                               const int32_t* dst_row, const int32_t* counts,
                               const int32_t* offsets, void* x_perm, hipStream_t s) {
@@ -323,12 +341,18 @@ hipError_t launch_permute_mx(const void* xq, const void* xs, const int32_t* topk
   hipLaunchKernelGGL(rank_kernel<false>, dim3(nbp + 1), dim3(kThreads), 0, s, topk_idx, T, k, E,
                      m_tile, 0, m_cap, nbh, hist, bad, counts, offsets, tile_expert, dev_err,
                      dst_row, src_row);
-  // the rows are copied as raw bytes: D code bytes = D/2 two-byte units, D/32 scale bytes
-  // = D/64 units (D % 512 == 0 keeps both whole 16-byte chunks); pad rows get zero bytes
-  // (code 0 is +0, scale byte 0 is 2^-127)
+  // the code rows are copied as raw bytes (D bytes = D/2 two-byte units, whole 16-byte
+  // chunks as D % 128 == 0); pad rows get zero bytes (code 0 is +0). The scales go into
+  // k-step words, zero for pad rows.
   const hipError_t e = launch_copy(kBF16, xq, T, D / 2, k, E, dst_row, counts, offsets, xq_perm, s);
   if (e != hipSuccess) return e;
-  return launch_copy(kBF16, xs, T, D / 64, k, E, dst_row, counts, offsets, xs_perm, s);
+  const int nsw = D / 128;
+  const int grid = (int)std::min<int64_t>(8 * cu_count(),
+                                          (m_cap * nsw + kThreads - 1) / kThreads);
+  hipLaunchKernelGGL(scale_ksteps_kernel, dim3(grid), dim3(kThreads), 0, s,
+                     static_cast<const uint32_t*>(xs), nsw, k, E, offsets, src_row, m_cap,
+                     static_cast<uint32_t*>(xs_perm));
+  return hipGetLastError();
 }
 
 }  // namespace moe

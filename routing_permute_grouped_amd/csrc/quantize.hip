@@ -6,7 +6,9 @@
 // largest OCP E4M3 value), so no value saturates, and -127 for an all-zero block. Each
 // value becomes the e4m3 code of v / 2^X rounded to nearest, ties to even. One thread
 // per block: the scale comes from frexp of the block's max (exact), the division by 2^X
-// is an exact ldexp, and the rounding to e4m3 is done on the float32 bits.
+// is an exact ldexp, and the rounding to e4m3 is done on the float32 bits. The scale
+// bytes go row by row ([R, C/32]) or in k-step words ([C/128][R] words of 4 bytes, byte
+// j of word (s, r) for block 4*s + j of row r), the layout the fc1 GEMM reads.
 #include <math.h>
 
 #include <algorithm>
@@ -37,9 +39,9 @@ __device__ __forceinline__ uint32_t e4m3_code(float v) {
   return sign | code;
 }
 
-template <typename TIn>
+template <typename TIn, bool KSTEPS>
 __global__ __launch_bounds__(kThreads) void quantize_mx_kernel(const TIn* __restrict__ x,
-                                                              int64_t nblocks, int C,
+                                                              int64_t nblocks, int64_t R, int C,
                                                               uint8_t* __restrict__ q,
                                                               uint8_t* __restrict__ scales) {
   constexpr int V = Chunk<TIn>::V;   // values per 16-byte chunk
@@ -69,25 +71,35 @@ __global__ __launch_bounds__(kThreads) void quantize_mx_kernel(const TIn* __rest
     }
     st16(q + b * 32, u32x4{w[0], w[1], w[2], w[3]});
     st16(q + b * 32 + 16, u32x4{w[4], w[5], w[6], w[7]});
-    scales[b] = (uint8_t)(X + 127);
+    if (KSTEPS) {
+      const int nb = C / 32;
+      const int64_t r = b / nb;
+      const int blk = (int)(b - r * nb);
+      scales[((int64_t)(blk >> 2) * R + r) * 4 + (blk & 3)] = (uint8_t)(X + 127);
+    } else {
+      scales[b] = (uint8_t)(X + 127);
+    }
   }
-  (void)C;
 }
 
 }  // namespace
 
-hipError_t launch_quantize_mx(int dt, const void* x, int64_t R, int C, void* q, void* scales,
-                              hipStream_t s) {
+template <typename TIn>
+void launch_quantize_t(const void* x, int64_t R, int C, void* q, void* scales, bool ksteps,
+                       hipStream_t s) {
   const int64_t nblocks = R * (C / 32);
   const int grid = (int)std::min<int64_t>(8 * cu_count(), (nblocks + kThreads - 1) / kThreads);
+  auto kern = ksteps ? quantize_mx_kernel<TIn, true> : quantize_mx_kernel<TIn, false>;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), 0, s, static_cast<const TIn*>(x),
+                     nblocks, R, C, static_cast<uint8_t*>(q), static_cast<uint8_t*>(scales));
+}
+
+hipError_t launch_quantize_mx(int dt, const void* x, int64_t R, int C, void* q, void* scales,
+                              bool ksteps, hipStream_t s) {
   if (dt == kF32)
-    hipLaunchKernelGGL(quantize_mx_kernel<float>, dim3(grid), dim3(kThreads), 0, s,
-                       static_cast<const float*>(x), nblocks, C, static_cast<uint8_t*>(q),
-                       static_cast<uint8_t*>(scales));
+    launch_quantize_t<float>(x, R, C, q, scales, ksteps, s);
   else
-    hipLaunchKernelGGL(quantize_mx_kernel<bf16_t>, dim3(grid), dim3(kThreads), 0, s,
-                       static_cast<const bf16_t*>(x), nblocks, C, static_cast<uint8_t*>(q),
-                       static_cast<uint8_t*>(scales));
+    launch_quantize_t<bf16_t>(x, R, C, q, scales, ksteps, s);
   return hipGetLastError();
 }
 

@@ -130,8 +130,9 @@ def moe_layer_masked(x: torch.Tensor, w1: torch.Tensor, w3: torch.Tensor, w2: to
 
 @dataclass
 class MxWeights:
-    """fc1's weights quantized once for the FP8 payload: e4m3 codes [E,F,D] and E8M0
-    scales [E,F,D/32] of w1 and w3."""
+    """fc1's weights quantized once for the FP8 payload: e4m3 codes [E,F,D] of w1 and w3,
+    and their E8M0 scales in the GEMM's k-step words (uint8 [D/128, E*F, 4]: word (s, r)
+    holds row r's scales of values 128*s .. 128*s + 127)."""
     w1q: torch.Tensor
     w1s: torch.Tensor
     w3q: torch.Tensor
@@ -139,8 +140,8 @@ class MxWeights:
 
     @staticmethod
     def quantize(w1: torch.Tensor, w3: torch.Tensor) -> "MxWeights":
-        w1q, w1s = B.moe_quantize_mxfp8(w1)
-        w3q, w3s = B.moe_quantize_mxfp8(w3)
+        w1q, w1s = B.moe_quantize_mxfp8(w1, layout=B.MOE_MX_KSTEPS)
+        w3q, w3s = B.moe_quantize_mxfp8(w3, layout=B.MOE_MX_KSTEPS)
         return MxWeights(w1q, w1s, w3q, w3s)
 
 

@@ -32,6 +32,13 @@ def to_host(t: torch.Tensor) -> np.ndarray:
     return t.contiguous().cpu().numpy()
 
 
+def mx_rows(words: np.ndarray) -> np.ndarray:
+    """MX scales in k-step words (uint8 [C/128, R, 4]: word (s, r) holds row r's scale
+    bytes of blocks 4s .. 4s+3) back to rows [R, C/32]; index reshuffling only."""
+    S, R, _ = words.shape
+    return np.ascontiguousarray(words.transpose(1, 0, 2)).reshape(R, 4 * S)
+
+
 def rel_err(got, ref) -> float:
     g, r = orc.values64(got), np.asarray(ref, dtype=np.float64)
     den = np.abs(r).max()

@@ -267,17 +267,19 @@ def test_grouped_masked_validation(kw, code):
 
 def test_mxfp8_calls_validate():
     q = lib.moe_quantize_mxfp8
-    assert q(5, FAKE, 16, 64, FAKE, FAKE, None) == MOE_EINVAL
-    assert q(1, FAKE + 2, 16, 64, FAKE, FAKE, None) == MOE_EINVAL
-    assert q(1, FAKE, 16, 64, FAKE, None, None) == MOE_EINVAL
-    assert q(1, FAKE, 0, 64, FAKE, FAKE, None) == MOE_ESHAPE
-    assert q(1, FAKE, 16, 48, FAKE, FAKE, None) == MOE_ESHAPE
+    assert q(5, FAKE, 16, 64, FAKE, FAKE, 0, None) == MOE_EINVAL
+    assert q(1, FAKE + 2, 16, 64, FAKE, FAKE, 0, None) == MOE_EINVAL
+    assert q(1, FAKE, 16, 64, FAKE, None, 0, None) == MOE_EINVAL
+    assert q(1, FAKE, 16, 64, FAKE, FAKE, 2, None) == MOE_EINVAL     # unknown layout
+    assert q(1, FAKE, 0, 64, FAKE, FAKE, 0, None) == MOE_ESHAPE
+    assert q(1, FAKE, 16, 48, FAKE, FAKE, 0, None) == MOE_ESHAPE
+    assert q(1, FAKE, 16, 96, FAKE, FAKE, 1, None) == MOE_ESHAPE     # k-step words: C % 128
     p = lambda **kw: lib.moe_permute_mxfp8(kw.get("xq", FAKE), FAKE, FAKE, kw.get("T", 64),
                                            kw.get("D", 512), 8, 2, kw.get("mt", 128),
                                            kw.get("m_cap", 2048), FAKE, FAKE, FAKE, FAKE, FAKE,
                                            FAKE, FAKE, FAKE, kw.get("ws", 1 << 20), FAKE, None)
     assert p(xq=None) == MOE_EINVAL
-    assert p(D=256) == MOE_ESHAPE           # scale rows must be whole 16-byte chunks
+    assert p(D=192) == MOE_ESHAPE           # k-step scale words need D % 128 == 0
     assert p(m_cap=100) == MOE_ECAPACITY
     assert p(ws=0) == MOE_EWORKSPACE
     f = lambda **kw: lib.moe_grouped_fc1_swiglu_mxfp8(

@@ -1,7 +1,8 @@
 """GPU parity of the FP8 payload (e4m3 codes with MX block scales) against the oracle.
 
-Bar: codes and scales bit-exact (the quantization is a deterministic rounding); the
-permute's metadata, code rows and scale rows bit-exact; fc1's h and the layer output
+Bar: codes and scales bit-exact (the quantization is a deterministic rounding), in both
+scale layouts (rows, and the GEMM's k-step words, compared after reshuffling them back
+into rows); the permute's metadata, code rows and scales bit-exact; fc1's h and the layer output
 within max|gpu - ref| / max|ref| <= 2e-2 (float32 accumulation of the same dequantized
 products, bf16 storage)."""
 import numpy as np
@@ -16,9 +17,10 @@ from tests import _parity as P
 pytestmark = pytest.mark.gpu
 
 
+@pytest.mark.parametrize("layout", [rpg.MOE_MX_ROWS, rpg.MOE_MX_KSTEPS])
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
-def test_quantize_matches_oracle_bit_for_bit(dt):
-    P.log(f"[mx] quantize {dt}")
+def test_quantize_matches_oracle_bit_for_bit(dt, layout):
+    P.log(f"[mx] quantize {dt} layout {layout}")
     rng = np.random.default_rng(81)
     x = (rng.standard_normal((300, 512)) * 10.0 ** rng.uniform(-8, 8, (300, 1))).astype(np.float32)
     x[4] = 0.0
@@ -27,10 +29,11 @@ def test_quantize_matches_oracle_bit_for_bit(dt):
     x[7, 64:96] = 2.0 ** -20 * rng.integers(-9, 9, 32)
     if dt == "bf16":
         x = W.f32_to_bf16_bits(x)
-    q, s = rpg.moe_quantize_mxfp8(P.to_dev(x))
+    q, s = rpg.moe_quantize_mxfp8(P.to_dev(x), layout=layout)
     torch.cuda.synchronize()
     rq, rs = orc.mx_quantize(x)
-    np.testing.assert_array_equal(P.to_host(s), rs)
+    s = P.to_host(s)
+    np.testing.assert_array_equal(P.mx_rows(s) if layout == rpg.MOE_MX_KSTEPS else s, rs)
     np.testing.assert_array_equal(P.to_host(q), rq)
 
 
@@ -66,13 +69,16 @@ def test_mxfp8_layer_parity(name, split_k):
     h = {n: P.to_host(v) if isinstance(v, torch.Tensor) else v for n, v in g.items()}
     for key in ("xq", "xs"):
         np.testing.assert_array_equal(h[key], ref[key], err_msg=key)
-    for key, rk in (("w1q", "w1q"), ("w1s", "w1s"), ("w3q", "w3q"), ("w3s", "w3s")):
-        np.testing.assert_array_equal(P.to_host(getattr(mw, key)), ref[rk], err_msg=key)
+    for key in ("w1q", "w3q"):
+        np.testing.assert_array_equal(P.to_host(getattr(mw, key)), ref[key], err_msg=key)
+    for key in ("w1s", "w3s"):   # k-step words over the E*F rows
+        got = P.mx_rows(P.to_host(getattr(mw, key))).reshape(ref[key].shape)
+        np.testing.assert_array_equal(got, ref[key], err_msg=key)
     for key in ("counts", "offsets", "dst_row", "src_row", "tile_expert"):
         np.testing.assert_array_equal(h[key], ref[key], err_msg=key)
     used = int(ref["offsets"][-1])
     np.testing.assert_array_equal(h["xq_perm"][:used], ref["xq_perm"][:used])
-    np.testing.assert_array_equal(h["xs_perm"][:used], ref["xs_perm"][:used])
+    np.testing.assert_array_equal(P.mx_rows(h["xs_perm"])[:used], ref["xs_perm"][:used])
     pad = ref["src_row"][:used] < 0
     hv = orc.values64(h["h"][:used])
     assert np.all(np.isfinite(hv)) and np.all(hv[pad] == 0)
