@@ -626,7 +626,9 @@ __device__ __forceinline__ void mx_scale_words(const Tile& t, const MxScales& ms
 }
 
 // The MFMAs of one k step (two 64-wide slices) from the LDS stage at sA / sB, with the
-// next stage's loads issued by `issue(ks)` at the start of slice ks. Lane half h takes
+// next stage's loads issued in two halves by `issue(part)`: the A pieces before the
+// first MFMA, the panel pieces after the first panel block's MFMAs (a quarter of the
+// step; at the start of the second slice they land 2-4% later). Lane half h takes
 // 16-byte chunks 4*ks + h and 4*ks + 2 + h of slice ks: the first half of both lanes of
 // a row is the slice's first MX block, the second half the other. There is one set of
 // fragments (8 registers each; a second set would not fit beside the 128 accumulators),
@@ -661,7 +663,7 @@ __device__ __forceinline__ void mx_step(const char* sA, const char* sB,
   for (int mb = 0; mb < WM; ++mb) af[mb] = frag(sA, arow0 + mb * 32 + fr, 0);
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
-    issue(ks);
+    if (ks == 0) issue(0);
     // lane half h supplies the scale of block 2*ks + h of the step, in byte 0 (the byte
     // the instruction reads with op_sel 0)
     const int sh = 8 * (2 * ks + half);
@@ -676,6 +678,7 @@ __device__ __forceinline__ void mx_step(const char* sA, const char* sB,
         __builtin_amdgcn_sched_barrier(0);
       }
       if (ks == 0) wf[nb] = frag(sB, prow0 + nb * 32 + fr, 1);
+      if (ks == 0 && nb == 0) issue(1);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
