@@ -33,9 +33,12 @@ METRIC = "MoE-layer tokens/sec; grouped-GEMM TFLOP/s (% bf16 MFMA peak); permute
 # FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0, the factors measured on a device copy of known
 # size (bench.py --copy-calibration 256). Taken for the current kernel source; a
 # workload without an entry reports null. Forward: grouped fc1; backward: the wgrad of
-# fc1 ([dW1 | dW3]).
-TRAFFIC_BYTES_PER_LAUNCH = {"dense8_bf16": 4.493e9}
-BWD_TRAFFIC_BYTES_PER_LAUNCH = {"dense8_bf16": 8.600e9}
+# fc1 ([dW1 | dW3]); FP8 payload: the FP8 fc1; decode: the masked grouped GEMM's fc1 and
+# fc2 launches (with their split-K reductions) of one step.
+TRAFFIC_BYTES_PER_LAUNCH = {"dense8_bf16": 4.343e9}
+BWD_TRAFFIC_BYTES_PER_LAUNCH = {"dense8_bf16": 8.590e9}
+FP8_TRAFFIC_BYTES_PER_LAUNCH = {"dense8_bf16": 2.769e9}
+MASKED_TRAFFIC_BYTES_PER_STEP = {"decode8_bf16": 2.981e9}
 
 
 def parse():
@@ -444,8 +447,9 @@ def bench_masked(args, cfg, d, inp) -> dict:
         "roofline": {"kernel": "grouped fc1 + fc2 on the masked layout "
                                "(gg_bf16_kernel<kFc1>, <kFc2>)", "bound": "hbm",
                      "achieved": gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                     "frac": gbps / PEAK_HBM_GBPS, "traffic": None,
-                     "traffic_unit": "bytes per launch",
+                     "frac": gbps / PEAK_HBM_GBPS,
+                     "traffic": MASKED_TRAFFIC_BYTES_PER_STEP.get(cfg.name),
+                     "traffic_unit": "bytes per step (fc1 + fc2 launches)",
                      "algorithmic_bytes": gemm_bytes,
                      "note": "active experts' w1, w3, w2 once plus the valid rows' x, h "
                              "(written and read) and y"},
@@ -541,7 +545,9 @@ def bench_fp8(args, cfg, d, buf, shared, gws, flush, n_valid) -> dict:
         "fc1": {"kernel": "grouped fc1 + silu(a)*b on MX e4m3 (gg_bf16_kernel<kFc1, MX>)",
                 "achieved_tflops": fc1_tf, "peak_fp8_tflops": PEAK_FP8_TFLOPS,
                 "frac_fp8_peak": fc1_tf / PEAK_FP8_TFLOPS,
-                "frac_bf16_peak": fc1_tf / PEAK_BF16_TFLOPS},
+                "frac_bf16_peak": fc1_tf / PEAK_BF16_TFLOPS,
+                "traffic": FP8_TRAFFIC_BYTES_PER_LAUNCH.get(cfg.name),
+                "traffic_unit": "bytes per launch"},
         "stage_us_mean": avg,
         "out_rel_diff_vs_bf16_step": dev_out,
         "note": "x quantized per token (32-value blocks, power-of-two scales, no saturation); "
