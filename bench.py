@@ -38,7 +38,7 @@ METRIC = "MoE-layer tokens/sec; grouped-GEMM TFLOP/s (% bf16 MFMA peak); permute
 TRAFFIC_BYTES_PER_LAUNCH = {"dense8_bf16": 4.343e9}
 BWD_TRAFFIC_BYTES_PER_LAUNCH = {"dense8_bf16": 8.590e9}
 FP8_TRAFFIC_BYTES_PER_LAUNCH = {"dense8_bf16": 2.769e9}
-MASKED_TRAFFIC_BYTES_PER_STEP = {"decode8_bf16": 2.981e9}
+MASKED_TRAFFIC_BYTES_PER_STEP = {}
 
 
 def parse():
@@ -444,8 +444,9 @@ def bench_masked(args, cfg, d, inp) -> dict:
         "config": {"workload": cfg.name, "T": T, "D": D, "F": F, "E": E, "k": k,
                    "layout": "masked", "cap": cap, "n_shared": cfg.n_shared,
                    "F_shared": cfg.F_shared, "split_k_tail": gws is not None},
-        "roofline": {"kernel": "grouped fc1 + fc2 on the masked layout "
-                               "(gg_bf16_kernel<kFc1>, <kFc2>)", "bound": "hbm",
+        "roofline": {"kernel": "grouped fc1 + fc2 on the masked layout (dec_kernel<fc1>, "
+                               "<fc2> for bf16 slabs of at most 128 rows, else "
+                               "gg_bf16_kernel)", "bound": "hbm",
                      "achieved": gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": gbps / PEAK_HBM_GBPS,
                      "traffic": MASKED_TRAFFIC_BYTES_PER_STEP.get(cfg.name),

@@ -17,7 +17,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB_NAME = "libmoe_mi355x.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 SOURCES = ["moe_capi.hip", "route.hip", "permute.hip", "grouped_gemm.hip", "combine.hip",
-           "quantize.hip"]
+           "quantize.hip", "decode_gemm.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -37,6 +37,7 @@
 
 #include "common.hpp"
 #include "kernels.hpp"
+#include "lds_dma.hpp"
 
 namespace moe {
 namespace {
@@ -149,39 +150,6 @@ __device__ __forceinline__ int block_scan_excl(int v, int* wtot) {
 struct Tile {
   int e, m0, rows, n0;
 };
-
-// LDS byte address of a pointer into a __shared__ array.
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) char*)p);
-}
-
-// Raw buffer descriptor over [base, base + bytes): the hardware zero-fills any lane
-// whose offset falls outside the range.
-typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ i32x4 buffer_rsrc(const void* base, uint32_t bytes) {
-  const uint64_t a = (uint64_t)(uintptr_t)base;
-  i32x4 r;
-  r[0] = __builtin_amdgcn_readfirstlane((int32_t)(uint32_t)a);
-  r[1] = __builtin_amdgcn_readfirstlane((int32_t)((uint32_t)(a >> 32) & 0xffffu));
-  r[2] = __builtin_amdgcn_readfirstlane((int32_t)bytes);
-  r[3] = 0x00020000;   // raw (untyped) buffer, 32-bit data format
-  return r;
-}
-
-// 16 bytes per lane from a buffer straight into LDS: lane l reads base + voff_l + soff
-// and the 64 lanes of the wave fill 1 KiB at LDS address `lds` (wave-uniform), lane l
-// at lds + 16*l. Buffer addressing takes a 32-bit offset per lane and the k-step in a
-// scalar offset, which issues faster than 64-bit flat addresses. Issued as inline
-// assembly so the compiler adds no waits of its own for it; the pipeline below waits
-// with an explicit s_waitcnt vmcnt(0) and a barrier before any wave reads the stage
-// the loads fill.
-__device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
-               :
-               : "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(soff)),
-                 "s"(__builtin_amdgcn_readfirstlane(lds))
-               : "memory", "m0");
-}
 
 // Each operand of a tile is staged per k-step as 256 "rows" (A rows or panel rows,
 // the MFMA's M or N index) x 64 k values, in one of two LDS layouts:
@@ -1419,6 +1387,8 @@ hipError_t launch_grouped_swiglu(int dt, int phases, const void* x_perm, const i
                                  const void* w3, const void* w2, void* h, void* ab, void* y_perm,
                                  void* workspace, size_t ws_bytes, hipStream_t s) {
   const Segs sg{offsets, counts, cap};
+  if (cap > 0 && phases == 3 && !ab && decode_swiglu_ok(dt, cap, D, F))
+    return launch_decode_swiglu(x_perm, counts, cap, E, D, F, w1, w3, w2, h, y_perm, s);
   if (phases & 1) {
     const hipError_t e = launch_mgrouped(dt, kFc1, false, x_perm, sg, tile_expert, E, D, m_tile,
                                          m_cap, w1, w3, D, h, ab, nullptr, F, workspace, ws_bytes,

@@ -55,6 +55,13 @@ hipError_t launch_grouped_fc1_mx(const void* xq_perm, const void* xs_perm,
                                  const void* w3s, void* h, void* workspace, size_t ws_bytes,
                                  hipStream_t s);
 
+// decode path of the masked grouped SwiGLU (bf16, cap <= 128, D and F multiples of 128):
+// the active experts' weights streamed past their few rows
+bool decode_swiglu_ok(int dt, int cap, int D, int F);
+hipError_t launch_decode_swiglu(const void* x, const int32_t* counts, int cap, int E, int D,
+                                int F, const void* w1, const void* w3, const void* w2, void* h,
+                                void* y, hipStream_t s);
+
 // MX quantization of x [R, C] (dt) -> e4m3 codes [R, C] and E8M0 scales, [R, C/32]
 // bytes or (ksteps) [C/128][R] words of four bytes
 hipError_t launch_quantize_mx(int dt, const void* x, int64_t R, int C, void* q, void* scales,
