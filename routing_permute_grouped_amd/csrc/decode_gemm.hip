@@ -1,6 +1,7 @@
-// Grouped SwiGLU for decode on the masked layout ("Expert Parallelism (EP)",
-// llm-infra-atlas, section 2: decode runs the masked grouped GEMM, each local expert's
-// rows sitting in a fixed slab whose valid count is known only on the device).
+// Grouped SwiGLU for decode ("Expert Parallelism (EP)", llm-infra-atlas, section 2:
+// decode runs the masked grouped GEMM, each local expert's rows sitting in a fixed slab
+// whose valid count is known only on the device). Also taken by contiguous segments in
+// a row buffer of at most 128 rows (the shared experts of a decode batch).
 //
 // At decode sizes an expert holds a few rows (tokens), so the GEMM is a stream of the
 // active experts' weights past those rows: its bound is HBM, and what it needs is many
@@ -50,14 +51,34 @@ __device__ __forceinline__ float silu_mul(float a, float b) {
   return a / (1.0f + __expf(-a)) * b;
 }
 
-// FC1: out [E*cap, N] = silu(X w1^T) * (X w3^T) with N = F, K = D; else out = X w2^T with
-// N = D, K = F (W3 unused), for expert e's rows [e*cap, e*cap + rows), rows <= 16*NB.
+// The rows of expert e: the masked layout's slab [e*cap, e*cap + min(counts[e], cap))
+// (offsets null), or the contiguous layout's segment [offsets[e], offsets[e+1]) of an
+// m_cap-row buffer, clamped into [0, min(offsets[E], m_cap)] (offsets that break the
+// contract can only shrink the work) and to at most cap rows.
+struct DecSegs {
+  const int32_t* offsets;
+  const int32_t* counts;
+  int cap, E, m_cap;
+  __device__ void get(int e, int& r0, int& rows) const {
+    if (offsets) {
+      const int lim = max(0, min(offsets[E], m_cap));
+      r0 = max(0, min(offsets[e], lim));
+      rows = max(0, min(min(offsets[e + 1], lim) - r0, cap));
+    } else {
+      r0 = e * cap;
+      rows = max(0, min(counts[e], cap));
+    }
+  }
+};
+
+// FC1: out [rows, N] = silu(X w1^T) * (X w3^T) with N = F, K = D; else out = X w2^T with
+// N = D, K = F (W3 unused), for expert e's rows [r0, r0 + rows), rows <= 16*NB.
 // NB: row blocks of 16 computed (exactly the expert's, so the loop has no branch on the
 // count). KS: 32-value slices per chunk (4 or 8). PD: weight chunks in flight per wave.
 // N is a multiple of 64, K of 32*KS.
 template <bool FC1, int NB, int KS, int PD>
 __device__ __forceinline__ void dec_body(char* xs, int xbytes, const bf16_t* __restrict__ X,
-                                         int e, int rows, int cap, int K, int N,
+                                         int e, int r0, int rows, int K, int N,
                                          const bf16_t* __restrict__ W1,
                                          const bf16_t* __restrict__ W3,
                                          bf16_t* __restrict__ out) {
@@ -89,7 +110,7 @@ __device__ __forceinline__ void dec_body(char* xs, int xbytes, const bf16_t* __r
   // row copies: piece q = wave + 4*i (i < NP) is LDS rows RPP*q .. of a buffer; lane l
   // fills row r = RPP*q + l/UPR, physical unit l%UPR, i.e. the row's unit
   // (l%UPR) ^ (r%16)
-  const i32x4 rs = buffer_rsrc(X + (size_t)e * cap * K, (uint32_t)rows * K * 2u);
+  const i32x4 rs = buffer_rsrc(X + (size_t)r0 * K, (uint32_t)rows * K * 2u);
   uint32_t voff[NP];
 #pragma unroll
   for (int i = 0; i < NP; ++i) {
@@ -164,7 +185,7 @@ __device__ __forceinline__ void dec_body(char* xs, int xbytes, const bf16_t* __r
   for (int b = 0; b < NB; ++b) {
     const int r = 16 * b + fr;
     if (r < rows) {
-      bf16_t* p = out + ((size_t)e * cap + r) * N + col;
+      bf16_t* p = out + ((size_t)r0 + r) * N + col;
       const f32x4& a = acc[0][b];
       if (FC1) {
         const f32x4& u = acc[NW - 1][b];
@@ -180,21 +201,21 @@ __device__ __forceinline__ void dec_body(char* xs, int xbytes, const bf16_t* __r
 // One workgroup per (64 output columns, expert); TB: the most row blocks any expert may
 // have (cap <= 16*TB). The body is chosen by the expert's own number of row blocks.
 template <bool FC1, int TB, int KS, int PD>
-__global__ __launch_bounds__(DW * 64) void dec_kernel(const bf16_t* __restrict__ X,
-                                                      const int32_t* __restrict__ counts,
-                                                      int cap, int K, int N,
+__global__ __launch_bounds__(DW * 64) void dec_kernel(const bf16_t* __restrict__ X, DecSegs sg,
+                                                      int K, int N,
                                                       const bf16_t* __restrict__ W1,
                                                       const bf16_t* __restrict__ W3,
                                                       bf16_t* __restrict__ out) {
   constexpr int XBYTES = TB * 16 * KS * 64;   // one row buffer
   __shared__ __attribute__((aligned(1024))) char xs[2 * XBYTES];
   const int e = blockIdx.y;
-  const int rows = max(0, min(counts[e], cap));
+  int r0, rows;
+  sg.get(e, r0, rows);
   if (rows == 0) return;   // uniform over the workgroup: the expert's weights stay unread
 #define DEC_CASE(n)                                                                         \
   case n:                                                                                   \
     if (TB >= n)                                                                            \
-      dec_body<FC1, (TB >= n ? n : 1), KS, PD>(xs, XBYTES, X, e, rows, cap, K, N, W1, W3, out); \
+      dec_body<FC1, (TB >= n ? n : 1), KS, PD>(xs, XBYTES, X, e, r0, rows, K, N, W1, W3, out); \
     break;
   switch ((rows + 15) >> 4) {
     DEC_CASE(1)
@@ -205,46 +226,53 @@ __global__ __launch_bounds__(DW * 64) void dec_kernel(const bf16_t* __restrict__
     DEC_CASE(6)
     DEC_CASE(7)
     default:
-      if (TB >= 8) dec_body<FC1, (TB >= 8 ? 8 : 1), KS, PD>(xs, XBYTES, X, e, rows, cap, K, N, W1, W3, out);
+      if (TB >= 8) dec_body<FC1, (TB >= 8 ? 8 : 1), KS, PD>(xs, XBYTES, X, e, r0, rows, K, N, W1, W3, out);
       break;
   }
 #undef DEC_CASE
 }
 
 template <bool FC1, int KS, int PD>
-void launch_dec(int tb, const void* X, const int32_t* counts, int cap, int E, int K, int N,
-                const void* W1, const void* W3, void* out, hipStream_t s) {
+void launch_dec(int tb, const void* X, DecSegs sg, int E, int K, int N, const void* W1,
+                const void* W3, void* out, hipStream_t s) {
   const dim3 grid((N + DW * DCOLS - 1) / (DW * DCOLS), E);
   const bf16_t* x = static_cast<const bf16_t*>(X);
   const bf16_t* w1 = static_cast<const bf16_t*>(W1);
   const bf16_t* w3 = static_cast<const bf16_t*>(W3);
   bf16_t* o = static_cast<bf16_t*>(out);
   if (tb <= 2)
-    hipLaunchKernelGGL((dec_kernel<FC1, 2, KS, PD>), grid, dim3(DW * 64), 0, s, x, counts, cap,
-                       K, N, w1, w3, o);
+    hipLaunchKernelGGL((dec_kernel<FC1, 2, KS, PD>), grid, dim3(DW * 64), 0, s, x, sg, K, N, w1,
+                       w3, o);
   else if (tb <= 4)
-    hipLaunchKernelGGL((dec_kernel<FC1, 4, KS, PD>), grid, dim3(DW * 64), 0, s, x, counts, cap,
-                       K, N, w1, w3, o);
+    hipLaunchKernelGGL((dec_kernel<FC1, 4, KS, PD>), grid, dim3(DW * 64), 0, s, x, sg, K, N, w1,
+                       w3, o);
   else
-    hipLaunchKernelGGL((dec_kernel<FC1, 8, 4, PD>), grid, dim3(DW * 64), 0, s, x, counts, cap,
-                       K, N, w1, w3, o);
+    hipLaunchKernelGGL((dec_kernel<FC1, 8, 4, PD>), grid, dim3(DW * 64), 0, s, x, sg, K, N, w1,
+                       w3, o);
 }
 
 }  // namespace
 
-bool decode_swiglu_ok(int dt, int cap, int D, int F) {
-  return dt == kBF16 && cap >= 1 && cap <= 128 && D % KMIN == 0 && F % KMIN == 0 &&
-         (int64_t)cap * (D > F ? D : F) * 2 < ((int64_t)1 << 32);
+int decode_rows_max(int dt, int cap, int64_t m_cap, int E, int D, int F) {
+  const int64_t rmax = cap > 0 ? cap : m_cap;
+  if (dt != kBF16 || rmax < 1 || rmax > 128 || D % KMIN != 0 || F % KMIN != 0) return 0;
+  // a few experts (a dense or shared FFN) give too few workgroups to stream at the HBM
+  // rate; the split-K tile kernel serves them better
+  if ((int64_t)E * (std::min(D, F) / (DW * DCOLS)) < 2 * cu_count()) return 0;
+  if ((cap > 0 ? (int64_t)cap : m_cap) * (D > F ? D : F) * 2 >= ((int64_t)1 << 32)) return 0;
+  return (int)rmax;
 }
 
-hipError_t launch_decode_swiglu(const void* x, const int32_t* counts, int cap, int E, int D,
-                                int F, const void* w1, const void* w3, const void* w2, void* h,
-                                void* y, hipStream_t s) {
-  const int tb = (cap + 15) / 16;
+hipError_t launch_decode_swiglu(int phases, const void* x, const int32_t* offsets,
+                                const int32_t* counts, int cap, int rmax, int E, int D, int F,
+                                const void* w1, const void* w3, const void* w2, void* h, void* y,
+                                hipStream_t s) {
+  const int tb = (rmax + 15) / 16;
+  const DecSegs sg{offsets, counts, offsets ? rmax : cap, E, rmax};
   // fc1 keeps two weight streams in flight per chunk, fc2 one: the same registers.
   // (256-value chunks, 512 contiguous bytes per row and request, measured no faster.)
-  launch_dec<true, 4, 2>(tb, x, counts, cap, E, D, F, w1, w3, h, s);
-  launch_dec<false, 4, 4>(tb, h, counts, cap, E, F, D, w2, w2, y, s);
+  if (phases & 1) launch_dec<true, 4, 2>(tb, x, sg, E, D, F, w1, w3, h, s);
+  if (phases & 2) launch_dec<false, 4, 4>(tb, h, sg, E, F, D, w2, w2, y, s);
   return hipGetLastError();
 }
 

@@ -1387,8 +1387,11 @@ hipError_t launch_grouped_swiglu(int dt, int phases, const void* x_perm, const i
                                  const void* w3, const void* w2, void* h, void* ab, void* y_perm,
                                  void* workspace, size_t ws_bytes, hipStream_t s) {
   const Segs sg{offsets, counts, cap};
-  if (cap > 0 && phases == 3 && !ab && decode_swiglu_ok(dt, cap, D, F))
-    return launch_decode_swiglu(x_perm, counts, cap, E, D, F, w1, w3, w2, h, y_perm, s);
+  // decode-sized batches (at most 128 rows per expert) stream the weights instead
+  const int rmax = ab ? 0 : decode_rows_max(dt, cap, m_cap, E, D, F);
+  if (rmax > 0)
+    return launch_decode_swiglu(phases, x_perm, cap > 0 ? nullptr : offsets, counts, cap, rmax,
+                                E, D, F, w1, w3, w2, h, y_perm, s);
   if (phases & 1) {
     const hipError_t e = launch_mgrouped(dt, kFc1, false, x_perm, sg, tile_expert, E, D, m_tile,
                                          m_cap, w1, w3, D, h, ab, nullptr, F, workspace, ws_bytes,

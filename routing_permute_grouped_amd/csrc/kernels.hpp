@@ -55,12 +55,16 @@ hipError_t launch_grouped_fc1_mx(const void* xq_perm, const void* xs_perm,
                                  const void* w3s, void* h, void* workspace, size_t ws_bytes,
                                  hipStream_t s);
 
-// decode path of the masked grouped SwiGLU (bf16, cap <= 128, D and F multiples of 128):
-// the active experts' weights streamed past their few rows
-bool decode_swiglu_ok(int dt, int cap, int D, int F);
-hipError_t launch_decode_swiglu(const void* x, const int32_t* counts, int cap, int E, int D,
-                                int F, const void* w1, const void* w3, const void* w2, void* h,
-                                void* y, hipStream_t s);
+// decode path of the grouped SwiGLU (bf16; the masked layout with cap <= 128, or
+// contiguous segments in m_cap <= 128 rows; D and F multiples of 128): the active
+// experts' weights streamed past their few rows. decode_rows_max returns the most rows
+// an expert can have there, 0 when the path does not apply (also when E*min(D,F)/64 gives
+// fewer than two workgroups per CU); phases bit 0 fc1, bit 1 fc2.
+int decode_rows_max(int dt, int cap, int64_t m_cap, int E, int D, int F);
+hipError_t launch_decode_swiglu(int phases, const void* x, const int32_t* offsets,
+                                const int32_t* counts, int cap, int rmax, int E, int D, int F,
+                                const void* w1, const void* w3, const void* w2, void* h, void* y,
+                                hipStream_t s);
 
 // MX quantization of x [R, C] (dt) -> e4m3 codes [R, C] and E8M0 scales, [R, C/32]
 // bytes or (ksteps) [C/128][R] words of four bytes

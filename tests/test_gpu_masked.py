@@ -18,20 +18,28 @@ from tests import _parity as P
 
 pytestmark = pytest.mark.gpu
 
+# The decode GEMM serves bf16 slabs of at most 128 rows when the experts give at least two
+# workgroups of 64 output columns per CU (E * min(D, F) / 64 >= 512 on 256 CUs); the
+# other cases run on the tile kernel. Both paths are covered here.
 CASES = {
+    # tile kernel: 8 experts of D=512 are too few workgroups for the decode GEMM
     "decode8": W.shrink(W.preset("decode8_bf16"), D=512, F=1024),
-    "decode64_shared2": W.shrink(W.preset("decode64_shared2_bf16"), T=96, D=256, F=320,
-                                 F_shared=192, cap=96),
-    # the skewed router: its hot expert gets far more than cap slots, some get none
-    "skew_drops": dataclasses.replace(W.shrink(W.preset("skew32_zipf_bf16"), T=128, D=256,
-                                               F=256), cap=32),
-    "etp_given_masked": dataclasses.replace(
-        W.shrink(W.preset("etp_shard32_bf16"), D=512, F=256, poisson_mean=20.0), cap=48),
     "tiny_f32_masked": dataclasses.replace(W.preset("tiny_f32"), T=40, cap=16),
-    # 99..130 rows per expert in slabs of 128: 7 and 8 row blocks of 16, partial last
-    # blocks, two slots dropped (the decode GEMM's largest bodies)
-    "wide_slabs": dataclasses.replace(W.shrink(W.preset("decode8_bf16"), T=480, D=256, F=384),
-                                      cap=128),
+    # decode GEMM: one row block per expert, shared experts beside (tile kernel, E=1)
+    "decode64_shared2": W.shrink(W.preset("decode64_shared2_bf16"), T=96, D=512, F=512,
+                                 F_shared=256, cap=96),
+    # the skewed router: its hot experts get far more than cap slots, 20 get none
+    "skew_drops": dataclasses.replace(W.shrink(W.preset("skew32_zipf_bf16"), T=128, D=1024,
+                                               F=1024), cap=32),
+    "etp_given_masked": dataclasses.replace(
+        W.shrink(W.preset("etp_shard32_bf16"), D=1024, F=1024, poisson_mean=20.0), cap=48),
+    # 3 and 4 row blocks, slabs of 64 with drops
+    "mid_slabs": dataclasses.replace(W.shrink(W.preset("decode64_shared2_bf16"), T=600, D=512,
+                                              F=512), cap=64, n_shared=0),
+    # 5 to 8 row blocks of 16 in slabs of 128, partial last blocks, 13 slots dropped (the
+    # decode GEMM's largest bodies)
+    "wide_slabs": dataclasses.replace(W.shrink(W.preset("decode64_shared2_bf16"), T=1100,
+                                               D=512, F=512), cap=128, n_shared=0),
 }
 
 
