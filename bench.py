@@ -56,11 +56,13 @@ def parse():
                     help="skip the timed backward pass (reported under \"backward\")")
     ap.add_argument("--no-split-k", action="store_true",
                     help="give the grouped GEMMs no workspace (every tile whole)")
-    ap.add_argument("--shared-overlap", choices=["none", "start", "after-route"],
-                    default="none",
+    ap.add_argument("--shared-overlap", choices=["auto", "none", "start", "after-route"],
+                    default="auto",
                     help="run the shared experts' GEMM on a second stream (with its own "
                          "split-K workspace), from the step's start or after the router; the "
-                         "per-stage times of route / permute then include waiting for CUs")
+                         "per-stage times of route / permute then include waiting for CUs. "
+                         "auto: from the start for decode steps (masked layout), where the "
+                         "shared GEMM leaves most CUs idle, none for the others")
     ap.add_argument("--flush-mib", type=int, default=512,
                     help="MiB written between timed steps to evict the Infinity Cache (0: none)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -160,6 +162,8 @@ def main():
         return torch.from_numpy(a).to(dev)
 
     d = {n: up(a) for n, a in inp.items() if isinstance(a, np.ndarray)}
+    if args.shared_overlap == "auto":
+        args.shared_overlap = "start" if cfg.cap else "none"
     if cfg.cap:
         print(json.dumps(bench_masked(args, cfg, d, inp)), flush=True)
         return
@@ -364,14 +368,34 @@ def bench_masked(args, cfg, d, inp) -> dict:
         buf["hs"] = torch.empty((rows.m_cap, shared.w1.shape[1]), dtype=tdt, device=dev)
         buf["ys"] = torch.empty((rows.m_cap, D), dtype=tdt, device=dev)
     marks = ["route", "permute", "gemm", "shared", "combine"]
+    overlap = shared is not None and args.shared_overlap != "none"
+    if overlap:
+        side = torch.cuda.Stream(device=dev)          # default priority
+        gws_side = None if args.no_split_k else rpg.grouped_workspace(dev)
+        ev_go, ev_sh = torch.cuda.Event(), torch.cuda.Event()
+
+    def shared_gemm(on, ws):
+        rpg.moe_grouped_swiglu(d["x"], rows.offsets, rows.tile_expert, shared.w1, shared.w3,
+                               shared.w2, mt, m_cap=rows.m_cap, h=buf["hs"], y_perm=buf["ys"],
+                               workspace=ws, stream=on)
+
+    def launch_side():
+        ev_go.record(stream)
+        side.wait_event(ev_go)
+        shared_gemm(side, gws_side)
+        ev_sh.record(side)
 
     def step(ev=None, contiguous=False):
         def mark(i):
             if ev is not None:
                 ev[i].record(stream)
         mark(0)
+        if overlap and args.shared_overlap == "start":
+            launch_side()
         rpg.moe_route(d["x"], d["wg"], k, bias=d.get("bias"), topk_idx=buf["idx"],
                       topk_w=buf["w"], stream=stream)
+        if overlap and args.shared_overlap == "after-route":
+            launch_side()
         mark(1)
         if contiguous:
             p = rpg.moe_permute(d["x"], buf["idx"], E, mt, m_cap=m_cap, out=cbuf, stream=stream)
@@ -393,9 +417,10 @@ def bench_masked(args, cfg, d, inp) -> dict:
         mark(3)
         sh = None
         if shared is not None:
-            rpg.moe_grouped_swiglu(d["x"], rows.offsets, rows.tile_expert, shared.w1, shared.w3,
-                                   shared.w2, mt, m_cap=rows.m_cap, h=buf["hs"], y_perm=buf["ys"],
-                                   workspace=gws, stream=stream)
+            if overlap:
+                stream.wait_event(ev_sh)
+            else:
+                shared_gemm(stream, gws)
             sh = buf["ys"][:T]
         mark(4)
         rpg.moe_combine(y, p["dst_row"], buf["w"], shared=sh, out=buf["out"], m_cap=mc,
@@ -443,6 +468,7 @@ def bench_masked(args, cfg, d, inp) -> dict:
         "data": "synthetic (seeded numpy PCG64 draws; Gaussian inputs and weights)",
         "config": {"workload": cfg.name, "T": T, "D": D, "F": F, "E": E, "k": k,
                    "layout": "masked", "cap": cap, "n_shared": cfg.n_shared,
+                   "shared_overlap": args.shared_overlap if shared is not None else None,
                    "F_shared": cfg.F_shared, "split_k_tail": gws is not None},
         "roofline": {"kernel": "grouped fc1 + fc2 on the masked layout (dec_kernel<fc1>, "
                                "<fc2> for bf16 slabs of at most 128 rows, else "
