@@ -38,7 +38,7 @@ METRIC = "MoE-layer tokens/sec; grouped-GEMM TFLOP/s (% bf16 MFMA peak); permute
 TRAFFIC_BYTES_PER_LAUNCH = {"dense8_bf16": 4.343e9}
 BWD_TRAFFIC_BYTES_PER_LAUNCH = {"dense8_bf16": 8.590e9}
 FP8_TRAFFIC_BYTES_PER_LAUNCH = {"dense8_bf16": 2.769e9}
-MASKED_TRAFFIC_BYTES_PER_STEP = {}
+MASKED_TRAFFIC_BYTES_PER_STEP = {"decode8_bf16": 2.922e9, "decode64_shared2_bf16": 1.167e9}
 
 
 def parse():
