@@ -113,3 +113,46 @@ def test_mxfp8_full_size_dense8_sampled():
     e = P.rel_err(got, out)
     P.log(f"[mx] full-size dense8: out rel err {e:.2e}")
     assert e <= P.TOL["bf16"]
+
+
+@pytest.mark.parametrize("name", ["fine64_shared2_bf16", "skew32_zipf_bf16", "etp_shard32_bf16"])
+def test_mxfp8_full_size_sampled(name):
+    """The other workloads at full size, in the bench's launch configuration (split-K
+    workspace): routing and layout bit-exact; sampled tokens' outputs against the oracle,
+    which quantizes only the experts those tokens use (tokens are picked among those
+    whose experts all lie in the few most-used ones)."""
+    cfg = W.preset(name)
+    P.log(f"[mx] full-size {name}: generating")
+    inp = W.generate(cfg, seed=0)
+    cfg = inp["cfg"]
+    d = {n: P.to_dev(a) for n, a in inp.items() if isinstance(a, np.ndarray)}
+    if "topk_idx" in inp:
+        idx, w = inp["topk_idx"], inp["topk_w"].astype(np.float64)
+        kw = dict(topk_idx=d["topk_idx"], topk_w=d["topk_w"])
+    else:
+        idx, w, _ = orc.route(inp["x"], inp["wg"], cfg.k, "bf16", inp.get("bias"))
+        kw = dict(wg=d["wg"], bias=d.get("bias"))
+    sw = rpg.SharedExperts.from_stacked(d["ws1"], d["ws3"], d["ws2"]) if "ws1" in d else None
+    mw = rpg.MxWeights.quantize(d["w1"], d["w3"])
+    g = rpg.moe_layer_mxfp8(d["x"], mw, d["w2"], cfg.k, cfg.m_tile, shared=sw, **kw)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(P.to_host(g["topk_idx"]), idx)
+    lay = orc.dispatch_layout(idx, cfg.E, cfg.m_tile)
+    for key in ("offsets", "dst_row"):
+        np.testing.assert_array_equal(P.to_host(g[key]), lay[key], err_msg=key)
+    freq = np.argsort(-np.bincount(idx[idx >= 0].ravel(), minlength=cfg.E), kind="stable")
+    T = idx.shape[0]
+    for n in (4, 6, 8, 12, 16, 24, cfg.E):
+        top = set(freq[:n].tolist())
+        cand = [t for t in range(T) if set(idx[t][idx[t] >= 0].tolist()) <= top and
+                (idx[t] >= 0).any()]
+        if len(cand) >= 4:
+            break
+    toks = np.sort(np.random.default_rng(7).choice(cand, 4, replace=False))
+    P.log(f"[mx] full-size {name}: oracle on tokens {toks.tolist()} ({n} experts)")
+    shared = (inp["ws1"], inp["ws3"], inp["ws2"]) if "ws1" in inp else None
+    out = orc.token_outputs_mx(toks, inp["x"], idx, w, inp["w1"], inp["w3"], inp["w2"], shared)
+    got = P.to_host(g["out"].index_select(0, torch.from_numpy(toks).cuda()))
+    e = P.rel_err(got, out)
+    P.log(f"[mx] full-size {name}: out rel err {e:.2e}")
+    assert e <= P.TOL["bf16"]
