@@ -69,6 +69,14 @@ def test_single_token():
     P.check_layer(_bf16_layer(1, 128, 128, 8, 2), 2, 128, "bf16")
 
 
+def test_single_assignment_on_the_decode_gemm():
+    """T=1, k=1 over 64 experts of D=F=512: the contiguous buffer holds 128 rows and the
+    experts give 512 workgroups of 64 columns, so the grouped call takes the decode GEMM
+    (contiguous segments); the one active expert's segment is 1 valid row + 127 pad rows."""
+    P.log("[parity] T=1 k=1 E=64 decode GEMM")
+    P.check_layer(_bf16_layer(1, 512, 512, 64, 1), 1, 128, "bf16")
+
+
 @pytest.mark.parametrize("k", [1, 2])
 def test_zero_gate_ties_send_every_token_to_lowest_experts(k):
     P.log(f"[parity] zero gate k={k}")
