@@ -152,6 +152,9 @@ moe_status_t moe_permute_masked(moe_dtype_t dt, const void* x, const int32_t* to
  * x_masked [E*cap,D] give h [E*cap,F] and y [E*cap,D] with the same arithmetic,
  * storage and workspace rules as moe_grouped_swiglu; the other rows of h and y are
  * neither read nor written. counts stays on the device (no host synchronisation).
+ * bf16 slabs of at most 128 rows (D and F multiples of 128, at least two workgroups of
+ * 64 output columns per CU) run on a decode kernel that streams each active expert's
+ * weights past its rows; the workspace is then unused.
  * cap a multiple of 16 (E*cap < 2^31); D*F < 2^31.
  * Errors: MOE_EINVAL, MOE_ESHAPE, MOE_ECAPACITY (cap), MOE_EHIP.
  */
@@ -190,7 +193,10 @@ moe_status_t moe_grouped_swiglu_masked(moe_dtype_t dt, const void* x_masked,
  * such round split; a smaller one splits less or not at all. The split changes
  * only the float32 summation order of those tiles; results are deterministic for
  * a given device and ws_bytes. Calls that share a workspace must not overlap.
- * float32 ignores the workspace.
+ * float32 ignores the workspace, and so does a bf16 call whose buffer holds at most
+ * 128 rows with enough experts (D and F multiples of 128, E*min(D,F)/64 at least two
+ * workgroups per CU): such decode-sized calls stream each active expert's weights
+ * past its rows instead of tiling (fc1 without ab, fc2).
  * Errors: MOE_EINVAL, MOE_ESHAPE, MOE_ECAPACITY (m_cap % m_tile),
  * MOE_EUNSUPPORTED, MOE_EHIP.
  */
