@@ -657,11 +657,24 @@ __device__ __forceinline__ void mx_step(const char* sA, const char* sB,
 // next step of this tile with no branch in the loop body, so the compiler keeps the
 // MFMAs between the two halves of the issue; the last step, peeled off, issues the
 // next tile's first.
+// The operands of the FP8 fc1: the load descriptors and per-lane offsets of a tile are
+// built from these where they are needed (the next tile's only in the last step), so
+// they do not occupy registers through the main loop.
+struct MxSrc {
+  const bf16_t* A;
+  const bf16_t* W1;
+  const bf16_t* W3;
+  int K, N;
+  __device__ TileLoads loads(const Tile& t) const {
+    return tile_loads<true, false, 1>(t, A, W1, W3, K, N, K);
+  }
+};
+
 template <bool HALF>
 __device__ __forceinline__ void mainloop_mx(char* smem, const TileLoads& ld, int kb, int ke,
-                                            int stage0, bool primed, const TileLoads& nxt,
-                                            bool has_next, int nkb, const Tile& t,
-                                            const MxScales& ms, int E, int N,
+                                            int stage0, bool primed, const Tile& nt,
+                                            const MxSrc& src, bool has_next, int nkb,
+                                            const Tile& t, const MxScales& ms, int E, int N,
                                             f32x16 (&acc)[HALF ? 2 : 4][2]) {
   constexpr int WM = HALF ? 2 : 4;
   constexpr int WN = 2;
@@ -720,19 +733,20 @@ __device__ __forceinline__ void mainloop_mx(char* smem, const TileLoads& ld, int
   enter(kt, sa, sw);
   const char* sA = smem + cur * STAGE_BYTES;
   const uint32_t lnext = lds0 + (cur ^ 1) * STAGE_BYTES;
+  const TileLoads nxt = src.loads(nt);   // nt is this tile when there is no next one
   mx_step<HALF>(sA, sA + A_BYTES, sa, sw, acc, [&](int ks) {
     if (has_next) issue_loads(nxt, lnext, nkb, ks);
   });
 }
 
 template <bool HALF>
-__device__ __forceinline__ void run_tile_mx(char* smem, const Tile& t, const TileLoads& ld,
-                                            const Epi& ep, int kb, int ke,
-                                            float* __restrict__ part, int stage0, bool primed,
-                                            const TileLoads& nxt, bool has_next, int nkb,
-                                            const MxScales& ms, int E, int N) {
+__device__ __forceinline__ void run_tile_mx(char* smem, const Tile& t, const Epi& ep, int kb,
+                                            int ke, float* __restrict__ part, int stage0,
+                                            bool primed, const Tile& nt, bool has_next, int nkb,
+                                            const MxSrc& src, const MxScales& ms, int E, int N) {
   f32x16 acc[HALF ? 2 : 4][2];
-  mainloop_mx<HALF>(smem, ld, kb, ke, stage0, primed, nxt, has_next, nkb, t, ms, E, N, acc);
+  const TileLoads ld = src.loads(t);
+  mainloop_mx<HALF>(smem, ld, kb, ke, stage0, primed, nt, src, has_next, nkb, t, ms, E, N, acc);
   finish_tile<kFc1, HALF>(smem, t, ep, kb, ke, part, stage0, acc);
 }
 
@@ -894,6 +908,26 @@ __global__ __launch_bounds__(NTHR, 1) void gg_bf16_kernel(
 
   if (vb >= items) return;
   Work cur = work(vb);
+  if (MX) {
+    // FP8 fc1: tile loads are built inside the tile (see MxSrc)
+    const MxSrc src{A, W1, W3, K, N};
+    int stage0 = 0;
+    bool primed = false;
+    for (int w = vb; w < items; w += gridDim.x) {
+      const bool has_next = w + (int)gridDim.x < items;
+      const Work nw = has_next ? work(w + gridDim.x) : cur;
+      if (cur.t.rows > BM / 2)
+        run_tile_mx<false>(smem, cur.t, ep, cur.kb, cur.ke, cur.part, stage0, primed, nw.t,
+                           has_next, nw.kb, src, ms, E, N);
+      else
+        run_tile_mx<true>(smem, cur.t, ep, cur.kb, cur.ke, cur.part, stage0, primed, nw.t,
+                          has_next, nw.kb, src, ms, E, N);
+      stage0 = (stage0 + cur.ke - cur.kb) & 1;
+      primed = has_next;
+      cur = nw;
+    }
+    return;
+  }
   TileLoads ld = tile_loads<FC1, P_MN, EB>(cur.t, A, W1, W3, K, N, ksplit);
   int stage0 = 0;
   bool primed = false;
@@ -905,14 +939,7 @@ __global__ __launch_bounds__(NTHR, 1) void gg_bf16_kernel(
       nw = work(w + gridDim.x);
       nl = tile_loads<FC1, P_MN, EB>(nw.t, A, W1, W3, K, N, ksplit);
     }
-    if (MX) {
-      if (cur.t.rows > BM / 2)
-        run_tile_mx<false>(smem, cur.t, ld, ep, cur.kb, cur.ke, cur.part, stage0, primed, nl,
-                           has_next, nw.kb, ms, E, N);
-      else
-        run_tile_mx<true>(smem, cur.t, ld, ep, cur.kb, cur.ke, cur.part, stage0, primed, nl,
-                          has_next, nw.kb, ms, E, N);
-    } else if (cur.t.rows > BM / 2) {
+    if (cur.t.rows > BM / 2) {
       run_tile<MODE, false, P_MN>(smem, cur.t, ld, ep, cur.kb, cur.ke, cur.part, stage0, primed,
                                   nl, has_next, nw.kb);
     } else {
