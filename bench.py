@@ -35,9 +35,9 @@ METRIC = "MoE-layer tokens/sec; grouped-GEMM TFLOP/s (% bf16 MFMA peak); permute
 # workload without an entry reports null. Forward: grouped fc1; backward: the wgrad of
 # fc1 ([dW1 | dW3]); FP8 payload: the FP8 fc1; decode: the masked grouped GEMM's fc1 and
 # fc2 launches (with their split-K reductions) of one step.
-TRAFFIC_BYTES_PER_LAUNCH = {"dense8_bf16": 4.343e9}
-BWD_TRAFFIC_BYTES_PER_LAUNCH = {"dense8_bf16": 8.590e9}
-FP8_TRAFFIC_BYTES_PER_LAUNCH = {"dense8_bf16": 2.769e9}
+TRAFFIC_BYTES_PER_LAUNCH = {"dense8_bf16": 4.333e9}
+BWD_TRAFFIC_BYTES_PER_LAUNCH = {"dense8_bf16": 8.282e9}
+FP8_TRAFFIC_BYTES_PER_LAUNCH = {"dense8_bf16": 2.487e9}
 MASKED_TRAFFIC_BYTES_PER_STEP = {"decode8_bf16": 2.922e9, "decode64_shared2_bf16": 1.167e9}
 
 
