@@ -198,6 +198,61 @@ def test_two_call_form_matches_one_call():
     assert torch.equal(y1[:used].view(torch.int16), y2[:used].view(torch.int16))
 
 
+def test_two_streams_in_flight_match_serial():
+    # the routed experts' grouped call and the shared experts' call in flight at once on
+    # two streams, each with its own split-K workspace (the shared call's lone partial
+    # round takes the split-K tail here), give the bits the same calls give one after the
+    # other on one stream: a call keeps no state beyond the buffers it is handed
+    P.log("[parity] routed and shared grouped calls on two streams")
+    cfg = W.shrink(W.preset("fine64_shared2_bf16"), T=2048, D=512, F=512, F_shared=512)
+    inp = W.generate(cfg, seed=11)
+    d = {n: P.to_dev(a) for n, a in inp.items() if isinstance(a, np.ndarray)}
+    T, D, E, k = inp["x"].shape[0], inp["x"].shape[1], inp["w1"].shape[0], cfg.k
+    dev = d["x"].device
+    shared = rpg.SharedExperts.from_stacked(d["ws1"], d["ws3"], d["ws2"])
+    rows = rpg.DenseRows(T, 128, dev)
+    idx, _, _ = rpg.moe_route(d["x"], d["wg"], k)
+    m_cap = rpg.moe_capacity(T, k, E, 128)
+    p = rpg.moe_permute(d["x"], idx, E, 128, m_cap=m_cap)
+    ws_main, ws_side = rpg.grouped_workspace(dev), rpg.grouped_workspace(dev)
+    F, Fs = inp["w1"].shape[1], shared.w1.shape[1]
+
+    def outputs():
+        return (torch.empty((m_cap, F), dtype=d["x"].dtype, device=dev),
+                torch.empty((m_cap, D), dtype=d["x"].dtype, device=dev),
+                torch.empty((rows.m_cap, Fs), dtype=d["x"].dtype, device=dev),
+                torch.empty((rows.m_cap, D), dtype=d["x"].dtype, device=dev))
+
+    def routed(o, ws, stream):
+        rpg.moe_grouped_swiglu(p["x_perm"], p["offsets"], p["tile_expert"], d["w1"], d["w3"],
+                               d["w2"], 128, m_cap=m_cap, h=o[0], y_perm=o[1], workspace=ws,
+                               stream=stream)
+
+    def shared_call(o, ws, stream):
+        rpg.moe_grouped_swiglu(d["x"], rows.offsets, rows.tile_expert, shared.w1, shared.w3,
+                               shared.w2, 128, m_cap=rows.m_cap, h=o[2], y_perm=o[3],
+                               workspace=ws, stream=stream)
+
+    main = torch.cuda.current_stream()
+    a, b = outputs(), outputs()
+    torch.cuda.synchronize()
+    routed(a, ws_main, main)
+    shared_call(a, ws_main, main)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream(device=dev)   # default priority
+    go, done = torch.cuda.Event(), torch.cuda.Event()
+    go.record(main)
+    side.wait_event(go)
+    shared_call(b, ws_side, side)
+    done.record(side)
+    routed(b, ws_main, main)
+    main.wait_event(done)
+    torch.cuda.synchronize()
+    used = int(p["offsets"][-1].item())
+    for i, n in ((0, used), (1, used), (2, T), (3, T)):
+        assert torch.equal(a[i][:n].view(torch.int16), b[i][:n].view(torch.int16)), i
+
+
 def test_bitwise_run_to_run_determinism():
     P.log("[parity] determinism")
     inp = W.generate(SMALL["fine64_shared2"], seed=4)
