@@ -652,11 +652,6 @@ __device__ __forceinline__ void mx_step(const char* sA, const char* sB,
   }
 }
 
-// The bf16 main loop's pipeline (same stages, barrier, split issue and cross-tile
-// prefetch) with FP8 fragments and scaled MFMAs. The steps before the last issue the
-// next step of this tile with no branch in the loop body, so the compiler keeps the
-// MFMAs between the two halves of the issue; the last step, peeled off, issues the
-// next tile's first.
 // The operands of the FP8 fc1: the load descriptors and per-lane offsets of a tile are
 // built from these where they are needed (the next tile's only in the last step), so
 // they do not occupy registers through the main loop.
@@ -670,6 +665,11 @@ struct MxSrc {
   }
 };
 
+// The bf16 main loop's pipeline (same stages, barrier, split issue and cross-tile
+// prefetch) with FP8 fragments and scaled MFMAs. The steps before the last issue the
+// next step of this tile with no branch in the loop body, so the compiler keeps the
+// MFMAs between the two halves of the issue; the last step, peeled off, issues the
+// first step of the next tile `nt`.
 template <bool HALF>
 __device__ __forceinline__ void mainloop_mx(char* smem, const TileLoads& ld, int kb, int ke,
                                             int stage0, bool primed, const Tile& nt,
