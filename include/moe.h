@@ -70,9 +70,10 @@ typedef enum {
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype_t;
 
 /*
- * moe_route - router gating and routing ("Expert Parallelism (EP)", section 1:
- * "router.gating: logits = x @ W_g^T" then "routing: top-k + score_func ->
- * probs, routing_map").
+ * moe_route - router gating and routing ("Expert Parallelism (EP)", section 1
+ * "MoE layer 的 forward 通路", forward-path figure: the gate gives every token a
+ * logit per expert, then a score function and a top-k give each token its experts
+ * and their probabilities).
  *
  *   x [T,D] (dt), wg [E,D] (dt), bias [E] float32 or NULL
  *   -> topk_idx [T,k] int32, topk_w [T,k] float32, logits [T,E] float32 or NULL
@@ -96,8 +97,8 @@ moe_status_t moe_route(moe_dtype_t dt, const void* x, const void* wg, const floa
 
 /*
  * moe_permute - dispatch metadata and permute ("Expert Parallelism (EP)",
- * section 1 "preprocess: tokens_per_expert" and "permute ... each local
- * expert's tokens contiguous"; section 2: the layout contract, every expert
+ * section 1, forward-path figure: the per-expert token counts, then the reordering
+ * that groups each local expert's tokens together; section 2: the layout contract, every expert
  * segment aligned to the GEMM M tile; section 5: permute is an index_select).
  *
  *   x [T,D] (dt), topk_idx [T,k] int32 (-1 = slot not handled here)
@@ -121,8 +122,9 @@ moe_status_t moe_permute(moe_dtype_t dt, const void* x, const int32_t* topk_idx,
 
 /*
  * moe_permute_masked - the masked (fixed-capacity) layout for decode ("Expert
- * Parallelism (EP)", section 2: the masked grouped GEMM serves decode; section 3:
- * the rows each local expert receives are known only at run time).
+ * Parallelism (EP)", section 2: the masked grouped GEMM serves decode; section 6
+ * "DeepSeek-V3 量级的示例数字": how many rows each local expert receives is known
+ * only at run time).
  *
  *   x [T,D] (dt), topk_idx [T,k] int32 (-1 = slot not handled here), cap
  *   -> x_masked [E*cap,D]  expert e's slab is rows [e*cap, (e+1)*cap); slot (t,j)
@@ -166,8 +168,8 @@ moe_status_t moe_grouped_swiglu_masked(moe_dtype_t dt, const void* x_masked,
 
 /*
  * moe_grouped_swiglu - the m-grouped expert GEMMs ("Expert Parallelism (EP)",
- * section 1 "routed_experts_compute: fc1 -> act -> fc2, grouped GEMM
- * (m-grouped)" and section 2: one kernel over same-shape expert GEMMs whose
+ * section 1, forward-path figure: the routed experts run fc1, the activation and
+ * fc2 as m-grouped GEMMs; section 2: one kernel over same-shape expert GEMMs whose
  * row counts differ, scheduled across groups; weight layout from the
  * "Expert Tensor Parallel" design note, section 4.3: w1, w3 [E,F,D], w2 [E,D,F]).
  *
@@ -226,8 +228,8 @@ moe_status_t moe_grouped_fc2(moe_dtype_t dt, const void* h, const int32_t* offse
                              size_t ws_bytes, void* stream);
 
 /*
- * FP8 payload ("Expert Parallelism (EP)", section 3: dispatch in FP8 e4m3 "plus scale",
- * combine in BF16). The token rows travel through the permute and fc1 as OCP E4M3 codes
+ * FP8 payload ("Expert Parallelism (EP)", section 6 "DeepSeek-V3 量级的示例数字": the
+ * dispatch payload is FP8 e4m3 with scales, the combine stays BF16). The token rows travel through the permute and fc1 as OCP E4M3 codes
  * (bias 7, no infinities, largest value 448) with MX block scales: one power-of-two
  * scale 2^X per 32 consecutive values of a row, stored as the byte X + 127 (E8M0). X is
  * the smallest integer with max|v| <= 448 * 2^X over the block (no value saturates),
@@ -278,8 +280,9 @@ moe_status_t moe_grouped_fc1_swiglu_mxfp8(const void* xq_perm, const void* xs_pe
 
 /*
  * moe_combine - unpermute and weighted reduce ("Expert Parallelism (EP)",
- * section 1 "combine_postprocess: unpermute-1, weighted by the top-k weights,
- * reduce back to the original order" plus the shared experts; section 5:
+ * section 1, forward-path figure: the last stage restores token order, weighting
+ * each expert row by its top-k probability, and the shared experts are added;
+ * section 5:
  * unpermute is a scatter_add, the transpose of the permute).
  *
  *   y_perm [m_cap,D], dst_row [T,k], topk_w [T,k] float32, shared [T,D] or NULL

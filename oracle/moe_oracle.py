@@ -69,8 +69,8 @@ local expert's row count is known only at run time). Readings:
     flagged. counts[e] = min(#slots of e, cap) rows are valid; the rest of a slab is
     neither computed nor read.
 
-FP8 payload (section 3 of the same page: dispatch in FP8 e4m3 "plus scales", combine in
-BF16). Readings:
+FP8 payload (section 6 "DeepSeek-V3 量级的示例数字" of the same page: the dispatch payload
+is FP8 e4m3 with scales, the combine stays BF16). Readings:
 
 16. The scales are MX block scales: one power-of-two scale 2^X per 32 consecutive values
     along D (E8M0, stored as X + 127). X is the smallest integer with max|v| <= 448 * 2^X
@@ -165,7 +165,7 @@ def capacity(T: int, k: int, E: int, m_tile: int) -> int:
 
 
 # ----------------------------------------------------------------------------
-# routing ("Expert Parallelism (EP)", section 1: router.gating and routing)
+# routing ("Expert Parallelism (EP)", section 1, forward-path figure: gate and top-k)
 # ----------------------------------------------------------------------------
 
 def router_logits(x: np.ndarray, wg: np.ndarray, dtype: str,
@@ -303,7 +303,8 @@ def permute(x: np.ndarray, layout: Dict[str, np.ndarray]) -> np.ndarray:
 
 
 # ----------------------------------------------------------------------------
-# experts (section 1 "routed_experts_compute: fc1 -> act -> fc2"; ETP note 4.3)
+# experts (section 1, forward-path figure: the routed experts' fc1, activation, fc2;
+# ETP note 4.3)
 # ----------------------------------------------------------------------------
 
 def silu(a: np.ndarray) -> np.ndarray:
@@ -358,7 +359,7 @@ def shared_experts(x, ws1, ws3, ws2, dtype: str):
 
 
 # ----------------------------------------------------------------------------
-# combine (section 1 "combine_postprocess: unpermute-1, weighted reduce")
+# combine (section 1, forward-path figure: back to token order, weighted by top-k)
 # ----------------------------------------------------------------------------
 
 def combine(y_perm, dst_row, topk_w, dtype: str, shared=None):
@@ -637,8 +638,9 @@ def expert_weight_grad_slices(x_rows, dy_rows, w1e, w3e, w2e, fs, dtype: str):
 
 
 # ----------------------------------------------------------------------------
-# masked layout for decode (section 2 "m_grouped_*_masked (decode)"; section 3: the
-# rows each local expert receives are known only at run time)
+# masked layout for decode (section 2: the masked grouped GEMM kernel serves decode;
+# section 6 "DeepSeek-V3 量级的示例数字": how many rows each local expert receives is
+# known only at run time)
 # ----------------------------------------------------------------------------
 
 def masked_layout(topk_idx: np.ndarray, E: int, cap: int) -> Dict[str, np.ndarray]:
@@ -715,8 +717,8 @@ def forward_masked(inputs: dict, k: int, cap: int, dtype: str, renorm: bool = Fa
 
 
 # ----------------------------------------------------------------------------
-# FP8 (e4m3) payload with MX block scales (section 3: dispatch = FP8 e4m3 plus scales,
-# combine = BF16)
+# FP8 (e4m3) payload with MX block scales (section 6 "DeepSeek-V3 量级的示例数字": the
+# dispatch payload is FP8 e4m3 with scales, the combine stays BF16)
 # ----------------------------------------------------------------------------
 
 def e4m3_decode(code) -> np.ndarray:

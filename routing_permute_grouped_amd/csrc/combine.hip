@@ -1,8 +1,8 @@
 // Combine: unpermute and top-k-weighted reduce back to token order, plus the
-// shared experts ("Expert Parallelism (EP)", llm-infra-atlas, section 1:
-// combine_postprocess "unpermute-1, reduce back to the original order weighted by
-// the top-k weights", output "+ shared expert"; section 5: the unpermute is the
-// transpose of the permute).
+// shared experts ("Expert Parallelism (EP)", llm-infra-atlas, section 1 "MoE layer 的 forward 通路", its forward-path figure:
+// the combine stage after the expert GEMMs, which restores token order and weights
+// each expert row by its top-k probability, and the shared experts added to the
+// output; section 5: the unpermute is the transpose of the permute).
 //
 // Each token's k expert rows are gathered by 16-byte chunks and reduced in float32
 // in slot order; the shared row is added last and the sum is rounded once. Every

@@ -1,8 +1,8 @@
 // m-grouped expert GEMMs: fc1 with the fused silu(a)*b activation, then fc2
-// ("Expert Parallelism (EP)", llm-infra-atlas, section 1 "routed_experts_compute:
-// fc1 -> act -> fc2, grouped GEMM (m-grouped)"; section 2: one kernel over
-// same-shape expert GEMMs with different row counts, a tile scheduler across the
-// groups, rows laid out expert-contiguous and tile aligned). Weight layout from the
+// ("Expert Parallelism (EP)", llm-infra-atlas, section 1 "MoE layer 的 forward 通路", its forward-path figure:
+// the routed experts run fc1, the activation and fc2 as grouped GEMMs; section 2:
+// one kernel over same-shape expert GEMMs with different row counts, a tile scheduler
+// across the groups, rows laid out expert-contiguous and tile aligned). Weight layout from the
 // "Expert Tensor Parallel" design note, section 4.3: w1, w3 [E,F,D], w2 [E,D,F].
 // The backward's GEMMs (section 5: an m-grouped fc mirrors into an m-grouped dgrad and
 // a k-grouped wgrad) run on the same tile pipeline.
@@ -550,9 +550,9 @@ __device__ __forceinline__ void run_tile(char* smem, const Tile& t, const TileLo
 }
 
 // ---------------------------------------------------------------------------
-// fc1 on the FP8 payload ("Expert Parallelism (EP)", section 3: dispatch in FP8 e4m3
-// with scales): activations and w1, w3 in OCP e4m3 with one E8M0 scale per 32 values
-// along K, on v_mfma_scale_f32_32x32x64_f8f6f4. A k-step holds 128 k (128-byte LDS
+// fc1 on the FP8 payload ("Expert Parallelism (EP)", section 6 "DeepSeek-V3 量级的示例
+// 数字": the dispatch payload is FP8 e4m3 with scales): activations and w1, w3 in OCP
+// e4m3 with one E8M0 scale per 32 values along K, on v_mfma_scale_f32_32x32x64_f8f6f4. A k-step holds 128 k (128-byte LDS
 // rows, the bf16 kernel's stage layout); each of its two 64-wide slices is one scaled
 // MFMA per block. In that instruction lane l supplies row (or column) l % 32 and 32 of
 // the slice's 64 k values as two 16-byte halves, and one scale byte: the first halves

@@ -1,7 +1,8 @@
 // Dispatch metadata and permute ("Expert Parallelism (EP)", llm-infra-atlas:
-// section 1 "preprocess: tokens_per_expert" and "permute: sort local tokens by
-// expert so each local expert's tokens are contiguous"; section 2: the output
-// layout must be expert-contiguous with every segment aligned to the GEMM M tile).
+// section 1 "MoE layer 的 forward 通路", its forward-path figure: the per-expert token counts,
+// then the reordering that groups each local expert's tokens together; section 2:
+// the output layout must be expert-contiguous with every segment aligned to the GEMM
+// M tile).
 //
 // Three launches:
 //   1. hist_kernel   per 256-token block, the slots of each expert (LDS atomics:

@@ -1,5 +1,6 @@
 // MX quantization of the FP8 payload ("Expert Parallelism (EP)", llm-infra-atlas,
-// section 3: dispatch in FP8 e4m3 with scales, combine in BF16).
+// section 6 "DeepSeek-V3 量级的示例数字": the dispatch payload is FP8 e4m3 with
+// scales, the combine stays in BF16).
 //
 // Every 32 consecutive values of a row share one power-of-two scale 2^X, stored as the
 // E8M0 byte X + 127: X is the smallest integer with max|v| <= 448 * 2^X (448 is the

@@ -1,6 +1,7 @@
 // Router gating and softmax-then-top-k routing ("Expert Parallelism (EP)",
-// llm-infra-atlas, section 1: router.gating logits = x @ W_g^T over [T, E], then
-// routing = top-k + score function -> probs and routing map).
+// llm-infra-atlas, section 1 "MoE layer 的 forward 通路", its forward-path figure: the gate
+// scores every token against every expert, then a score function and a top-k pick
+// each token's experts and their weights).
 //
 // A pass covers TW tokens x EC experts: lane l accumulates the 16-byte chunks
 // c = l, l+64, ... of x[t] . wg[e] for the TW*EC (token, expert) pairs, in increasing d.
