@@ -202,7 +202,7 @@ def main():
     def shared_gemm(on, ws):
         rpg.moe_grouped_swiglu(d["x"], rows.offsets, rows.tile_expert, shared.w1, shared.w3,
                                shared.w2, mt, m_cap=rows.m_cap, h=buf["hs"], y_perm=buf["ys"],
-                               workspace=ws, stream=on)
+                               workspace=ws, stream=on, rows_used=T)
 
     def launch_side():
         ev_go.record(stream)
@@ -377,7 +377,7 @@ def bench_masked(args, cfg, d, inp) -> dict:
     def shared_gemm(on, ws):
         rpg.moe_grouped_swiglu(d["x"], rows.offsets, rows.tile_expert, shared.w1, shared.w3,
                                shared.w2, mt, m_cap=rows.m_cap, h=buf["hs"], y_perm=buf["ys"],
-                               workspace=ws, stream=on)
+                               workspace=ws, stream=on, rows_used=T)
 
     def launch_side():
         ev_go.record(stream)
@@ -542,7 +542,7 @@ def bench_fp8(args, cfg, d, buf, shared, gws, flush, n_valid) -> dict:
             rows = rpg.DenseRows(T, mt, dev)
             rpg.moe_grouped_swiglu(d["x"], rows.offsets, rows.tile_expert, shared.w1, shared.w3,
                                    shared.w2, mt, m_cap=rows.m_cap, h=buf["hs"],
-                                   y_perm=buf["ys"], workspace=gws, stream=stream)
+                                   y_perm=buf["ys"], workspace=gws, stream=stream, rows_used=T)
             sh = buf["ys"][:T]
         mark(6)
         rpg.moe_combine(buf["y"], fb["dst_row"], buf["w"], shared=sh, out=fb["out"],
@@ -621,20 +621,22 @@ def bench_backward(args, cfg, d, buf, shared, gws, flush, n_valid) -> dict:
                  s_dw1=em(1, SF, D, dtype=f32), s_dw3=em(1, SF, D, dtype=f32),
                  s_dw2=em(1, D, SF, dtype=f32))
         rpg.moe_grouped_fc1_swiglu(d["x"], rows.offsets, rows.tile_expert, shared.w1, shared.w3,
-                                   mt, rows.m_cap, b["s_h"], ab=b["s_ab"], workspace=gws)
+                                   mt, rows.m_cap, b["s_h"], ab=b["s_ab"], workspace=gws,
+                                   rows_used=T)
 
-    def experts_bwd(dy, xr, ab, h, o, tt, w1, w3, w2, mcap, pre):
+    def experts_bwd(dy, xr, ab, h, o, tt, w1, w3, w2, mcap, pre, ru=None):
         Fx = w1.shape[1]
         rpg.moe_grouped_dgrad_swiglu(dy, o, tt, w2, ab, mt, mcap, dab=b[pre + "dab"],
-                                     workspace=gws, stream=stream)
+                                     workspace=gws, stream=stream, rows_used=ru)
         mark()
         rpg.moe_grouped_dgrad_fc1(b[pre + "dab"], o, tt, w1, w3, mt, mcap, dx_perm=b[pre + "dX"],
-                                  workspace=gws, stream=stream)
+                                  workspace=gws, stream=stream, rows_used=ru)
         mark()
         rpg.moe_grouped_wgrad(b[pre + "dab"], xr, o, mt, mcap, NS=Fx, out_lo=b[pre + "dw1"],
-                              out_hi=b[pre + "dw3"], stream=stream)
+                              out_hi=b[pre + "dw3"], stream=stream, rows_used=ru)
         mark()
-        rpg.moe_grouped_wgrad(dy, h, o, mt, mcap, NS=D, out_lo=b[pre + "dw2"], stream=stream)
+        rpg.moe_grouped_wgrad(dy, h, o, mt, mcap, NS=D, out_lo=b[pre + "dw2"], stream=stream,
+                              rows_used=ru)
         mark()
 
     marks = ["combine_bwd", "dgrad_fc2", "dgrad_fc1", "wgrad_fc1", "wgrad_fc2"]
@@ -659,7 +661,7 @@ def bench_backward(args, cfg, d, buf, shared, gws, flush, n_valid) -> dict:
         sh = None
         if shared is not None:
             experts_bwd(dout, d["x"], b["s_ab"], b["s_h"], rows.offsets, rows.tile_expert,
-                        shared.w1, shared.w3, shared.w2, rows.m_cap, "s_")
+                        shared.w1, shared.w3, shared.w2, rows.m_cap, "s_", T)
             sh = b["s_dX"][:T]
         rpg.moe_combine(b["dX"], buf["dst_row"], None, shared=sh, out=b["dx"], m_cap=m_cap,
                         stream=stream)

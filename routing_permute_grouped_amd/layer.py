@@ -35,6 +35,7 @@ class DenseRows:
     """offsets/tile_expert describing one expert over T rows (the shared-expert call)."""
 
     def __init__(self, T: int, m_tile: int, device):
+        self.T = T
         self.m_cap = -(-T // m_tile) * m_tile
         self.offsets = torch.tensor([0, T], dtype=torch.int32, device=device)
         self.tile_expert = torch.zeros(self.m_cap // m_tile, dtype=torch.int32, device=device)
@@ -81,13 +82,15 @@ def moe_layer(x: torch.Tensor, w1: torch.Tensor, w3: torch.Tensor, w2: torch.Ten
             abs_ = torch.empty((rows.m_cap, 2 * SF), dtype=x.dtype, device=x.device)
             ys = torch.empty((rows.m_cap, D), dtype=x.dtype, device=x.device)
             B.moe_grouped_fc1_swiglu(x, rows.offsets, rows.tile_expert, shared.w1, shared.w3,
-                                     m_tile, rows.m_cap, hs, ab=abs_, workspace=ws)
+                                     m_tile, rows.m_cap, hs, ab=abs_, workspace=ws,
+                                     rows_used=rows.T)
             B.moe_grouped_fc2(hs, rows.offsets, rows.tile_expert, shared.w2, m_tile, rows.m_cap,
                               ys, workspace=ws)
             res["shared_h"], res["shared_ab"] = hs, abs_
         else:
             _, ys = B.moe_grouped_swiglu(x, rows.offsets, rows.tile_expert, shared.w1, shared.w3,
-                                         shared.w2, m_tile, m_cap=rows.m_cap, workspace=ws)
+                                         shared.w2, m_tile, m_cap=rows.m_cap, workspace=ws,
+                                         rows_used=rows.T)
         sh = ys[: x.shape[0]]
         res["shared"] = sh
     res["out"] = B.moe_combine(y, p["dst_row"], topk_w, shared=sh, m_cap=m_cap)
@@ -121,7 +124,8 @@ def moe_layer_masked(x: torch.Tensor, w1: torch.Tensor, w3: torch.Tensor, w2: to
     if shared is not None:
         rows = DenseRows(x.shape[0], shared_m_tile, x.device)
         _, ys = B.moe_grouped_swiglu(x, rows.offsets, rows.tile_expert, shared.w1, shared.w3,
-                                     shared.w2, shared_m_tile, m_cap=rows.m_cap, workspace=ws)
+                                     shared.w2, shared_m_tile, m_cap=rows.m_cap, workspace=ws,
+                                     rows_used=rows.T)
         sh = ys[: x.shape[0]]
         res["shared"] = sh
     res["out"] = B.moe_combine(y, p["dst_row"], topk_w, shared=sh, m_cap=p["m_cap"])
@@ -151,8 +155,8 @@ def moe_layer_mxfp8(x: torch.Tensor, mw: MxWeights, w2: torch.Tensor, k: int, m_
                     topk_w: Optional[torch.Tensor] = None,
                     shared: Optional[SharedExperts] = None, renorm: bool = False,
                     split_k: bool = True) -> dict:
-    """The layer with an FP8 payload (EP page section 3: dispatch in e4m3 plus scales,
-    combine in bf16): route on the bf16 x -> MX-quantize x -> permute codes and scales ->
+    """The layer with an FP8 payload (EP page, section 6 "DeepSeek-V3 量级的示例数字": the
+    dispatch payload is FP8 e4m3 with scales, the combine stays bf16): route on the bf16 x -> MX-quantize x -> permute codes and scales ->
     fc1 on the scaled-FP8 MFMA -> fc2 (bf16) [-> shared experts, bf16] -> combine."""
     E = mw.w1q.shape[0]
     res = {}
@@ -175,23 +179,27 @@ def moe_layer_mxfp8(x: torch.Tensor, mw: MxWeights, w2: torch.Tensor, k: int, m_
     if shared is not None:
         rows = DenseRows(x.shape[0], m_tile, x.device)
         _, ys = B.moe_grouped_swiglu(x, rows.offsets, rows.tile_expert, shared.w1, shared.w3,
-                                     shared.w2, m_tile, m_cap=rows.m_cap, workspace=ws)
+                                     shared.w2, m_tile, m_cap=rows.m_cap, workspace=ws,
+                                     rows_used=rows.T)
         sh = ys[: x.shape[0]]
         res["shared"] = sh
     res["out"] = B.moe_combine(y, p["dst_row"], topk_w, shared=sh, m_cap=m_cap)
     return res
 
 
-def _experts_backward(dy, x_rows, ab, h, offsets, tile_expert, w1, w3, w2, m_tile, m_cap, ws):
+def _experts_backward(dy, x_rows, ab, h, offsets, tile_expert, w1, w3, w2, m_tile, m_cap, ws,
+                      rows_used=None):
     """dgrad and wgrad of one grouped SwiGLU FFN over rows [0, m_cap) (section 5 of
     "Expert Parallelism (EP)": the m-grouped fc mirrors into an m-grouped dgrad and a
     k-grouped wgrad). Returns (dab, dX, dw1, dw3, dw2)."""
     F, D = w1.shape[1], w1.shape[2]
+    ru = rows_used
     dab = B.moe_grouped_dgrad_swiglu(dy, offsets, tile_expert, w2, ab, m_tile, m_cap,
-                                     workspace=ws)
-    dX = B.moe_grouped_dgrad_fc1(dab, offsets, tile_expert, w1, w3, m_tile, m_cap, workspace=ws)
-    dw1, dw3 = B.moe_grouped_wgrad(dab, x_rows, offsets, m_tile, m_cap, NS=F)
-    dw2, _ = B.moe_grouped_wgrad(dy, h, offsets, m_tile, m_cap, NS=D)
+                                     workspace=ws, rows_used=ru)
+    dX = B.moe_grouped_dgrad_fc1(dab, offsets, tile_expert, w1, w3, m_tile, m_cap, workspace=ws,
+                                 rows_used=ru)
+    dw1, dw3 = B.moe_grouped_wgrad(dab, x_rows, offsets, m_tile, m_cap, NS=F, rows_used=ru)
+    dw2, _ = B.moe_grouped_wgrad(dy, h, offsets, m_tile, m_cap, NS=D, rows_used=ru)
     return dab, dX, dw1, dw3, dw2
 
 
@@ -221,7 +229,7 @@ def moe_layer_backward(fwd: dict, dout: torch.Tensor, x: torch.Tensor, w1: torch
         rows = DenseRows(T, m_tile, x.device)
         _, dXs, dws1, dws3, dws2 = _experts_backward(
             dout, x, fwd["shared_ab"], fwd["shared_h"], rows.offsets, rows.tile_expert,
-            shared.w1, shared.w3, shared.w2, m_tile, rows.m_cap, ws)
+            shared.w1, shared.w3, shared.w2, m_tile, rows.m_cap, ws, rows_used=T)
         dxs = dXs[:T]
         res.update(dx_shared=dxs, dws1=dws1, dws3=dws3, dws2=dws2)
     res["dx"] = B.moe_combine(dX, fwd["dst_row"], None, shared=dxs, m_cap=m_cap)

@@ -88,7 +88,7 @@ def run_gpu(inp: dict, k: int, m_tile: int, renorm: bool = False, want_logits: b
         hs = poison(torch.empty((rows.m_cap, sw.w1.shape[1]), dtype=d["x"].dtype, device="cuda"))
         ys = poison(torch.empty((rows.m_cap, inp["x"].shape[1]), dtype=d["x"].dtype, device="cuda"))
         rpg.moe_grouped_swiglu(d["x"], rows.offsets, rows.tile_expert, sw.w1, sw.w3, sw.w2, m_tile,
-                               m_cap=rows.m_cap, h=hs, y_perm=ys, workspace=ws)
+                               m_cap=rows.m_cap, h=hs, y_perm=ys, workspace=ws, rows_used=T)
         shared = ys[:T]
         out["shared"] = shared
     o = poison(torch.empty_like(d["x"]))

@@ -298,3 +298,127 @@ def test_binding_raises_on_rejected_call():
     with pytest.raises(rpg.MoEError) as ei:
         rpg._binding._check("moe_route", MOE_ESHAPE)
     assert ei.value.status == MOE_ESHAPE
+
+
+# ---------------------------------------------------------------------------
+# Python binding: dtype and buffer-size checks run on the host before any pointer is
+# taken (the C ABI cannot see either), so CPU tensors reach them and no GPU is needed.
+# ---------------------------------------------------------------------------
+import torch  # noqa: E402
+
+BF = torch.bfloat16
+
+
+def _perm_args(T=64, D=128, k=2):
+    return torch.zeros((T, D), dtype=BF), torch.zeros((T, k), dtype=torch.int32)
+
+
+def test_binding_rejects_int64_topk_idx():
+    x, idx = _perm_args()
+    with pytest.raises(TypeError, match="topk_idx"):
+        rpg.moe_permute(x, idx.to(torch.int64), 8, 16)
+
+
+def test_binding_rejects_undersized_x_perm():
+    x, idx = _perm_args()
+    m_cap = rpg.moe_capacity(64, 2, 8, 16)
+    with pytest.raises(ValueError, match="x_perm"):
+        rpg.moe_permute(x, idx, 8, 16, out={"x_perm": torch.zeros((m_cap - 1, 128), dtype=BF)})
+    with pytest.raises(TypeError, match="x_perm"):
+        rpg.moe_permute(x, idx, 8, 16, out={"x_perm": torch.zeros((m_cap, 128))})
+
+
+@pytest.mark.parametrize("name,bad", [("counts", 7), ("offsets", 8), ("src_row", 10),
+                                      ("tile_expert", 1), ("dev_err", 0)])
+def test_binding_rejects_undersized_metadata(name, bad):
+    x, idx = _perm_args()
+    with pytest.raises(ValueError, match=name):
+        rpg.moe_permute(x, idx, 8, 16, m_cap=640,
+                        out={name: torch.zeros(bad, dtype=torch.int32)})
+
+
+def test_binding_rejects_topk_idx_row_mismatch():
+    x, _ = _perm_args()
+    with pytest.raises(ValueError, match="topk_idx"):
+        rpg.moe_permute(x, torch.zeros((63, 2), dtype=torch.int32), 8, 16)
+
+
+def _grouped(E=4, F=256, D=128, m_cap=512, dt=BF):
+    return (torch.zeros((m_cap, D), dtype=dt), torch.zeros(E + 1, dtype=torch.int32),
+            torch.zeros(m_cap // 128, dtype=torch.int32), torch.zeros((E, F, D), dtype=dt),
+            torch.zeros((E, F, D), dtype=dt), torch.zeros((E, D, F), dtype=dt))
+
+
+def test_binding_rejects_weight_dtype_and_shape():
+    xp, off, te, w1, w3, w2 = _grouped()
+    with pytest.raises(TypeError, match="w3"):
+        rpg.moe_grouped_swiglu(xp, off, te, w1, w3.float(), w2, 128)
+    with pytest.raises(ValueError, match="w2"):
+        rpg.moe_grouped_swiglu(xp, off, te, w1, w3, w2[:, :64], 128)
+    with pytest.raises(TypeError, match="offsets"):
+        rpg.moe_grouped_swiglu(xp, off.long(), te, w1, w3, w2, 128)
+
+
+def test_binding_rejects_undersized_gemm_buffers():
+    xp, off, te, w1, w3, w2 = _grouped()
+    with pytest.raises(ValueError, match="h:"):
+        rpg.moe_grouped_swiglu(xp, off, te, w1, w3, w2, 128, h=torch.zeros((511, 256), dtype=BF))
+    with pytest.raises(ValueError, match="x_perm"):
+        rpg.moe_grouped_fc1_swiglu(xp[:500], off, te, w1, w3, 128, 512,
+                                   torch.zeros((512, 256), dtype=BF))
+    with pytest.raises(ValueError, match="tile_expert"):
+        rpg.moe_grouped_fc2(torch.zeros((512, 256), dtype=BF), off, te[:3], w2, 128, 512,
+                            torch.zeros((512, 128), dtype=BF))
+    with pytest.raises(ValueError, match="rows_used"):
+        rpg.moe_grouped_swiglu(xp, off, te, w1, w3, w2, 128, rows_used=513)
+
+
+def test_binding_rows_used_admits_a_shorter_read_operand():
+    # the shared experts' call: x holds T rows, m_cap is T rounded up to the tile; the
+    # check passes and the call stops only at the device check of the CPU tensor
+    xp, off, te, w1, w3, w2 = _grouped()
+    with pytest.raises(ValueError, match="must live on the GPU"):
+        rpg.moe_grouped_swiglu(xp[:500], off, te, w1, w3, w2, 128, m_cap=512, rows_used=500)
+    with pytest.raises(ValueError, match="x_perm"):
+        rpg.moe_grouped_swiglu(xp[:500], off, te, w1, w3, w2, 128, m_cap=512)
+
+
+def test_binding_rejects_combine_dtypes_and_sizes():
+    y = torch.zeros((640, 128), dtype=BF)
+    dst = torch.zeros((64, 2), dtype=torch.int32)
+    w = torch.zeros((64, 2))
+    with pytest.raises(TypeError, match="dst_row"):
+        rpg.moe_combine(y, dst.long(), w)
+    with pytest.raises(TypeError, match="topk_w"):
+        rpg.moe_combine(y, dst, w.double())
+    with pytest.raises(ValueError, match="out"):
+        rpg.moe_combine(y, dst, w, out=torch.zeros((63, 128), dtype=BF))
+    with pytest.raises(TypeError, match="shared"):
+        rpg.moe_combine(y, dst, w, shared=torch.zeros((64, 128)))
+
+
+def test_binding_rejects_route_buffers():
+    x = torch.zeros((64, 128), dtype=BF)
+    wg = torch.zeros((8, 128), dtype=BF)
+    with pytest.raises(TypeError, match="wg"):
+        rpg.moe_route(x, wg.float(), 2)
+    with pytest.raises(TypeError, match="topk_idx"):
+        rpg.moe_route(x, wg, 2, topk_idx=torch.zeros((64, 2), dtype=torch.int64))
+    with pytest.raises(ValueError, match="topk_w"):
+        rpg.moe_route(x, wg, 2, topk_w=torch.zeros((64, 1)))
+    with pytest.raises(TypeError, match="bias"):
+        rpg.moe_route(x, wg, 2, bias=torch.zeros(8, dtype=torch.float64))
+
+
+def test_binding_rejects_wgrad_and_mx_buffers():
+    P_ = torch.zeros((512, 320), dtype=BF)
+    Q_ = torch.zeros((512, 192), dtype=BF)
+    off = torch.zeros(5, dtype=torch.int32)
+    with pytest.raises(ValueError, match="out_lo"):
+        rpg.moe_grouped_wgrad(P_, Q_, off, 128, NS=192, out_lo=torch.zeros((4, 191, 192)))
+    with pytest.raises(TypeError, match="Q:"):
+        rpg.moe_grouped_wgrad(P_, Q_.float(), off, 128)
+    xq = torch.zeros((64, 256), dtype=torch.uint8)
+    with pytest.raises(ValueError, match="xs"):
+        rpg.moe_permute_mxfp8(xq, torch.zeros((64, 7), dtype=torch.uint8),
+                              torch.zeros((64, 2), dtype=torch.int32), 8, 128)

@@ -67,7 +67,7 @@ def run_masked(inp, cfg, split_k=True):
         sw = rpg.SharedExperts.from_stacked(d["ws1"], d["ws3"], d["ws2"])
         rows = rpg.DenseRows(T, 128, "cuda")
         _, ys = rpg.moe_grouped_swiglu(d["x"], rows.offsets, rows.tile_expert, sw.w1, sw.w3, sw.w2,
-                                       128, m_cap=rows.m_cap, workspace=ws)
+                                       128, m_cap=rows.m_cap, workspace=ws, rows_used=T)
         shared = ys[:T]
     o = P.poison(torch.empty_like(d["x"]))
     out["out"] = rpg.moe_combine(y, p["dst_row"], w, shared=shared, out=o, m_cap=E * cap)

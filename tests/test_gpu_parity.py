@@ -231,7 +231,7 @@ def test_two_streams_in_flight_match_serial():
     def shared_call(o, ws, stream):
         rpg.moe_grouped_swiglu(d["x"], rows.offsets, rows.tile_expert, shared.w1, shared.w3,
                                shared.w2, 128, m_cap=rows.m_cap, h=o[2], y_perm=o[3],
-                               workspace=ws, stream=stream)
+                               workspace=ws, stream=stream, rows_used=T)
 
     main = torch.cuda.current_stream()
     a, b = outputs(), outputs()
