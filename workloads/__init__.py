@@ -37,7 +37,7 @@ from typing import Dict, Optional
 import numpy as np
 
 __all__ = [
-    "MoEConfig", "PRESETS", "preset", "shrink", "generate", "output_grad",
+    "MoEConfig", "PRESETS", "preset", "shrink", "generate", "router_inputs", "output_grad",
     "f32_to_bf16_bits", "bf16_bits_to_f32", "as_f32",
 ]
 
@@ -65,9 +65,9 @@ class MoEConfig:
         return 4 if self.dtype == "f32" else 2
 
 
-# Skew strength of the Zipf router bias. Chosen by workloads/calibrate_skew.py
-# (the smallest beta in {1.5, 2, 2.5, 3} whose seeded routing puts >= 24% of the
-# assignments on one expert and leaves at least one expert empty).
+# Skew strength of the Zipf router bias: the smallest beta in {1.5, 2, 2.5, 3} whose
+# seeded routing puts >= 24% of the assignments on one expert (top-4 caps a share at
+# 25%) and leaves at least one expert empty (tests/test_workloads.py checks this rule).
 SKEW_BETA = 2.0
 
 PRESETS: Dict[str, MoEConfig] = {
@@ -195,9 +195,7 @@ def generate(cfg: MoEConfig, seed: int = 0) -> dict:
         cfg = dataclasses.replace(cfg, T=T)
         out["topk_idx"], out["topk_w"] = idx, w
     with ThreadPoolExecutor(_POOL_THREADS) as pool:
-        out["x"] = _activations(seed, T, D, dt, pool)
-        if cfg.routing != "given":
-            out["wg"] = _slab(seed, "wg", 0, (E, D), 1.0 / math.sqrt(D), dt)
+        out.update(router_inputs(cfg, seed, pool))
         out["w1"] = _expert_stack(seed, "w1", E, F, D, 1.0 / math.sqrt(D), dt, pool)
         out["w3"] = _expert_stack(seed, "w3", E, F, D, 1.0 / math.sqrt(D), dt, pool)
         out["w2"] = _expert_stack(seed, "w2", E, D, F, 1.0 / math.sqrt(F), dt, pool)
@@ -206,10 +204,25 @@ def generate(cfg: MoEConfig, seed: int = 0) -> dict:
             out["ws1"] = _expert_stack(seed, "ws1", S, Fs, D, 1.0 / math.sqrt(D), dt, pool)
             out["ws3"] = _expert_stack(seed, "ws3", S, Fs, D, 1.0 / math.sqrt(D), dt, pool)
             out["ws2"] = _expert_stack(seed, "ws2", S, D, Fs, 1.0 / math.sqrt(Fs), dt, pool)
+    out["cfg"] = cfg
+    return out
+
+
+def router_inputs(cfg: MoEConfig, seed: int = 0, pool=None) -> dict:
+    """The router's inputs of ``cfg`` (T filled in), drawn as ``generate`` draws them:
+    x [T,D], and for routed presets wg [E,D] and (skewed preset) the bias [E]."""
+    T, D, E, dt = cfg.T, cfg.D, cfg.E, cfg.dtype
+    out = {}
+    if pool is None:
+        with ThreadPoolExecutor(_POOL_THREADS) as own:
+            out["x"] = _activations(seed, T, D, dt, own)
+    else:
+        out["x"] = _activations(seed, T, D, dt, pool)
+    if cfg.routing != "given":
+        out["wg"] = _slab(seed, "wg", 0, (E, D), 1.0 / math.sqrt(D), dt)
     if cfg.zipf_s:
         rank = _rng(seed, "bias").permutation(E).astype(np.float64) + 1.0
         out["bias"] = (-cfg.zipf_s * cfg.zipf_beta * np.log(rank)).astype(np.float32)
-    out["cfg"] = cfg
     return out
 
 
