@@ -142,7 +142,49 @@ def _mx_floor_scale(x, block=32):
     return orc.e4m3_encode(q).reshape(R, C), (X + 127).astype(np.uint8)
 
 
+def _combine_rounds_each_slot(y_perm, dst_row, topk_w, dtype, shared=None):
+    # every slot's weighted row rounded to storage before the sum (one rounding per slot
+    # instead of one for the whole sum)
+    Y = orc.values64(y_perm)
+    dst = np.asarray(dst_row, dtype=np.int64)
+    w = np.asarray(topk_w, dtype=np.float64)
+    out = np.zeros((dst.shape[0], Y.shape[1]))
+    for j in range(dst.shape[1]):
+        ok = dst[:, j] >= 0
+        out[ok] += orc.round_storage(w[ok, j:j + 1] * Y[dst[ok, j]], dtype)
+    if shared is not None:
+        out += orc.values64(shared)
+    return orc.round_storage(out, dtype)
+
+
+def _y_from_unrounded_h(A, w1e, w3e, w2e, dtype):
+    A64 = orc.values64(A)
+    hu = orc.silu(A64 @ orc.values64(w1e).T) * (A64 @ orc.values64(w3e).T)
+    # h is stored rounded, but fc2 reads the unrounded values
+    return orc.round_storage(hu, dtype), orc.round_storage(hu @ orc.values64(w2e).T, dtype)
+
+
+def _h_from_rounded_preactivations(A, w1e, w3e, w2e, dtype):
+    A64 = orc.values64(A)
+    a = orc.round_storage(A64 @ orc.values64(w1e).T, dtype)
+    b = orc.round_storage(A64 @ orc.values64(w3e).T, dtype)
+    h = orc.round_storage(orc.silu(a) * b, dtype)
+    return h, orc.round_storage(h @ orc.values64(w2e).T, dtype)
+
+
+def _shared_rounded_per_expert(x, ws1, ws3, ws2, dtype):
+    total = 0.0
+    for s_ in range(ws1.shape[0]):
+        total = total + orc.__dict__["_orig_shared_experts"](x, ws1[s_:s_ + 1], ws3[s_:s_ + 1],
+                                                              ws2[s_:s_ + 1], dtype)
+    return orc.round_storage(total, dtype)
+
+
 MUTATIONS = {
+    "combine_rounds_each_slot": ("combine", _combine_rounds_each_slot, "brute_bf16"),
+    "y_from_unrounded_h": ("expert_swiglu", _y_from_unrounded_h, "brute_bf16"),
+    "h_from_rounded_ab": ("expert_swiglu", _h_from_rounded_preactivations, "brute_bf16"),
+    "shared_rounded_per_expert": ("shared_experts", _shared_rounded_per_expert, "brute_bf16"),
     "e4m3_truncating": ("e4m3_round", _e4m3_truncating, "fp8"),
     "mx_floor_scale": ("mx_quantize", _mx_floor_scale, "fp8"),
     "masked_keeps_last": ("masked_layout", _masked_keeps_the_last, "masked"),
@@ -180,6 +222,9 @@ def _run_pin(kind):
     elif kind == "masked":   # one case with full slabs and drops, one with partly filled slabs
         pins.test_masked_layout_matches_loop_and_contiguous_ranks(33, 3, 4, 8)
         pins.test_masked_layout_matches_loop_and_contiguous_ranks(20, 2, 5, 16)
+    elif kind == "brute_bf16":
+        for seed in (0, 1, 2):
+            pins._check_bf16_storage_points(orc, seed)
     elif kind == "autograd":
         bpins._check_backward_against_autograd(orc, 0)
 
@@ -194,5 +239,6 @@ def test_planted_mistake_is_caught(name, monkeypatch):
 
 
 def test_unmutated_pins_pass():
-    for kind in ("brute", "brute_bias", "ties", "layout", "autograd", "masked", "fp8"):
+    for kind in ("brute", "brute_bias", "brute_bf16", "ties", "layout", "autograd", "masked",
+                 "fp8"):
         _run_pin(kind)

@@ -121,6 +121,119 @@ def test_layer_bruteforce_k_equals_e():
 
 
 # ---------------------------------------------------------------------------
+# brute force in bf16 storage mode: where the layer rounds, not only what it sums
+# ---------------------------------------------------------------------------
+
+def _py_rne_bf16(v):
+    """v (a Python float) rounded to the nearest bf16 value, ties to even: 8 significant
+    bits; below 2^-126 the spacing stays 2^-133. Python's round() breaks ties to even."""
+    if v == 0.0:
+        return 0.0
+    _, e = math.frexp(v)                  # |v| in [2^(e-1), 2^e)
+    q = 2.0 ** (max(e, -125) - 8)
+    return round(v / q) * q
+
+
+def _py_ffn_bf16(xrow, w1e, w3e, w2e):
+    """One expert on one row with the bf16 storage points written out: every h value is
+    rounded before fc2 reads it, every y value is rounded once. Returns (h, y)."""
+    D, F = len(xrow), len(w1e)
+    h = []
+    for f in range(F):
+        a = sum(float(xrow[d]) * float(w1e[f][d]) for d in range(D))
+        b = sum(float(xrow[d]) * float(w3e[f][d]) for d in range(D))
+        h.append(_py_rne_bf16(_py_silu(a) * b))
+    y = [_py_rne_bf16(sum(h[f] * float(w2e[o][f]) for f in range(F))) for o in range(len(w2e))]
+    return h, y
+
+
+def brute_layer_bf16(inp):
+    """Per-token layer output for given routing (topk_idx, topk_w; -1 slots skipped) in
+    bf16 storage mode: the routed rows' h and y rounded as stored, the shared experts'
+    h rounded and their summed output rounded once, then out[t] = sum_j w[t,j] y_j plus
+    the stored shared output, rounded once. Returns (out, h per slot, y per slot, shared)."""
+    x, idx, w = inp["x"], inp["topk_idx"], inp["topk_w"]
+    T, D = x.shape
+    out, hs, ys, sh = [], {}, {}, []
+    for t in range(T):
+        acc = [0.0] * D
+        for j in range(idx.shape[1]):
+            e = int(idx[t, j])
+            if e < 0:
+                continue
+            h, y = _py_ffn_bf16(x[t], inp["w1"][e], inp["w3"][e], inp["w2"][e])
+            hs[(t, j)], ys[(t, j)] = h, y
+            acc = [acc[d] + float(w[t, j]) * y[d] for d in range(D)]
+        s = [0.0] * D
+        if "ws1" in inp:
+            for s_ in range(inp["ws1"].shape[0]):
+                w1s, w3s, w2s = inp["ws1"][s_], inp["ws3"][s_], inp["ws2"][s_]
+                hsh = []
+                for f in range(len(w1s)):
+                    a = sum(float(x[t, d]) * float(w1s[f][d]) for d in range(D))
+                    b = sum(float(x[t, d]) * float(w3s[f][d]) for d in range(D))
+                    hsh.append(_py_rne_bf16(_py_silu(a) * b))
+                s = [s[d] + sum(hsh[f] * float(w2s[d][f]) for f in range(len(w1s)))
+                     for d in range(D)]
+            s = [_py_rne_bf16(v) for v in s]
+        sh.append(s)
+        out.append([_py_rne_bf16(acc[d] + s[d]) for d in range(D)])
+    return np.array(out), hs, ys, np.array(sh)
+
+
+def _bf16_given_layer(seed, T=9, D=16, F=12, E=5, k=3, shared=True, holes=True):
+    """bf16-representable inputs (values64 of bf16 bit patterns) with given routing,
+    some -1 slots, top-k weights in float32."""
+    inp = _tiny_layer(seed, T=T, D=D, F=F, E=E, k=k, shared=shared)
+    for name in ("x", "w1", "w3", "w2", "ws1", "ws3", "ws2"):
+        if name in inp:
+            inp[name] = orc.round_bf16(inp[name].astype(np.float64)).astype(np.float32)
+    rng = np.random.default_rng(seed + 100)
+    idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    if holes:
+        idx[rng.random((T, k)) < 0.25] = -1
+    w = rng.random((T, k)).astype(np.float32)
+    w[idx < 0] = 0.0
+    inp["topk_idx"], inp["topk_w"] = idx, w
+    del inp["wg"]
+    return inp
+
+
+def _check_bf16_storage_points(oracle, seed, **kw):
+    inp = _bf16_given_layer(seed, **kw)
+    k = inp["topk_idx"].shape[1]
+    res = oracle.forward(inp, k=k, m_tile=4, dtype="bf16")
+    out_b, hs, ys, sh_b = brute_layer_bf16(inp)
+    for (t, j), h in hs.items():
+        r = int(res["dst_row"][t, j])
+        np.testing.assert_array_equal(res["h"][r], np.array(h), err_msg=f"h of slot {(t, j)}")
+        np.testing.assert_array_equal(res["y_perm"][r], np.array(ys[(t, j)]),
+                                      err_msg=f"y of slot {(t, j)}")
+    if "ws1" in inp:
+        np.testing.assert_array_equal(res["shared"], sh_b, err_msg="shared")
+    np.testing.assert_array_equal(res["out"], out_b, err_msg="out")
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_bf16_storage_points_match_bruteforce(seed):
+    _check_bf16_storage_points(orc, seed)
+
+
+def test_bf16_storage_points_without_shared_or_holes():
+    _check_bf16_storage_points(orc, 3, shared=False, holes=False, k=2, E=4)
+
+
+def test_py_rne_bf16_agrees_with_torch_on_float32_values():
+    # the brute force's rounding, checked against torch's float32 -> bf16 conversion
+    rng = np.random.default_rng(8)
+    a = np.concatenate([rng.standard_normal(3000), rng.standard_normal(300) * 1e-38,
+                        [0.5 + 2.0 ** -9, 1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8]]).astype(np.float32)
+    ref = torch.from_numpy(a).to(torch.bfloat16).to(torch.float64).numpy()
+    got = np.array([_py_rne_bf16(float(v)) for v in a])
+    np.testing.assert_array_equal(got, ref)
+
+
+# ---------------------------------------------------------------------------
 # storage rounding
 # ---------------------------------------------------------------------------
 
