@@ -5,17 +5,23 @@ One step = route -> permute -> grouped fc1+SwiGLU -> grouped fc2 [-> shared expe
 -> combine over one batch of seeded synthetic tokens, all inputs resident in HBM.
 Between timed steps (outside the HIP-event brackets of each step) a 512 MiB buffer is
 written so the 256 MB Infinity Cache holds nothing of the previous step.
-Prints one JSON line: MoE-layer tokens/s, the grouped GEMM's TFLOP/s and fraction
-of the bf16 MFMA peak, the permute and combine GB/s and fraction of HBM bandwidth,
-per-stage median / p10 / p90 / CV, the roofline of the dominant kernel (grouped fc1)
-measured with HIP events on the stream the kernels run on, and the CPU oracle timed
-on a bounded sample.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME]
+By default every bf16 layer workload runs one after the other (dense 8-expert, the
+fine-grained 64-expert layer with shared experts, the skewed 32-expert layer, the
+expert-tensor-parallel shard); the dense layer is the headline. Prints one JSON line:
+the headline's MoE-layer tokens/s, its grouped GEMM's TFLOP/s and fraction of the bf16
+MFMA peak, permute and combine GB/s and fraction of HBM bandwidth, per-stage median /
+p10 / p90 / CV, the roofline of the dominant kernel (grouped fc1) measured with HIP
+events on the stream the kernels run on, its backward and FP8-payload steps, the CPU
+oracle timed on a bounded sample, and under "configs" the same figures for every
+workload.
+
+    python bench.py [--steps K] [--warmup W] [--workload all|NAME]
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import statistics
@@ -28,17 +34,41 @@ PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA (AMD spec)
 PEAK_F32_TFLOPS = 157.3       # MI355X fp32 vector
 PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
 METRIC = "MoE-layer tokens/sec; grouped-GEMM TFLOP/s (% bf16 MFMA peak); permute GB/s"
+HEADLINE = "dense8_bf16"
+SUITE = ["dense8_bf16", "fine64_shared2_bf16", "skew32_zipf_bf16", "etp_shard32_bf16"]
 
-# HBM-side traffic of the dominant kernels per launch, per workload: rocprofv3
-# FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0, the factors measured on a device copy of known
-# size (bench.py --copy-calibration 256). Taken for the current kernel source; a
-# workload without an entry reports null. Forward: grouped fc1; backward: the wgrad of
-# fc1 ([dW1 | dW3]); FP8 payload: the FP8 fc1; decode: the masked grouped GEMM's fc1 and
-# fc2 launches (with their split-K reductions) of one step.
-TRAFFIC_BYTES_PER_LAUNCH = {"dense8_bf16": 4.333e9}
-BWD_TRAFFIC_BYTES_PER_LAUNCH = {"dense8_bf16": 8.282e9}
-FP8_TRAFFIC_BYTES_PER_LAUNCH = {"dense8_bf16": 2.487e9}
-MASKED_TRAFFIC_BYTES_PER_STEP = {"decode8_bf16": 2.922e9, "decode64_shared2_bf16": 1.167e9}
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_GEMM_SOURCES = ["grouped_gemm.hip", "lds_dma.hpp", "common.hpp", "decode_gemm.hip"]
+
+
+def gemm_source_sha16() -> str:
+    """sha256 (first 16 hex digits) of the grouped GEMM kernels' sources."""
+    h = hashlib.sha256()
+    for n in _GEMM_SOURCES:
+        with open(os.path.join(_HERE, "routing_permute_grouped_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+# HBM-side traffic of the dominant kernels per launch (per step for the masked decode
+# GEMM): rocprofv3 FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0 bytes, the factors measured on a
+# device copy of known size (bench.py --copy-calibration 256), each taken at the GEMM
+# sources whose hash is stored beside it. A workload without an entry, or an entry taken
+# at other sources, reports null: the counters describe the kernel they were read on.
+# kind: fc1 (forward), wgrad_fc1 (backward), fp8_fc1 (FP8 payload), masked (decode).
+TRAFFIC = {}
+
+
+def traffic(kind: str, workload: str):
+    """(bytes, note) for the kernel ``kind`` on ``workload``: the stored counter reading
+    when it was taken at the current GEMM sources, else (None, why)."""
+    ent = TRAFFIC.get(kind, {}).get(workload)
+    if ent is None:
+        return None, "no counter reading for this workload"
+    val, sha = ent
+    if sha != gemm_source_sha16():
+        return None, f"counters taken at GEMM sources {sha}; current {gemm_source_sha16()}"
+    return val, f"rocprofv3 FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0 at GEMM sources {sha}"
 
 
 def parse():
@@ -46,14 +76,17 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="dense8_bf16")
+    ap.add_argument("--workload", default="all",
+                    help="all (the four bf16 layer workloads, dense8_bf16 first and the "
+                         "headline) or one workload name")
     ap.add_argument("--cpu-sample-tokens", type=int, default=4096)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--fp8", action="store_true",
-                    help="also time the layer with the FP8 (e4m3, MX-scaled) payload "
+    ap.add_argument("--no-fp8", action="store_true",
+                    help="skip the headline's step with the FP8 (e4m3, MX-scaled) payload "
                          "(reported under \"fp8_payload\")")
     ap.add_argument("--no-backward", action="store_true",
-                    help="skip the timed backward pass (reported under \"backward\")")
+                    help="skip the headline's timed backward pass (reported under "
+                         "\"backward\")")
     ap.add_argument("--no-split-k", action="store_true",
                     help="give the grouped GEMMs no workspace (every tile whole)")
     ap.add_argument("--shared-overlap", choices=["auto", "none", "start", "after-route"],
@@ -145,28 +178,68 @@ def main():
 
     import torch
 
-    import routing_permute_grouped_amd as rpg
     import workloads as W
 
-    cfg = W.preset(args.workload)
-    inp = W.generate(cfg, seed=0)
-    cfg = inp["cfg"]
-    T, D, F, E, k, mt = cfg.T, cfg.D, cfg.F, cfg.E, cfg.k, cfg.m_tile
     torch.cuda.set_device(0)
     dev = torch.device("cuda", 0)
+    names = SUITE if args.workload == "all" else [args.workload]
+    overlap_arg = args.shared_overlap
+    results, head_inp = {}, None
+    for i, name in enumerate(names):
+        t0 = time.perf_counter()
+        inp = W.generate(W.preset(name), seed=0)
+        cfg = inp["cfg"]
+        print(f"[bench] {name}: inputs drawn in {time.perf_counter() - t0:.1f} s",
+              file=sys.stderr, flush=True)
 
-    def up(a):
-        a = np.ascontiguousarray(a)
-        if a.dtype == np.uint16:
-            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
-        return torch.from_numpy(a).to(dev)
+        def up(a):
+            a = np.ascontiguousarray(a)
+            if a.dtype == np.uint16:
+                return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+            return torch.from_numpy(a).to(dev)
 
-    d = {n: up(a) for n, a in inp.items() if isinstance(a, np.ndarray)}
-    if args.shared_overlap == "auto":
-        args.shared_overlap = "start" if cfg.cap else "none"
-    if cfg.cap:
-        print(json.dumps(bench_masked(args, cfg, d, inp)), flush=True)
-        return
+        d = {n: up(a) for n, a in inp.items() if isinstance(a, np.ndarray)}
+        args.shared_overlap = overlap_arg
+        if args.shared_overlap == "auto":
+            args.shared_overlap = "start" if cfg.cap else "none"
+        if cfg.cap:
+            rec = bench_masked(args, cfg, d, inp)
+        else:
+            rec = run_contiguous(args, cfg, d, headline=(i == 0))
+        results[name] = rec
+        print(f"[bench] {name}: {rec['value'] / 1e6:.3f} M tokens/s", file=sys.stderr, flush=True)
+        if i == 0:
+            head_inp = inp
+        del d, inp
+        torch.cuda.empty_cache()
+    rec = results[names[0]]
+    if len(names) > 1:
+        rec["configs"] = {n: config_summary(r) for n, r in results.items()}
+    if not args.no_cpu_baseline and not W.preset(names[0]).cap:
+        cfg0 = head_inp["cfg"]
+        rec["cpu_baseline"] = cpu_baseline(head_inp, cfg0, min(args.cpu_sample_tokens, cfg0.T))
+    print(json.dumps(rec), flush=True)
+
+
+def config_summary(r: dict) -> dict:
+    """The per-workload figures carried under "configs" in the JSON line."""
+    keys = ["value", "unit", "ms_per_step", "config", "roofline", "grouped_gemm_tflops",
+            "grouped_gemm_frac_bf16_peak", "fc1_tflops", "fc2_tflops", "fc1_frac_bf16_peak",
+            "fc2_frac_bf16_peak", "permute_GBps", "permute_frac_hbm", "combine_GBps",
+            "combine_frac_hbm", "route_us", "stage_us_mean", "stage_us_spread",
+            "expert_rows_min_max", "assignments", "padded"]
+    return {k: r[k] for k in keys if k in r}
+
+
+def run_contiguous(args, cfg, d: dict, headline: bool) -> dict:
+    """Time the layer on the contiguous (padded-segment) layout; the headline workload
+    also times its backward and its FP8-payload step unless switched off."""
+    import torch
+
+    import routing_permute_grouped_amd as rpg
+
+    T, D, F, E, k, mt = cfg.T, cfg.D, cfg.F, cfg.E, cfg.k, cfg.m_tile
+    dev = d["x"].device
     tdt = d["x"].dtype
     m_cap = rpg.moe_capacity(T, k, E, mt)
     i32 = dict(dtype=torch.int32, device=dev)
@@ -288,7 +361,9 @@ def main():
     comb_gbps = comb_bytes / (avg["combine"] * 1e-6) / 1e9
     peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
     fc1_tflops = fc1_flop / (avg["fc1"] * 1e-6) / 1e12
+    fc2_tflops = fc2_flop / (avg["fc2"] * 1e-6) / 1e12
     ms_per_step = avg["step"] * 1e-3
+    fc1_traffic, fc1_traffic_note = traffic("fc1", cfg.name)
     rec = {
         "metric": METRIC,
         "value": T / (avg["step"] * 1e-6),
@@ -308,11 +383,14 @@ def main():
                    "shared_overlap": args.shared_overlap if shared is not None else None},
         "roofline": {"kernel": "grouped fc1 + silu(a)*b (gg_bf16_kernel<kFc1>)", "bound": "mfma",
                      "achieved": fc1_tflops, "peak": peak, "unit": "TFLOP/s",
-                     "frac": fc1_tflops / peak, "traffic": TRAFFIC_BYTES_PER_LAUNCH.get(cfg.name),
-                     "traffic_unit": "bytes per launch",
+                     "frac": fc1_tflops / peak, "traffic": fc1_traffic,
+                     "traffic_unit": "bytes per launch", "traffic_note": fc1_traffic_note,
                      "algorithmic_flop_per_launch": fc1_flop, "avg_launch_us": avg["fc1"]},
         "grouped_gemm_tflops": gemm_tflops,
         "grouped_gemm_frac_bf16_peak": gemm_tflops / peak,
+        "fc1_tflops": fc1_tflops, "fc1_frac_bf16_peak": fc1_tflops / peak,
+        "fc2_tflops": fc2_tflops, "fc2_frac_bf16_peak": fc2_tflops / peak,
+        "route_us": avg["route"] if routed else None,
         "padded": {"rows": n_padded, "fc1_tflops": fc1_tflops * n_padded / max(n_valid, 1),
                    "grouped_gemm_tflops": gemm_tflops * n_padded / max(n_valid, 1),
                    "note": "the same times with pad rows counted as work"},
@@ -326,13 +404,11 @@ def main():
         "expert_rows_min_max": [int(counts.min()), int(counts.max())],
         "cpu_baseline": None,
     }
-    if not args.no_backward:
+    if headline and not args.no_backward:
         rec["backward"] = bench_backward(args, cfg, d, buf, shared, gws, flush, n_valid)
-    if args.fp8:
+    if headline and not args.no_fp8 and cfg.dtype == "bf16" and D % 128 == 0:
         rec["fp8_payload"] = bench_fp8(args, cfg, d, buf, shared, gws, flush, n_valid)
-    if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(inp, cfg, min(args.cpu_sample_tokens, T))
-    print(json.dumps(rec), flush=True)
+    return rec
 
 
 def bench_masked(args, cfg, d, inp) -> dict:
@@ -475,8 +551,9 @@ def bench_masked(args, cfg, d, inp) -> dict:
                                "gg_bf16_kernel)", "bound": "hbm",
                      "achieved": gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": gbps / PEAK_HBM_GBPS,
-                     "traffic": MASKED_TRAFFIC_BYTES_PER_STEP.get(cfg.name),
+                     "traffic": traffic("masked", cfg.name)[0],
                      "traffic_unit": "bytes per step (fc1 + fc2 launches)",
+                     "traffic_note": traffic("masked", cfg.name)[1],
                      "algorithmic_bytes": gemm_bytes,
                      "note": "active experts' w1, w3, w2 once plus the valid rows' x, h "
                              "(written and read) and y"},
@@ -573,8 +650,9 @@ def bench_fp8(args, cfg, d, buf, shared, gws, flush, n_valid) -> dict:
                 "achieved_tflops": fc1_tf, "peak_fp8_tflops": PEAK_FP8_TFLOPS,
                 "frac_fp8_peak": fc1_tf / PEAK_FP8_TFLOPS,
                 "frac_bf16_peak": fc1_tf / PEAK_BF16_TFLOPS,
-                "traffic": FP8_TRAFFIC_BYTES_PER_LAUNCH.get(cfg.name),
-                "traffic_unit": "bytes per launch"},
+                "traffic": traffic("fp8_fc1", cfg.name)[0],
+                "traffic_unit": "bytes per launch",
+                "traffic_note": traffic("fp8_fc1", cfg.name)[1]},
         "stage_us_mean": avg,
         "out_rel_diff_vs_bf16_step": dev_out,
         "note": "x quantized per token (32-value blocks, power-of-two scales, no saturation); "
@@ -703,8 +781,9 @@ def bench_backward(args, cfg, d, buf, shared, gws, flush, n_valid) -> dict:
                            "wgrad_fc2 (dW2)": tf(2 * ndf, "wgrad_fc2")},
         "roofline": {"kernel": "k-grouped wgrad of fc1, [dW1 | dW3] (wg_bf16_kernel)",
                      "bound": "mfma", "achieved": wg1, "peak": peak, "unit": "TFLOP/s",
-                     "frac": wg1 / peak, "traffic": BWD_TRAFFIC_BYTES_PER_LAUNCH.get(cfg.name),
+                     "frac": wg1 / peak, "traffic": traffic("wgrad_fc1", cfg.name)[0],
                      "traffic_unit": "bytes per launch",
+                     "traffic_note": traffic("wgrad_fc1", cfg.name)[1],
                      "algorithmic_flop_per_launch": 4 * ndf, "avg_launch_us": avg["wgrad_fc1"]},
         "grouped_gemm_tflops": tf(routed_flop, *gemm_stages),
         "grouped_gemm_frac_bf16_peak": tf(routed_flop, *gemm_stages) / peak,
