@@ -64,7 +64,8 @@ typedef enum {
   MOE_ECAPACITY = 3,    /* m_cap < moe_capacity(...) or m_cap % m_tile != 0         */
   MOE_EWORKSPACE = 4,   /* workspace smaller than moe_permute_workspace_bytes(...)  */
   MOE_EHIP = 5,         /* the HIP runtime reported an error while launching        */
-  MOE_EUNSUPPORTED = 6  /* valid request with no kernel for it (see below)          */
+  MOE_EUNSUPPORTED = 6, /* valid request with no kernel for it (see below)          */
+  MOE_ESCRATCH = 7      /* input too large for the library's static scratch         */
 } moe_status_t;
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype_t;
@@ -119,6 +120,27 @@ moe_status_t moe_permute(moe_dtype_t dt, const void* x, const int32_t* topk_idx,
                          void* x_perm, int32_t* counts, int32_t* offsets,
                          int32_t* dst_row, int32_t* src_row, int32_t* tile_expert,
                          void* workspace, size_t ws_bytes, int32_t* dev_err, void* stream);
+
+/*
+ * moe_permute_noalloc - moe_permute for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same arguments, outputs and errors as moe_permute without the workspace. The
+ * histogram table the permute needs lives in a static device array of the library,
+ * 1 MiB per device, held from the library's first use on a device until the process
+ * ends; the call itself allocates nothing. It serves ceil(T/256) * (E+1) * 4 bytes
+ * <= 1 MiB (moe_permute_workspace_bytes(T,k,E) <= 1 MiB; e.g. T <= 65536 with
+ * E <= 1023) and returns MOE_ESCRATCH beyond that. The first call on a device looks
+ * up the array's address (hipGetSymbolAddress); a failure there returns MOE_EHIP.
+ * Every call on one GPU uses that GPU's one array: calls that overlap on one GPU (on
+ * different streams without ordering between them) race and must not be issued; calls
+ * ordered on a stream are safe. Nothing in the array has to start at zero (each call
+ * writes the part it reads first).
+ */
+moe_status_t moe_permute_noalloc(moe_dtype_t dt, const void* x, const int32_t* topk_idx,
+                                 int T, int D, int E, int k, int m_tile, int64_t m_cap,
+                                 void* x_perm, int32_t* counts, int32_t* offsets,
+                                 int32_t* dst_row, int32_t* src_row, int32_t* tile_expert,
+                                 int32_t* dev_err, void* stream);
 
 /*
  * moe_permute_masked - the masked (fixed-capacity) layout for decode ("Expert

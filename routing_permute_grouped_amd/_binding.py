@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_PKG, "libmoe_mi355x.so")
 MOE_F32, MOE_BF16 = 0, 1
 MOE_MX_ROWS, MOE_MX_KSTEPS = 0, 1   # moe_mx_layout_t
 _STATUS = {0: "MOE_OK", 1: "MOE_EINVAL", 2: "MOE_ESHAPE", 3: "MOE_ECAPACITY",
-           4: "MOE_EWORKSPACE", 5: "MOE_EHIP", 6: "MOE_EUNSUPPORTED"}
+           4: "MOE_EWORKSPACE", 5: "MOE_EHIP", 6: "MOE_EUNSUPPORTED", 7: "MOE_ESCRATCH"}
 
 # (name, restype, argtypes) of every symbol include/moe.h declares
 _P, _I, _I64, _SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
@@ -27,6 +27,8 @@ SIGNATURES = [
     ("moe_route", _I, [_I, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P]),
     ("moe_permute", _I, [_I, _P, _P, _I, _I, _I, _I, _I, _I64, _P, _P, _P, _P, _P, _P, _P, _SZ,
                          _P, _P]),
+    ("moe_permute_noalloc", _I, [_I, _P, _P, _I, _I, _I, _I, _I, _I64, _P, _P, _P, _P, _P, _P,
+                                 _P, _P]),
     ("moe_grouped_swiglu", _I, [_I, _P, _P, _P, _I, _I, _I, _I, _I64, _P, _P, _P, _P, _P, _P,
                                 _SZ, _P]),
     ("moe_grouped_fc1_swiglu", _I, [_I, _P, _P, _P, _I, _I, _I, _I, _I64, _P, _P, _P, _P, _P,
@@ -284,6 +286,39 @@ def moe_permute(x: torch.Tensor, topk_idx: torch.Tensor, E: int, m_tile: int,
         _ptr(o["tile_expert"]), _ptr(o["workspace"]),
         o["workspace"].numel() * o["workspace"].element_size(), _ptr(o["dev_err"]),
         _stream(stream)))
+    o["m_cap"] = m_cap
+    return o
+
+
+def moe_permute_noalloc(x: torch.Tensor, topk_idx: torch.Tensor, E: int, m_tile: int,
+                        m_cap: Optional[int] = None, out: Optional[dict] = None,
+                        stream=None) -> dict:
+    """moe_permute without a workspace (the library's static scratch holds its histogram
+    table; see moe_permute_noalloc in include/moe.h for the size limit and the rule that
+    calls overlapping on one GPU race). Allocates only the output buffers not given in
+    ``out``; with all of them given the call allocates nothing."""
+    _dims(x, "x", 2)
+    T, D = x.shape
+    dt = _layer_dtype(x, "x")
+    k = _check_idx(topk_idx, T)
+    dev = x.device
+    if m_cap is None:
+        m_cap = moe_capacity(T, k, E, m_tile)
+    o = dict(out or {})
+    _rows(o.get("x_perm"), "x_perm", m_cap, D, dt)
+    _check_layout_out(o, T, k, E, m_cap, m_tile)
+    i32 = dict(dtype=torch.int32, device=dev)
+    o.setdefault("x_perm", torch.empty((m_cap, D), dtype=x.dtype, device=dev))
+    o.setdefault("counts", torch.empty(E, **i32))
+    o.setdefault("offsets", torch.empty(E + 1, **i32))
+    o.setdefault("dst_row", torch.empty((T, k), **i32))
+    o.setdefault("src_row", torch.empty(m_cap, **i32))
+    o.setdefault("tile_expert", torch.empty(m_cap // m_tile, **i32))
+    o.setdefault("dev_err", torch.empty(1, **i32))
+    _check("moe_permute_noalloc", lib.moe_permute_noalloc(
+        _dt(x), _ptr(x), _ptr(topk_idx), T, D, E, k, m_tile, m_cap, _ptr(o["x_perm"]),
+        _ptr(o["counts"]), _ptr(o["offsets"]), _ptr(o["dst_row"]), _ptr(o["src_row"]),
+        _ptr(o["tile_expert"]), _ptr(o["dev_err"]), _stream(stream)))
     o["m_cap"] = m_cap
     return o
 

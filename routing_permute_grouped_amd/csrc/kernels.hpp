@@ -22,6 +22,11 @@ hipError_t launch_route(int dt, const void* x, const void* wg, const float* bias
 
 size_t permute_workspace_bytes(int T, int k, int E);
 
+// The allocation-free permute's static scratch: its size and, for the current device,
+// its device address (resolved once per device; later calls return the cached address).
+constexpr size_t kPermuteScratchBytes = (size_t)1 << 20;
+hipError_t permute_scratch(void** ptr);
+
 hipError_t launch_permute(int dt, const void* x, const int32_t* topk_idx, int T, int D, int E,
                           int k, int m_tile, int64_t m_cap, void* x_perm, int32_t* counts,
                           int32_t* offsets, int32_t* dst_row, int32_t* src_row,

@@ -71,6 +71,9 @@ const char* moe_status_str(moe_status_t s) {
     case MOE_EWORKSPACE: return "workspace smaller than moe_permute_workspace_bytes";
     case MOE_EHIP: return "HIP runtime error while launching";
     case MOE_EUNSUPPORTED: return "no kernel for this combination of dtype and m_tile";
+    case MOE_ESCRATCH:
+      return "input too large for the static scratch of moe_permute_noalloc "
+             "(ceil(T/256) * (E+1) * 4 bytes must not exceed 1 MiB)";
   }
   return "unknown status";
 }
@@ -88,23 +91,53 @@ moe_status_t moe_route(moe_dtype_t dt, const void* x, const void* wg, const floa
                                       logits, static_cast<hipStream_t>(stream)));
 }
 
-moe_status_t moe_permute(moe_dtype_t dt, const void* x, const int32_t* topk_idx, int T, int D,
-                         int E, int k, int m_tile, int64_t m_cap, void* x_perm, int32_t* counts,
-                         int32_t* offsets, int32_t* dst_row, int32_t* src_row,
-                         int32_t* tile_expert, void* workspace, size_t ws_bytes, int32_t* dev_err,
-                         void* stream) {
+// Checks shared by moe_permute and moe_permute_noalloc (everything but the workspace).
+static moe_status_t permute_args(moe_dtype_t dt, const void* x, const int32_t* topk_idx, int T,
+                                 int D, int E, int k, int m_tile, int64_t m_cap,
+                                 const void* x_perm, const int32_t* counts,
+                                 const int32_t* offsets, const int32_t* dst_row,
+                                 const int32_t* src_row, const int32_t* tile_expert,
+                                 const int32_t* dev_err) {
   if (!dtype_ok(dt) || !aligned16(x) || !aligned16(x_perm) || !aligned4(topk_idx) ||
       !aligned4(counts) || !aligned4(offsets) || !aligned4(dst_row) || !aligned4(src_row) ||
-      !aligned4(tile_expert) || !aligned4(workspace) || !aligned4(dev_err))
+      !aligned4(tile_expert) || !aligned4(dev_err))
     return MOE_EINVAL;
   if (!tk_ok(T, k) || !dim_ok(D) || E < 1 || E > kMaxExperts || k < 1 || k > E || k > kMaxK ||
       !mtile_ok(m_tile))
     return MOE_ESHAPE;
   const int64_t need = moe_capacity(T, k, E, m_tile);
   if (m_cap < need || m_cap % m_tile != 0 || m_cap > INT32_MAX) return MOE_ECAPACITY;
+  return MOE_OK;
+}
+
+moe_status_t moe_permute(moe_dtype_t dt, const void* x, const int32_t* topk_idx, int T, int D,
+                         int E, int k, int m_tile, int64_t m_cap, void* x_perm, int32_t* counts,
+                         int32_t* offsets, int32_t* dst_row, int32_t* src_row,
+                         int32_t* tile_expert, void* workspace, size_t ws_bytes, int32_t* dev_err,
+                         void* stream) {
+  const moe_status_t st = permute_args(dt, x, topk_idx, T, D, E, k, m_tile, m_cap, x_perm,
+                                       counts, offsets, dst_row, src_row, tile_expert, dev_err);
+  if (st != MOE_OK) return st;
+  if (!aligned4(workspace)) return MOE_EINVAL;
   if (ws_bytes < moe::permute_workspace_bytes(T, k, E)) return MOE_EWORKSPACE;
   return hip_status(moe::launch_permute(dt, x, topk_idx, T, D, E, k, m_tile, m_cap, x_perm,
                                         counts, offsets, dst_row, src_row, tile_expert, workspace,
+                                        dev_err, static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_permute_noalloc(moe_dtype_t dt, const void* x, const int32_t* topk_idx, int T,
+                                 int D, int E, int k, int m_tile, int64_t m_cap, void* x_perm,
+                                 int32_t* counts, int32_t* offsets, int32_t* dst_row,
+                                 int32_t* src_row, int32_t* tile_expert, int32_t* dev_err,
+                                 void* stream) {
+  const moe_status_t st = permute_args(dt, x, topk_idx, T, D, E, k, m_tile, m_cap, x_perm,
+                                       counts, offsets, dst_row, src_row, tile_expert, dev_err);
+  if (st != MOE_OK) return st;
+  if (moe::permute_workspace_bytes(T, k, E) > moe::kPermuteScratchBytes) return MOE_ESCRATCH;
+  void* scratch = nullptr;   // this device's copy of the library's static array
+  if (moe::permute_scratch(&scratch) != hipSuccess) return MOE_EHIP;
+  return hip_status(moe::launch_permute(dt, x, topk_idx, T, D, E, k, m_tile, m_cap, x_perm,
+                                        counts, offsets, dst_row, src_row, tile_expert, scratch,
                                         dev_err, static_cast<hipStream_t>(stream)));
 }
 

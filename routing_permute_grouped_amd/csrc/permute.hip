@@ -18,11 +18,38 @@
 //                    four in flight per thread) and written to its k rows; the pad
 //                    rows of every segment are zeroed by the same grid.
 #include <algorithm>
+#include <mutex>
 
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace moe {
+
+// Scratch of the allocation-free permute (moe_permute_noalloc): the histogram table of
+// one call, held by every device the library runs on until the process ends. Host code
+// never passes `scratch` itself to a kernel (on the host it names a stand-in, not device
+// memory): it uses the address hipGetSymbolAddress gives for the current device.
+static __device__ __align__(256) int32_t scratch[kPermuteScratchBytes / sizeof(int32_t)];
+
+hipError_t permute_scratch(void** ptr) {
+  static std::mutex mu;
+  static void* cache[64] = {nullptr};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (cache[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    cache[dev] = p;
+  }
+  *ptr = cache[dev];
+  return hipSuccess;
+}
+
 namespace {
 
 constexpr int kMaxExperts = 1024;

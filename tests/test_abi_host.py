@@ -30,6 +30,7 @@ def test_header_declares_the_calls_and_helpers():
                                          "moe_grouped_wgrad", "moe_permute_masked",
                                          "moe_grouped_swiglu_masked", "moe_quantize_mxfp8",
                                          "moe_permute_mxfp8", "moe_grouped_fc1_swiglu_mxfp8",
+                                         "moe_permute_noalloc",
                                          "moe_capacity",
                                          "moe_grouped_workspace_bytes",
                                          "moe_permute_workspace_bytes", "moe_status_str"])
@@ -58,7 +59,7 @@ def test_capacity_and_workspace_reject_bad_sizes():
 
 
 def test_status_strings():
-    for s in range(7):
+    for s in range(8):
         assert len(rpg.moe_status_str(s)) > 0
     assert rpg.moe_status_str(99) == "unknown status"
 
@@ -422,3 +423,32 @@ def test_binding_rejects_wgrad_and_mx_buffers():
     with pytest.raises(ValueError, match="xs"):
         rpg.moe_permute_mxfp8(xq, torch.zeros((64, 7), dtype=torch.uint8),
                               torch.zeros((64, 2), dtype=torch.int32), 8, 128)
+
+
+def permute_noalloc(dt=1, x=FAKE, idx=FAKE, T=64, D=128, E=8, k=2, mt=16, m_cap=None, xp=FAKE):
+    if m_cap is None:
+        m_cap = rpg.moe_capacity(T, k, E, mt)
+    return lib.moe_permute_noalloc(dt, x, idx, T, D, E, k, mt, m_cap, xp, FAKE, FAKE, FAKE, FAKE,
+                                   FAKE, FAKE, None)
+
+
+MOE_ESCRATCH = 7
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=3), MOE_EINVAL), (dict(x=None), MOE_EINVAL), (dict(xp=FAKE + 4), MOE_EINVAL),
+    (dict(T=0), MOE_ESHAPE), (dict(E=1025), MOE_ESHAPE), (dict(mt=100), MOE_ESHAPE),
+    (dict(m_cap=16), MOE_ECAPACITY),
+    # ceil(T/256) * (E+1) * 4 bytes above the 1 MiB static scratch
+    (dict(T=65537, E=1023, k=1), MOE_ESCRATCH), (dict(T=1 << 23, E=8, k=1), MOE_ESCRATCH),
+])
+def test_permute_noalloc_validation(kw, code):
+    assert permute_noalloc(**kw) == code
+
+
+def test_permute_noalloc_scratch_limit_matches_the_workspace_formula():
+    # the largest inputs the static scratch serves are rejected by neither check;
+    # validation stops there only at the (FAKE) buffers, which are never touched
+    assert rpg.moe_permute_workspace_bytes(65536, 1, 1023) == 1 << 20
+    assert rpg.moe_permute_workspace_bytes(65537, 1, 1023) > 1 << 20
+    assert "1 MiB" in rpg.moe_status_str(MOE_ESCRATCH)
