@@ -195,8 +195,8 @@ moe_status_t moe_grouped_swiglu_masked(moe_dtype_t dt, const void* x_masked,
  * row counts differ, scheduled across groups; weight layout from the
  * "Expert Tensor Parallel" design note, section 4.3: w1, w3 [E,F,D], w2 [E,D,F]).
  *
- *   x_perm [m_cap,D], offsets [E+1], tile_expert [m_cap/m_tile] (from moe_permute)
- *   w1, w3 [E,F,D], w2 [E,D,F]
+ *   x_perm [m_cap,D], offsets [E+1], counts [E] or NULL, tile_expert [m_cap/m_tile]
+ *   (from moe_permute), w1, w3 [E,F,D], w2 [E,D,F]
  *   -> h [m_cap,F]       h = silu(x_perm w1[e]^T) * (x_perm w3[e]^T), stored in dt
  *      y_perm [m_cap,D]  y = h w2[e]^T, stored in dt
  * for the rows [offsets[e], offsets[e+1]) of every expert e; float32
@@ -204,6 +204,12 @@ moe_status_t moe_grouped_swiglu_masked(moe_dtype_t dt, const void* x_masked,
  * (zero in x_perm) give exact zeros. offsets[e] for e < E must be multiples of
  * m_tile; offsets[E] may be any value <= m_cap (so a dense FFN over T tokens is
  * the call with E = 1, offsets = {0, T}, tile_expert all 0).
+ * counts (the permute's) marks the pad rows: rows [offsets[e] + counts[e],
+ * offsets[e+1]) of each segment hold no token. With it the tiled kernels neither
+ * read those rows nor run the matrix work of a 32-row block that lies wholly in them,
+ * and still write exact zeros to their h and y_perm rows; the decode-sized path
+ * below reads them (they hold zeros as moe_permute leaves them). NULL: every row of
+ * a segment is computed. counts outside [0, offsets[e+1] - offsets[e]] is clamped.
  * bf16 needs m_tile in {128, 256}; float32 accepts every m_tile. D*F < 2^31.
  * offsets that break this contract (negative, decreasing, past m_cap) give
  * unspecified values in h and y_perm but no access outside rows [0, m_cap).
@@ -225,10 +231,10 @@ moe_status_t moe_grouped_swiglu_masked(moe_dtype_t dt, const void* x_masked,
  * MOE_EUNSUPPORTED, MOE_EHIP.
  */
 moe_status_t moe_grouped_swiglu(moe_dtype_t dt, const void* x_perm, const int32_t* offsets,
-                                const int32_t* tile_expert, int E, int D, int F, int m_tile,
-                                int64_t m_cap, const void* w1, const void* w3, const void* w2,
-                                void* h, void* y_perm, void* workspace, size_t ws_bytes,
-                                void* stream);
+                                const int32_t* counts, const int32_t* tile_expert, int E, int D,
+                                int F, int m_tile, int64_t m_cap, const void* w1, const void* w3,
+                                const void* w2, void* h, void* y_perm, void* workspace,
+                                size_t ws_bytes, void* stream);
 
 /*
  * moe_grouped_fc1_swiglu / moe_grouped_fc2 - the two halves of moe_grouped_swiglu
@@ -241,13 +247,14 @@ moe_status_t moe_grouped_swiglu(moe_dtype_t dt, const void* x_perm, const int32_
  * Errors: as moe_grouped_swiglu.
  */
 moe_status_t moe_grouped_fc1_swiglu(moe_dtype_t dt, const void* x_perm, const int32_t* offsets,
-                                    const int32_t* tile_expert, int E, int D, int F, int m_tile,
-                                    int64_t m_cap, const void* w1, const void* w3, void* h,
-                                    void* ab, void* workspace, size_t ws_bytes, void* stream);
+                                    const int32_t* counts, const int32_t* tile_expert, int E,
+                                    int D, int F, int m_tile, int64_t m_cap, const void* w1,
+                                    const void* w3, void* h, void* ab, void* workspace,
+                                    size_t ws_bytes, void* stream);
 moe_status_t moe_grouped_fc2(moe_dtype_t dt, const void* h, const int32_t* offsets,
-                             const int32_t* tile_expert, int E, int D, int F, int m_tile,
-                             int64_t m_cap, const void* w2, void* y_perm, void* workspace,
-                             size_t ws_bytes, void* stream);
+                             const int32_t* counts, const int32_t* tile_expert, int E, int D,
+                             int F, int m_tile, int64_t m_cap, const void* w2, void* y_perm,
+                             void* workspace, size_t ws_bytes, void* stream);
 
 /*
  * FP8 payload ("Expert Parallelism (EP)", section 6 "DeepSeek-V3 量级的示例数字": the
@@ -294,10 +301,11 @@ moe_status_t moe_permute_mxfp8(const void* xq, const void* xs, const int32_t* to
                                void* workspace, size_t ws_bytes, int32_t* dev_err,
                                void* stream);
 moe_status_t moe_grouped_fc1_swiglu_mxfp8(const void* xq_perm, const void* xs_perm,
-                                          const int32_t* offsets, const int32_t* tile_expert,
-                                          int E, int D, int F, int m_tile, int64_t m_cap,
-                                          const void* w1q, const void* w1s, const void* w3q,
-                                          const void* w3s, void* h, void* workspace,
+                                          const int32_t* offsets, const int32_t* counts,
+                                          const int32_t* tile_expert, int E, int D, int F,
+                                          int m_tile, int64_t m_cap, const void* w1q,
+                                          const void* w1s, const void* w3q, const void* w3s,
+                                          void* h, void* workspace,
                                           size_t ws_bytes, void* stream);
 
 /*
@@ -346,7 +354,7 @@ moe_status_t moe_combine_backward(moe_dtype_t dt, const void* dout, const void* 
  * of silu(a)*b ("Expert Parallelism (EP)", section 5: an m-grouped fc mirrors
  * into an m-grouped dgrad).
  *
- *   dy_perm [m_cap,D], offsets, tile_expert (as moe_grouped_swiglu),
+ *   dy_perm [m_cap,D], offsets, counts, tile_expert (as moe_grouped_swiglu),
  *   w2 [E,D,F] (the forward's), ab [m_cap,2F] (from moe_grouped_fc1_swiglu)
  *   -> dh = dy_perm w2[e] per segment row, rounded to dt, then
  *      dab [m_cap,2F] = [dh*b*silu'(a) | dh*silu(a)] rounded to dt, with
@@ -357,15 +365,16 @@ moe_status_t moe_combine_backward(moe_dtype_t dt, const void* dout, const void* 
  * over k the same way).
  */
 moe_status_t moe_grouped_dgrad_swiglu(moe_dtype_t dt, const void* dy_perm, const int32_t* offsets,
-                                      const int32_t* tile_expert, int E, int D, int F, int m_tile,
-                                      int64_t m_cap, const void* w2, const void* ab, void* dab,
-                                      void* dh, void* workspace, size_t ws_bytes, void* stream);
+                                      const int32_t* counts, const int32_t* tile_expert, int E,
+                                      int D, int F, int m_tile, int64_t m_cap, const void* w2,
+                                      const void* ab, void* dab, void* dh, void* workspace,
+                                      size_t ws_bytes, void* stream);
 
 /*
  * moe_grouped_dgrad_fc1 - the m-grouped dgrad of fc1 (same passage): the input
  * gradient of the routed experts.
  *
- *   dab [m_cap,2F] = [da | db] (from moe_grouped_dgrad_swiglu), offsets,
+ *   dab [m_cap,2F] = [da | db] (from moe_grouped_dgrad_swiglu), offsets, counts,
  *   tile_expert, w1, w3 [E,F,D] (the forward's)
  *   -> dx_perm [m_cap,D] = da w1[e] + db w3[e] per segment row (one float32 sum
  *      over the 2F terms, rounded once to dt).
@@ -373,16 +382,19 @@ moe_status_t moe_grouped_dgrad_swiglu(moe_dtype_t dt, const void* dy_perm, const
  * errors as moe_grouped_swiglu.
  */
 moe_status_t moe_grouped_dgrad_fc1(moe_dtype_t dt, const void* dab, const int32_t* offsets,
-                                   const int32_t* tile_expert, int E, int D, int F, int m_tile,
-                                   int64_t m_cap, const void* w1, const void* w3, void* dx_perm,
-                                   void* workspace, size_t ws_bytes, void* stream);
+                                   const int32_t* counts, const int32_t* tile_expert, int E, int D,
+                                   int F, int m_tile, int64_t m_cap, const void* w1,
+                                   const void* w3, void* dx_perm, void* workspace,
+                                   size_t ws_bytes, void* stream);
 
 /*
  * moe_grouped_wgrad - k-grouped GEMM for the weight gradients ("Expert
  * Parallelism (EP)", section 5: the backward of an m-grouped fc holds a
  * k-grouped GEMM, whose reduction runs over each expert's rows).
  *
- *   P [m_cap, N1], Q [m_cap, N2] (dt, row-major), offsets [E+1] (segment rows)
+ *   P [m_cap, N1], Q [m_cap, N2] (dt, row-major), offsets [E+1] (segment rows),
+ *   counts [E] or NULL (with counts the sum stops at offsets[e] + counts[e], the end
+ *   of the token rows: pad rows add nothing)
  *   -> out[e][i][j] = sum_{offsets[e] <= r < offsets[e+1]} P[r][i] * Q[r][j]
  *      in float32, i < N1, j < N2; rows i < NS go to out_lo [E,NS,N2], rows
  *      i >= NS to out_hi [E,N1-NS,N2] (either may be NULL when it gets no rows).
@@ -396,8 +408,9 @@ moe_status_t moe_grouped_dgrad_fc1(moe_dtype_t dt, const void* dab, const int32_
  * Errors: MOE_EINVAL, MOE_ESHAPE, MOE_ECAPACITY, MOE_EHIP.
  */
 moe_status_t moe_grouped_wgrad(moe_dtype_t dt, const void* P, const void* Q,
-                               const int32_t* offsets, int E, int N1, int N2, int NS, int m_tile,
-                               int64_t m_cap, float* out_lo, float* out_hi, void* stream);
+                               const int32_t* offsets, const int32_t* counts, int E, int N1,
+                               int N2, int NS, int m_tile, int64_t m_cap, float* out_lo,
+                               float* out_hi, void* stream);
 
 /* Worst-case rows of the permuted buffer: with N = T*k slots,
  * m_tile * floor((N + min(E, N) * (m_tile - 1)) / m_tile). Returns -1 on bad sizes. */

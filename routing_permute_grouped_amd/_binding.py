@@ -29,26 +29,26 @@ SIGNATURES = [
                          _P, _P]),
     ("moe_permute_noalloc", _I, [_I, _P, _P, _I, _I, _I, _I, _I, _I64, _P, _P, _P, _P, _P, _P,
                                  _P, _P]),
-    ("moe_grouped_swiglu", _I, [_I, _P, _P, _P, _I, _I, _I, _I, _I64, _P, _P, _P, _P, _P, _P,
-                                _SZ, _P]),
-    ("moe_grouped_fc1_swiglu", _I, [_I, _P, _P, _P, _I, _I, _I, _I, _I64, _P, _P, _P, _P, _P,
-                                    _SZ, _P]),
-    ("moe_grouped_fc2", _I, [_I, _P, _P, _P, _I, _I, _I, _I, _I64, _P, _P, _P, _SZ, _P]),
+    ("moe_grouped_swiglu", _I, [_I, _P, _P, _P, _P, _I, _I, _I, _I, _I64, _P, _P, _P, _P, _P,
+                                _P, _SZ, _P]),
+    ("moe_grouped_fc1_swiglu", _I, [_I, _P, _P, _P, _P, _I, _I, _I, _I, _I64, _P, _P, _P, _P,
+                                    _P, _SZ, _P]),
+    ("moe_grouped_fc2", _I, [_I, _P, _P, _P, _P, _I, _I, _I, _I, _I64, _P, _P, _P, _SZ, _P]),
     ("moe_combine", _I, [_I, _P, _P, _P, _P, _I, _I, _I, _I64, _P, _P]),
     ("moe_quantize_mxfp8", _I, [_I, _P, _I64, _I, _P, _P, _I, _P]),
     ("moe_permute_mxfp8", _I, [_P, _P, _P, _I, _I, _I, _I, _I, _I64, _P, _P, _P, _P, _P, _P, _P, _P,
                                _SZ, _P, _P]),
-    ("moe_grouped_fc1_swiglu_mxfp8", _I, [_P, _P, _P, _P, _I, _I, _I, _I, _I64, _P, _P, _P, _P, _P,
-                                          _P, _SZ, _P]),
+    ("moe_grouped_fc1_swiglu_mxfp8", _I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I64, _P, _P, _P,
+                                          _P, _P, _P, _SZ, _P]),
     ("moe_permute_masked", _I, [_I, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _SZ, _P, _P]),
     ("moe_grouped_swiglu_masked", _I, [_I, _P, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _SZ,
                                        _P]),
     ("moe_combine_backward", _I, [_I, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I64, _P, _P, _P]),
-    ("moe_grouped_dgrad_swiglu", _I, [_I, _P, _P, _P, _I, _I, _I, _I, _I64, _P, _P, _P, _P, _P,
-                                      _SZ, _P]),
-    ("moe_grouped_dgrad_fc1", _I, [_I, _P, _P, _P, _I, _I, _I, _I, _I64, _P, _P, _P, _P, _SZ,
-                                   _P]),
-    ("moe_grouped_wgrad", _I, [_I, _P, _P, _P, _I, _I, _I, _I, _I, _I64, _P, _P, _P]),
+    ("moe_grouped_dgrad_swiglu", _I, [_I, _P, _P, _P, _P, _I, _I, _I, _I, _I64, _P, _P, _P, _P,
+                                      _P, _SZ, _P]),
+    ("moe_grouped_dgrad_fc1", _I, [_I, _P, _P, _P, _P, _I, _I, _I, _I, _I64, _P, _P, _P, _P,
+                                   _SZ, _P]),
+    ("moe_grouped_wgrad", _I, [_I, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I64, _P, _P, _P]),
     ("moe_capacity", _I64, [_I, _I, _I, _I]),
     ("moe_grouped_workspace_bytes", _SZ, []),
     ("moe_permute_workspace_bytes", _SZ, [_I, _I, _I]),
@@ -334,7 +334,8 @@ def moe_grouped_swiglu(x_perm: torch.Tensor, offsets: torch.Tensor, tile_expert:
                        m_cap: Optional[int] = None, h: Optional[torch.Tensor] = None,
                        y_perm: Optional[torch.Tensor] = None,
                        workspace: Optional[torch.Tensor] = None, stream=None,
-                       rows_used: Optional[int] = None):
+                       rows_used: Optional[int] = None,
+                       counts: Optional[torch.Tensor] = None):
     _dims(w1, "w1", 3)
     E, F, D = w1.shape
     dt = _layer_dtype(x_perm, "x_perm")
@@ -343,6 +344,7 @@ def moe_grouped_swiglu(x_perm: torch.Tensor, offsets: torch.Tensor, tile_expert:
         m_cap = x_perm.shape[0]
     _rows(x_perm, "x_perm", _used(rows_used, m_cap), D, dt)
     _check_segments(offsets, tile_expert, E, m_cap, m_tile)
+    _numel(counts, "counts", E, torch.int32)
     _rows(h, "h", m_cap, F, dt)
     _rows(y_perm, "y_perm", m_cap, D, dt)
     dev = x_perm.device
@@ -351,7 +353,8 @@ def moe_grouped_swiglu(x_perm: torch.Tensor, offsets: torch.Tensor, tile_expert:
     if y_perm is None:
         y_perm = torch.empty((m_cap, D), dtype=x_perm.dtype, device=dev)
     _check("moe_grouped_swiglu", lib.moe_grouped_swiglu(
-        _dt(x_perm), _ptr(x_perm), _ptr(offsets), _ptr(tile_expert), E, D, F, m_tile, m_cap,
+        _dt(x_perm), _ptr(x_perm), _ptr(offsets), _ptr(counts), _ptr(tile_expert), E, D, F, m_tile,
+        m_cap,
         _ptr(w1), _ptr(w3), _ptr(w2), _ptr(h), _ptr(y_perm), *_ws(workspace), _stream(stream)))
     return h, y_perm
 
@@ -360,7 +363,8 @@ def moe_grouped_fc1_swiglu(x_perm: torch.Tensor, offsets: torch.Tensor, tile_exp
                            w1: torch.Tensor, w3: torch.Tensor, m_tile: int, m_cap: int,
                            h: torch.Tensor, ab: Optional[torch.Tensor] = None,
                            workspace: Optional[torch.Tensor] = None, stream=None,
-                           rows_used: Optional[int] = None) -> torch.Tensor:
+                           rows_used: Optional[int] = None,
+                           counts: Optional[torch.Tensor] = None) -> torch.Tensor:
     """h = silu(x_perm w1[e]^T) * (x_perm w3[e]^T); with ``ab`` [m_cap, 2F] also the
     pre-activations [a | b] that the backward reads."""
     _dims(w1, "w1", 3)
@@ -369,10 +373,12 @@ def moe_grouped_fc1_swiglu(x_perm: torch.Tensor, offsets: torch.Tensor, tile_exp
     _weights(w1, w3, None, dt, E, F, D)
     _rows(x_perm, "x_perm", _used(rows_used, m_cap), D, dt)
     _check_segments(offsets, tile_expert, E, m_cap, m_tile)
+    _numel(counts, "counts", E, torch.int32)
     _rows(h, "h", m_cap, F, dt)
     _rows(ab, "ab", m_cap, 2 * F, dt)
     _check("moe_grouped_fc1_swiglu", lib.moe_grouped_fc1_swiglu(
-        _dt(x_perm), _ptr(x_perm), _ptr(offsets), _ptr(tile_expert), E, D, F, m_tile, m_cap,
+        _dt(x_perm), _ptr(x_perm), _ptr(offsets), _ptr(counts), _ptr(tile_expert), E, D, F, m_tile,
+        m_cap,
         _ptr(w1), _ptr(w3), _ptr(h), _ptr(ab), *_ws(workspace), _stream(stream)))
     return h
 
@@ -380,16 +386,19 @@ def moe_grouped_fc1_swiglu(x_perm: torch.Tensor, offsets: torch.Tensor, tile_exp
 def moe_grouped_fc2(h: torch.Tensor, offsets: torch.Tensor, tile_expert: torch.Tensor,
                     w2: torch.Tensor, m_tile: int, m_cap: int, y_perm: torch.Tensor,
                     workspace: Optional[torch.Tensor] = None, stream=None,
-                    rows_used: Optional[int] = None) -> torch.Tensor:
+                    rows_used: Optional[int] = None,
+                    counts: Optional[torch.Tensor] = None) -> torch.Tensor:
     _dims(w2, "w2", 3)
     E, D, F = w2.shape
     dt = _layer_dtype(h, "h")
     _weights(None, None, w2, dt, E, F, D)
     _rows(h, "h", _used(rows_used, m_cap), F, dt)
     _check_segments(offsets, tile_expert, E, m_cap, m_tile)
+    _numel(counts, "counts", E, torch.int32)
     _rows(y_perm, "y_perm", m_cap, D, dt)
     _check("moe_grouped_fc2", lib.moe_grouped_fc2(
-        _dt(h), _ptr(h), _ptr(offsets), _ptr(tile_expert), E, D, F, m_tile, m_cap, _ptr(w2),
+        _dt(h), _ptr(h), _ptr(offsets), _ptr(counts), _ptr(tile_expert), E, D, F, m_tile, m_cap,
+        _ptr(w2),
         _ptr(y_perm), *_ws(workspace), _stream(stream)))
     return y_perm
 
@@ -455,7 +464,8 @@ def moe_grouped_dgrad_swiglu(dy_perm: torch.Tensor, offsets: torch.Tensor,
                              m_tile: int, m_cap: Optional[int] = None,
                              dab: Optional[torch.Tensor] = None, dh: Optional[torch.Tensor] = None,
                              workspace: Optional[torch.Tensor] = None, stream=None,
-                             rows_used: Optional[int] = None):
+                             rows_used: Optional[int] = None,
+                             counts: Optional[torch.Tensor] = None):
     """dab [m_cap, 2F] = [dh*b*silu'(a) | dh*silu(a)] with dh = dy_perm w2[e] (w2 [E,D,F]);
     ``dh`` [m_cap, F], when given, receives dh."""
     _dims(w2, "w2", 3)
@@ -467,13 +477,15 @@ def moe_grouped_dgrad_swiglu(dy_perm: torch.Tensor, offsets: torch.Tensor,
     ru = _used(rows_used, m_cap)
     _rows(dy_perm, "dy_perm", ru, D, dt)
     _check_segments(offsets, tile_expert, E, m_cap, m_tile)
+    _numel(counts, "counts", E, torch.int32)
     _rows(ab, "ab", ru, 2 * F, dt)
     _rows(dab, "dab", m_cap, 2 * F, dt)
     _rows(dh, "dh", m_cap, F, dt)
     if dab is None:
         dab = torch.empty((m_cap, 2 * F), dtype=dy_perm.dtype, device=dy_perm.device)
     _check("moe_grouped_dgrad_swiglu", lib.moe_grouped_dgrad_swiglu(
-        _dt(dy_perm), _ptr(dy_perm), _ptr(offsets), _ptr(tile_expert), E, D, F, m_tile, m_cap,
+        _dt(dy_perm), _ptr(dy_perm), _ptr(offsets), _ptr(counts), _ptr(tile_expert), E, D, F,
+        m_tile, m_cap,
         _ptr(w2), _ptr(ab), _ptr(dab), _ptr(dh), *_ws(workspace), _stream(stream)))
     return dab
 
@@ -482,7 +494,8 @@ def moe_grouped_dgrad_fc1(dab: torch.Tensor, offsets: torch.Tensor, tile_expert:
                           w1: torch.Tensor, w3: torch.Tensor, m_tile: int,
                           m_cap: Optional[int] = None, dx_perm: Optional[torch.Tensor] = None,
                           workspace: Optional[torch.Tensor] = None, stream=None,
-                          rows_used: Optional[int] = None) -> torch.Tensor:
+                          rows_used: Optional[int] = None,
+                          counts: Optional[torch.Tensor] = None) -> torch.Tensor:
     """dx_perm [m_cap, D] = da w1[e] + db w3[e] for dab = [da | db] (w1, w3 [E,F,D])."""
     _dims(w1, "w1", 3)
     E, F, D = w1.shape
@@ -492,11 +505,13 @@ def moe_grouped_dgrad_fc1(dab: torch.Tensor, offsets: torch.Tensor, tile_expert:
         m_cap = dab.shape[0]
     _rows(dab, "dab", _used(rows_used, m_cap), 2 * F, dt)
     _check_segments(offsets, tile_expert, E, m_cap, m_tile)
+    _numel(counts, "counts", E, torch.int32)
     _rows(dx_perm, "dx_perm", m_cap, D, dt)
     if dx_perm is None:
         dx_perm = torch.empty((m_cap, D), dtype=dab.dtype, device=dab.device)
     _check("moe_grouped_dgrad_fc1", lib.moe_grouped_dgrad_fc1(
-        _dt(dab), _ptr(dab), _ptr(offsets), _ptr(tile_expert), E, D, F, m_tile, m_cap, _ptr(w1),
+        _dt(dab), _ptr(dab), _ptr(offsets), _ptr(counts), _ptr(tile_expert), E, D, F, m_tile,
+        m_cap, _ptr(w1),
         _ptr(w3), _ptr(dx_perm), *_ws(workspace), _stream(stream)))
     return dx_perm
 
@@ -504,7 +519,8 @@ def moe_grouped_dgrad_fc1(dab: torch.Tensor, offsets: torch.Tensor, tile_expert:
 def moe_grouped_wgrad(P: torch.Tensor, Q: torch.Tensor, offsets: torch.Tensor, m_tile: int,
                       m_cap: Optional[int] = None, NS: Optional[int] = None,
                       out_lo: Optional[torch.Tensor] = None, out_hi: Optional[torch.Tensor] = None,
-                      stream=None, rows_used: Optional[int] = None):
+                      stream=None, rows_used: Optional[int] = None,
+                      counts: Optional[torch.Tensor] = None):
     """out[e] = P[seg e]^T Q[seg e] in float32 (P [m_cap, N1], Q [m_cap, N2]), rows < NS in
     out_lo [E, NS, N2] and the rest in out_hi [E, N1-NS, N2]. Returns (out_lo, out_hi)."""
     _dims(P, "P", 2)
@@ -518,6 +534,7 @@ def moe_grouped_wgrad(P: torch.Tensor, Q: torch.Tensor, offsets: torch.Tensor, m
     _rows(P, "P", ru, N1, dt)
     _rows(Q, "Q", ru, N2, dt)
     _dtype(offsets, "offsets", torch.int32)
+    _numel(counts, "counts", E, torch.int32)
     NS = N1 if NS is None else NS
     _exact(out_lo, "out_lo", (E, NS, N2), torch.float32)
     _exact(out_hi, "out_hi", (E, N1 - NS, N2), torch.float32)
@@ -527,7 +544,8 @@ def moe_grouped_wgrad(P: torch.Tensor, Q: torch.Tensor, offsets: torch.Tensor, m
     if out_hi is None and NS < N1:
         out_hi = torch.empty((E, N1 - NS, N2), **f32)
     _check("moe_grouped_wgrad", lib.moe_grouped_wgrad(
-        _dt(P), _ptr(P), _ptr(Q), _ptr(offsets), E, N1, N2, NS, m_tile, m_cap, _ptr(out_lo),
+        _dt(P), _ptr(P), _ptr(Q), _ptr(offsets), _ptr(counts), E, N1, N2, NS, m_tile, m_cap,
+        _ptr(out_lo),
         _ptr(out_hi), _stream(stream)))
     return out_lo, out_hi
 
@@ -657,7 +675,7 @@ def moe_grouped_fc1_swiglu_mxfp8(xq_perm: torch.Tensor, xs_perm: torch.Tensor,
                                  w3s: torch.Tensor, m_tile: int, m_cap: Optional[int] = None,
                                  h: Optional[torch.Tensor] = None,
                                  workspace: Optional[torch.Tensor] = None,
-                                 stream=None) -> torch.Tensor:
+                                 stream=None, counts: Optional[torch.Tensor] = None) -> torch.Tensor:
     """h [m_cap, F] bf16 = silu(a)*b from the FP8 payload and MX-quantized w1, w3 (codes
     [E, F, D], scales in k-step words [D/128, E*F, 4])."""
     _dims(w1q, "w1q", 3)
@@ -671,11 +689,13 @@ def moe_grouped_fc1_swiglu_mxfp8(xq_perm: torch.Tensor, xs_perm: torch.Tensor,
     _numel(w1s, "w1s", (D // 128) * E * F * 4, torch.uint8)
     _numel(w3s, "w3s", (D // 128) * E * F * 4, torch.uint8)
     _check_segments(offsets, tile_expert, E, m_cap, m_tile)
+    _numel(counts, "counts", E, torch.int32)
     _rows(h, "h", m_cap, F, torch.bfloat16)
     if h is None:
         h = torch.empty((m_cap, F), dtype=torch.bfloat16, device=xq_perm.device)
     _check("moe_grouped_fc1_swiglu_mxfp8", lib.moe_grouped_fc1_swiglu_mxfp8(
-        _bytes_ptr(xq_perm), _bytes_ptr(xs_perm), _ptr(offsets), _ptr(tile_expert), E, D, F,
+        _bytes_ptr(xq_perm), _bytes_ptr(xs_perm), _ptr(offsets), _ptr(counts), _ptr(tile_expert), E,
+        D, F,
         m_tile, m_cap, _bytes_ptr(w1q), _bytes_ptr(w1s), _bytes_ptr(w3q), _bytes_ptr(w3s), _ptr(h),
         *_ws(workspace), _stream(stream)))
     return h

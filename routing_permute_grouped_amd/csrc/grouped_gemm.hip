@@ -147,8 +147,10 @@ __device__ __forceinline__ int block_scan_excl(int v, int* wtot) {
   return before + inc - v;
 }
 
+// rows: the tile's rows of its segment (pad rows included); vrows: how many of them, from
+// the first, hold tokens (rows past them are pad rows, whose outputs are zero).
 struct Tile {
-  int e, m0, rows, n0;
+  int e, m0, rows, n0, vrows;
 };
 
 // Each operand of a tile is staged per k-step as 256 "rows" (A rows or panel rows,
@@ -201,7 +203,8 @@ __device__ __forceinline__ TileLoads tile_loads(const Tile& t, const bf16_t* __r
 #pragma unroll
   for (int j = 0; j < 4; ++j)
     o.aoff[j] = (uint32_t)(min(64 * j + lrow, t.rows - 1) * K) * EB + lchunk * 16;
-  o.rsa = buffer_rsrc(Ab + (size_t)t.m0 * K * EB, (uint32_t)t.rows * K * EB);
+  // the descriptor ends at the last row holding a token: pad rows read as zeros
+  o.rsa = buffer_rsrc(Ab + (size_t)t.m0 * K * EB, (uint32_t)t.vrows * K * EB);
   o.astep = BK * 2;
   if (P_MN) {
     // columns past N read into the next row (or past the end, zero-filled): such panel
@@ -296,18 +299,23 @@ __device__ __forceinline__ bf16x8 frag_mn(const char* stage, int nbase, int ks) 
 // step the free stage instead receives the first step of the next tile (`nxt`, step
 // `nkb`), so its load latency hides under this tile's last MFMAs and its epilogue;
 // `primed` says that this tile's first step was loaded that way.
-template <bool HALF, bool A_MN, bool P_MN>
+//
+// GUARD: the tile's rows from `vrows` on hold no token (pad rows, read as zeros): a
+// wave runs no MFMA for its 32-row blocks that lie wholly among them.
+template <bool HALF, bool A_MN, bool P_MN, bool GUARD = false>
 __device__ __forceinline__ void mainloop(char* smem, const TileLoads& ld, int kb, int ke,
                                          int stage0, bool primed, const TileLoads& nxt,
-                                         bool has_next, int nkb, f32x16 (&acc)[HALF ? 2 : 4][2]) {
+                                         bool has_next, int nkb, f32x16 (&acc)[HALF ? 2 : 4][2],
+                                         int vrows = BM) {
   constexpr int WM = HALF ? 2 : 4;   // 32-row blocks of A per wave
   constexpr int WN = 2;              // 32-row panel blocks per wave
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int arow0 = (wave & 1) * (HALF ? 64 : 128);   // first A row of this wave
   const int prow0 = (wave >> 1) * 64;                 // first panel row of this wave
   const uint32_t lds0 = lds_addr(smem) + wave * 1024;
+  const int nmb = GUARD ? max(0, min(WM, (vrows - arow0 + 31) >> 5)) : WM;
 
 #pragma unroll
   for (int i = 0; i < WM; ++i)
@@ -351,11 +359,13 @@ __device__ __forceinline__ void mainloop(char* smem, const TileLoads& ld, int kb
       }
       if (ks + 1 < BK / 16) frag(ks + 1, (ks + 1) & 1);
 #pragma unroll
-      for (int mb = 0; mb < WM; ++mb)
+      for (int mb = 0; mb < WM; ++mb) {
+        if (GUARD && mb >= nmb) continue;
 #pragma unroll
         for (int nb = 0; nb < WN; ++nb)
           acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[ks & 1][nb], af[ks & 1][mb],
                                                                 acc[mb][nb], 0, 0, 0);
+      }
     }
   }
   // No barrier here: the next tile's first step went into the stage nobody reads in
@@ -432,7 +442,8 @@ __device__ __forceinline__ void dgrad_epilogue(char* stage, const Tile& t, const
         const int r = p * 128 + rl;
         ok[i] = r < t.rows && n < N;
         row[i] = (size_t)(t.m0 + r) * N;
-        if (ok[i]) {
+        va[i] = vb[i] = uint4{0u, 0u, 0u, 0u};   // pad rows: dh = 0 and a = b = 0 give zeros
+        if (ok[i] && r < t.vrows) {
           va[i] = *reinterpret_cast<const uint4*>(ep.ab + 2 * row[i] + n);
           vb[i] = *reinterpret_cast<const uint4*>(ep.ab + 2 * row[i] + N + n);
         }
@@ -539,13 +550,14 @@ __device__ __forceinline__ void finish_tile(char* smem, const Tile& t, const Epi
 }
 
 // One tile of the m-grouped kernel: the main loop, then finish_tile.
-template <int MODE, bool HALF, bool P_MN>
+template <int MODE, bool HALF, bool P_MN, bool GUARD = false>
 __device__ __forceinline__ void run_tile(char* smem, const Tile& t, const TileLoads& ld,
                                          const Epi& ep, int kb, int ke,
                                          float* __restrict__ part, int stage0, bool primed,
                                          const TileLoads& nxt, bool has_next, int nkb) {
   f32x16 acc[HALF ? 2 : 4][2];
-  mainloop<HALF, false, P_MN>(smem, ld, kb, ke, stage0, primed, nxt, has_next, nkb, acc);
+  mainloop<HALF, false, P_MN, GUARD>(smem, ld, kb, ke, stage0, primed, nxt, has_next, nkb, acc,
+                                     t.vrows);
   finish_tile<MODE, HALF>(smem, t, ep, kb, ke, part, stage0, acc);
 }
 
@@ -750,8 +762,10 @@ __device__ __forceinline__ void run_tile_mx(char* smem, const Tile& t, const Epi
   finish_tile<kFc1, HALF>(smem, t, ep, kb, ke, part, stage0, acc);
 }
 
-// The rows of each expert: contiguous segments [offsets[e], offsets[e+1]) (cap = 0), or
-// the masked layout's slabs, rows [e*cap, e*cap + min(counts[e], cap)) (cap > 0).
+// The rows of each expert: contiguous segments [offsets[e], offsets[e+1]) (cap = 0), of
+// which the first counts[e] hold tokens and the rest are zero pad rows (counts may be
+// null: then every row is treated as a token row), or the masked layout's slabs, rows
+// [e*cap, e*cap + min(counts[e], cap)) (cap > 0).
 struct Segs {
   const int32_t* offsets;
   const int32_t* counts;
@@ -763,6 +777,7 @@ struct Segs {
 struct Sched {
   int segoff[MAXE + 1];   // segment starts (clamped to the rows in use)
   int segend[MAXE];       // segment ends
+  int segval[MAXE];       // ends of the rows that hold tokens (segoff <= segval <= segend)
   int tstart[MAXE + 1];   // first 256-row block of each expert
   int wtot[16];
 };
@@ -773,14 +788,21 @@ __device__ void build_sched(Sched& sc, const Segs& sg, int E, int m_cap) {
     for (int e = tid; e < E; e += blockDim.x) {
       sc.segoff[e] = e * sg.cap;
       sc.segend[e] = e * sg.cap + max(0, min(sg.counts[e], sg.cap));
+      sc.segval[e] = sc.segend[e];
     }
   } else {
     // clamped into [0, min(offsets[E], m_cap)], so offsets that break the contract
-    // (negative, decreasing, past m_cap) can only shrink the work, never move it outside
+    // (negative, decreasing, past m_cap) can only shrink the work, never move it outside;
+    // the token rows end inside their segment whatever counts holds
     const int mend = max(0, min(sg.offsets[E], m_cap));
     for (int e = tid; e <= E; e += blockDim.x) sc.segoff[e] = max(0, min(sg.offsets[e], mend));
     __syncthreads();
-    for (int e = tid; e < E; e += blockDim.x) sc.segend[e] = sc.segoff[e + 1];
+    for (int e = tid; e < E; e += blockDim.x) {
+      sc.segend[e] = sc.segoff[e + 1];
+      sc.segval[e] = sg.counts ? max(sc.segoff[e], min(sc.segoff[e] + max(sg.counts[e], 0),
+                                                       sc.segend[e]))
+                               : sc.segend[e];
+    }
   }
   __syncthreads();
   const int per = (MAXE + blockDim.x - 1) / blockDim.x;   // experts per thread (<= 4)
@@ -825,6 +847,7 @@ __device__ Tile decode_item(const Sched& sc, int E, int n_nt, int cols, int w) {
   t.e = lo;
   t.m0 = sc.segoff[lo] + (mb - sc.tstart[lo]) * BM;
   t.rows = min(BM, sc.segend[lo] - t.m0);
+  t.vrows = max(0, min(t.rows, sc.segval[lo] - t.m0));
   t.n0 = (within / gm) * cols;
   return t;
 }
@@ -939,12 +962,22 @@ __global__ __launch_bounds__(NTHR, 1) void gg_bf16_kernel(
       nw = work(w + gridDim.x);
       nl = tile_loads<FC1, P_MN, EB>(nw.t, A, W1, W3, K, N, ksplit);
     }
+    // a tile whose token rows end inside it skips the MFMAs of its pad-row blocks
+    const bool guard = cur.t.vrows < cur.t.rows;
     if (cur.t.rows > BM / 2) {
-      run_tile<MODE, false, P_MN>(smem, cur.t, ld, ep, cur.kb, cur.ke, cur.part, stage0, primed,
-                                  nl, has_next, nw.kb);
+      if (guard)
+        run_tile<MODE, false, P_MN, true>(smem, cur.t, ld, ep, cur.kb, cur.ke, cur.part, stage0,
+                                          primed, nl, has_next, nw.kb);
+      else
+        run_tile<MODE, false, P_MN>(smem, cur.t, ld, ep, cur.kb, cur.ke, cur.part, stage0,
+                                    primed, nl, has_next, nw.kb);
     } else {
-      run_tile<MODE, true, P_MN>(smem, cur.t, ld, ep, cur.kb, cur.ke, cur.part, stage0, primed,
-                                 nl, has_next, nw.kb);
+      if (guard)
+        run_tile<MODE, true, P_MN, true>(smem, cur.t, ld, ep, cur.kb, cur.ke, cur.part, stage0,
+                                         primed, nl, has_next, nw.kb);
+      else
+        run_tile<MODE, true, P_MN>(smem, cur.t, ld, ep, cur.kb, cur.ke, cur.part, stage0,
+                                   primed, nl, has_next, nw.kb);
     }
     stage0 = (stage0 + cur.ke - cur.kb) & 1;
     primed = has_next;
@@ -991,7 +1024,13 @@ __global__ __launch_bounds__(256) void gg_tail_reduce(Segs sg, int E, int K, int
       }
     }
     const int n = t.n0 + fl;
-    if (n < N) emit4<MODE>(ep, t.m0 + r, n, a, b);
+    if (n >= N) continue;
+    if (MODE == kDgrad && r >= t.vrows) {   // pad row: zeros, its [a | b] is never read
+      const float z[4] = {0.f, 0.f, 0.f, 0.f};
+      dgrad4(ep, (size_t)(t.m0 + r) * N, n, z, uint2{0u, 0u}, uint2{0u, 0u});
+    } else {
+      emit4<MODE>(ep, t.m0 + r, n, a, b);
+    }
   }
 }
 
@@ -1011,15 +1050,21 @@ __global__ __launch_bounds__(256) void gg_tail_reduce(Segs sg, int E, int K, int
 // ---------------------------------------------------------------------------
 struct WSched {
   int seg[MAXE + 1];   // segment bounds
-  int elist[MAXE];     // experts with rows, in order
+  int sval[MAXE];      // ends of the rows that hold tokens (the sums run over those only)
+  int elist[MAXE];     // experts with token rows, in order
   int nne;
   int wtot[16];
 };
 
-__device__ void build_wsched(WSched& sc, const int32_t* __restrict__ offsets, int E, int m_cap) {
+__device__ void build_wsched(WSched& sc, const int32_t* __restrict__ offsets,
+                             const int32_t* __restrict__ counts, int E, int m_cap) {
   const int tid = threadIdx.x;
   const int mend = max(0, min(offsets[E], m_cap));
   for (int e = tid; e <= E; e += blockDim.x) sc.seg[e] = max(0, min(offsets[e], mend));
+  __syncthreads();
+  for (int e = tid; e < E; e += blockDim.x)
+    sc.sval[e] = counts ? max(sc.seg[e], min(sc.seg[e] + max(counts[e], 0), sc.seg[e + 1]))
+                        : sc.seg[e + 1];
   __syncthreads();
   const int per = (MAXE + blockDim.x - 1) / blockDim.x;   // experts per thread (<= 4)
   bool has[4];
@@ -1027,7 +1072,7 @@ __device__ void build_wsched(WSched& sc, const int32_t* __restrict__ offsets, in
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int e = tid * per + i;
-    has[i] = i < per && e < E && sc.seg[e + 1] > sc.seg[e];
+    has[i] = i < per && e < E && sc.sval[e] > sc.seg[e];
     local += has[i];
   }
   int run = block_scan_excl(local, sc.wtot);
@@ -1059,9 +1104,10 @@ __device__ __forceinline__ WTile wg_decode(const WSched& sc, int N1, int N2, int
   r.t.e = sc.elist[ei];
   r.t.m0 = (first + within % gm) * BM;
   r.t.rows = min(BM, N1 - r.t.m0);
+  r.t.vrows = r.t.rows;
   r.t.n0 = (within / gm) * BP;
   r.kseg0 = sc.seg[r.t.e];
-  r.klen = sc.seg[r.t.e + 1] - r.kseg0;
+  r.klen = sc.sval[r.t.e] - r.kseg0;
   r.nk = (r.klen + BK - 1) / BK;
   return r;
 }
@@ -1143,11 +1189,11 @@ __device__ __forceinline__ void wg_tile(char* smem, const WTile& w, const TileLo
 
 __global__ __launch_bounds__(NTHR, 1) void wg_bf16_kernel(
     const bf16_t* __restrict__ P, const bf16_t* __restrict__ Q,
-    const int32_t* __restrict__ offsets, int E, int N1, int N2, int NS, int m_cap,
-    float* __restrict__ out_lo, float* __restrict__ out_hi) {
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ counts, int E, int N1,
+    int N2, int NS, int m_cap, float* __restrict__ out_lo, float* __restrict__ out_hi) {
   __shared__ __attribute__((aligned(16))) char smem[2 * STAGE_BYTES];
   __shared__ WSched sc;
-  build_wsched(sc, offsets, E, m_cap);
+  build_wsched(sc, offsets, counts, E, m_cap);
   int vb = blockIdx.x;
   if (gridDim.x % XCDS == 0) vb = (blockIdx.x % XCDS) * (gridDim.x / XCDS) + blockIdx.x / XCDS;
 
@@ -1155,7 +1201,7 @@ __global__ __launch_bounds__(NTHR, 1) void wg_bf16_kernel(
   const int q2 = N2 / 4;
   const int64_t per_e = (int64_t)N1 * q2;
   for (int e = 0; e < E; ++e) {
-    if (sc.seg[e + 1] > sc.seg[e]) continue;
+    if (sc.sval[e] > sc.seg[e]) continue;
     for (int64_t u = (int64_t)vb * NTHR + threadIdx.x; u < per_e; u += (int64_t)gridDim.x * NTHR) {
       const int i = (int)(u / q2), j = (int)(u - (int64_t)i * q2) * 4;
       float* orow = i < NS ? out_lo + ((size_t)e * NS + i) * N2
@@ -1215,15 +1261,18 @@ __global__ __launch_bounds__(256) void gg_f32_kernel(const float* __restrict__ A
   __shared__ float B1[FN][FK + 1];
   __shared__ float B3[FC1 ? FN : 1][FK + 1];
   const int m0 = blockIdx.x * FM;
-  int e, mend;
+  int e, mend, vend;   // vend: end of the rows holding tokens (later rows read as zeros)
   if (sg.cap > 0) {   // masked slabs (cap a multiple of FM: a block never straddles two)
     e = m0 / sg.cap;
     if (e >= E) return;
     mend = e * sg.cap + max(0, min(sg.counts[e], sg.cap));
+    vend = mend;
   } else {
     mend = min(sg.offsets[E], m_cap);
     if (m0 >= mend) return;
     e = tile_expert[m0 / m_tile];
+    vend = mend;
+    if (sg.counts && e >= 0 && e < E) vend = min(mend, sg.offsets[e] + max(sg.counts[e], 0));
   }
   if (m0 >= mend || e < 0 || e >= E) return;
   const int n0 = blockIdx.y * FN;
@@ -1234,7 +1283,7 @@ __global__ __launch_bounds__(256) void gg_f32_kernel(const float* __restrict__ A
     for (int i = tid; i < FM * FK; i += 256) {
       const int r = i / FK, c = i % FK;
       const int gm = min(m0 + r, mend - 1);
-      As[r][c] = A[(size_t)gm * K + k0 + c];
+      As[r][c] = m0 + r < vend ? A[(size_t)gm * K + k0 + c] : 0.0f;
     }
     if (P_MN) {   // W1 [E][ksplit][N] then W3 [E][K - ksplit][N], read along N
       for (int i = tid; i < FN * FK; i += 256) {
@@ -1294,7 +1343,8 @@ constexpr int WT = 64, WK = 16;
 
 __global__ __launch_bounds__(256) void wg_f32_kernel(const float* __restrict__ P,
                                                      const float* __restrict__ Q,
-                                                     const int32_t* __restrict__ offsets, int E,
+                                                     const int32_t* __restrict__ offsets,
+                                                     const int32_t* __restrict__ counts, int E,
                                                      int N1, int N2, int NS, int m_cap,
                                                      float* __restrict__ out_lo,
                                                      float* __restrict__ out_hi) {
@@ -1305,7 +1355,8 @@ __global__ __launch_bounds__(256) void wg_f32_kernel(const float* __restrict__ P
   const int i0 = (blockIdx.x / nt2) * WT, j0 = (blockIdx.x % nt2) * WT;
   const int mend = max(0, min(offsets[E], m_cap));
   const int s0 = max(0, min(offsets[e], mend));
-  const int s1 = max(s0, min(offsets[e + 1], mend));
+  int s1 = max(s0, min(offsets[e + 1], mend));
+  if (counts) s1 = min(s1, s0 + max(counts[e], 0));   // token rows only
   const int tid = threadIdx.x;
   const int ti = tid / 16, tj = tid % 16;
   float acc[4][4] = {};
@@ -1432,14 +1483,15 @@ hipError_t launch_grouped_swiglu(int dt, int phases, const void* x_perm, const i
 }
 
 hipError_t launch_grouped_fc1_mx(const void* xq_perm, const void* xs_perm,
-                                 const int32_t* offsets, int E, int D, int F, int64_t m_cap,
+                                 const int32_t* offsets, const int32_t* counts, int E, int D, int F,
+                                 int64_t m_cap,
                                  const void* w1q, const void* w1s, const void* w3q,
                                  const void* w3s, void* h, void* workspace, size_t ws_bytes,
                                  hipStream_t s) {
   const int G = cu_count();
   float* ws = static_cast<float*>(workspace);
   const int slots = ws ? (int)std::min<size_t>(ws_bytes / (BM * BP * sizeof(float)), 1 << 20) : 0;
-  const Segs sg{offsets, nullptr, 0};
+  const Segs sg{offsets, counts, 0};
   const Epi ep{static_cast<bf16_t*>(h), nullptr, nullptr, F};
   const MxScales ms{static_cast<const uint32_t*>(xs_perm), static_cast<const uint32_t*>(w1s),
                     static_cast<const uint32_t*>(w3s), m_cap};
@@ -1456,39 +1508,41 @@ hipError_t launch_grouped_fc1_mx(const void* xq_perm, const void* xs_perm,
 }
 
 hipError_t launch_grouped_dgrad_swiglu(int dt, const void* dy_perm, const int32_t* offsets,
-                                       const int32_t* tile_expert, int E, int D, int F,
+                                       const int32_t* counts, const int32_t* tile_expert, int E,
+                                       int D, int F,
                                        int m_tile, int64_t m_cap, const void* w2, const void* ab,
                                        void* dab, void* dh, void* workspace, size_t ws_bytes,
                                        hipStream_t s) {
   // dh = dY w2[e]: w2 [E][D][F] is the [K = D][N = F] operand, read MN-major
-  return launch_mgrouped(dt, kDgrad, true, dy_perm, Segs{offsets, nullptr, 0}, tile_expert, E, D,
+  return launch_mgrouped(dt, kDgrad, true, dy_perm, Segs{offsets, counts, 0}, tile_expert, E, D,
                          m_tile, m_cap, w2,
                          w2, D, dab, const_cast<void*>(ab), dh, F, workspace, ws_bytes, s);
 }
 
 hipError_t launch_grouped_dgrad_fc1(int dt, const void* dab, const int32_t* offsets,
-                                    const int32_t* tile_expert, int E, int D, int F, int m_tile,
+                                    const int32_t* counts, const int32_t* tile_expert, int E,
+                                    int D, int F, int m_tile,
                                     int64_t m_cap, const void* w1, const void* w3, void* dx_perm,
                                     void* workspace, size_t ws_bytes, hipStream_t s) {
   // dX = [da | db] [w1[e] ; w3[e]]: K = 2F, k < F from w1 [E][F][D], the rest from w3
-  return launch_mgrouped(dt, kFc2, true, dab, Segs{offsets, nullptr, 0}, tile_expert, E, 2 * F,
+  return launch_mgrouped(dt, kFc2, true, dab, Segs{offsets, counts, 0}, tile_expert, E, 2 * F,
                          m_tile, m_cap, w1,
                          w3, F, dx_perm, nullptr, nullptr, D, workspace, ws_bytes, s);
 }
 
 hipError_t launch_grouped_wgrad(int dt, const void* P, const void* Q, const int32_t* offsets,
-                                int E, int N1, int N2, int NS, int64_t m_cap, float* out_lo,
-                                float* out_hi, hipStream_t s) {
+                                const int32_t* counts, int E, int N1, int N2, int NS,
+                                int64_t m_cap, float* out_lo, float* out_hi, hipStream_t s) {
   if (dt == kF32) {
     const dim3 grid(((N1 + WT - 1) / WT) * ((N2 + WT - 1) / WT), E), block(256);
     hipLaunchKernelGGL(wg_f32_kernel, grid, block, 0, s, static_cast<const float*>(P),
-                       static_cast<const float*>(Q), offsets, E, N1, N2, NS, (int)m_cap, out_lo,
-                       out_hi);
+                       static_cast<const float*>(Q), offsets, counts, E, N1, N2, NS, (int)m_cap,
+                       out_lo, out_hi);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(wg_bf16_kernel, dim3(cu_count()), dim3(NTHR), 0, s,
-                     static_cast<const bf16_t*>(P), static_cast<const bf16_t*>(Q), offsets, E, N1,
-                     N2, NS, (int)m_cap, out_lo, out_hi);
+                     static_cast<const bf16_t*>(P), static_cast<const bf16_t*>(Q), offsets, counts,
+                     E, N1, N2, NS, (int)m_cap, out_lo, out_hi);
   return hipGetLastError();
 }
 

@@ -45,7 +45,8 @@ size_t grouped_workspace_bytes();
 
 // phase bit 1: fc1 (x_perm, w1, w3 -> h, and ab = [a | b] when non-null);
 // bit 2: fc2 (h, w2 -> y_perm). Rows: the segments [offsets[e], offsets[e+1]) when
-// cap == 0, else the masked slabs [e*cap, e*cap + min(counts[e], cap)).
+// cap == 0 (the first counts[e] hold tokens, the rest are pad rows; counts may be null),
+// else the masked slabs [e*cap, e*cap + min(counts[e], cap)).
 hipError_t launch_grouped_swiglu(int dt, int phases, const void* x_perm, const int32_t* offsets,
                                  const int32_t* counts, int cap, const int32_t* tile_expert, int E,
                                  int D, int F, int m_tile, int64_t m_cap, const void* w1,
@@ -55,7 +56,8 @@ hipError_t launch_grouped_swiglu(int dt, int phases, const void* x_perm, const i
 // fc1 on the FP8 payload: x (e4m3 [m_cap, D], E8M0 scales [m_cap, D/32]) against w1, w3
 // (e4m3 [E,F,D], scales [E,F,D/32]) -> h = silu(a)*b in bf16
 hipError_t launch_grouped_fc1_mx(const void* xq_perm, const void* xs_perm,
-                                 const int32_t* offsets, int E, int D, int F, int64_t m_cap,
+                                 const int32_t* offsets, const int32_t* counts, int E, int D, int F,
+                                 int64_t m_cap,
                                  const void* w1q, const void* w1s, const void* w3q,
                                  const void* w3s, void* h, void* workspace, size_t ws_bytes,
                                  hipStream_t s);
@@ -86,22 +88,24 @@ hipError_t launch_permute_mx(const void* xq, const void* xs, const int32_t* topk
 
 // dh = dy_perm w2[e] (w2 [E,D,F]), then [da | db] from ab -> dab; dh stored if non-null
 hipError_t launch_grouped_dgrad_swiglu(int dt, const void* dy_perm, const int32_t* offsets,
-                                       const int32_t* tile_expert, int E, int D, int F,
+                                       const int32_t* counts, const int32_t* tile_expert, int E,
+                                       int D, int F,
                                        int m_tile, int64_t m_cap, const void* w2, const void* ab,
                                        void* dab, void* dh, void* workspace, size_t ws_bytes,
                                        hipStream_t s);
 
 // dx_perm = da w1[e] + db w3[e] with dab = [da | db] [m_cap, 2F], w1, w3 [E,F,D]
 hipError_t launch_grouped_dgrad_fc1(int dt, const void* dab, const int32_t* offsets,
-                                    const int32_t* tile_expert, int E, int D, int F, int m_tile,
+                                    const int32_t* counts, const int32_t* tile_expert, int E,
+                                    int D, int F, int m_tile,
                                     int64_t m_cap, const void* w1, const void* w3, void* dx_perm,
                                     void* workspace, size_t ws_bytes, hipStream_t s);
 
 // out[e] = P[seg e]^T Q[seg e] (P [rows, N1], Q [rows, N2]), rows < NS of it to out_lo,
 // the rest to out_hi (float32)
 hipError_t launch_grouped_wgrad(int dt, const void* P, const void* Q, const int32_t* offsets,
-                                int E, int N1, int N2, int NS, int64_t m_cap, float* out_lo,
-                                float* out_hi, hipStream_t s);
+                                const int32_t* counts, int E, int N1, int N2, int NS,
+                                int64_t m_cap, float* out_lo, float* out_hi, hipStream_t s);
 
 // dy_perm rows [0, min(offsets[E], m_cap)): topk_w[s] * dout[s / k] for the row of slot s,
 // zero for pad rows; dtopk_w[s] = <dout[t], y_perm[row of s]>, 0 for slots without a row

@@ -142,12 +142,14 @@ moe_status_t moe_permute_noalloc(moe_dtype_t dt, const void* x, const int32_t* t
 }
 
 static moe_status_t grouped(int phases, moe_dtype_t dt, const void* x_perm,
-                            const int32_t* offsets, const int32_t* tile_expert, int E, int D, int F,
-                            int m_tile, int64_t m_cap, const void* w1, const void* w3,
-                            const void* w2, void* h, void* ab, void* y_perm, void* workspace,
-                            size_t ws_bytes, void* stream) {
+                            const int32_t* offsets, const int32_t* counts,
+                            const int32_t* tile_expert, int E, int D, int F, int m_tile,
+                            int64_t m_cap, const void* w1, const void* w3, const void* w2,
+                            void* h, void* ab, void* y_perm, void* workspace, size_t ws_bytes,
+                            void* stream) {
   if (!dtype_ok(dt) || !aligned4(offsets) || !aligned4(tile_expert) || !aligned16(h))
     return MOE_EINVAL;
+  if (counts && !aligned4(counts)) return MOE_EINVAL;
   if (workspace && !aligned16(workspace)) return MOE_EINVAL;
   if (ab && !aligned16(ab)) return MOE_EINVAL;
   if (!workspace) ws_bytes = 0;
@@ -157,35 +159,36 @@ static moe_status_t grouped(int phases, moe_dtype_t dt, const void* x_perm,
   if ((int64_t)D * F >= ((int64_t)1 << 31)) return MOE_ESHAPE;  // one expert's matrix is int32-indexed
   if (m_cap < 1 || m_cap % m_tile != 0 || m_cap > INT32_MAX) return MOE_ECAPACITY;
   if (dt == MOE_BF16 && m_tile != 128 && m_tile != 256) return MOE_EUNSUPPORTED;
-  return hip_status(moe::launch_grouped_swiglu(dt, phases, x_perm, offsets, nullptr, 0,
+  return hip_status(moe::launch_grouped_swiglu(dt, phases, x_perm, offsets, counts, 0,
                                                tile_expert, E, D, F, m_tile, m_cap, w1, w3, w2, h,
                                                ab, y_perm, ws_bytes ? workspace : nullptr,
                                                ws_bytes, static_cast<hipStream_t>(stream)));
 }
 
 moe_status_t moe_grouped_swiglu(moe_dtype_t dt, const void* x_perm, const int32_t* offsets,
-                                const int32_t* tile_expert, int E, int D, int F, int m_tile,
-                                int64_t m_cap, const void* w1, const void* w3, const void* w2,
-                                void* h, void* y_perm, void* workspace, size_t ws_bytes,
-                                void* stream) {
-  return grouped(3, dt, x_perm, offsets, tile_expert, E, D, F, m_tile, m_cap, w1, w3, w2, h,
-                 nullptr, y_perm, workspace, ws_bytes, stream);
+                                const int32_t* counts, const int32_t* tile_expert, int E, int D,
+                                int F, int m_tile, int64_t m_cap, const void* w1, const void* w3,
+                                const void* w2, void* h, void* y_perm, void* workspace,
+                                size_t ws_bytes, void* stream) {
+  return grouped(3, dt, x_perm, offsets, counts, tile_expert, E, D, F, m_tile, m_cap, w1, w3, w2,
+                 h, nullptr, y_perm, workspace, ws_bytes, stream);
 }
 
 moe_status_t moe_grouped_fc1_swiglu(moe_dtype_t dt, const void* x_perm, const int32_t* offsets,
-                                    const int32_t* tile_expert, int E, int D, int F, int m_tile,
-                                    int64_t m_cap, const void* w1, const void* w3, void* h,
-                                    void* ab, void* workspace, size_t ws_bytes, void* stream) {
-  return grouped(1, dt, x_perm, offsets, tile_expert, E, D, F, m_tile, m_cap, w1, w3, nullptr, h,
-                 ab, nullptr, workspace, ws_bytes, stream);
+                                    const int32_t* counts, const int32_t* tile_expert, int E,
+                                    int D, int F, int m_tile, int64_t m_cap, const void* w1,
+                                    const void* w3, void* h, void* ab, void* workspace,
+                                    size_t ws_bytes, void* stream) {
+  return grouped(1, dt, x_perm, offsets, counts, tile_expert, E, D, F, m_tile, m_cap, w1, w3,
+                 nullptr, h, ab, nullptr, workspace, ws_bytes, stream);
 }
 
 moe_status_t moe_grouped_fc2(moe_dtype_t dt, const void* h, const int32_t* offsets,
-                             const int32_t* tile_expert, int E, int D, int F, int m_tile,
-                             int64_t m_cap, const void* w2, void* y_perm, void* workspace,
-                             size_t ws_bytes, void* stream) {
-  return grouped(2, dt, nullptr, offsets, tile_expert, E, D, F, m_tile, m_cap, nullptr, nullptr,
-                 w2, const_cast<void*>(h), nullptr, y_perm, workspace, ws_bytes, stream);
+                             const int32_t* counts, const int32_t* tile_expert, int E, int D,
+                             int F, int m_tile, int64_t m_cap, const void* w2, void* y_perm,
+                             void* workspace, size_t ws_bytes, void* stream) {
+  return grouped(2, dt, nullptr, offsets, counts, tile_expert, E, D, F, m_tile, m_cap, nullptr,
+                 nullptr, w2, const_cast<void*>(h), nullptr, y_perm, workspace, ws_bytes, stream);
 }
 
 moe_status_t moe_permute_masked(moe_dtype_t dt, const void* x, const int32_t* topk_idx, int T,
@@ -256,14 +259,16 @@ moe_status_t moe_permute_mxfp8(const void* xq, const void* xs, const int32_t* to
 }
 
 moe_status_t moe_grouped_fc1_swiglu_mxfp8(const void* xq_perm, const void* xs_perm,
-                                          const int32_t* offsets, const int32_t* tile_expert,
-                                          int E, int D, int F, int m_tile, int64_t m_cap,
-                                          const void* w1q, const void* w1s, const void* w3q,
-                                          const void* w3s, void* h, void* workspace,
-                                          size_t ws_bytes, void* stream) {
+                                          const int32_t* offsets, const int32_t* counts,
+                                          const int32_t* tile_expert, int E, int D, int F,
+                                          int m_tile, int64_t m_cap, const void* w1q,
+                                          const void* w1s, const void* w3q, const void* w3s,
+                                          void* h, void* workspace, size_t ws_bytes,
+                                          void* stream) {
   if (!aligned16(xq_perm) || !aligned4(xs_perm) || !aligned4(offsets) || !aligned4(tile_expert) ||
       !aligned16(w1q) || !aligned4(w1s) || !aligned16(w3q) || !aligned4(w3s) || !aligned16(h))
     return MOE_EINVAL;
+  if (counts && !aligned4(counts)) return MOE_EINVAL;
   if (workspace && !aligned16(workspace)) return MOE_EINVAL;
   if (!workspace) ws_bytes = 0;
   if (E < 1 || E > kMaxExperts || !dim_ok(D) || D % 128 != 0 || !dim_ok(F) || !mtile_ok(m_tile))
@@ -271,17 +276,19 @@ moe_status_t moe_grouped_fc1_swiglu_mxfp8(const void* xq_perm, const void* xs_pe
   if ((int64_t)D * F >= ((int64_t)1 << 31)) return MOE_ESHAPE;
   if (m_cap < 1 || m_cap % m_tile != 0 || m_cap > INT32_MAX) return MOE_ECAPACITY;
   if (m_tile != 128 && m_tile != 256) return MOE_EUNSUPPORTED;
-  return hip_status(moe::launch_grouped_fc1_mx(xq_perm, xs_perm, offsets, E, D, F, m_cap, w1q,
+  return hip_status(moe::launch_grouped_fc1_mx(xq_perm, xs_perm, offsets, counts, E, D, F, m_cap,
+                                               w1q,
                                                w1s, w3q, w3s, h,
                                                ws_bytes ? workspace : nullptr, ws_bytes,
                                                static_cast<hipStream_t>(stream)));
 }
 
 static moe_status_t dgrad_common(moe_dtype_t dt, const void* a, const int32_t* offsets,
-                                 const int32_t* tile_expert, int E, int D, int F, int m_tile,
-                                 int64_t m_cap, void* workspace) {
+                                 const int32_t* counts, const int32_t* tile_expert, int E, int D,
+                                 int F, int m_tile, int64_t m_cap, void* workspace) {
   if (!dtype_ok(dt) || !aligned4(offsets) || !aligned4(tile_expert) || !aligned16(a))
     return MOE_EINVAL;
+  if (counts && !aligned4(counts)) return MOE_EINVAL;
   if (workspace && !aligned16(workspace)) return MOE_EINVAL;
   if (E < 1 || E > kMaxExperts || !dim_ok(D) || !dim_ok(F) || !mtile_ok(m_tile)) return MOE_ESHAPE;
   if ((int64_t)D * F >= ((int64_t)1 << 31)) return MOE_ESHAPE;
@@ -291,40 +298,46 @@ static moe_status_t dgrad_common(moe_dtype_t dt, const void* a, const int32_t* o
 }
 
 moe_status_t moe_grouped_dgrad_swiglu(moe_dtype_t dt, const void* dy_perm, const int32_t* offsets,
-                                      const int32_t* tile_expert, int E, int D, int F, int m_tile,
-                                      int64_t m_cap, const void* w2, const void* ab, void* dab,
-                                      void* dh, void* workspace, size_t ws_bytes, void* stream) {
+                                      const int32_t* counts, const int32_t* tile_expert, int E,
+                                      int D, int F, int m_tile, int64_t m_cap, const void* w2,
+                                      const void* ab, void* dab, void* dh, void* workspace,
+                                      size_t ws_bytes, void* stream) {
   if (!aligned16(w2) || !aligned16(ab) || !aligned16(dab) || (dh && !aligned16(dh)))
     return MOE_EINVAL;
-  const moe_status_t st = dgrad_common(dt, dy_perm, offsets, tile_expert, E, D, F, m_tile, m_cap,
-                                       workspace);
+  const moe_status_t st = dgrad_common(dt, dy_perm, offsets, counts, tile_expert, E, D, F, m_tile,
+                                       m_cap, workspace);
   if (st != MOE_OK) return st;
   if (!workspace) ws_bytes = 0;
-  return hip_status(moe::launch_grouped_dgrad_swiglu(dt, dy_perm, offsets, tile_expert, E, D, F,
+  return hip_status(moe::launch_grouped_dgrad_swiglu(dt, dy_perm, offsets, counts, tile_expert, E,
+                                                     D, F,
                                                      m_tile, m_cap, w2, ab, dab, dh,
                                                      ws_bytes ? workspace : nullptr, ws_bytes,
                                                      static_cast<hipStream_t>(stream)));
 }
 
 moe_status_t moe_grouped_dgrad_fc1(moe_dtype_t dt, const void* dab, const int32_t* offsets,
-                                   const int32_t* tile_expert, int E, int D, int F, int m_tile,
-                                   int64_t m_cap, const void* w1, const void* w3, void* dx_perm,
-                                   void* workspace, size_t ws_bytes, void* stream) {
+                                   const int32_t* counts, const int32_t* tile_expert, int E, int D,
+                                   int F, int m_tile, int64_t m_cap, const void* w1,
+                                   const void* w3, void* dx_perm, void* workspace,
+                                   size_t ws_bytes, void* stream) {
   if (!aligned16(w1) || !aligned16(w3) || !aligned16(dx_perm)) return MOE_EINVAL;
-  const moe_status_t st = dgrad_common(dt, dab, offsets, tile_expert, E, D, F, m_tile, m_cap,
-                                       workspace);
+  const moe_status_t st = dgrad_common(dt, dab, offsets, counts, tile_expert, E, D, F, m_tile,
+                                       m_cap, workspace);
   if (st != MOE_OK) return st;
   if (!workspace) ws_bytes = 0;
-  return hip_status(moe::launch_grouped_dgrad_fc1(dt, dab, offsets, tile_expert, E, D, F, m_tile,
+  return hip_status(moe::launch_grouped_dgrad_fc1(dt, dab, offsets, counts, tile_expert, E, D, F,
+                                                  m_tile,
                                                   m_cap, w1, w3, dx_perm,
                                                   ws_bytes ? workspace : nullptr, ws_bytes,
                                                   static_cast<hipStream_t>(stream)));
 }
 
 moe_status_t moe_grouped_wgrad(moe_dtype_t dt, const void* P, const void* Q,
-                               const int32_t* offsets, int E, int N1, int N2, int NS, int m_tile,
-                               int64_t m_cap, float* out_lo, float* out_hi, void* stream) {
+                               const int32_t* offsets, const int32_t* counts, int E, int N1,
+                               int N2, int NS, int m_tile, int64_t m_cap, float* out_lo,
+                               float* out_hi, void* stream) {
   if (!dtype_ok(dt) || !aligned16(P) || !aligned16(Q) || !aligned4(offsets)) return MOE_EINVAL;
+  if (counts && !aligned4(counts)) return MOE_EINVAL;
   if (NS < 0 || NS > N1) return MOE_ESHAPE;
   if ((NS > 0 && !aligned16(out_lo)) || (NS < N1 && !aligned16(out_hi))) return MOE_EINVAL;
   if (E < 1 || E > kMaxExperts || !dim_ok(N1) || !dim_ok(N2) || !mtile_ok(m_tile))
@@ -332,7 +345,8 @@ moe_status_t moe_grouped_wgrad(moe_dtype_t dt, const void* P, const void* Q,
   if (m_cap < 1 || m_cap % m_tile != 0 || m_cap > INT32_MAX) return MOE_ECAPACITY;
   // a segment's rows of one operand are addressed with 32-bit byte offsets
   if ((m_cap + 64) * (int64_t)(N1 > N2 ? N1 : N2) >= ((int64_t)1 << 31)) return MOE_ESHAPE;
-  return hip_status(moe::launch_grouped_wgrad(dt, P, Q, offsets, E, N1, N2, NS, m_cap, out_lo,
+  return hip_status(moe::launch_grouped_wgrad(dt, P, Q, offsets, counts, E, N1, N2, NS, m_cap,
+                                              out_lo,
                                               out_hi, static_cast<hipStream_t>(stream)));
 }
 

@@ -66,12 +66,13 @@ def moe_layer(x: torch.Tensor, w1: torch.Tensor, w3: torch.Tensor, w2: torch.Ten
         ab = torch.empty((m_cap, 2 * F), dtype=x.dtype, device=x.device)
         y = torch.empty((m_cap, D), dtype=x.dtype, device=x.device)
         B.moe_grouped_fc1_swiglu(p["x_perm"], p["offsets"], p["tile_expert"], w1, w3, m_tile,
-                                 m_cap, h, ab=ab, workspace=ws)
-        B.moe_grouped_fc2(h, p["offsets"], p["tile_expert"], w2, m_tile, m_cap, y, workspace=ws)
+                                 m_cap, h, ab=ab, workspace=ws, counts=p["counts"])
+        B.moe_grouped_fc2(h, p["offsets"], p["tile_expert"], w2, m_tile, m_cap, y, workspace=ws,
+                          counts=p["counts"])
         res["ab"] = ab
     else:
         h, y = B.moe_grouped_swiglu(p["x_perm"], p["offsets"], p["tile_expert"], w1, w3, w2,
-                                    m_tile, m_cap=m_cap, workspace=ws)
+                                    m_tile, m_cap=m_cap, workspace=ws, counts=p["counts"])
     res["h"], res["y_perm"] = h, y
     sh = None
     if shared is not None:
@@ -171,9 +172,10 @@ def moe_layer_mxfp8(x: torch.Tensor, mw: MxWeights, w2: torch.Tensor, k: int, m_
     ws = B.grouped_workspace(x.device) if split_k else None
     h = B.moe_grouped_fc1_swiglu_mxfp8(p["xq_perm"], p["xs_perm"], p["offsets"], p["tile_expert"],
                                        mw.w1q, mw.w1s, mw.w3q, mw.w3s, m_tile, m_cap,
-                                       workspace=ws)
+                                       workspace=ws, counts=p["counts"])
     y = torch.empty((m_cap, x.shape[1]), dtype=x.dtype, device=x.device)
-    B.moe_grouped_fc2(h, p["offsets"], p["tile_expert"], w2, m_tile, m_cap, y, workspace=ws)
+    B.moe_grouped_fc2(h, p["offsets"], p["tile_expert"], w2, m_tile, m_cap, y, workspace=ws,
+                      counts=p["counts"])
     res["h"], res["y_perm"] = h, y
     sh = None
     if shared is not None:
@@ -188,18 +190,19 @@ def moe_layer_mxfp8(x: torch.Tensor, mw: MxWeights, w2: torch.Tensor, k: int, m_
 
 
 def _experts_backward(dy, x_rows, ab, h, offsets, tile_expert, w1, w3, w2, m_tile, m_cap, ws,
-                      rows_used=None):
+                      rows_used=None, counts=None):
     """dgrad and wgrad of one grouped SwiGLU FFN over rows [0, m_cap) (section 5 of
     "Expert Parallelism (EP)": the m-grouped fc mirrors into an m-grouped dgrad and a
     k-grouped wgrad). Returns (dab, dX, dw1, dw3, dw2)."""
     F, D = w1.shape[1], w1.shape[2]
-    ru = rows_used
+    ru, c = rows_used, counts
     dab = B.moe_grouped_dgrad_swiglu(dy, offsets, tile_expert, w2, ab, m_tile, m_cap,
-                                     workspace=ws, rows_used=ru)
+                                     workspace=ws, rows_used=ru, counts=c)
     dX = B.moe_grouped_dgrad_fc1(dab, offsets, tile_expert, w1, w3, m_tile, m_cap, workspace=ws,
-                                 rows_used=ru)
-    dw1, dw3 = B.moe_grouped_wgrad(dab, x_rows, offsets, m_tile, m_cap, NS=F, rows_used=ru)
-    dw2, _ = B.moe_grouped_wgrad(dy, h, offsets, m_tile, m_cap, NS=D, rows_used=ru)
+                                 rows_used=ru, counts=c)
+    dw1, dw3 = B.moe_grouped_wgrad(dab, x_rows, offsets, m_tile, m_cap, NS=F, rows_used=ru,
+                                   counts=c)
+    dw2, _ = B.moe_grouped_wgrad(dy, h, offsets, m_tile, m_cap, NS=D, rows_used=ru, counts=c)
     return dab, dX, dw1, dw3, dw2
 
 
@@ -221,7 +224,8 @@ def moe_layer_backward(fwd: dict, dout: torch.Tensor, x: torch.Tensor, w1: torch
                                      fwd["topk_w"], m_cap=m_cap)
     res["dy_perm"], res["dtopk_w"] = dy, dtw
     dab, dX, dw1, dw3, dw2 = _experts_backward(dy, fwd["x_perm"], fwd["ab"], fwd["h"], offs, te,
-                                               w1, w3, w2, m_tile, m_cap, ws)
+                                               w1, w3, w2, m_tile, m_cap, ws,
+                                               counts=fwd["counts"])
     res.update(dab=dab, dx_perm=dX, dw1=dw1, dw3=dw3, dw2=dw2)
     dxs = None
     if shared is not None:

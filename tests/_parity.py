@@ -79,7 +79,7 @@ def run_gpu(inp: dict, k: int, m_tile: int, renorm: bool = False, want_logits: b
     h = poison(torch.empty((m_cap, F), dtype=d["x"].dtype, device="cuda"))
     y = poison(torch.empty((m_cap, inp["x"].shape[1]), dtype=d["x"].dtype, device="cuda"))
     rpg.moe_grouped_swiglu(p["x_perm"], p["offsets"], p["tile_expert"], d["w1"], d["w3"], d["w2"],
-                           m_tile, m_cap=m_cap, h=h, y_perm=y, workspace=ws)
+                           m_tile, m_cap=m_cap, h=h, y_perm=y, workspace=ws, counts=p["counts"])
     out["h"], out["y_perm"] = h, y
     shared = None
     if "ws1" in d:

@@ -101,9 +101,9 @@ def test_permute_validation(kw, code):
 
 
 def grouped(dt=1, xp=FAKE, E=8, D=128, F=256, mt=128, m_cap=1024, w1=FAKE, h=FAKE, ws=None,
-            ws_bytes=0):
-    return lib.moe_grouped_swiglu(dt, xp, FAKE, FAKE, E, D, F, mt, m_cap, w1, FAKE, FAKE, h, FAKE,
-                                  ws, ws_bytes, None)
+            ws_bytes=0, counts=None):
+    return lib.moe_grouped_swiglu(dt, xp, FAKE, counts, FAKE, E, D, F, mt, m_cap, w1, FAKE, FAKE, h,
+                                  FAKE, ws, ws_bytes, None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -112,24 +112,24 @@ def grouped(dt=1, xp=FAKE, E=8, D=128, F=256, mt=128, m_cap=1024, w1=FAKE, h=FAK
     (dict(mt=7), MOE_ESHAPE), (dict(m_cap=0), MOE_ECAPACITY), (dict(m_cap=1000), MOE_ECAPACITY),
     (dict(mt=64, m_cap=1024), MOE_EUNSUPPORTED), (dict(D=65536, F=32768), MOE_ESHAPE),
     (dict(mt=16, m_cap=1024), MOE_EUNSUPPORTED), (dict(ws=FAKE + 8, ws_bytes=1 << 20), MOE_EINVAL),
-    (dict(dt=7, ws=FAKE, ws_bytes=1 << 20), MOE_EINVAL),
+    (dict(dt=7, ws=FAKE, ws_bytes=1 << 20), MOE_EINVAL), (dict(counts=FAKE + 2), MOE_EINVAL),
 ])
 def test_grouped_validation(kw, code):
     assert grouped(**kw) == code
 
 
 def test_split_grouped_calls_validate():
-    assert lib.moe_grouped_fc1_swiglu(1, FAKE, FAKE, FAKE, 8, 128, 256, 128, 1024, None, FAKE,
+    assert lib.moe_grouped_fc1_swiglu(1, FAKE, FAKE, None, FAKE, 8, 128, 256, 128, 1024, None, FAKE,
                                       FAKE, None, None, 0, None) == MOE_EINVAL
-    assert lib.moe_grouped_fc1_swiglu(1, FAKE, FAKE, FAKE, 8, 128, 250, 128, 1024, FAKE, FAKE,
+    assert lib.moe_grouped_fc1_swiglu(1, FAKE, FAKE, None, FAKE, 8, 128, 250, 128, 1024, FAKE, FAKE,
                                       FAKE, None, None, 0, None) == MOE_ESHAPE
-    assert lib.moe_grouped_fc1_swiglu(1, FAKE, FAKE, FAKE, 8, 128, 256, 128, 1024, FAKE, FAKE,
+    assert lib.moe_grouped_fc1_swiglu(1, FAKE, FAKE, None, FAKE, 8, 128, 256, 128, 1024, FAKE, FAKE,
                                       FAKE, None, FAKE + 4, 1 << 20, None) == MOE_EINVAL
-    assert lib.moe_grouped_fc1_swiglu(1, FAKE, FAKE, FAKE, 8, 128, 256, 128, 1024, FAKE, FAKE,
+    assert lib.moe_grouped_fc1_swiglu(1, FAKE, FAKE, None, FAKE, 8, 128, 256, 128, 1024, FAKE, FAKE,
                                       FAKE, FAKE + 2, None, 0, None) == MOE_EINVAL
-    assert lib.moe_grouped_fc2(1, FAKE, FAKE, FAKE, 8, 128, 256, 128, 1000, FAKE, FAKE,
+    assert lib.moe_grouped_fc2(1, FAKE, FAKE, None, FAKE, 8, 128, 256, 128, 1000, FAKE, FAKE,
                                None, 0, None) == MOE_ECAPACITY
-    assert lib.moe_grouped_fc2(1, FAKE, FAKE, FAKE, 8, 128, 256, 64, 1024, FAKE, FAKE,
+    assert lib.moe_grouped_fc2(1, FAKE, FAKE, None, FAKE, 8, 128, 256, 64, 1024, FAKE, FAKE,
                                FAKE, 1 << 20, None) == MOE_EUNSUPPORTED
 
 
@@ -175,7 +175,7 @@ def test_combine_backward_validation(kw, code):
 
 def dgrad(dt=1, dy=FAKE, E=8, D=128, F=256, mt=128, m_cap=1024, w2=FAKE, ab=FAKE, dab=FAKE,
           dh=None, ws=None, ws_bytes=0):
-    return lib.moe_grouped_dgrad_swiglu(dt, dy, FAKE, FAKE, E, D, F, mt, m_cap, w2, ab, dab, dh,
+    return lib.moe_grouped_dgrad_swiglu(dt, dy, FAKE, None, FAKE, E, D, F, mt, m_cap, w2, ab, dab, dh,
                                         ws, ws_bytes, None)
 
 
@@ -192,7 +192,7 @@ def test_dgrad_validation(kw, code):
 
 def dgrad_fc1(dt=1, dab=FAKE, E=8, D=128, F=256, mt=128, m_cap=1024, w1=FAKE, w3=FAKE, dx=FAKE,
               ws=None, ws_bytes=0):
-    return lib.moe_grouped_dgrad_fc1(dt, dab, FAKE, FAKE, E, D, F, mt, m_cap, w1, w3, dx, ws,
+    return lib.moe_grouped_dgrad_fc1(dt, dab, FAKE, None, FAKE, E, D, F, mt, m_cap, w1, w3, dx, ws,
                                      ws_bytes, None)
 
 
@@ -209,7 +209,7 @@ def test_dgrad_fc1_validation(kw, code):
 
 def wgrad(dt=1, P=FAKE, Q=FAKE, off=FAKE, E=8, N1=512, N2=128, NS=256, mt=128, m_cap=1024,
           lo=FAKE, hi=FAKE):
-    return lib.moe_grouped_wgrad(dt, P, Q, off, E, N1, N2, NS, mt, m_cap, lo, hi, None)
+    return lib.moe_grouped_wgrad(dt, P, Q, off, None, E, N1, N2, NS, mt, m_cap, lo, hi, None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -284,7 +284,7 @@ def test_mxfp8_calls_validate():
     assert p(m_cap=100) == MOE_ECAPACITY
     assert p(ws=0) == MOE_EWORKSPACE
     f = lambda **kw: lib.moe_grouped_fc1_swiglu_mxfp8(
-        kw.get("xq", FAKE), FAKE, FAKE, FAKE, 8, kw.get("D", 512), kw.get("F", 256),
+        kw.get("xq", FAKE), FAKE, FAKE, None, FAKE, 8, kw.get("D", 512), kw.get("F", 256),
         kw.get("mt", 128), kw.get("m_cap", 1024), FAKE, FAKE, FAKE, FAKE, kw.get("h", FAKE),
         None, 0, None)
     assert f(xq=FAKE + 4) == MOE_EINVAL

@@ -263,3 +263,81 @@ def test_bitwise_run_to_run_determinism():
         np.testing.assert_array_equal(a[key], b[key], err_msg=key)
     for key in ("x_perm", "h", "y_perm"):
         np.testing.assert_array_equal(a[key][:used], b[key][:used], err_msg=key)
+
+
+@pytest.mark.parametrize("split", [True, False])
+def test_grouped_calls_skip_pad_rows_given_counts(split):
+    # pad rows hold NaN: with counts the tiled kernels must neither read them nor let them
+    # reach any output (h, y_perm pad rows exactly 0), while token rows match the oracle;
+    # the token rows end at many places inside full (256-row) and half (128-row) tiles
+    P.log(f"[parity] grouped calls with counts and NaN pad rows, split={split}")
+    D, F, mt = 256, 384, 128
+    counts = np.array([1, 31, 32, 33, 100, 127, 129, 200, 255, 256, 257, 383, 0, 64], np.int32)
+    E = counts.size
+    padded = -(-counts // mt) * mt
+    offsets = np.concatenate([[0], np.cumsum(padded)]).astype(np.int32)
+    m_cap = int(offsets[-1])
+    rng = np.random.default_rng(21)
+    x = W.f32_to_bf16_bits(rng.standard_normal((m_cap, D)).astype(np.float32))
+    w1 = W.f32_to_bf16_bits((rng.standard_normal((E, F, D)) / 16).astype(np.float32))
+    w3 = W.f32_to_bf16_bits((rng.standard_normal((E, F, D)) / 16).astype(np.float32))
+    w2 = W.f32_to_bf16_bits((rng.standard_normal((E, D, F)) / 20).astype(np.float32))
+    pad = np.ones(m_cap, bool)
+    for e in range(E):
+        pad[offsets[e]:offsets[e] + counts[e]] = False
+    x_zero = x.copy()
+    x_zero[pad] = 0
+    x_nan = x.copy()
+    x_nan[pad] = 0x7FC0                                     # bf16 quiet NaN
+    h_ref, y_ref = orc.grouped_swiglu(x_zero, offsets, w1, w3, w2, "bf16")
+    te = np.repeat(np.arange(E, dtype=np.int32), padded // mt)
+    ws = rpg.grouped_workspace("cuda") if split else None
+    h = P.poison(torch.empty((m_cap, F), dtype=torch.bfloat16, device="cuda"))
+    y = P.poison(torch.empty((m_cap, D), dtype=torch.bfloat16, device="cuda"))
+    dc = P.to_dev(counts)
+    rpg.moe_grouped_swiglu(P.to_dev(x_nan), P.to_dev(offsets), P.to_dev(te), P.to_dev(w1),
+                           P.to_dev(w3), P.to_dev(w2), mt, m_cap=m_cap, h=h, y_perm=y,
+                           workspace=ws, counts=dc)
+    torch.cuda.synchronize()
+    for name, got, ref in (("h", h, h_ref), ("y", y, y_ref)):
+        v = orc.values64(P.to_host(got))
+        assert np.all(v[pad] == 0), f"{name}: pad rows not exactly zero"
+        assert np.all(np.isfinite(v)), f"{name}: unwritten or NaN rows"
+        e = P.rel_err(P.to_host(got)[~pad], ref[~pad])
+        assert e <= P.TOL["bf16"], (name, e)
+    # backward: NaN pad rows in dy and in the saved [a | b] must not reach dab, dX or the
+    # weight gradients
+    ab_ref = orc.preactivations(x_zero, offsets, w1, w3, "bf16")
+    dy = W.f32_to_bf16_bits(rng.standard_normal((m_cap, D)).astype(np.float32))
+    dy_zero = dy.copy()
+    dy_zero[pad] = 0
+    dy_nan = dy.copy()
+    dy_nan[pad] = 0x7FC0
+    ab_st = W.f32_to_bf16_bits(ab_ref.astype(np.float32))
+    ab_nan = ab_st.copy()
+    ab_nan[pad] = 0x7FC0
+    bw = orc.grouped_backward(x_zero, ab_st, h_ref, dy_zero, offsets, w1, w3, w2, "bf16")
+    dab = P.poison(torch.empty((m_cap, 2 * F), dtype=torch.bfloat16, device="cuda"))
+    rpg.moe_grouped_dgrad_swiglu(P.to_dev(dy_nan), P.to_dev(offsets), P.to_dev(te), P.to_dev(w2),
+                                 P.to_dev(ab_nan), mt, m_cap, dab=dab, workspace=ws, counts=dc)
+    dab_st = W.f32_to_bf16_bits(bw[1].astype(np.float32))
+    dab_nan = dab_st.copy()
+    dab_nan[pad] = 0x7FC0
+    dx = P.poison(torch.empty((m_cap, D), dtype=torch.bfloat16, device="cuda"))
+    rpg.moe_grouped_dgrad_fc1(P.to_dev(dab_nan), P.to_dev(offsets), P.to_dev(te), P.to_dev(w1),
+                              P.to_dev(w3), mt, m_cap, dx_perm=dx, workspace=ws, counts=dc)
+    x_nan_dev = P.to_dev(x_nan)
+    dw1, dw3 = rpg.moe_grouped_wgrad(P.to_dev(dab_nan), x_nan_dev, P.to_dev(offsets), mt, m_cap,
+                                     NS=F, counts=dc)
+    torch.cuda.synchronize()
+    for name, got, ref in (("dab", P.to_host(dab), bw[1]), ("dX", P.to_host(dx), bw[2])):
+        v = orc.values64(got)
+        assert np.all(v[pad] == 0) and np.all(np.isfinite(v)), name
+        e = P.rel_err(got[~pad], ref[~pad])
+        assert e <= P.TOL["bf16"], (name, e)
+    for name, got, ref in (("dW1", dw1, bw[3]), ("dW3", dw3, bw[4])):
+        g = P.to_host(got).astype(np.float64)
+        assert np.all(np.isfinite(g)), name
+        assert np.all(g[counts == 0] == 0), name
+        e = np.abs(g - ref).max() / np.abs(ref).max()
+        assert e <= P.TOL["bf16"], (name, e)
