@@ -59,6 +59,48 @@ def gemm_source_sha16() -> str:
 TRAFFIC = {}
 
 
+class HipEvent:
+    """A timing-only HIP event recorded on a given stream. It is created with
+    hipEventDisableSystemFence: a default event's record makes a system-scope fence (an L2
+    writeback and invalidate), which costs microseconds at every stage boundary and starts
+    the next stage with a cold L2; a timing event needs none of it (the record still waits
+    for the work before it on the stream). Same interface as torch.cuda.Event."""
+    _lib = None
+
+    def __init__(self):
+        import ctypes
+        if HipEvent._lib is None:
+            lib = ctypes.CDLL("libamdhip64.so")
+            lib.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                ctypes.c_void_p]
+            lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            HipEvent._lib = lib
+        self._ct = ctypes
+        self.h = ctypes.c_void_p()
+        rc = HipEvent._lib.hipEventCreateWithFlags(ctypes.byref(self.h), 0x20000000)
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+
+    def record(self, stream) -> None:
+        rc = HipEvent._lib.hipEventRecord(self.h, self._ct.c_void_p(stream.cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
+
+    def elapsed_time(self, end: "HipEvent") -> float:
+        """Milliseconds from this event to ``end`` (both recorded and completed)."""
+        ms = self._ct.c_float()
+        rc = HipEvent._lib.hipEventElapsedTime(self._ct.byref(ms), self.h, end.h)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return ms.value
+
+    def __del__(self):
+        if HipEvent._lib is not None and self.h:
+            HipEvent._lib.hipEventDestroy(self.h)
+
+
 def traffic(kind: str, workload: str):
     """(bytes, note) for the kernel ``kind`` on ``workload``: the stored counter reading
     when it was taken at the current GEMM sources, else (None, why)."""
@@ -299,10 +341,11 @@ def run_contiguous(args, cfg, d: dict, headline: bool) -> dict:
         rpg.moe_permute(d["x"], buf["idx"], E, mt, m_cap=m_cap, out=buf, stream=stream)
         mark(2)
         rpg.moe_grouped_fc1_swiglu(buf["x_perm"], buf["offsets"], buf["tile_expert"], d["w1"],
-                                   d["w3"], mt, m_cap, buf["h"], workspace=gws, stream=stream)
+                                   d["w3"], mt, m_cap, buf["h"], workspace=gws, stream=stream,
+                                   counts=buf["counts"])
         mark(3)
         rpg.moe_grouped_fc2(buf["h"], buf["offsets"], buf["tile_expert"], d["w2"], mt, m_cap,
-                            buf["y"], workspace=gws, stream=stream)
+                            buf["y"], workspace=gws, stream=stream, counts=buf["counts"])
         mark(4)
         sh = None
         if shared is not None:
@@ -324,7 +367,7 @@ def run_contiguous(args, cfg, d: dict, headline: bool) -> dict:
     if int(buf["dev_err"].item()) != 0:
         raise RuntimeError("permute reported expert indices outside [-1, E)")
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(marks) + 1)]
+    events = [[HipEvent() for _ in range(len(marks) + 1)]
               for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -398,6 +441,8 @@ def run_contiguous(args, cfg, d: dict, headline: bool) -> dict:
         "combine_GBps": comb_gbps, "combine_frac_hbm": comb_gbps / PEAK_HBM_GBPS,
         "stage_us_median": med, "stage_us_mean": avg, "stage_us_spread": spread,
         "timing": {"value_from": "sum of per-step HIP-event durations on the compute stream",
+                   "events": "hipEventCreateWithFlags(hipEventDisableSystemFence): timing only, "
+                             "no cache writeback or invalidate at a stage boundary",
                    "cache_flush_MiB_between_steps": args.flush_mib,
                    "wall_ms_per_step_incl_flush": wall * 1e3 / args.steps},
         "assignments": n_valid,
@@ -510,7 +555,7 @@ def bench_masked(args, cfg, d, inp) -> dict:
         for _ in range(args.warmup):
             step(contiguous=contiguous)
         torch.cuda.synchronize()
-        events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(marks) + 1)]
+        events = [[HipEvent() for _ in range(len(marks) + 1)]
                   for _ in range(args.steps)]
         for s_ in range(args.steps):
             if flush is not None:
@@ -609,10 +654,11 @@ def bench_fp8(args, cfg, d, buf, shared, gws, flush, n_valid) -> dict:
         mark(3)
         rpg.moe_grouped_fc1_swiglu_mxfp8(fb["xq_perm"], fb["xs_perm"], fb["offsets"],
                                          fb["tile_expert"], mw.w1q, mw.w1s, mw.w3q, mw.w3s, mt,
-                                         m_cap, h=buf["h"], workspace=gws, stream=stream)
+                                         m_cap, h=buf["h"], workspace=gws, stream=stream,
+                                         counts=fb["counts"])
         mark(4)
         rpg.moe_grouped_fc2(buf["h"], fb["offsets"], fb["tile_expert"], d["w2"], mt, m_cap,
-                            buf["y"], workspace=gws, stream=stream)
+                            buf["y"], workspace=gws, stream=stream, counts=fb["counts"])
         mark(5)
         sh = None
         if shared is not None:
@@ -629,7 +675,7 @@ def bench_fp8(args, cfg, d, buf, shared, gws, flush, n_valid) -> dict:
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(marks) + 1)]
+    events = [[HipEvent() for _ in range(len(marks) + 1)]
               for _ in range(args.steps)]
     for s_ in range(args.steps):
         if flush is not None:
@@ -688,9 +734,11 @@ def bench_backward(args, cfg, d, buf, shared, gws, flush, n_valid) -> dict:
          "dw3": em(E, F, D, dtype=f32), "dw2": em(E, D, F, dtype=f32), "dx": em(T, D)}
     offs, te = buf["offsets"], buf["tile_expert"]
     # forward once more, keeping fc1's pre-activations (routing/permute as in the timed run)
+    cnt = buf["counts"]
     rpg.moe_grouped_fc1_swiglu(buf["x_perm"], offs, te, d["w1"], d["w3"], mt, m_cap, buf["h"],
-                               ab=b["ab"], workspace=gws)
-    rpg.moe_grouped_fc2(buf["h"], offs, te, d["w2"], mt, m_cap, buf["y"], workspace=gws)
+                               ab=b["ab"], workspace=gws, counts=cnt)
+    rpg.moe_grouped_fc2(buf["h"], offs, te, d["w2"], mt, m_cap, buf["y"], workspace=gws,
+                        counts=cnt)
     if shared is not None:
         rows = rpg.DenseRows(T, mt, dev)
         SF = shared.w1.shape[1]
@@ -702,19 +750,19 @@ def bench_backward(args, cfg, d, buf, shared, gws, flush, n_valid) -> dict:
                                    mt, rows.m_cap, b["s_h"], ab=b["s_ab"], workspace=gws,
                                    rows_used=T)
 
-    def experts_bwd(dy, xr, ab, h, o, tt, w1, w3, w2, mcap, pre, ru=None):
+    def experts_bwd(dy, xr, ab, h, o, tt, w1, w3, w2, mcap, pre, ru=None, c=None):
         Fx = w1.shape[1]
         rpg.moe_grouped_dgrad_swiglu(dy, o, tt, w2, ab, mt, mcap, dab=b[pre + "dab"],
-                                     workspace=gws, stream=stream, rows_used=ru)
+                                     workspace=gws, stream=stream, rows_used=ru, counts=c)
         mark()
         rpg.moe_grouped_dgrad_fc1(b[pre + "dab"], o, tt, w1, w3, mt, mcap, dx_perm=b[pre + "dX"],
-                                  workspace=gws, stream=stream, rows_used=ru)
+                                  workspace=gws, stream=stream, rows_used=ru, counts=c)
         mark()
         rpg.moe_grouped_wgrad(b[pre + "dab"], xr, o, mt, mcap, NS=Fx, out_lo=b[pre + "dw1"],
-                              out_hi=b[pre + "dw3"], stream=stream, rows_used=ru)
+                              out_hi=b[pre + "dw3"], stream=stream, rows_used=ru, counts=c)
         mark()
         rpg.moe_grouped_wgrad(dy, h, o, mt, mcap, NS=D, out_lo=b[pre + "dw2"], stream=stream,
-                              rows_used=ru)
+                              rows_used=ru, counts=c)
         mark()
 
     marks = ["combine_bwd", "dgrad_fc2", "dgrad_fc1", "wgrad_fc1", "wgrad_fc2"]
@@ -735,7 +783,7 @@ def bench_backward(args, cfg, d, buf, shared, gws, flush, n_valid) -> dict:
                                  m_cap=m_cap, dy_perm=b["dy"], dtopk_w=b["dtw"], stream=stream)
         mark()
         experts_bwd(b["dy"], buf["x_perm"], b["ab"], buf["h"], offs, te, d["w1"], d["w3"],
-                    d["w2"], m_cap, "")
+                    d["w2"], m_cap, "", c=cnt)
         sh = None
         if shared is not None:
             experts_bwd(dout, d["x"], b["s_ab"], b["s_h"], rows.offsets, rows.tile_expert,
@@ -748,7 +796,7 @@ def bench_backward(args, cfg, d, buf, shared, gws, flush, n_valid) -> dict:
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(marks) + 1)]
+    events = [[HipEvent() for _ in range(len(marks) + 1)]
               for _ in range(args.steps)]
     for s_ in range(args.steps):
         if flush is not None:
