@@ -14,6 +14,9 @@ enum DType { kF32 = 0, kBF16 = 1 };
 // number of earlier slots of its expert: earlier blocks + earlier in the block).
 constexpr int kHistTokens = 256;
 
+// Largest top-k the entry points accept.
+constexpr int kMaxTopK = 32;
+
 int cu_count();  // compute units of the current device (cached per device)
 
 hipError_t launch_route(int dt, const void* x, const void* wg, const float* bias, int T, int D,

@@ -30,7 +30,7 @@ namespace {
 
 constexpr int kMaxExpertsRoute = 64;
 constexpr int kMaxExperts = 1024;
-constexpr int kMaxK = 32;
+constexpr int kMaxK = moe::kMaxTopK;
 constexpr int kMaxDim = 1 << 16;
 
 bool aligned16(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }

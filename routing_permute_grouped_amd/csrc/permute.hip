@@ -56,6 +56,7 @@ constexpr int kMaxExperts = 1024;
 constexpr int kPlaceTokens = 16;
 constexpr int kThreads = 256;
 constexpr int kUnroll = 4;   // 16-byte chunks per thread in flight during the copy
+constexpr int kBatch = 8;    // index loads per thread in flight while counting
 static_assert(kHistTokens % kPlaceTokens == 0, "place blocks nest in histogram blocks");
 
 __global__ __launch_bounds__(kThreads) void hist_kernel(const int32_t* __restrict__ idx, int T,
@@ -68,12 +69,22 @@ __global__ __launch_bounds__(kThreads) void hist_kernel(const int32_t* __restric
   __syncthreads();
   const int64_t a0 = (int64_t)blockIdx.x * kHistTokens * k;
   const int64_t a1 = min(a0 + (int64_t)kHistTokens * k, (int64_t)T * k);
-  for (int64_t a = a0 + threadIdx.x; a < a1; a += kThreads) {
-    const int e = idx[a];
-    if (e >= 0 && e < E)
-      atomicAdd(&cnt[e], 1);
-    else if (e != -1)
-      atomicAdd(&nbad, 1);
+  // kBatch loads per thread go out before their atomics: one memory round trip per batch
+  for (int64_t g = a0 + threadIdx.x; g < a1; g += (int64_t)kThreads * kBatch) {
+    int ev[kBatch];
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int64_t a = g + (int64_t)i * kThreads;
+      ev[i] = a < a1 ? idx[a] : -1;
+    }
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int e = ev[i];
+      if (e >= 0 && e < E)
+        atomicAdd(&cnt[e], 1);
+      else if (e != -1)
+        atomicAdd(&nbad, 1);
+    }
   }
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += kThreads) hist[(size_t)blockIdx.x * E + e] = cnt[e];
@@ -125,12 +136,33 @@ __global__ __launch_bounds__(kThreads) void rank_kernel(
     base[e] = 0;
   }
   __syncthreads();
-  for (int i = tid; i < nbh * E; i += kThreads) {
-    const int h = i / E, e = i - h * E;
-    const int c = hist[i];
-    if (c) {
-      atomicAdd(&cnt[e], c);
-      if (h < hb) atomicAdd(&base[e], c);
+  // wave 0 fetches the expert indices of this workgroup's own slots now, so their load
+  // overlaps the table's (up to kPlaceTokens * kMaxTopK / kWave = 8 per lane)
+  const int t_end = token_block ? min(T, t_begin + kPlaceTokens) : t_begin;
+  const int n = (t_end - t_begin) * k;
+  const int64_t a0 = (int64_t)t_begin * k;
+  int own[kPlaceTokens * kMaxTopK / kWave];
+  if (tid < kWave) {
+#pragma unroll
+    for (int i = 0; i < kPlaceTokens * kMaxTopK / kWave; ++i) {
+      const int a = i * kWave + tid;
+      own[i] = a < n ? idx[a0 + a] : -1;
+    }
+  }
+  for (int i0 = tid; i0 < nbh * E; i0 += kThreads * kBatch) {
+    int cv[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int i = i0 + j * kThreads;
+      cv[j] = i < nbh * E ? hist[i] : 0;
+    }
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      if (cv[j] == 0) continue;
+      const int i = i0 + j * kThreads;
+      const int h = i / E, e = i - h * E;
+      atomicAdd(&cnt[e], cv[j]);
+      if (h < hb) atomicAdd(&base[e], cv[j]);
     }
   }
   __syncthreads();
@@ -202,23 +234,32 @@ __global__ __launch_bounds__(kThreads) void rank_kernel(
     return;
   }
 
-  // slots of this histogram block that precede this workgroup's tokens
-  for (int64_t a = (int64_t)hb * kHistTokens * k + tid; a < (int64_t)t_begin * k; a += kThreads) {
-    const int e = idx[a];
-    if (e >= 0 && e < E) atomicAdd(&base[e], 1);
+  // slots of this histogram block that precede this workgroup's tokens (loads batched
+  // ahead of their atomics, as in hist_kernel)
+  const int64_t p1 = (int64_t)t_begin * k;
+  for (int64_t g = (int64_t)hb * kHistTokens * k + tid; g < p1; g += (int64_t)kThreads * kBatch) {
+    int ev[kBatch];
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int64_t a = g + (int64_t)i * kThreads;
+      ev[i] = a < p1 ? idx[a] : -1;
+    }
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i)
+      if (ev[i] >= 0 && ev[i] < E) atomicAdd(&base[ev[i]], 1);
   }
   __syncthreads();
 
-  const int t_end = min(T, t_begin + kPlaceTokens);
-  const int n = (t_end - t_begin) * k;
-  const int64_t a0 = (int64_t)t_begin * k;
   if (tid < kWave) {
     const int lane = tid;
     const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
     const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
-    for (int r0 = 0; r0 < n; r0 += kWave) {
+#pragma unroll
+    for (int i = 0; i < kPlaceTokens * kMaxTopK / kWave; ++i) {
+      const int r0 = i * kWave;
+      if (r0 >= n) break;
       const int a = r0 + lane;
-      const int e = a < n ? idx[a0 + a] : -1;
+      const int e = own[i];
       const bool valid = a < n && e >= 0 && e < E;
       uint64_t same = __ballot(valid);
       for (int bit = 0; bit < nbits; ++bit) {
