@@ -23,9 +23,11 @@
 //     wgrad) is staged as 512-byte k rows and read back with the transposing LDS load.
 //     Both layouts are free of bank conflicts for the fragment reads.
 //   * weights are the MFMA A operand and activations the B operand: each lane ends
-//     with 4 consecutive output columns of one row (8-byte stores); for fc1 the w1
-//     and w3 blocks of the same columns land in the same wave, which applies
-//     silu(a)*b before rounding to bf16.
+//     with 4 consecutive output columns of one row; for fc1 the w1 and w3 blocks of
+//     the same columns land in the same wave, which applies silu(a)*b before rounding
+//     to bf16 (8-byte stores). fc2, the dgrad of fc1 (same mode) and the dgrad of fc2
+//     pass their rounded tile through the LDS stage of the last k step and store rows
+//     in 16-byte chunks.
 //   * persistent grid (one workgroup per CU). Each workgroup builds the list of
 //     256-row blocks per expert from offsets[] on the device (no host sync), walks
 //     each expert's (block, column) tiles with up to GROUP_M blocks per column sweep,
@@ -482,6 +484,66 @@ __device__ __forceinline__ void dgrad_epilogue(char* stage, const Tile& t, const
   }
 }
 
+// kFc2 epilogue through LDS, the same passes as the dgrad epilogue: the sums, rounded
+// to bf16, go into the LDS stage of the tile's last k-step, 128 rows x 256 columns per
+// pass, and come back by rows, so every store is a whole 16-byte chunk and 32 lanes
+// write 512 consecutive bytes of one row. Stored straight from the accumulator layout, a
+// wave instruction would touch 32 rows with 16 bytes each.
+template <bool HALF>
+__device__ __forceinline__ void fc2_epilogue(char* stage, const Tile& t, const Epi& ep,
+                                             const f32x16 (&acc)[HALF ? 2 : 4][2]) {
+  constexpr int WM = HALF ? 2 : 4;
+  constexpr int PASSES = HALF ? 1 : 2;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int arow0 = (wave & 1) * (HALF ? 64 : 128);
+  const int prow0 = (wave >> 1) * 64;
+  const int fr = lane & 31;
+  const int N = ep.N;
+  uint2 pk[WM][2][4];
+#pragma unroll
+  for (int mb = 0; mb < WM; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x16& a = acc[mb][nb];
+        pk[mb][nb][g] = uint2{pack_bf16x2(a[4 * g], a[4 * g + 1]),
+                              pack_bf16x2(a[4 * g + 2], a[4 * g + 3])};
+      }
+  const int c = threadIdx.x & 31;
+  const int n = t.n0 + 8 * c;
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) {
+    lds_barrier();   // the stage is free: MFMA reads (or the previous pass) are done
+    if (HALF || (wave & 1) == p) {
+#pragma unroll
+      for (int mb = 0; mb < WM; ++mb) {
+        const int rl = (HALF ? arow0 : 0) + mb * 32 + fr;   // row within the pass
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int u = (prow0 + nb * 32 + g * 8 + (lane >> 5) * 4) >> 2;
+            *reinterpret_cast<uint2*>(stage + rl * 512 + ((u ^ (rl & 31)) << 3)) = pk[mb][nb][g];
+          }
+      }
+    }
+    lds_barrier();
+    // 128 rows x 32 chunks of 8 columns; 16 rows per round of the 512 threads
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int rl = (threadIdx.x >> 5) + 16 * it;
+      const int r = p * 128 + rl;
+      if (r >= t.rows || n >= N) continue;
+      const int m = rl & 31;
+      uint4 d = *reinterpret_cast<const uint4*>(stage + rl * 512 + ((c ^ (m >> 1)) << 4));
+      if (m & 1) d = uint4{d.z, d.w, d.x, d.y};
+      *reinterpret_cast<uint4*>(ep.C + (size_t)(t.m0 + r) * N + n) = d;
+    }
+  }
+}
+
 // The end of a tile: the raw float32 sums of a split-K share (`part`, row-major
 // [BM][BP]) or the MODE epilogue. Lane l holds column m = l % 32 of every 32x32 block
 // and panel rows 8*g + 4*(l / 32) + i (i = 0..3) for g = 0..3.
@@ -514,6 +576,10 @@ __device__ __forceinline__ void finish_tile(char* smem, const Tile& t, const Epi
   }
   if (MODE == kDgrad) {
     dgrad_epilogue<HALF>(smem + ((stage0 + ke - kb - 1) & 1) * STAGE_BYTES, t, ep, acc);
+    return;
+  }
+  if (MODE == kFc2) {
+    fc2_epilogue<HALF>(smem + ((stage0 + ke - kb - 1) & 1) * STAGE_BYTES, t, ep, acc);
     return;
   }
 #pragma unroll
