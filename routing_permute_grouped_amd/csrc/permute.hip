@@ -7,13 +7,14 @@
 // Three launches:
 //   1. hist_kernel   per 256-token block, the slots of each expert (LDS atomics:
 //                    counts do not depend on their order) and the bad-index count.
-//   2. rank_kernel   every workgroup reads the small histogram table and derives
-//                    the counts, padded offsets and its own starting rank per expert
-//                    (earlier histogram blocks + earlier tokens of its own block),
-//                    so no single-workgroup scan is needed. Token workgroups (16
-//                    tokens each) rank their slots stably (ballot match inside a
-//                    wave) and write dst_row / src_row; the last workgroup writes
-//                    counts, offsets, tile_expert, the unused rows and the error flag.
+//   2. rank_kernel   one workgroup per histogram block reads the small histogram
+//                    table and derives the counts, padded offsets and its block's
+//                    starting rank per expert (the earlier blocks), so no
+//                    single-workgroup scan is needed; it ranks its slots stably
+//                    (per-wave counts prefix-summed over the waves, then a ballot
+//                    match inside each wave) and writes dst_row / src_row. The last
+//                    workgroup writes counts, offsets, tile_expert, the unused rows
+//                    and the error flag.
 //   3. copy_kernel   streams the rows: each token row is read once (16-byte chunks,
 //                    four in flight per thread) and written to its k rows; the pad
 //                    rows of every segment are zeroed by the same grid.
@@ -53,11 +54,9 @@ hipError_t permute_scratch(void** ptr) {
 namespace {
 
 constexpr int kMaxExperts = 1024;
-constexpr int kPlaceTokens = 16;
 constexpr int kThreads = 256;
 constexpr int kUnroll = 4;   // 16-byte chunks per thread in flight during the copy
 constexpr int kBatch = 8;    // index loads per thread in flight while counting
-static_assert(kHistTokens % kPlaceTokens == 0, "place blocks nest in histogram blocks");
 
 __global__ __launch_bounds__(kThreads) void hist_kernel(const int32_t* __restrict__ idx, int T,
                                                         int k, int E, int32_t* __restrict__ hist,
@@ -110,6 +109,15 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* wsum) {
 // MASKED: the masked layout (fixed slabs of `cap` rows, expert e from row e*cap; m_tile
 // unused, m_cap = E*cap): ranks at or past cap are dropped, counts are capped, offsets
 // and tile_expert are not written.
+//
+// Workgroup hb < nbh ranks the slots of histogram block hb (tokens [256 hb, 256 hb + 256)):
+// its starting rank per expert is the sum of the table rows before hb, so each
+// workgroup reads the nbh x E table once (nbh^2 E reads in all: 16 M at 65536 tokens
+// and 256 experts). Its four waves take contiguous quarters of the block's slots: each
+// counts its quarter per expert, the counts are prefix-summed over the waves, and each
+// wave then ranks its quarter 64 slots at a time (ballot match), so ranks follow slot
+// order. Workgroup nbh writes counts, offsets, tile_expert, the unused rows and the
+// error flag.
 template <bool MASKED>
 __global__ __launch_bounds__(kThreads) void rank_kernel(
     const int32_t* __restrict__ idx, int T, int k, int E, int m_tile, int cap, int64_t m_cap,
@@ -118,37 +126,41 @@ __global__ __launch_bounds__(kThreads) void rank_kernel(
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
     int32_t* __restrict__ tile_expert, int32_t* __restrict__ dev_err,
     int32_t* __restrict__ dst_row, int32_t* __restrict__ src_row) {
+  constexpr int kWaves = kThreads / kWave;
+  constexpr int kChunks = kHistTokens * kMaxTopK / kWaves / kWave;   // 64-slot chunks per wave
   __shared__ int off[kMaxExperts + 1];   // padded segment starts
   __shared__ int cnt[kMaxExperts];       // rows per expert
-  __shared__ int base[kMaxExperts];      // next free row per expert for this block
-  __shared__ int wsum[kThreads / kWave];
+  __shared__ int base[kMaxExperts];      // rank of this block's first slot per expert
+  __shared__ int wcnt[kWaves][kMaxExperts];   // per wave: its slots, then its next rank
+  __shared__ int wsum[kWaves];
   const int tid = threadIdx.x;
-  const int nbp = (T + kPlaceTokens - 1) / kPlaceTokens;
-  const int b = blockIdx.x;
-  const bool token_block = b < nbp;
-  const int t_begin = b * kPlaceTokens;
-  const int hb = token_block ? t_begin / kHistTokens : nbh;
+  const int lane = tid & (kWave - 1);
+  const int wv = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int hb = blockIdx.x;
+  const bool token_block = hb < nbh;
+  const int t_begin = hb * kHistTokens;
+  const int t_end = token_block ? min(T, t_begin + kHistTokens) : t_begin;
+  const int n = (t_end - t_begin) * k;   // slots of this block
+  const int64_t a0 = (int64_t)t_begin * k;
+  const int per_wave = (n + kWaves * kWave - 1) / (kWaves * kWave) * kWave;
+  const int w0 = min(n, wv * per_wave), w1 = min(n, w0 + per_wave);   // this wave's slots
 
-  // per-expert totals and this block's starting rank (earlier histogram blocks);
-  // integer LDS atomics, so the sums do not depend on their order
   for (int e = tid; e < E; e += kThreads) {
     cnt[e] = 0;
     base[e] = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) wcnt[w][e] = 0;
+  }
+  // this wave's expert indices, fetched once (their load overlaps the table's)
+  int own[kChunks];
+#pragma unroll
+  for (int i = 0; i < kChunks; ++i) {
+    const int a = w0 + i * kWave + lane;
+    own[i] = a < w1 ? idx[a0 + a] : -1;
   }
   __syncthreads();
-  // wave 0 fetches the expert indices of this workgroup's own slots now, so their load
-  // overlaps the table's (up to kPlaceTokens * kMaxTopK / kWave = 8 per lane)
-  const int t_end = token_block ? min(T, t_begin + kPlaceTokens) : t_begin;
-  const int n = (t_end - t_begin) * k;
-  const int64_t a0 = (int64_t)t_begin * k;
-  int own[kPlaceTokens * kMaxTopK / kWave];
-  if (tid < kWave) {
-#pragma unroll
-    for (int i = 0; i < kPlaceTokens * kMaxTopK / kWave; ++i) {
-      const int a = i * kWave + tid;
-      own[i] = a < n ? idx[a0 + a] : -1;
-    }
-  }
+  // per-expert totals and this block's starting rank (earlier histogram blocks);
+  // integer LDS atomics, so the sums do not depend on their order
   for (int i0 = tid; i0 < nbh * E; i0 += kThreads * kBatch) {
     int cv[kBatch];
 #pragma unroll
@@ -165,6 +177,10 @@ __global__ __launch_bounds__(kThreads) void rank_kernel(
       if (h < hb) atomicAdd(&base[e], cv[j]);
     }
   }
+  // this wave's slots per expert
+#pragma unroll
+  for (int i = 0; i < kChunks; ++i)
+    if (own[i] >= 0 && own[i] < E) atomicAdd(&wcnt[wv][own[i]], 1);
   __syncthreads();
   if (MASKED) {
     for (int e = tid; e <= E; e += kThreads) off[e] = e * cap;
@@ -186,6 +202,16 @@ __global__ __launch_bounds__(kThreads) void rank_kernel(
     }
     if (tid == kThreads - 1) off[E] = run;
   }
+  // each wave's starting rank per expert: the block's, plus the earlier waves' slots
+  for (int e = tid; e < E; e += kThreads) {
+    int run = base[e];
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const int c = wcnt[w][e];
+      wcnt[w][e] = run;
+      run += c;
+    }
+  }
   __syncthreads();
 
   if (!token_block && MASKED) {   // capped counts, unused slab rows, error flags
@@ -205,80 +231,61 @@ __global__ __launch_bounds__(kThreads) void rank_kernel(
     return;
   }
   if (!token_block) {   // metadata, unused rows, error flag
-    {
-      for (int i = tid; i < E; i += kThreads) counts[i] = cnt[i];
-      for (int i = tid; i <= E; i += kThreads) offsets[i] = off[i];
-      const int total = off[E];
-      const int64_t ntiles = m_cap / m_tile;
-      for (int64_t q = tid; q < ntiles; q += kThreads) {
-        const int64_t r = q * m_tile;
-        int owner = -1;
-        if (r < total) {
-          int lo = 0, hi = E;  // largest e with off[e] <= r
-          while (hi - lo > 1) {
-            const int mid = (lo + hi) >> 1;
-            if (off[mid] <= r) lo = mid; else hi = mid;
-          }
-          owner = lo;
+    for (int i = tid; i < E; i += kThreads) counts[i] = cnt[i];
+    for (int i = tid; i <= E; i += kThreads) offsets[i] = off[i];
+    const int total = off[E];
+    const int64_t ntiles = m_cap / m_tile;
+    for (int64_t q = tid; q < ntiles; q += kThreads) {
+      const int64_t r = q * m_tile;
+      int owner = -1;
+      if (r < total) {
+        int lo = 0, hi = E;  // largest e with off[e] <= r
+        while (hi - lo > 1) {
+          const int mid = (lo + hi) >> 1;
+          if (off[mid] <= r) lo = mid; else hi = mid;
         }
-        tile_expert[q] = owner;
+        owner = lo;
       }
-      for (int e = 0; e < E; ++e)   // pad rows of every segment
-        for (int r = off[e] + cnt[e] + tid; r < off[e + 1]; r += kThreads) src_row[r] = -1;
-      for (int64_t r = total + tid; r < m_cap; r += kThreads) src_row[r] = -1;
-      int anybad = 0;
-      for (int h = tid; h < nbh; h += kThreads) anybad |= bad[h] != 0;
-      anybad = __syncthreads_or(anybad);
-      if (tid == 0) *dev_err = anybad;
+      tile_expert[q] = owner;
     }
+    for (int e = 0; e < E; ++e)   // pad rows of every segment
+      for (int r = off[e] + cnt[e] + tid; r < off[e + 1]; r += kThreads) src_row[r] = -1;
+    for (int64_t r = total + tid; r < m_cap; r += kThreads) src_row[r] = -1;
+    int anybad = 0;
+    for (int h = tid; h < nbh; h += kThreads) anybad |= bad[h] != 0;
+    anybad = __syncthreads_or(anybad);
+    if (tid == 0) *dev_err = anybad;
     return;
   }
 
-  // slots of this histogram block that precede this workgroup's tokens (loads batched
-  // ahead of their atomics, as in hist_kernel)
-  const int64_t p1 = (int64_t)t_begin * k;
-  for (int64_t g = (int64_t)hb * kHistTokens * k + tid; g < p1; g += (int64_t)kThreads * kBatch) {
-    int ev[kBatch];
+  // rank this wave's slots in order, 64 at a time; wcnt[wv][e] is the wave's next rank
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+  const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
+  int* next = wcnt[wv];
 #pragma unroll
-    for (int i = 0; i < kBatch; ++i) {
-      const int64_t a = g + (int64_t)i * kThreads;
-      ev[i] = a < p1 ? idx[a] : -1;
+  for (int i = 0; i < kChunks; ++i) {
+    const int r0 = w0 + i * kWave;
+    if (r0 >= w1) break;
+    const int a = r0 + lane;
+    const int e = own[i];
+    const bool valid = a < w1 && e >= 0 && e < E;
+    uint64_t same = __ballot(valid);
+    for (int bit = 0; bit < nbits; ++bit) {
+      const uint64_t bal = __ballot(valid && ((e >> bit) & 1));
+      same &= ((e >> bit) & 1) ? bal : ~bal;
     }
-#pragma unroll
-    for (int i = 0; i < kBatch; ++i)
-      if (ev[i] >= 0 && ev[i] < E) atomicAdd(&base[ev[i]], 1);
-  }
-  __syncthreads();
-
-  if (tid < kWave) {
-    const int lane = tid;
-    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
-    const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
-#pragma unroll
-    for (int i = 0; i < kPlaceTokens * kMaxTopK / kWave; ++i) {
-      const int r0 = i * kWave;
-      if (r0 >= n) break;
-      const int a = r0 + lane;
-      const int e = own[i];
-      const bool valid = a < n && e >= 0 && e < E;
-      uint64_t same = __ballot(valid);
-      for (int bit = 0; bit < nbits; ++bit) {
-        const uint64_t bal = __ballot(valid && ((e >> bit) & 1));
-        same &= ((e >> bit) & 1) ? bal : ~bal;
-      }
-      int pos = -1;
-      if (valid) {
-        const int rank = base[e] + __popcll(same & lt);
-        pos = (MASKED && rank >= cap) ? -1 : off[e] + rank;   // masked: past the slab is dropped
-      }
-      if (pos >= m_cap) pos = -1;  // cannot happen with consistent counts; never write past m_cap
-      __builtin_amdgcn_wave_barrier();
-      if (valid && (same >> lane) == 1ull) base[e] = base[e] + __popcll(same);
-      __builtin_amdgcn_wave_barrier();
-      if (a < n) {
-        dst_row[a0 + a] = pos;
-        if (pos >= 0) src_row[pos] = (int32_t)(a0 + a);
-      }
+    int pos = -1;
+    if (valid) {
+      const int rank = next[e] + __popcll(same & lt);
+      pos = (MASKED && rank >= cap) ? -1 : off[e] + rank;   // masked: past the slab is dropped
+    }
+    if (pos >= m_cap) pos = -1;  // cannot happen with consistent counts; never write past m_cap
+    __builtin_amdgcn_wave_barrier();
+    if (valid && (same >> lane) == 1ull) next[e] = next[e] + __popcll(same);
+    __builtin_amdgcn_wave_barrier();
+    if (a < w1) {
+      dst_row[a0 + a] = pos;
+      if (pos >= 0) src_row[pos] = (int32_t)(a0 + a);
     }
   }
 }
@@ -374,8 +381,7 @@ hipError_t launch_permute(int dt, const void* x, const int32_t* topk_idx, int T,
   int32_t* hist = static_cast<int32_t*>(workspace);
   int32_t* bad = hist + (size_t)nbh * E;
   hipLaunchKernelGGL(hist_kernel, dim3(nbh), dim3(kThreads), 0, s, topk_idx, T, k, E, hist, bad);
-  const int nbp = (T + kPlaceTokens - 1) / kPlaceTokens;
-  hipLaunchKernelGGL(rank_kernel<false>, dim3(nbp + 1), dim3(kThreads), 0, s, topk_idx, T, k, E,
+  hipLaunchKernelGGL(rank_kernel<false>, dim3(nbh + 1), dim3(kThreads), 0, s, topk_idx, T, k, E,
                      m_tile, 0, m_cap, nbh, hist, bad, counts, offsets, tile_expert, dev_err,
                      dst_row, src_row);
   return launch_copy(dt, x, T, D, k, E, dst_row, counts, offsets, x_perm, s);
@@ -389,8 +395,7 @@ hipError_t launch_permute_masked(int dt, const void* x, const int32_t* topk_idx,
   int32_t* hist = static_cast<int32_t*>(workspace);
   int32_t* bad = hist + (size_t)nbh * E;
   hipLaunchKernelGGL(hist_kernel, dim3(nbh), dim3(kThreads), 0, s, topk_idx, T, k, E, hist, bad);
-  const int nbp = (T + kPlaceTokens - 1) / kPlaceTokens;
-  hipLaunchKernelGGL(rank_kernel<true>, dim3(nbp + 1), dim3(kThreads), 0, s, topk_idx, T, k, E, 0,
+  hipLaunchKernelGGL(rank_kernel<true>, dim3(nbh + 1), dim3(kThreads), 0, s, topk_idx, T, k, E, 0,
                      cap, (int64_t)E * cap, nbh, hist, bad, counts, nullptr, nullptr, dev_err,
                      dst_row, src_row);
   // no pad rows to zero in the masked layout (E = 0 skips that pass)
@@ -406,8 +411,7 @@ hipError_t launch_permute_mx(const void* xq, const void* xs, const int32_t* topk
   int32_t* hist = static_cast<int32_t*>(workspace);
   int32_t* bad = hist + (size_t)nbh * E;
   hipLaunchKernelGGL(hist_kernel, dim3(nbh), dim3(kThreads), 0, s, topk_idx, T, k, E, hist, bad);
-  const int nbp = (T + kPlaceTokens - 1) / kPlaceTokens;
-  hipLaunchKernelGGL(rank_kernel<false>, dim3(nbp + 1), dim3(kThreads), 0, s, topk_idx, T, k, E,
+  hipLaunchKernelGGL(rank_kernel<false>, dim3(nbh + 1), dim3(kThreads), 0, s, topk_idx, T, k, E,
                      m_tile, 0, m_cap, nbh, hist, bad, counts, offsets, tile_expert, dev_err,
                      dst_row, src_row);
   // the code rows are copied as raw bytes (D bytes = D/2 two-byte units, whole 16-byte

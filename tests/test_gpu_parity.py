@@ -341,3 +341,33 @@ def test_grouped_calls_skip_pad_rows_given_counts(split):
         assert np.all(g[counts == 0] == 0), name
         e = np.abs(g - ref).max() / np.abs(ref).max()
         assert e <= P.TOL["bf16"], (name, e)
+
+
+@pytest.mark.parametrize("T,E,k,mt", [(700, 64, 32, 128), (1537, 1024, 8, 64), (4097, 3, 2, 256),
+                                      (300, 7, 7, 128)])
+def test_permute_layout_extremes(T, E, k, mt):
+    # the permute alone against the oracle's layout: top-32 routing (the largest k), the
+    # largest expert count, several 256-token histogram blocks with a ragged last one,
+    # and -1 slots; every map bit-exact, x_perm exact on token rows and zero on pad rows
+    # (rows past offsets[E] are not the permute's to write)
+    P.log(f"[parity] permute layout T={T} E={E} k={k} m_tile={mt}")
+    rng = np.random.default_rng(T + E + k)
+    idx = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+    idx[rng.random((T, k)) < 0.05] = -1
+    x = W.f32_to_bf16_bits(rng.standard_normal((T, 64)).astype(np.float32))
+    lay = orc.dispatch_layout(idx, E, mt)
+    g = rpg.moe_permute(P.to_dev(x), P.to_dev(idx), E, mt)
+    torch.cuda.synchronize()
+    for key in ("counts", "offsets", "dst_row", "src_row", "tile_expert"):
+        np.testing.assert_array_equal(P.to_host(g[key]), lay[key], err_msg=key)
+    assert int(P.to_host(g["dev_err"])[0]) == 0
+    used = int(lay["offsets"][-1])
+    np.testing.assert_array_equal(P.to_host(g["x_perm"])[:used], orc.permute(x, lay)[:used])
+    # the masked layout on the same routing, with slabs small enough to drop slots
+    cap = max(16, int(np.bincount(idx[idx >= 0], minlength=E).mean() * 0.8) // 16 * 16)
+    ml = orc.masked_layout(idx, E, cap)
+    gm = rpg.moe_permute_masked(P.to_dev(x), P.to_dev(idx), E, cap)
+    torch.cuda.synchronize()
+    for key in ("counts", "dst_row", "src_row"):
+        np.testing.assert_array_equal(P.to_host(gm[key]), ml[key], err_msg="masked " + key)
+    assert int(P.to_host(gm["dev_err"])[0]) == (2 if ml["dropped"] else 0)
