@@ -338,9 +338,9 @@ def run_contiguous(args, cfg, d: dict, headline: bool) -> dict:
         shared_gemm(side, gws_side)
         ev_sh.record(side)
 
-    def step(ev=None):
+    def step(ev=None, ends_only=False):
         def mark(i):
-            if ev is not None:
+            if ev is not None and (not ends_only or i in (0, len(marks))):
                 ev[i].record(stream)
         mark(0)
         if overlap and args.shared_overlap == "start":
@@ -380,20 +380,33 @@ def run_contiguous(args, cfg, d: dict, headline: bool) -> dict:
     if int(buf["dev_err"].item()) != 0:
         raise RuntimeError("permute reported expert indices outside [-1, E)")
 
-    events = [[HipEvent() for _ in range(len(marks) + 1)]
-              for _ in range(args.steps)]
+    # the K timed steps: one event at each end of a step, nothing recorded inside it
+    ends = [[HipEvent() for _ in range(len(marks) + 1)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
         if flush is not None:
             flush.fill_(float(s))          # outside the step's event brackets
-        step(events[s])
+        step(ends[s], ends_only=True)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    step_us = [ends[s][0].elapsed_time(ends[s][-1]) * 1e3 for s in range(args.steps)]
+    # K more steps with an event between every two stages: the per-stage times (their
+    # marked_step agrees with the timed steps within the run-to-run spread)
+    events = [[HipEvent() for _ in range(len(marks) + 1)]
+              for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for s in range(args.steps):
+        if flush is not None:
+            flush.fill_(float(s))
+        step(events[s])
+    torch.cuda.synchronize()
 
     per = {m: [events[s][i].elapsed_time(events[s][i + 1]) * 1e3 for s in range(args.steps)]
            for i, m in enumerate(marks)}
-    per["step"] = [events[s][0].elapsed_time(events[s][-1]) * 1e3 for s in range(args.steps)]
+    per["marked_step"] = [events[s][0].elapsed_time(events[s][-1]) * 1e3
+                          for s in range(args.steps)]
+    per["step"] = step_us
     med = {m: statistics.median(v) for m, v in per.items()}
     avg = {m: statistics.fmean(v) for m, v in per.items()}
 
@@ -453,7 +466,11 @@ def run_contiguous(args, cfg, d: dict, headline: bool) -> dict:
         "permute_GBps": perm_gbps, "permute_frac_hbm": perm_gbps / PEAK_HBM_GBPS,
         "combine_GBps": comb_gbps, "combine_frac_hbm": comb_gbps / PEAK_HBM_GBPS,
         "stage_us_median": med, "stage_us_mean": avg, "stage_us_spread": spread,
-        "timing": {"value_from": "sum of per-step HIP-event durations on the compute stream",
+        "timing": {"value_from": "mean of the K steps' durations, each between two HIP events "
+                                 "on the compute stream at the step's ends (nothing recorded "
+                                 "inside the step)",
+                   "stages_from": "K further steps with an event between every two stages "
+                                  "(stage_us_*; marked_step is their whole-step mean)",
                    "events": "hipEventCreateWithFlags(hipEventDisableSystemFence): timing only, "
                              "no cache writeback or invalidate at a stage boundary",
                    "cache_flush_MiB_between_steps": args.flush_mib,
@@ -519,9 +536,9 @@ def bench_masked(args, cfg, d, inp) -> dict:
         shared_gemm(side, gws_side)
         ev_sh.record(side)
 
-    def step(ev=None, contiguous=False):
+    def step(ev=None, contiguous=False, ends_only=False):
         def mark(i):
-            if ev is not None:
+            if ev is not None and (not ends_only or i in (0, len(marks))):
                 ev[i].record(stream)
         mark(0)
         if overlap and args.shared_overlap == "start":
@@ -568,6 +585,12 @@ def bench_masked(args, cfg, d, inp) -> dict:
         for _ in range(args.warmup):
             step(contiguous=contiguous)
         torch.cuda.synchronize()
+        # the K timed steps with events at their ends only, then K with stage markers
+        ends = [[HipEvent() for _ in range(len(marks) + 1)] for _ in range(args.steps)]
+        for s_ in range(args.steps):
+            if flush is not None:
+                flush.fill_(float(s_))
+            step(ends[s_], contiguous, ends_only=True)
         events = [[HipEvent() for _ in range(len(marks) + 1)]
                   for _ in range(args.steps)]
         for s_ in range(args.steps):
@@ -577,7 +600,9 @@ def bench_masked(args, cfg, d, inp) -> dict:
         torch.cuda.synchronize()
         per = {m: [events[s_][i].elapsed_time(events[s_][i + 1]) * 1e3
                    for s_ in range(args.steps)] for i, m in enumerate(marks)}
-        per["step"] = [events[s_][0].elapsed_time(events[s_][-1]) * 1e3
+        per["marked_step"] = [events[s_][0].elapsed_time(events[s_][-1]) * 1e3
+                              for s_ in range(args.steps)]
+        per["step"] = [ends[s_][0].elapsed_time(ends[s_][-1]) * 1e3
                        for s_ in range(args.steps)]
         return ({m: statistics.fmean(v) for m, v in per.items()},
                 {m: statistics.median(v) for m, v in per.items()})
@@ -617,6 +642,10 @@ def bench_masked(args, cfg, d, inp) -> dict:
                              "(written and read) and y"},
         "grouped_gemm_tflops": flop / (avg["gemm"] * 1e-6) / 1e12,
         "stage_us_mean": avg, "stage_us_median": med,
+        "timing": {"value_from": "mean of the K steps' durations between HIP events at the "
+                                 "step's ends (nothing recorded inside the step)",
+                   "stages_from": "K further steps with an event between every two stages",
+                   "cache_flush_MiB_between_steps": args.flush_mib},
         "contiguous_layout": {"m_tile": mt, "stage_us_mean": cavg,
                               "ms_per_step": cavg["step"] * 1e-3},
         "assignments": n_valid, "active_experts": active,
