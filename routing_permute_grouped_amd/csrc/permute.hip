@@ -15,9 +15,10 @@
 //                    match inside each wave) and writes dst_row / src_row. The last
 //                    workgroup writes counts, offsets, tile_expert, the unused rows
 //                    and the error flag.
-//   3. copy_kernel   streams the rows: each token row is read once (16-byte chunks,
-//                    four in flight per thread) and written to its k rows; the pad
-//                    rows of every segment are zeroed by the same grid.
+//   3. copy_kernel   streams the rows: each token row is read once (16-byte chunks of
+//                    four tokens in flight per thread) and written to its k rows; the
+//                    pad rows of every segment are zeroed by the same grid, a row per
+//                    wave.
 #include <algorithm>
 #include <mutex>
 
@@ -55,8 +56,8 @@ namespace {
 
 constexpr int kMaxExperts = 1024;
 constexpr int kThreads = 256;
-constexpr int kUnroll = 4;   // 16-byte chunks per thread in flight during the copy
 constexpr int kBatch = 8;    // index loads per thread in flight while counting
+constexpr int kCopyTokens = 4;   // tokens whose row chunks a copy thread reads together
 
 __global__ __launch_bounds__(kThreads) void hist_kernel(const int32_t* __restrict__ idx, int T,
                                                         int k, int E, int32_t* __restrict__ hist,
@@ -290,43 +291,84 @@ __global__ __launch_bounds__(kThreads) void rank_kernel(
   }
 }
 
-// Row copy: grid-stride over the T x (D/V) chunks of x (each read once) followed by
-// the pad rows of every segment (zeroed). dst_row, offsets and counts come from
-// rank_kernel.
+// Row copy. A work item is a group of kCopyTokens consecutive tokens x a slab of 256
+// 16-byte chunks of their rows; workgroups take items in turn. Thread i reads chunk i of
+// the slab for every token of the group (kCopyTokens reads in flight) and writes it to
+// each of the token's destination rows. Then the pad rows of every segment, [offsets[e] + counts[e],
+// offsets[e+1]), are zeroed one row per wave: the rows are numbered across experts by a
+// prefix sum in LDS and each wave finds its expert by binary search. dst_row, offsets and
+// counts come from rank_kernel; E = 0 skips the pad rows (the masked layout has none).
 template <typename TIn>
 __global__ __launch_bounds__(kThreads) void copy_kernel(
     const TIn* __restrict__ x, int T, int D, int k, int E, const int32_t* __restrict__ dst_row,
     const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
     TIn* __restrict__ x_perm) {
   constexpr int V = Chunk<TIn>::V;
+  __shared__ int ds[kCopyTokens * kMaxTopK];
+  __shared__ int pstart[kMaxExperts];       // first pad row of each expert
+  __shared__ int ppre[kMaxExperts + 1];     // pad rows of the experts before e
+  __shared__ int wsum[kThreads / kWave];
   const int nck = D / V;
-  const int64_t ncopy = (int64_t)T * nck;
-  const int64_t stride = (int64_t)gridDim.x * kThreads;
-  for (int64_t g0 = (int64_t)blockIdx.x * kThreads + threadIdx.x; g0 < ncopy; g0 += stride * kUnroll) {
-    u32x4 v[kUnroll];
+  const int nslab = (nck + kThreads - 1) / kThreads;   // 256-chunk column slabs of a row
+  const int64_t items = (int64_t)((T + kCopyTokens - 1) / kCopyTokens) * nslab;
+  for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
+    const int g = (int)(it / nslab);
+    const int t0 = g * kCopyTokens;
+    const int nt = min(kCopyTokens, T - t0);
+    __syncthreads();   // the previous item's destinations are no longer read
+    for (int i = threadIdx.x; i < nt * k; i += kThreads) ds[i] = dst_row[(int64_t)t0 * k + i];
+    __syncthreads();
+    const int c = (int)(it - (int64_t)g * nslab) * kThreads + threadIdx.x;
+    if (c < nck) {
+      u32x4 v[kCopyTokens];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int64_t g = min(g0 + u * stride, ncopy - 1);
-      v[u] = ld16_nt(x + (g / nck) * D + (g % nck) * V);
-    }
+      for (int i = 0; i < kCopyTokens; ++i)
+        if (i < nt) v[i] = ld16_nt(x + (int64_t)(t0 + i) * D + (int64_t)c * V);
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int64_t g = g0 + u * stride;
-      if (g >= ncopy) continue;
-      const int64_t t = g / nck, c = g % nck;
-      for (int j = 0; j < k; ++j) {
-        const int d = dst_row[t * k + j];
-        if (d >= 0) st16(x_perm + (int64_t)d * D + c * V, v[u]);
+      for (int i = 0; i < kCopyTokens; ++i) {
+        if (i >= nt) continue;
+        for (int j = 0; j < k; ++j) {
+          const int d = ds[i * k + j];
+          if (d >= 0) st16(x_perm + (int64_t)d * D + (int64_t)c * V, v[i]);
+        }
       }
     }
   }
-  // pad rows: [offsets[e] + counts[e], offsets[e+1]) for every expert
+  if (E == 0) return;
+  // pad rows, numbered across experts
+  int pads[4] = {0, 0, 0, 0};
+  int local = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = threadIdx.x * 4 + i;
+    if (e < E) {
+      const int r0 = offsets[e] + counts[e];
+      pstart[e] = r0;
+      pads[i] = max(0, offsets[e + 1] - r0);
+    }
+    local += pads[i];
+  }
+  int run = block_exclusive_scan(local, wsum);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = threadIdx.x * 4 + i;
+    if (e < E) ppre[e] = run;
+    run += pads[i];
+  }
+  if (threadIdx.x == kThreads - 1) ppre[E] = run;
+  __syncthreads();
+  const int npad = ppre[E];
+  const int lane = threadIdx.x & (kWave - 1);
   const u32x4 z = {0u, 0u, 0u, 0u};
-  for (int e = 0; e < E; ++e) {
-    const int r0 = offsets[e] + counts[e], r1 = offsets[e + 1];
-    const int64_t n = (int64_t)(r1 - r0) * nck;
-    for (int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x; g < n; g += stride)
-      st16(x_perm + (r0 + g / nck) * D + (g % nck) * V, z);
+  const int nwaves = gridDim.x * (kThreads / kWave);
+  for (int q = blockIdx.x * (kThreads / kWave) + threadIdx.x / kWave; q < npad; q += nwaves) {
+    int lo = 0, hi = E;   // largest e with ppre[e] <= q
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (ppre[mid] <= q) lo = mid; else hi = mid;
+    }
+    TIn* row = x_perm + (int64_t)(pstart[lo] + (q - ppre[lo])) * D;
+    for (int c = lane; c < nck; c += kWave) st16(row + (int64_t)c * V, z);
   }
 }
 
@@ -351,9 +393,10 @@ __global__ __launch_bounds__(kThreads) void scale_ksteps_kernel(
 hipError_t launch_copy(int dt, const void* x, int T, int D, int k, int E,
                               const int32_t* dst_row, const int32_t* counts,
                               const int32_t* offsets, void* x_perm, hipStream_t s) {
-  const int V = dt == kF32 ? 4 : 8;
-  const int64_t chunks = (int64_t)T * (D / V);
-  const int grid = (int)std::min<int64_t>(8 * cu_count(), (chunks + kThreads * kUnroll - 1) / (kThreads * kUnroll));
+  // a workgroup per work item, at most 8 per CU, and at least one per CU for the pad rows
+  const int64_t items = (int64_t)((T + kCopyTokens - 1) / kCopyTokens) *
+                        ((D / (dt == kF32 ? 4 : 8) + kThreads - 1) / kThreads);
+  const int grid = (int)std::min<int64_t>(8 * cu_count(), std::max<int64_t>(items, cu_count()));
   if (dt == kF32)
     hipLaunchKernelGGL(copy_kernel<float>, dim3(grid), dim3(kThreads), 0, s,
                        static_cast<const float*>(x), T, D, k, E, dst_row, counts, offsets,
