@@ -44,8 +44,8 @@
  *   returns an error without touching the GPU. Device data that is wrong
  *   (an expert index outside [-1, E)) never causes an out-of-bounds access:
  *   the slot is skipped and moe_permute reports it through *dev_err.
- * - Sizes: T >= 1; D, F multiples of 64; E in [1, 64] for moe_route and
- *   [1, 1024] elsewhere; k in [1, min(E, 32)]; m_tile in {16,32,64,128,256}.
+ * - Sizes: T >= 1; D, F multiples of 64; E in [1, 1024]; k in [1, min(E, 32)];
+ *   m_tile in {16,32,64,128,256}.
  */
 #ifndef MOE_MI355X_H
 #define MOE_MI355X_H
@@ -90,7 +90,7 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype_t;
  * Score: softmax over all E logits. Selection: the k largest logits, best
  * first, ties to the lower expert index. topk_w[t,j] = softmax probability of
  * topk_idx[t,j] (renorm = 1 divides the k weights by their sum).
- * Errors: MOE_EINVAL, MOE_ESHAPE (E > 64 or k > E), MOE_EHIP.
+ * Errors: MOE_EINVAL, MOE_ESHAPE (E > 1024 or k > E), MOE_EHIP.
  */
 moe_status_t moe_route(moe_dtype_t dt, const void* x, const void* wg, const float* bias,
                        int T, int D, int E, int k, int renorm,
@@ -210,7 +210,9 @@ moe_status_t moe_grouped_swiglu_masked(moe_dtype_t dt, const void* x_masked,
  * and still write exact zeros to their h and y_perm rows; the decode-sized path
  * below reads them (they hold zeros as moe_permute leaves them). NULL: every row of
  * a segment is computed. counts outside [0, offsets[e+1] - offsets[e]] is clamped.
- * bf16 needs m_tile in {128, 256}; float32 accepts every m_tile. D*F < 2^31.
+ * Every m_tile is accepted (the bf16 kernel cuts each segment into 256-row tiles
+ * from its bounds and a shorter last tile; m_tile only sets the alignment the
+ * segments come with). D*F < 2^31.
  * offsets that break this contract (negative, decreasing, past m_cap) give
  * unspecified values in h and y_perm but no access outside rows [0, m_cap).
  *

@@ -28,7 +28,6 @@ int cu_count() {
 
 namespace {
 
-constexpr int kMaxExpertsRoute = 64;
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxK = moe::kMaxTopK;
 constexpr int kMaxDim = 1 << 16;
@@ -85,7 +84,7 @@ moe_status_t moe_route(moe_dtype_t dt, const void* x, const void* wg, const floa
     return MOE_EINVAL;
   if ((bias && !aligned4(bias)) || (logits && !aligned4(logits))) return MOE_EINVAL;
   if (renorm != 0 && renorm != 1) return MOE_EINVAL;
-  if (!tk_ok(T, k) || !dim_ok(D) || E < 1 || E > kMaxExpertsRoute || k < 1 || k > E || k > kMaxK)
+  if (!tk_ok(T, k) || !dim_ok(D) || E < 1 || E > kMaxExperts || k < 1 || k > E || k > kMaxK)
     return MOE_ESHAPE;
   return hip_status(moe::launch_route(dt, x, wg, bias, T, D, E, k, renorm, topk_idx, topk_w,
                                       logits, static_cast<hipStream_t>(stream)));
@@ -158,7 +157,6 @@ static moe_status_t grouped(int phases, moe_dtype_t dt, const void* x_perm,
   if (E < 1 || E > kMaxExperts || !dim_ok(D) || !dim_ok(F) || !mtile_ok(m_tile)) return MOE_ESHAPE;
   if ((int64_t)D * F >= ((int64_t)1 << 31)) return MOE_ESHAPE;  // one expert's matrix is int32-indexed
   if (m_cap < 1 || m_cap % m_tile != 0 || m_cap > INT32_MAX) return MOE_ECAPACITY;
-  if (dt == MOE_BF16 && m_tile != 128 && m_tile != 256) return MOE_EUNSUPPORTED;
   return hip_status(moe::launch_grouped_swiglu(dt, phases, x_perm, offsets, counts, 0,
                                                tile_expert, E, D, F, m_tile, m_cap, w1, w3, w2, h,
                                                ab, y_perm, ws_bytes ? workspace : nullptr,
@@ -293,7 +291,6 @@ static moe_status_t dgrad_common(moe_dtype_t dt, const void* a, const int32_t* o
   if (E < 1 || E > kMaxExperts || !dim_ok(D) || !dim_ok(F) || !mtile_ok(m_tile)) return MOE_ESHAPE;
   if ((int64_t)D * F >= ((int64_t)1 << 31)) return MOE_ESHAPE;
   if (m_cap < 1 || m_cap % m_tile != 0 || m_cap > INT32_MAX) return MOE_ECAPACITY;
-  if (dt == MOE_BF16 && m_tile != 128 && m_tile != 256) return MOE_EUNSUPPORTED;
   return MOE_OK;
 }
 

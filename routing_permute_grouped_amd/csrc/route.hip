@@ -13,7 +13,9 @@
 // over lane distances 32, 16, 8, 4, 2, 1: recursive halving while a lane holds more
 // than one pair, then plain butterfly steps. Each pair's partials meet in exactly the
 // butterfly's order, so every logit is the same float32 value the fixed order defines,
-// and the top-k choice is reproducible bit for bit.
+// and the top-k choice is reproducible bit for bit. In the softmax and top-k each lane
+// holds the logits of experts lane, lane + 64, ... (up to 16 of them: 1024 experts);
+// each top-k round takes every lane's best available expert, then the wave's.
 #include <math.h>
 
 #include "common.hpp"
@@ -59,7 +61,8 @@ __device__ __forceinline__ float reduce_pairs(float* v, int lane) {
   }
 }
 
-template <typename TIn, int TW, int EC, bool SHARED>
+// NE: logits per lane in the softmax and top-k (experts e = lane + 64 i, i < NE).
+template <typename TIn, int TW, int EC, bool SHARED, int NE>
 __global__ __launch_bounds__(kWave * kWavesPerBlock) void route_kernel(
     const TIn* __restrict__ x, const TIn* __restrict__ wg, const float* __restrict__ bias, int T,
     int D, int E, int k, int renorm, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
@@ -69,7 +72,7 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock) void route_kernel(
   constexpr int LOGP = P == 16 ? 4 : (P == 32 ? 5 : 6);
   static_assert(P == 16 || P == 32 || P == 64, "pairs per pass");
   constexpr int NL = SHARED ? 1 : kWavesPerBlock;   // logit tables per block
-  __shared__ float lg[NL][TW][kWave];
+  __shared__ float lg[NL][TW][NE * kWave];
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   // SHARED: the block's waves share tokens t0 .. t0+TW-1 and split the passes
@@ -148,34 +151,59 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock) void route_kernel(
   for (int t = SHARED ? wave : 0; t < TW; t += SHARED ? kWavesPerBlock : 1) {
     const int tok = t0 + t;
     if (tok >= T) break;
-    const bool have = lane < E;
-    const float l = have ? lg[tab][t][lane] : -INFINITY;
-    if (logits_out && have) logits_out[(size_t)tok * E + lane] = l;
-    float mx = l;
+    float l[NE];
+#pragma unroll
+    for (int i = 0; i < NE; ++i) {
+      const int e = lane + kWave * i;
+      l[i] = e < E ? lg[tab][t][e] : -INFINITY;
+      if (logits_out && e < E) logits_out[(size_t)tok * E + e] = l[i];
+    }
+    float mx = l[0];
+#pragma unroll
+    for (int i = 1; i < NE; ++i) mx = fmaxf(mx, l[i]);
 #pragma unroll
     for (int m = kWave / 2; m >= 1; m >>= 1) mx = fmaxf(mx, __shfl_xor(mx, m));
-    const float ex = have ? expf(l - mx) : 0.0f;
-    float sum = ex;
+    float ex[NE];
+    float sum = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NE; ++i) {
+      ex[i] = lane + kWave * i < E ? expf(l[i] - mx) : 0.0f;
+      sum += ex[i];
+    }
 #pragma unroll
     for (int m = kWave / 2; m >= 1; m >>= 1) sum += __shfl_xor(sum, m);
 
-    bool avail = have;
+    uint32_t avail = 0;   // bit i: expert lane + 64 i is still available
+#pragma unroll
+    for (int i = 0; i < NE; ++i)
+      if (lane + kWave * i < E) avail |= 1u << i;
     int my_idx = 0;
     float my_w = 0.0f, wtot = 0.0f;
     for (int j = 0; j < k; ++j) {
-      float key = avail ? l : -INFINITY;
-      int id = avail ? lane : 0x7fffffff;
+      // this lane's best available expert (in increasing index, so a tie keeps the lower)
+      float key = -INFINITY, xv = 0.0f;
+      int id = 0x7fffffff;
+#pragma unroll
+      for (int i = 0; i < NE; ++i)
+        if (((avail >> i) & 1u) && (id == 0x7fffffff || l[i] > key)) {
+          key = l[i];
+          id = lane + kWave * i;
+          xv = ex[i];
+        }
+      // then the wave's: the larger logit, ties to the lower index
 #pragma unroll
       for (int m = kWave / 2; m >= 1; m >>= 1) {
         const float ok = __shfl_xor(key, m);
         const int oi = __shfl_xor(id, m);
+        const float ox = __shfl_xor(xv, m);
         if (ok > key || (ok == key && oi < id)) {
           key = ok;
           id = oi;
+          xv = ox;
         }
       }
-      if (lane == id) avail = false;
-      const float wj = __shfl(ex, id) / sum;
+      if (id % kWave == lane) avail &= ~(1u << (id / kWave));
+      const float wj = xv / sum;
       wtot += wj;
       if (lane == j) {
         my_idx = id;
@@ -196,13 +224,20 @@ void launch_typed(const TIn* x, const TIn* wg, const float* bias, int T, int D, 
   if (E <= 8) {
     constexpr int TW = 2;
     const dim3 grid((T + TW * kWavesPerBlock - 1) / (TW * kWavesPerBlock));
-    hipLaunchKernelGGL((route_kernel<TIn, TW, 8, false>), grid, block, 0, s, x, wg, bias, T, D,
-                       E, k, renorm, topk_idx, topk_w, logits);
+    hipLaunchKernelGGL((route_kernel<TIn, TW, 8, false, 1>), grid, block, 0, s, x, wg, bias, T,
+                       D, E, k, renorm, topk_idx, topk_w, logits);
   } else {
     constexpr int TW = 8;
     const dim3 grid((T + TW - 1) / TW);
-    hipLaunchKernelGGL((route_kernel<TIn, TW, 8, true>), grid, block, 0, s, x, wg, bias, T, D, E,
-                       k, renorm, topk_idx, topk_w, logits);
+    if (E <= kWave)
+      hipLaunchKernelGGL((route_kernel<TIn, TW, 8, true, 1>), grid, block, 0, s, x, wg, bias, T,
+                         D, E, k, renorm, topk_idx, topk_w, logits);
+    else if (E <= 4 * kWave)
+      hipLaunchKernelGGL((route_kernel<TIn, TW, 8, true, 4>), grid, block, 0, s, x, wg, bias, T,
+                         D, E, k, renorm, topk_idx, topk_w, logits);
+    else
+      hipLaunchKernelGGL((route_kernel<TIn, TW, 8, true, 16>), grid, block, 0, s, x, wg, bias, T,
+                         D, E, k, renorm, topk_idx, topk_w, logits);
   }
 }
 

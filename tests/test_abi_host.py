@@ -73,7 +73,7 @@ def route(dt=0, x=FAKE, wg=FAKE, bias=None, T=16, D=128, E=8, k=2, renorm=0, idx
     (dict(dt=2), MOE_EINVAL), (dict(x=None), MOE_EINVAL), (dict(x=FAKE + 8), MOE_EINVAL),
     (dict(idx=None), MOE_EINVAL), (dict(bias=FAKE + 2), MOE_EINVAL), (dict(renorm=2), MOE_EINVAL),
     (dict(T=0), MOE_ESHAPE), (dict(D=100), MOE_ESHAPE), (dict(D=0), MOE_ESHAPE),
-    (dict(E=65), MOE_ESHAPE), (dict(E=0), MOE_ESHAPE), (dict(k=0), MOE_ESHAPE),
+    (dict(E=1025), MOE_ESHAPE), (dict(E=0), MOE_ESHAPE), (dict(k=0), MOE_ESHAPE),
     (dict(k=9), MOE_ESHAPE), (dict(E=64, k=33), MOE_ESHAPE),
 ])
 def test_route_validation(kw, code):
@@ -110,8 +110,8 @@ def grouped(dt=1, xp=FAKE, E=8, D=128, F=256, mt=128, m_cap=1024, w1=FAKE, h=FAK
     (dict(dt=5), MOE_EINVAL), (dict(w1=None), MOE_EINVAL), (dict(h=FAKE + 8), MOE_EINVAL),
     (dict(E=0), MOE_ESHAPE), (dict(F=100), MOE_ESHAPE), (dict(D=32), MOE_ESHAPE),
     (dict(mt=7), MOE_ESHAPE), (dict(m_cap=0), MOE_ECAPACITY), (dict(m_cap=1000), MOE_ECAPACITY),
-    (dict(mt=64, m_cap=1024), MOE_EUNSUPPORTED), (dict(D=65536, F=32768), MOE_ESHAPE),
-    (dict(mt=16, m_cap=1024), MOE_EUNSUPPORTED), (dict(ws=FAKE + 8, ws_bytes=1 << 20), MOE_EINVAL),
+    (dict(D=65536, F=32768), MOE_ESHAPE), (dict(mt=64, m_cap=1000), MOE_ECAPACITY),
+    (dict(mt=16, m_cap=1016), MOE_ECAPACITY), (dict(ws=FAKE + 8, ws_bytes=1 << 20), MOE_EINVAL),
     (dict(dt=7, ws=FAKE, ws_bytes=1 << 20), MOE_EINVAL), (dict(counts=FAKE + 2), MOE_EINVAL),
 ])
 def test_grouped_validation(kw, code):
@@ -129,8 +129,8 @@ def test_split_grouped_calls_validate():
                                       FAKE, FAKE + 2, None, 0, None) == MOE_EINVAL
     assert lib.moe_grouped_fc2(1, FAKE, FAKE, None, FAKE, 8, 128, 256, 128, 1000, FAKE, FAKE,
                                None, 0, None) == MOE_ECAPACITY
-    assert lib.moe_grouped_fc2(1, FAKE, FAKE, None, FAKE, 8, 128, 256, 64, 1024, FAKE, FAKE,
-                               FAKE, 1 << 20, None) == MOE_EUNSUPPORTED
+    assert lib.moe_grouped_fc2(1, FAKE, FAKE, None, FAKE, 8, 128, 256, 64, 1000, FAKE, FAKE,
+                               FAKE, 1 << 20, None) == MOE_ECAPACITY
 
 
 def test_grouped_workspace_size_is_whole_slots():
@@ -184,7 +184,7 @@ def dgrad(dt=1, dy=FAKE, E=8, D=128, F=256, mt=128, m_cap=1024, w2=FAKE, ab=FAKE
     (dict(ab=None), MOE_EINVAL), (dict(dab=None), MOE_EINVAL), (dict(dh=FAKE + 8), MOE_EINVAL),
     (dict(ws=FAKE + 4, ws_bytes=1 << 20), MOE_EINVAL), (dict(E=0), MOE_ESHAPE),
     (dict(F=200), MOE_ESHAPE), (dict(D=65536, F=32768), MOE_ESHAPE),
-    (dict(m_cap=1000), MOE_ECAPACITY), (dict(mt=64), MOE_EUNSUPPORTED),
+    (dict(m_cap=1000), MOE_ECAPACITY), (dict(mt=32, m_cap=1000), MOE_ECAPACITY),
 ])
 def test_dgrad_validation(kw, code):
     assert dgrad(**kw) == code
@@ -201,7 +201,7 @@ def dgrad_fc1(dt=1, dab=FAKE, E=8, D=128, F=256, mt=128, m_cap=1024, w1=FAKE, w3
     (dict(w3=FAKE + 2), MOE_EINVAL), (dict(dx=FAKE + 4), MOE_EINVAL),
     (dict(ws=FAKE + 8, ws_bytes=1 << 20), MOE_EINVAL), (dict(E=1025), MOE_ESHAPE),
     (dict(D=100), MOE_ESHAPE), (dict(mt=100), MOE_ESHAPE), (dict(m_cap=0), MOE_ECAPACITY),
-    (dict(mt=32, m_cap=1024), MOE_EUNSUPPORTED),
+    (dict(mt=16, m_cap=1000), MOE_ECAPACITY),
 ])
 def test_dgrad_fc1_validation(kw, code):
     assert dgrad_fc1(**kw) == code

@@ -178,6 +178,8 @@ BWD = {
     "fine64_shared2": W.shrink(W.preset("fine64_shared2_bf16"), T=389, D=256, F=320, F_shared=192),
     "skew32_zipf": W.shrink(W.preset("skew32_zipf_bf16"), T=1024, D=512, F=256),
     "etp_shard32": W.shrink(W.preset("etp_shard32_bf16"), D=1024, F=512, poisson_mean=40.0),
+    "bf16_mt64": W.shrink(W.preset("dense8_bf16"), T=900, D=512, F=768, m_tile=64),
+    "bf16_mt16": W.shrink(W.preset("skew32_zipf_bf16"), T=500, D=256, F=320, m_tile=16),
 }
 
 

@@ -29,6 +29,20 @@ SMALL = {
     "etp_shard32": W.shrink(W.preset("etp_shard32_bf16"), D=1024, F=512, poisson_mean=40.0),
     "f32_mt64": W.shrink(W.preset("tiny_f32"), T=300, D=192, F=320, E=6, k=3, m_tile=64),
     "f32_mt256": W.shrink(W.preset("tiny_f32"), T=77, D=64, F=128, E=5, k=2, m_tile=256),
+    # bf16 at the smaller M tiles: segments start at multiples of 16, 32 or 64 rows and
+    # end inside the kernel's 256-row tiles (and its 128-row half tiles)
+    "bf16_mt16": W.shrink(W.preset("fine64_shared2_bf16"), T=300, D=256, F=320, F_shared=192,
+                          m_tile=16),
+    "bf16_mt32": W.shrink(W.preset("skew32_zipf_bf16"), T=700, D=256, F=384, m_tile=32),
+    "bf16_mt64": W.shrink(W.preset("dense8_bf16"), T=900, D=512, F=768, m_tile=64),
+    # the router past 64 experts: 256 experts top-8 (each lane holds 4 logits in the
+    # softmax and top-k) and 1024 experts top-4 (16 per lane), a Zipf bias on the latter
+    "route256_top8": W.MoEConfig("route256_top8", T=384, D=512, F=128, E=256, k=8, m_tile=16,
+                                 dtype="bf16"),
+    "route1024_top4": W.MoEConfig("route1024_top4", T=200, D=256, F=64, E=1024, k=4, m_tile=16,
+                                  dtype="bf16", zipf_s=1.2),
+    "route100_f32": W.MoEConfig("route100_f32", T=150, D=128, F=64, E=100, k=5, m_tile=16,
+                                dtype="f32"),
 }
 
 
@@ -77,14 +91,18 @@ def test_single_assignment_on_the_decode_gemm():
     P.check_layer(_bf16_layer(1, 512, 512, 64, 1), 1, 128, "bf16")
 
 
-@pytest.mark.parametrize("k", [1, 2])
-def test_zero_gate_ties_send_every_token_to_lowest_experts(k):
-    P.log(f"[parity] zero gate k={k}")
-    inp = _bf16_layer(333, 128, 128, 8, k)
+@pytest.mark.parametrize("E,k", [(8, 1), (8, 2), (40, 6), (256, 8), (1024, 3)])
+def test_zero_gate_ties_send_every_token_to_lowest_experts(E, k):
+    # all logits equal: every pick is a tie, resolved to the lowest index, also where
+    # the experts spread over several logits per lane (E > 64)
+    P.log(f"[parity] zero gate E={E} k={k}")
+    mt = 128 if E <= 64 else 16
+    T = 333 if E <= 64 else 64
+    inp = _bf16_layer(T, 128, 128, E, k, m_tile=mt)
     inp["wg"][:] = 0
-    g = P.check_layer(inp, k, 128, "bf16")
+    g = P.check_layer(inp, k, mt, "bf16")
     assert np.all(g["topk_idx"] == np.arange(k))
-    np.testing.assert_array_equal(g["counts"], [333] * k + [0] * (8 - k))
+    np.testing.assert_array_equal(g["counts"], [T] * k + [0] * (E - k))
 
 
 def test_out_of_range_expert_ids_are_flagged_and_skipped():
