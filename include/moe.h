@@ -64,7 +64,7 @@ typedef enum {
   MOE_ECAPACITY = 3,    /* m_cap < moe_capacity(...) or m_cap % m_tile != 0         */
   MOE_EWORKSPACE = 4,   /* workspace smaller than moe_permute_workspace_bytes(...)  */
   MOE_EHIP = 5,         /* the HIP runtime reported an error while launching        */
-  MOE_EUNSUPPORTED = 6, /* valid request with no kernel for it (see below)          */
+  MOE_EUNSUPPORTED = 6, /* valid request with no kernel for it (no call returns it now) */
   MOE_ESCRATCH = 7      /* input too large for the library's static scratch         */
 } moe_status_t;
 
@@ -229,8 +229,7 @@ moe_status_t moe_grouped_swiglu_masked(moe_dtype_t dt, const void* x_masked,
  * 128 rows with enough experts (D and F multiples of 128, E*min(D,F)/64 at least two
  * workgroups per CU): such decode-sized calls stream each active expert's weights
  * past its rows instead of tiling (fc1 without ab, fc2).
- * Errors: MOE_EINVAL, MOE_ESHAPE, MOE_ECAPACITY (m_cap % m_tile),
- * MOE_EUNSUPPORTED, MOE_EHIP.
+ * Errors: MOE_EINVAL, MOE_ESHAPE, MOE_ECAPACITY (m_cap % m_tile), MOE_EHIP.
  */
 moe_status_t moe_grouped_swiglu(moe_dtype_t dt, const void* x_perm, const int32_t* offsets,
                                 const int32_t* counts, const int32_t* tile_expert, int E, int D,
@@ -288,9 +287,9 @@ moe_status_t moe_grouped_fc2(moe_dtype_t dt, const void* h, const int32_t* offse
  *   products of the dequantized rows and w1q/w1s, w3q/w3s ([E,F,D] codes; scales in
  *   MOE_MX_KSTEPS over the E*F rows, [D/128][E*F] words), per segment as
  *   moe_grouped_fc1_swiglu (workspace likewise); xs_perm as moe_permute_mxfp8 writes it.
- *   D a multiple of 128; m_tile 128 or 256.
+ *   D a multiple of 128; every m_tile, as for moe_grouped_swiglu.
  * Errors: MOE_EINVAL (also an unknown layout), MOE_ESHAPE, MOE_ECAPACITY,
- * MOE_EWORKSPACE, MOE_EUNSUPPORTED, MOE_EHIP.
+ * MOE_EWORKSPACE, MOE_EHIP.
  */
 typedef enum { MOE_MX_ROWS = 0, MOE_MX_KSTEPS = 1 } moe_mx_layout_t;
 

@@ -273,7 +273,6 @@ moe_status_t moe_grouped_fc1_swiglu_mxfp8(const void* xq_perm, const void* xs_pe
     return MOE_ESHAPE;
   if ((int64_t)D * F >= ((int64_t)1 << 31)) return MOE_ESHAPE;
   if (m_cap < 1 || m_cap % m_tile != 0 || m_cap > INT32_MAX) return MOE_ECAPACITY;
-  if (m_tile != 128 && m_tile != 256) return MOE_EUNSUPPORTED;
   return hip_status(moe::launch_grouped_fc1_mx(xq_perm, xs_perm, offsets, counts, E, D, F, m_cap,
                                                w1q,
                                                w1s, w3q, w3s, h,

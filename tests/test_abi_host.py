@@ -292,7 +292,7 @@ def test_mxfp8_calls_validate():
     assert f(D=192) == MOE_ESHAPE
     assert f(F=100) == MOE_ESHAPE
     assert f(m_cap=1000) == MOE_ECAPACITY
-    assert f(mt=64, m_cap=1024) == MOE_EUNSUPPORTED
+    assert f(mt=64, m_cap=1000) == MOE_ECAPACITY
 
 
 def test_binding_raises_on_rejected_call():

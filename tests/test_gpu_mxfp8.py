@@ -45,12 +45,13 @@ def _layer_case(name):
         "skew32_zipf": W.shrink(W.preset("skew32_zipf_bf16"), T=1024, D=512, F=256),
         "etp_shard32": W.shrink(W.preset("etp_shard32_bf16"), D=1024, F=512, poisson_mean=40.0),
         "dense8_mt256": W.shrink(W.preset("dense8_bf16"), T=520, D=512, F=512, m_tile=256),
+        "skew32_mt32": W.shrink(W.preset("skew32_zipf_bf16"), T=700, D=512, F=384, m_tile=32),
     }
     return cases[name]
 
 
 @pytest.mark.parametrize("name", ["dense8", "fine64_shared2", "skew32_zipf", "etp_shard32",
-                                  "dense8_mt256"])
+                                  "dense8_mt256", "skew32_mt32"])
 @pytest.mark.parametrize("split_k", [True, False])
 def test_mxfp8_layer_parity(name, split_k):
     cfg = _layer_case(name)
