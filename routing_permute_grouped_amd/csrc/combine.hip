@@ -5,8 +5,8 @@
 // output; section 5: the unpermute is the transpose of the permute).
 //
 // Each token's k expert rows are gathered by 16-byte chunks and reduced in float32
-// in slot order; the shared row is added last and the sum is rounded once. Every
-// thread keeps four chunks' row reads in flight per slot. Without weights the same
+// in slot order; the shared row is added last and the sum is rounded once. A thread
+// takes one chunk at a time and keeps its reads of up to four slots in flight. Without weights the same
 // kernel is the plain unpermute-and-sum, which is also the backward of the permute
 // (section 5: the permute's mirror is a scatter_add).
 //
@@ -26,7 +26,10 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kTokens = 4;
 constexpr int kMaxK = 32;
-constexpr int kU = 4;   // 16-byte chunks per thread whose reads are in flight together
+constexpr int kU = 1;   // 16-byte chunks per thread (more registers per thread cost more
+                        // than they give: at most 64 VGPRs keeps 8 waves per SIMD)
+constexpr int kJ = 4;   // slots whose reads of those chunks are in flight together
+constexpr int kUB = 4;  // the backward's chunks in flight per lane (each with two reads)
 
 template <typename TIn>
 __global__ __launch_bounds__(kThreads) void combine_kernel(
@@ -46,7 +49,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(
   __syncthreads();
   const int nck = D / V;
   const int total = ntok * nck;
-  // kU chunks per thread: for each slot j their kU row reads are in flight together
+  // kU chunks per thread, the reads of kJ slots in flight together
   for (int i0 = threadIdx.x; i0 < total; i0 += kThreads * kU) {
     float acc[kU][V];
     int tl[kU], cc[kU];
@@ -58,22 +61,32 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(
 #pragma unroll
       for (int v = 0; v < V; ++v) acc[u][v] = 0.0f;
     }
-    for (int j = 0; j < k; ++j) {
-      u32x4 yv[kU];
+    for (int j0 = 0; j0 < k; j0 += kJ) {
+      u32x4 yv[kJ][kU];
 #pragma unroll
-      for (int u = 0; u < kU; ++u) {
-        const int d = ds[tl[u] * k + j];
-        if (d >= 0) yv[u] = ld16_nt(y + (size_t)d * D + (size_t)cc[u] * V);
+      for (int jj = 0; jj < kJ; ++jj) {
+        const int j = j0 + jj;
+        if (j >= k) break;
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+          const int d = ds[tl[u] * k + j];
+          if (d >= 0) yv[jj][u] = ld16_nt(y + (size_t)d * D + (size_t)cc[u] * V);
+        }
       }
 #pragma unroll
-      for (int u = 0; u < kU; ++u) {
-        const int d = ds[tl[u] * k + j];
-        if (d < 0) continue;
-        const float wj = ws[tl[u] * k + j];
-        float f[V];
-        Chunk<TIn>::widen(yv[u], f);
+      for (int jj = 0; jj < kJ; ++jj) {
+        const int j = j0 + jj;
+        if (j >= k) break;
 #pragma unroll
-        for (int v = 0; v < V; ++v) acc[u][v] = __builtin_fmaf(wj, f[v], acc[u][v]);
+        for (int u = 0; u < kU; ++u) {
+          const int d = ds[tl[u] * k + j];
+          if (d < 0) continue;
+          const float wj = ws[tl[u] * k + j];
+          float f[V];
+          Chunk<TIn>::widen(yv[jj][u], f);
+#pragma unroll
+          for (int v = 0; v < V; ++v) acc[u][v] = __builtin_fmaf(wj, f[v], acc[u][v]);
+        }
       }
     }
 #pragma unroll
@@ -92,7 +105,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(
 }
 
 // One wave per row of the permuted buffer, rows [0, min(offsets[E], m_cap)); each lane
-// takes 16-byte chunks lane, lane+64, ... in increasing order, kU of them in flight.
+// takes 16-byte chunks lane, lane+64, ... in increasing order, kUB of them in flight.
 // The dot product is summed per lane in chunk order, then over lanes by an xor
 // butterfly (every lane ends with the same value, lane 0 stores it).
 template <typename TIn>
@@ -120,10 +133,10 @@ __global__ __launch_bounds__(kThreads) void combine_bwd_kernel(
     const TIn* yr = y + r * D;
     const float wj = w[s];
     float acc = 0.0f;
-    for (int c0 = lane; c0 < nck; c0 += 64 * kU) {
-      u32x4 gv[kU], yv[kU];
+    for (int c0 = lane; c0 < nck; c0 += 64 * kUB) {
+      u32x4 gv[kUB], yv[kUB];
 #pragma unroll
-      for (int u = 0; u < kU; ++u) {
+      for (int u = 0; u < kUB; ++u) {
         const int c = c0 + 64 * u;
         if (c < nck) {
           gv[u] = ld16(g + (size_t)c * V);
@@ -131,7 +144,7 @@ __global__ __launch_bounds__(kThreads) void combine_bwd_kernel(
         }
       }
 #pragma unroll
-      for (int u = 0; u < kU; ++u) {
+      for (int u = 0; u < kUB; ++u) {
         const int c = c0 + 64 * u;
         if (c >= nck) continue;
         float gf[V], yf[V], o[V];
