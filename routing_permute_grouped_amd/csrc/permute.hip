@@ -4,7 +4,9 @@
 // the output layout must be expert-contiguous with every segment aligned to the GEMM
 // M tile).
 //
-// Three launches:
+// Two launches while the histogram table is small (hist_kernel, then place_kernel, which
+// ranks and copies in one pass; up to 2^24 table reads in all, every benchmark workload),
+// else three:
 //   1. hist_kernel   per 256-token block, the slots of each expert (LDS atomics:
 //                    counts do not depend on their order) and the bad-index count.
 //   2. rank_kernel   one workgroup per histogram block reads the small histogram
@@ -372,6 +374,214 @@ __global__ __launch_bounds__(kThreads) void copy_kernel(
   }
 }
 
+// Rank and copy in one launch (the contiguous layout, when the histogram table is small
+// enough for every workgroup to read it; see launch_permute). Workgroup g takes tokens
+// [kCopyTokens g, kCopyTokens g + kCopyTokens): it sums the table into the per-expert
+// totals and its histogram block's starting ranks, counts the slots of that block that
+// precede its tokens, derives the padded offsets, ranks its own slots in slot order
+// (ballot match in wave 0), writes dst_row / src_row, and copies its tokens' rows to
+// their destination rows. Every workgroup then takes a share of the pad rows (zeroed,
+// src_row -1) and of the rows past offsets[E] (src_row -1); workgroup 0 also writes
+// counts, offsets, tile_expert and the error flag.
+template <typename TIn>
+__global__ __launch_bounds__(kThreads) void place_kernel(
+    const TIn* __restrict__ x, const int32_t* __restrict__ idx, int T, int D, int k, int E,
+    int m_tile, int64_t m_cap, int nbh, const int32_t* __restrict__ hist,
+    const int32_t* __restrict__ bad, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ tile_expert, int32_t* __restrict__ dev_err,
+    int32_t* __restrict__ dst_row, int32_t* __restrict__ src_row, TIn* __restrict__ x_perm) {
+  constexpr int V = Chunk<TIn>::V;
+  __shared__ int off[kMaxExperts + 1];   // padded segment starts
+  __shared__ int cnt[kMaxExperts];       // rows per expert
+  __shared__ int base[kMaxExperts];      // next free row per expert for this workgroup
+  __shared__ int ds[kCopyTokens * kMaxTopK];
+  __shared__ int pstart[kMaxExperts];    // first pad row of each expert
+  __shared__ int ppre[kMaxExperts + 1];  // pad rows of the experts before e
+  __shared__ int wsum[kThreads / kWave];
+  __shared__ int wsum2[kThreads / kWave];
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int t0 = blockIdx.x * kCopyTokens;
+  const int nt = min(kCopyTokens, T - t0);
+  const int hb = t0 / kHistTokens;
+  const int n = nt * k;                  // this workgroup's slots
+  const int64_t a0 = (int64_t)t0 * k;
+
+  for (int e = tid; e < E; e += kThreads) {
+    cnt[e] = 0;
+    base[e] = 0;
+  }
+  int own[kCopyTokens * kMaxTopK / kWave];
+  if (tid < kWave) {
+#pragma unroll
+    for (int i = 0; i < kCopyTokens * kMaxTopK / kWave; ++i) {
+      const int a = i * kWave + tid;
+      own[i] = a < n ? idx[a0 + a] : -1;
+    }
+  }
+  __syncthreads();
+  // totals and the starting rank of histogram block hb (integer atomics: any order)
+  for (int i0 = tid; i0 < nbh * E; i0 += kThreads * kBatch) {
+    int cv[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int i = i0 + j * kThreads;
+      cv[j] = i < nbh * E ? hist[i] : 0;
+    }
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      if (cv[j] == 0) continue;
+      const int i = i0 + j * kThreads;
+      const int h = i / E, e = i - h * E;
+      atomicAdd(&cnt[e], cv[j]);
+      if (h < hb) atomicAdd(&base[e], cv[j]);
+    }
+  }
+  // slots of block hb before this workgroup's tokens
+  const int64_t p0 = (int64_t)hb * kHistTokens * k;
+  for (int64_t g = p0 + tid; g < a0; g += (int64_t)kThreads * kBatch) {
+    int ev[kBatch];
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int64_t a = g + (int64_t)i * kThreads;
+      ev[i] = a < a0 ? idx[a] : -1;
+    }
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i)
+      if (ev[i] >= 0 && ev[i] < E) atomicAdd(&base[ev[i]], 1);
+  }
+  __syncthreads();
+  {
+    int padded[4] = {0, 0, 0, 0};
+    int local = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = tid * 4 + i;
+      if (e < E) padded[i] = (cnt[e] + m_tile - 1) / m_tile * m_tile;
+      local += padded[i];
+    }
+    int run = block_exclusive_scan(local, wsum);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = tid * 4 + i;
+      if (e < E) off[e] = run;
+      run += padded[i];
+    }
+    if (tid == kThreads - 1) off[E] = run;
+  }
+  __syncthreads();
+
+  // rank this workgroup's slots in slot order (wave 0), then its rows' destinations
+  if (tid < kWave) {
+    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+    const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
+#pragma unroll
+    for (int i = 0; i < kCopyTokens * kMaxTopK / kWave; ++i) {
+      const int r0 = i * kWave;
+      if (r0 >= n) break;
+      const int a = r0 + lane;
+      const int e = own[i];
+      const bool valid = a < n && e >= 0 && e < E;
+      uint64_t same = __ballot(valid);
+      for (int bit = 0; bit < nbits; ++bit) {
+        const uint64_t bal = __ballot(valid && ((e >> bit) & 1));
+        same &= ((e >> bit) & 1) ? bal : ~bal;
+      }
+      int pos = -1;
+      if (valid) pos = off[e] + base[e] + __popcll(same & lt);
+      if (pos >= m_cap) pos = -1;  // cannot happen with consistent counts; never write past m_cap
+      __builtin_amdgcn_wave_barrier();
+      if (valid && (same >> lane) == 1ull) base[e] = base[e] + __popcll(same);
+      __builtin_amdgcn_wave_barrier();
+      if (a < n) {
+        ds[a] = pos;
+        dst_row[a0 + a] = pos;
+        if (pos >= 0) src_row[pos] = (int32_t)(a0 + a);
+      }
+    }
+  }
+  __syncthreads();
+  const int nck = D / V;
+  for (int c = tid; c < nck; c += kThreads) {
+    u32x4 v[kCopyTokens];
+#pragma unroll
+    for (int i = 0; i < kCopyTokens; ++i)
+      if (i < nt) v[i] = ld16_nt(x + (int64_t)(t0 + i) * D + (int64_t)c * V);
+#pragma unroll
+    for (int i = 0; i < kCopyTokens; ++i) {
+      if (i >= nt) continue;
+      for (int j = 0; j < k; ++j) {
+        const int d = ds[i * k + j];
+        if (d >= 0) st16(x_perm + (int64_t)d * D + (int64_t)c * V, v[i]);
+      }
+    }
+  }
+
+  // pad rows (zero rows, src_row -1), numbered across experts; rows past offsets[E]
+  {
+    int pads[4] = {0, 0, 0, 0};
+    int local = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = tid * 4 + i;
+      if (e < E) {
+        pstart[e] = off[e] + cnt[e];
+        pads[i] = off[e + 1] - off[e] - cnt[e];
+      }
+      local += pads[i];
+    }
+    int run = block_exclusive_scan(local, wsum2);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = tid * 4 + i;
+      if (e < E) ppre[e] = run;
+      run += pads[i];
+    }
+    if (tid == kThreads - 1) ppre[E] = run;
+  }
+  __syncthreads();
+  const int npad = ppre[E];
+  const u32x4 z = {0u, 0u, 0u, 0u};
+  const int nwaves = gridDim.x * (kThreads / kWave);
+  for (int q = blockIdx.x * (kThreads / kWave) + tid / kWave; q < npad; q += nwaves) {
+    int lo = 0, hi = E;   // largest e with ppre[e] <= q
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (ppre[mid] <= q) lo = mid; else hi = mid;
+    }
+    const int r = pstart[lo] + (q - ppre[lo]);
+    TIn* row = x_perm + (int64_t)r * D;
+    for (int c = lane; c < nck; c += kWave) st16(row + (int64_t)c * V, z);
+    if (lane == 0) src_row[r] = -1;
+  }
+  const int64_t total = off[E];
+  for (int64_t r = total + (int64_t)blockIdx.x * kThreads + tid; r < m_cap;
+       r += (int64_t)gridDim.x * kThreads)
+    src_row[r] = -1;
+  if (blockIdx.x == 0) {   // metadata and the error flag
+    for (int i = tid; i < E; i += kThreads) counts[i] = cnt[i];
+    for (int i = tid; i <= E; i += kThreads) offsets[i] = off[i];
+    const int64_t ntiles = m_cap / m_tile;
+    for (int64_t q = tid; q < ntiles; q += kThreads) {
+      const int64_t r = q * m_tile;
+      int owner = -1;
+      if (r < total) {
+        int lo = 0, hi = E;  // largest e with off[e] <= r
+        while (hi - lo > 1) {
+          const int mid = (lo + hi) >> 1;
+          if (off[mid] <= r) lo = mid; else hi = mid;
+        }
+        owner = lo;
+      }
+      tile_expert[q] = owner;
+    }
+    int anybad = 0;
+    for (int h = tid; h < nbh; h += kThreads) anybad |= bad[h] != 0;
+    anybad = __syncthreads_or(anybad);
+    if (tid == 0) *dev_err = anybad;
+  }
+}
+
 // Scales of the FP8 payload into k-step words: out[s * m_cap + row] is word s of the
 // [T, D/32]-byte scale row of the token that fills permuted row `row` (its src_row
 // assignment / k), 0 for a pad row; rows at or past offsets[E] are not written. Threads
@@ -424,6 +634,22 @@ hipError_t launch_permute(int dt, const void* x, const int32_t* topk_idx, int T,
   int32_t* hist = static_cast<int32_t*>(workspace);
   int32_t* bad = hist + (size_t)nbh * E;
   hipLaunchKernelGGL(hist_kernel, dim3(nbh), dim3(kThreads), 0, s, topk_idx, T, k, E, hist, bad);
+  const int ngroups = (T + kCopyTokens - 1) / kCopyTokens;
+  // rank and copy in one launch while every workgroup reading the whole table stays cheap
+  // (at most 2^24 table reads in all: e.g. 16384 tokens with 64 experts)
+  if ((int64_t)ngroups * nbh * E <= ((int64_t)1 << 24)) {
+    if (dt == kF32)
+      hipLaunchKernelGGL(place_kernel<float>, dim3(ngroups), dim3(kThreads), 0, s,
+                         static_cast<const float*>(x), topk_idx, T, D, k, E, m_tile, m_cap, nbh,
+                         hist, bad, counts, offsets, tile_expert, dev_err, dst_row, src_row,
+                         static_cast<float*>(x_perm));
+    else
+      hipLaunchKernelGGL(place_kernel<bf16_t>, dim3(ngroups), dim3(kThreads), 0, s,
+                         static_cast<const bf16_t*>(x), topk_idx, T, D, k, E, m_tile, m_cap, nbh,
+                         hist, bad, counts, offsets, tile_expert, dev_err, dst_row, src_row,
+                         static_cast<bf16_t*>(x_perm));
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(rank_kernel<false>, dim3(nbh + 1), dim3(kThreads), 0, s, topk_idx, T, k, E,
                      m_tile, 0, m_cap, nbh, hist, bad, counts, offsets, tile_expert, dev_err,
                      dst_row, src_row);
