@@ -362,14 +362,15 @@ def test_grouped_calls_skip_pad_rows_given_counts(split):
 
 
 @pytest.mark.parametrize("T,E,k,mt", [(700, 64, 32, 128), (1537, 1024, 8, 64), (4097, 3, 2, 256),
-                                      (300, 7, 7, 128), (16384, 1024, 2, 64)])
+                                      (300, 7, 7, 128), (8192, 8, 4, 128), (16384, 1024, 2, 64)])
 def test_permute_layout_extremes(T, E, k, mt):
     # the permute alone against the oracle's layout: top-32 routing (the largest k), the
     # largest expert count, several 256-token histogram blocks with a ragged last one,
     # and -1 slots; every map bit-exact, x_perm exact on token rows and zero on pad rows
-    # (rows past offsets[E] are not the permute's to write). The last case has a
-    # histogram table too large for the one-launch rank-and-copy kernel, so it takes the
-    # separate rank and copy kernels.
+    # (rows past offsets[E] are not the permute's to write). A small histogram table
+    # takes the histogram then the rank-and-copy kernel (8192 tokens x top-4 here, like
+    # every benchmark workload); the last case's table is too large for it and takes the
+    # histogram, rank and copy kernels.
     P.log(f"[parity] permute layout T={T} E={E} k={k} m_tile={mt}")
     rng = np.random.default_rng(T + E + k)
     idx = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
