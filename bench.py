@@ -58,16 +58,16 @@ def gemm_source_sha16() -> str:
 # kind: fc1 (forward), wgrad_fc1 (backward), fp8_fc1 (FP8 payload), masked (decode).
 TRAFFIC = {
     "fc1": {
-        "dense8_bf16": (5262960390, "fbcaaa6c3bad33cb"),
-        "etp_shard32_bf16": (839717128, "fbcaaa6c3bad33cb"),
-        "fine64_shared2_bf16": (1668580941, "fbcaaa6c3bad33cb"),
-        "skew32_zipf_bf16": (5186537267, "fbcaaa6c3bad33cb"),
+        "dense8_bf16": (5209979413, "fbcaaa6c3bad33cb"),
+        "etp_shard32_bf16": (837568492, "fbcaaa6c3bad33cb"),
+        "fine64_shared2_bf16": (1593426228, "fbcaaa6c3bad33cb"),
+        "skew32_zipf_bf16": (5250033637, "fbcaaa6c3bad33cb"),
     },
     "wgrad_fc1": {
-        "dense8_bf16": (8024598243, "fbcaaa6c3bad33cb"),
+        "dense8_bf16": (8081100900, "fbcaaa6c3bad33cb"),
     },
     "fp8_fc1": {
-        "dense8_bf16": (2457863066, "fbcaaa6c3bad33cb"),
+        "dense8_bf16": (2442766130, "fbcaaa6c3bad33cb"),
     },
 }
 
