@@ -25,6 +25,7 @@ namespace moe {
 namespace {
 
 constexpr int kWavesPerBlock = 4;
+constexpr int kRawBuffer = 0x00020000;   // descriptor word 3: raw buffer, 32-bit data
 
 // float32: a rounded multiply followed by a rounded add (no contraction).
 __device__ __forceinline__ void dot_step(float& acc, float a, float b, float) {
@@ -61,6 +62,91 @@ __device__ __forceinline__ float reduce_pairs(float* v, int lane) {
   }
 }
 
+// Element i of a 16-byte chunk, widened exactly to float32.
+template <typename TIn>
+__device__ __forceinline__ float elem(const u32x4& c, int i);
+template <>
+__device__ __forceinline__ float elem<float>(const u32x4& c, int i) {
+  return __uint_as_float(c[i]);
+}
+template <>
+__device__ __forceinline__ float elem<bf16_t>(const u32x4& c, int i) {
+  return (i & 1) ? bf16_hi(c[i >> 1]) : bf16_lo(c[i >> 1]);
+}
+
+// Softmax and top-k of one token from its logits in LDS (lgrow[e], e < E), by one wave:
+// lane l holds the logits of experts l, l + 64, ... (NE of them); each top-k round takes
+// every lane's best available expert, then the wave's.
+template <int NE>
+__device__ __forceinline__ void route_token(const float* lgrow, int tok, int E, int k,
+                                            int renorm, int32_t* __restrict__ topk_idx,
+                                            float* __restrict__ topk_w,
+                                            float* __restrict__ logits_out, int lane) {
+  float l[NE];
+#pragma unroll
+  for (int i = 0; i < NE; ++i) {
+    const int e = lane + kWave * i;
+    l[i] = e < E ? lgrow[e] : -INFINITY;
+    if (logits_out && e < E) logits_out[(size_t)tok * E + e] = l[i];
+  }
+  float mx = l[0];
+#pragma unroll
+  for (int i = 1; i < NE; ++i) mx = fmaxf(mx, l[i]);
+#pragma unroll
+  for (int m = kWave / 2; m >= 1; m >>= 1) mx = fmaxf(mx, __shfl_xor(mx, m));
+  float ex[NE];
+  float sum = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NE; ++i) {
+    ex[i] = lane + kWave * i < E ? expf(l[i] - mx) : 0.0f;
+    sum += ex[i];
+  }
+#pragma unroll
+  for (int m = kWave / 2; m >= 1; m >>= 1) sum += __shfl_xor(sum, m);
+
+  uint32_t avail = 0;   // bit i: expert lane + 64 i is still available
+#pragma unroll
+  for (int i = 0; i < NE; ++i)
+    if (lane + kWave * i < E) avail |= 1u << i;
+  int my_idx = 0;
+  float my_w = 0.0f, wtot = 0.0f;
+  for (int j = 0; j < k; ++j) {
+    // this lane's best available expert (in increasing index, so a tie keeps the lower)
+    float key = -INFINITY, xv = 0.0f;
+    int id = 0x7fffffff;
+#pragma unroll
+    for (int i = 0; i < NE; ++i)
+      if (((avail >> i) & 1u) && (id == 0x7fffffff || l[i] > key)) {
+        key = l[i];
+        id = lane + kWave * i;
+        xv = ex[i];
+      }
+    // then the wave's: the larger logit, ties to the lower index
+#pragma unroll
+    for (int m = kWave / 2; m >= 1; m >>= 1) {
+      const float ok = __shfl_xor(key, m);
+      const int oi = __shfl_xor(id, m);
+      const float ox = __shfl_xor(xv, m);
+      if (ok > key || (ok == key && oi < id)) {
+        key = ok;
+        id = oi;
+        xv = ox;
+      }
+    }
+    if (id % kWave == lane) avail &= ~(1u << (id / kWave));
+    const float wj = xv / sum;
+    wtot += wj;
+    if (lane == j) {
+      my_idx = id;
+      my_w = wj;
+    }
+  }
+  if (lane < k) {
+    topk_idx[(size_t)tok * k + lane] = my_idx;
+    topk_w[(size_t)tok * k + lane] = renorm ? my_w / wtot : my_w;
+  }
+}
+
 // NE: logits per lane in the softmax and top-k (experts e = lane + 64 i, i < NE).
 template <typename TIn, int TW, int EC, bool SHARED, int NE>
 __global__ __launch_bounds__(kWave * kWavesPerBlock) void route_kernel(
@@ -74,67 +160,78 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock) void route_kernel(
   constexpr int NL = SHARED ? 1 : kWavesPerBlock;   // logit tables per block
   __shared__ float lg[NL][TW][NE * kWave];
   const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   // SHARED: the block's waves share tokens t0 .. t0+TW-1 and split the passes
   const int t0 = SHARED ? blockIdx.x * TW : (blockIdx.x * kWavesPerBlock + wave) * TW;
   const int tab = SHARED ? 0 : wave;
   const int nchunk = D / V;
+  // every lane takes the same whole number of chunk pairs, and byte offsets fit 31 bits
+  const bool pipelined = nchunk % (2 * kWave) == 0 &&
+                         (int64_t)max(T, E) * D * (int64_t)sizeof(TIn) < ((int64_t)1 << 31);
 
   for (int e0 = SHARED ? wave * EC : 0; e0 < E; e0 += SHARED ? kWavesPerBlock * EC : EC) {
     float acc[P];
 #pragma unroll
     for (int p = 0; p < P; ++p) acc[p] = 0.0f;
-    if constexpr (!SHARED) {
-      // few experts: the raw chunks of step c + 64 are loaded while step c is summed
-      // (the summation order is unchanged)
-      u32x4 xr[2][TW], wr[2][EC];
-      auto load = [&](int c, int b) {
+    // Element i of every token chunk and every gate-weight chunk is widened once and
+    // feeds the TW x EC products of that element; each pair still adds its 8 (4)
+    // products of a chunk in increasing d.
+    auto sum = [&](const u32x4 (&xc)[TW], const u32x4 (&wc)[EC]) {
+#pragma unroll
+      for (int i = 0; i < V; ++i) {
+        float xe[TW], we[EC];
+#pragma unroll
+        for (int t = 0; t < TW; ++t) xe[t] = elem<TIn>(xc[t], i);
+#pragma unroll
+        for (int e = 0; e < EC; ++e) we[e] = elem<TIn>(wc[e], i);
 #pragma unroll
         for (int t = 0; t < TW; ++t)
-          xr[b][t] = ld16(x + (size_t)min(t0 + t, T - 1) * D + (size_t)c * V);
 #pragma unroll
-        for (int e = 0; e < EC; ++e) wr[b][e] = ld16(wg + (size_t)min(e0 + e, E - 1) * D + (size_t)c * V);
+          for (int e = 0; e < EC; ++e) dot_step(acc[t * EC + e], xe[t], we[e], TIn());
+      }
+    };
+    u32x4 xr[2][TW], wr[2][EC];
+    if (pipelined) {
+      // Buffer loads: one descriptor per tensor, the row's byte offset in a scalar
+      // register and the chunk's in one vector register shared by every load. The
+      // loop is uniform and holds no branch, the loads of the step ahead are issued
+      // one step before their sum (the load past the last pair reads a valid chunk and
+      // is not summed), and the compiler's wait before each sum counts exactly the
+      // loads still in flight for the step ahead.
+      const __amdgpu_buffer_rsrc_t rx =
+          __builtin_amdgcn_make_buffer_rsrc((void*)x, (short)0, T * D * (int)sizeof(TIn), kRawBuffer);
+      const __amdgpu_buffer_rsrc_t rw =
+          __builtin_amdgcn_make_buffer_rsrc((void*)wg, (short)0, E * D * (int)sizeof(TIn), kRawBuffer);
+      int sx[TW], sw[EC];
+#pragma unroll
+      for (int t = 0; t < TW; ++t) sx[t] = min(t0 + t, T - 1) * D * (int)sizeof(TIn);
+#pragma unroll
+      for (int e = 0; e < EC; ++e) sw[e] = min(e0 + e, E - 1) * D * (int)sizeof(TIn);
+      auto load = [&](int c, int b) {
+        int off = c * 16;
+        asm volatile("" : "+v"(off));   // the step-ahead load stays a load of its own
+#pragma unroll
+        for (int t = 0; t < TW; ++t) xr[b][t] = __builtin_amdgcn_raw_buffer_load_b128(rx, off, sx[t], 0);
+#pragma unroll
+        for (int e = 0; e < EC; ++e) wr[b][e] = __builtin_amdgcn_raw_buffer_load_b128(rw, off, sw[e], 0);
+        __builtin_amdgcn_sched_barrier(0);   // and the scheduler keeps them ahead of the sum
       };
-      auto sum = [&](int b) {
-        float xv[TW][V];
-#pragma unroll
-        for (int t = 0; t < TW; ++t) Chunk<TIn>::widen(xr[b][t], xv[t]);
-#pragma unroll
-        for (int e = 0; e < EC; ++e) {
-          float wv[V];
-          Chunk<TIn>::widen(wr[b][e], wv);
-#pragma unroll
-          for (int t = 0; t < TW; ++t)
-#pragma unroll
-            for (int i = 0; i < V; ++i) dot_step(acc[t * EC + e], xv[t][i], wv[i], TIn());
-        }
-      };
-      if (lane < nchunk) load(lane, 0);
-      for (int c = lane; c < nchunk; c += 2 * kWave) {   // buffers 0 / 1 hold c / c + 64
-        if (c + kWave < nchunk) load(c + kWave, 1);
-        sum(0);
-        if (c + kWave >= nchunk) break;
-        if (c + 2 * kWave < nchunk) load(c + 2 * kWave, 0);
-        sum(1);
+      const int npair = nchunk / (2 * kWave);
+      load(lane, 0);
+      for (int j = 0; j < npair; ++j) {
+        const int c = lane + j * 2 * kWave;
+        load(c + kWave, 1);
+        sum(xr[0], wr[0]);
+        load(min(c + 2 * kWave, nchunk - 1), 0);
+        sum(xr[1], wr[1]);
       }
     } else {
       for (int c = lane; c < nchunk; c += kWave) {
-        float xv[TW][V];
 #pragma unroll
-        for (int t = 0; t < TW; ++t) {
-          const int tok = min(t0 + t, T - 1);
-          Chunk<TIn>::widen(ld16(x + (size_t)tok * D + (size_t)c * V), xv[t]);
-        }
+        for (int t = 0; t < TW; ++t) xr[0][t] = ld16(x + (size_t)min(t0 + t, T - 1) * D + (size_t)c * V);
 #pragma unroll
-        for (int e = 0; e < EC; ++e) {
-          const int ee = min(e0 + e, E - 1);
-          float wv[V];
-          Chunk<TIn>::widen(ld16(wg + (size_t)ee * D + (size_t)c * V), wv);
-#pragma unroll
-          for (int t = 0; t < TW; ++t)
-#pragma unroll
-            for (int i = 0; i < V; ++i) dot_step(acc[t * EC + e], xv[t][i], wv[i], TIn());
-        }
+        for (int e = 0; e < EC; ++e) wr[0][e] = ld16(wg + (size_t)min(e0 + e, E - 1) * D + (size_t)c * V);
+        sum(xr[0], wr[0]);
       }
     }
     float logit = reduce_pairs<P, kWave / 2>(acc, lane);
@@ -151,69 +248,7 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock) void route_kernel(
   for (int t = SHARED ? wave : 0; t < TW; t += SHARED ? kWavesPerBlock : 1) {
     const int tok = t0 + t;
     if (tok >= T) break;
-    float l[NE];
-#pragma unroll
-    for (int i = 0; i < NE; ++i) {
-      const int e = lane + kWave * i;
-      l[i] = e < E ? lg[tab][t][e] : -INFINITY;
-      if (logits_out && e < E) logits_out[(size_t)tok * E + e] = l[i];
-    }
-    float mx = l[0];
-#pragma unroll
-    for (int i = 1; i < NE; ++i) mx = fmaxf(mx, l[i]);
-#pragma unroll
-    for (int m = kWave / 2; m >= 1; m >>= 1) mx = fmaxf(mx, __shfl_xor(mx, m));
-    float ex[NE];
-    float sum = 0.0f;
-#pragma unroll
-    for (int i = 0; i < NE; ++i) {
-      ex[i] = lane + kWave * i < E ? expf(l[i] - mx) : 0.0f;
-      sum += ex[i];
-    }
-#pragma unroll
-    for (int m = kWave / 2; m >= 1; m >>= 1) sum += __shfl_xor(sum, m);
-
-    uint32_t avail = 0;   // bit i: expert lane + 64 i is still available
-#pragma unroll
-    for (int i = 0; i < NE; ++i)
-      if (lane + kWave * i < E) avail |= 1u << i;
-    int my_idx = 0;
-    float my_w = 0.0f, wtot = 0.0f;
-    for (int j = 0; j < k; ++j) {
-      // this lane's best available expert (in increasing index, so a tie keeps the lower)
-      float key = -INFINITY, xv = 0.0f;
-      int id = 0x7fffffff;
-#pragma unroll
-      for (int i = 0; i < NE; ++i)
-        if (((avail >> i) & 1u) && (id == 0x7fffffff || l[i] > key)) {
-          key = l[i];
-          id = lane + kWave * i;
-          xv = ex[i];
-        }
-      // then the wave's: the larger logit, ties to the lower index
-#pragma unroll
-      for (int m = kWave / 2; m >= 1; m >>= 1) {
-        const float ok = __shfl_xor(key, m);
-        const int oi = __shfl_xor(id, m);
-        const float ox = __shfl_xor(xv, m);
-        if (ok > key || (ok == key && oi < id)) {
-          key = ok;
-          id = oi;
-          xv = ox;
-        }
-      }
-      if (id % kWave == lane) avail &= ~(1u << (id / kWave));
-      const float wj = xv / sum;
-      wtot += wj;
-      if (lane == j) {
-        my_idx = id;
-        my_w = wj;
-      }
-    }
-    if (lane < k) {
-      topk_idx[(size_t)tok * k + lane] = my_idx;
-      topk_w[(size_t)tok * k + lane] = renorm ? my_w / wtot : my_w;
-    }
+    route_token<NE>(&lg[tab][t][0], tok, E, k, renorm, topk_idx, topk_w, logits_out, lane);
   }
 }
 

@@ -105,6 +105,37 @@ def test_zero_gate_ties_send_every_token_to_lowest_experts(E, k):
     np.testing.assert_array_equal(g["counts"], [T] * k + [0] * (E - k))
 
 
+@pytest.mark.parametrize("T,D,E,k,dtype,zipf", [
+    # whole pairs of 64-lane chunk steps: the pipelined loop, up to 8 experts per wave
+    (333, 1024, 8, 2, "bf16", 0.0),     # one pair per lane
+    (333, 2048, 8, 2, "bf16", 0.0),
+    (130, 3072, 8, 2, "bf16", 0.0),     # three pairs
+    (130, 4096, 6, 2, "bf16", 1.1),     # fewer than 8 experts, a bias
+    (101, 512, 6, 3, "f32", 0.0),       # float32: 4 values per chunk
+    (101, 1024, 8, 3, "f32", 0.0),
+    (250, 2048, 32, 4, "bf16", 1.1),    # shared tokens (E > 8), a bias, T % 8 != 0
+    (77, 1024, 256, 8, "bf16", 0.0),    # four logits per lane in the top-k
+    (90, 1024, 100, 5, "f32", 0.0),
+    # 192 chunks: not whole pairs, the plain loop
+    (64, 1536, 8, 2, "bf16", 0.0),
+])
+def test_router_chunk_loops(T, D, E, k, dtype, zipf):
+    """The router alone against the oracle: logits and indices bit for bit, weights to
+    float rounding, on both of its chunk loops (the pipelined loop over whole pairs of
+    64-lane steps, and the plain loop)."""
+    P.log(f"[parity] router T={T} D={D} E={E} k={k} {dtype}")
+    cfg = W.MoEConfig("router", T=T, D=D, F=64, E=E, k=k, m_tile=16, dtype=dtype, zipf_s=zipf)
+    inp = W.router_inputs(cfg, seed=7)
+    bias = inp.get("bias")
+    idx, w, lg = rpg.moe_route(P.to_dev(inp["x"]), P.to_dev(inp["wg"]), k,
+                               bias=None if bias is None else P.to_dev(bias), want_logits=True)
+    torch.cuda.synchronize()
+    ridx, rw, rlg = orc.route(inp["x"], inp["wg"], k, dtype, bias=bias)
+    np.testing.assert_array_equal(P.to_host(lg).view(np.uint32), rlg.view(np.uint32))
+    np.testing.assert_array_equal(P.to_host(idx), ridx)
+    np.testing.assert_allclose(P.to_host(w), rw, rtol=1e-6, atol=1e-7)
+
+
 def test_out_of_range_expert_ids_are_flagged_and_skipped():
     P.log("[parity] invalid expert ids")
     cfg = W.shrink(W.preset("etp_shard32_bf16"), D=256, F=256, poisson_mean=20.0)
