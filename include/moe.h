@@ -413,6 +413,22 @@ moe_status_t moe_grouped_wgrad(moe_dtype_t dt, const void* P, const void* Q,
                                int N2, int NS, int m_tile, int64_t m_cap, float* out_lo,
                                float* out_hi, void* stream);
 
+/*
+ * moe_round_bf16 - the float32 -> bf16 rounding that every bf16 value the library
+ * stores goes through (h, y_perm, the shared output and out of a bf16 layer, and the
+ * backward's bf16 gradients): round to nearest, ties to even, over the whole float32
+ * range (subnormal results kept, overflow to infinity); a NaN stays a NaN (quiet).
+ * The pages fix bf16 as the storage type of the combined output ("Expert Parallelism
+ * (EP)", section 6 "DeepSeek-V3 量级的示例数字") but not its rounding; IEEE
+ * round-to-nearest-even is the reading taken.
+ *
+ *   x [n] float32 -> y [n] bf16 bit patterns (device memory, caller-owned; x 4-byte and
+ *   y 2-byte aligned). n = 0 does nothing.
+ * Errors: MOE_EINVAL (null or misaligned pointer with n > 0), MOE_ESHAPE (n < 0 or
+ * n >= 2^40), MOE_EHIP.
+ */
+moe_status_t moe_round_bf16(const float* x, uint16_t* y, int64_t n, void* stream);
+
 /* Worst-case rows of the permuted buffer: with N = T*k slots,
  * m_tile * floor((N + min(E, N) * (m_tile - 1)) / m_tile). Returns -1 on bad sizes. */
 int64_t moe_capacity(int T, int k, int E, int m_tile);

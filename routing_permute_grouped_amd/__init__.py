@@ -11,7 +11,7 @@ from ._binding import (LIB_PATH, MOE_BF16, MOE_F32, MOE_MX_KSTEPS, MOE_MX_ROWS, 
                        moe_grouped_workspace_bytes, moe_permute, moe_permute_masked,
                        moe_permute_noalloc,
                        moe_permute_mxfp8, moe_permute_workspace_bytes, moe_quantize_mxfp8,
-                       moe_route, moe_status_str)
+                       moe_round_bf16, moe_route, moe_status_str)
 from .layer import (DenseRows, MxWeights, SharedExperts, moe_layer, moe_layer_backward,
                     moe_layer_masked, moe_layer_mxfp8)
 
@@ -22,7 +22,7 @@ __all__ = [
     "moe_grouped_wgrad", "moe_grouped_swiglu_masked", "moe_grouped_workspace_bytes",
     "moe_grouped_fc1_swiglu_mxfp8", "moe_permute", "moe_permute_masked", "moe_permute_mxfp8",
     "moe_permute_noalloc",
-    "moe_quantize_mxfp8",
+    "moe_quantize_mxfp8", "moe_round_bf16",
     "moe_permute_workspace_bytes", "moe_route", "moe_status_str", "DenseRows", "SharedExperts",
     "moe_layer", "moe_layer_backward", "moe_layer_masked", "moe_layer_mxfp8", "MxWeights",
 ]

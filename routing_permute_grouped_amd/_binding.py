@@ -36,6 +36,7 @@ SIGNATURES = [
     ("moe_grouped_fc2", _I, [_I, _P, _P, _P, _P, _I, _I, _I, _I, _I64, _P, _P, _P, _SZ, _P]),
     ("moe_combine", _I, [_I, _P, _P, _P, _P, _I, _I, _I, _I64, _P, _P]),
     ("moe_quantize_mxfp8", _I, [_I, _P, _I64, _I, _P, _P, _I, _P]),
+    ("moe_round_bf16", _I, [_P, _P, _I64, _P]),
     ("moe_permute_mxfp8", _I, [_P, _P, _P, _I, _I, _I, _I, _I, _I64, _P, _P, _P, _P, _P, _P, _P, _P,
                                _SZ, _P, _P]),
     ("moe_grouped_fc1_swiglu_mxfp8", _I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I64, _P, _P, _P,
@@ -608,6 +609,18 @@ def _bytes_ptr(t: torch.Tensor) -> int:
     if t.dtype != torch.uint8:
         raise TypeError("FP8 codes and scales are uint8 tensors")
     return _ptr(t)
+
+
+def moe_round_bf16(x: torch.Tensor, out: Optional[torch.Tensor] = None,
+                   stream=None) -> torch.Tensor:
+    """bf16 of float32 x (any shape), rounded as every bf16 value the library stores.
+    Returns out (bfloat16, x's shape)."""
+    _dtype(x, "x", torch.float32)
+    _exact(out, "out", tuple(x.shape), torch.bfloat16)
+    if out is None:
+        out = torch.empty(x.shape, dtype=torch.bfloat16, device=x.device)
+    _check("moe_round_bf16", lib.moe_round_bf16(_ptr(x), _ptr(out), x.numel(), _stream(stream)))
+    return out
 
 
 def moe_quantize_mxfp8(x: torch.Tensor, q: Optional[torch.Tensor] = None,

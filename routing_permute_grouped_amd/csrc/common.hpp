@@ -15,12 +15,11 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
   return __uint_as_float(bits16 << 16);
 }
 
-// Round to nearest, ties to even. NaN stays a quiet NaN.
+// Round to nearest, ties to even (gfx950's v_cvt_pk_bf16_f32, which the __bf16
+// conversion compiles to). NaN stays a quiet NaN.
+typedef __bf16 bf16x2_hw __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
 // Low and high bf16 of a packed 32-bit word, widened exactly.
@@ -28,7 +27,8 @@ __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w 
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+  const bf16x2_hw v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 // 16-byte chunk as 4 or 8 floats.

@@ -78,6 +78,9 @@ hipError_t launch_decode_swiglu(int phases, const void* x, const int32_t* offset
 
 // MX quantization of x [R, C] (dt) -> e4m3 codes [R, C] and E8M0 scales, [R, C/32]
 // bytes or (ksteps) [C/128][R] words of four bytes
+// float32 -> bf16 bit patterns, rounded as every bf16 store of the library
+hipError_t launch_round_bf16(const float* x, uint16_t* y, int64_t n, hipStream_t s);
+
 hipError_t launch_quantize_mx(int dt, const void* x, int64_t R, int C, void* q, void* scales,
                               bool ksteps, hipStream_t s);
 

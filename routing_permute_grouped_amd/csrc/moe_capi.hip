@@ -346,6 +346,12 @@ moe_status_t moe_grouped_wgrad(moe_dtype_t dt, const void* P, const void* Q,
                                               out_hi, static_cast<hipStream_t>(stream)));
 }
 
+moe_status_t moe_round_bf16(const float* x, uint16_t* y, int64_t n, void* stream) {
+  if (n < 0 || n >= ((int64_t)1 << 40)) return MOE_ESHAPE;
+  if (n > 0 && (!aligned4(x) || !y || (reinterpret_cast<uintptr_t>(y) & 1u))) return MOE_EINVAL;
+  return hip_status(moe::launch_round_bf16(x, y, n, static_cast<hipStream_t>(stream)));
+}
+
 moe_status_t moe_combine(moe_dtype_t dt, const void* y_perm, const int32_t* dst_row,
                          const float* topk_w, const void* shared, int T, int D, int k,
                          int64_t m_cap, void* out, void* stream) {

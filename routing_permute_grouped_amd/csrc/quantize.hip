@@ -83,6 +83,14 @@ __global__ __launch_bounds__(kThreads) void quantize_mx_kernel(const TIn* __rest
   }
 }
 
+// float32 -> bf16 with the rounding of every bf16 store (f32_to_bf16)
+__global__ __launch_bounds__(kThreads) void round_bf16_kernel(const float* __restrict__ x,
+                                                             uint16_t* __restrict__ y, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * kThreads)
+    y[i] = (uint16_t)f32_to_bf16(x[i]);
+}
+
 }  // namespace
 
 template <typename TIn>
@@ -93,6 +101,13 @@ void launch_quantize_t(const void* x, int64_t R, int C, void* q, void* scales, b
   auto kern = ksteps ? quantize_mx_kernel<TIn, true> : quantize_mx_kernel<TIn, false>;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), 0, s, static_cast<const TIn*>(x),
                      nblocks, R, C, static_cast<uint8_t*>(q), static_cast<uint8_t*>(scales));
+}
+
+hipError_t launch_round_bf16(const float* x, uint16_t* y, int64_t n, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  const int grid = (int)std::min<int64_t>(8 * cu_count(), (n + kThreads - 1) / kThreads);
+  hipLaunchKernelGGL(round_bf16_kernel, dim3(grid), dim3(kThreads), 0, s, x, y, n);
+  return hipGetLastError();
 }
 
 hipError_t launch_quantize_mx(int dt, const void* x, int64_t R, int C, void* q, void* scales,

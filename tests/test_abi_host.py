@@ -30,7 +30,7 @@ def test_header_declares_the_calls_and_helpers():
                                          "moe_grouped_wgrad", "moe_permute_masked",
                                          "moe_grouped_swiglu_masked", "moe_quantize_mxfp8",
                                          "moe_permute_mxfp8", "moe_grouped_fc1_swiglu_mxfp8",
-                                         "moe_permute_noalloc",
+                                         "moe_permute_noalloc", "moe_round_bf16",
                                          "moe_capacity",
                                          "moe_grouped_workspace_bytes",
                                          "moe_permute_workspace_bytes", "moe_status_str"])
@@ -155,6 +155,15 @@ def test_combine_accepts_missing_weights_only_as_null():
     # NULL weights are the unit-weight unpermute; a misaligned pointer is still rejected
     assert combine(w=FAKE + 2) == MOE_EINVAL
     assert combine(w=None, T=0) == MOE_ESHAPE
+
+
+@pytest.mark.parametrize("x,y,n,code", [
+    (FAKE, FAKE, -1, MOE_ESHAPE), (FAKE, FAKE, 1 << 40, MOE_ESHAPE), (None, FAKE, 10, MOE_EINVAL),
+    (FAKE, None, 10, MOE_EINVAL), (FAKE + 2, FAKE, 10, MOE_EINVAL), (FAKE, FAKE + 1, 10, MOE_EINVAL),
+    (None, None, 0, 0),   # nothing to round: no pointer is needed and nothing is launched
+])
+def test_round_bf16_validation(x, y, n, code):
+    assert lib.moe_round_bf16(x, y, n, None) == code
 
 
 def combine_bwd(dt=1, dout=FAKE, y=FAKE, src=FAKE, off=FAKE, dst=FAKE, w=FAKE, T=64, D=128, E=8,
