@@ -58,16 +58,16 @@ def gemm_source_sha16() -> str:
 # kind: fc1 (forward), wgrad_fc1 (backward), fp8_fc1 (FP8 payload), masked (decode).
 TRAFFIC = {
     "fc1": {
-        "dense8_bf16": (5209979413, "fbcaaa6c3bad33cb"),
-        "etp_shard32_bf16": (837568492, "fbcaaa6c3bad33cb"),
-        "fine64_shared2_bf16": (1593426228, "fbcaaa6c3bad33cb"),
-        "skew32_zipf_bf16": (5250033637, "fbcaaa6c3bad33cb"),
+        "dense8_bf16": (5674999900, "97c5c428d1172108"),
+        "etp_shard32_bf16": (834307914, "97c5c428d1172108"),
+        "fine64_shared2_bf16": (1592039477, "97c5c428d1172108"),
+        "skew32_zipf_bf16": (5333036518, "97c5c428d1172108"),
     },
     "wgrad_fc1": {
-        "dense8_bf16": (8081100900, "fbcaaa6c3bad33cb"),
+        "dense8_bf16": (8012402997, "97c5c428d1172108"),
     },
     "fp8_fc1": {
-        "dense8_bf16": (2442766130, "fbcaaa6c3bad33cb"),
+        "dense8_bf16": (2474709399, "97c5c428d1172108"),
     },
 }
 
