@@ -165,8 +165,8 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock) void route_kernel(
   const int t0 = SHARED ? blockIdx.x * TW : (blockIdx.x * kWavesPerBlock + wave) * TW;
   const int tab = SHARED ? 0 : wave;
   const int nchunk = D / V;
-  // every lane takes the same whole number of chunk pairs, and byte offsets fit 31 bits
-  const bool pipelined = nchunk % (2 * kWave) == 0 &&
+  // every lane takes the same number of chunks, and byte offsets fit 31 bits
+  const bool pipelined = nchunk % kWave == 0 &&
                          (int64_t)max(T, E) * D * (int64_t)sizeof(TIn) < ((int64_t)1 << 31);
 
   for (int e0 = SHARED ? wave * EC : 0; e0 < E; e0 += SHARED ? kWavesPerBlock * EC : EC) {
@@ -194,10 +194,11 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock) void route_kernel(
     if (pipelined) {
       // Buffer loads: one descriptor per tensor, the row's byte offset in a scalar
       // register and the chunk's in one vector register shared by every load. The
-      // loop is uniform and holds no branch, the loads of the step ahead are issued
-      // one step before their sum (the load past the last pair reads a valid chunk and
-      // is not summed), and the compiler's wait before each sum counts exactly the
-      // loads still in flight for the step ahead.
+      // loop runs over pairs of 64-lane steps, is uniform and holds no branch; the
+      // loads of the step ahead are issued one step before their sum (after the last
+      // pair they fetch the odd last step, or re-read a valid chunk that is not
+      // summed), and the compiler's wait before each sum counts exactly the loads
+      // still in flight for the step ahead.
       const __amdgpu_buffer_rsrc_t rx =
           __builtin_amdgcn_make_buffer_rsrc((void*)x, (short)0, T * D * (int)sizeof(TIn), kRawBuffer);
       const __amdgpu_buffer_rsrc_t rw =
@@ -216,15 +217,16 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock) void route_kernel(
         for (int e = 0; e < EC; ++e) wr[b][e] = __builtin_amdgcn_raw_buffer_load_b128(rw, off, sw[e], 0);
         __builtin_amdgcn_sched_barrier(0);   // and the scheduler keeps them ahead of the sum
       };
-      const int npair = nchunk / (2 * kWave);
+      const int nstep = nchunk / kWave;   // chunks per lane
       load(lane, 0);
-      for (int j = 0; j < npair; ++j) {
+      for (int j = 0; j < nstep / 2; ++j) {
         const int c = lane + j * 2 * kWave;
         load(c + kWave, 1);
         sum(xr[0], wr[0]);
         load(min(c + 2 * kWave, nchunk - 1), 0);
         sum(xr[1], wr[1]);
       }
+      if (nstep & 1) sum(xr[0], wr[0]);   // the odd last step, loaded by the last pair
     } else {
       for (int c = lane; c < nchunk; c += kWave) {
 #pragma unroll

@@ -106,7 +106,8 @@ def test_zero_gate_ties_send_every_token_to_lowest_experts(E, k):
 
 
 @pytest.mark.parametrize("T,D,E,k,dtype,zipf", [
-    # whole pairs of 64-lane chunk steps: the pipelined loop, up to 8 experts per wave
+    # a whole number of 64-lane chunk steps per lane: the pipelined loop, up to 8
+    # experts per wave
     (333, 1024, 8, 2, "bf16", 0.0),     # one pair per lane
     (333, 2048, 8, 2, "bf16", 0.0),
     (130, 3072, 8, 2, "bf16", 0.0),     # three pairs
@@ -116,13 +117,18 @@ def test_zero_gate_ties_send_every_token_to_lowest_experts(E, k):
     (250, 2048, 32, 4, "bf16", 1.1),    # shared tokens (E > 8), a bias, T % 8 != 0
     (77, 1024, 256, 8, "bf16", 0.0),    # four logits per lane in the top-k
     (90, 1024, 100, 5, "f32", 0.0),
-    # 192 chunks: not whole pairs, the plain loop
+    # an odd number of steps per lane (3 and 5): the last one after the pairs
     (64, 1536, 8, 2, "bf16", 0.0),
+    (99, 2560, 40, 6, "bf16", 0.0),
+    (70, 256, 8, 3, "f32", 0.0),        # one step per lane, no pair
+    # 136 chunks: lanes take different counts, the plain loop
+    (64, 1088, 8, 2, "bf16", 0.0),
+    (50, 1088, 24, 4, "bf16", 1.1),
 ])
 def test_router_chunk_loops(T, D, E, k, dtype, zipf):
     """The router alone against the oracle: logits and indices bit for bit, weights to
-    float rounding, on both of its chunk loops (the pipelined loop over whole pairs of
-    64-lane steps, and the plain loop)."""
+    float rounding, on both of its chunk loops (the pipelined loop, where every lane takes
+    the same number of 64-lane steps, and the plain loop)."""
     P.log(f"[parity] router T={T} D={D} E={E} k={k} {dtype}")
     cfg = W.MoEConfig("router", T=T, D=D, F=64, E=E, k=k, m_tile=16, dtype=dtype, zipf_s=zipf)
     inp = W.router_inputs(cfg, seed=7)
