@@ -155,7 +155,8 @@ def parse():
                     help="MiB written between timed steps to evict the Infinity Cache (0: none)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only copy MIB MiB device-to-device 10 times (a kernel of known "
-                         "traffic for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE), then exit")
+                         "traffic for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE), then 10 "
+                         "more timed with events (the device-copy rate), then exit")
     return ap.parse_args()
 
 
@@ -168,9 +169,19 @@ def copy_calibration(mib: int) -> None:
     for _ in range(10):
         b.copy_(a)
     torch.cuda.synchronize()
-    print(json.dumps({"copy_calibration_MiB": mib, "launches": 10,
-                      "bytes_read_per_launch": mib * 1024 * 1024,
-                      "bytes_written_per_launch": mib * 1024 * 1024}))
+    # ten more, timed: the rate a plain device copy reaches (read + write bytes), the
+    # ceiling the permute and combine are compared with
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / 10
+    nbytes = mib * 1024 * 1024
+    print(json.dumps({"copy_calibration_MiB": mib, "launches": 20,
+                      "bytes_read_per_launch": nbytes, "bytes_written_per_launch": nbytes,
+                      "us_per_copy_timed": us, "GBps_read_plus_write": 2 * nbytes / us / 1e3}))
 
 
 def cpu_baseline(inp: dict, cfg, tokens: int, min_seconds: float = 10.0) -> dict:
