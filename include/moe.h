@@ -29,12 +29,16 @@
  * The backward GEMMs read the weights and activations in the layouts the forward
  * uses; nothing is transposed in memory.
  *
+ * moe_round_bf16 exposes the float32 -> bf16 rounding that every stored bf16 value
+ * goes through, so that callers and tests can round the same way.
+ *
  * Conventions shared by every call
  * --------------------------------
  * - Pointers named as device buffers are HIP device memory, 16-byte aligned.
  *   The caller allocates and owns every buffer (outputs and scratch included).
  *   The library never allocates or frees memory and keeps no state between
- *   calls except a per-device cache of the compute-unit count.
+ *   calls except a per-device cache of the compute-unit count (and, for
+ *   moe_permute_noalloc, of its static scratch array's device address).
  * - `stream` is a hipStream_t (NULL = the legacy default stream). A call only
  *   enqueues kernels on it; it never synchronises. Calls are re-entrant.
  * - Dense arrays are row-major and contiguous. All float buffers of one call
