@@ -9,7 +9,10 @@
 // With more, the 4 waves of a block share 8 tokens (every gate-weight chunk a wave
 // reads serves 8 tokens) and take the passes over the experts in turn, so there are
 // four times as many waves to hide memory latency; the logits meet in LDS and each
-// wave then routes 2 of the tokens. The 64 lane partials of every pair are combined
+// wave then routes 2 of the tokens. For few tokens (fewer than 8 per two compute units,
+// as in decode batches) blocks of 8 waves share 4 tokens instead, so that the grid
+// still spreads over the chip and each wave runs one pass up to 64 experts.
+// The 64 lane partials of every pair are combined
 // over lane distances 32, 16, 8, 4, 2, 1: recursive halving while a lane holds more
 // than one pair, then plain butterfly steps. Each pair's partials meet in exactly the
 // butterfly's order, so every logit is the same float32 value the fixed order defines,
@@ -148,8 +151,9 @@ __device__ __forceinline__ void route_token(const float* lgrow, int tok, int E, 
 }
 
 // NE: logits per lane in the softmax and top-k (experts e = lane + 64 i, i < NE).
-template <typename TIn, int TW, int EC, bool SHARED, int NE>
-__global__ __launch_bounds__(kWave * kWavesPerBlock) void route_kernel(
+// WPB: waves per block.
+template <typename TIn, int TW, int EC, bool SHARED, int NE, int WPB = kWavesPerBlock>
+__global__ __launch_bounds__(kWave * WPB) void route_kernel(
     const TIn* __restrict__ x, const TIn* __restrict__ wg, const float* __restrict__ bias, int T,
     int D, int E, int k, int renorm, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
     float* __restrict__ logits_out) {
@@ -157,19 +161,19 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock) void route_kernel(
   constexpr int P = TW * EC;                     // (token, expert) pairs per pass
   constexpr int LOGP = P == 16 ? 4 : (P == 32 ? 5 : 6);
   static_assert(P == 16 || P == 32 || P == 64, "pairs per pass");
-  constexpr int NL = SHARED ? 1 : kWavesPerBlock;   // logit tables per block
+  constexpr int NL = SHARED ? 1 : WPB;   // logit tables per block
   __shared__ float lg[NL][TW][NE * kWave];
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   // SHARED: the block's waves share tokens t0 .. t0+TW-1 and split the passes
-  const int t0 = SHARED ? blockIdx.x * TW : (blockIdx.x * kWavesPerBlock + wave) * TW;
+  const int t0 = SHARED ? blockIdx.x * TW : (blockIdx.x * WPB + wave) * TW;
   const int tab = SHARED ? 0 : wave;
   const int nchunk = D / V;
   // every lane takes the same number of chunks, and byte offsets fit 31 bits
   const bool pipelined = nchunk % kWave == 0 &&
                          (int64_t)max(T, E) * D * (int64_t)sizeof(TIn) < ((int64_t)1 << 31);
 
-  for (int e0 = SHARED ? wave * EC : 0; e0 < E; e0 += SHARED ? kWavesPerBlock * EC : EC) {
+  for (int e0 = SHARED ? wave * EC : 0; e0 < E; e0 += SHARED ? WPB * EC : EC) {
     float acc[P];
 #pragma unroll
     for (int p = 0; p < P; ++p) acc[p] = 0.0f;
@@ -247,7 +251,7 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock) void route_kernel(
   }
   __syncthreads();
 
-  for (int t = SHARED ? wave : 0; t < TW; t += SHARED ? kWavesPerBlock : 1) {
+  for (int t = SHARED ? wave : 0; t < TW; t += SHARED ? WPB : 1) {
     const int tok = t0 + t;
     if (tok >= T) break;
     route_token<NE>(&lg[tab][t][0], tok, E, k, renorm, topk_idx, topk_w, logits_out, lane);
@@ -263,7 +267,7 @@ void launch_typed(const TIn* x, const TIn* wg, const float* bias, int T, int D, 
     const dim3 grid((T + TW * kWavesPerBlock - 1) / (TW * kWavesPerBlock));
     hipLaunchKernelGGL((route_kernel<TIn, TW, 8, false, 1>), grid, block, 0, s, x, wg, bias, T,
                        D, E, k, renorm, topk_idx, topk_w, logits);
-  } else {
+  } else if ((T + 7) / 8 >= cu_count() / 2) {
     constexpr int TW = 8;
     const dim3 grid((T + TW - 1) / TW);
     if (E <= kWave)
@@ -275,6 +279,21 @@ void launch_typed(const TIn* x, const TIn* wg, const float* bias, int T, int D, 
     else
       hipLaunchKernelGGL((route_kernel<TIn, TW, 8, true, 16>), grid, block, 0, s, x, wg, bias, T,
                          D, E, k, renorm, topk_idx, topk_w, logits);
+  } else {
+    // Few tokens (decode batches): 8-token blocks would leave most CUs idle and give each
+    // wave a long chain of passes, so blocks of 8 waves share 4 tokens and each wave
+    // takes one group of 8 experts per pass (one pass in all up to 64 experts).
+    constexpr int TW = 4, WPB = 8;
+    const dim3 grid((T + TW - 1) / TW), bigblock(kWave * WPB);
+    if (E <= kWave)
+      hipLaunchKernelGGL((route_kernel<TIn, TW, 8, true, 1, WPB>), grid, bigblock, 0, s, x, wg,
+                         bias, T, D, E, k, renorm, topk_idx, topk_w, logits);
+    else if (E <= 4 * kWave)
+      hipLaunchKernelGGL((route_kernel<TIn, TW, 8, true, 4, WPB>), grid, bigblock, 0, s, x, wg,
+                         bias, T, D, E, k, renorm, topk_idx, topk_w, logits);
+    else
+      hipLaunchKernelGGL((route_kernel<TIn, TW, 8, true, 16, WPB>), grid, bigblock, 0, s, x, wg,
+                         bias, T, D, E, k, renorm, topk_idx, topk_w, logits);
   }
 }
 

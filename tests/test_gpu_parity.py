@@ -114,9 +114,15 @@ def test_zero_gate_ties_send_every_token_to_lowest_experts(E, k):
     (130, 4096, 6, 2, "bf16", 1.1),     # fewer than 8 experts, a bias
     (101, 512, 6, 3, "f32", 0.0),       # float32: 4 values per chunk
     (101, 1024, 8, 3, "f32", 0.0),
-    (250, 2048, 32, 4, "bf16", 1.1),    # shared tokens (E > 8), a bias, T % 8 != 0
+    # E > 8 with few tokens: blocks of 8 waves share 4 tokens
+    (250, 2048, 32, 4, "bf16", 1.1),    # a bias, T % 4 != 0
     (77, 1024, 256, 8, "bf16", 0.0),    # four logits per lane in the top-k
     (90, 1024, 100, 5, "f32", 0.0),
+    (128, 2048, 64, 6, "bf16", 0.0),    # the decode64 router shape
+    # E > 8 with many tokens: blocks of 4 waves share 8 tokens
+    (1500, 512, 32, 4, "bf16", 1.1),
+    (1030, 1024, 256, 8, "bf16", 0.0),
+    (1100, 512, 100, 5, "f32", 0.0),
     # an odd number of steps per lane (3 and 5): the last one after the pairs
     (64, 1536, 8, 2, "bf16", 0.0),
     (99, 2560, 40, 6, "bf16", 0.0),
