@@ -35,7 +35,8 @@ PEAK_F32_TFLOPS = 157.3       # MI355X fp32 vector
 PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
 METRIC = "MoE-layer tokens/sec; grouped-GEMM TFLOP/s (% bf16 MFMA peak); permute GB/s"
 HEADLINE = "dense8_bf16"
-SUITE = ["dense8_bf16", "fine64_shared2_bf16", "skew32_zipf_bf16", "etp_shard32_bf16"]
+SUITE = ["dense8_bf16", "fine64_shared2_bf16", "skew32_zipf_bf16", "etp_shard32_bf16",
+         "decode8_bf16", "decode64_shared2_bf16"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _GEMM_SOURCES = ["grouped_gemm.hip", "lds_dma.hpp", "common.hpp", "decode_gemm.hip"]
@@ -68,6 +69,10 @@ TRAFFIC = {
     },
     "fp8_fc1": {
         "dense8_bf16": (2474709399, "97c5c428d1172108"),
+    },
+    "masked": {
+        "decode8_bf16": (2920374272, "97c5c428d1172108"),
+        "decode64_shared2_bf16": (1168388096, "97c5c428d1172108"),
     },
 }
 
@@ -133,7 +138,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="all",
                     help="all (the four bf16 layer workloads, dense8_bf16 first and the "
-                         "headline) or one workload name")
+                         "headline, then the two decode workloads on the masked layout) or "
+                         "one workload name")
     ap.add_argument("--cpu-sample-tokens", type=int, default=4096)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fp8", action="store_true",
