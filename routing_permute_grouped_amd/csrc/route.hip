@@ -5,7 +5,8 @@
 //
 // A pass covers TW tokens x EC experts: lane l accumulates the 16-byte chunks
 // c = l, l+64, ... of x[t] . wg[e] for the TW*EC (token, expert) pairs, in increasing d.
-// With at most 8 experts every wave takes its own 2 tokens and does the one pass.
+// With at most 8 experts every wave takes its own 2 tokens (1 when there are few) and
+// does the one pass.
 // With more, the 4 waves of a block share 8 tokens (every gate-weight chunk a wave
 // reads serves 8 tokens) and take the passes over the experts in turn, so there are
 // four times as many waves to hide memory latency; the logits meet in LDS and each
@@ -159,8 +160,8 @@ __global__ __launch_bounds__(kWave * WPB) void route_kernel(
     float* __restrict__ logits_out) {
   constexpr int V = Chunk<TIn>::V;
   constexpr int P = TW * EC;                     // (token, expert) pairs per pass
-  constexpr int LOGP = P == 16 ? 4 : (P == 32 ? 5 : 6);
-  static_assert(P == 16 || P == 32 || P == 64, "pairs per pass");
+  constexpr int LOGP = P == 8 ? 3 : (P == 16 ? 4 : (P == 32 ? 5 : 6));
+  static_assert(P == 8 || P == 16 || P == 32 || P == 64, "pairs per pass");
   constexpr int NL = SHARED ? 1 : WPB;   // logit tables per block
   __shared__ float lg[NL][TW][NE * kWave];
   const int lane = threadIdx.x & (kWave - 1);
@@ -262,12 +263,19 @@ template <typename TIn>
 void launch_typed(const TIn* x, const TIn* wg, const float* bias, int T, int D, int E, int k,
                   int renorm, int32_t* topk_idx, float* topk_w, float* logits, hipStream_t s) {
   const dim3 block(kWave * kWavesPerBlock);
-  if (E <= 8) {
+  const bool few = (T + 7) / 8 < cu_count() / 2;   // fewer than 8 tokens per two CUs
+  if (E <= 8 && few) {
+    // few tokens: one per wave, twice the waves for the same chains of chunk steps
+    constexpr int TW = 1;
+    const dim3 grid((T + TW * kWavesPerBlock - 1) / (TW * kWavesPerBlock));
+    hipLaunchKernelGGL((route_kernel<TIn, TW, 8, false, 1>), grid, block, 0, s, x, wg, bias, T,
+                       D, E, k, renorm, topk_idx, topk_w, logits);
+  } else if (E <= 8) {
     constexpr int TW = 2;
     const dim3 grid((T + TW * kWavesPerBlock - 1) / (TW * kWavesPerBlock));
     hipLaunchKernelGGL((route_kernel<TIn, TW, 8, false, 1>), grid, block, 0, s, x, wg, bias, T,
                        D, E, k, renorm, topk_idx, topk_w, logits);
-  } else if ((T + 7) / 8 >= cu_count() / 2) {
+  } else if (!few) {
     constexpr int TW = 8;
     const dim3 grid((T + TW - 1) / TW);
     if (E <= kWave)

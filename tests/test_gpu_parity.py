@@ -107,8 +107,9 @@ def test_zero_gate_ties_send_every_token_to_lowest_experts(E, k):
 
 @pytest.mark.parametrize("T,D,E,k,dtype,zipf", [
     # a whole number of 64-lane chunk steps per lane: the pipelined loop, up to 8
-    # experts per wave
+    # experts per wave (one token per wave below ~1000 tokens, two above)
     (333, 1024, 8, 2, "bf16", 0.0),     # one pair per lane
+    (1201, 1024, 8, 2, "bf16", 0.0),
     (333, 2048, 8, 2, "bf16", 0.0),
     (130, 3072, 8, 2, "bf16", 0.0),     # three pairs
     (130, 4096, 6, 2, "bf16", 1.1),     # fewer than 8 experts, a bias
