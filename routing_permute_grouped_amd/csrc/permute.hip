@@ -600,6 +600,157 @@ __global__ __launch_bounds__(kThreads) void scale_ksteps_kernel(
   }
 }
 
+// Masked layout for a batch of at most kHistTokens tokens (decode): one launch in place
+// of histogram + rank + copy. Every workgroup ranks all T*k slots itself, exactly as
+// rank_kernel ranks one histogram block: each wave counts its contiguous share of the
+// slots per expert, the counts are prefix-summed over the waves, and each wave ranks
+// its slots 64 at a time with ballots. The destinations stay in LDS for the copy of the
+// workgroup's share of the rows (items of kCopyTokens tokens x a 256-chunk slab, as in
+// copy_kernel), whose first rows are read before the ranking so that their latency
+// hides behind it. One more workgroup, the last, copies nothing and writes the maps,
+// the capped counts, the unused slab rows of src_row and the error flags. A few hundred
+// slots cost each workgroup less than the two launches they save.
+template <typename TIn>
+__global__ __launch_bounds__(kThreads) void masked_small_kernel(
+    const TIn* __restrict__ x, const int32_t* __restrict__ idx, int T, int D, int k, int E,
+    int cap, TIn* __restrict__ x_masked, int32_t* __restrict__ counts,
+    int32_t* __restrict__ dst_row, int32_t* __restrict__ src_row,
+    int32_t* __restrict__ dev_err) {
+  constexpr int V = Chunk<TIn>::V;
+  constexpr int kWaves = kThreads / kWave;
+  constexpr int kChunks = kHistTokens * kMaxTopK / kWaves / kWave;   // 64-slot chunks per wave
+  __shared__ int cnt[kMaxExperts];
+  __shared__ int wcnt[kWaves][kMaxExperts];   // per wave: its slots, then its next rank
+  __shared__ int ds[kHistTokens * kMaxTopK];  // every slot's destination row (-1: none)
+  __shared__ int nbad;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wv = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const bool meta = blockIdx.x == gridDim.x - 1;   // the others copy
+  const int ncopy = gridDim.x - 1;
+  const int n = T * k;
+  const int nck = D / V;
+  const int nslab = (nck + kThreads - 1) / kThreads;
+  const int items = (T + kCopyTokens - 1) / kCopyTokens * nslab;
+  const int per_wave = (n + kWaves * kWave - 1) / (kWaves * kWave) * kWave;
+  const int w0 = min(n, wv * per_wave), w1 = min(n, w0 + per_wave);   // this wave's slots
+
+  for (int e = tid; e < E; e += kThreads) {
+    cnt[e] = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) wcnt[w][e] = 0;
+  }
+  if (tid == 0) nbad = 0;
+  // the first item's rows, read ahead of the ranking (a copy workgroup has one: ncopy <= items)
+  u32x4 v[kCopyTokens];
+  if (!meta) {
+    const int g = blockIdx.x / nslab;
+    const int t0 = g * kCopyTokens;
+    const int c = (blockIdx.x - g * nslab) * kThreads + tid;
+    if (c < nck) {
+#pragma unroll
+      for (int i = 0; i < kCopyTokens; ++i)
+        if (t0 + i < T) v[i] = ld16_nt(x + (int64_t)(t0 + i) * D + (int64_t)c * V);
+    }
+  }
+  int own[kChunks];
+#pragma unroll
+  for (int i = 0; i < kChunks; ++i) {
+    const int a = w0 + i * kWave + lane;
+    own[i] = a < w1 ? idx[a] : -1;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kChunks; ++i) {
+    const int e = own[i];
+    if (e >= 0 && e < E)
+      atomicAdd(&wcnt[wv][e], 1);
+    else if (e != -1)
+      atomicAdd(&nbad, 1);
+  }
+  __syncthreads();
+  // totals, and each wave's starting rank per expert (the earlier waves' slots)
+  for (int e = tid; e < E; e += kThreads) {
+    int run = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const int c = wcnt[w][e];
+      wcnt[w][e] = run;
+      run += c;
+    }
+    cnt[e] = run;
+  }
+  __syncthreads();
+
+  // rank this wave's slots in order, 64 at a time; wcnt[wv][e] is the wave's next rank
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+  const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
+  int* next = wcnt[wv];
+#pragma unroll
+  for (int i = 0; i < kChunks; ++i) {
+    const int r0 = w0 + i * kWave;
+    if (r0 >= w1) break;
+    const int a = r0 + lane;
+    const int e = own[i];
+    const bool valid = a < w1 && e >= 0 && e < E;
+    uint64_t same = __ballot(valid);
+    for (int bit = 0; bit < nbits; ++bit) {
+      const uint64_t bal = __ballot(valid && ((e >> bit) & 1));
+      same &= ((e >> bit) & 1) ? bal : ~bal;
+    }
+    int pos = -1;
+    if (valid) {
+      const int rank = next[e] + __popcll(same & lt);
+      pos = rank >= cap ? -1 : e * cap + rank;   // past the slab: dropped
+    }
+    __builtin_amdgcn_wave_barrier();
+    if (valid && (same >> lane) == 1ull) next[e] = next[e] + __popcll(same);
+    __builtin_amdgcn_wave_barrier();
+    if (a < w1) {
+      ds[a] = pos;
+      if (meta) {
+        dst_row[a] = pos;
+        if (pos >= 0) src_row[pos] = a;
+      }
+    }
+  }
+  __syncthreads();
+  if (meta) {   // capped counts, unused slab rows, error flags
+    int over = 0;
+    for (int e = tid; e < E; e += kThreads) {
+      counts[e] = min(cnt[e], cap);
+      over |= cnt[e] > cap;
+    }
+    for (int e = wv; e < E; e += kWaves)   // each wave its experts' unused rows
+      for (int r = min(cnt[e], cap) + lane; r < cap; r += kWave) src_row[(int64_t)e * cap + r] = -1;
+    over = __syncthreads_or(over);
+    if (tid == 0) *dev_err = (nbad != 0) | (over << 1);
+    return;
+  }
+
+  // the rows: this workgroup's items, the first one already in v
+  for (int it = blockIdx.x; it < items; it += ncopy) {
+    const int g = it / nslab;
+    const int t0 = g * kCopyTokens;
+    const int nt = min(kCopyTokens, T - t0);
+    const int c = (it - g * nslab) * kThreads + tid;
+    if (c >= nck) continue;
+    if (it != blockIdx.x) {
+#pragma unroll
+      for (int i = 0; i < kCopyTokens; ++i)
+        if (i < nt) v[i] = ld16_nt(x + (int64_t)(t0 + i) * D + (int64_t)c * V);
+    }
+#pragma unroll
+    for (int i = 0; i < kCopyTokens; ++i) {
+      if (i >= nt) continue;
+      for (int j = 0; j < k; ++j) {
+        const int d = ds[(t0 + i) * k + j];
+        if (d >= 0) st16(x_masked + (int64_t)d * D + (int64_t)c * V, v[i]);
+      }
+    }
+  }
+}
+
 hipError_t launch_copy(int dt, const void* x, int T, int D, int k, int E,
                               const int32_t* dst_row, const int32_t* counts,
                               const int32_t* offsets, void* x_perm, hipStream_t s) {
@@ -660,6 +811,20 @@ hipError_t launch_permute_masked(int dt, const void* x, const int32_t* topk_idx,
                                  int E, int k, int cap, void* x_masked, int32_t* counts,
                                  int32_t* dst_row, int32_t* src_row, void* workspace,
                                  int32_t* dev_err, hipStream_t s) {
+  if (T <= kHistTokens) {   // a decode batch: one launch
+    const int items = (T + kCopyTokens - 1) / kCopyTokens *
+                      ((D / (dt == kF32 ? 4 : 8) + kThreads - 1) / kThreads);
+    const int grid = std::min(8 * cu_count(), items) + 1;   // + the metadata workgroup
+    if (dt == kF32)
+      hipLaunchKernelGGL(masked_small_kernel<float>, dim3(grid), dim3(kThreads), 0, s,
+                         static_cast<const float*>(x), topk_idx, T, D, k, E, cap,
+                         static_cast<float*>(x_masked), counts, dst_row, src_row, dev_err);
+    else
+      hipLaunchKernelGGL(masked_small_kernel<bf16_t>, dim3(grid), dim3(kThreads), 0, s,
+                         static_cast<const bf16_t*>(x), topk_idx, T, D, k, E, cap,
+                         static_cast<bf16_t*>(x_masked), counts, dst_row, src_row, dev_err);
+    return hipGetLastError();
+  }
   const int nbh = (T + kHistTokens - 1) / kHistTokens;
   int32_t* hist = static_cast<int32_t*>(workspace);
   int32_t* bad = hist + (size_t)nbh * E;

@@ -165,6 +165,28 @@ def test_out_of_range_expert_ids_are_flagged_and_skipped():
     assert P.rel_err(g["out"], ref["out"]) <= P.TOL["bf16"]
 
 
+@pytest.mark.parametrize("T", [100, 300])
+def test_masked_out_of_range_expert_ids_are_flagged_and_skipped(T):
+    # the masked permute with bad expert ids, in its one-launch form (T <= 256) and its
+    # three-launch form: flagged in bit 0 of dev_err, skipped like -1 slots
+    P.log(f"[parity] masked permute, invalid expert ids, T={T}")
+    E, k, cap = 16, 4, 32
+    rng = np.random.default_rng(T)
+    idx = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+    idx[3, 0], idx[10, 2], idx[T - 1, 3] = E, -7, 1000
+    clean = np.where((idx >= -1) & (idx < E), idx, -1).astype(np.int32)
+    x = W.f32_to_bf16_bits(rng.standard_normal((T, 128)).astype(np.float32))
+    ml = orc.masked_layout(clean, E, cap)
+    gm = rpg.moe_permute_masked(P.to_dev(x), P.to_dev(idx), E, cap)
+    torch.cuda.synchronize()
+    for key in ("counts", "dst_row", "src_row"):
+        np.testing.assert_array_equal(P.to_host(gm[key]), ml[key], err_msg=key)
+    assert int(P.to_host(gm["dev_err"])[0]) == 1 | (2 if ml["dropped"] else 0)
+    valid = ml["src_row"] >= 0
+    np.testing.assert_array_equal(P.to_host(gm["x_masked"])[valid],
+                                  x[ml["src_row"][valid] // k])
+
+
 @pytest.mark.parametrize("ws_slots", [0, 10])
 def test_grouped_gemm_workspace_sizes(ws_slots):
     # no workspace: every tile whole; 10 slots of 256x256 float32: fc1's 4 tiles split
@@ -406,12 +428,15 @@ def test_grouped_calls_skip_pad_rows_given_counts(split):
 
 
 @pytest.mark.parametrize("T,E,k,mt", [(700, 64, 32, 128), (1537, 1024, 8, 64), (4097, 3, 2, 256),
-                                      (300, 7, 7, 128), (8192, 8, 4, 128), (16384, 1024, 2, 64)])
+                                      (300, 7, 7, 128), (8192, 8, 4, 128), (16384, 1024, 2, 64),
+                                      (256, 1024, 32, 64), (97, 5, 3, 16)])
 def test_permute_layout_extremes(T, E, k, mt):
     # the permute alone against the oracle's layout: top-32 routing (the largest k), the
     # largest expert count, several 256-token histogram blocks with a ragged last one,
     # and -1 slots; every map bit-exact, x_perm exact on token rows and zero on pad rows
-    # (rows past offsets[E] are not the permute's to write). A small histogram table
+    # (rows past offsets[E] are not the permute's to write). At most 256 tokens (the last
+    # two cases: the most slots one masked launch ranks, and a handful) the masked
+    # permute is one launch that ranks every slot in each workgroup. A small histogram table
     # takes the histogram then the rank-and-copy kernel (8192 tokens x top-4 here, like
     # every benchmark workload); the last case's table is too large for it and takes the
     # histogram, rank and copy kernels.
