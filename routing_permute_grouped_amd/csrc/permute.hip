@@ -93,6 +93,53 @@ __global__ __launch_bounds__(kThreads) void hist_kernel(const int32_t* __restric
   if (threadIdx.x == 0) bad[blockIdx.x] = nbad;
 }
 
+// In-place inclusive prefix of the histogram table over its blocks: hist[h][e] becomes
+// expert e's slots in histogram blocks 0..h, so block hb's starting rank is row hb-1
+// and the totals are the last row. A workgroup takes 64 experts, a lane each, and its
+// four waves contiguous quarters of the blocks: each wave sums its quarter, the sums are
+// prefix-summed over the waves, and each wave rewrites its quarter. Integer sums: the
+// result does not depend on their order.
+__global__ __launch_bounds__(kThreads) void hist_scan_kernel(int32_t* __restrict__ hist, int nbh,
+                                                             int E) {
+  constexpr int kWaves = kThreads / kWave;
+  __shared__ int wsum[kWaves][kWave];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wv = threadIdx.x / kWave;
+  const int e = blockIdx.x * kWave + lane;
+  const int per = (nbh + kWaves - 1) / kWaves;
+  const int h0 = min(nbh, wv * per), h1 = min(nbh, h0 + per);
+  int run = 0;
+  if (e < E) {
+    for (int h = h0; h < h1; h += kBatch) {
+      int v[kBatch];
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) v[j] = h + j < h1 ? hist[(int64_t)(h + j) * E + e] : 0;
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) run += v[j];
+    }
+  }
+  wsum[wv][lane] = run;
+  __syncthreads();
+  run = 0;
+  for (int w = 0; w < wv; ++w) run += wsum[w][lane];
+  if (e < E) {
+    for (int h = h0; h < h1; h += kBatch) {
+      int v[kBatch];
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) v[j] = h + j < h1 ? hist[(int64_t)(h + j) * E + e] : 0;
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        run += v[j];
+        if (h + j < h1) hist[(int64_t)(h + j) * E + e] = run;
+      }
+    }
+  }
+}
+
+// The rank pass reads the whole table in each workgroup up to this many entries; above
+// it the table is prefix-summed first (hist_scan_kernel) and each workgroup reads two rows.
+constexpr int kScanAbove = 2048;
+
 // Exclusive prefix sum over the 256 threads of the block.
 __device__ __forceinline__ int block_exclusive_scan(int v, int* wsum) {
   const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
@@ -109,14 +156,34 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* wsum) {
   return before + inc - v;
 }
 
+// src_row[r] = -1 over rows [lo, hi) of every expert e < E, bounds(e, lo, hi) giving the
+// range. Each wave takes 64 experts at a time: its lanes read their bounds, then the wave
+// walks them one by one with the bounds in scalar registers and its lanes over the rows,
+// so no step of the walk waits on LDS. WV is the wave's index (uniform).
+template <typename Bounds>
+__device__ __forceinline__ void clear_rows(int32_t* __restrict__ src_row, int E, int wv, int lane,
+                                           Bounds bounds) {
+  constexpr int kWaves = kThreads / kWave;
+  for (int e0 = wv * kWave; e0 < E; e0 += kWaves * kWave) {
+    int lo = 0, hi = 0;
+    if (e0 + lane < E) bounds(e0 + lane, lo, hi);
+    const int ne = min(kWave, E - e0);
+    for (int j = 0; j < ne; ++j) {
+      const int l = __builtin_amdgcn_readlane(lo, j), h = __builtin_amdgcn_readlane(hi, j);
+      for (int r = l + lane; r < h; r += kWave) src_row[r] = -1;
+    }
+  }
+}
+
 // MASKED: the masked layout (fixed slabs of `cap` rows, expert e from row e*cap; m_tile
 // unused, m_cap = E*cap): ranks at or past cap are dropped, counts are capped, offsets
 // and tile_expert are not written.
 //
 // Workgroup hb < nbh ranks the slots of histogram block hb (tokens [256 hb, 256 hb + 256)):
-// its starting rank per expert is the sum of the table rows before hb, so each
-// workgroup reads the nbh x E table once (nbh^2 E reads in all: 16 M at 65536 tokens
-// and 256 experts). Its four waves take contiguous quarters of the block's slots: each
+// its starting rank per expert is the sum of the table rows before hb. Up to kScanAbove
+// entries each workgroup reads the whole nbh x E table; above, SCANNED, the table
+// holds inclusive prefixes (hist_scan_kernel), row hb-1 is the start and row nbh-1 the
+// totals, so the reads stay linear in the token count. Its four waves take contiguous quarters of the block's slots: each
 // counts its quarter per expert, the counts are prefix-summed over the waves, and each
 // wave then ranks its quarter 64 slots at a time (ballot match), so ranks follow slot
 // order. Workgroup nbh writes counts, offsets, tile_expert, the unused rows and the
@@ -124,7 +191,7 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* wsum) {
 template <bool MASKED>
 __global__ __launch_bounds__(kThreads) void rank_kernel(
     const int32_t* __restrict__ idx, int T, int k, int E, int m_tile, int cap, int64_t m_cap,
-    int nbh,
+    int nbh, bool scanned,
     const int32_t* __restrict__ hist, const int32_t* __restrict__ bad,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
     int32_t* __restrict__ tile_expert, int32_t* __restrict__ dev_err,
@@ -149,8 +216,8 @@ __global__ __launch_bounds__(kThreads) void rank_kernel(
   const int w0 = min(n, wv * per_wave), w1 = min(n, w0 + per_wave);   // this wave's slots
 
   for (int e = tid; e < E; e += kThreads) {
-    cnt[e] = 0;
-    base[e] = 0;
+    cnt[e] = scanned ? hist[(int64_t)(nbh - 1) * E + e] : 0;
+    base[e] = scanned && token_block && hb > 0 ? hist[(int64_t)(hb - 1) * E + e] : 0;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) wcnt[w][e] = 0;
   }
@@ -164,7 +231,7 @@ __global__ __launch_bounds__(kThreads) void rank_kernel(
   __syncthreads();
   // per-expert totals and this block's starting rank (earlier histogram blocks);
   // integer LDS atomics, so the sums do not depend on their order
-  for (int i0 = tid; i0 < nbh * E; i0 += kThreads * kBatch) {
+  for (int i0 = tid; !scanned && i0 < nbh * E; i0 += kThreads * kBatch) {
     int cv[kBatch];
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
@@ -223,9 +290,10 @@ __global__ __launch_bounds__(kThreads) void rank_kernel(
       counts[e] = min(cnt[e], cap);
       over |= cnt[e] > cap;
     }
-    for (int e = 0; e < E; ++e)
-      for (int r = e * cap + min(cnt[e], cap) + tid; r < (e + 1) * cap; r += kThreads)
-        src_row[r] = -1;
+    clear_rows(src_row, E, wv, lane, [&](int e, int& lo, int& hi) {
+      lo = e * cap + min(cnt[e], cap);
+      hi = (e + 1) * cap;
+    });
     int anybad = 0;
     for (int h = tid; h < nbh; h += kThreads) anybad |= bad[h] != 0;
     anybad = __syncthreads_or(anybad);
@@ -251,8 +319,10 @@ __global__ __launch_bounds__(kThreads) void rank_kernel(
       }
       tile_expert[q] = owner;
     }
-    for (int e = 0; e < E; ++e)   // pad rows of every segment
-      for (int r = off[e] + cnt[e] + tid; r < off[e + 1]; r += kThreads) src_row[r] = -1;
+    clear_rows(src_row, E, wv, lane, [&](int e, int& lo, int& hi) {   // every segment's pad rows
+      lo = off[e] + cnt[e];
+      hi = off[e + 1];
+    });
     for (int64_t r = total + tid; r < m_cap; r += kThreads) src_row[r] = -1;
     int anybad = 0;
     for (int h = tid; h < nbh; h += kThreads) anybad |= bad[h] != 0;
@@ -721,8 +791,10 @@ __global__ __launch_bounds__(kThreads) void masked_small_kernel(
       counts[e] = min(cnt[e], cap);
       over |= cnt[e] > cap;
     }
-    for (int e = wv; e < E; e += kWaves)   // each wave its experts' unused rows
-      for (int r = min(cnt[e], cap) + lane; r < cap; r += kWave) src_row[(int64_t)e * cap + r] = -1;
+    clear_rows(src_row, E, wv, lane, [&](int e, int& lo, int& hi) {   // unused slab rows
+      lo = e * cap + min(cnt[e], cap);
+      hi = (e + 1) * cap;
+    });
     over = __syncthreads_or(over);
     if (tid == 0) *dev_err = (nbad != 0) | (over << 1);
     return;
@@ -749,6 +821,15 @@ __global__ __launch_bounds__(kThreads) void masked_small_kernel(
       }
     }
   }
+}
+
+// Prefix-sums a large histogram table in place for the rank pass (true), or leaves a
+// small one for each rank workgroup to read whole (false).
+bool scan_hist(int32_t* hist, int nbh, int E, hipStream_t s) {
+  if ((int64_t)nbh * E <= kScanAbove) return false;
+  hipLaunchKernelGGL(hist_scan_kernel, dim3((E + kWave - 1) / kWave), dim3(kThreads), 0, s, hist,
+                     nbh, E);
+  return true;
 }
 
 hipError_t launch_copy(int dt, const void* x, int T, int D, int k, int E,
@@ -801,8 +882,9 @@ hipError_t launch_permute(int dt, const void* x, const int32_t* topk_idx, int T,
                          static_cast<bf16_t*>(x_perm));
     return hipGetLastError();
   }
+  const bool scanned = scan_hist(hist, nbh, E, s);
   hipLaunchKernelGGL(rank_kernel<false>, dim3(nbh + 1), dim3(kThreads), 0, s, topk_idx, T, k, E,
-                     m_tile, 0, m_cap, nbh, hist, bad, counts, offsets, tile_expert, dev_err,
+                     m_tile, 0, m_cap, nbh, scanned, hist, bad, counts, offsets, tile_expert, dev_err,
                      dst_row, src_row);
   return launch_copy(dt, x, T, D, k, E, dst_row, counts, offsets, x_perm, s);
 }
@@ -829,8 +911,9 @@ hipError_t launch_permute_masked(int dt, const void* x, const int32_t* topk_idx,
   int32_t* hist = static_cast<int32_t*>(workspace);
   int32_t* bad = hist + (size_t)nbh * E;
   hipLaunchKernelGGL(hist_kernel, dim3(nbh), dim3(kThreads), 0, s, topk_idx, T, k, E, hist, bad);
+  const bool scanned = scan_hist(hist, nbh, E, s);
   hipLaunchKernelGGL(rank_kernel<true>, dim3(nbh + 1), dim3(kThreads), 0, s, topk_idx, T, k, E, 0,
-                     cap, (int64_t)E * cap, nbh, hist, bad, counts, nullptr, nullptr, dev_err,
+                     cap, (int64_t)E * cap, nbh, scanned, hist, bad, counts, nullptr, nullptr, dev_err,
                      dst_row, src_row);
   // no pad rows to zero in the masked layout (E = 0 skips that pass)
   return launch_copy(dt, x, T, D, k, 0, dst_row, counts, nullptr, x_masked, s);
@@ -845,8 +928,9 @@ hipError_t launch_permute_mx(const void* xq, const void* xs, const int32_t* topk
   int32_t* hist = static_cast<int32_t*>(workspace);
   int32_t* bad = hist + (size_t)nbh * E;
   hipLaunchKernelGGL(hist_kernel, dim3(nbh), dim3(kThreads), 0, s, topk_idx, T, k, E, hist, bad);
+  const bool scanned = scan_hist(hist, nbh, E, s);
   hipLaunchKernelGGL(rank_kernel<false>, dim3(nbh + 1), dim3(kThreads), 0, s, topk_idx, T, k, E,
-                     m_tile, 0, m_cap, nbh, hist, bad, counts, offsets, tile_expert, dev_err,
+                     m_tile, 0, m_cap, nbh, scanned, hist, bad, counts, offsets, tile_expert, dev_err,
                      dst_row, src_row);
   // the code rows are copied as raw bytes (D bytes = D/2 two-byte units, whole 16-byte
   // chunks as D % 128 == 0); pad rows get zero bytes (code 0 is +0). The scales go into

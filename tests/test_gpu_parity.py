@@ -429,7 +429,8 @@ def test_grouped_calls_skip_pad_rows_given_counts(split):
 
 @pytest.mark.parametrize("T,E,k,mt", [(700, 64, 32, 128), (1537, 1024, 8, 64), (4097, 3, 2, 256),
                                       (300, 7, 7, 128), (8192, 8, 4, 128), (16384, 1024, 2, 64),
-                                      (256, 1024, 32, 64), (97, 5, 3, 16)])
+                                      (256, 1024, 32, 64), (97, 5, 3, 16), (16384, 256, 2, 128),
+                                      (40000, 200, 3, 32), (65536, 8, 2, 128)])
 def test_permute_layout_extremes(T, E, k, mt):
     # the permute alone against the oracle's layout: top-32 routing (the largest k), the
     # largest expert count, several 256-token histogram blocks with a ragged last one,
@@ -438,8 +439,12 @@ def test_permute_layout_extremes(T, E, k, mt):
     # two cases: the most slots one masked launch ranks, and a handful) the masked
     # permute is one launch that ranks every slot in each workgroup. A small histogram table
     # takes the histogram then the rank-and-copy kernel (8192 tokens x top-4 here, like
-    # every benchmark workload); the last case's table is too large for it and takes the
-    # histogram, rank and copy kernels.
+    # every benchmark workload); larger tables take the histogram, rank and copy kernels.
+    # Above 2048 table entries the table is first prefix-summed over its histogram
+    # blocks (16384 tokens over 1024 and 256 experts, 40000 tokens over 200 experts:
+    # 157 blocks, a ragged split over the scan's waves); 65536 tokens over 8 experts
+    # (256 blocks, 2048 entries) is the largest table each rank workgroup reads whole.
+    # The masked layouts of the small cases take the rank kernel without the scan.
     P.log(f"[parity] permute layout T={T} E={E} k={k} m_tile={mt}")
     rng = np.random.default_rng(T + E + k)
     idx = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
