@@ -445,9 +445,10 @@ __global__ __launch_bounds__(kThreads) void copy_kernel(
 }
 
 // Rank and copy in one launch (the contiguous layout, when the histogram table is small
-// enough for every workgroup to read it; see launch_permute). Workgroup g takes tokens
-// [kCopyTokens g, kCopyTokens g + kCopyTokens): it sums the table into the per-expert
-// totals and its histogram block's starting ranks, counts the slots of that block that
+// enough for every workgroup to read it, or SCANNED into inclusive prefixes; see
+// launch_permute). Workgroup g takes tokens [kCopyTokens g, kCopyTokens g + kCopyTokens):
+// it sums the table into the per-expert totals and its histogram block's starting ranks
+// (reads them off rows nbh-1 and hb-1 when SCANNED), counts the slots of that block that
 // precede its tokens, derives the padded offsets, ranks its own slots in slot order
 // (ballot match in wave 0), writes dst_row / src_row, and copies its tokens' rows to
 // their destination rows. Every workgroup then takes a share of the pad rows (zeroed,
@@ -456,7 +457,7 @@ __global__ __launch_bounds__(kThreads) void copy_kernel(
 template <typename TIn>
 __global__ __launch_bounds__(kThreads) void place_kernel(
     const TIn* __restrict__ x, const int32_t* __restrict__ idx, int T, int D, int k, int E,
-    int m_tile, int64_t m_cap, int nbh, const int32_t* __restrict__ hist,
+    int m_tile, int64_t m_cap, int nbh, bool scanned, const int32_t* __restrict__ hist,
     const int32_t* __restrict__ bad, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
     int32_t* __restrict__ tile_expert, int32_t* __restrict__ dev_err,
     int32_t* __restrict__ dst_row, int32_t* __restrict__ src_row, TIn* __restrict__ x_perm) {
@@ -478,8 +479,8 @@ __global__ __launch_bounds__(kThreads) void place_kernel(
   const int64_t a0 = (int64_t)t0 * k;
 
   for (int e = tid; e < E; e += kThreads) {
-    cnt[e] = 0;
-    base[e] = 0;
+    cnt[e] = scanned ? hist[(int64_t)(nbh - 1) * E + e] : 0;
+    base[e] = scanned && hb > 0 ? hist[(int64_t)(hb - 1) * E + e] : 0;
   }
   int own[kCopyTokens * kMaxTopK / kWave];
   if (tid < kWave) {
@@ -491,7 +492,7 @@ __global__ __launch_bounds__(kThreads) void place_kernel(
   }
   __syncthreads();
   // totals and the starting rank of histogram block hb (integer atomics: any order)
-  for (int i0 = tid; i0 < nbh * E; i0 += kThreads * kBatch) {
+  for (int i0 = tid; !scanned && i0 < nbh * E; i0 += kThreads * kBatch) {
     int cv[kBatch];
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
@@ -868,21 +869,24 @@ hipError_t launch_permute(int dt, const void* x, const int32_t* topk_idx, int T,
   hipLaunchKernelGGL(hist_kernel, dim3(nbh), dim3(kThreads), 0, s, topk_idx, T, k, E, hist, bad);
   const int ngroups = (T + kCopyTokens - 1) / kCopyTokens;
   // rank and copy in one launch while every workgroup reading the whole table stays cheap
-  // (at most 2^24 table reads in all: e.g. 16384 tokens with 64 experts)
-  if ((int64_t)ngroups * nbh * E <= ((int64_t)1 << 24)) {
+  // (at most 2^24 table reads in all: e.g. 16384 tokens with 64 experts), or reads two
+  // rows of the prefix-summed table
+  const bool scanned = scan_hist(hist, nbh, E, s);
+  if (scanned || (int64_t)ngroups * nbh * E <= ((int64_t)1 << 24)) {
     if (dt == kF32)
       hipLaunchKernelGGL(place_kernel<float>, dim3(ngroups), dim3(kThreads), 0, s,
                          static_cast<const float*>(x), topk_idx, T, D, k, E, m_tile, m_cap, nbh,
-                         hist, bad, counts, offsets, tile_expert, dev_err, dst_row, src_row,
+                         scanned, hist, bad, counts, offsets, tile_expert, dev_err, dst_row,
+                         src_row,
                          static_cast<float*>(x_perm));
     else
       hipLaunchKernelGGL(place_kernel<bf16_t>, dim3(ngroups), dim3(kThreads), 0, s,
                          static_cast<const bf16_t*>(x), topk_idx, T, D, k, E, m_tile, m_cap, nbh,
-                         hist, bad, counts, offsets, tile_expert, dev_err, dst_row, src_row,
+                         scanned, hist, bad, counts, offsets, tile_expert, dev_err, dst_row,
+                         src_row,
                          static_cast<bf16_t*>(x_perm));
     return hipGetLastError();
   }
-  const bool scanned = scan_hist(hist, nbh, E, s);
   hipLaunchKernelGGL(rank_kernel<false>, dim3(nbh + 1), dim3(kThreads), 0, s, topk_idx, T, k, E,
                      m_tile, 0, m_cap, nbh, scanned, hist, bad, counts, offsets, tile_expert, dev_err,
                      dst_row, src_row);

@@ -89,6 +89,32 @@ def test_mxfp8_layer_parity(name, split_k):
     assert e <= P.TOL["bf16"], f"out: rel err {e:.3e}"
 
 
+def test_mxfp8_permute_large_table():
+    # the FP8 permute with a histogram table large enough to be prefix-summed over its
+    # blocks first (16384 tokens over 256 experts: 64 blocks x 256 entries), -1 slots
+    # among them: metadata, code rows and scales bit-exact, pad rows zero bytes
+    T, E, k, D, mt = 16384, 256, 2, 128, 64
+    P.log(f"[mx] permute T={T} E={E} k={k} D={D} m_tile={mt}")
+    rng = np.random.default_rng(5)
+    idx = np.argsort(rng.random((T, E)), axis=1)[:, :k].astype(np.int32)
+    idx[rng.random((T, k)) < 0.05] = -1
+    xq = rng.integers(0, 256, size=(T, D), dtype=np.uint8)
+    xs = rng.integers(100, 140, size=(T, D // 32), dtype=np.uint8)
+    lay = orc.dispatch_layout(idx, E, mt)
+    g = rpg.moe_permute_mxfp8(P.to_dev(xq), P.to_dev(xs), P.to_dev(idx), E, mt)
+    torch.cuda.synchronize()
+    for key in ("counts", "offsets", "dst_row", "src_row", "tile_expert"):
+        np.testing.assert_array_equal(P.to_host(g[key]), lay[key], err_msg=key)
+    assert int(P.to_host(g["dev_err"])[0]) == 0
+    used = int(lay["offsets"][-1])
+    rows = lay["src_row"][:used]
+    tok = np.where(rows >= 0, rows // k, 0)
+    gq = P.to_host(g["xq_perm"])[:used]
+    gs = P.mx_rows(P.to_host(g["xs_perm"]))[:used]
+    np.testing.assert_array_equal(gq, np.where((rows >= 0)[:, None], xq[tok], 0))
+    np.testing.assert_array_equal(gs, np.where((rows >= 0)[:, None], xs[tok], 0))
+
+
 def test_mxfp8_full_size_dense8_sampled():
     """The dense 8-expert workload at full size, in the bench's launch configuration:
     routing and layout bit-exact; 4 sampled tokens' outputs against the oracle."""

@@ -439,12 +439,13 @@ def test_permute_layout_extremes(T, E, k, mt):
     # two cases: the most slots one masked launch ranks, and a handful) the masked
     # permute is one launch that ranks every slot in each workgroup. A small histogram table
     # takes the histogram then the rank-and-copy kernel (8192 tokens x top-4 here, like
-    # every benchmark workload); larger tables take the histogram, rank and copy kernels.
-    # Above 2048 table entries the table is first prefix-summed over its histogram
-    # blocks (16384 tokens over 1024 and 256 experts, 40000 tokens over 200 experts:
-    # 157 blocks, a ragged split over the scan's waves); 65536 tokens over 8 experts
-    # (256 blocks, 2048 entries) is the largest table each rank workgroup reads whole.
-    # The masked layouts of the small cases take the rank kernel without the scan.
+    # every benchmark workload). Above 2048 table entries the table is first
+    # prefix-summed over its histogram blocks and each rank-and-copy workgroup reads two
+    # rows of it (16384 tokens over 1024 and 256 experts, 40000 tokens over 200 experts:
+    # 157 blocks, a ragged split over the scan's waves); a table of at most 2048 entries
+    # too large for every workgroup to read whole (65536 tokens over 8 experts) takes
+    # the histogram, rank and copy kernels. The masked layouts above 256 tokens take the
+    # rank kernel, with the scan from 1537 tokens over 1024 experts up.
     P.log(f"[parity] permute layout T={T} E={E} k={k} m_tile={mt}")
     rng = np.random.default_rng(T + E + k)
     idx = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
