@@ -119,3 +119,30 @@ def test_masked_layer_full_size(name):
     (split-K workspace given; bf16 slabs of at most 128 rows take the decode GEMM). A
     decode batch is small enough for the oracle to compute every row."""
     check_masked(W.preset(name), True, f"full-size {name}")
+
+
+# The masked permute alone at its edges: one token, one expert, top-k = E, the largest
+# row (float32 rows of 65536 values: more copy items than workgroups, so a workgroup
+# copies several), the most slots one launch ranks (256 tokens x top-32 over 1024
+# experts) and the first batch size past it (257 tokens: histogram, rank and copy).
+EDGES = [(1, 1, 1, 64, 16, "f32"), (1, 8, 8, 64, 16, "bf16"), (256, 3, 3, 65536, 256, "f32"),
+         (256, 1024, 32, 64, 16, "bf16"), (257, 16, 4, 128, 32, "bf16"),
+         (200, 40, 6, 192, 16, "bf16")]
+
+
+@pytest.mark.parametrize("T,E,k,D,cap,dt", EDGES)
+def test_masked_permute_edges(T, E, k, D, cap, dt):
+    P.log(f"[masked] permute edge T={T} E={E} k={k} D={D} cap={cap} {dt}")
+    rng = np.random.default_rng(T * 7 + E)
+    idx = np.argsort(rng.random((T, E)), axis=1)[:, :k].astype(np.int32)
+    x32 = rng.standard_normal((T, D)).astype(np.float32)
+    x = x32 if dt == "f32" else W.f32_to_bf16_bits(x32)
+    ml = orc.masked_layout(idx, E, cap)
+    g = rpg.moe_permute_masked(P.to_dev(x), P.to_dev(idx), E, cap)
+    torch.cuda.synchronize()
+    for key in ("counts", "dst_row", "src_row"):
+        np.testing.assert_array_equal(P.to_host(g[key]), ml[key], err_msg=key)
+    assert int(P.to_host(g["dev_err"])[0]) == (2 if ml["dropped"] else 0)
+    rows = ml["src_row"]
+    valid = rows >= 0
+    np.testing.assert_array_equal(P.to_host(g["x_masked"])[valid], x[rows[valid] // k])
