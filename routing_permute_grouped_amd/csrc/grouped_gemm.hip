@@ -1056,6 +1056,244 @@ __global__ __launch_bounds__(NTHR, 1) void gg_bf16_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Ring pipeline for fc1 (bf16) with at most 64 experts: two activation slots and three
+// weight-panel slots (160 KiB, all of the LDS), so a panel is requested two k-steps
+// before its use and the activations one step before. The schedule tables live in
+// registers: lane e holds expert e's segment bounds and first 256-row block. Tiles,
+// their order and the split-K plan are those of gg_bf16_kernel, so gg_tail_reduce
+// serves both. fc1's epilogue stores from registers; the epilogues that stage the tile
+// in a stage's LDS (fc2, dgrad) stay on gg_bf16_kernel.
+// ---------------------------------------------------------------------------
+constexpr int RING_BYTES = 2 * A_BYTES + 3 * B_BYTES;
+constexpr int RING_MAXE = 64;
+
+struct SchedR {
+  int off, end, val, ts;   // segment start and end, end of its token rows, first block
+};
+
+__device__ __forceinline__ SchedR build_sched_r(const Segs& sg, int E, int m_cap, int& total) {
+  const int e = threadIdx.x & 63;
+  SchedR s{0, 0, 0, 0};
+  if (e < E) {   // the bounds build_sched gives
+    if (sg.cap > 0) {
+      s.off = e * sg.cap;
+      s.end = s.off + max(0, min(sg.counts[e], sg.cap));
+      s.val = s.end;
+    } else {
+      const int mend = max(0, min(sg.offsets[E], m_cap));
+      s.off = max(0, min(sg.offsets[e], mend));
+      s.end = max(0, min(sg.offsets[e + 1], mend));
+      s.val = sg.counts ? max(s.off, min(s.off + max(sg.counts[e], 0), s.end)) : s.end;
+    }
+  }
+  const int nb = (max(s.end - s.off, 0) + BM - 1) / BM;
+  int inc = nb;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int v = __shfl_up(inc, d, 64);
+    if (e >= d) inc += v;
+  }
+  s.ts = inc - nb;
+  total = __builtin_amdgcn_readlane(inc, 63);
+  return s;
+}
+
+__device__ __forceinline__ Tile decode_item_r(const SchedR& s, int E, int n_nt, int cols, int w) {
+  const int lane = threadIdx.x & 63;
+  const int blk = w / n_nt;
+  const unsigned long long m = __ballot(lane < E && s.ts <= blk);
+  const int lo = 63 - __clzll(m);
+  const int ts = __builtin_amdgcn_readlane(s.ts, lo);
+  const int off = __builtin_amdgcn_readlane(s.off, lo);
+  const int end = __builtin_amdgcn_readlane(s.end, lo);
+  const int val = __builtin_amdgcn_readlane(s.val, lo);
+  const int nb_e = (max(end - off, 0) + BM - 1) / BM;
+  const int local = w - ts * n_nt;
+  const int gsz = min(GROUP_M, nb_e);
+  const int grp = local / (gsz * n_nt);
+  const int first = grp * gsz;
+  const int gm = min(gsz, nb_e - first);
+  const int within = local - grp * gsz * n_nt;
+  Tile t;
+  t.e = lo;
+  t.m0 = off + (first + within % gm) * BM;
+  t.rows = min(BM, end - t.m0);
+  t.vrows = max(0, min(t.rows, val - t.m0));
+  t.n0 = (within / gm) * cols;
+  return t;
+}
+
+// Slots of a tile's first k-step: activations a (of 2), panel b (of 3). Consecutive
+// k-steps (also across tiles) take consecutive slots.
+struct RingPos {
+  int a, b;
+};
+
+// One tile's main loop on the ring. `aprimed`: the tile's first activation step was
+// issued by the previous tile; `bpre`: how many of its first panel steps were. During
+// step s the activations of step s+1 and the panel of step s+2 are issued (crossing into
+// the next tile: its first activation step and first two panel steps). Each wave's
+// panel pieces of step s+2 are the last vector-memory instructions it issues in step s,
+// so the wait at the top of step s+1 leaves exactly those 4 in flight. Returns the
+// next tile's bpre.
+template <bool HALF>
+__device__ __forceinline__ int mainloop_ring(char* smem, const TileLoads& ld, int kb, int ke,
+                                             RingPos p0, bool aprimed, int bpre,
+                                             const TileLoads& nxt, bool has_next, int nkb,
+                                             int nn, f32x16 (&acc)[HALF ? 2 : 4][2]) {
+  constexpr int WM = HALF ? 2 : 4;
+  constexpr int WN = 2;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int arow0 = (wave & 1) * (HALF ? 64 : 128);
+  const int prow0 = (wave >> 1) * 64;
+  const uint32_t lds0 = lds_addr(smem) + wave * 1024;
+  const uint32_t ldsb = lds0 + 2 * A_BYTES - A_BYTES;   // issue_loads adds A_BYTES for the panel
+
+#pragma unroll
+  for (int i = 0; i < WM; ++i)
+#pragma unroll
+    for (int j = 0; j < WN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+  const int n = ke - kb;
+  const int blim = n + (has_next ? min(2, nn) : 0);
+  auto issue_b = [&](int j) {
+    const int slot = (p0.b + j) % 3;
+    if (j < n) issue_loads(ld, ldsb + slot * B_BYTES, kb + j, 1);
+    else issue_loads(nxt, ldsb + slot * B_BYTES, nkb + j - n, 1);
+  };
+  const int fr = lane & 31;
+  if (!aprimed) issue_loads(ld, lds0 + p0.a * A_BYTES, kb, 0);
+  int bnext = bpre;
+  if (bnext < min(2, n)) issue_b(bnext++);
+  if (bnext < min(2, n)) issue_b(bnext++);
+  int a = p0.a, b = p0.b;
+  bool tail4 = false;
+  for (int s = 0; s < n; ++s) {
+    if (tail4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    const char* sa = smem + a * A_BYTES;
+    const char* sb = smem + 2 * A_BYTES + b * B_BYTES;
+    const bool dob = bnext <= s + 2 && bnext < blim;
+    bf16x8 wf[2][WN], af[2][WM];
+    auto frag = [&](int ks, int buf) {
+      const int chk = ks * 2 + (lane >> 5);
+#pragma unroll
+      for (int nb = 0; nb < WN; ++nb)
+        wf[buf][nb] = *reinterpret_cast<const bf16x8*>(sb + swz(prow0 + nb * 32 + fr, chk));
+#pragma unroll
+      for (int mb = 0; mb < WM; ++mb)
+        af[buf][mb] = *reinterpret_cast<const bf16x8*>(sa + swz(arow0 + mb * 32 + fr, chk));
+    };
+    frag(0, 0);
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      if (ks == 0) {
+        if (s + 1 < n) issue_loads(ld, lds0 + (a ^ 1) * A_BYTES, kb + s + 1, 0);
+        else if (has_next) issue_loads(nxt, lds0 + (a ^ 1) * A_BYTES, nkb, 0);
+      }
+      if (ks == 1 && dob) issue_b(bnext);
+      if (ks + 1 < BK / 16) frag(ks + 1, (ks + 1) & 1);
+#pragma unroll
+      for (int mb = 0; mb < WM; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < WN; ++nb)
+          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[ks & 1][nb], af[ks & 1][mb],
+                                                                acc[mb][nb], 0, 0, 0);
+    }
+    tail4 = dob && bnext == s + 2;
+    if (dob) ++bnext;
+    a ^= 1;
+    b = b == 2 ? 0 : b + 1;
+  }
+  return bnext - n;
+}
+
+template <int MODE>
+__global__ __launch_bounds__(NTHR, 1) void gg_ring_kernel(
+    const bf16_t* __restrict__ A, Segs sg, int E, int K, int N, int m_cap,
+    const bf16_t* __restrict__ W1, const bf16_t* __restrict__ W3, Epi ep,
+    float* __restrict__ ws, int slots) {
+  static_assert(MODE == kFc1, "the ring serves fc1 only");
+  constexpr bool FC1 = true;
+  __shared__ __attribute__((aligned(16))) char smem[RING_BYTES];
+  int nblk;
+  const SchedR sr = build_sched_r(sg, E, m_cap, nblk);
+
+  const int cols = FC1 ? BP / 2 : BP;
+  const int n_nt = (N + cols - 1) / cols;
+  const int total = nblk * n_nt;
+  const int nk = K / BK;
+  const Split sp = split_plan(total, gridDim.x, ws ? slots : 0, nk);
+  const int items = sp.full + sp.tail * sp.S;
+  int vb = blockIdx.x;
+  if (gridDim.x % XCDS == 0) vb = (blockIdx.x % XCDS) * (gridDim.x / XCDS) + blockIdx.x / XCDS;
+
+  struct Work {
+    Tile t;
+    int kb, ke;
+    float* part;
+  };
+  auto work = [&](int w) {
+    Work r;
+    int tile = w;
+    r.kb = 0;
+    r.ke = nk;
+    r.part = nullptr;
+    if (w >= sp.full) {
+      const int j = w - sp.full, sh = j / sp.tail, i = j - sh * sp.tail;
+      tile = sp.full + i;
+      r.kb = sh * sp.nks;
+      r.ke = min(nk, r.kb + sp.nks);
+      r.part = ws + (size_t)j * (BM * BP);
+    }
+    r.t = decode_item_r(sr, E, n_nt, cols, tile);
+    return r;
+  };
+
+  if (vb >= items) return;
+  Work cur = work(vb);
+  TileLoads ld = tile_loads<FC1, false, 2>(cur.t, A, W1, W3, K, N, K);
+  RingPos p{0, 0};
+  bool aprimed = false;
+  int bpre = 0;
+  for (int w = vb; w < items; w += gridDim.x) {
+    const bool has_next = w + (int)gridDim.x < items;
+    Work nw = cur;
+    TileLoads nl = ld;
+    if (has_next) {
+      nw = work(w + gridDim.x);
+      nl = tile_loads<FC1, false, 2>(nw.t, A, W1, W3, K, N, K);
+    }
+    const int nn = has_next ? nw.ke - nw.kb : 0;
+    int nbp;
+    if (cur.t.rows > BM / 2) {
+      f32x16 acc[4][2];
+      nbp = mainloop_ring<false>(smem, ld, cur.kb, cur.ke, p, aprimed, bpre, nl, has_next, nw.kb,
+                                 nn, acc);
+      finish_tile<MODE, false>(smem, cur.t, ep, cur.kb, cur.ke, cur.part, 0, acc);
+    } else {
+      f32x16 acc[2][2];
+      nbp = mainloop_ring<true>(smem, ld, cur.kb, cur.ke, p, aprimed, bpre, nl, has_next, nw.kb,
+                                nn, acc);
+      finish_tile<MODE, true>(smem, cur.t, ep, cur.kb, cur.ke, cur.part, 0, acc);
+    }
+    const int n = cur.ke - cur.kb;
+    p.a ^= n & 1;
+    p.b = (p.b + n) % 3;
+    aprimed = has_next;
+    bpre = nbp;
+    cur = nw;
+    ld = nl;
+  }
+}
+
 // Sums the split-K shares of the tail tiles in split order and applies the MODE
 // epilogue, rounding once to bf16. G must be the grid size the GEMM ran with.
 template <int MODE>
@@ -1504,8 +1742,15 @@ static hipError_t launch_mgrouped(int dt, int mode, bool p_mn, const void* A, Se
   const bf16_t* w3 = static_cast<const bf16_t*>(W3);
   const int mc = (int)m_cap;
   if (mode == kFc1) {
-    hipLaunchKernelGGL((gg_bf16_kernel<kFc1, false>), grid, block, 0, s, a, sg, E, K, N, mc,
-                       w1, w3, K, ep, ws, slots, MxScales{});
+    // the ring while an expert's row blocks fit about one column sweep (then every weight
+    // panel comes from HBM once and the deeper lookahead pays); with more, later sweeps
+    // find their panels in the caches and the ring only costs
+    if (E <= RING_MAXE && m_cap <= (int64_t)(GROUP_M + 1) * BM * E)
+      hipLaunchKernelGGL(gg_ring_kernel<kFc1>, grid, block, 0, s, a, sg, E, K, N, mc, w1, w3,
+                         ep, ws, slots);
+    else
+      hipLaunchKernelGGL((gg_bf16_kernel<kFc1, false>), grid, block, 0, s, a, sg, E, K, N, mc,
+                         w1, w3, K, ep, ws, slots, MxScales{});
     if (slots)
       hipLaunchKernelGGL(gg_tail_reduce<kFc1>, rgrid, rblock, 0, s, sg, E, K, mc, G, slots,
                          ws, ep);
