@@ -59,20 +59,20 @@ def gemm_source_sha16() -> str:
 # kind: fc1 (forward), wgrad_fc1 (backward), fp8_fc1 (FP8 payload), masked (decode).
 TRAFFIC = {
     "fc1": {
-        "dense8_bf16": (5674999900, "97c5c428d1172108"),
-        "etp_shard32_bf16": (834307914, "97c5c428d1172108"),
-        "fine64_shared2_bf16": (1592039477, "97c5c428d1172108"),
-        "skew32_zipf_bf16": (5333036518, "97c5c428d1172108"),
+        "dense8_bf16": (4316497758, "c7786870b4c2bc40"),
+        "etp_shard32_bf16": (1036421241, "c7786870b4c2bc40"),
+        "fine64_shared2_bf16": (2363703753, "c7786870b4c2bc40"),
+        "skew32_zipf_bf16": (5311555045, "c7786870b4c2bc40"),
     },
     "wgrad_fc1": {
-        "dense8_bf16": (8012402997, "97c5c428d1172108"),
+        "dense8_bf16": (8020176733, "c7786870b4c2bc40"),
     },
     "fp8_fc1": {
-        "dense8_bf16": (2474709399, "97c5c428d1172108"),
+        "dense8_bf16": (2479007496, "c7786870b4c2bc40"),
     },
     "masked": {
-        "decode8_bf16": (2920374272, "97c5c428d1172108"),
-        "decode64_shared2_bf16": (1168388096, "97c5c428d1172108"),
+        "decode8_bf16": (2919446509, "c7786870b4c2bc40"),
+        "decode64_shared2_bf16": (1167785760, "c7786870b4c2bc40"),
     },
 }
 
