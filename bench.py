@@ -77,6 +77,12 @@ TRAFFIC = {
 }
 
 
+def fc1_kernel_name(E: int, m_cap: int) -> str:
+    """The kernel the library runs the bf16 fc1 on: the LDS ring while the experts have at
+    most about five 256-row blocks each (at most 64 experts), else the two-stage kernel."""
+    return "gg_ring_kernel<kFc1>" if E <= 64 and m_cap <= 5 * 256 * E else "gg_bf16_kernel<kFc1>"
+
+
 class HipEvent:
     """A timing-only HIP event recorded on a given stream. It is created with
     hipEventDisableSystemFence: a default event's record makes a system-scope fence (an L2
@@ -467,7 +473,8 @@ def run_contiguous(args, cfg, d: dict, headline: bool) -> dict:
                    "n_shared": cfg.n_shared, "F_shared": cfg.F_shared,
                    "routing": cfg.routing, "split_k_tail": gws is not None,
                    "shared_overlap": args.shared_overlap if shared is not None else None},
-        "roofline": {"kernel": "grouped fc1 + silu(a)*b (gg_bf16_kernel<kFc1>)", "bound": "mfma",
+        "roofline": {"kernel": "grouped fc1 + silu(a)*b (%s)" % fc1_kernel_name(E, m_cap),
+                     "bound": "mfma",
                      "achieved": fc1_tflops, "peak": peak, "unit": "TFLOP/s",
                      "frac": fc1_tflops / peak, "traffic": fc1_traffic,
                      "traffic_unit": "bytes per launch", "traffic_note": fc1_traffic_note,
