@@ -489,13 +489,16 @@ __device__ __forceinline__ void dgrad_epilogue(char* stage, const Tile& t, const
 }
 
 // kFc2 epilogue through LDS, the same passes as the dgrad epilogue: the sums, rounded
-// to bf16, go into the LDS stage of the tile's last k-step, 128 rows x 256 columns per
+// to bf16, go into free LDS of the tile's last k-step, 128 rows x 256 columns per
 // pass, and come back by rows, so every store is a whole 16-byte chunk and 32 lanes
 // write 512 consecutive bytes of one row. Stored straight from the accumulator layout, a
-// wave instruction would touch 32 rows with 16 bytes each.
+// wave instruction would touch 32 rows with 16 bytes each. Rows 0-63 of a pass go to
+// `lo`, rows 64-127 to `hi` (32 KiB each: the halves of a stage, or the ring's free
+// activation and panel slots).
 template <bool HALF>
-__device__ __forceinline__ void fc2_epilogue(char* stage, const Tile& t, const Epi& ep,
+__device__ __forceinline__ void fc2_epilogue(char* lo, char* hi, const Tile& t, const Epi& ep,
                                              const f32x16 (&acc)[HALF ? 2 : 4][2]) {
+  auto row = [&](int rl) { return (rl < 64 ? lo : hi) + (rl & 63) * 512; };
   constexpr int WM = HALF ? 2 : 4;
   constexpr int PASSES = HALF ? 1 : 2;
   const int lane = threadIdx.x & 63;
@@ -529,7 +532,7 @@ __device__ __forceinline__ void fc2_epilogue(char* stage, const Tile& t, const E
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             const int u = (prow0 + nb * 32 + g * 8 + (lane >> 5) * 4) >> 2;
-            *reinterpret_cast<uint2*>(stage + rl * 512 + ((u ^ (rl & 31)) << 3)) = pk[mb][nb][g];
+            *reinterpret_cast<uint2*>(row(rl) + ((u ^ (rl & 31)) << 3)) = pk[mb][nb][g];
           }
       }
     }
@@ -541,7 +544,7 @@ __device__ __forceinline__ void fc2_epilogue(char* stage, const Tile& t, const E
       const int r = p * 128 + rl;
       if (r >= t.rows || n >= N) continue;
       const int m = rl & 31;
-      uint4 d = *reinterpret_cast<const uint4*>(stage + rl * 512 + ((c ^ (m >> 1)) << 4));
+      uint4 d = *reinterpret_cast<const uint4*>(row(rl) + ((c ^ (m >> 1)) << 4));
       if (m & 1) d = uint4{d.z, d.w, d.x, d.y};
       *reinterpret_cast<uint4*>(ep.C + (size_t)(t.m0 + r) * N + n) = d;
     }
@@ -551,10 +554,13 @@ __device__ __forceinline__ void fc2_epilogue(char* stage, const Tile& t, const E
 // The end of a tile: the raw float32 sums of a split-K share (`part`, row-major
 // [BM][BP]) or the MODE epilogue. Lane l holds column m = l % 32 of every 32x32 block
 // and panel rows 8*g + 4*(l / 32) + i (i = 0..3) for g = 0..3.
+// ELO, EHI: the free LDS the fc2 epilogue stages through (default: the two halves of the
+// stage the last k-step used).
 template <int MODE, bool HALF>
 __device__ __forceinline__ void finish_tile(char* smem, const Tile& t, const Epi& ep, int kb,
                                             int ke, float* __restrict__ part, int stage0,
-                                            const f32x16 (&acc)[HALF ? 2 : 4][2]) {
+                                            const f32x16 (&acc)[HALF ? 2 : 4][2],
+                                            char* elo = nullptr, char* ehi = nullptr) {
   constexpr int WM = HALF ? 2 : 4;
   constexpr int WN = 2;
   const int lane = threadIdx.x & 63;
@@ -583,7 +589,8 @@ __device__ __forceinline__ void finish_tile(char* smem, const Tile& t, const Epi
     return;
   }
   if (MODE == kFc2) {
-    fc2_epilogue<HALF>(smem + ((stage0 + ke - kb - 1) & 1) * STAGE_BYTES, t, ep, acc);
+    char* st = smem + ((stage0 + ke - kb - 1) & 1) * STAGE_BYTES;
+    fc2_epilogue<HALF>(elo ? elo : st, ehi ? ehi : st + A_BYTES, t, ep, acc);
     return;
   }
 #pragma unroll
@@ -1057,13 +1064,14 @@ __global__ __launch_bounds__(NTHR, 1) void gg_bf16_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Ring pipeline for fc1 (bf16) with at most 64 experts: two activation slots and three
-// weight-panel slots (160 KiB, all of the LDS), so a panel is requested two k-steps
-// before its use and the activations one step before. The schedule tables live in
-// registers: lane e holds expert e's segment bounds and first 256-row block. Tiles,
-// their order and the split-K plan are those of gg_bf16_kernel, so gg_tail_reduce
-// serves both. fc1's epilogue stores from registers; the epilogues that stage the tile
-// in a stage's LDS (fc2, dgrad) stay on gg_bf16_kernel.
+// Ring pipeline for the forward GEMMs (bf16, K-contiguous weights) with at most 64
+// experts: two activation slots and three weight-panel slots (160 KiB, all of the LDS),
+// so a panel is requested two k-steps before its use and the activations one step
+// before. The schedule tables live in registers: lane e holds expert e's segment bounds
+// and first 256-row block. Tiles, their order and the split-K plan are those of
+// gg_bf16_kernel, so gg_tail_reduce serves both. fc2's epilogue stages its tile in the
+// activation and panel slots the tile's last step used (the next tile's first loads
+// went to the others).
 // ---------------------------------------------------------------------------
 constexpr int RING_BYTES = 2 * A_BYTES + 3 * B_BYTES;
 constexpr int RING_MAXE = 64;
@@ -1220,8 +1228,8 @@ __global__ __launch_bounds__(NTHR, 1) void gg_ring_kernel(
     const bf16_t* __restrict__ A, Segs sg, int E, int K, int N, int m_cap,
     const bf16_t* __restrict__ W1, const bf16_t* __restrict__ W3, Epi ep,
     float* __restrict__ ws, int slots) {
-  static_assert(MODE == kFc1, "the ring serves fc1 only");
-  constexpr bool FC1 = true;
+  static_assert(MODE == kFc1 || MODE == kFc2, "the ring serves the forward GEMMs");
+  constexpr bool FC1 = MODE == kFc1;
   __shared__ __attribute__((aligned(16))) char smem[RING_BYTES];
   int nblk;
   const SchedR sr = build_sched_r(sg, E, m_cap, nblk);
@@ -1272,17 +1280,22 @@ __global__ __launch_bounds__(NTHR, 1) void gg_ring_kernel(
       nl = tile_loads<FC1, false, 2>(nw.t, A, W1, W3, K, N, K);
     }
     const int nn = has_next ? nw.ke - nw.kb : 0;
+    // free after the tile's last step: its activation slot and its panel slot (the next
+    // tile's first loads went to the others)
+    const int nlast = cur.ke - cur.kb - 1;
+    char* elo = smem + ((p.a + nlast) & 1) * A_BYTES;
+    char* ehi = smem + 2 * A_BYTES + ((p.b + nlast) % 3) * B_BYTES;
     int nbp;
     if (cur.t.rows > BM / 2) {
       f32x16 acc[4][2];
       nbp = mainloop_ring<false>(smem, ld, cur.kb, cur.ke, p, aprimed, bpre, nl, has_next, nw.kb,
                                  nn, acc);
-      finish_tile<MODE, false>(smem, cur.t, ep, cur.kb, cur.ke, cur.part, 0, acc);
+      finish_tile<MODE, false>(smem, cur.t, ep, cur.kb, cur.ke, cur.part, 0, acc, elo, ehi);
     } else {
       f32x16 acc[2][2];
       nbp = mainloop_ring<true>(smem, ld, cur.kb, cur.ke, p, aprimed, bpre, nl, has_next, nw.kb,
                                 nn, acc);
-      finish_tile<MODE, true>(smem, cur.t, ep, cur.kb, cur.ke, cur.part, 0, acc);
+      finish_tile<MODE, true>(smem, cur.t, ep, cur.kb, cur.ke, cur.part, 0, acc, elo, ehi);
     }
     const int n = cur.ke - cur.kb;
     p.a ^= n & 1;
@@ -1741,11 +1754,12 @@ static hipError_t launch_mgrouped(int dt, int mode, bool p_mn, const void* A, Se
   const bf16_t* w1 = static_cast<const bf16_t*>(W1);
   const bf16_t* w3 = static_cast<const bf16_t*>(W3);
   const int mc = (int)m_cap;
+  // the ring while an expert's row blocks fit about one column sweep (then every weight
+  // panel comes from HBM once and the deeper lookahead pays); with more, later sweeps
+  // find their panels in the caches and the ring only costs
+  const bool ring = E <= RING_MAXE && m_cap <= (int64_t)(GROUP_M + 1) * BM * E;
   if (mode == kFc1) {
-    // the ring while an expert's row blocks fit about one column sweep (then every weight
-    // panel comes from HBM once and the deeper lookahead pays); with more, later sweeps
-    // find their panels in the caches and the ring only costs
-    if (E <= RING_MAXE && m_cap <= (int64_t)(GROUP_M + 1) * BM * E)
+    if (ring)
       hipLaunchKernelGGL(gg_ring_kernel<kFc1>, grid, block, 0, s, a, sg, E, K, N, mc, w1, w3,
                          ep, ws, slots);
     else
@@ -1758,6 +1772,9 @@ static hipError_t launch_mgrouped(int dt, int mode, bool p_mn, const void* A, Se
     if (p_mn)
       hipLaunchKernelGGL((gg_bf16_kernel<kFc2, true>), grid, block, 0, s, a, sg, E, K, N, mc,
                          w1, w3, ksplit, ep, ws, slots, MxScales{});
+    else if (ring)
+      hipLaunchKernelGGL(gg_ring_kernel<kFc2>, grid, block, 0, s, a, sg, E, K, N, mc, w1, w1,
+                         ep, ws, slots);
     else
       hipLaunchKernelGGL((gg_bf16_kernel<kFc2, false>), grid, block, 0, s, a, sg, E, K, N,
                          mc, w1, w1, K, ep, ws, slots, MxScales{});
