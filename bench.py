@@ -59,20 +59,20 @@ def gemm_source_sha16() -> str:
 # kind: fc1 (forward), wgrad_fc1 (backward), fp8_fc1 (FP8 payload), masked (decode).
 TRAFFIC = {
     "fc1": {
-        "dense8_bf16": (4316497758, "c7786870b4c2bc40"),
-        "etp_shard32_bf16": (1036421241, "c7786870b4c2bc40"),
-        "fine64_shared2_bf16": (2363703753, "c7786870b4c2bc40"),
-        "skew32_zipf_bf16": (5311555045, "c7786870b4c2bc40"),
+        "dense8_bf16": (4316417075, "ec23b0769012bcba"),
+        "etp_shard32_bf16": (1034965483, "ec23b0769012bcba"),
+        "fine64_shared2_bf16": (2384506166, "ec23b0769012bcba"),
+        "skew32_zipf_bf16": (5397533361, "ec23b0769012bcba"),
     },
     "wgrad_fc1": {
-        "dense8_bf16": (8020176733, "c7786870b4c2bc40"),
+        "dense8_bf16": (8144705579, "ec23b0769012bcba"),
     },
     "fp8_fc1": {
-        "dense8_bf16": (2479007496, "c7786870b4c2bc40"),
+        "dense8_bf16": (2480918277, "ec23b0769012bcba"),
     },
     "masked": {
-        "decode8_bf16": (2919446509, "c7786870b4c2bc40"),
-        "decode64_shared2_bf16": (1167785760, "c7786870b4c2bc40"),
+        "decode8_bf16": (2920594913, "ec23b0769012bcba"),
+        "decode64_shared2_bf16": (1167546070, "ec23b0769012bcba"),
     },
 }
 
