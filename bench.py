@@ -163,6 +163,9 @@ def parse():
                          "per-stage times of route / permute then include waiting for CUs. "
                          "auto: from the start for decode steps (masked layout), where the "
                          "shared GEMM leaves most CUs idle, none for the others")
+    ap.add_argument("--graph", action="store_true",
+                    help="also capture one contiguous-layout step (without a second stream) in "
+                         "a HIP graph and time K replays of it (reported under `graph`)")
     ap.add_argument("--flush-mib", type=int, default=512,
                     help="MiB written between timed steps to evict the Infinity Cache (0: none)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -440,6 +443,38 @@ def run_contiguous(args, cfg, d: dict, headline: bool) -> dict:
                   "cv": statistics.pstdev(v) / statistics.fmean(v) if statistics.fmean(v) else 0.0}
               for m, v in per.items()}
 
+    graph = None
+    if args.graph and not overlap:
+        # the same step captured once (its kernels only: every buffer is allocated above)
+        # and replayed K times, each between two events, the cache flush outside them; the
+        # replayed output must equal the eager step's bit for bit
+        # (captured on a stream of its own, which step() then launches on; replayed on the
+        # compute stream)
+        ref = buf["out"].clone()
+        g = torch.cuda.CUDAGraph()
+        main_stream, stream = stream, torch.cuda.Stream()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=stream):
+            step()
+        stream = main_stream
+        gev = [[HipEvent(), HipEvent()] for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for s in range(args.steps):
+            buf["out"].zero_()
+            if flush is not None:
+                flush.fill_(float(s))
+            gev[s][0].record(stream)
+            g.replay()
+            gev[s][1].record(stream)
+        torch.cuda.synchronize()
+        g_us = [gev[s][0].elapsed_time(gev[s][1]) * 1e3 for s in range(args.steps)]
+        graph = {"step_us_mean": statistics.fmean(g_us), "step_us_median": statistics.median(g_us),
+                 "tokens_per_s": T / (statistics.fmean(g_us) * 1e-6),
+                 "matches_eager_bitwise": bool(torch.equal(buf["out"], ref)),
+                 "note": "one step captured with torch.cuda.graph on the compute stream and "
+                         "replayed; eager `value` is unchanged"}
+        del g
+
     counts = buf["counts"].cpu().numpy().astype(np.int64)
     n_valid = int(counts.sum())
     n_padded = int(buf["offsets"][-1].item())      # rows the GEMMs compute, pad rows included
@@ -503,6 +538,8 @@ def run_contiguous(args, cfg, d: dict, headline: bool) -> dict:
         "expert_rows_min_max": [int(counts.min()), int(counts.max())],
         "cpu_baseline": None,
     }
+    if graph is not None:
+        rec["graph"] = graph
     if headline and not args.no_backward:
         rec["backward"] = bench_backward(args, cfg, d, buf, shared, gws, flush, n_valid)
     if headline and not args.no_fp8 and cfg.dtype == "bf16" and D % 128 == 0:
